@@ -1,0 +1,197 @@
+/*
+ * strata_moe.h -- C ABI of the MI355X (gfx950) routed-expert prompt MoE layer.
+ *
+ * One call runs the prompt-prefill mixture-of-experts layer that the Strata
+ * pages describe as the "fused int8 experts" (Strata compare
+ * v0.1.35...v0.1.37 page, include/strata/prefill/moe_fused.hpp; called from
+ * the MoE half of Prefill::run on the Winery-Strata prefill.cpp page):
+ *
+ *   1. router projection of the layer input and route() to K experts/token
+ *      with their weights (prefill.cpp, MoE half);
+ *   2. the input rounded to int8 once per token, one scale per 32 values
+ *      (moe_fused.hpp, quantize_act);
+ *   3. the (token, k) pairs grouped by expert on the GPU, no host wait
+ *      (moe_fused.hpp, group: slot[i] = row of pair i, src[row] = token);
+ *   4. per expert: gate/up on the grouped int8 rows, SwiGLU, H rounded to
+ *      int8 per 32 values, then down (moe_fused.hpp, experts);
+ *   5. the combine of each token's K rows with its routing weights.
+ *
+ * Every expert stays resident in device memory (no streaming ring).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named in the argument lists are DEVICE pointers owned by the
+ *     caller unless stated otherwise; the library keeps no reference to them
+ *     after the call returns.  `stream` is a hipStream_t (NULL = the default
+ *     stream); all work is enqueued on it in order and the call returns
+ *     without waiting for the GPU unless stated.
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     non-zero return means nothing (or, for STRATA_MOE_EHIP, not all) of the
+ *     work was enqueued; strata_moe_last_error() then describes why.
+ *   - Sizes: H and I multiples of 64 and 32 respectively (H >= 64, I >= 32),
+ *     1 <= K <= 16, K <= E <= 1024, T * K < 2^31.  T = 0 is a no-op.
+ *   - Thread safety: calls may come from several host threads; calls that
+ *     share the library-owned workspace of one device (the default when no
+ *     workspace was set) must not overlap on different streams.
+ */
+#ifndef STRATA_MOE_H
+#define STRATA_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define STRATA_MOE_OK 0
+#define STRATA_MOE_EINVAL (-1)       /* bad argument: null pointer, size, alignment */
+#define STRATA_MOE_EUNSUPPORTED (-2) /* no gfx950 device, or an unknown weight format */
+#define STRATA_MOE_ENOMEM (-3)       /* workspace allocation failed or was too small */
+#define STRATA_MOE_EHIP (-4)         /* a HIP runtime call or launch failed */
+#define STRATA_MOE_EDATA (-5)        /* a routed expert id out of range (strata_moe_group) */
+
+/* Weight format: 2-bit codes q in {0,1,2,3} with one fp16 scale d per 32
+ * consecutive codes along the reduction dimension; w = d * (q - 1.5).  The
+ * pages' own Q2_0 packs use w = d * (q - 1) (moe_fused.hpp header comment);
+ * this build's layer uses the symmetric map. */
+#define STRATA_MOE_Q2_SYM 1
+
+/* A layer's experts, resident in device memory.  The blobs are written by
+ * strata_moe_pack() in the kernels' own layout (not a GGUF layout).
+ *   gate_up: E blobs of gate_up_stride bytes, expert e at gate_up + e*stride,
+ *            holding the stacked [gate; up] matrix (2I rows x H, reduction
+ *            over H), from which expert e's SwiGLU input is computed.
+ *   down:    E blobs of down_stride bytes (H rows x I, reduction over I).
+ *   router_bias: [E] fp32 added to the router logits before the top-K and
+ *            the softmax, or NULL. */
+typedef struct strata_moe_experts {
+    int32_t n_expert; /* E */
+    int32_t hidden;   /* H */
+    int32_t ffn;      /* I */
+    int32_t format;   /* STRATA_MOE_Q2_SYM */
+    const void* gate_up;
+    int64_t gate_up_stride;
+    const void* down;
+    int64_t down_stride;
+    const float* router_bias;
+} strata_moe_experts;
+
+/* Optional intermediate outputs of strata_moe_prefill_debug (each may be
+ * NULL; all device pointers, sized for T tokens).  The library's own buffers
+ * are copied into them after the layer has run. */
+typedef struct strata_moe_debug {
+    int32_t* ids;     /* [T][K] routed experts, rank order */
+    float* p;         /* [T][K] routing weights */
+    int32_t* offsets; /* [E+1] first grouped row of each expert */
+    int32_t* src;     /* [T*K] token of each grouped row */
+    int32_t* slot;    /* [T*K] grouped row of pair i = t*K + k */
+    int8_t* qx;       /* [T][H] int8 codes of the layer input */
+    float* sx;        /* [T][H/32] their scales */
+    int8_t* qh;       /* [T*K][I] int8 codes of the SwiGLU output, grouped rows */
+    float* sh;        /* [T*K][I/32] their scales */
+} strata_moe_debug;
+
+/* ---------------------------------------------------------------- queries */
+
+/* 1 if the current HIP device is gfx950 (this library's only target), else 0. */
+int strata_moe_device_supported(void);
+
+/* Message for the last non-zero return on this host thread ("" if none). */
+const char* strata_moe_last_error(void);
+
+/* Bytes of one expert's packed gate/up blob and down blob for (H, I); the
+ * caller allocates E times each (the strides passed in strata_moe_experts
+ * must be at least these, multiples of 256). */
+int strata_moe_packed_bytes(int32_t hidden, int32_t ffn, int64_t* gate_up_bytes, int64_t* down_bytes);
+
+/* Device workspace a strata_moe_prefill call of T tokens needs. */
+int strata_moe_workspace_bytes(int64_t T, int32_t K, const strata_moe_experts* experts, size_t* bytes);
+
+/* Hand the library a caller-owned device workspace for the current device
+ * (NULL/0 returns to library-owned, lazily grown workspace).  Calls whose need
+ * exceeds it fail with STRATA_MOE_ENOMEM. */
+int strata_moe_set_workspace(void* dev_ptr, size_t bytes);
+
+/* ---------------------------------------------------------------- packing */
+
+/* Pack experts [e0, e1) from canonical device arrays into the kernels' blobs.
+ *   codes_gu  uint8 [e1-e0][2I][H]     gate rows 0..I-1 then up rows, codes 0..3
+ *   scales_gu uint16 [e1-e0][2I][H/32] fp16 bit patterns
+ *   codes_d   uint8 [e1-e0][H][I]
+ *   scales_d  uint16 [e1-e0][H][I/32]
+ * Expert e is written at gate_up + e*gate_up_stride and down + e*down_stride.
+ * Codes above 3 are masked to their low 2 bits.  Asynchronous on `stream`. */
+int strata_moe_pack(const uint8_t* codes_gu, const uint16_t* scales_gu, const uint8_t* codes_d,
+                    const uint16_t* scales_d, int32_t e0, int32_t e1, int32_t hidden, int32_t ffn, void* gate_up,
+                    int64_t gate_up_stride, void* down, int64_t down_stride, void* stream);
+
+/* The inverse of strata_moe_pack for experts [e0, e1) (round-trip checks). */
+int strata_moe_unpack(const void* gate_up, int64_t gate_up_stride, const void* down, int64_t down_stride, int32_t e0,
+                      int32_t e1, int32_t hidden, int32_t ffn, uint8_t* codes_gu, uint16_t* scales_gu,
+                      uint8_t* codes_d, uint16_t* scales_d, void* stream);
+
+/* ------------------------------------------------------------- the layer */
+
+/* The whole routed-expert layer for T tokens.
+ *   x        [T][H] fp32 layer input (row-major)
+ *   router_w [H][E] fp32 router matrix (column e is expert e's router vector)
+ *   out      [T][H] fp32, overwritten with y[t] = sum_k p[t][k] * down_e(...)
+ * Output rows are accumulated with fp32 atomic adds (the weighted
+ * scatter-add combine), so the last bits may differ between runs. */
+int strata_moe_prefill(const float* x, const float* router_w, const strata_moe_experts* experts, int64_t T,
+                       int32_t K, float* out, void* stream);
+
+/* strata_moe_prefill, then the intermediates copied into `dbg` (host struct
+ * of device pointers). */
+int strata_moe_prefill_debug(const float* x, const float* router_w, const strata_moe_experts* experts, int64_t T,
+                             int32_t K, float* out, const strata_moe_debug* dbg, void* stream);
+
+/* ------------------------------------------- single steps (parity checks) */
+
+/* Router logits and route(): ids [T][K] int32 in rank order (ties -> lower
+ * expert index), p [T][K] fp32 = softmax over the K selected logits.  bias
+ * [E] or NULL.  Near-ties are settled in fp64. */
+int strata_moe_route(const float* x, const float* router_w, const float* bias, int64_t T, int32_t H, int32_t E,
+                     int32_t K, int32_t* ids, float* p, void* stream);
+
+/* Grouping of the (token, k) pairs by expert (stable: ascending pair index).
+ * offsets [E+1], src [T*K], slot [T*K].  Synchronises `stream` to check the
+ * ids; returns STRATA_MOE_EDATA if any id is outside [0, E). */
+int strata_moe_group(const int32_t* ids, int64_t T, int32_t K, int32_t E, int32_t* offsets, int32_t* src,
+                     int32_t* slot, void* stream);
+
+/* Per-32 int8 rounding of fp32 rows: codes [rows][cols], scales
+ * [rows][cols/32]; s = max|v|/127 (fp32), q = round-half-away(v/s). */
+int strata_moe_quantize(const float* v, int64_t rows, int32_t cols, int8_t* codes, float* scales, void* stream);
+
+/* Gate/up + SwiGLU + int8 H for grouped rows: qx/sx from strata_moe_quantize
+ * of the layer input, offsets/src from strata_moe_group; writes qh
+ * [T*K][I] and sh [T*K][I/32]. */
+int strata_moe_gate_up(const int8_t* qx, const float* sx, const int32_t* offsets, const int32_t* src, int64_t T,
+                       int32_t K, const strata_moe_experts* experts, int8_t* qh, float* sh, void* stream);
+
+/* Down + combine from given H codes: out [T][H] is overwritten with
+ * sum_k p[t][k] * down(qh[slot[t*K+k]]).  p [T][K]. */
+int strata_moe_down(const int8_t* qh, const float* sh, const int32_t* offsets, const int32_t* src,
+                    const int32_t* slot, const float* p, int64_t T, int32_t K, const strata_moe_experts* experts,
+                    float* out, void* stream);
+
+/* ----------------------------------------------------------------- timing */
+
+/* Per-kernel GPU timing with HIP events on the launch stream.  enable=1
+ * starts a session of at most `max_calls` layer calls (events are recorded
+ * around each kernel of each call); enable=0 ends it and frees the events. */
+int strata_moe_timing(int enable, int32_t max_calls);
+/* Number of kernel kinds the timing reports and the name of kind `id`. */
+int strata_moe_timing_kinds(void);
+const char* strata_moe_timing_name(int id);
+/* Waits for the recorded events, then writes for each kind the total
+ * milliseconds and the number of launches timed so far in the session. */
+int strata_moe_timing_read(double* total_ms, int32_t* launches, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STRATA_MOE_H */

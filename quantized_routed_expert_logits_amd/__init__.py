@@ -1,0 +1,312 @@
+"""Python binding of libstrata_moe (the MI355X routed-expert prompt MoE layer).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  Tensors are torch tensors on the GPU (torch provides device memory
+and streams); each function takes the same arguments as the C entry point of
+the same name in include/strata_moe.h, with shapes taken from the tensors
+where the C call takes sizes.  There is no CPU fallback: importing this
+package fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libstrata_moe.so")
+
+OK = 0
+EINVAL = -1
+EUNSUPPORTED = -2
+ENOMEM = -3
+EHIP = -4
+EDATA = -5
+Q2_SYM = 1
+
+
+class StrataMoeError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P = ctypes.c_void_p
+_i64, _i32 = ctypes.c_int64, ctypes.c_int32
+
+
+class ExpertsStruct(ctypes.Structure):
+    _fields_ = [("n_expert", _i32), ("hidden", _i32), ("ffn", _i32), ("format", _i32),
+                ("gate_up", _P), ("gate_up_stride", _i64), ("down", _P), ("down_stride", _i64),
+                ("router_bias", _P)]
+
+
+class DebugStruct(ctypes.Structure):
+    _fields_ = [(name, _P) for name in ("ids", "p", "offsets", "src", "slot", "qx", "sx", "qh", "sh")]
+
+
+def _sig(name, args, res=ctypes.c_int):
+    f = getattr(_lib, name)
+    f.argtypes = args
+    f.restype = res
+    return f
+
+
+_sig("strata_moe_device_supported", [])
+_sig("strata_moe_last_error", [], ctypes.c_char_p)
+_sig("strata_moe_packed_bytes", [_i32, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)])
+_sig("strata_moe_workspace_bytes", [_i64, _i32, ctypes.POINTER(ExpertsStruct), ctypes.POINTER(ctypes.c_size_t)])
+_sig("strata_moe_set_workspace", [_P, ctypes.c_size_t])
+_sig("strata_moe_pack", [_P, _P, _P, _P, _i32, _i32, _i32, _i32, _P, _i64, _P, _i64, _P])
+_sig("strata_moe_unpack", [_P, _i64, _P, _i64, _i32, _i32, _i32, _i32, _P, _P, _P, _P, _P])
+_sig("strata_moe_prefill", [_P, _P, ctypes.POINTER(ExpertsStruct), _i64, _i32, _P, _P])
+_sig("strata_moe_prefill_debug", [_P, _P, ctypes.POINTER(ExpertsStruct), _i64, _i32, _P,
+                                  ctypes.POINTER(DebugStruct), _P])
+_sig("strata_moe_route", [_P, _P, _P, _i64, _i32, _i32, _i32, _P, _P, _P])
+_sig("strata_moe_group", [_P, _i64, _i32, _i32, _P, _P, _P, _P])
+_sig("strata_moe_quantize", [_P, _i64, _i32, _P, _P, _P])
+_sig("strata_moe_gate_up", [_P, _P, _P, _P, _i64, _i32, ctypes.POINTER(ExpertsStruct), _P, _P, _P])
+_sig("strata_moe_down", [_P, _P, _P, _P, _P, _P, _i64, _i32, ctypes.POINTER(ExpertsStruct), _P, _P])
+_sig("strata_moe_timing", [ctypes.c_int, _i32])
+_sig("strata_moe_timing_kinds", [])
+_sig("strata_moe_timing_name", [ctypes.c_int], ctypes.c_char_p)
+_sig("strata_moe_timing_read", [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i32), ctypes.c_int])
+
+EXPORTED = [
+    "strata_moe_device_supported", "strata_moe_last_error", "strata_moe_packed_bytes",
+    "strata_moe_workspace_bytes", "strata_moe_set_workspace", "strata_moe_pack", "strata_moe_unpack",
+    "strata_moe_prefill", "strata_moe_prefill_debug", "strata_moe_route", "strata_moe_group",
+    "strata_moe_quantize", "strata_moe_gate_up", "strata_moe_down", "strata_moe_timing",
+    "strata_moe_timing_kinds", "strata_moe_timing_name", "strata_moe_timing_read",
+]
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+def strata_moe_last_error() -> str:
+    return _lib.strata_moe_last_error().decode()
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise StrataMoeError(rc, f"{what}: {strata_moe_last_error()}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("expected a CUDA (HIP) torch tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype(t, dt, name):
+    if t is not None and t.dtype != dt:
+        raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+
+
+# ------------------------------------------------------------------- queries
+def strata_moe_device_supported() -> bool:
+    return bool(_lib.strata_moe_device_supported())
+
+
+def strata_moe_packed_bytes(hidden: int, ffn: int) -> tuple[int, int]:
+    gu, dn = _i64(), _i64()
+    _check(_lib.strata_moe_packed_bytes(hidden, ffn, ctypes.byref(gu), ctypes.byref(dn)), "strata_moe_packed_bytes")
+    return gu.value, dn.value
+
+
+def strata_moe_set_workspace(buf: torch.Tensor | None) -> None:
+    if buf is None:
+        _check(_lib.strata_moe_set_workspace(None, 0), "strata_moe_set_workspace")
+    else:
+        _check(_lib.strata_moe_set_workspace(_ptr(buf), buf.numel() * buf.element_size()), "strata_moe_set_workspace")
+
+
+# ------------------------------------------------------------------- experts
+class Experts:
+    """A layer's packed experts in device memory (blobs owned by torch)."""
+
+    def __init__(self, n_expert: int, hidden: int, ffn: int, router_bias: torch.Tensor | None = None,
+                 device: str | torch.device = "cuda"):
+        self.n_expert, self.hidden, self.ffn = n_expert, hidden, ffn
+        self.gate_up_stride, self.down_stride = strata_moe_packed_bytes(hidden, ffn)
+        self.gate_up = torch.empty(n_expert * self.gate_up_stride, dtype=torch.uint8, device=device)
+        self.down = torch.empty(n_expert * self.down_stride, dtype=torch.uint8, device=device)
+        _dtype(router_bias, torch.float32, "router_bias")
+        self.router_bias = router_bias
+        self.struct = ExpertsStruct(n_expert, hidden, ffn, Q2_SYM, self.gate_up.data_ptr(), self.gate_up_stride,
+                                    self.down.data_ptr(), self.down_stride,
+                                    None if router_bias is None else router_bias.data_ptr())
+
+    def with_router_bias(self, router_bias: torch.Tensor | None) -> "Experts":
+        """The same blobs with another router bias (or none)."""
+        import copy
+
+        _dtype(router_bias, torch.float32, "router_bias")
+        other = copy.copy(self)
+        other.router_bias = router_bias
+        other.struct = ExpertsStruct(self.n_expert, self.hidden, self.ffn, Q2_SYM, self.gate_up.data_ptr(),
+                                     self.gate_up_stride, self.down.data_ptr(), self.down_stride,
+                                     None if router_bias is None else router_bias.data_ptr())
+        return other
+
+    def pack(self, e0: int, codes_gu, scales_gu, codes_d, scales_d, stream=None):
+        """Pack experts [e0, e0 + len(codes_gu)) from canonical arrays (numpy
+        or torch; copied to the device if needed)."""
+        dev = self.gate_up.device
+
+        def to_dev(a, dt):
+            if isinstance(a, np.ndarray):
+                a = torch.from_numpy(np.ascontiguousarray(a))
+            return a.to(device=dev, dtype=dt).contiguous()
+
+        cg, sg = to_dev(codes_gu, torch.uint8), to_dev(scales_gu.view(np.int16) if isinstance(scales_gu, np.ndarray)
+                                                       else scales_gu, torch.int16)
+        cd, sd = to_dev(codes_d, torch.uint8), to_dev(scales_d.view(np.int16) if isinstance(scales_d, np.ndarray)
+                                                      else scales_d, torch.int16)
+        ne = cg.shape[0]
+        assert cg.shape == (ne, 2 * self.ffn, self.hidden) and cd.shape == (ne, self.hidden, self.ffn)
+        strata_moe_pack(cg, sg, cd, sd, e0, e0 + ne, self.hidden, self.ffn, self.gate_up, self.gate_up_stride,
+                        self.down, self.down_stride, stream)
+
+
+def strata_moe_pack(codes_gu, scales_gu, codes_d, scales_d, e0, e1, hidden, ffn, gate_up, gate_up_stride, down,
+                    down_stride, stream=None):
+    _check(_lib.strata_moe_pack(_ptr(codes_gu), _ptr(scales_gu), _ptr(codes_d), _ptr(scales_d), e0, e1, hidden, ffn,
+                                _ptr(gate_up), gate_up_stride, _ptr(down), down_stride, _stream(stream)),
+           "strata_moe_pack")
+
+
+def strata_moe_unpack(experts: Experts, e0: int, e1: int, stream=None):
+    """Returns canonical (codes_gu, scales_gu, codes_d, scales_d) device tensors of experts [e0, e1)."""
+    ne, H, I = e1 - e0, experts.hidden, experts.ffn
+    dev = experts.gate_up.device
+    cg = torch.empty((ne, 2 * I, H), dtype=torch.uint8, device=dev)
+    sg = torch.empty((ne, 2 * I, H // 32), dtype=torch.int16, device=dev)
+    cd = torch.empty((ne, H, I), dtype=torch.uint8, device=dev)
+    sd = torch.empty((ne, H, I // 32), dtype=torch.int16, device=dev)
+    _check(_lib.strata_moe_unpack(_ptr(experts.gate_up), experts.gate_up_stride, _ptr(experts.down),
+                                  experts.down_stride, e0, e1, H, I, _ptr(cg), _ptr(sg), _ptr(cd), _ptr(sd),
+                                  _stream(stream)), "strata_moe_unpack")
+    return cg, sg, cd, sd
+
+
+def strata_moe_workspace_bytes(T: int, K: int, experts: Experts) -> int:
+    b = ctypes.c_size_t()
+    _check(_lib.strata_moe_workspace_bytes(T, K, ctypes.byref(experts.struct), ctypes.byref(b)),
+           "strata_moe_workspace_bytes")
+    return b.value
+
+
+# --------------------------------------------------------------------- layer
+def strata_moe_prefill(x: torch.Tensor, router_w: torch.Tensor, experts: Experts, K: int, out: torch.Tensor,
+                       stream=None) -> torch.Tensor:
+    _dtype(x, torch.float32, "x")
+    _dtype(router_w, torch.float32, "router_w")
+    _dtype(out, torch.float32, "out")
+    T = x.shape[0]
+    _check(_lib.strata_moe_prefill(_ptr(x), _ptr(router_w), ctypes.byref(experts.struct), T, K, _ptr(out),
+                                   _stream(stream)), "strata_moe_prefill")
+    return out
+
+
+def strata_moe_prefill_debug(x, router_w, experts: Experts, K: int, out, stream=None) -> dict:
+    """The layer plus its intermediates (ids, p, offsets, src, slot, qx, sx, qh, sh) as device tensors."""
+    T, H = x.shape
+    E, I, n = experts.n_expert, experts.ffn, x.shape[0] * K
+    dev = x.device
+    d = dict(ids=torch.empty((T, K), dtype=torch.int32, device=dev),
+             p=torch.empty((T, K), dtype=torch.float32, device=dev),
+             offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+             src=torch.empty(n, dtype=torch.int32, device=dev),
+             slot=torch.empty(n, dtype=torch.int32, device=dev),
+             qx=torch.empty((T, H), dtype=torch.int8, device=dev),
+             sx=torch.empty((T, H // 32), dtype=torch.float32, device=dev),
+             qh=torch.empty((n, I), dtype=torch.int8, device=dev),
+             sh=torch.empty((n, I // 32), dtype=torch.float32, device=dev))
+    dbg = DebugStruct(*[d[k].data_ptr() for k in ("ids", "p", "offsets", "src", "slot", "qx", "sx", "qh", "sh")])
+    _check(_lib.strata_moe_prefill_debug(_ptr(x), _ptr(router_w), ctypes.byref(experts.struct), T, K, _ptr(out),
+                                         ctypes.byref(dbg), _stream(stream)), "strata_moe_prefill_debug")
+    d["out"] = out
+    return d
+
+
+# -------------------------------------------------------------- single steps
+def strata_moe_route(x, router_w, bias, K: int, ids=None, p=None, stream=None):
+    T, H = x.shape
+    E = router_w.shape[1]
+    ids = torch.empty((T, K), dtype=torch.int32, device=x.device) if ids is None else ids
+    p = torch.empty((T, K), dtype=torch.float32, device=x.device) if p is None else p
+    _check(_lib.strata_moe_route(_ptr(x), _ptr(router_w), _ptr(bias), T, H, E, K, _ptr(ids), _ptr(p),
+                                 _stream(stream)), "strata_moe_route")
+    return ids, p
+
+
+def strata_moe_group(ids, E: int, stream=None):
+    _dtype(ids, torch.int32, "ids")
+    T, K = ids.shape
+    dev = ids.device
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    src = torch.empty(T * K, dtype=torch.int32, device=dev)
+    slot = torch.empty(T * K, dtype=torch.int32, device=dev)
+    _check(_lib.strata_moe_group(_ptr(ids), T, K, E, _ptr(offsets), _ptr(src), _ptr(slot), _stream(stream)),
+           "strata_moe_group")
+    return offsets, src, slot
+
+
+def strata_moe_quantize(v, stream=None):
+    _dtype(v, torch.float32, "v")
+    rows, cols = v.shape
+    codes = torch.empty((rows, cols), dtype=torch.int8, device=v.device)
+    scales = torch.empty((rows, cols // 32), dtype=torch.float32, device=v.device)
+    _check(_lib.strata_moe_quantize(_ptr(v), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)),
+           "strata_moe_quantize")
+    return codes, scales
+
+
+def strata_moe_gate_up(qx, sx, offsets, src, K: int, experts: Experts, stream=None):
+    T = qx.shape[0]
+    n, I = T * K, experts.ffn
+    qh = torch.empty((n, I), dtype=torch.int8, device=qx.device)
+    sh = torch.empty((n, I // 32), dtype=torch.float32, device=qx.device)
+    _check(_lib.strata_moe_gate_up(_ptr(qx), _ptr(sx), _ptr(offsets), _ptr(src), T, K, ctypes.byref(experts.struct),
+                                   _ptr(qh), _ptr(sh), _stream(stream)), "strata_moe_gate_up")
+    return qh, sh
+
+
+def strata_moe_down(qh, sh, offsets, src, slot, p, experts: Experts, out, stream=None):
+    T, K = p.shape
+    _check(_lib.strata_moe_down(_ptr(qh), _ptr(sh), _ptr(offsets), _ptr(src), _ptr(slot), _ptr(p), T, K,
+                                ctypes.byref(experts.struct), _ptr(out), _stream(stream)), "strata_moe_down")
+    return out
+
+
+# -------------------------------------------------------------------- timing
+def strata_moe_timing(enable: bool, max_calls: int = 0) -> None:
+    _check(_lib.strata_moe_timing(int(enable), max_calls), "strata_moe_timing")
+
+
+def strata_moe_timing_read() -> dict:
+    """{kernel kind: (total ms, launches)} of the current timing session."""
+    n = _lib.strata_moe_timing_kinds()
+    ms = (ctypes.c_double * n)()
+    cnt = (_i32 * n)()
+    _check(_lib.strata_moe_timing_read(ms, cnt, n), "strata_moe_timing_read")
+    return {_lib.strata_moe_timing_name(i).decode(): (ms[i], cnt[i]) for i in range(n)}

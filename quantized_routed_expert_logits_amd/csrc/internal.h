@@ -1,0 +1,66 @@
+// Internal declarations shared by the host library and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace strata_moe {
+
+constexpr int kBlock = 32;        // values per quantization block (both activations and weights)
+constexpr int kTileRows = 64;     // routed rows per GEMM tile (the pages' kTileRows, moe_fused.hpp)
+constexpr int kGroupChunk = 2048; // (token, k) pairs per grouping chunk
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 16;
+constexpr int kSliceRows = 64;    // weight rows per wave slice of a packed matrix (4 MFMA fragments of 16)
+
+// One tile of grouped rows: rows [row0, row0 + nrows) all belong to expert e.
+struct Tile {
+    int32_t e, row0, nrows, pad;
+};
+
+// Packed blob geometry of an M x Kd matrix (M rows, reduction over Kd):
+//   codes  [M/64 slices][Kd/32 blocks][64 lanes][2 x u32]       (2 bits per weight)
+//   scales [M/64 slices][Kd/32 blocks][16 rows][4 fragments] fp16
+inline int64_t packed_matrix_bytes(int64_t M, int64_t Kd) { return M * Kd / 4 + M * Kd / 16; }
+inline int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// Upper bound of the tile count of n grouped rows over E experts.
+inline int64_t max_tiles(int64_t n, int32_t E) { return n / kTileRows + E; }
+
+// ---- launchers; each returns hipGetLastError() after its launches.
+hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, _Float16* q16, int8_t* q8, float* s,
+                           float* u, float* zero_out, hipStream_t st);
+hipError_t launch_f16_to_i8(const _Float16* v, int64_t count, int8_t* out, hipStream_t st);
+hipError_t launch_i8_to_f16(const int8_t* v, int64_t count, _Float16* out, hipStream_t st);
+hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t st);
+
+hipError_t launch_router_logits(const float* x, const float* wr, const float* bias, int64_t T, int32_t H, int32_t E,
+                                float* logits, hipStream_t st);
+hipError_t launch_topk(const float* logits, const float* x, const float* wr, const float* bias, int64_t T, int32_t H,
+                       int32_t E, int32_t K, int32_t* ids, float* p, hipStream_t st);
+
+hipError_t launch_group(const int32_t* ids, const float* p, int64_t n, int32_t K, int32_t E, int32_t* hist,
+                        int32_t* base, int32_t* offsets, Tile* tiles, int32_t* ntiles, int32_t* src, int32_t* slot,
+                        float* prow, int32_t* err, hipStream_t st);
+// The correction term of each (row, block) of H codes, from codes and scales (for injected H codes).
+hipError_t launch_block_correction(const int8_t* q, const float* s, int64_t rows, int32_t cols, float* u,
+                                   hipStream_t st);
+hipError_t launch_tiles_from_offsets(const int32_t* offsets, int32_t E, Tile* tiles, int32_t* ntiles,
+                                     hipStream_t st);
+hipError_t launch_row_weights(const int32_t* slot, const float* p, int64_t n, float* prow, hipStream_t st);
+
+hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const Tile* tiles, const int32_t* ntiles,
+                          int64_t tiles_cap, const int32_t* src, const _Float16* xq, const float* xs,
+                          const float* xu, int32_t H, int32_t I, _Float16* hq, float* hs, float* hu,
+                          hipStream_t st);
+hipError_t launch_down(const uint8_t* blobs, int64_t stride, const Tile* tiles, const int32_t* ntiles,
+                       int64_t tiles_cap, const int32_t* src, const float* prow, const _Float16* hq,
+                       const float* hs, const float* hu, int32_t H, int32_t I, float* y, hipStream_t st);
+
+hipError_t launch_pack(const uint8_t* codes, const uint16_t* scales, int32_t nexp, int32_t M, int32_t Kd,
+                       int32_t gate_up_I, uint8_t* dst, int64_t stride, hipStream_t st);
+hipError_t launch_unpack(const uint8_t* src, int64_t stride, int32_t nexp, int32_t M, int32_t Kd, int32_t gate_up_I,
+                         uint8_t* codes, uint16_t* scales, hipStream_t st);
+
+}  // namespace strata_moe

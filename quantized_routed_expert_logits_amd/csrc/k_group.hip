@@ -1,0 +1,219 @@
+// Grouping of the (token, k) pairs by expert, on the GPU.
+//
+// Strata compare v0.1.35...v0.1.37 page, include/strata/prefill/moe_fused.hpp,
+// group: from the router's ids, per expert its rows (counts, offsets, the list
+// of 64-row tiles), slot[i] = the row of pair i and src[row] = its token
+// i / K, without a host wait.  The order of rows within an expert is left open
+// there; these kernels produce the stable order (ascending pair index) of the
+// MMQ path's host counting sort (Winery-Strata prefill.cpp page, Prefill::run,
+// MoE half), so the grouping is unique and can be compared exactly.
+//
+// Three launches, none of which waits on the host:
+//   hist    one workgroup per chunk of 2048 pairs: LDS histogram of its ids;
+//   scan    one workgroup: per expert the exclusive prefix over chunks, the
+//           counts' exclusive scan over experts (offsets), and the tile list;
+//   scatter one wave per chunk: pairs in order, 64 at a time; each lane's rank
+//           among the lanes of the same expert comes from ballots over the id
+//           bits (multi-split), so rows are assigned in pair order.
+#include "internal.h"
+
+namespace strata_moe {
+
+namespace {
+
+__global__ void __launch_bounds__(256) group_hist_kernel(const int32_t* __restrict__ ids, int64_t n, int32_t E,
+                                                         int32_t* __restrict__ hist, int32_t* __restrict__ err) {
+    __shared__ int32_t h[kMaxExperts];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) h[e] = 0;
+    __syncthreads();
+    const int64_t i0 = (int64_t)blockIdx.x * kGroupChunk;
+    const int64_t i1 = i0 + kGroupChunk < n ? i0 + kGroupChunk : n;
+    bool bad = false;
+    for (int64_t i = i0 + threadIdx.x; i < i1; i += blockDim.x) {
+        const int32_t e = ids[i];
+        if (e < 0 || e >= E)
+            bad = true;
+        else
+            atomicAdd(&h[e], 1);
+    }
+    if (bad) atomicOr(err, 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(int64_t)blockIdx.x * E + e] = h[e];
+}
+
+// Exclusive scan of one value per thread over a workgroup of 1024 threads.
+__device__ int block_exclusive_scan(int v, int* total) {
+    __shared__ int wsum[16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        int w = lane < 16 ? wsum[lane] : 0;
+        int wi = w;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            const int o = __shfl_up(wi, off);
+            if (lane >= off) wi += o;
+        }
+        if (lane < 16) wsum[lane] = wi - w;  // exclusive over waves
+        if (lane == 15) *total = wi;
+    }
+    __syncthreads();
+    const int r = wsum[wave] + incl - v;
+    __syncthreads();
+    return r;
+}
+
+__global__ void __launch_bounds__(1024) group_scan_kernel(const int32_t* __restrict__ hist, int64_t nchunks, int64_t n,
+                                                          int32_t E, int32_t* __restrict__ base,
+                                                          int32_t* __restrict__ offsets, Tile* __restrict__ tiles,
+                                                          int32_t* __restrict__ ntiles) {
+    __shared__ int total_rows, total_tiles;
+    const int e = threadIdx.x;
+    int cnt = 0;
+    if (e < E) {
+        // exclusive prefix over chunks, 8 loads in flight per thread
+        int64_t c = 0;
+        for (; c + 8 <= nchunks; c += 8) {
+            int h[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) h[j] = hist[(c + j) * E + e];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                base[(c + j) * E + e] = cnt;
+                cnt += h[j];
+            }
+        }
+        for (; c < nchunks; ++c) {
+            const int h = hist[c * E + e];
+            base[c * E + e] = cnt;
+            cnt += h;
+        }
+    }
+    const int off = block_exclusive_scan(e < E ? cnt : 0, &total_rows);
+    const int nt = e < E ? (cnt + kTileRows - 1) / kTileRows : 0;
+    const int toff = block_exclusive_scan(nt, &total_tiles);
+    if (e < E) {
+        offsets[e] = off;
+        for (int i = 0; i < nt; ++i) {
+            Tile tl;
+            tl.e = e;
+            tl.row0 = off + i * kTileRows;
+            tl.nrows = cnt - i * kTileRows < kTileRows ? cnt - i * kTileRows : kTileRows;
+            tl.pad = 0;
+            tiles[toff + i] = tl;
+        }
+    }
+    if (e == 0) {
+        offsets[E] = (int32_t)n;
+        *ntiles = total_tiles;
+    }
+}
+
+__global__ void __launch_bounds__(64) group_scatter_kernel(const int32_t* __restrict__ ids, const float* __restrict__ p,
+                                                           int64_t n, int32_t K, int32_t E,
+                                                           const int32_t* __restrict__ base,
+                                                           const int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ src, int32_t* __restrict__ slot,
+                                                           float* __restrict__ prow) {
+    __shared__ int32_t next[kMaxExperts];
+    const int lane = threadIdx.x;
+    for (int e = lane; e < E; e += 64) next[e] = offsets[e] + base[(int64_t)blockIdx.x * E + e];
+    __syncthreads();
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    const int64_t i0 = (int64_t)blockIdx.x * kGroupChunk;
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int step = 0; step < kGroupChunk / 64; ++step) {
+        const int64_t i = i0 + step * 64 + lane;
+        const int32_t e = i < n ? ids[i] : -1;
+        const bool ok = e >= 0 && e < E;
+        uint64_t same = __ballot(ok);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = ok && ((e >> b) & 1);
+            const uint64_t m = __ballot(bit);
+            same &= bit ? m : ~m;
+        }
+        if (!ok) same = 0;
+        const int rank = __popcll(same & below);
+        const int first = ok ? next[e] : 0;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        if (ok) {
+            const int row = first + rank;
+            slot[i] = row;
+            src[row] = (int32_t)(i / K);
+            if (prow) prow[row] = p[i];
+            if ((same >> lane) == 1ull) next[e] = first + __popcll(same);  // the highest lane of this expert
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// The tile list of a given grouping (offsets from the caller).
+__global__ void __launch_bounds__(1024) tiles_from_offsets_kernel(const int32_t* __restrict__ offsets, int32_t E,
+                                                                  Tile* __restrict__ tiles,
+                                                                  int32_t* __restrict__ ntiles) {
+    __shared__ int total_tiles;
+    const int e = threadIdx.x;
+    const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
+    const int nt = (cnt + kTileRows - 1) / kTileRows;
+    const int toff = block_exclusive_scan(nt, &total_tiles);
+    if (e < E)
+        for (int i = 0; i < nt; ++i) {
+            Tile tl;
+            tl.e = e;
+            tl.row0 = offsets[e] + i * kTileRows;
+            tl.nrows = cnt - i * kTileRows < kTileRows ? cnt - i * kTileRows : kTileRows;
+            tl.pad = 0;
+            tiles[toff + i] = tl;
+        }
+    if (e == 0) *ntiles = total_tiles;
+}
+
+__global__ void row_weights_kernel(const int32_t* __restrict__ slot, const float* __restrict__ p, int64_t n,
+                                   float* __restrict__ prow) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) prow[slot[i]] = p[i];
+}
+
+}  // namespace
+
+hipError_t launch_group(const int32_t* ids, const float* p, int64_t n, int32_t K, int32_t E, int32_t* hist,
+                        int32_t* base, int32_t* offsets, Tile* tiles, int32_t* ntiles, int32_t* src, int32_t* slot,
+                        float* prow, int32_t* err, hipStream_t st) {
+    const int64_t nchunks = (n + kGroupChunk - 1) / kGroupChunk;
+    if (nchunks > 0) {
+        hipLaunchKernelGGL(group_hist_kernel, dim3((unsigned)nchunks), dim3(256), 0, st, ids, n, E, hist, err);
+        hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(1024), 0, st, hist, nchunks, n, E, base, offsets,
+                           tiles, ntiles);
+        hipLaunchKernelGGL(group_scatter_kernel, dim3((unsigned)nchunks), dim3(64), 0, st, ids, p, n, K, E, base,
+                           offsets, src, slot, prow);
+    } else {
+        hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(1024), 0, st, hist, (int64_t)0, (int64_t)0, E, base,
+                           offsets, tiles, ntiles);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_tiles_from_offsets(const int32_t* offsets, int32_t E, Tile* tiles, int32_t* ntiles,
+                                     hipStream_t st) {
+    hipLaunchKernelGGL(tiles_from_offsets_kernel, dim3(1), dim3(1024), 0, st, offsets, E, tiles, ntiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_weights(const int32_t* slot, const float* p, int64_t n, float* prow, hipStream_t st) {
+    if (n > 0)
+        hipLaunchKernelGGL(row_weights_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, slot, p, n,
+                           prow);
+    return hipGetLastError();
+}
+
+}  // namespace strata_moe

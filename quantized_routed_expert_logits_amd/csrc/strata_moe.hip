@@ -1,0 +1,600 @@
+// Host side of libstrata_moe: argument checks, the device workspace, the
+// launch sequence of one layer call, the single-step entry points and the
+// per-kernel event timing.  All launches go on the caller's stream; nothing
+// here waits for the GPU except strata_moe_group (its id check) and
+// strata_moe_timing_read.
+//
+// The sequence follows the MoE half of Prefill::run (Winery-Strata
+// prefill.cpp page) on the fused path of moe_fused.hpp (Strata compare
+// v0.1.35...v0.1.37 page): router -> route -> int8 activations once per
+// token -> grouping on the GPU -> experts -> combine, with the combine folded
+// into the down GEMM's epilogue as a weighted scatter-add.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/strata_moe.h"
+#include "internal.h"
+
+using namespace strata_moe;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(STRATA_MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr, what)                        \
+    do {                                           \
+        hipError_t e_ = (expr);                    \
+        if (e_ != hipSuccess) return hip_fail(e_, what); \
+    } while (0)
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// ----------------------------------------------------------------- device
+int check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(STRATA_MOE_EUNSUPPORTED, "no HIP device");
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(STRATA_MOE_EUNSUPPORTED, "no HIP device");
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(STRATA_MOE_EUNSUPPORTED, "device %d is %s; this library is built for gfx950 only", dev,
+                    prop.gcnArchName);
+    return 0;
+}
+
+// -------------------------------------------------------------- workspace
+struct Workspace {
+    void* owned = nullptr;
+    size_t owned_bytes = 0;
+    void* user = nullptr;
+    size_t user_bytes = 0;
+};
+std::mutex g_ws_mu;
+Workspace g_ws[64];
+
+int get_workspace(size_t need, char** out) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(STRATA_MOE_EINVAL, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    Workspace& w = g_ws[dev];
+    if (w.user) {
+        if (w.user_bytes < need)
+            return fail(STRATA_MOE_ENOMEM, "workspace of %zu bytes set, %zu needed", w.user_bytes, need);
+        *out = (char*)w.user;
+        return 0;
+    }
+    if (w.owned_bytes < need) {
+        if (w.owned) {
+            HIP_TRY(hipDeviceSynchronize(), "hipDeviceSynchronize");
+            HIP_TRY(hipFree(w.owned), "hipFree");
+            w.owned = nullptr;
+            w.owned_bytes = 0;
+        }
+        const size_t bytes = (size_t)round_up((int64_t)need, 1 << 20);
+        if (hipMalloc(&w.owned, bytes) != hipSuccess) {
+            w.owned = nullptr;
+            return fail(STRATA_MOE_ENOMEM, "hipMalloc of %zu workspace bytes failed", bytes);
+        }
+        w.owned_bytes = bytes;
+    }
+    *out = (char*)w.owned;
+    return 0;
+}
+
+// Carves the workspace of one layer call.  Every region is 256-byte aligned.
+struct Layout {
+    size_t off = 0;
+    template <typename T>
+    size_t take(int64_t count) {
+        const size_t at = off;
+        off += (size_t)round_up((int64_t)sizeof(T) * (count > 0 ? count : 1), 256);
+        return at;
+    }
+};
+
+struct Buffers {
+    float* logits;
+    int32_t* ids;
+    float* p;
+    _Float16* xq;
+    float* xs;
+    float* xu;
+    int32_t* hist;
+    int32_t* base;
+    int32_t* offsets;
+    Tile* tiles;
+    int32_t* ntiles;
+    int32_t* err;
+    int32_t* src;
+    int32_t* slot;
+    float* prow;
+    _Float16* hq;
+    float* hs;
+    float* hu;
+    int64_t tiles_cap;
+};
+
+struct Offsets {
+    size_t logits, ids, p, xq, xs, xu, hist, base, offsets, tiles, ntiles, err, src, slot, prow, hq, hs, hu, total;
+    int64_t tiles_cap;
+};
+
+Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I) {
+    const int64_t n = T * K;
+    const int64_t nchunks = (n + kGroupChunk - 1) / kGroupChunk;
+    Layout L;
+    Offsets o;
+    o.tiles_cap = max_tiles(n, E);
+    o.logits = L.take<float>(T * E);
+    o.ids = L.take<int32_t>(n);
+    o.p = L.take<float>(n);
+    o.xq = L.take<_Float16>(T * H);
+    o.xs = L.take<float>(T * (H / kBlock));
+    o.xu = L.take<float>(T * (H / kBlock));
+    o.hist = L.take<int32_t>(nchunks * E);
+    o.base = L.take<int32_t>(nchunks * E);
+    o.offsets = L.take<int32_t>(E + 1);
+    o.tiles = L.take<Tile>(o.tiles_cap);
+    o.ntiles = L.take<int32_t>(1);
+    o.err = L.take<int32_t>(1);
+    o.src = L.take<int32_t>(n);
+    o.slot = L.take<int32_t>(n);
+    o.prow = L.take<float>(n);
+    o.hq = L.take<_Float16>(n * I);
+    o.hs = L.take<float>(n * (I / kBlock));
+    o.hu = L.take<float>(n * (I / kBlock));
+    o.total = L.off;
+    return o;
+}
+
+Buffers carve(char* ws, const Offsets& o) {
+    Buffers b;
+    b.logits = (float*)(ws + o.logits);
+    b.ids = (int32_t*)(ws + o.ids);
+    b.p = (float*)(ws + o.p);
+    b.xq = (_Float16*)(ws + o.xq);
+    b.xs = (float*)(ws + o.xs);
+    b.xu = (float*)(ws + o.xu);
+    b.hist = (int32_t*)(ws + o.hist);
+    b.base = (int32_t*)(ws + o.base);
+    b.offsets = (int32_t*)(ws + o.offsets);
+    b.tiles = (Tile*)(ws + o.tiles);
+    b.ntiles = (int32_t*)(ws + o.ntiles);
+    b.err = (int32_t*)(ws + o.err);
+    b.src = (int32_t*)(ws + o.src);
+    b.slot = (int32_t*)(ws + o.slot);
+    b.prow = (float*)(ws + o.prow);
+    b.hq = (_Float16*)(ws + o.hq);
+    b.hs = (float*)(ws + o.hs);
+    b.hu = (float*)(ws + o.hu);
+    b.tiles_cap = o.tiles_cap;
+    return b;
+}
+
+// ----------------------------------------------------------------- timing
+enum Kind { kQuantize, kRouter, kTopK, kGroup, kGateUp, kDown, kNumKinds };
+const char* const kKindNames[kNumKinds] = {"quantize", "router_gemm", "topk", "group", "gate_up", "down"};
+
+struct Timing {
+    bool on = false;
+    int max_calls = 0;
+    int used = 0;
+    std::vector<hipEvent_t> ev;   // [max_calls][kinds][2]
+    std::vector<char> recorded;   // [max_calls][kinds]
+};
+std::mutex g_tm_mu;
+Timing g_tm;
+
+struct CallTimer {
+    int call = -1;
+    hipStream_t st;
+    explicit CallTimer(hipStream_t s) : st(s) {
+        std::lock_guard<std::mutex> lock(g_tm_mu);
+        if (g_tm.on && g_tm.used < g_tm.max_calls) call = g_tm.used++;
+    }
+    void begin(Kind k) {
+        if (call >= 0) hipEventRecord(g_tm.ev[((size_t)call * kNumKinds + k) * 2], st);
+    }
+    void end(Kind k) {
+        if (call >= 0) {
+            hipEventRecord(g_tm.ev[((size_t)call * kNumKinds + k) * 2 + 1], st);
+            g_tm.recorded[(size_t)call * kNumKinds + k] = 1;
+        }
+    }
+};
+
+// ------------------------------------------------------------- validation
+int check_experts(const strata_moe_experts* ex) {
+    if (!ex) return fail(STRATA_MOE_EINVAL, "experts is NULL");
+    if (ex->format != STRATA_MOE_Q2_SYM) return fail(STRATA_MOE_EUNSUPPORTED, "unknown weight format %d", ex->format);
+    if (ex->n_expert < 1 || ex->n_expert > kMaxExperts)
+        return fail(STRATA_MOE_EINVAL, "n_expert %d outside [1, %d]", ex->n_expert, kMaxExperts);
+    if (ex->hidden < 64 || ex->hidden % 64)
+        return fail(STRATA_MOE_EINVAL, "hidden %d is not a positive multiple of 64", ex->hidden);
+    if (ex->ffn < 32 || ex->ffn % 32) return fail(STRATA_MOE_EINVAL, "ffn %d is not a positive multiple of 32", ex->ffn);
+    if (!ex->gate_up || !ex->down) return fail(STRATA_MOE_EINVAL, "expert blob pointer is NULL");
+    const int64_t gu = round_up(packed_matrix_bytes(2LL * ex->ffn, ex->hidden), 256);
+    const int64_t dn = round_up(packed_matrix_bytes(ex->hidden, ex->ffn), 256);
+    if (ex->gate_up_stride < gu || ex->down_stride < dn)
+        return fail(STRATA_MOE_EINVAL, "expert strides (%lld, %lld) below the packed sizes (%lld, %lld)",
+                    (long long)ex->gate_up_stride, (long long)ex->down_stride, (long long)gu, (long long)dn);
+    if (ex->gate_up_stride % 256 || ex->down_stride % 256 || !aligned(ex->gate_up, 256) || !aligned(ex->down, 256))
+        return fail(STRATA_MOE_EINVAL, "expert blobs and strides must be 256-byte aligned");
+    return 0;
+}
+
+int check_tk(int64_t T, int32_t K, int32_t E) {
+    if (T < 0) return fail(STRATA_MOE_EINVAL, "T = %lld is negative", (long long)T);
+    if (K < 1 || K > kMaxTopK) return fail(STRATA_MOE_EINVAL, "K = %d outside [1, %d]", K, kMaxTopK);
+    if (K > E) return fail(STRATA_MOE_EINVAL, "K = %d exceeds the %d experts", K, E);
+    if (T * (int64_t)K >= (int64_t)1 << 31) return fail(STRATA_MOE_EINVAL, "T*K = %lld too large", (long long)(T * K));
+    return 0;
+}
+
+// The layer zeroes `out` before its router reads `x`: the two must not overlap.
+int check_no_overlap(const void* a, const void* b, int64_t bytes) {
+    const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+    if (pa < pb + (uintptr_t)bytes && pb < pa + (uintptr_t)bytes)
+        return fail(STRATA_MOE_EINVAL, "out overlaps x");
+    return 0;
+}
+
+#define TRY(expr)                 \
+    do {                          \
+        int rc_ = (expr);         \
+        if (rc_ != 0) return rc_; \
+    } while (0)
+
+int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int64_t T, int32_t K, float* out,
+              hipStream_t st, Buffers* keep) {
+    const int32_t E = ex->n_expert, H = ex->hidden, I = ex->ffn;
+    const int64_t n = T * K;
+    const Offsets o = plan(T, K, E, H, I);
+    char* ws = nullptr;
+    TRY(get_workspace(o.total, &ws));
+    Buffers b = carve(ws, o);
+    CallTimer tm(st);
+    tm.begin(kQuantize);
+    HIP_TRY(launch_quantize(x, T, H, b.xq, nullptr, b.xs, b.xu, out, st), "quantize launch");
+    tm.end(kQuantize);
+    tm.begin(kRouter);
+    HIP_TRY(launch_router_logits(x, wr, ex->router_bias, T, H, E, b.logits, st), "router launch");
+    tm.end(kRouter);
+    tm.begin(kTopK);
+    HIP_TRY(launch_topk(b.logits, x, wr, ex->router_bias, T, H, E, K, b.ids, b.p, st), "top-K launch");
+    tm.end(kTopK);
+    tm.begin(kGroup);
+    HIP_TRY(launch_fill_zero((float*)b.err, 1, st), "fill launch");
+    HIP_TRY(launch_group(b.ids, b.p, n, K, E, b.hist, b.base, b.offsets, b.tiles, b.ntiles, b.src, b.slot, b.prow,
+                         b.err, st),
+            "group launch");
+    tm.end(kGroup);
+    tm.begin(kGateUp);
+    HIP_TRY(launch_gate_up((const uint8_t*)ex->gate_up, ex->gate_up_stride, b.tiles, b.ntiles, b.tiles_cap, b.src,
+                           b.xq, b.xs, b.xu, H, I, b.hq, b.hs, b.hu, st),
+            "gate/up launch");
+    tm.end(kGateUp);
+    tm.begin(kDown);
+    HIP_TRY(launch_down((const uint8_t*)ex->down, ex->down_stride, b.tiles, b.ntiles, b.tiles_cap, b.src, b.prow,
+                        b.hq, b.hs, b.hu, H, I, out, st),
+            "down launch");
+    tm.end(kDown);
+    if (keep) *keep = b;
+    return 0;
+}
+
+}  // namespace
+
+// ===================================================================== C ABI
+extern "C" {
+
+int strata_moe_device_supported(void) {
+    const std::string saved = g_err;
+    const int rc = check_device();
+    g_err = saved;
+    return rc == 0 ? 1 : 0;
+}
+
+const char* strata_moe_last_error(void) { return g_err.c_str(); }
+
+int strata_moe_packed_bytes(int32_t hidden, int32_t ffn, int64_t* gate_up_bytes, int64_t* down_bytes) {
+    g_err.clear();
+    if (!gate_up_bytes || !down_bytes) return fail(STRATA_MOE_EINVAL, "null output pointer");
+    if (hidden < 64 || hidden % 64 || ffn < 32 || ffn % 32)
+        return fail(STRATA_MOE_EINVAL, "hidden %d / ffn %d must be multiples of 64 / 32", hidden, ffn);
+    *gate_up_bytes = round_up(packed_matrix_bytes(2LL * ffn, hidden), 256);
+    *down_bytes = round_up(packed_matrix_bytes(hidden, ffn), 256);
+    return 0;
+}
+
+int strata_moe_workspace_bytes(int64_t T, int32_t K, const strata_moe_experts* experts, size_t* bytes) {
+    g_err.clear();
+    if (!bytes) return fail(STRATA_MOE_EINVAL, "bytes is NULL");
+    TRY(check_experts(experts));
+    TRY(check_tk(T, K, experts->n_expert));
+    *bytes = plan(T, K, experts->n_expert, experts->hidden, experts->ffn).total;
+    return 0;
+}
+
+int strata_moe_set_workspace(void* dev_ptr, size_t bytes) {
+    g_err.clear();
+    if (dev_ptr && !aligned(dev_ptr, 256)) return fail(STRATA_MOE_EINVAL, "workspace must be 256-byte aligned");
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(STRATA_MOE_EINVAL, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    g_ws[dev].user = dev_ptr;
+    g_ws[dev].user_bytes = dev_ptr ? bytes : 0;
+    return 0;
+}
+
+int strata_moe_pack(const uint8_t* codes_gu, const uint16_t* scales_gu, const uint8_t* codes_d,
+                    const uint16_t* scales_d, int32_t e0, int32_t e1, int32_t hidden, int32_t ffn, void* gate_up,
+                    int64_t gate_up_stride, void* down, int64_t down_stride, void* stream) {
+    g_err.clear();
+    int64_t gu = 0, dn = 0;
+    TRY(strata_moe_packed_bytes(hidden, ffn, &gu, &dn));
+    if (!codes_gu || !scales_gu || !codes_d || !scales_d || !gate_up || !down)
+        return fail(STRATA_MOE_EINVAL, "null pointer");
+    if (e0 < 0 || e1 < e0) return fail(STRATA_MOE_EINVAL, "bad expert range [%d, %d)", e0, e1);
+    if (gate_up_stride < gu || down_stride < dn || gate_up_stride % 256 || down_stride % 256 ||
+        !aligned(gate_up, 256) || !aligned(down, 256))
+        return fail(STRATA_MOE_EINVAL, "blob strides/pointers must be 256-byte aligned and >= the packed sizes");
+    TRY(check_device());
+    hipStream_t st = (hipStream_t)stream;
+    const int32_t ne = e1 - e0;
+    HIP_TRY(launch_pack(codes_gu, scales_gu, ne, 2 * ffn, hidden, ffn, (uint8_t*)gate_up + (int64_t)e0 * gate_up_stride,
+                        gate_up_stride, st),
+            "pack launch");
+    HIP_TRY(launch_pack(codes_d, scales_d, ne, hidden, ffn, 0, (uint8_t*)down + (int64_t)e0 * down_stride, down_stride,
+                        st),
+            "pack launch");
+    return 0;
+}
+
+int strata_moe_unpack(const void* gate_up, int64_t gate_up_stride, const void* down, int64_t down_stride, int32_t e0,
+                      int32_t e1, int32_t hidden, int32_t ffn, uint8_t* codes_gu, uint16_t* scales_gu,
+                      uint8_t* codes_d, uint16_t* scales_d, void* stream) {
+    g_err.clear();
+    int64_t gu = 0, dn = 0;
+    TRY(strata_moe_packed_bytes(hidden, ffn, &gu, &dn));
+    if (!codes_gu || !scales_gu || !codes_d || !scales_d || !gate_up || !down)
+        return fail(STRATA_MOE_EINVAL, "null pointer");
+    if (e0 < 0 || e1 < e0) return fail(STRATA_MOE_EINVAL, "bad expert range [%d, %d)", e0, e1);
+    if (gate_up_stride < gu || down_stride < dn) return fail(STRATA_MOE_EINVAL, "strides below the packed sizes");
+    TRY(check_device());
+    hipStream_t st = (hipStream_t)stream;
+    const int32_t ne = e1 - e0;
+    HIP_TRY(launch_unpack((const uint8_t*)gate_up + (int64_t)e0 * gate_up_stride, gate_up_stride, ne, 2 * ffn, hidden,
+                          ffn, codes_gu, scales_gu, st),
+            "unpack launch");
+    HIP_TRY(launch_unpack((const uint8_t*)down + (int64_t)e0 * down_stride, down_stride, ne, hidden, ffn, 0, codes_d,
+                          scales_d, st),
+            "unpack launch");
+    return 0;
+}
+
+int strata_moe_prefill(const float* x, const float* router_w, const strata_moe_experts* experts, int64_t T,
+                       int32_t K, float* out, void* stream) {
+    g_err.clear();
+    TRY(check_experts(experts));
+    TRY(check_tk(T, K, experts->n_expert));
+    if (T == 0) return 0;
+    if (!x || !router_w || !out) return fail(STRATA_MOE_EINVAL, "null x / router_w / out");
+    if (!aligned(x, 16) || !aligned(out, 16)) return fail(STRATA_MOE_EINVAL, "x and out must be 16-byte aligned");
+    TRY(check_no_overlap(x, out, T * experts->hidden * 4));
+    TRY(check_device());
+    return run_layer(x, router_w, experts, T, K, out, (hipStream_t)stream, nullptr);
+}
+
+int strata_moe_prefill_debug(const float* x, const float* router_w, const strata_moe_experts* experts, int64_t T,
+                             int32_t K, float* out, const strata_moe_debug* dbg, void* stream) {
+    g_err.clear();
+    TRY(check_experts(experts));
+    TRY(check_tk(T, K, experts->n_expert));
+    if (T == 0) return 0;
+    if (!x || !router_w || !out || !dbg) return fail(STRATA_MOE_EINVAL, "null x / router_w / out / dbg");
+    if (!aligned(x, 16) || !aligned(out, 16)) return fail(STRATA_MOE_EINVAL, "x and out must be 16-byte aligned");
+    TRY(check_no_overlap(x, out, T * experts->hidden * 4));
+    TRY(check_device());
+    hipStream_t st = (hipStream_t)stream;
+    Buffers b;
+    TRY(run_layer(x, router_w, experts, T, K, out, st, &b));
+    const int32_t E = experts->n_expert, H = experts->hidden, I = experts->ffn;
+    const int64_t n = T * K;
+    auto cp = [&](void* dst, const void* src, size_t bytes) -> int {
+        if (dst) HIP_TRY(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st), "hipMemcpyAsync");
+        return 0;
+    };
+    TRY(cp(dbg->ids, b.ids, n * 4));
+    TRY(cp(dbg->p, b.p, n * 4));
+    TRY(cp(dbg->offsets, b.offsets, (E + 1) * 4));
+    TRY(cp(dbg->src, b.src, n * 4));
+    TRY(cp(dbg->slot, b.slot, n * 4));
+    TRY(cp(dbg->sx, b.xs, T * (H / kBlock) * 4));
+    TRY(cp(dbg->sh, b.hs, n * (I / kBlock) * 4));
+    if (dbg->qx) HIP_TRY(launch_f16_to_i8(b.xq, T * H, dbg->qx, st), "convert launch");
+    if (dbg->qh) HIP_TRY(launch_f16_to_i8(b.hq, n * I, dbg->qh, st), "convert launch");
+    return 0;
+}
+
+int strata_moe_route(const float* x, const float* router_w, const float* bias, int64_t T, int32_t H, int32_t E,
+                     int32_t K, int32_t* ids, float* p, void* stream) {
+    g_err.clear();
+    if (E < 1 || E > kMaxExperts) return fail(STRATA_MOE_EINVAL, "E = %d outside [1, %d]", E, kMaxExperts);
+    if (H < 64 || H % 64) return fail(STRATA_MOE_EINVAL, "H = %d is not a positive multiple of 64", H);
+    TRY(check_tk(T, K, E));
+    if (T == 0) return 0;
+    if (!x || !router_w || !ids || !p) return fail(STRATA_MOE_EINVAL, "null pointer");
+    if (!aligned(x, 16)) return fail(STRATA_MOE_EINVAL, "x must be 16-byte aligned");
+    TRY(check_device());
+    hipStream_t st = (hipStream_t)stream;
+    Layout L;
+    const size_t lo = L.take<float>(T * E);
+    char* ws = nullptr;
+    TRY(get_workspace(L.off, &ws));
+    float* logits = (float*)(ws + lo);
+    HIP_TRY(launch_router_logits(x, router_w, bias, T, H, E, logits, st), "router launch");
+    HIP_TRY(launch_topk(logits, x, router_w, bias, T, H, E, K, ids, p, st), "top-K launch");
+    return 0;
+}
+
+int strata_moe_group(const int32_t* ids, int64_t T, int32_t K, int32_t E, int32_t* offsets, int32_t* src,
+                     int32_t* slot, void* stream) {
+    g_err.clear();
+    if (E < 1 || E > kMaxExperts) return fail(STRATA_MOE_EINVAL, "E = %d outside [1, %d]", E, kMaxExperts);
+    TRY(check_tk(T, K, E));
+    if (!ids || !offsets || !src || !slot) return fail(STRATA_MOE_EINVAL, "null pointer");
+    TRY(check_device());
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t n = T * K;
+    const int64_t nchunks = (n + kGroupChunk - 1) / kGroupChunk;
+    Layout L;
+    const size_t o_hist = L.take<int32_t>(nchunks * E), o_base = L.take<int32_t>(nchunks * E);
+    const size_t o_tiles = L.take<Tile>(max_tiles(n, E)), o_nt = L.take<int32_t>(1), o_err = L.take<int32_t>(1);
+    char* ws = nullptr;
+    TRY(get_workspace(L.off, &ws));
+    int32_t* err = (int32_t*)(ws + o_err);
+    HIP_TRY(launch_fill_zero((float*)err, 1, st), "fill launch");
+    HIP_TRY(launch_group(ids, nullptr, n, K, E, (int32_t*)(ws + o_hist), (int32_t*)(ws + o_base), offsets,
+                         (Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), src, slot, nullptr, err, st),
+            "group launch");
+    int32_t herr = 0;
+    HIP_TRY(hipMemcpyAsync(&herr, err, 4, hipMemcpyDeviceToHost, st), "hipMemcpyAsync");
+    HIP_TRY(hipStreamSynchronize(st), "hipStreamSynchronize");
+    if (herr) return fail(STRATA_MOE_EDATA, "routed expert id out of range [0, %d)", E);
+    return 0;
+}
+
+int strata_moe_quantize(const float* v, int64_t rows, int32_t cols, int8_t* codes, float* scales, void* stream) {
+    g_err.clear();
+    if (rows < 0 || cols < 32 || cols % 32) return fail(STRATA_MOE_EINVAL, "rows %lld / cols %d", (long long)rows, cols);
+    if (rows == 0) return 0;
+    if (!v || !codes || !scales) return fail(STRATA_MOE_EINVAL, "null pointer");
+    if (!aligned(v, 16) || !aligned(codes, 4)) return fail(STRATA_MOE_EINVAL, "v must be 16-, codes 4-byte aligned");
+    TRY(check_device());
+    HIP_TRY(launch_quantize(v, rows, cols, nullptr, codes, scales, nullptr, nullptr, (hipStream_t)stream),
+            "quantize launch");
+    return 0;
+}
+
+int strata_moe_gate_up(const int8_t* qx, const float* sx, const int32_t* offsets, const int32_t* src, int64_t T,
+                       int32_t K, const strata_moe_experts* experts, int8_t* qh, float* sh, void* stream) {
+    g_err.clear();
+    TRY(check_experts(experts));
+    TRY(check_tk(T, K, experts->n_expert));
+    if (T == 0) return 0;
+    if (!qx || !sx || !offsets || !src || !qh || !sh) return fail(STRATA_MOE_EINVAL, "null pointer");
+    TRY(check_device());
+    hipStream_t st = (hipStream_t)stream;
+    const int32_t E = experts->n_expert, H = experts->hidden, I = experts->ffn;
+    const int64_t n = T * K;
+    Layout L;
+    const size_t o_xq = L.take<_Float16>(T * H), o_xu = L.take<float>(T * (H / kBlock));
+    const size_t o_tiles = L.take<Tile>(max_tiles(n, E)), o_nt = L.take<int32_t>(1);
+    const size_t o_hq = L.take<_Float16>(n * I), o_hu = L.take<float>(n * (I / kBlock));
+    char* ws = nullptr;
+    TRY(get_workspace(L.off, &ws));
+    _Float16* xq = (_Float16*)(ws + o_xq);
+    float* xu = (float*)(ws + o_xu);
+    _Float16* hq = (_Float16*)(ws + o_hq);
+    HIP_TRY(launch_i8_to_f16(qx, T * H, xq, st), "convert launch");
+    HIP_TRY(launch_block_correction(qx, sx, T, H, xu, st), "correction launch");
+    HIP_TRY(launch_tiles_from_offsets(offsets, E, (Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), st), "tiles launch");
+    HIP_TRY(launch_gate_up((const uint8_t*)experts->gate_up, experts->gate_up_stride, (Tile*)(ws + o_tiles),
+                           (int32_t*)(ws + o_nt), max_tiles(n, E), src, xq, sx, xu, H, I, hq, sh,
+                           (float*)(ws + o_hu), st),
+            "gate/up launch");
+    HIP_TRY(launch_f16_to_i8(hq, n * I, qh, st), "convert launch");
+    return 0;
+}
+
+int strata_moe_down(const int8_t* qh, const float* sh, const int32_t* offsets, const int32_t* src,
+                    const int32_t* slot, const float* p, int64_t T, int32_t K, const strata_moe_experts* experts,
+                    float* out, void* stream) {
+    g_err.clear();
+    TRY(check_experts(experts));
+    TRY(check_tk(T, K, experts->n_expert));
+    if (T == 0) return 0;
+    if (!qh || !sh || !offsets || !src || !slot || !p || !out) return fail(STRATA_MOE_EINVAL, "null pointer");
+    TRY(check_device());
+    hipStream_t st = (hipStream_t)stream;
+    const int32_t E = experts->n_expert, H = experts->hidden, I = experts->ffn;
+    const int64_t n = T * K;
+    Layout L;
+    const size_t o_hq = L.take<_Float16>(n * I), o_hu = L.take<float>(n * (I / kBlock));
+    const size_t o_tiles = L.take<Tile>(max_tiles(n, E)), o_nt = L.take<int32_t>(1), o_prow = L.take<float>(n);
+    char* ws = nullptr;
+    TRY(get_workspace(L.off, &ws));
+    _Float16* hq = (_Float16*)(ws + o_hq);
+    float* hu = (float*)(ws + o_hu);
+    float* prow = (float*)(ws + o_prow);
+    HIP_TRY(launch_i8_to_f16(qh, n * I, hq, st), "convert launch");
+    HIP_TRY(launch_block_correction(qh, sh, n, I, hu, st), "correction launch");
+    HIP_TRY(launch_tiles_from_offsets(offsets, E, (Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), st), "tiles launch");
+    HIP_TRY(launch_row_weights(slot, p, n, prow, st), "weights launch");
+    HIP_TRY(launch_fill_zero(out, T * H, st), "fill launch");
+    HIP_TRY(launch_down((const uint8_t*)experts->down, experts->down_stride, (Tile*)(ws + o_tiles),
+                        (int32_t*)(ws + o_nt), max_tiles(n, E), src, prow, hq, sh, hu, H, I, out, st),
+            "down launch");
+    return 0;
+}
+
+int strata_moe_timing(int enable, int32_t max_calls) {
+    g_err.clear();
+    std::lock_guard<std::mutex> lock(g_tm_mu);
+    for (hipEvent_t e : g_tm.ev) hipEventDestroy(e);
+    g_tm = Timing();
+    if (!enable) return 0;
+    if (max_calls < 1 || max_calls > 100000) return fail(STRATA_MOE_EINVAL, "max_calls %d", max_calls);
+    g_tm.ev.resize((size_t)max_calls * kNumKinds * 2);
+    for (auto& e : g_tm.ev) HIP_TRY(hipEventCreate(&e), "hipEventCreate");
+    g_tm.recorded.assign((size_t)max_calls * kNumKinds, 0);
+    g_tm.max_calls = max_calls;
+    g_tm.on = true;
+    return 0;
+}
+
+int strata_moe_timing_kinds(void) { return kNumKinds; }
+
+const char* strata_moe_timing_name(int id) { return id >= 0 && id < kNumKinds ? kKindNames[id] : ""; }
+
+int strata_moe_timing_read(double* total_ms, int32_t* launches, int n) {
+    g_err.clear();
+    if (!total_ms || !launches || n < kNumKinds) return fail(STRATA_MOE_EINVAL, "need arrays of %d", kNumKinds);
+    std::lock_guard<std::mutex> lock(g_tm_mu);
+    for (int k = 0; k < kNumKinds; ++k) total_ms[k] = 0.0, launches[k] = 0;
+    for (int c = 0; c < g_tm.used; ++c)
+        for (int k = 0; k < kNumKinds; ++k) {
+            if (!g_tm.recorded[(size_t)c * kNumKinds + k]) continue;
+            hipEvent_t a = g_tm.ev[((size_t)c * kNumKinds + k) * 2], b = g_tm.ev[((size_t)c * kNumKinds + k) * 2 + 1];
+            HIP_TRY(hipEventSynchronize(b), "hipEventSynchronize");
+            float ms = 0.f;
+            HIP_TRY(hipEventElapsedTime(&ms, a, b), "hipEventElapsedTime");
+            total_ms[k] += ms;
+            launches[k] += 1;
+        }
+    return 0;
+}
+
+}  // extern "C"

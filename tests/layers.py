@@ -1,0 +1,74 @@
+"""Test helpers: seeded layers on the GPU and oracle references, cached per
+session (the four full-size layers share one set of 512 experts)."""
+from __future__ import annotations
+
+import numpy as np
+
+import synthetic as S
+
+_expert_cache: dict = {}
+_gpu_experts: dict = {}
+
+
+def canonical_expert(s: S.LayerShape, e: int, seed: int = 0):
+    key = (s.H, s.I, seed, e)
+    ex = _expert_cache.get(key)
+    if ex is None:
+        ex = S.expert(s, e, seed)
+        _expert_cache[key] = ex
+    return ex
+
+
+def getter(s: S.LayerShape, seed: int = 0):
+    return lambda e: canonical_expert(s, e, seed)
+
+
+def gpu_experts(s: S.LayerShape, seed: int = 0, chunk: int = 32):
+    """Packed experts of the layer on cuda, with the layer's router bias."""
+    import torch
+
+    import quantized_routed_expert_logits_amd as qm
+
+    key = (s.E, s.H, s.I, seed)
+    base = _gpu_experts.get(key)
+    if base is None:
+        base = qm.Experts(s.E, s.H, s.I, device="cuda")
+        for e0 in range(0, s.E, chunk):
+            e1 = min(s.E, e0 + chunk)
+            parts = [canonical_expert(s, e, seed) for e in range(e0, e1)]
+            base.pack(e0, np.stack([p.codes_gu for p in parts]), np.stack([p.scales_gu for p in parts]),
+                      np.stack([p.codes_d for p in parts]), np.stack([p.scales_d for p in parts]))
+        torch.cuda.synchronize()
+        _gpu_experts[key] = base
+    bias = S.router_bias(s, seed)
+    return base.with_router_bias(None if bias is None else torch.from_numpy(bias).cuda())
+
+
+def check_h_codes(q_gpu, s_gpu, h_ref, q_ref, s_ref, tie_tol=2e-3):
+    """SwiGLU-output codes: the GPU rounds its fp32 h, the oracle RN32 of an
+    exact h, so a code may differ only where the oracle's quotient is within
+    tie_tol of a rounding boundary, and then by one.  Returns the mismatch
+    rate."""
+    q_gpu = np.asarray(q_gpu, np.int32)
+    q_ref = np.asarray(q_ref, np.int32)
+    s_gpu = np.asarray(s_gpu, np.float64)
+    s_ref = np.asarray(s_ref, np.float64)
+    nz = s_ref > 0
+    assert np.all(s_gpu[~nz] == 0)
+    rel = np.abs(s_gpu[nz] / s_ref[nz] - 1.0)
+    assert rel.max(initial=0.0) <= 1e-5, f"H scales differ by {rel.max():.2e}"
+    diff = q_gpu != q_ref
+    if diff.any():
+        rows, cols = np.nonzero(diff)
+        sr = np.repeat(s_ref, 32, axis=1)[rows, cols]
+        t = np.abs(h_ref[rows, cols]) / sr
+        frac = t - np.floor(t)
+        assert np.all(np.abs(frac - 0.5) < tie_tol), "an H code differs away from a rounding tie"
+        assert np.all(np.abs(q_gpu[rows, cols] - q_ref[rows, cols]) == 1)
+    return diff.mean()
+
+
+def rel_err(y, ref) -> float:
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.abs(y - ref).max() / max(np.abs(ref).max(), 1e-300))

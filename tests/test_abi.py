@@ -1,0 +1,121 @@
+"""The C ABI boundary without a GPU: the library loads, exports every entry
+point include/strata_moe.h declares, sizes its buffers, and rejects bad
+arguments on the host before anything would be enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "strata_moe.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(strata_moe_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def qm():
+    import quantized_routed_expert_logits_amd as qm
+    return qm
+
+
+def test_header_declares_the_layer_entry_points():
+    names = _declared()
+    for n in ("strata_moe_prefill", "strata_moe_route", "strata_moe_group", "strata_moe_quantize",
+              "strata_moe_gate_up", "strata_moe_down", "strata_moe_pack", "strata_moe_workspace_bytes"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(qm):
+    lib = ctypes.CDLL(qm.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert sorted(qm.EXPORTED) == _declared()
+
+
+def test_packed_sizes_are_two_bits_plus_fp16_scales(qm):
+    gu, dn = qm.strata_moe_packed_bytes(2560, 1024)
+    # 2 bits per weight + one fp16 per 32 weights, rounded up to 256 bytes
+    assert gu == 2 * 1024 * 2560 * (2 / 8 + 2 / 32)
+    assert dn == 2560 * 1024 * (2 / 8 + 2 / 32)
+    assert gu + dn == 3 * 2560 * 1024 * 10 // 32  # 2.4576 MB per expert
+    with pytest.raises(qm.StrataMoeError) as ei:
+        qm.strata_moe_packed_bytes(2560, 1000)
+    assert ei.value.code == qm.EINVAL
+
+
+def _experts_struct(qm, E=512, H=2560, I=1024, fmt=1):
+    try:
+        gu, dn = qm.strata_moe_packed_bytes(H, I)
+    except qm.StrataMoeError:
+        gu = dn = 1 << 24
+    return qm.ExpertsStruct(E, H, I, fmt, 1 << 20, gu, 1 << 30, dn, None)
+
+
+def test_workspace_bytes_scale_with_tokens(qm):
+    st = _experts_struct(qm)
+    b = ctypes.c_size_t()
+    lib = qm.library()
+    assert lib.strata_moe_workspace_bytes(8192, 10, ctypes.byref(st), ctypes.byref(b)) == 0
+    small = b.value
+    assert lib.strata_moe_workspace_bytes(32768, 10, ctypes.byref(st), ctypes.byref(b)) == 0
+    assert b.value > 3.5 * small
+    # H codes as fp16 (n*I*2) dominate: at least that much
+    assert small >= 8192 * 10 * 1024 * 2
+
+
+@pytest.mark.parametrize("K,T,fmt,H,I,E,code", [
+    (0, 8, 1, 2560, 1024, 512, -1),      # K < 1
+    (17, 8, 1, 2560, 1024, 512, -1),     # K > 16
+    (10, -1, 1, 2560, 1024, 512, -1),    # negative T
+    (10, 8, 7, 2560, 1024, 512, -2),     # unknown format
+    (10, 8, 1, 2600, 1024, 512, -1),     # H not a multiple of 64
+    (10, 8, 1, 2560, 1000, 512, -1),     # I not a multiple of 32
+    (10, 8, 1, 2560, 1024, 2048, -1),    # too many experts
+    (4, 8, 1, 256, 128, 3, -1),          # K > E
+])
+def test_prefill_rejects_bad_arguments_on_the_host(qm, K, T, fmt, H, I, E, code):
+    st = _experts_struct(qm, E=E, H=H, I=I, fmt=fmt)
+    lib = qm.library()
+    rc = lib.strata_moe_prefill(ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.byref(st), T, K,
+                                ctypes.c_void_p(16), None)
+    assert rc == code
+    assert qm.strata_moe_last_error() != ""
+
+
+def test_prefill_rejects_short_strides_and_null(qm):
+    lib = qm.library()
+    st = _experts_struct(qm)
+    st.gate_up_stride -= 256
+    assert lib.strata_moe_prefill(ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.byref(st), 8, 10,
+                                  ctypes.c_void_p(16), None) == qm.EINVAL
+    assert lib.strata_moe_prefill(ctypes.c_void_p(16), ctypes.c_void_p(16), None, 8, 10,
+                                  ctypes.c_void_p(16), None) == qm.EINVAL
+
+
+def test_zero_tokens_is_a_no_op(qm):
+    lib = qm.library()
+    st = _experts_struct(qm)
+    assert lib.strata_moe_prefill(None, None, ctypes.byref(st), 0, 10, None, None) == 0
+
+
+def test_debug_entry_points_validate_sizes(qm):
+    lib = qm.library()
+    assert lib.strata_moe_quantize(ctypes.c_void_p(16), 4, 48, ctypes.c_void_p(16), ctypes.c_void_p(16), None) \
+        == qm.EINVAL
+    assert lib.strata_moe_route(ctypes.c_void_p(16), ctypes.c_void_p(16), None, 4, 2560, 2000, 10,
+                                ctypes.c_void_p(16), ctypes.c_void_p(16), None) == qm.EINVAL
+    assert lib.strata_moe_group(ctypes.c_void_p(16), 4, 12, 8, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                ctypes.c_void_p(16), None) == qm.EINVAL
+
+
+def test_timing_names(qm):
+    lib = qm.library()
+    n = lib.strata_moe_timing_kinds()
+    names = [lib.strata_moe_timing_name(i).decode() for i in range(n)]
+    assert "gate_up" in names and "down" in names

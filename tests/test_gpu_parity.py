@@ -1,0 +1,244 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bars: routing ids, grouping tables and the layer input's int8 codes and
+scales bit-exact; routing weights within 2e-5 absolute (fp32 logits: about
+4e-6 of logit error, far below); SwiGLU-output codes equal except at rounding
+ties of the oracle's exact quotient (then off by one); the layer output within
+max|err| / max|ref| <= 2e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic as S
+from layers import canonical_expert, check_h_codes, getter, gpu_experts, rel_err
+
+pytestmark = pytest.mark.gpu
+
+P_TOL = 2e-5
+Y_TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def qm():
+    import quantized_routed_expert_logits_amd as qm
+
+    assert qm.strata_moe_device_supported(), "this test needs a gfx950 device"
+    return qm
+
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+# ----------------------------------------------------------------- quantize
+def test_quantize_bit_exact(qm):
+    rng = np.random.default_rng(7)
+    v = (rng.standard_normal((700, 320)) * rng.choice([1e-6, 1e-2, 1.0, 300.0], (700, 1))).astype(np.float32)
+    v[0, :32] = 0.0                                     # all-zero block
+    v[1, :32] = np.float32(np.arange(32) - 15.5)        # half-way quotients with s == 1
+    v[1, 0] = 127.0
+    v[2, 32:64] = -2.75                                 # constant block
+    v[3, :32] = np.float32(1e-40)                       # subnormal block
+    q, s = qm.strata_moe_quantize(_t(v))
+    qr, sr = oracle.quantize(v)
+    assert np.array_equal(s.cpu().numpy(), sr)
+    assert np.array_equal(q.cpu().numpy(), qr)
+
+
+def test_quantize_full_size_input_bit_exact(qm):
+    x = S.activations(S.shape("chunk_8k"))
+    q, s = qm.strata_moe_quantize(_t(x))
+    qr, sr = oracle.quantize(x)
+    assert np.array_equal(s.cpu().numpy(), sr) and np.array_equal(q.cpu().numpy(), qr)
+
+
+# --------------------------------------------------------------------- pack
+@pytest.mark.parametrize("shape", [S.shape("tiny"), S.custom(T=1, H=192, E=3, K=1, I=96)])
+def test_pack_unpack_round_trip(qm, shape):
+    ex = gpu_experts(shape)
+    cg, sg, cd, sd = qm.strata_moe_unpack(ex, 0, shape.E)
+    for e in range(shape.E):
+        c = canonical_expert(shape, e)
+        assert np.array_equal(cg[e].cpu().numpy(), c.codes_gu)
+        assert np.array_equal(sg[e].cpu().numpy().view(np.uint16), c.scales_gu)
+        assert np.array_equal(cd[e].cpu().numpy(), c.codes_d)
+        assert np.array_equal(sd[e].cpu().numpy().view(np.uint16), c.scales_d)
+
+
+# -------------------------------------------------------------------- route
+def _route_case(qm, x, wr, bias, K):
+    ids, p = qm.strata_moe_route(_t(x), _t(wr), None if bias is None else _t(bias), K)
+    ids_r, p_r = oracle.topk_softmax(oracle.router_logits(x, wr, bias), K)
+    ids, p = ids.cpu().numpy(), p.cpu().numpy()
+    assert np.array_equal(ids, ids_r)
+    assert np.abs(p - p_r).max() <= P_TOL
+    assert np.abs(p.astype(np.float64).sum(1) - 1).max() <= 1e-6
+
+
+@pytest.mark.parametrize("name", ["tiny", "stream_all_1k", "skewed_4k"])
+def test_route_matches_oracle(qm, name):
+    s = S.shape(name)
+    _route_case(qm, S.activations(s), S.router_weight(s), S.router_bias(s), s.K)
+
+
+def test_route_exact_ties_and_zero_router(qm):
+    s = S.custom(T=300, H=512, E=40, K=7, I=32)
+    x, wr = S.activations(s, 3), S.router_weight(s, 3)
+    wr[:, 11] = wr[:, 4]            # exact ties: lower index first
+    wr[:, 30] = wr[:, 29]
+    _route_case(qm, x, wr, None, s.K)
+    _route_case(qm, x, np.zeros_like(wr), None, s.K)   # all equal: 0..K-1, p = 1/K
+
+
+def test_route_near_ties_are_settled_exactly(qm):
+    """Columns that differ by one fp32 ulp in a single entry: logits a few
+    1e-7 apart, below fp32 accumulation noise."""
+    s = S.custom(T=512, H=1024, E=64, K=10, I=32)
+    x, wr = S.activations(s, 4), S.router_weight(s, 4)
+    for a, b in [(3, 17), (40, 41), (9, 60)]:
+        wr[:, b] = wr[:, a]
+        wr[5, b] = np.nextafter(wr[5, a], np.float32(np.inf))
+    _route_case(qm, x, wr, None, s.K)
+
+
+@pytest.mark.parametrize("name", ["chunk_8k", "long_32k"])
+def test_route_full_size_sampled(qm, name):
+    s = S.shape(name)
+    x, wr = S.activations(s), S.router_weight(s)
+    ids, p = qm.strata_moe_route(_t(x), _t(wr), None, s.K)
+    rng = np.random.default_rng(11)
+    tok = np.unique(np.concatenate([[0, s.T - 1], rng.choice(s.T, 1022, replace=False)]))
+    ids_r, p_r = oracle.topk_softmax(oracle.router_logits(x[tok], wr), s.K)
+    assert np.array_equal(ids.cpu().numpy()[tok], ids_r)
+    assert np.abs(p.cpu().numpy()[tok] - p_r).max() <= P_TOL
+
+
+# -------------------------------------------------------------------- group
+@pytest.mark.parametrize("T,E,K,skew", [(64, 16, 2, 0.0), (3000, 512, 10, 0.0), (4096, 512, 10, 3.0),
+                                        (32768, 512, 10, 0.0), (257, 1024, 16, 0.0), (9, 1, 1, 0.0)])
+def test_group_bit_exact(qm, T, E, K, skew):
+    rng = np.random.default_rng(T + E)
+    logits = rng.standard_normal((T, E)) - skew * np.log1p(np.arange(E))[None, :]
+    ids, _ = oracle.topk_softmax(logits, K)
+    offsets, src, slot = qm.strata_moe_group(_t(ids), E)
+    o_r, s_r, sl_r = oracle.group(ids, E)
+    assert np.array_equal(offsets.cpu().numpy(), o_r)
+    assert np.array_equal(src.cpu().numpy(), s_r)
+    assert np.array_equal(slot.cpu().numpy(), sl_r)
+
+
+def test_group_rejects_out_of_range_ids(qm):
+    ids = np.zeros((100, 4), np.int32)
+    ids[:, 1], ids[:, 2], ids[:, 3] = 1, 2, 3
+    ids[57, 2] = 16
+    with pytest.raises(qm.StrataMoeError) as ei:
+        qm.strata_moe_group(_t(ids), 16)
+    assert ei.value.code == qm.EDATA
+
+
+# ------------------------------------------------------------ expert stages
+def _stage_ref(s):
+    x, wr = S.activations(s), S.router_weight(s)
+    return x, wr, oracle.layer(x, wr, S.router_bias(s), getter(s), s.E, s.K, want_h=True)
+
+
+STAGE_SHAPES = [S.shape("tiny"), S.custom(T=300, H=256, E=12, K=3, I=96), S.custom(T=70, H=640, E=5, K=2, I=160)]
+
+
+@pytest.mark.parametrize("s", STAGE_SHAPES, ids=lambda s: s.name)
+def test_gate_up_stage(qm, s):
+    x, wr, ref = _stage_ref(s)
+    ex = gpu_experts(s)
+    qh, sh = qm.strata_moe_gate_up(_t(ref["qx"]), _t(ref["sx"]), _t(ref["offsets"]), _t(ref["src"]), s.K, ex)
+    rate = check_h_codes(qh.cpu().numpy(), sh.cpu().numpy(), ref["h"], ref["qh"], ref["sh"])
+    assert rate < 1e-3
+
+
+@pytest.mark.parametrize("s", STAGE_SHAPES, ids=lambda s: s.name)
+def test_down_stage(qm, s):
+    x, wr, ref = _stage_ref(s)
+    ex = gpu_experts(s)
+    out = torch.empty((s.T, s.H), dtype=torch.float32, device="cuda")
+    qm.strata_moe_down(_t(ref["qh"]), _t(ref["sh"]), _t(ref["offsets"]), _t(ref["src"]), _t(ref["slot"]),
+                       _t(ref["p"].astype(np.float32)), ex, out)
+    assert rel_err(out.cpu().numpy(), ref["y"]) <= 1e-5
+
+
+# --------------------------------------------------------------- the layer
+LAYER_SHAPES = STAGE_SHAPES + [S.custom(T=129, H=256, E=8, K=4, I=64, skewed=True)]
+
+
+@pytest.mark.parametrize("s", LAYER_SHAPES, ids=lambda s: s.name)
+def test_layer_all_intermediates(qm, s):
+    x, wr, ref = _stage_ref(s)
+    ex = gpu_experts(s)
+    out = torch.empty((s.T, s.H), dtype=torch.float32, device="cuda")
+    d = qm.strata_moe_prefill_debug(_t(x), _t(wr), ex, s.K, out)
+    g = {k: v.cpu().numpy() for k, v in d.items()}
+    for k in ("ids", "offsets", "src", "slot", "qx", "sx"):
+        assert np.array_equal(g[k], ref[k]), k
+    assert np.abs(g["p"] - ref["p"]).max() <= P_TOL
+    check_h_codes(g["qh"], g["sh"], ref["h"], ref["qh"], ref["sh"])
+    assert rel_err(g["out"], ref["y"]) <= Y_TOL
+
+
+def test_layer_zero_input_and_repeat(qm):
+    s = S.shape("tiny")
+    ex = gpu_experts(s)
+    wr = _t(S.router_weight(s))
+    out = torch.full((s.T, s.H), 7.0, device="cuda")
+    qm.strata_moe_prefill(torch.zeros((s.T, s.H), device="cuda"), wr, ex, s.K, out)
+    assert torch.count_nonzero(out).item() == 0
+    x = _t(S.activations(s))
+    a = qm.strata_moe_prefill(x, wr, ex, s.K, torch.empty_like(x)).clone()
+    b = qm.strata_moe_prefill(x, wr, ex, s.K, torch.empty_like(x))
+    assert rel_err(b.cpu().numpy(), a.cpu().numpy()) <= 1e-6
+
+
+def test_layer_zero_tokens(qm):
+    s = S.shape("tiny")
+    ex = gpu_experts(s)
+    x = torch.empty((0, s.H), device="cuda")
+    qm.strata_moe_prefill(x, _t(S.router_weight(s)), ex, s.K, torch.empty_like(x))
+
+
+# ------------------------------------------------- full-size layers, sampled
+def _check_grouping_props(g, T, K, E):
+    offsets, src, slot, ids = g["offsets"], g["src"], g["slot"], g["ids"].reshape(-1)
+    n = T * K
+    assert offsets[0] == 0 and offsets[E] == n and np.all(np.diff(offsets) >= 0)
+    assert np.array_equal(np.diff(offsets), np.bincount(ids, minlength=E))
+    assert np.array_equal(np.bincount(src, minlength=T), np.full(T, K))
+    assert np.array_equal(np.sort(slot), np.arange(n))
+    assert np.array_equal(src[slot], np.arange(n) // K)
+    grp = np.repeat(np.arange(E), np.diff(offsets))
+    assert np.array_equal(grp[slot], ids)
+    inner = np.diff(src)[np.diff(grp) == 0]
+    assert np.all(inner > 0)  # ascending tokens within each expert
+
+
+@pytest.mark.parametrize("name", ["stream_all_1k", "chunk_8k", "skewed_4k", "long_32k"])
+def test_full_layer_sampled(qm, name):
+    s = S.shape(name)
+    ex = gpu_experts(s)
+    x, wr, bias = S.activations(s), S.router_weight(s), S.router_bias(s)
+    xt, wt = _t(x), _t(wr)
+    out = torch.empty_like(xt)
+    qm.strata_moe_prefill(xt, wt, ex, s.K, out)          # the launch the benchmark times
+    y = out.cpu().numpy()
+    d = qm.strata_moe_prefill_debug(xt, wt, ex, s.K, torch.empty_like(xt))
+    g = {k: v.cpu().numpy() for k, v in d.items() if k in ("ids", "offsets", "src", "slot", "qx")}
+    _check_grouping_props(g, s.T, s.K, s.E)
+    rng = np.random.default_rng(5)
+    tok = [0, s.T - 1] + list(rng.choice(s.T, 30, replace=False))
+    if s.skewed:  # tokens of the busiest expert (its tiles run last in their group)
+        busiest = int(np.argmax(np.diff(g["offsets"])))
+        rows = g["src"][g["offsets"][busiest]:g["offsets"][busiest + 1]]
+        tok += list(rows[-8:])
+    tok = np.unique(tok)
+    ref = oracle.layer_tokens(x, wr, bias, getter(s), s.K, tok)
+    assert np.array_equal(g["ids"][tok], ref["ids"])
+    assert np.array_equal(g["qx"][tok], ref["qx"])
+    assert rel_err(y[tok], ref["y"]) <= Y_TOL
