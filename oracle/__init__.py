@@ -59,6 +59,7 @@ def _load():
     lib.oracle_quantize.argtypes = [P, i64, i32, P, P]
     lib.oracle_expert_rows.argtypes = [P, P, P, P, i32, i32, i64, P, P, P, P, P, P]
     lib.oracle_combine.argtypes = [P, P, P, i64, i32, i32, P]
+    lib.oracle_rows_multi.argtypes = [P, P, P, P, P, i32, i32, i64, P, P, P, P, P]
     lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_half_to_double.restype = ctypes.c_double
     lib.oracle_num_threads.restype = ctypes.c_int
@@ -198,6 +199,27 @@ def layer(x, wr, bias, get_expert, E: int, K: int, want_h: bool = False) -> dict
                 qh=qh, sh=sh, h=h, D=D, y=y)
 
 
+def rows_multi(experts: list, which, qx, sx):
+    """c5..c7 for rows of several experts: row r goes through experts[which[r]].
+    Returns (qh, sh, D)."""
+    keep = [(_c(e.codes_gu, np.uint8), _c(e.scales_gu, np.uint16), _c(e.codes_d, np.uint8),
+             _c(e.scales_d, np.uint16)) for e in experts]
+    H = keep[0][0].shape[1]
+    I = keep[0][0].shape[0] // 2
+    tables = [(ctypes.c_void_p * len(keep))(*[k[j].ctypes.data for k in keep]) for j in range(4)]
+    which = _c(which, np.int32)
+    qx = _c(qx, np.int8).reshape(-1, H)
+    sx = _c(sx, np.float32).reshape(-1, H // BLOCK)
+    n = qx.shape[0]
+    qh = np.empty((n, I), np.int8)
+    sh = np.empty((n, I // BLOCK), np.float32)
+    D = np.empty((n, H), np.float64)
+    if n:
+        _load().oracle_rows_multi(tables[0], tables[1], tables[2], tables[3], _p(which), H, I, n, _p(qx), _p(sx),
+                                  _p(qh), _p(sh), _p(D))
+    return qh, sh, D
+
+
 def layer_tokens(x, wr, bias, get_expert, K: int, tokens) -> dict:
     """The layer's output for a sample of tokens only.
 
@@ -213,22 +235,16 @@ def layer_tokens(x, wr, bias, get_expert, K: int, tokens) -> dict:
     qx, sx = quantize(xs)
     S = len(tokens)
     H = x.shape[1]
-    by_expert: dict[int, list[tuple[int, int]]] = {}
-    for s in range(S):
-        for k in range(K):
-            by_expert.setdefault(int(ids[s, k]), []).append((s, k))
-    I = None
-    D = np.zeros((S, K, H), np.float64)
-    qh = sh = None
-    for e, pairs in sorted(by_expert.items()):
-        rows = np.array([s for s, _ in pairs])
-        _, qhe, she, De = expert_rows(get_expert(e), qx[rows], sx[rows])
-        if I is None:
-            I = qhe.shape[1]
-            qh = np.zeros((S, K, I), np.int8)
-            sh = np.zeros((S, K, I // BLOCK), np.float32)
-        for j, (s, k) in enumerate(pairs):
-            D[s, k], qh[s, k], sh[s, k] = De[j], qhe[j], she[j]
+    used = sorted(set(int(e) for e in ids.reshape(-1)))
+    slot_of = {e: i for i, e in enumerate(used)}
+    which = np.array([slot_of[int(e)] for e in ids.reshape(-1)], np.int32)
+    # pairs token-major: row s*K + k is token s through its k-th expert
+    rows = np.repeat(np.arange(S), K)
+    qh, sh, D = rows_multi([get_expert(e) for e in used], which, qx[rows], sx[rows])
+    I = qh.shape[1]
     # c8 with the pairs laid out token-major: row s*K + k holds D of (s, k)
-    y = combine(D.reshape(S * K, H), p, np.arange(S * K, dtype=np.int32))
+    y = combine(D, p, np.arange(S * K, dtype=np.int32))
+    D = D.reshape(S, K, H)
+    qh = qh.reshape(S, K, I)
+    sh = sh.reshape(S, K, I // BLOCK)
     return dict(tokens=tokens, logits=logits, ids=ids, p=p, qx=qx, sx=sx, qh=qh, sh=sh, D=D, y=y)

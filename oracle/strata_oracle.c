@@ -268,6 +268,20 @@ void oracle_expert_rows(const uint8_t* cgu, const uint16_t* sgu, const uint8_t* 
     }
 }
 
+/* Rows of several experts at once: row r uses expert slot which[r] of the
+ * pointer tables (the same per-row computation as oracle_expert_rows, with
+ * the loop over rows spread across threads). */
+void oracle_rows_multi(const uint8_t* const* cgu, const uint16_t* const* sgu, const uint8_t* const* cd,
+                       const uint16_t* const* sd, const int32_t* which, int32_t H, int32_t I, int64_t nrows,
+                       const int8_t* qx, const float* sx, int8_t* qh_out, float* sh_out, double* D) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int32_t w = which[r];
+        oracle_expert_rows(cgu[w], sgu[w], cd[w], sd[w], H, I, 1, qx + r * H, sx + r * (H / QBLOCK), NULL,
+                           qh_out ? qh_out + r * I : NULL, sh_out ? sh_out + r * (I / QBLOCK) : NULL, D + r * H);
+    }
+}
+
 /* ------------------------------------------------------------- c8 combine
  * [moe_fused] the combine reads the per-slot rows: y[t] = sum_k p[t][k] *
  * D[slot[t*K + k]], k ascending, in double.  The shared expert that the pages
