@@ -27,8 +27,9 @@
  *   - Arguments are validated on the host before anything is enqueued.  A
  *     non-zero return means nothing (or, for STRATA_MOE_EHIP, not all) of the
  *     work was enqueued; strata_moe_last_error() then describes why.
- *   - Sizes: H and I multiples of 64 and 32 respectively (H >= 64, I >= 32),
- *     1 <= K <= 16, K <= E <= 1024, T * K < 2^31.  T = 0 is a no-op.
+ *   - Sizes: H a multiple of 128 and I a multiple of 64, both at most 4096;
+ *     1 <= K <= 16, K <= E <= 1024, T * K < 2^31.  T = 0 is a no-op.  (The
+ *     single-step route entry point only needs H a multiple of 64.)
  *   - Thread safety: calls may come from several host threads; calls that
  *     share the library-owned workspace of one device (the default when no
  *     workspace was set) must not overlap on different streams.
@@ -137,8 +138,9 @@ int strata_moe_unpack(const void* gate_up, int64_t gate_up_stride, const void* d
  *   x        [T][H] fp32 layer input (row-major)
  *   router_w [H][E] fp32 router matrix (column e is expert e's router vector)
  *   out      [T][H] fp32, overwritten with y[t] = sum_k p[t][k] * down_e(...)
- * Output rows are accumulated with fp32 atomic adds (the weighted
- * scatter-add combine), so the last bits may differ between runs. */
+ * The down GEMM writes each routed row's weighted output to its grouped row;
+ * the combine adds a token's K rows in k order, so results are bitwise
+ * reproducible from run to run. */
 int strata_moe_prefill(const float* x, const float* router_w, const strata_moe_experts* experts, int64_t T,
                        int32_t K, float* out, void* stream);
 

@@ -9,6 +9,8 @@ shared library next to this file.  Flags:
   -fhip-fp32-correctly-rounded-divide-sqrt
                                  IEEE fp32 division (the int8 rounding of the
                                  activations depends on it)
+  -mllvm -amdgpu-mfma-vgpr-form  MFMA results in VGPRs: the block loop reads
+                                 every result with VALU FMAs
 """
 from __future__ import annotations
 
@@ -29,6 +31,7 @@ FLAGS = [
     "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-Wno-unused-function",
 ]

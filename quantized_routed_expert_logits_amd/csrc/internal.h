@@ -8,25 +8,26 @@
 namespace strata_moe {
 
 constexpr int kBlock = 32;        // values per quantization block (both activations and weights)
-constexpr int kTileRows = 64;     // routed rows per GEMM tile (the pages' kTileRows, moe_fused.hpp)
+constexpr int kChunkRows = 192;   // grouped rows per GEMM work item (12 tiles of 16 rows)
 constexpr int kGroupChunk = 2048; // (token, k) pairs per grouping chunk
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
-constexpr int kSliceRows = 64;    // weight rows per wave slice of a packed matrix (4 MFMA fragments of 16)
+constexpr int kSlabRows = 128;    // weight rows per GEMM work item (8 MFMA fragments of 16)
+constexpr int kRecordCodeBytes = 1024;                    // one slab's codes of one 32-wide block
+constexpr int kRecordBytes = kRecordCodeBytes + 256;      // ... plus its 128 fp16 scales
+constexpr int kMaxOffsetChunks = 4;                       // reduction length <= 4 * 32 blocks = 4096
 
-// One tile of grouped rows: rows [row0, row0 + nrows) all belong to expert e.
+// One chunk of grouped rows: rows [row0, row0 + nrows) all belong to expert e.
 struct Tile {
     int32_t e, row0, nrows, pad;
 };
 
-// Packed blob geometry of an M x Kd matrix (M rows, reduction over Kd):
-//   codes  [M/64 slices][Kd/32 blocks][64 lanes][2 x u32]       (2 bits per weight)
-//   scales [M/64 slices][Kd/32 blocks][16 rows][4 fragments] fp16
+// Packed blob bytes of an M x Kd matrix (2 bits per weight + one fp16 per 32).
 inline int64_t packed_matrix_bytes(int64_t M, int64_t Kd) { return M * Kd / 4 + M * Kd / 16; }
 inline int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
-// Upper bound of the tile count of n grouped rows over E experts.
-inline int64_t max_tiles(int64_t n, int32_t E) { return n / kTileRows + E; }
+// Upper bound of the chunk count of n grouped rows over E experts.
+inline int64_t max_tiles(int64_t n, int32_t E) { return n / kChunkRows + E; }
 
 // ---- launchers; each returns hipGetLastError() after its launches.
 hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, _Float16* q16, int8_t* q8, float* s,
@@ -56,7 +57,9 @@ hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const Tile* tile
                           hipStream_t st);
 hipError_t launch_down(const uint8_t* blobs, int64_t stride, const Tile* tiles, const int32_t* ntiles,
                        int64_t tiles_cap, const int32_t* src, const float* prow, const _Float16* hq,
-                       const float* hs, const float* hu, int32_t H, int32_t I, float* y, hipStream_t st);
+                       const float* hs, const float* hu, int32_t H, int32_t I, float* dm, hipStream_t st);
+hipError_t launch_combine(const float* dm, const int32_t* slot, int64_t T, int32_t K, int32_t H, float* y,
+                          hipStream_t st);
 
 hipError_t launch_pack(const uint8_t* codes, const uint16_t* scales, int32_t nexp, int32_t M, int32_t Kd,
                        int32_t gate_up_I, uint8_t* dst, int64_t stride, hipStream_t st);

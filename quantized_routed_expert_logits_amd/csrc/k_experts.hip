@@ -1,34 +1,42 @@
 // Grouped expert GEMMs: gate/up with SwiGLU and the int8 rounding of H fused
-// in the epilogue, and down with the weighted scatter-add combine fused in its
-// epilogue.
+// in the epilogue; down with the routing weight applied in its epilogue,
+// writing each routed row's output to its grouped row; and the combine that
+// adds a token's K rows.
 //
 // Strata compare v0.1.35...v0.1.37 page, include/strata/prefill/moe_fused.hpp,
 // experts: per expert, gate/up on the int8 activations of its grouped rows
 // (through src), SwiGLU, H rounded to int8 per 32 values in the epilogue, then
 // down into the rows the combine reads; each expert is read where it is (no
-// gather), in 64-row tiles; the 2-bit codes are unpacked in registers.
+// gather); the 2-bit codes are unpacked on chip.
 //
 // Arithmetic.  One weight block is 32 codes q of one row with one fp16 scale
 // d, w = d * (q - 1.5); one activation block is 32 int8 codes a with an fp32
 // scale s.  Their contribution to an output is
-//     s * d * sum(q - 1.5) * a = s * [d * sum (q - 1) * a] + d * u,
-//     u = -0.5 * s * sum(a)  (computed once per activation block).
+//     s * d * sum (q - 1.5) * a = s * [d * sum (q - 1) * a] + d * u,
+//     u = -0.5 * s * sum(a)  (one value per activation block).
 // The bracket is one v_mfma_f32_16x16x32_f16 (K = 32 = one block): the A
 // operand d*(q-1) is exact in fp16 (q - 1 in {-1, 0, 1, 2}), the B operand
 // holds the integer codes (exact in fp16), products are exact and every
-// partial sum is a multiple of d's last place below 2^24 of them, so the fp32
-// result is exact.  The per-block scale s then needs one fp32 FMA per output
-// (s differs per token and per block, so it cannot enter the MFMA exactly);
-// the offset term d*u a second one.
+// partial sum is an integer multiple of d's last place below 2^24 of them, so
+// the fp32 result is exact.  s differs per routed row and block, so it cannot
+// enter the MFMA exactly: one fp32 FMA per output per block applies it.  The
+// d*u terms of all blocks form a small matrix product over the block index
+// (K = Kd/32), done after the block loop on the MFMA unit: A = d (exact in
+// fp16), B = u of each row scaled by a power of two to [-1, 1] and split into
+// a high and a low fp16 part (22 bits).
 //
-// Operand roles: A = weights (rows = weight rows, 16 per fragment), B =
-// activations (columns = routed rows).  Lane l of the 16x16 output holds
-// column l % 16 (one routed row) and rows 4*(l/16) + v, v = 0..3, so the
-// activation scale s and u are one value per lane per block.
+// Work split.  A workgroup (4 waves) takes one chunk of at most 256 grouped
+// rows of one expert and one 128-row weight slab (8 fragments of 16 rows).
+// Per 32-wide block each thread unpacks one dword of 16 codes into LDS, so the
+// slab's block is unpacked once and read by all 4 waves (double-buffered, one
+// barrier per block).  The chunk's rows form 16-row tiles; wave w owns tiles
+// w, w+4, w+8, w+12 and keeps their activation fragments in registers.  Lane
+// l of a 16x16 output holds routed row (column) l % 16 and weight rows
+// 4*(l/16) + v, v = 0..3, so a row's scale is one value per lane.
 //
-// Work split: a workgroup (4 waves) takes one 64-row tile of one expert
-// (its rows in the grouped order) and 4 consecutive weight slices of 64 rows;
-// each wave one slice: 4 fragments x 4 token tiles = 16 MFMAs per block.
+// Mapping.  Workgroups are dealt round-robin to the 8 XCDs; the id ->
+// (chunk, slab) map keeps every slab of a chunk on one XCD, so that chunk's
+// activation rows are fetched into one L2 only.
 #include "internal.h"
 
 namespace strata_moe {
@@ -41,16 +49,19 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
+constexpr int kFrags = kSlabRows / 16;                               // 8
+constexpr int kTilesPerWave = kChunkRows / (16 * kWaves);            // 3
+constexpr int kParkStride = kSlabRows + 4;                           // floats per parked output row
 
 __device__ __forceinline__ _Float16 lo_half(uint32_t w) { return __builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
 __device__ __forceinline__ _Float16 hi_half(uint32_t w) { return __builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
 // One packed dword (16 codes) -> two A fragments of 8 fp16 values d*(q-1).
 // Pair m (0..7) of the dword fills fragment m/4, elements 2(m%4) and
-// 2(m%4)+1; its codes sit at bits [2m, 2m+1] and [16+2m, 17+2m].  OR-ing the
+// 2(m%4)+1; its codes sit at bits [2m, 2m+1] and [16+2m, 17+2m].  OR-ing a
 // code into the mantissa of 1024.0 (0x6400) gives 1024 + q exactly; minus
 // 1025 gives q - 1; times d is exact.
-__device__ __forceinline__ void unpack_pair(uint32_t x, _Float16 d0, _Float16 d1, half8_t& a0, half8_t& a1) {
+__device__ __forceinline__ void unpack_dword(uint32_t x, _Float16 d0, _Float16 d1, half8_t& a0, half8_t& a1) {
 #pragma clang fp contract(off)
     const half2_t bias = {(_Float16)1025.0f, (_Float16)1025.0f};
     const half2_t s0 = {d0, d0}, s1 = {d1, d1};
@@ -68,188 +79,364 @@ __device__ __forceinline__ void unpack_pair(uint32_t x, _Float16 d0, _Float16 d1
     }
 }
 
-// The block loop shared by both GEMMs.  blob: one expert's packed matrix
-// (M rows, reduction Kd); slice: this wave's 64-row slice; act [rows][Kd]
-// fp16 integer codes with as/au [rows][Kd/32]; arow[tt]: the activation row
-// of this lane's column in token tile tt (-1: padding).
-__device__ __forceinline__ void block_loop(const uint8_t* __restrict__ blob, int32_t M, int32_t Kd, int slice,
-                                           int lane, const int64_t (&arow)[4], const _Float16* __restrict__ act,
-                                           const float* __restrict__ as, const float* __restrict__ au,
-                                           float4_t (&acc)[4][4]) {
-    const int nblk = Kd / kBlock;
-    const uint2* codes = reinterpret_cast<const uint2*>(blob) + (int64_t)slice * nblk * 64 + lane;
-    const uint16_t* scl = reinterpret_cast<const uint16_t*>(blob + (int64_t)M * Kd / 4) + (int64_t)slice * nblk * 64;
-    const int r16 = lane & 15, kg = lane >> 4;
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) acc[f][tt] = (float4_t){0.f, 0.f, 0.f, 0.f};
-    for (int b = 0; b < nblk; ++b) {
-        const uint2 c = codes[(int64_t)b * 64];
-        const uint16_t* sb = scl + (int64_t)b * 64;
-        const uint2 du = *reinterpret_cast<const uint2*>(sb + r16 * 4);
-        const uint4 dc0 = *reinterpret_cast<const uint4*>(sb + kg * 16);
-        const uint4 dc1 = *reinterpret_cast<const uint4*>(sb + kg * 16 + 8);
-        half8_t A[4];
-        unpack_pair(c.x, lo_half(du.x), hi_half(du.x), A[0], A[1]);
-        unpack_pair(c.y, lo_half(du.y), hi_half(du.y), A[2], A[3]);
-        // correction scales d of output rows 4*kg + v, fragment f: halves [v*4 + f]
-        const uint32_t dw[8] = {dc0.x, dc0.y, dc0.z, dc0.w, dc1.x, dc1.y, dc1.z, dc1.w};
-        float dcorr[4][4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-#pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                const uint32_t w = dw[(v * 4 + f) >> 1];
-                dcorr[f][v] = (float)(((v * 4 + f) & 1) ? hi_half(w) : lo_half(w));
-            }
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            half8_t B = {};
-            float s = 0.f, u = 0.f;
-            if (arow[tt] >= 0) {
-                B = *reinterpret_cast<const half8_t*>(act + arow[tt] * Kd + b * kBlock + kg * 8);
-                s = as[arow[tt] * nblk + b];
-                u = au[arow[tt] * nblk + b];
-            }
-#pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                const float4_t q = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[f], B, (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) acc[f][tt][v] = fmaf(q[v], s, fmaf(dcorr[f][v], u, acc[f][tt][v]));
-            }
-        }
-    }
-}
-
 __device__ __forceinline__ float round_half_away(float t) {
     const float r = floorf(fabsf(t) + 0.5f);
     return copysignf(fminf(r, 127.0f), t);
 }
 
-// Gate/up: M = 2I rows stacked per slice as [gate 32 | up 32]; fragments 0,1
-// are gate rows j0 + 16f + 4*kg + v, fragments 2,3 the up rows of the same j.
-// The 32 SwiGLU outputs of one slice are exactly one int8 block of H.
-__global__ void __launch_bounds__(256) gate_up_kernel(const uint8_t* __restrict__ blobs, int64_t stride,
-                                                      const Tile* __restrict__ tiles, const int32_t* __restrict__ ntiles,
-                                                      const int32_t* __restrict__ src, const _Float16* __restrict__ xq,
-                                                      const float* __restrict__ xs, const float* __restrict__ xu,
-                                                      int32_t H, int32_t I, _Float16* __restrict__ hq,
-                                                      float* __restrict__ hs, float* __restrict__ hu) {
-    if ((int)blockIdx.x >= *ntiles) return;
-    const Tile tl = tiles[blockIdx.x];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int slice = blockIdx.y * kWaves + wave;
-    if (slice >= I / 32) return;  // waves are independent: no LDS, no barrier
-    const int r16 = lane & 15, kg = lane >> 4;
-    int64_t arow[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        const int r = tt * 16 + r16;
-        arow[tt] = r < tl.nrows ? (int64_t)src[tl.row0 + r] : -1;
-    }
-    float4_t acc[4][4];
-    block_loop(blobs + (int64_t)tl.e * stride, 2 * I, H, slice, lane, arow, xq, xs, xu, acc);
+struct GemmArgs {
+    const uint8_t* blobs;  // packed matrices, one per expert
+    int64_t stride;        // bytes between experts
+    const Tile* chunks;    // chunks of grouped rows
+    const int32_t* nchunks;
+    int32_t nslab;         // 128-row slabs of the packed matrix
+    int32_t Kd;            // reduction length (H for gate/up, I for down)
+    const int32_t* src;    // token of each grouped row
+    const float* prow;     // routing weight of each grouped row (down)
+    const _Float16* act;   // activation codes [rows][Kd] (exact integers)
+    const float* as;       // activation scales [rows][Kd/32]
+    const float* au;       // activation offset terms [rows][Kd/32]
+    int32_t I, H;
+    _Float16* hq;          // gate/up: H codes [n][I]
+    float* hs;             // gate/up: H scales [n][I/32]
+    float* hu;             // gate/up: H offset terms [n][I/32]
+    float* y;              // down: weighted routed rows dm [n][H]
+};
 
-    const int nbi = I / kBlock;
+// The K loop over 32-wide blocks.  Per block: every thread unpacks its dword
+// of the slab's record into LDS buffer b&1 (and the two scales into the
+// offset-pass matrix), one barrier, then the wave's NT tiles x 8 fragments of
+// products, fragment-major so that one A fragment and NT results are live at a
+// time.  Two register sets hold the prefetched next block (record dword and
+// scales, activation fragments and scales), alternating, so the loop body has
+// no copies and each load has a block of compute to land.
+struct BlockLoop {
+    const uint8_t* rec;
+    const _Float16* act;
+    const float* as;
+    int32_t Kd, nblk, dstride;
+    int tau, lane, r16, kg, p;
+    _Float16* d_lds;
+    half8_t (*a_lds)[kFrags][64];
+
+    // arow[i] < 0 (padding rows) reads row 0 with scale 0: branch-free loads.
+    template <int NT>
+    __device__ __forceinline__ void load(int blk, const int64_t (&arow)[kTilesPerWave], uint32_t& xw, uint32_t& sw,
+                                         half8_t (&bf)[kTilesPerWave], float (&sf)[kTilesPerWave]) const {
+        const uint8_t* rb = rec + (int64_t)blk * kRecordBytes;
+        xw = reinterpret_cast<const uint32_t*>(rb)[tau];
+        sw = reinterpret_cast<const uint32_t*>(rb + kRecordCodeBytes)[p * 16 + r16];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        float h[2][4];
-        float amax = 0.f;
+        for (int i = 0; i < NT; ++i) {
+            const int64_t r = arow[i] >= 0 ? arow[i] : 0;
+            bf[i] = *reinterpret_cast<const half8_t*>(act + r * Kd + blk * kBlock + kg * 8);
+            const float sv = as[r * nblk + blk];
+            sf[i] = arow[i] >= 0 ? sv : 0.f;
+        }
+    }
+
+    __device__ __forceinline__ void unpack(int blk, uint32_t xw, uint32_t sw) const {
+        half8_t a0, a1;
+        const _Float16 d0 = lo_half(sw), d1 = hi_half(sw);
+        unpack_dword(xw, d0, d1, a0, a1);
+        a_lds[blk & 1][2 * p][lane] = a0;
+        a_lds[blk & 1][2 * p + 1][lane] = a1;
+        if (kg == 0) {
+            d_lds[(32 * p + r16) * dstride + blk] = d0;
+            d_lds[(32 * p + 16 + r16) * dstride + blk] = d1;
+        }
+    }
+
+    template <int NT>
+    __device__ __forceinline__ void products(int blk, const half8_t (&bf)[kTilesPerWave],
+                                             const float (&sf)[kTilesPerWave],
+                                             float4_t (&acc)[kFrags][kTilesPerWave]) const {
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
+        for (int f = 0; f < kFrags; ++f) {
+            const half8_t a = a_lds[blk & 1][f][lane];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float g = acc[f][tt][v], up = acc[f + 2][tt][v];
-                h[f][v] = g / (1.0f + expf(-g)) * up;
-                amax = fmaxf(amax, fabsf(h[f][v]));
+            for (int i = 0; i < NT; ++i) {
+                const float4_t q =
+                    __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf[i], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[f][i][v] = fmaf(q[v], sf[i], acc[f][i][v]);
             }
-        amax = fmaxf(amax, __shfl_xor(amax, 16));
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
-        const float sh = amax / 127.0f;
-        float q[2][4];
-        int qsum = 0;
+        }
+    }
+
+    // nblk is even (H is a multiple of 128, I of 64): two blocks per
+    // iteration, no exit in between; the last prefetch re-reads the last block.
+    template <int NT>
+    __device__ __forceinline__ void run(const int64_t (&arow)[kTilesPerWave],
+                                        float4_t (&acc)[kFrags][kTilesPerWave]) const {
+        uint32_t xw0, sw0, xw1, sw1;
+        half8_t bf0[kTilesPerWave], bf1[kTilesPerWave];
+        float sf0[kTilesPerWave], sf1[kTilesPerWave];
+        load<NT>(0, arow, xw0, sw0, bf0, sf0);
+        for (int b = 0; b < nblk; b += 2) {
+            unpack(b, xw0, sw0);
+            __syncthreads();
+            load<NT>(b + 1, arow, xw1, sw1, bf1, sf1);
+            products<NT>(b, bf0, sf0, acc);
+            unpack(b + 1, xw1, sw1);
+            __syncthreads();
+            load<NT>(b + 2 < nblk ? b + 2 : nblk - 1, arow, xw0, sw0, bf0, sf0);
+            products<NT>(b + 1, bf1, sf1, acc);
+        }
+    }
+};
+
+// kGateUp: activation rows are tokens (through src), epilogue SwiGLU + int8 H.
+// Otherwise: activation rows are the grouped rows, epilogue weighted row stores.
+template <bool kGateUp>
+__global__ void __launch_bounds__(256, 2) expert_gemm_kernel(GemmArgs g) {
+    __shared__ half8_t a_lds[2][kFrags][64];
+    extern __shared__ _Float16 d_lds[];  // [kSlabRows][dstride]: d of every row and block (offset pass)
+
+    // workgroup -> (chunk, slab), all slabs of a chunk on one XCD
+    const int id = blockIdx.x;
+    const int local = id >> 3;
+    const int chunk = (local / g.nslab) * 8 + (id & 7);
+    const int slab = local % g.nslab;
+    if (chunk >= *g.nchunks) return;  // uniform over the workgroup, before any barrier
+    const Tile tl = g.chunks[chunk];
+
+    const int tau = threadIdx.x, lane = tau & 63, r16 = lane & 15, kg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tau >> 6);
+    const int nblk = g.Kd / kBlock;
+    const int nch = (nblk + 31) / 32;
+    const int dstride = nch * 32 + 8;
+
+    // zero the padding blocks of the offset-pass matrix
+    for (int i = tau; i < kSlabRows * (nch * 32 - nblk); i += 256) {
+        const int r = i / (nch * 32 - nblk), c = nblk + i % (nch * 32 - nblk);
+        d_lds[r * dstride + c] = (_Float16)0.0f;
+    }
+
+    // this wave's tiles
+    int64_t arow[kTilesPerWave];
+    int ntw = 0;
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
+    for (int i = 0; i < kTilesPerWave; ++i) {
+        const int tt = wave + kWaves * i;
+        const int r = 16 * tt + r16;
+        if (16 * tt < tl.nrows) ntw = i + 1;  // wave-uniform
+        arow[i] = -1;
+        if (r < tl.nrows) arow[i] = kGateUp ? (int64_t)g.src[tl.row0 + r] : (int64_t)(tl.row0 + r);
+    }
+
+    const uint8_t* rec = g.blobs + (int64_t)tl.e * g.stride + (int64_t)slab * nblk * kRecordBytes;
+    const int p = wave;  // fragment pair this thread unpacks: fragments 2p, 2p+1
+
+    float4_t acc[kFrags][kTilesPerWave];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                q[f][v] = sh != 0.0f ? round_half_away(h[f][v] / sh) : 0.0f;
-                qsum += (int)q[f][v];
-            }
-        qsum += __shfl_xor(qsum, 16);
-        qsum += __shfl_xor(qsum, 32);
-        const int r = tt * 16 + r16;
-        if (r < tl.nrows) {
-            const int64_t row = tl.row0 + r;
-            _Float16* dst = hq + row * I + slice * 32 + 4 * kg;
+    for (int f = 0; f < kFrags; ++f)
 #pragma unroll
-            for (int f = 0; f < 2; ++f) {
-                const half4_t hv = {(_Float16)q[f][0], (_Float16)q[f][1], (_Float16)q[f][2], (_Float16)q[f][3]};
-                *reinterpret_cast<half4_t*>(dst + 16 * f) = hv;
+        for (int i = 0; i < kTilesPerWave; ++i) acc[f][i] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    BlockLoop L{rec, g.act, g.as, g.Kd, nblk, dstride, tau, lane, r16, kg, p, d_lds, a_lds};
+    switch (ntw) {  // wave-uniform: the block loop is straight-line code for 1..3 tiles
+        case 1: L.run<1>(arow, acc); break;
+        case 2: L.run<2>(arow, acc); break;
+        case 3: L.run<3>(arow, acc); break;
+        default: L.run<0>(arow, acc); break;  // no tiles: still unpack and meet every barrier
+    }
+    __syncthreads();  // every d of the slab is in LDS
+
+    // offset pass: acc += sum_b d[row][b] * u[tok][b], 32 blocks per MFMA; u of
+    // each routed row is scaled by a power of two to [-1, 1] and split into
+    // two fp16 parts (first sweep: the row's max |u|; second: the products).
+#pragma unroll
+    for (int i = 0; i < kTilesPerWave; ++i) {
+        if (i >= ntw) continue;
+        const float* urow = g.au + (arow[i] >= 0 ? arow[i] : 0) * nblk;
+        const bool valid = arow[i] >= 0;
+        float m = 0.f;
+        for (int c = 0; c < nch; ++c)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int blk = 32 * c + 8 * kg + j;
+                if (valid && blk < nblk) m = fmaxf(m, fabsf(urow[blk]));
             }
-            if (kg == 0) {
-                hs[row * nbi + slice] = sh;
-                hu[row * nbi + slice] = -0.5f * sh * (float)qsum;
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        int ex = 0;
+        if (m > 0.f) frexpf(m, &ex);
+        const float down_scale = ldexpf(1.0f, -ex), up_scale = ldexpf(1.0f, ex);
+        float4_t corr[kFrags];
+#pragma unroll
+        for (int f = 0; f < kFrags; ++f) corr[f] = (float4_t){0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < nch; ++c) {
+            half8_t bhi, blo;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int blk = 32 * c + 8 * kg + j;
+                const float un = (valid && blk < nblk) ? urow[blk] * down_scale : 0.f;
+                const _Float16 h = (_Float16)un;
+                bhi[j] = h;
+                blo[j] = (_Float16)(un - (float)h);
             }
+#pragma unroll
+            for (int f = 0; f < kFrags; ++f) {
+                const half8_t da =
+                    *reinterpret_cast<const half8_t*>(&d_lds[(16 * f + r16) * dstride + 32 * c + 8 * kg]);
+                corr[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(da, bhi, corr[f], 0, 0, 0);
+                corr[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(da, blo, corr[f], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int f = 0; f < kFrags; ++f)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[f][i][v] = fmaf(corr[f][v], up_scale, acc[f][i][v]);
+    }
+
+    if constexpr (kGateUp) {
+        // fragments 0..3: gate rows 64*slab + 16f + 4kg + v; 4..7: the up rows of the same j
+        const int nbi = g.I / kBlock;
+#pragma unroll
+        for (int i = 0; i < kTilesPerWave; ++i) {
+            if (i >= ntw) continue;
+            const int r = 16 * (wave + kWaves * i) + r16;
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                float h[2][4];
+                float amax = 0.f;
+#pragma unroll
+                for (int ff = 0; ff < 2; ++ff)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const float gt = acc[2 * hb + ff][i][v], up = acc[4 + 2 * hb + ff][i][v];
+                        h[ff][v] = gt / (1.0f + expf(-gt)) * up;
+                        amax = fmaxf(amax, fabsf(h[ff][v]));
+                    }
+                amax = fmaxf(amax, __shfl_xor(amax, 16));
+                amax = fmaxf(amax, __shfl_xor(amax, 32));
+                const float sh = amax / 127.0f;
+                float q[2][4];
+                int qsum = 0;
+#pragma unroll
+                for (int ff = 0; ff < 2; ++ff)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        q[ff][v] = sh != 0.0f ? round_half_away(h[ff][v] / sh) : 0.0f;
+                        qsum += (int)q[ff][v];
+                    }
+                qsum += __shfl_xor(qsum, 16);
+                qsum += __shfl_xor(qsum, 32);
+                if (r < tl.nrows) {
+                    const int64_t row = tl.row0 + r;
+                    _Float16* dst = g.hq + row * g.I + 64 * slab + 32 * hb + 4 * kg;
+#pragma unroll
+                    for (int ff = 0; ff < 2; ++ff) {
+                        const half4_t hv = {(_Float16)q[ff][0], (_Float16)q[ff][1], (_Float16)q[ff][2],
+                                            (_Float16)q[ff][3]};
+                        *reinterpret_cast<half4_t*>(dst + 16 * ff) = hv;
+                    }
+                    if (kg == 0) {
+                        g.hs[row * nbi + 2 * slab + hb] = sh;
+                        g.hu[row * nbi + 2 * slab + hb] = -0.5f * sh * (float)qsum;
+                    }
+                }
+            }
+        }
+    } else {
+        // Each routed row's output times its routing weight, written to its
+        // grouped row of dm [n][H] (the rows the combine reads).  Per tile the
+        // wave parks its 16 rows x 128 outputs in LDS and stores them row by
+        // row, 512 contiguous bytes per row.
+        float* park = reinterpret_cast<float*>(d_lds + kSlabRows * dstride) + wave * 16 * kParkStride;
+#pragma unroll
+        for (int i = 0; i < kTilesPerWave; ++i) {
+            if (i >= ntw) continue;
+            const float w = arow[i] >= 0 ? g.prow[arow[i]] : 0.f;
+#pragma unroll
+            for (int f = 0; f < kFrags; ++f) {
+                const float4 v4 = make_float4(w * acc[f][i][0], w * acc[f][i][1], w * acc[f][i][2], w * acc[f][i][3]);
+                *reinterpret_cast<float4*>(park + r16 * kParkStride + 16 * f + 4 * kg) = v4;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            const int tt = wave + kWaves * i;
+            // float4 (j*64 + lane): row (j*64 + lane) / 32 of the tile, outputs 4*((j*64 + lane) % 32)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int flat = j * 64 + lane;
+                const int rr = flat >> 5, c4 = flat & 31;
+                const int r = 16 * tt + rr;
+                if (r < tl.nrows) {
+                    const float4 v4 = *reinterpret_cast<const float4*>(park + rr * kParkStride + 4 * c4);
+                    *reinterpret_cast<float4*>(g.y + (int64_t)(tl.row0 + r) * g.H + kSlabRows * slab + 4 * c4) = v4;
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
         }
     }
 }
 
-// Down: M = H rows, slice rows o0 + 16f + 4*kg + v; the epilogue adds each
-// routed row, times its routing weight, into the output row of its token.
-__global__ void __launch_bounds__(256) down_kernel(const uint8_t* __restrict__ blobs, int64_t stride,
-                                                   const Tile* __restrict__ tiles, const int32_t* __restrict__ ntiles,
-                                                   const int32_t* __restrict__ src, const float* __restrict__ prow,
-                                                   const _Float16* __restrict__ hq, const float* __restrict__ hs,
-                                                   const float* __restrict__ hu, int32_t H, int32_t I,
-                                                   float* __restrict__ y) {
-    if ((int)blockIdx.x >= *ntiles) return;
-    const Tile tl = tiles[blockIdx.x];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int slice = blockIdx.y * kWaves + wave;
-    if (slice >= H / 64) return;
-    const int r16 = lane & 15, kg = lane >> 4;
-    int64_t arow[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        const int r = tt * 16 + r16;
-        arow[tt] = r < tl.nrows ? (int64_t)(tl.row0 + r) : -1;
+// The combine: y[t] = sum_k dm[slot[t*K + k]] (rows already weighted), k in
+// order, so the result does not depend on scheduling.  One workgroup of 256
+// threads per token row chunk of 1024 outputs; float4 per thread.
+__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ dm, const int32_t* __restrict__ slot,
+                                                      int64_t T, int32_t K, int32_t H, float* __restrict__ y) {
+    const int64_t t = blockIdx.y;
+    const int o = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (o >= H) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < K; ++k) {
+        const int64_t r = slot[t * K + k];
+        const float4 v = *reinterpret_cast<const float4*>(dm + r * H + o);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
     }
-    float4_t acc[4][4];
-    block_loop(blobs + (int64_t)tl.e * stride, H, I, slice, lane, arow, hq, hs, hu, acc);
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        if (arow[tt] < 0) continue;
-        const int64_t t = src[arow[tt]];
-        const float w = prow[arow[tt]];
-        float* dst = y + t * H + slice * 64 + 4 * kg;
-#pragma unroll
-        for (int f = 0; f < 4; ++f)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) unsafeAtomicAdd(dst + 16 * f + v, w * acc[f][tt][v]);
-    }
+    *reinterpret_cast<float4*>(y + t * H + o) = acc;
+}
+
+// Dynamic LDS: the offset-pass matrix d [128][dstride] fp16, then (down only)
+// 4 waves x 16 parked output rows.
+inline size_t dynamic_lds_bytes(int32_t Kd, bool park) {
+    const int nblk = Kd / kBlock, nch = (nblk + 31) / 32;
+    size_t b = (size_t)kSlabRows * (nch * 32 + 8) * sizeof(_Float16);
+    b = (b + 15) / 16 * 16;
+    if (park) b += (size_t)kWaves * 16 * kParkStride * sizeof(float);
+    return b;
+}
+
+inline unsigned grid_of(int64_t chunks_cap, int32_t nslab) {
+    return (unsigned)(8 * ((chunks_cap + 7) / 8) * nslab);
 }
 
 }  // namespace
 
-hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const Tile* tiles, const int32_t* ntiles,
-                          int64_t tiles_cap, const int32_t* src, const _Float16* xq, const float* xs,
+hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const Tile* chunks, const int32_t* nchunks,
+                          int64_t chunks_cap, const int32_t* src, const _Float16* xq, const float* xs,
                           const float* xu, int32_t H, int32_t I, _Float16* hq, float* hs, float* hu,
                           hipStream_t st) {
-    const int nslices = I / 32;
-    if (tiles_cap > 0)
-        hipLaunchKernelGGL(gate_up_kernel, dim3((unsigned)tiles_cap, (nslices + kWaves - 1) / kWaves), dim3(256), 0,
-                           st, blobs, stride, tiles, ntiles, src, xq, xs, xu, H, I, hq, hs, hu);
+    GemmArgs g{blobs, stride, chunks, nchunks, 2 * I / kSlabRows, H, src, nullptr, xq, xs, xu, I, H, hq, hs, hu,
+               nullptr};
+    if (chunks_cap > 0)
+        hipLaunchKernelGGL(expert_gemm_kernel<true>, dim3(grid_of(chunks_cap, g.nslab)), dim3(256),
+                           dynamic_lds_bytes(H, false), st, g);
     return hipGetLastError();
 }
 
-hipError_t launch_down(const uint8_t* blobs, int64_t stride, const Tile* tiles, const int32_t* ntiles,
-                       int64_t tiles_cap, const int32_t* src, const float* prow, const _Float16* hq,
-                       const float* hs, const float* hu, int32_t H, int32_t I, float* y, hipStream_t st) {
-    const int nslices = H / 64;
-    if (tiles_cap > 0)
-        hipLaunchKernelGGL(down_kernel, dim3((unsigned)tiles_cap, (nslices + kWaves - 1) / kWaves), dim3(256), 0, st,
-                           blobs, stride, tiles, ntiles, src, prow, hq, hs, hu, H, I, y);
+hipError_t launch_down(const uint8_t* blobs, int64_t stride, const Tile* chunks, const int32_t* nchunks,
+                       int64_t chunks_cap, const int32_t* src, const float* prow, const _Float16* hq,
+                       const float* hs, const float* hu, int32_t H, int32_t I, float* dm, hipStream_t st) {
+    GemmArgs g{blobs, stride, chunks, nchunks, H / kSlabRows, I, src, prow, hq, hs, hu, I, H, nullptr, nullptr,
+               nullptr, dm};
+    if (chunks_cap > 0)
+        hipLaunchKernelGGL(expert_gemm_kernel<false>, dim3(grid_of(chunks_cap, g.nslab)), dim3(256),
+                           dynamic_lds_bytes(I, true), st, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* dm, const int32_t* slot, int64_t T, int32_t K, int32_t H, float* y,
+                          hipStream_t st) {
+    if (T > 0)
+        hipLaunchKernelGGL(combine_kernel, dim3((H / 4 + 255) / 256, (unsigned)T), dim3(256), 0, st, dm, slot, T, K, H,
+                           y);
     return hipGetLastError();
 }
 

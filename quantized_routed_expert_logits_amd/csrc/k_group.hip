@@ -2,7 +2,8 @@
 //
 // Strata compare v0.1.35...v0.1.37 page, include/strata/prefill/moe_fused.hpp,
 // group: from the router's ids, per expert its rows (counts, offsets, the list
-// of 64-row tiles), slot[i] = the row of pair i and src[row] = its token
+// of 64-row tiles; here chunks of up to 256 rows), slot[i] = the row of pair
+// i and src[row] = its token
 // i / K, without a host wait.  The order of rows within an expert is left open
 // there; these kernels produce the stable order (ascending pair index) of the
 // MMQ path's host counting sort (Winery-Strata prefill.cpp page, Prefill::run,
@@ -11,7 +12,8 @@
 // Three launches, none of which waits on the host:
 //   hist    one workgroup per chunk of 2048 pairs: LDS histogram of its ids;
 //   scan    one workgroup: per expert the exclusive prefix over chunks, the
-//           counts' exclusive scan over experts (offsets), and the tile list;
+//           counts' exclusive scan over experts (offsets), and the list of
+//           row chunks (at most 256 rows of one expert each) the GEMMs walk;
 //   scatter one wave per chunk: pairs in order, 64 at a time; each lane's rank
 //           among the lanes of the same expert comes from ballots over the id
 //           bits (multi-split), so rows are assigned in pair order.
@@ -39,6 +41,20 @@ __global__ void __launch_bounds__(256) group_hist_kernel(const int32_t* __restri
     if (bad) atomicOr(err, 1);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(int64_t)blockIdx.x * E + e] = h[e];
+}
+
+// An expert's rows in chunks of at most kChunkRows, of equal size rounded up to
+// whole 16-row tiles (so no chunk is much smaller than the others); returns
+// the chunk count and the rows per chunk (the last may have fewer).
+__device__ int chunk_split(int cnt, int* per) {
+    if (cnt <= 0) {
+        *per = 0;
+        return 0;
+    }
+    const int n0 = (cnt + kChunkRows - 1) / kChunkRows;
+    const int p = ((cnt + n0 - 1) / n0 + 15) / 16 * 16;
+    *per = p;
+    return (cnt + p - 1) / p;
 }
 
 // Exclusive scan of one value per thread over a workgroup of 1024 threads.
@@ -97,15 +113,16 @@ __global__ void __launch_bounds__(1024) group_scan_kernel(const int32_t* __restr
         }
     }
     const int off = block_exclusive_scan(e < E ? cnt : 0, &total_rows);
-    const int nt = e < E ? (cnt + kTileRows - 1) / kTileRows : 0;
+    int per = 0;
+    const int nt = e < E ? chunk_split(cnt, &per) : 0;
     const int toff = block_exclusive_scan(nt, &total_tiles);
     if (e < E) {
         offsets[e] = off;
         for (int i = 0; i < nt; ++i) {
             Tile tl;
             tl.e = e;
-            tl.row0 = off + i * kTileRows;
-            tl.nrows = cnt - i * kTileRows < kTileRows ? cnt - i * kTileRows : kTileRows;
+            tl.row0 = off + i * per;
+            tl.nrows = cnt - i * per < per ? cnt - i * per : per;
             tl.pad = 0;
             tiles[toff + i] = tl;
         }
@@ -164,14 +181,15 @@ __global__ void __launch_bounds__(1024) tiles_from_offsets_kernel(const int32_t*
     __shared__ int total_tiles;
     const int e = threadIdx.x;
     const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
-    const int nt = (cnt + kTileRows - 1) / kTileRows;
+    int per = 0;
+    const int nt = chunk_split(cnt, &per);
     const int toff = block_exclusive_scan(nt, &total_tiles);
     if (e < E)
         for (int i = 0; i < nt; ++i) {
             Tile tl;
             tl.e = e;
-            tl.row0 = offsets[e] + i * kTileRows;
-            tl.nrows = cnt - i * kTileRows < kTileRows ? cnt - i * kTileRows : kTileRows;
+            tl.row0 = offsets[e] + i * per;
+            tl.nrows = cnt - i * per < per ? cnt - i * per : per;
             tl.pad = 0;
             tiles[toff + i] = tl;
         }

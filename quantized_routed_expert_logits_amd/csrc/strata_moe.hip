@@ -7,8 +7,9 @@
 // The sequence follows the MoE half of Prefill::run (Winery-Strata
 // prefill.cpp page) on the fused path of moe_fused.hpp (Strata compare
 // v0.1.35...v0.1.37 page): router -> route -> int8 activations once per
-// token -> grouping on the GPU -> experts -> combine, with the combine folded
-// into the down GEMM's epilogue as a weighted scatter-add.
+// token -> grouping on the GPU -> experts -> combine.  The down GEMM applies
+// each routed row's weight and writes the row to its grouped slot; the combine
+// then adds every token's K rows in k order (deterministic).
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -131,11 +132,12 @@ struct Buffers {
     _Float16* hq;
     float* hs;
     float* hu;
+    float* dm;
     int64_t tiles_cap;
 };
 
 struct Offsets {
-    size_t logits, ids, p, xq, xs, xu, hist, base, offsets, tiles, ntiles, err, src, slot, prow, hq, hs, hu, total;
+    size_t logits, ids, p, xq, xs, xu, hist, base, offsets, tiles, ntiles, err, src, slot, prow, hq, hs, hu, dm, total;
     int64_t tiles_cap;
 };
 
@@ -163,6 +165,7 @@ Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I) {
     o.hq = L.take<_Float16>(n * I);
     o.hs = L.take<float>(n * (I / kBlock));
     o.hu = L.take<float>(n * (I / kBlock));
+    o.dm = L.take<float>(n * H);
     o.total = L.off;
     return o;
 }
@@ -187,13 +190,14 @@ Buffers carve(char* ws, const Offsets& o) {
     b.hq = (_Float16*)(ws + o.hq);
     b.hs = (float*)(ws + o.hs);
     b.hu = (float*)(ws + o.hu);
+    b.dm = (float*)(ws + o.dm);
     b.tiles_cap = o.tiles_cap;
     return b;
 }
 
 // ----------------------------------------------------------------- timing
-enum Kind { kQuantize, kRouter, kTopK, kGroup, kGateUp, kDown, kNumKinds };
-const char* const kKindNames[kNumKinds] = {"quantize", "router_gemm", "topk", "group", "gate_up", "down"};
+enum Kind { kQuantize, kRouter, kTopK, kGroup, kGateUp, kDown, kCombine, kNumKinds };
+const char* const kKindNames[kNumKinds] = {"quantize", "router_gemm", "topk", "group", "gate_up", "down", "combine"};
 
 struct Timing {
     bool on = false;
@@ -224,14 +228,28 @@ struct CallTimer {
 };
 
 // ------------------------------------------------------------- validation
+#define TRY(expr)                 \
+    do {                          \
+        int rc_ = (expr);         \
+        if (rc_ != 0) return rc_; \
+    } while (0)
+
+// H: 128-row slabs of the down matrix; I: 64-row slabs of gate and of up;
+// both <= 4096 (the offset pass covers at most 128 blocks).
+int check_dims(int32_t hidden, int32_t ffn) {
+    if (hidden < 128 || hidden % 128 || hidden > 4096)
+        return fail(STRATA_MOE_EINVAL, "hidden %d is not a multiple of 128 in [128, 4096]", hidden);
+    if (ffn < 64 || ffn % 64 || ffn > 4096)
+        return fail(STRATA_MOE_EINVAL, "ffn %d is not a multiple of 64 in [64, 4096]", ffn);
+    return 0;
+}
+
 int check_experts(const strata_moe_experts* ex) {
     if (!ex) return fail(STRATA_MOE_EINVAL, "experts is NULL");
     if (ex->format != STRATA_MOE_Q2_SYM) return fail(STRATA_MOE_EUNSUPPORTED, "unknown weight format %d", ex->format);
     if (ex->n_expert < 1 || ex->n_expert > kMaxExperts)
         return fail(STRATA_MOE_EINVAL, "n_expert %d outside [1, %d]", ex->n_expert, kMaxExperts);
-    if (ex->hidden < 64 || ex->hidden % 64)
-        return fail(STRATA_MOE_EINVAL, "hidden %d is not a positive multiple of 64", ex->hidden);
-    if (ex->ffn < 32 || ex->ffn % 32) return fail(STRATA_MOE_EINVAL, "ffn %d is not a positive multiple of 32", ex->ffn);
+    TRY(check_dims(ex->hidden, ex->ffn));
     if (!ex->gate_up || !ex->down) return fail(STRATA_MOE_EINVAL, "expert blob pointer is NULL");
     const int64_t gu = round_up(packed_matrix_bytes(2LL * ex->ffn, ex->hidden), 256);
     const int64_t dn = round_up(packed_matrix_bytes(ex->hidden, ex->ffn), 256);
@@ -259,12 +277,6 @@ int check_no_overlap(const void* a, const void* b, int64_t bytes) {
     return 0;
 }
 
-#define TRY(expr)                 \
-    do {                          \
-        int rc_ = (expr);         \
-        if (rc_ != 0) return rc_; \
-    } while (0)
-
 int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int64_t T, int32_t K, float* out,
               hipStream_t st, Buffers* keep) {
     const int32_t E = ex->n_expert, H = ex->hidden, I = ex->ffn;
@@ -275,7 +287,7 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     Buffers b = carve(ws, o);
     CallTimer tm(st);
     tm.begin(kQuantize);
-    HIP_TRY(launch_quantize(x, T, H, b.xq, nullptr, b.xs, b.xu, out, st), "quantize launch");
+    HIP_TRY(launch_quantize(x, T, H, b.xq, nullptr, b.xs, b.xu, nullptr, st), "quantize launch");
     tm.end(kQuantize);
     tm.begin(kRouter);
     HIP_TRY(launch_router_logits(x, wr, ex->router_bias, T, H, E, b.logits, st), "router launch");
@@ -296,9 +308,12 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     tm.end(kGateUp);
     tm.begin(kDown);
     HIP_TRY(launch_down((const uint8_t*)ex->down, ex->down_stride, b.tiles, b.ntiles, b.tiles_cap, b.src, b.prow,
-                        b.hq, b.hs, b.hu, H, I, out, st),
+                        b.hq, b.hs, b.hu, H, I, b.dm, st),
             "down launch");
     tm.end(kDown);
+    tm.begin(kCombine);
+    HIP_TRY(launch_combine(b.dm, b.slot, T, K, H, out, st), "combine launch");
+    tm.end(kCombine);
     if (keep) *keep = b;
     return 0;
 }
@@ -320,8 +335,7 @@ const char* strata_moe_last_error(void) { return g_err.c_str(); }
 int strata_moe_packed_bytes(int32_t hidden, int32_t ffn, int64_t* gate_up_bytes, int64_t* down_bytes) {
     g_err.clear();
     if (!gate_up_bytes || !down_bytes) return fail(STRATA_MOE_EINVAL, "null output pointer");
-    if (hidden < 64 || hidden % 64 || ffn < 32 || ffn % 32)
-        return fail(STRATA_MOE_EINVAL, "hidden %d / ffn %d must be multiples of 64 / 32", hidden, ffn);
+    TRY(check_dims(hidden, ffn));
     *gate_up_bytes = round_up(packed_matrix_bytes(2LL * ffn, hidden), 256);
     *down_bytes = round_up(packed_matrix_bytes(hidden, ffn), 256);
     return 0;
@@ -442,7 +456,7 @@ int strata_moe_route(const float* x, const float* router_w, const float* bias, i
                      int32_t K, int32_t* ids, float* p, void* stream) {
     g_err.clear();
     if (E < 1 || E > kMaxExperts) return fail(STRATA_MOE_EINVAL, "E = %d outside [1, %d]", E, kMaxExperts);
-    if (H < 64 || H % 64) return fail(STRATA_MOE_EINVAL, "H = %d is not a positive multiple of 64", H);
+    if (H < 64 || H % 64) return fail(STRATA_MOE_EINVAL, "H = %d is not a positive multiple of 64", H);  // top-K rescore
     TRY(check_tk(T, K, E));
     if (T == 0) return 0;
     if (!x || !router_w || !ids || !p) return fail(STRATA_MOE_EINVAL, "null pointer");
@@ -544,19 +558,21 @@ int strata_moe_down(const int8_t* qh, const float* sh, const int32_t* offsets, c
     Layout L;
     const size_t o_hq = L.take<_Float16>(n * I), o_hu = L.take<float>(n * (I / kBlock));
     const size_t o_tiles = L.take<Tile>(max_tiles(n, E)), o_nt = L.take<int32_t>(1), o_prow = L.take<float>(n);
+    const size_t o_dm = L.take<float>(n * H);
     char* ws = nullptr;
     TRY(get_workspace(L.off, &ws));
     _Float16* hq = (_Float16*)(ws + o_hq);
     float* hu = (float*)(ws + o_hu);
     float* prow = (float*)(ws + o_prow);
+    float* dm = (float*)(ws + o_dm);
     HIP_TRY(launch_i8_to_f16(qh, n * I, hq, st), "convert launch");
     HIP_TRY(launch_block_correction(qh, sh, n, I, hu, st), "correction launch");
     HIP_TRY(launch_tiles_from_offsets(offsets, E, (Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), st), "tiles launch");
     HIP_TRY(launch_row_weights(slot, p, n, prow, st), "weights launch");
-    HIP_TRY(launch_fill_zero(out, T * H, st), "fill launch");
     HIP_TRY(launch_down((const uint8_t*)experts->down, experts->down_stride, (Tile*)(ws + o_tiles),
-                        (int32_t*)(ws + o_nt), max_tiles(n, E), src, prow, hq, sh, hu, H, I, out, st),
+                        (int32_t*)(ws + o_nt), max_tiles(n, E), src, prow, hq, sh, hu, H, I, dm, st),
             "down launch");
+    HIP_TRY(launch_combine(dm, slot, T, K, H, out, st), "combine launch");
     return 0;
 }
 

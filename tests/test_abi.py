@@ -74,8 +74,11 @@ def test_workspace_bytes_scale_with_tokens(qm):
     (17, 8, 1, 2560, 1024, 512, -1),     # K > 16
     (10, -1, 1, 2560, 1024, 512, -1),    # negative T
     (10, 8, 7, 2560, 1024, 512, -2),     # unknown format
-    (10, 8, 1, 2600, 1024, 512, -1),     # H not a multiple of 64
-    (10, 8, 1, 2560, 1000, 512, -1),     # I not a multiple of 32
+    (10, 8, 1, 2600, 1024, 512, -1),     # H not a multiple of 128
+    (10, 8, 1, 2624, 1024, 512, -1),     # H a multiple of 64 but not of 128
+    (10, 8, 1, 2560, 1000, 512, -1),     # I not a multiple of 64
+    (10, 8, 1, 2560, 1056, 512, -1),     # I a multiple of 32 but not of 64
+    (10, 8, 1, 8192, 1024, 512, -1),     # H above 4096
     (10, 8, 1, 2560, 1024, 2048, -1),    # too many experts
     (4, 8, 1, 256, 128, 3, -1),          # K > E
 ])

@@ -55,7 +55,7 @@ def test_quantize_full_size_input_bit_exact(qm):
 
 
 # --------------------------------------------------------------------- pack
-@pytest.mark.parametrize("shape", [S.shape("tiny"), S.custom(T=1, H=192, E=3, K=1, I=96)])
+@pytest.mark.parametrize("shape", [S.shape("tiny"), S.custom(T=1, H=384, E=3, K=1, I=192)])
 def test_pack_unpack_round_trip(qm, shape):
     ex = gpu_experts(shape)
     cg, sg, cd, sd = qm.strata_moe_unpack(ex, 0, shape.E)
@@ -144,7 +144,8 @@ def _stage_ref(s):
     return x, wr, oracle.layer(x, wr, S.router_bias(s), getter(s), s.E, s.K, want_h=True)
 
 
-STAGE_SHAPES = [S.shape("tiny"), S.custom(T=300, H=256, E=12, K=3, I=96), S.custom(T=70, H=640, E=5, K=2, I=160)]
+STAGE_SHAPES = [S.shape("tiny"), S.custom(T=300, H=256, E=12, K=3, I=128), S.custom(T=70, H=640, E=5, K=2, I=192),
+                S.custom(T=2000, H=384, E=3, K=2, I=64)]
 
 
 @pytest.mark.parametrize("s", STAGE_SHAPES, ids=lambda s: s.name)
@@ -194,7 +195,7 @@ def test_layer_zero_input_and_repeat(qm):
     x = _t(S.activations(s))
     a = qm.strata_moe_prefill(x, wr, ex, s.K, torch.empty_like(x)).clone()
     b = qm.strata_moe_prefill(x, wr, ex, s.K, torch.empty_like(x))
-    assert rel_err(b.cpu().numpy(), a.cpu().numpy()) <= 1e-6
+    assert torch.equal(a, b)  # the combine adds each token's rows in a fixed order
 
 
 def test_layer_zero_tokens(qm):
