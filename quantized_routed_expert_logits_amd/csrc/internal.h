@@ -52,11 +52,11 @@ hipError_t launch_tiles_from_offsets(const int32_t* offsets, int32_t E, Tile* ti
 hipError_t launch_row_weights(const int32_t* slot, const float* p, int64_t n, float* prow, hipStream_t st);
 
 hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const Tile* tiles, const int32_t* ntiles,
-                          int64_t tiles_cap, const int32_t* src, const _Float16* xq, const float* xs,
+                          int64_t tiles_cap, const int32_t* src, const _Float16* xq, int64_t act_rows, const float* xs,
                           const float* xu, int32_t H, int32_t I, _Float16* hq, float* hs, float* hu,
                           hipStream_t st);
 hipError_t launch_down(const uint8_t* blobs, int64_t stride, const Tile* tiles, const int32_t* ntiles,
-                       int64_t tiles_cap, const int32_t* src, const float* prow, const _Float16* hq,
+                       int64_t tiles_cap, const int32_t* src, const float* prow, const _Float16* hq, int64_t act_rows,
                        const float* hs, const float* hu, int32_t H, int32_t I, float* dm, hipStream_t st);
 hipError_t launch_combine(const float* dm, const int32_t* slot, int64_t T, int32_t K, int32_t H, float* y,
                           hipStream_t st);

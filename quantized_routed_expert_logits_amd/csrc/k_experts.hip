@@ -52,6 +52,7 @@ constexpr int kWaves = 4;
 constexpr int kFrags = kSlabRows / 16;                               // 8
 constexpr int kTilesPerWave = kChunkRows / (16 * kWaves);            // 3
 constexpr int kParkStride = kSlabRows + 4;                           // floats per parked output row
+constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3 for raw dword loads on gfx9 (gfx950)
 
 __device__ __forceinline__ _Float16 lo_half(uint32_t w) { return __builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
 __device__ __forceinline__ _Float16 hi_half(uint32_t w) { return __builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
@@ -94,6 +95,7 @@ struct GemmArgs {
     const int32_t* src;    // token of each grouped row
     const float* prow;     // routing weight of each grouped row (down)
     const _Float16* act;   // activation codes [rows][Kd] (exact integers)
+    int64_t act_rows;      // rows of act / as / au
     const float* as;       // activation scales [rows][Kd/32]
     const float* au;       // activation offset terms [rows][Kd/32]
     int32_t I, H;
@@ -111,26 +113,34 @@ struct GemmArgs {
 // scales, activation fragments and scales), alternating, so the loop body has
 // no copies and each load has a block of compute to land.
 struct BlockLoop {
-    const uint8_t* rec;
-    const _Float16* act;
-    const float* as;
+    __amdgpu_buffer_rsrc_t rec;  // this slab's records (nblk x 1280 bytes)
+    __amdgpu_buffer_rsrc_t act;  // activation codes, fp16 [rows][Kd]
+    __amdgpu_buffer_rsrc_t as;   // activation scales [rows][nblk]
     int32_t Kd, nblk, dstride;
     int tau, lane, r16, kg, p;
     _Float16* d_lds;
     half8_t (*a_lds)[kFrags][64];
 
-    // arow[i] < 0 (padding rows) reads row 0 with scale 0: branch-free loads.
+    // Buffer loads: per-lane offsets are loop-invariant, the block enters as a
+    // scalar offset.  A block beyond the last re-reads the last one.
+    __device__ __forceinline__ void load_record(int blk, uint32_t& xw, uint32_t& sw) const {
+        blk = blk < nblk ? blk : nblk - 1;
+        xw = __builtin_amdgcn_raw_buffer_load_b32(rec, tau * 4, blk * kRecordBytes, 0);
+        sw = __builtin_amdgcn_raw_buffer_load_b32(rec, kRecordCodeBytes + (p * 16 + r16) * 4, blk * kRecordBytes, 0);
+    }
+
+    // Activation fragments and scales of a block; arow[i] < 0 (padding rows)
+    // reads row 0 with scale 0.
     template <int NT>
-    __device__ __forceinline__ void load(int blk, const int64_t (&arow)[kTilesPerWave], uint32_t& xw, uint32_t& sw,
-                                         half8_t (&bf)[kTilesPerWave], float (&sf)[kTilesPerWave]) const {
-        const uint8_t* rb = rec + (int64_t)blk * kRecordBytes;
-        xw = reinterpret_cast<const uint32_t*>(rb)[tau];
-        sw = reinterpret_cast<const uint32_t*>(rb + kRecordCodeBytes)[p * 16 + r16];
+    __device__ __forceinline__ void load_act(int blk, const int64_t (&arow)[kTilesPerWave],
+                                             half8_t (&bf)[kTilesPerWave], float (&sf)[kTilesPerWave]) const {
+        blk = blk < nblk ? blk : nblk - 1;
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
-            const int64_t r = arow[i] >= 0 ? arow[i] : 0;
-            bf[i] = *reinterpret_cast<const half8_t*>(act + r * Kd + blk * kBlock + kg * 8);
-            const float sv = as[r * nblk + blk];
+            const int r = arow[i] >= 0 ? (int)arow[i] : 0;
+            bf[i] = __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(act, r * Kd * 2 + kg * 16,
+                                                                                        blk * kBlock * 2, 0));
+            const float sv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(as, r * nblk * 4, blk * 4, 0));
             sf[i] = arow[i] >= 0 ? sv : 0.f;
         }
     }
@@ -165,22 +175,28 @@ struct BlockLoop {
     }
 
     // nblk is even (H is a multiple of 128, I of 64): two blocks per
-    // iteration, no exit in between; the last prefetch re-reads the last block.
+    // iteration, no exit in between.  Records (from HBM) are loaded two blocks
+    // ahead, activation fragments (mostly from L2) one block ahead; each load
+    // goes out right after the barrier that frees its registers.
     template <int NT>
     __device__ __forceinline__ void run(const int64_t (&arow)[kTilesPerWave],
                                         float4_t (&acc)[kFrags][kTilesPerWave]) const {
         uint32_t xw0, sw0, xw1, sw1;
         half8_t bf0[kTilesPerWave], bf1[kTilesPerWave];
         float sf0[kTilesPerWave], sf1[kTilesPerWave];
-        load<NT>(0, arow, xw0, sw0, bf0, sf0);
+        load_record(0, xw0, sw0);
+        load_record(1, xw1, sw1);
+        load_act<NT>(0, arow, bf0, sf0);
         for (int b = 0; b < nblk; b += 2) {
             unpack(b, xw0, sw0);
             __syncthreads();
-            load<NT>(b + 1, arow, xw1, sw1, bf1, sf1);
+            load_act<NT>(b + 1, arow, bf1, sf1);
+            load_record(b + 2, xw0, sw0);
             products<NT>(b, bf0, sf0, acc);
             unpack(b + 1, xw1, sw1);
             __syncthreads();
-            load<NT>(b + 2 < nblk ? b + 2 : nblk - 1, arow, xw0, sw0, bf0, sf0);
+            load_act<NT>(b + 2, arow, bf0, sf0);
+            load_record(b + 3, xw1, sw1);
             products<NT>(b + 1, bf1, sf1, acc);
         }
     }
@@ -207,11 +223,8 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_kernel(GemmArgs g) {
     const int nch = (nblk + 31) / 32;
     const int dstride = nch * 32 + 8;
 
-    // zero the padding blocks of the offset-pass matrix
-    for (int i = tau; i < kSlabRows * (nch * 32 - nblk); i += 256) {
-        const int r = i / (nch * 32 - nblk), c = nblk + i % (nch * 32 - nblk);
-        d_lds[r * dstride + c] = (_Float16)0.0f;
-    }
+    // zero the padding blocks of the offset-pass matrix: two threads per row
+    for (int c = nblk + (tau & 1); c < nch * 32; c += 2) d_lds[(tau >> 1) * dstride + c] = (_Float16)0.0f;
 
     // this wave's tiles
     int64_t arow[kTilesPerWave];
@@ -233,7 +246,10 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_kernel(GemmArgs g) {
     for (int f = 0; f < kFrags; ++f)
 #pragma unroll
         for (int i = 0; i < kTilesPerWave; ++i) acc[f][i] = (float4_t){0.f, 0.f, 0.f, 0.f};
-    BlockLoop L{rec, g.act, g.as, g.Kd, nblk, dstride, tau, lane, r16, kg, p, d_lds, a_lds};
+    BlockLoop L{__builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, nblk * kRecordBytes, kBufferWord3),
+                __builtin_amdgcn_make_buffer_rsrc((void*)g.act, (short)0, (int)(g.act_rows * g.Kd * 2), kBufferWord3),
+                __builtin_amdgcn_make_buffer_rsrc((void*)g.as, (short)0, (int)(g.act_rows * nblk * 4), kBufferWord3),
+                g.Kd, nblk, dstride, tau, lane, r16, kg, p, d_lds, a_lds};
     switch (ntw) {  // wave-uniform: the block loop is straight-line code for 1..3 tiles
         case 1: L.run<1>(arow, acc); break;
         case 2: L.run<2>(arow, acc); break;
@@ -305,7 +321,9 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_kernel(GemmArgs g) {
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const float gt = acc[2 * hb + ff][i][v], up = acc[4 + 2 * hb + ff][i][v];
-                        h[ff][v] = gt / (1.0f + expf(-gt)) * up;
+                        // silu(gate) * up; hardware exp and reciprocal (about 2 ulp),
+                        // far inside the rounding-tie tolerance of the int8 H codes
+                        h[ff][v] = gt * up * __builtin_amdgcn_rcpf(1.0f + __expf(-gt));
                         amax = fmaxf(amax, fabsf(h[ff][v]));
                     }
                 amax = fmaxf(amax, __shfl_xor(amax, 16));
@@ -410,11 +428,11 @@ inline unsigned grid_of(int64_t chunks_cap, int32_t nslab) {
 }  // namespace
 
 hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const Tile* chunks, const int32_t* nchunks,
-                          int64_t chunks_cap, const int32_t* src, const _Float16* xq, const float* xs,
+                          int64_t chunks_cap, const int32_t* src, const _Float16* xq, int64_t act_rows, const float* xs,
                           const float* xu, int32_t H, int32_t I, _Float16* hq, float* hs, float* hu,
                           hipStream_t st) {
-    GemmArgs g{blobs, stride, chunks, nchunks, 2 * I / kSlabRows, H, src, nullptr, xq, xs, xu, I, H, hq, hs, hu,
-               nullptr};
+    GemmArgs g{blobs, stride, chunks, nchunks, 2 * I / kSlabRows, H, src, nullptr, xq, act_rows, xs, xu, I, H, hq, hs,
+               hu, nullptr};
     if (chunks_cap > 0)
         hipLaunchKernelGGL(expert_gemm_kernel<true>, dim3(grid_of(chunks_cap, g.nslab)), dim3(256),
                            dynamic_lds_bytes(H, false), st, g);
@@ -422,9 +440,9 @@ hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const Tile* chun
 }
 
 hipError_t launch_down(const uint8_t* blobs, int64_t stride, const Tile* chunks, const int32_t* nchunks,
-                       int64_t chunks_cap, const int32_t* src, const float* prow, const _Float16* hq,
+                       int64_t chunks_cap, const int32_t* src, const float* prow, const _Float16* hq, int64_t act_rows,
                        const float* hs, const float* hu, int32_t H, int32_t I, float* dm, hipStream_t st) {
-    GemmArgs g{blobs, stride, chunks, nchunks, H / kSlabRows, I, src, prow, hq, hs, hu, I, H, nullptr, nullptr,
+    GemmArgs g{blobs, stride, chunks, nchunks, H / kSlabRows, I, src, prow, hq, act_rows, hs, hu, I, H, nullptr, nullptr,
                nullptr, dm};
     if (chunks_cap > 0)
         hipLaunchKernelGGL(expert_gemm_kernel<false>, dim3(grid_of(chunks_cap, g.nslab)), dim3(256),

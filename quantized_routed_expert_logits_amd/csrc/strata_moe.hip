@@ -261,6 +261,15 @@ int check_experts(const strata_moe_experts* ex) {
     return 0;
 }
 
+// The GEMMs address activations with 32-bit buffer offsets: the fp16 codes of
+// the input ([T][H]) and of H ([T*K][I]) must each stay below 2 GiB.
+int check_buffers(int64_t T, int32_t K, int32_t H, int32_t I) {
+    if (T * (int64_t)H * 2 >= ((int64_t)1 << 31) || T * (int64_t)K * I * 2 >= ((int64_t)1 << 31))
+        return fail(STRATA_MOE_EINVAL, "T = %lld too large for one call at H = %d, I = %d, K = %d", (long long)T, H, I,
+                    K);
+    return 0;
+}
+
 int check_tk(int64_t T, int32_t K, int32_t E) {
     if (T < 0) return fail(STRATA_MOE_EINVAL, "T = %lld is negative", (long long)T);
     if (K < 1 || K > kMaxTopK) return fail(STRATA_MOE_EINVAL, "K = %d outside [1, %d]", K, kMaxTopK);
@@ -303,12 +312,12 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     tm.end(kGroup);
     tm.begin(kGateUp);
     HIP_TRY(launch_gate_up((const uint8_t*)ex->gate_up, ex->gate_up_stride, b.tiles, b.ntiles, b.tiles_cap, b.src,
-                           b.xq, b.xs, b.xu, H, I, b.hq, b.hs, b.hu, st),
+                           b.xq, T, b.xs, b.xu, H, I, b.hq, b.hs, b.hu, st),
             "gate/up launch");
     tm.end(kGateUp);
     tm.begin(kDown);
     HIP_TRY(launch_down((const uint8_t*)ex->down, ex->down_stride, b.tiles, b.ntiles, b.tiles_cap, b.src, b.prow,
-                        b.hq, b.hs, b.hu, H, I, b.dm, st),
+                        b.hq, n, b.hs, b.hu, H, I, b.dm, st),
             "down launch");
     tm.end(kDown);
     tm.begin(kCombine);
@@ -346,6 +355,7 @@ int strata_moe_workspace_bytes(int64_t T, int32_t K, const strata_moe_experts* e
     if (!bytes) return fail(STRATA_MOE_EINVAL, "bytes is NULL");
     TRY(check_experts(experts));
     TRY(check_tk(T, K, experts->n_expert));
+    TRY(check_buffers(T, K, experts->hidden, experts->ffn));
     *bytes = plan(T, K, experts->n_expert, experts->hidden, experts->ffn).total;
     return 0;
 }
@@ -413,6 +423,7 @@ int strata_moe_prefill(const float* x, const float* router_w, const strata_moe_e
     g_err.clear();
     TRY(check_experts(experts));
     TRY(check_tk(T, K, experts->n_expert));
+    TRY(check_buffers(T, K, experts->hidden, experts->ffn));
     if (T == 0) return 0;
     if (!x || !router_w || !out) return fail(STRATA_MOE_EINVAL, "null x / router_w / out");
     if (!aligned(x, 16) || !aligned(out, 16)) return fail(STRATA_MOE_EINVAL, "x and out must be 16-byte aligned");
@@ -426,6 +437,7 @@ int strata_moe_prefill_debug(const float* x, const float* router_w, const strata
     g_err.clear();
     TRY(check_experts(experts));
     TRY(check_tk(T, K, experts->n_expert));
+    TRY(check_buffers(T, K, experts->hidden, experts->ffn));
     if (T == 0) return 0;
     if (!x || !router_w || !out || !dbg) return fail(STRATA_MOE_EINVAL, "null x / router_w / out / dbg");
     if (!aligned(x, 16) || !aligned(out, 16)) return fail(STRATA_MOE_EINVAL, "x and out must be 16-byte aligned");
@@ -517,6 +529,7 @@ int strata_moe_gate_up(const int8_t* qx, const float* sx, const int32_t* offsets
     g_err.clear();
     TRY(check_experts(experts));
     TRY(check_tk(T, K, experts->n_expert));
+    TRY(check_buffers(T, K, experts->hidden, experts->ffn));
     if (T == 0) return 0;
     if (!qx || !sx || !offsets || !src || !qh || !sh) return fail(STRATA_MOE_EINVAL, "null pointer");
     TRY(check_device());
@@ -536,7 +549,7 @@ int strata_moe_gate_up(const int8_t* qx, const float* sx, const int32_t* offsets
     HIP_TRY(launch_block_correction(qx, sx, T, H, xu, st), "correction launch");
     HIP_TRY(launch_tiles_from_offsets(offsets, E, (Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), st), "tiles launch");
     HIP_TRY(launch_gate_up((const uint8_t*)experts->gate_up, experts->gate_up_stride, (Tile*)(ws + o_tiles),
-                           (int32_t*)(ws + o_nt), max_tiles(n, E), src, xq, sx, xu, H, I, hq, sh,
+                           (int32_t*)(ws + o_nt), max_tiles(n, E), src, xq, T, sx, xu, H, I, hq, sh,
                            (float*)(ws + o_hu), st),
             "gate/up launch");
     HIP_TRY(launch_f16_to_i8(hq, n * I, qh, st), "convert launch");
@@ -549,6 +562,7 @@ int strata_moe_down(const int8_t* qh, const float* sh, const int32_t* offsets, c
     g_err.clear();
     TRY(check_experts(experts));
     TRY(check_tk(T, K, experts->n_expert));
+    TRY(check_buffers(T, K, experts->hidden, experts->ffn));
     if (T == 0) return 0;
     if (!qh || !sh || !offsets || !src || !slot || !p || !out) return fail(STRATA_MOE_EINVAL, "null pointer");
     TRY(check_device());
@@ -570,7 +584,7 @@ int strata_moe_down(const int8_t* qh, const float* sh, const int32_t* offsets, c
     HIP_TRY(launch_tiles_from_offsets(offsets, E, (Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), st), "tiles launch");
     HIP_TRY(launch_row_weights(slot, p, n, prow, st), "weights launch");
     HIP_TRY(launch_down((const uint8_t*)experts->down, experts->down_stride, (Tile*)(ws + o_tiles),
-                        (int32_t*)(ws + o_nt), max_tiles(n, E), src, prow, hq, sh, hu, H, I, dm, st),
+                        (int32_t*)(ws + o_nt), max_tiles(n, E), src, prow, hq, n, sh, hu, H, I, dm, st),
             "down launch");
     HIP_TRY(launch_combine(dm, slot, T, K, H, out, st), "combine launch");
     return 0;
