@@ -30,10 +30,12 @@ inline int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 inline int64_t max_tiles(int64_t n, int32_t E) { return n / kChunkRows + E; }
 
 // ---- launchers; each returns hipGetLastError() after its launches.
-hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, _Float16* q16, int8_t* q8, float* s,
-                           float* u, float* zero_out, hipStream_t st);
-hipError_t launch_f16_to_i8(const _Float16* v, int64_t count, int8_t* out, hipStream_t st);
-hipError_t launch_i8_to_f16(const int8_t* v, int64_t count, _Float16* out, hipStream_t st);
+hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q8, float* s, float* u,
+                           hipStream_t st);
+// fp16 GEMM operand q * s * 2^-e_r of int8 rows (parts 1: one fp16; 2: hi and
+// lo fp16 per value, block-interleaved) and the row multipliers 2^e_r.
+hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_t cols, int parts, _Float16* out,
+                           float* mult, hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t st);
 
 hipError_t launch_router_logits(const float* x, const float* wr, const float* bias, int64_t T, int32_t H, int32_t E,
@@ -51,13 +53,16 @@ hipError_t launch_tiles_from_offsets(const int32_t* offsets, int32_t E, Tile* ti
                                      hipStream_t st);
 hipError_t launch_row_weights(const int32_t* slot, const float* p, int64_t n, float* prow, hipStream_t st);
 
+// gate/up: xb = prescaled input rows (parts 2), xe = their multipliers, xu =
+// offset terms; writes int8 H codes hq, scales hs and offset terms hu.
 hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const Tile* tiles, const int32_t* ntiles,
-                          int64_t tiles_cap, const int32_t* src, const _Float16* xq, int64_t act_rows, const float* xs,
-                          const float* xu, int32_t H, int32_t I, _Float16* hq, float* hs, float* hu,
-                          hipStream_t st);
+                          int64_t tiles_cap, const int32_t* src, const _Float16* xb, int64_t act_rows, const float* xe,
+                          const float* xu, int32_t H, int32_t I, int8_t* hq, float* hs, float* hu, hipStream_t st);
+// down: hb = prescaled H rows (parts 1), he = their multipliers, hu = offset
+// terms; writes the weighted rows dm.
 hipError_t launch_down(const uint8_t* blobs, int64_t stride, const Tile* tiles, const int32_t* ntiles,
-                       int64_t tiles_cap, const int32_t* src, const float* prow, const _Float16* hq, int64_t act_rows,
-                       const float* hs, const float* hu, int32_t H, int32_t I, float* dm, hipStream_t st);
+                       int64_t tiles_cap, const int32_t* src, const float* prow, const _Float16* hb, int64_t act_rows,
+                       const float* he, const float* hu, int32_t H, int32_t I, float* dm, hipStream_t st);
 hipError_t launch_combine(const float* dm, const int32_t* slot, int64_t T, int32_t K, int32_t H, float* y,
                           hipStream_t st);
 

@@ -12,18 +12,18 @@
 // Arithmetic.  One weight block is 32 codes q of one row with one fp16 scale
 // d, w = d * (q - 1.5); one activation block is 32 int8 codes a with an fp32
 // scale s.  Their contribution to an output is
-//     s * d * sum (q - 1.5) * a = s * [d * sum (q - 1) * a] + d * u,
+//     d * sum (q - 1.5) * (s a) = sum [d (q - 1)] * (s a) + d * u,
 //     u = -0.5 * s * sum(a)  (one value per activation block).
-// The bracket is one v_mfma_f32_16x16x32_f16 (K = 32 = one block): the A
-// operand d*(q-1) is exact in fp16 (q - 1 in {-1, 0, 1, 2}), the B operand
-// holds the integer codes (exact in fp16), products are exact and every
-// partial sum is an integer multiple of d's last place below 2^24 of them, so
-// the fp32 result is exact.  s differs per routed row and block, so it cannot
-// enter the MFMA exactly: one fp32 FMA per output per block applies it.  The
-// d*u terms of all blocks form a small matrix product over the block index
-// (K = Kd/32), done after the block loop on the MFMA unit: A = d (exact in
-// fp16), B = u of each row scaled by a power of two to [-1, 1] and split into
-// a high and a low fp16 part (22 bits).
+// The first sum runs on v_mfma_f32_16x16x32_f16 (K = 32 = one block): the A
+// operand d*(q-1) is exact in fp16 (q - 1 in {-1, 0, 1, 2}); the B operand is
+// the prescaled activation s*a*2^-e of the row (one fp16 for down, a hi and a
+// lo fp16 for gate/up, two MFMAs into the same accumulator), so the block
+// scale needs no vector-ALU multiply and the accumulators run over the whole
+// reduction.  After the loop the results are multiplied by the row's 2^e
+// (exact).  The d*u terms of all blocks form a small matrix product over the
+// block index (K = Kd/32), done after the block loop on the MFMA unit: A = d
+// (exact in fp16), B = u of each row scaled by a power of two to [-1, 1] and
+// split into a high and a low fp16 part (22 bits).
 //
 // Work split.  A workgroup (4 waves) takes one chunk of at most 256 grouped
 // rows of one expert and one 128-row weight slab (8 fragments of 16 rows).
@@ -94,12 +94,12 @@ struct GemmArgs {
     int32_t Kd;            // reduction length (H for gate/up, I for down)
     const int32_t* src;    // token of each grouped row
     const float* prow;     // routing weight of each grouped row (down)
-    const _Float16* act;   // activation codes [rows][Kd] (exact integers)
-    int64_t act_rows;      // rows of act / as / au
-    const float* as;       // activation scales [rows][Kd/32]
+    const _Float16* act;   // prescaled activations [rows][Kd x parts]
+    int64_t act_rows;      // rows of act / am / au
+    const float* am;       // row multipliers 2^e [rows]
     const float* au;       // activation offset terms [rows][Kd/32]
     int32_t I, H;
-    _Float16* hq;          // gate/up: H codes [n][I]
+    int8_t* hq;            // gate/up: H codes [n][I]
     float* hs;             // gate/up: H scales [n][I/32]
     float* hu;             // gate/up: H offset terms [n][I/32]
     float* y;              // down: weighted routed rows dm [n][H]
@@ -107,15 +107,15 @@ struct GemmArgs {
 
 // The K loop over 32-wide blocks.  Per block: every thread unpacks its dword
 // of the slab's record into LDS buffer b&1 (and the two scales into the
-// offset-pass matrix), one barrier, then the wave's NT tiles x 8 fragments of
-// products, fragment-major so that one A fragment and NT results are live at a
-// time.  Two register sets hold the prefetched next block (record dword and
-// scales, activation fragments and scales), alternating, so the loop body has
-// no copies and each load has a block of compute to land.
+// offset-pass matrix), one barrier, then the wave's NT tiles x 8 fragments x
+// P parts of MFMAs, fragment-major so that one A fragment is live at a time.
+// Two register sets hold the prefetched next block (record dword and scales,
+// activation fragments), alternating, so the loop body has no copies and each
+// load has a block of compute to land.
+template <int P>
 struct BlockLoop {
     __amdgpu_buffer_rsrc_t rec;  // this slab's records (nblk x 1280 bytes)
-    __amdgpu_buffer_rsrc_t act;  // activation codes, fp16 [rows][Kd]
-    __amdgpu_buffer_rsrc_t as;   // activation scales [rows][nblk]
+    __amdgpu_buffer_rsrc_t act;  // prescaled activations [rows][Kd x P] fp16
     int32_t Kd, nblk, dstride;
     int tau, lane, r16, kg, p;
     _Float16* d_lds;
@@ -129,19 +129,21 @@ struct BlockLoop {
         sw = __builtin_amdgcn_raw_buffer_load_b32(rec, kRecordCodeBytes + (p * 16 + r16) * 4, blk * kRecordBytes, 0);
     }
 
-    // Activation fragments and scales of a block; arow[i] < 0 (padding rows)
-    // reads row 0 with scale 0.
+    // Activation fragments of a block: lane (r16, kg) takes values 8kg..8kg+7
+    // of its row (P x 16 contiguous bytes).  Padding rows (arow < 0) read row
+    // 0; their results are never stored.
     template <int NT>
     __device__ __forceinline__ void load_act(int blk, const int64_t (&arow)[kTilesPerWave],
-                                             half8_t (&bf)[kTilesPerWave], float (&sf)[kTilesPerWave]) const {
+                                             half8_t (&bf)[kTilesPerWave][P]) const {
         blk = blk < nblk ? blk : nblk - 1;
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
             const int r = arow[i] >= 0 ? (int)arow[i] : 0;
-            bf[i] = __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(act, r * Kd * 2 + kg * 16,
-                                                                                        blk * kBlock * 2, 0));
-            const float sv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(as, r * nblk * 4, blk * 4, 0));
-            sf[i] = arow[i] >= 0 ? sv : 0.f;
+            const int voff = r * Kd * 2 * P + kg * 16 * P;
+#pragma unroll
+            for (int h = 0; h < P; ++h)
+                bf[i][h] = __builtin_bit_cast(
+                    half8_t, __builtin_amdgcn_raw_buffer_load_b128(act, voff + 16 * h, blk * kBlock * 2 * P, 0));
         }
     }
 
@@ -158,19 +160,16 @@ struct BlockLoop {
     }
 
     template <int NT>
-    __device__ __forceinline__ void products(int blk, const half8_t (&bf)[kTilesPerWave],
-                                             const float (&sf)[kTilesPerWave],
+    __device__ __forceinline__ void products(int blk, const half8_t (&bf)[kTilesPerWave][P],
                                              float4_t (&acc)[kFrags][kTilesPerWave]) const {
 #pragma unroll
         for (int f = 0; f < kFrags; ++f) {
             const half8_t a = a_lds[blk & 1][f][lane];
 #pragma unroll
-            for (int i = 0; i < NT; ++i) {
-                const float4_t q =
-                    __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf[i], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            for (int h = 0; h < P; ++h)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) acc[f][i][v] = fmaf(q[v], sf[i], acc[f][i][v]);
-            }
+                for (int i = 0; i < NT; ++i)
+                    acc[f][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf[i][h], acc[f][i], 0, 0, 0);
         }
     }
 
@@ -182,22 +181,21 @@ struct BlockLoop {
     __device__ __forceinline__ void run(const int64_t (&arow)[kTilesPerWave],
                                         float4_t (&acc)[kFrags][kTilesPerWave]) const {
         uint32_t xw0, sw0, xw1, sw1;
-        half8_t bf0[kTilesPerWave], bf1[kTilesPerWave];
-        float sf0[kTilesPerWave], sf1[kTilesPerWave];
+        half8_t bf0[kTilesPerWave][P], bf1[kTilesPerWave][P];
         load_record(0, xw0, sw0);
         load_record(1, xw1, sw1);
-        load_act<NT>(0, arow, bf0, sf0);
+        load_act<NT>(0, arow, bf0);
         for (int b = 0; b < nblk; b += 2) {
             unpack(b, xw0, sw0);
             __syncthreads();
-            load_act<NT>(b + 1, arow, bf1, sf1);
+            load_act<NT>(b + 1, arow, bf1);
             load_record(b + 2, xw0, sw0);
-            products<NT>(b, bf0, sf0, acc);
+            products<NT>(b, bf0, acc);
             unpack(b + 1, xw1, sw1);
             __syncthreads();
-            load_act<NT>(b + 2, arow, bf0, sf0);
+            load_act<NT>(b + 2, arow, bf0);
             load_record(b + 3, xw1, sw1);
-            products<NT>(b + 1, bf1, sf1, acc);
+            products<NT>(b + 1, bf1, acc);
         }
     }
 };
@@ -246,17 +244,29 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_kernel(GemmArgs g) {
     for (int f = 0; f < kFrags; ++f)
 #pragma unroll
         for (int i = 0; i < kTilesPerWave; ++i) acc[f][i] = (float4_t){0.f, 0.f, 0.f, 0.f};
-    BlockLoop L{__builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, nblk * kRecordBytes, kBufferWord3),
-                __builtin_amdgcn_make_buffer_rsrc((void*)g.act, (short)0, (int)(g.act_rows * g.Kd * 2), kBufferWord3),
-                __builtin_amdgcn_make_buffer_rsrc((void*)g.as, (short)0, (int)(g.act_rows * nblk * 4), kBufferWord3),
-                g.Kd, nblk, dstride, tau, lane, r16, kg, p, d_lds, a_lds};
+    constexpr int P = kGateUp ? 2 : 1;
+    BlockLoop<P> L{__builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, nblk * kRecordBytes, kBufferWord3),
+                   __builtin_amdgcn_make_buffer_rsrc((void*)g.act, (short)0, (int)(g.act_rows * g.Kd * 2 * P),
+                                                     kBufferWord3),
+                   g.Kd, nblk, dstride, tau, lane, r16, kg, p, d_lds, a_lds};
     switch (ntw) {  // wave-uniform: the block loop is straight-line code for 1..3 tiles
-        case 1: L.run<1>(arow, acc); break;
-        case 2: L.run<2>(arow, acc); break;
-        case 3: L.run<3>(arow, acc); break;
-        default: L.run<0>(arow, acc); break;  // no tiles: still unpack and meet every barrier
+        case 1: L.template run<1>(arow, acc); break;
+        case 2: L.template run<2>(arow, acc); break;
+        case 3: L.template run<3>(arow, acc); break;
+        default: L.template run<0>(arow, acc); break;  // no tiles: still unpack and meet every barrier
     }
     __syncthreads();  // every d of the slab is in LDS
+
+    // undo the rows' power-of-two prescaling
+#pragma unroll
+    for (int i = 0; i < kTilesPerWave; ++i) {
+        if (i >= ntw) continue;
+        const float mult = arow[i] >= 0 ? g.am[arow[i]] : 0.f;
+#pragma unroll
+        for (int f = 0; f < kFrags; ++f)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[f][i][v] *= mult;
+    }
 
     // offset pass: acc += sum_b d[row][b] * u[tok][b], 32 blocks per MFMA; u of
     // each routed row is scaled by a power of two to [-1, 1] and split into
@@ -342,12 +352,14 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_kernel(GemmArgs g) {
                 qsum += __shfl_xor(qsum, 32);
                 if (r < tl.nrows) {
                     const int64_t row = tl.row0 + r;
-                    _Float16* dst = g.hq + row * g.I + 64 * slab + 32 * hb + 4 * kg;
+                    int8_t* dst = g.hq + row * g.I + 64 * slab + 32 * hb + 4 * kg;
 #pragma unroll
                     for (int ff = 0; ff < 2; ++ff) {
-                        const half4_t hv = {(_Float16)q[ff][0], (_Float16)q[ff][1], (_Float16)q[ff][2],
-                                            (_Float16)q[ff][3]};
-                        *reinterpret_cast<half4_t*>(dst + 16 * ff) = hv;
+                        const uint32_t packed = (uint32_t)(uint8_t)(int8_t)(int)q[ff][0] |
+                                                (uint32_t)(uint8_t)(int8_t)(int)q[ff][1] << 8 |
+                                                (uint32_t)(uint8_t)(int8_t)(int)q[ff][2] << 16 |
+                                                (uint32_t)(uint8_t)(int8_t)(int)q[ff][3] << 24;
+                        *reinterpret_cast<uint32_t*>(dst + 16 * ff) = packed;
                     }
                     if (kg == 0) {
                         g.hs[row * nbi + 2 * slab + hb] = sh;
@@ -428,10 +440,9 @@ inline unsigned grid_of(int64_t chunks_cap, int32_t nslab) {
 }  // namespace
 
 hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const Tile* chunks, const int32_t* nchunks,
-                          int64_t chunks_cap, const int32_t* src, const _Float16* xq, int64_t act_rows, const float* xs,
-                          const float* xu, int32_t H, int32_t I, _Float16* hq, float* hs, float* hu,
-                          hipStream_t st) {
-    GemmArgs g{blobs, stride, chunks, nchunks, 2 * I / kSlabRows, H, src, nullptr, xq, act_rows, xs, xu, I, H, hq, hs,
+                          int64_t chunks_cap, const int32_t* src, const _Float16* xb, int64_t act_rows, const float* xe,
+                          const float* xu, int32_t H, int32_t I, int8_t* hq, float* hs, float* hu, hipStream_t st) {
+    GemmArgs g{blobs, stride, chunks, nchunks, 2 * I / kSlabRows, H, src, nullptr, xb, act_rows, xe, xu, I, H, hq, hs,
                hu, nullptr};
     if (chunks_cap > 0)
         hipLaunchKernelGGL(expert_gemm_kernel<true>, dim3(grid_of(chunks_cap, g.nslab)), dim3(256),
@@ -440,9 +451,9 @@ hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const Tile* chun
 }
 
 hipError_t launch_down(const uint8_t* blobs, int64_t stride, const Tile* chunks, const int32_t* nchunks,
-                       int64_t chunks_cap, const int32_t* src, const float* prow, const _Float16* hq, int64_t act_rows,
-                       const float* hs, const float* hu, int32_t H, int32_t I, float* dm, hipStream_t st) {
-    GemmArgs g{blobs, stride, chunks, nchunks, H / kSlabRows, I, src, prow, hq, act_rows, hs, hu, I, H, nullptr, nullptr,
+                       int64_t chunks_cap, const int32_t* src, const float* prow, const _Float16* hb, int64_t act_rows,
+                       const float* he, const float* hu, int32_t H, int32_t I, float* dm, hipStream_t st) {
+    GemmArgs g{blobs, stride, chunks, nchunks, H / kSlabRows, I, src, prow, hb, act_rows, he, hu, I, H, nullptr, nullptr,
                nullptr, dm};
     if (chunks_cap > 0)
         hipLaunchKernelGGL(expert_gemm_kernel<false>, dim3(grid_of(chunks_cap, g.nslab)), dim3(256),

@@ -1,5 +1,5 @@
-// Per-32 int8 rounding of fp32 rows (the layer input, once per token), plus
-// small conversion kernels.
+// Per-32 int8 rounding of fp32 rows (the layer input, once per token), the
+// prescaled fp16 GEMM operands built from int8 codes, and small helpers.
 //
 // Strata compare v0.1.35...v0.1.37 page, include/strata/prefill/moe_fused.hpp,
 // quantize_act: the activations are rounded to int8 once per token with one
@@ -8,11 +8,26 @@
 // correctly rounded fp32 (IEEE), |q| <= 127, s = 0 and q = 0 for an all-zero
 // block.
 //
-// Layout: 8 lanes cover one block of 32 values, one float4 each, so a wave
-// reads 1 KiB of contiguous input per instruction.  Outputs per block: the
-// codes as exact fp16 integers (the GEMM operand), optionally as int8, the
-// scale, and u = -0.5 * s * (sum of the block's codes), the term the 2-bit
-// weight offset contributes (see k_experts.hip).
+// Quantize layout: 8 lanes cover one block of 32 values, one float4 each, so a
+// wave reads 1 KiB of contiguous input per instruction.  Outputs per block:
+// the int8 codes, the scale, and u = -0.5 * s * (sum of the block's codes),
+// the term the 2-bit weight offset contributes (see k_experts.hip).
+//
+// Prescale: the expert GEMMs take each activation value q * s as an fp16
+// operand, so the per-block scale rides inside the MFMA and no per-block
+// multiply is left on the vector ALU.  A row r is first scaled by 2^-e_r,
+// chosen so that the row's largest possible |q * s| (127 * max s) lands in
+// [2^14, 2^15): fp16 cannot overflow and small values keep their bits.  The
+// row multiplier 2^e_r is written beside the operand; the GEMM multiplies its
+// fp32 results by it (exact).  Two forms:
+//   parts = 1: hi = fp16(q * s * 2^-e), 11 significant bits (the down GEMM,
+//              whose output is not rounded to int8 again);
+//   parts = 2: hi as above and lo = fp16(v - hi), v = fp32(q * s * 2^-e), so
+//              hi + lo carries about 22 bits (the gate/up GEMM, whose output
+//              is rounded to int8 and must not move the rounding points).
+// parts = 2 layout per row: per 32-wide block, 4 groups of 8 values, each
+// stored as 8 hi then 8 lo (128 bytes per block), so the 32 bytes one MFMA
+// lane needs for a block (its 8 values, hi and lo) are contiguous.
 #include "internal.h"
 
 namespace strata_moe {
@@ -25,9 +40,8 @@ __device__ __forceinline__ float round_half_away(float t) {
 }
 
 __global__ void __launch_bounds__(256) quantize_kernel(const float4* __restrict__ v, int64_t n4,
-                                                       _Float16* __restrict__ q16, int8_t* __restrict__ q8,
-                                                       float* __restrict__ s_out, float* __restrict__ u_out,
-                                                       float4* __restrict__ zero_out) {
+                                                       int8_t* __restrict__ q8, float* __restrict__ s_out,
+                                                       float* __restrict__ u_out) {
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const bool valid = g < n4;
     const float4 x = valid ? v[g] : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -48,12 +62,7 @@ __global__ void __launch_bounds__(256) quantize_kernel(const float4* __restrict_
     sum += __shfl_xor(sum, 2);
     sum += __shfl_xor(sum, 4);
     if (!valid) return;
-    typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-    if (q16) {
-        half4_t h = {(_Float16)q[0], (_Float16)q[1], (_Float16)q[2], (_Float16)q[3]};
-        reinterpret_cast<half4_t*>(q16)[g] = h;
-    }
-    if (q8) {
+    {
         const uint32_t packed = ((uint32_t)(uint8_t)(int8_t)(int)q[0]) | ((uint32_t)(uint8_t)(int8_t)(int)q[1] << 8) |
                                 ((uint32_t)(uint8_t)(int8_t)(int)q[2] << 16) | ((uint32_t)(uint8_t)(int8_t)(int)q[3] << 24);
         reinterpret_cast<uint32_t*>(q8)[g] = packed;
@@ -62,17 +71,76 @@ __global__ void __launch_bounds__(256) quantize_kernel(const float4* __restrict_
         s_out[g >> 3] = s;
         if (u_out) u_out[g >> 3] = -0.5f * s * (float)sum;
     }
-    if (zero_out) zero_out[g] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-__global__ void f16_to_i8_kernel(const _Float16* __restrict__ v, int64_t count, int8_t* __restrict__ out) {
-    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (g < count) out[g] = (int8_t)(int)v[g];
-}
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 
-__global__ void i8_to_f16_kernel(const int8_t* __restrict__ v, int64_t count, _Float16* __restrict__ out) {
-    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (g < count) out[g] = (_Float16)(int)v[g];
+// One wave per row: the row multiplier from the block scales, then 16 codes
+// per lane per step (16 contiguous bytes in, 32 or 64 contiguous bytes out).
+template <int P>
+__global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict__ q, const float* __restrict__ s,
+                                                       int64_t rows, int32_t cols, _Float16* __restrict__ out,
+                                                       float* __restrict__ mult) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;  // wave-uniform; the kernel has no barrier
+    const int lane = threadIdx.x & 63;
+    const int nb = cols / kBlock;
+    const float* srow = s + row * nb;
+    float m = 0.0f;
+    for (int b = lane; b < nb; b += 64) m = fmaxf(m, srow[b]);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    const float bound = 127.0f * m;  // >= every |q * s| of the row
+    float scale = 1.0f, back = 1.0f;
+    if (bound > 0.0f) {
+        int ex = 0;
+        frexpf(bound, &ex);          // bound in [2^(ex-1), 2^ex)
+        ex = ex < -96 ? -96 : ex;    // keeps 2^(15-ex) finite
+        scale = ldexpf(1.0f, 15 - ex);
+        back = ldexpf(1.0f, ex - 15);
+    }
+    if (lane == 0) mult[row] = back;
+    const int8_t* qrow = q + row * cols;
+    for (int j = lane; j < cols / 16; j += 64) {
+        const uint4 w = *reinterpret_cast<const uint4*>(qrow + 16 * j);
+        const float sj = srow[j >> 1] * scale;  // exact: a power-of-two scaling
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            v[i] = (float)(int8_t)(ws[i >> 2] >> (8 * (i & 3))) * sj;
+            // v is the fp32-rounded product: without this barrier the compiler
+            // fuses multiply and fp16 conversion (one rounding), and hi can then
+            // differ by one ulp from the hi that lo is measured against when the
+            // fp32 product sits on an fp16 rounding tie.
+            asm volatile("" : "+v"(v[i]));
+        }
+        if constexpr (P == 1) {
+            half8_t h0, h1;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                h0[i] = (_Float16)v[i];
+                h1[i] = (_Float16)v[8 + i];
+            }
+            half8_t* dst = reinterpret_cast<half8_t*>(out + row * cols + 16 * j);
+            dst[0] = h0;
+            dst[1] = h1;
+        } else {
+            half8_t g[4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const _Float16 hi = (_Float16)v[8 * h + i];
+                    g[2 * h][i] = hi;
+                    g[2 * h + 1][i] = (_Float16)(v[8 * h + i] - (float)hi);
+                }
+            // block j/2, value groups 2*(j%2) and 2*(j%2)+1: 64 contiguous bytes
+            half8_t* dst = reinterpret_cast<half8_t*>(out + row * (int64_t)cols * 2 + 32 * j);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) dst[t] = g[t];
+        }
+    }
 }
 
 __global__ void fill_zero_kernel(float* __restrict__ p, int64_t count) {
@@ -94,23 +162,25 @@ inline unsigned grid_for(int64_t n, int threads) { return (unsigned)((n + thread
 
 }  // namespace
 
-hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, _Float16* q16, int8_t* q8, float* s, float* u,
-                           float* zero_out, hipStream_t st) {
+hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q8, float* s, float* u,
+                           hipStream_t st) {
     const int64_t n4 = rows * cols / 4;
     if (n4 > 0)
         hipLaunchKernelGGL(quantize_kernel, dim3(grid_for(n4, 256)), dim3(256), 0, st,
-                           reinterpret_cast<const float4*>(v), n4, q16, q8, s, u,
-                           reinterpret_cast<float4*>(zero_out));
+                           reinterpret_cast<const float4*>(v), n4, q8, s, u);
     return hipGetLastError();
 }
 
-hipError_t launch_f16_to_i8(const _Float16* v, int64_t count, int8_t* out, hipStream_t st) {
-    if (count > 0) hipLaunchKernelGGL(f16_to_i8_kernel, dim3(grid_for(count, 256)), dim3(256), 0, st, v, count, out);
-    return hipGetLastError();
-}
-
-hipError_t launch_i8_to_f16(const int8_t* v, int64_t count, _Float16* out, hipStream_t st) {
-    if (count > 0) hipLaunchKernelGGL(i8_to_f16_kernel, dim3(grid_for(count, 256)), dim3(256), 0, st, v, count, out);
+hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_t cols, int parts, _Float16* out,
+                           float* mult, hipStream_t st) {
+    if (rows > 0) {
+        if (parts == 2)
+            hipLaunchKernelGGL(prescale_kernel<2>, dim3(grid_for(rows, 4)), dim3(256), 0, st, q, s, rows, cols, out,
+                               mult);
+        else
+            hipLaunchKernelGGL(prescale_kernel<1>, dim3(grid_for(rows, 4)), dim3(256), 0, st, q, s, rows, cols, out,
+                               mult);
+    }
     return hipGetLastError();
 }
 

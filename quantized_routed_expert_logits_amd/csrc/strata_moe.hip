@@ -117,9 +117,11 @@ struct Buffers {
     float* logits;
     int32_t* ids;
     float* p;
-    _Float16* xq;
+    int8_t* xq;
     float* xs;
     float* xu;
+    _Float16* xb;
+    float* xe;
     int32_t* hist;
     int32_t* base;
     int32_t* offsets;
@@ -129,15 +131,18 @@ struct Buffers {
     int32_t* src;
     int32_t* slot;
     float* prow;
-    _Float16* hq;
+    int8_t* hq;
     float* hs;
     float* hu;
+    _Float16* hb;
+    float* he;
     float* dm;
     int64_t tiles_cap;
 };
 
 struct Offsets {
-    size_t logits, ids, p, xq, xs, xu, hist, base, offsets, tiles, ntiles, err, src, slot, prow, hq, hs, hu, dm, total;
+    size_t logits, ids, p, xq, xs, xu, xb, xe, hist, base, offsets, tiles, ntiles, err, src, slot, prow, hq, hs, hu, hb,
+        he, dm, total;
     int64_t tiles_cap;
 };
 
@@ -150,9 +155,11 @@ Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I) {
     o.logits = L.take<float>(T * E);
     o.ids = L.take<int32_t>(n);
     o.p = L.take<float>(n);
-    o.xq = L.take<_Float16>(T * H);
+    o.xq = L.take<int8_t>(T * H);
     o.xs = L.take<float>(T * (H / kBlock));
     o.xu = L.take<float>(T * (H / kBlock));
+    o.xb = L.take<_Float16>(2 * T * H);
+    o.xe = L.take<float>(T);
     o.hist = L.take<int32_t>(nchunks * E);
     o.base = L.take<int32_t>(nchunks * E);
     o.offsets = L.take<int32_t>(E + 1);
@@ -162,9 +169,11 @@ Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I) {
     o.src = L.take<int32_t>(n);
     o.slot = L.take<int32_t>(n);
     o.prow = L.take<float>(n);
-    o.hq = L.take<_Float16>(n * I);
+    o.hq = L.take<int8_t>(n * I);
     o.hs = L.take<float>(n * (I / kBlock));
     o.hu = L.take<float>(n * (I / kBlock));
+    o.hb = L.take<_Float16>(n * I);
+    o.he = L.take<float>(n);
     o.dm = L.take<float>(n * H);
     o.total = L.off;
     return o;
@@ -175,9 +184,11 @@ Buffers carve(char* ws, const Offsets& o) {
     b.logits = (float*)(ws + o.logits);
     b.ids = (int32_t*)(ws + o.ids);
     b.p = (float*)(ws + o.p);
-    b.xq = (_Float16*)(ws + o.xq);
+    b.xq = (int8_t*)(ws + o.xq);
     b.xs = (float*)(ws + o.xs);
     b.xu = (float*)(ws + o.xu);
+    b.xb = (_Float16*)(ws + o.xb);
+    b.xe = (float*)(ws + o.xe);
     b.hist = (int32_t*)(ws + o.hist);
     b.base = (int32_t*)(ws + o.base);
     b.offsets = (int32_t*)(ws + o.offsets);
@@ -187,17 +198,20 @@ Buffers carve(char* ws, const Offsets& o) {
     b.src = (int32_t*)(ws + o.src);
     b.slot = (int32_t*)(ws + o.slot);
     b.prow = (float*)(ws + o.prow);
-    b.hq = (_Float16*)(ws + o.hq);
+    b.hq = (int8_t*)(ws + o.hq);
     b.hs = (float*)(ws + o.hs);
     b.hu = (float*)(ws + o.hu);
+    b.hb = (_Float16*)(ws + o.hb);
+    b.he = (float*)(ws + o.he);
     b.dm = (float*)(ws + o.dm);
     b.tiles_cap = o.tiles_cap;
     return b;
 }
 
 // ----------------------------------------------------------------- timing
-enum Kind { kQuantize, kRouter, kTopK, kGroup, kGateUp, kDown, kCombine, kNumKinds };
-const char* const kKindNames[kNumKinds] = {"quantize", "router_gemm", "topk", "group", "gate_up", "down", "combine"};
+enum Kind { kQuantize, kRouter, kTopK, kGroup, kGateUp, kPrescaleH, kDown, kCombine, kNumKinds };
+const char* const kKindNames[kNumKinds] = {"quantize", "router_gemm", "topk",  "group",
+                                           "gate_up",  "prescale_h",  "down",  "combine"};
 
 struct Timing {
     bool on = false;
@@ -261,10 +275,11 @@ int check_experts(const strata_moe_experts* ex) {
     return 0;
 }
 
-// The GEMMs address activations with 32-bit buffer offsets: the fp16 codes of
-// the input ([T][H]) and of H ([T*K][I]) must each stay below 2 GiB.
+// The GEMMs address activations with 32-bit buffer offsets: the prescaled
+// input ([T][H], hi and lo fp16) and H ([T*K][I], fp16) must each stay below
+// 2 GiB.
 int check_buffers(int64_t T, int32_t K, int32_t H, int32_t I) {
-    if (T * (int64_t)H * 2 >= ((int64_t)1 << 31) || T * (int64_t)K * I * 2 >= ((int64_t)1 << 31))
+    if (T * (int64_t)H * 4 >= ((int64_t)1 << 31) || T * (int64_t)K * I * 2 >= ((int64_t)1 << 31))
         return fail(STRATA_MOE_EINVAL, "T = %lld too large for one call at H = %d, I = %d, K = %d", (long long)T, H, I,
                     K);
     return 0;
@@ -296,7 +311,8 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     Buffers b = carve(ws, o);
     CallTimer tm(st);
     tm.begin(kQuantize);
-    HIP_TRY(launch_quantize(x, T, H, b.xq, nullptr, b.xs, b.xu, nullptr, st), "quantize launch");
+    HIP_TRY(launch_quantize(x, T, H, b.xq, b.xs, b.xu, st), "quantize launch");
+    HIP_TRY(launch_prescale(b.xq, b.xs, T, H, 2, b.xb, b.xe, st), "prescale launch");
     tm.end(kQuantize);
     tm.begin(kRouter);
     HIP_TRY(launch_router_logits(x, wr, ex->router_bias, T, H, E, b.logits, st), "router launch");
@@ -312,12 +328,15 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     tm.end(kGroup);
     tm.begin(kGateUp);
     HIP_TRY(launch_gate_up((const uint8_t*)ex->gate_up, ex->gate_up_stride, b.tiles, b.ntiles, b.tiles_cap, b.src,
-                           b.xq, T, b.xs, b.xu, H, I, b.hq, b.hs, b.hu, st),
+                           b.xb, T, b.xe, b.xu, H, I, b.hq, b.hs, b.hu, st),
             "gate/up launch");
     tm.end(kGateUp);
+    tm.begin(kPrescaleH);
+    HIP_TRY(launch_prescale(b.hq, b.hs, n, I, 1, b.hb, b.he, st), "prescale launch");
+    tm.end(kPrescaleH);
     tm.begin(kDown);
     HIP_TRY(launch_down((const uint8_t*)ex->down, ex->down_stride, b.tiles, b.ntiles, b.tiles_cap, b.src, b.prow,
-                        b.hq, n, b.hs, b.hu, H, I, b.dm, st),
+                        b.hb, n, b.he, b.hu, H, I, b.dm, st),
             "down launch");
     tm.end(kDown);
     tm.begin(kCombine);
@@ -459,8 +478,8 @@ int strata_moe_prefill_debug(const float* x, const float* router_w, const strata
     TRY(cp(dbg->slot, b.slot, n * 4));
     TRY(cp(dbg->sx, b.xs, T * (H / kBlock) * 4));
     TRY(cp(dbg->sh, b.hs, n * (I / kBlock) * 4));
-    if (dbg->qx) HIP_TRY(launch_f16_to_i8(b.xq, T * H, dbg->qx, st), "convert launch");
-    if (dbg->qh) HIP_TRY(launch_f16_to_i8(b.hq, n * I, dbg->qh, st), "convert launch");
+    TRY(cp(dbg->qx, b.xq, T * H));
+    TRY(cp(dbg->qh, b.hq, n * I));
     return 0;
 }
 
@@ -519,8 +538,7 @@ int strata_moe_quantize(const float* v, int64_t rows, int32_t cols, int8_t* code
     if (!v || !codes || !scales) return fail(STRATA_MOE_EINVAL, "null pointer");
     if (!aligned(v, 16) || !aligned(codes, 4)) return fail(STRATA_MOE_EINVAL, "v must be 16-, codes 4-byte aligned");
     TRY(check_device());
-    HIP_TRY(launch_quantize(v, rows, cols, nullptr, codes, scales, nullptr, nullptr, (hipStream_t)stream),
-            "quantize launch");
+    HIP_TRY(launch_quantize(v, rows, cols, codes, scales, nullptr, (hipStream_t)stream), "quantize launch");
     return 0;
 }
 
@@ -537,22 +555,21 @@ int strata_moe_gate_up(const int8_t* qx, const float* sx, const int32_t* offsets
     const int32_t E = experts->n_expert, H = experts->hidden, I = experts->ffn;
     const int64_t n = T * K;
     Layout L;
-    const size_t o_xq = L.take<_Float16>(T * H), o_xu = L.take<float>(T * (H / kBlock));
+    const size_t o_xb = L.take<_Float16>(2 * T * H), o_xe = L.take<float>(T), o_xu = L.take<float>(T * (H / kBlock));
     const size_t o_tiles = L.take<Tile>(max_tiles(n, E)), o_nt = L.take<int32_t>(1);
-    const size_t o_hq = L.take<_Float16>(n * I), o_hu = L.take<float>(n * (I / kBlock));
+    const size_t o_hu = L.take<float>(n * (I / kBlock));
     char* ws = nullptr;
     TRY(get_workspace(L.off, &ws));
-    _Float16* xq = (_Float16*)(ws + o_xq);
+    _Float16* xb = (_Float16*)(ws + o_xb);
+    float* xe = (float*)(ws + o_xe);
     float* xu = (float*)(ws + o_xu);
-    _Float16* hq = (_Float16*)(ws + o_hq);
-    HIP_TRY(launch_i8_to_f16(qx, T * H, xq, st), "convert launch");
+    HIP_TRY(launch_prescale(qx, sx, T, H, 2, xb, xe, st), "prescale launch");
     HIP_TRY(launch_block_correction(qx, sx, T, H, xu, st), "correction launch");
     HIP_TRY(launch_tiles_from_offsets(offsets, E, (Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), st), "tiles launch");
     HIP_TRY(launch_gate_up((const uint8_t*)experts->gate_up, experts->gate_up_stride, (Tile*)(ws + o_tiles),
-                           (int32_t*)(ws + o_nt), max_tiles(n, E), src, xq, T, sx, xu, H, I, hq, sh,
+                           (int32_t*)(ws + o_nt), max_tiles(n, E), src, xb, T, xe, xu, H, I, qh, sh,
                            (float*)(ws + o_hu), st),
             "gate/up launch");
-    HIP_TRY(launch_f16_to_i8(hq, n * I, qh, st), "convert launch");
     return 0;
 }
 
@@ -570,21 +587,22 @@ int strata_moe_down(const int8_t* qh, const float* sh, const int32_t* offsets, c
     const int32_t E = experts->n_expert, H = experts->hidden, I = experts->ffn;
     const int64_t n = T * K;
     Layout L;
-    const size_t o_hq = L.take<_Float16>(n * I), o_hu = L.take<float>(n * (I / kBlock));
+    const size_t o_hb = L.take<_Float16>(n * I), o_he = L.take<float>(n), o_hu = L.take<float>(n * (I / kBlock));
     const size_t o_tiles = L.take<Tile>(max_tiles(n, E)), o_nt = L.take<int32_t>(1), o_prow = L.take<float>(n);
     const size_t o_dm = L.take<float>(n * H);
     char* ws = nullptr;
     TRY(get_workspace(L.off, &ws));
-    _Float16* hq = (_Float16*)(ws + o_hq);
+    _Float16* hb = (_Float16*)(ws + o_hb);
+    float* he = (float*)(ws + o_he);
     float* hu = (float*)(ws + o_hu);
     float* prow = (float*)(ws + o_prow);
     float* dm = (float*)(ws + o_dm);
-    HIP_TRY(launch_i8_to_f16(qh, n * I, hq, st), "convert launch");
+    HIP_TRY(launch_prescale(qh, sh, n, I, 1, hb, he, st), "prescale launch");
     HIP_TRY(launch_block_correction(qh, sh, n, I, hu, st), "correction launch");
     HIP_TRY(launch_tiles_from_offsets(offsets, E, (Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), st), "tiles launch");
     HIP_TRY(launch_row_weights(slot, p, n, prow, st), "weights launch");
     HIP_TRY(launch_down((const uint8_t*)experts->down, experts->down_stride, (Tile*)(ws + o_tiles),
-                        (int32_t*)(ws + o_nt), max_tiles(n, E), src, prow, hq, n, sh, hu, H, I, dm, st),
+                        (int32_t*)(ws + o_nt), max_tiles(n, E), src, prow, hb, n, he, hu, H, I, dm, st),
             "down launch");
     HIP_TRY(launch_combine(dm, slot, T, K, H, out, st), "combine launch");
     return 0;
