@@ -29,13 +29,18 @@ inline int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 // Upper bound of the chunk count of n grouped rows over E experts.
 inline int64_t max_tiles(int64_t n, int32_t E) { return n / kChunkRows + E; }
 
+// fp16 values per row of the offset-pass operand of a reduction length Kd:
+// 32-block chunks, hi and lo per block.
+inline int64_t offset_operand_halves(int32_t Kd) { return (int64_t)((Kd / kBlock + 31) / 32) * 64; }
+
 // ---- launchers; each returns hipGetLastError() after its launches.
-hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q8, float* s, float* u,
-                           hipStream_t st);
+hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q8, float* s, hipStream_t st);
 // fp16 GEMM operand q * s * 2^-e_r of int8 rows (parts 1: one fp16; 2: hi and
-// lo fp16 per value, block-interleaved) and the row multipliers 2^e_r.
+// lo fp16 per value, block-interleaved) and the row multipliers 2^e_r; plus
+// the offset-pass operand (u per block, hi/lo, [rows][offset_operand_halves])
+// and its row multipliers.
 hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_t cols, int parts, _Float16* out,
-                           float* mult, hipStream_t st);
+                           float* mult, _Float16* uop, float* umult, hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t st);
 
 hipError_t launch_router_logits(const float* x, const float* wr, const float* bias, int64_t T, int32_t H, int32_t E,
@@ -46,23 +51,23 @@ hipError_t launch_topk(const float* logits, const float* x, const float* wr, con
 hipError_t launch_group(const int32_t* ids, const float* p, int64_t n, int32_t K, int32_t E, int32_t* hist,
                         int32_t* base, int32_t* offsets, Tile* tiles, int32_t* ntiles, int32_t* src, int32_t* slot,
                         float* prow, int32_t* err, hipStream_t st);
-// The correction term of each (row, block) of H codes, from codes and scales (for injected H codes).
-hipError_t launch_block_correction(const int8_t* q, const float* s, int64_t rows, int32_t cols, float* u,
-                                   hipStream_t st);
 hipError_t launch_tiles_from_offsets(const int32_t* offsets, int32_t E, Tile* tiles, int32_t* ntiles,
                                      hipStream_t st);
 hipError_t launch_row_weights(const int32_t* slot, const float* p, int64_t n, float* prow, hipStream_t st);
 
-// gate/up: xb = prescaled input rows (parts 2), xe = their multipliers, xu =
-// offset terms; writes int8 H codes hq, scales hs and offset terms hu.
+// gate/up: xb = prescaled input rows (parts 2), xe = their multipliers,
+// xuop / xum = offset-pass operand and multipliers; writes int8 H codes hq and
+// scales hs.
 hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const Tile* tiles, const int32_t* ntiles,
                           int64_t tiles_cap, const int32_t* src, const _Float16* xb, int64_t act_rows, const float* xe,
-                          const float* xu, int32_t H, int32_t I, int8_t* hq, float* hs, float* hu, hipStream_t st);
-// down: hb = prescaled H rows (parts 1), he = their multipliers, hu = offset
-// terms; writes the weighted rows dm.
+                          const _Float16* xuop, const float* xum, int32_t H, int32_t I, int8_t* hq, float* hs,
+                          hipStream_t st);
+// down: hb = prescaled H rows (parts 1), he = their multipliers, huop / hum =
+// offset-pass operand and multipliers; writes the weighted rows dm.
 hipError_t launch_down(const uint8_t* blobs, int64_t stride, const Tile* tiles, const int32_t* ntiles,
                        int64_t tiles_cap, const int32_t* src, const float* prow, const _Float16* hb, int64_t act_rows,
-                       const float* he, const float* hu, int32_t H, int32_t I, float* dm, hipStream_t st);
+                       const float* he, const _Float16* huop, const float* hum, int32_t H, int32_t I, float* dm,
+                       hipStream_t st);
 hipError_t launch_combine(const float* dm, const int32_t* slot, int64_t T, int32_t K, int32_t H, float* y,
                           hipStream_t st);
 

@@ -95,20 +95,20 @@ struct GemmArgs {
     const int32_t* src;    // token of each grouped row
     const float* prow;     // routing weight of each grouped row (down)
     const _Float16* act;   // prescaled activations [rows][Kd x parts]
-    int64_t act_rows;      // rows of act / am / au
+    int64_t act_rows;      // rows of act / am / uop / um
     const float* am;       // row multipliers 2^e [rows]
-    const float* au;       // activation offset terms [rows][Kd/32]
+    const _Float16* uop;   // offset-pass operand [rows][nch x 32 blocks x 2] (hi, lo)
+    const float* um;       // its row multipliers [rows]
     int32_t I, H;
     int8_t* hq;            // gate/up: H codes [n][I]
     float* hs;             // gate/up: H scales [n][I/32]
-    float* hu;             // gate/up: H offset terms [n][I/32]
     float* y;              // down: weighted routed rows dm [n][H]
 };
 
 // The K loop over 32-wide blocks.  Per block: every thread unpacks its dword
 // of the slab's record into LDS buffer b&1 (and the two scales into the
 // offset-pass matrix), one barrier, then the wave's NT tiles x 8 fragments x
-// P parts of MFMAs, fragment-major so that one A fragment is live at a time.
+// P parts of MFMAs, fragment-major.
 // Two register sets hold the prefetched next block (record dword and scales,
 // activation fragments), alternating, so the loop body has no copies and each
 // load has a block of compute to land.
@@ -162,15 +162,19 @@ struct BlockLoop {
     template <int NT>
     __device__ __forceinline__ void products(int blk, const half8_t (&bf)[kTilesPerWave][P],
                                              float4_t (&acc)[kFrags][kTilesPerWave]) const {
+        // all A fragments of the block first: the MFMA stream then waits on
+        // LDS only until each fragment lands, never between fragments
+        half8_t a[kFrags];
 #pragma unroll
-        for (int f = 0; f < kFrags; ++f) {
-            const half8_t a = a_lds[blk & 1][f][lane];
+        for (int f = 0; f < kFrags; ++f) a[f] = a_lds[blk & 1][f][lane];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int f = 0; f < kFrags; ++f)
 #pragma unroll
             for (int h = 0; h < P; ++h)
 #pragma unroll
                 for (int i = 0; i < NT; ++i)
-                    acc[f][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf[i][h], acc[f][i], 0, 0, 0);
-        }
+                    acc[f][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[f], bf[i][h], acc[f][i], 0, 0, 0);
     }
 
     // nblk is even (H is a multiple of 128, I of 64): two blocks per
@@ -182,19 +186,28 @@ struct BlockLoop {
                                         float4_t (&acc)[kFrags][kTilesPerWave]) const {
         uint32_t xw0, sw0, xw1, sw1;
         half8_t bf0[kTilesPerWave][P], bf1[kTilesPerWave][P];
+        // Issue order matters: each unpack waits for its record with a vmcnt
+        // that counts the loads issued after it.  Records first here, as in
+        // the loop (a record is always followed by exactly one block of
+        // activation loads and one record), so the loop header's count holds
+        // on entry too; otherwise the header waits for every load in flight.
         load_record(0, xw0, sw0);
         load_record(1, xw1, sw1);
+        __builtin_amdgcn_sched_barrier(0);
         load_act<NT>(0, arow, bf0);
+        __builtin_amdgcn_sched_barrier(0);
         for (int b = 0; b < nblk; b += 2) {
             unpack(b, xw0, sw0);
             __syncthreads();
             load_act<NT>(b + 1, arow, bf1);
             load_record(b + 2, xw0, sw0);
+            __builtin_amdgcn_sched_barrier(0);  // loads go out before the MFMAs
             products<NT>(b, bf0, acc);
             unpack(b + 1, xw1, sw1);
             __syncthreads();
             load_act<NT>(b + 2, arow, bf0);
             load_record(b + 3, xw1, sw1);
+            __builtin_amdgcn_sched_barrier(0);
             products<NT>(b + 1, bf1, acc);
         }
     }
@@ -268,51 +281,40 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_kernel(GemmArgs g) {
             for (int v = 0; v < 4; ++v) acc[f][i][v] *= mult;
     }
 
-    // offset pass: acc += sum_b d[row][b] * u[tok][b], 32 blocks per MFMA; u of
-    // each routed row is scaled by a power of two to [-1, 1] and split into
-    // two fp16 parts (first sweep: the row's max |u|; second: the products).
+    // offset pass: acc += 2^eu * sum_b d[row][b] * u'[row][b], 32 blocks per
+    // MFMA, u' = u * 2^-eu as hi and lo fp16 (prepared with the activations,
+    // zero-padded to whole chunks of 32 blocks, like the zeroed d padding).
 #pragma unroll
     for (int i = 0; i < kTilesPerWave; ++i) {
         if (i >= ntw) continue;
-        const float* urow = g.au + (arow[i] >= 0 ? arow[i] : 0) * nblk;
-        const bool valid = arow[i] >= 0;
-        float m = 0.f;
-        for (int c = 0; c < nch; ++c)
+        const int64_t ar = arow[i] >= 0 ? arow[i] : 0;
+        const half8_t* urow = reinterpret_cast<const half8_t*>(g.uop + ar * nch * 64) + 2 * kg;
+        half8_t ub[kMaxOffsetChunks][2];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int blk = 32 * c + 8 * kg + j;
-                if (valid && blk < nblk) m = fmaxf(m, fabsf(urow[blk]));
+        for (int c = 0; c < kMaxOffsetChunks; ++c)
+            if (c < nch) {
+                ub[c][0] = urow[8 * c];
+                ub[c][1] = urow[8 * c + 1];
             }
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
-        int ex = 0;
-        if (m > 0.f) frexpf(m, &ex);
-        const float down_scale = ldexpf(1.0f, -ex), up_scale = ldexpf(1.0f, ex);
         float4_t corr[kFrags];
 #pragma unroll
         for (int f = 0; f < kFrags; ++f) corr[f] = (float4_t){0.f, 0.f, 0.f, 0.f};
-        for (int c = 0; c < nch; ++c) {
-            half8_t bhi, blo;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int blk = 32 * c + 8 * kg + j;
-                const float un = (valid && blk < nblk) ? urow[blk] * down_scale : 0.f;
-                const _Float16 h = (_Float16)un;
-                bhi[j] = h;
-                blo[j] = (_Float16)(un - (float)h);
-            }
+        for (int c = 0; c < kMaxOffsetChunks; ++c) {
+            if (c >= nch) break;
 #pragma unroll
             for (int f = 0; f < kFrags; ++f) {
                 const half8_t da =
                     *reinterpret_cast<const half8_t*>(&d_lds[(16 * f + r16) * dstride + 32 * c + 8 * kg]);
-                corr[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(da, bhi, corr[f], 0, 0, 0);
-                corr[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(da, blo, corr[f], 0, 0, 0);
+                corr[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(da, ub[c][0], corr[f], 0, 0, 0);
+                corr[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(da, ub[c][1], corr[f], 0, 0, 0);
             }
         }
+        const float up = arow[i] >= 0 ? g.um[arow[i]] : 0.f;
 #pragma unroll
         for (int f = 0; f < kFrags; ++f)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[f][i][v] = fmaf(corr[f][v], up_scale, acc[f][i][v]);
+            for (int v = 0; v < 4; ++v) acc[f][i][v] = fmaf(corr[f][v], up, acc[f][i][v]);
     }
 
     if constexpr (kGateUp) {
@@ -340,16 +342,10 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_kernel(GemmArgs g) {
                 amax = fmaxf(amax, __shfl_xor(amax, 32));
                 const float sh = amax / 127.0f;
                 float q[2][4];
-                int qsum = 0;
 #pragma unroll
                 for (int ff = 0; ff < 2; ++ff)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        q[ff][v] = sh != 0.0f ? round_half_away(h[ff][v] / sh) : 0.0f;
-                        qsum += (int)q[ff][v];
-                    }
-                qsum += __shfl_xor(qsum, 16);
-                qsum += __shfl_xor(qsum, 32);
+                    for (int v = 0; v < 4; ++v) q[ff][v] = sh != 0.0f ? round_half_away(h[ff][v] / sh) : 0.0f;
                 if (r < tl.nrows) {
                     const int64_t row = tl.row0 + r;
                     int8_t* dst = g.hq + row * g.I + 64 * slab + 32 * hb + 4 * kg;
@@ -361,10 +357,7 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_kernel(GemmArgs g) {
                                                 (uint32_t)(uint8_t)(int8_t)(int)q[ff][3] << 24;
                         *reinterpret_cast<uint32_t*>(dst + 16 * ff) = packed;
                     }
-                    if (kg == 0) {
-                        g.hs[row * nbi + 2 * slab + hb] = sh;
-                        g.hu[row * nbi + 2 * slab + hb] = -0.5f * sh * (float)qsum;
-                    }
+                    if (kg == 0) g.hs[row * nbi + 2 * slab + hb] = sh;
                 }
             }
         }
@@ -441,9 +434,10 @@ inline unsigned grid_of(int64_t chunks_cap, int32_t nslab) {
 
 hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const Tile* chunks, const int32_t* nchunks,
                           int64_t chunks_cap, const int32_t* src, const _Float16* xb, int64_t act_rows, const float* xe,
-                          const float* xu, int32_t H, int32_t I, int8_t* hq, float* hs, float* hu, hipStream_t st) {
-    GemmArgs g{blobs, stride, chunks, nchunks, 2 * I / kSlabRows, H, src, nullptr, xb, act_rows, xe, xu, I, H, hq, hs,
-               hu, nullptr};
+                          const _Float16* xuop, const float* xum, int32_t H, int32_t I, int8_t* hq, float* hs,
+                          hipStream_t st) {
+    GemmArgs g{blobs, stride, chunks, nchunks, 2 * I / kSlabRows, H, src, nullptr, xb, act_rows, xe, xuop, xum, I, H,
+               hq, hs, nullptr};
     if (chunks_cap > 0)
         hipLaunchKernelGGL(expert_gemm_kernel<true>, dim3(grid_of(chunks_cap, g.nslab)), dim3(256),
                            dynamic_lds_bytes(H, false), st, g);
@@ -452,8 +446,9 @@ hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const Tile* chun
 
 hipError_t launch_down(const uint8_t* blobs, int64_t stride, const Tile* chunks, const int32_t* nchunks,
                        int64_t chunks_cap, const int32_t* src, const float* prow, const _Float16* hb, int64_t act_rows,
-                       const float* he, const float* hu, int32_t H, int32_t I, float* dm, hipStream_t st) {
-    GemmArgs g{blobs, stride, chunks, nchunks, H / kSlabRows, I, src, prow, hb, act_rows, he, hu, I, H, nullptr, nullptr,
+                       const float* he, const _Float16* huop, const float* hum, int32_t H, int32_t I, float* dm,
+                       hipStream_t st) {
+    GemmArgs g{blobs, stride, chunks, nchunks, H / kSlabRows, I, src, prow, hb, act_rows, he, huop, hum, I, H, nullptr,
                nullptr, dm};
     if (chunks_cap > 0)
         hipLaunchKernelGGL(expert_gemm_kernel<false>, dim3(grid_of(chunks_cap, g.nslab)), dim3(256),

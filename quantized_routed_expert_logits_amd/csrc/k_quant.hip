@@ -1,5 +1,5 @@
 // Per-32 int8 rounding of fp32 rows (the layer input, once per token), the
-// prescaled fp16 GEMM operands built from int8 codes, and small helpers.
+// prescaled fp16 GEMM operands built from int8 codes, and a fill helper.
 //
 // Strata compare v0.1.35...v0.1.37 page, include/strata/prefill/moe_fused.hpp,
 // quantize_act: the activations are rounded to int8 once per token with one
@@ -10,8 +10,7 @@
 //
 // Quantize layout: 8 lanes cover one block of 32 values, one float4 each, so a
 // wave reads 1 KiB of contiguous input per instruction.  Outputs per block:
-// the int8 codes, the scale, and u = -0.5 * s * (sum of the block's codes),
-// the term the 2-bit weight offset contributes (see k_experts.hip).
+// the int8 codes and the scale.
 //
 // Prescale: the expert GEMMs take each activation value q * s as an fp16
 // operand, so the per-block scale rides inside the MFMA and no per-block
@@ -28,11 +27,19 @@
 // parts = 2 layout per row: per 32-wide block, 4 groups of 8 values, each
 // stored as 8 hi then 8 lo (128 bytes per block), so the 32 bytes one MFMA
 // lane needs for a block (its 8 values, hi and lo) are contiguous.
+//
+// The same kernel writes the operand of the GEMMs' offset pass: per block,
+// u = -0.5 * s * (sum of the block's codes) (the 2-bit weight offset's share,
+// see k_experts.hip), the row's u scaled by a power of two into (-1, 1) and
+// split hi/lo, in the parts = 2 layout over the block index (padded with
+// zeros to a multiple of 32 blocks), plus that power of two.
 #include "internal.h"
 
 namespace strata_moe {
 
 namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float round_half_away(float t) {
     const float r = floorf(fabsf(t) + 0.5f);  // exact: |t| <= 127.00002
@@ -40,8 +47,7 @@ __device__ __forceinline__ float round_half_away(float t) {
 }
 
 __global__ void __launch_bounds__(256) quantize_kernel(const float4* __restrict__ v, int64_t n4,
-                                                       int8_t* __restrict__ q8, float* __restrict__ s_out,
-                                                       float* __restrict__ u_out) {
+                                                       int8_t* __restrict__ q8, float* __restrict__ s_out) {
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const bool valid = g < n4;
     const float4 x = valid ? v[g] : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -57,34 +63,38 @@ __global__ void __launch_bounds__(256) quantize_kernel(const float4* __restrict_
         q[2] = round_half_away(x.z / s);
         q[3] = round_half_away(x.w / s);
     }
-    int sum = (int)q[0] + (int)q[1] + (int)q[2] + (int)q[3];
-    sum += __shfl_xor(sum, 1);
-    sum += __shfl_xor(sum, 2);
-    sum += __shfl_xor(sum, 4);
     if (!valid) return;
-    {
-        const uint32_t packed = ((uint32_t)(uint8_t)(int8_t)(int)q[0]) | ((uint32_t)(uint8_t)(int8_t)(int)q[1] << 8) |
-                                ((uint32_t)(uint8_t)(int8_t)(int)q[2] << 16) | ((uint32_t)(uint8_t)(int8_t)(int)q[3] << 24);
-        reinterpret_cast<uint32_t*>(q8)[g] = packed;
-    }
-    if ((g & 7) == 0) {
-        s_out[g >> 3] = s;
-        if (u_out) u_out[g >> 3] = -0.5f * s * (float)sum;
-    }
+    const uint32_t packed = ((uint32_t)(uint8_t)(int8_t)(int)q[0]) | ((uint32_t)(uint8_t)(int8_t)(int)q[1] << 8) |
+                            ((uint32_t)(uint8_t)(int8_t)(int)q[2] << 16) | ((uint32_t)(uint8_t)(int8_t)(int)q[3] << 24);
+    reinterpret_cast<uint32_t*>(q8)[g] = packed;
+    if ((g & 7) == 0) s_out[g >> 3] = s;
 }
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+// fp16 hi/lo split of an fp32 value.  The asm barrier keeps v an fp32-rounded
+// value: otherwise the compiler fuses a producing multiply into the fp16
+// conversion (one rounding), and hi can differ by one ulp from the hi that lo
+// is measured against when the fp32 value sits on an fp16 rounding tie.
+__device__ __forceinline__ void split_hi_lo(float v, _Float16& hi, _Float16& lo) {
+    asm volatile("" : "+v"(v));
+    hi = (_Float16)v;
+    lo = (_Float16)(v - (float)hi);
+}
 
 // One wave per row: the row multiplier from the block scales, then 16 codes
-// per lane per step (16 contiguous bytes in, 32 or 64 contiguous bytes out).
+// per lane per step (16 contiguous bytes in, 32 or 64 contiguous bytes out);
+// the block sums go through LDS to the lanes that write the offset operand.
 template <int P>
 __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict__ q, const float* __restrict__ s,
                                                        int64_t rows, int32_t cols, _Float16* __restrict__ out,
-                                                       float* __restrict__ mult) {
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;  // wave-uniform; the kernel has no barrier
+                                                       float* __restrict__ mult, _Float16* __restrict__ uop,
+                                                       float* __restrict__ umult) {
+    __shared__ float ush[4][kMaxOffsetChunks * 32];
+    const int w = threadIdx.x >> 6;
+    const int64_t row = (int64_t)blockIdx.x * 4 + w;
+    if (row >= rows) return;  // wave-uniform; only wave-level synchronisation below
     const int lane = threadIdx.x & 63;
     const int nb = cols / kBlock;
+    const int nch = (nb + 31) / 32;
     const float* srow = s + row * nb;
     float m = 0.0f;
     for (int b = lane; b < nb; b += 64) m = fmaxf(m, srow[b]);
@@ -101,24 +111,35 @@ __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict_
     }
     if (lane == 0) mult[row] = back;
     const int8_t* qrow = q + row * cols;
-    for (int j = lane; j < cols / 16; j += 64) {
-        const uint4 w = *reinterpret_cast<const uint4*>(qrow + 16 * j);
-        const float sj = srow[j >> 1] * scale;  // exact: a power-of-two scaling
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    float umax = 0.0f;
+    for (int j0 = 0; j0 < cols / 16; j0 += 64) {  // uniform trip count: the shuffle below sees whole waves
+        const int j = j0 + lane;
+        const bool on = j < cols / 16;
+        uint4 wv = make_uint4(0, 0, 0, 0);
+        if (on) wv = *reinterpret_cast<const uint4*>(qrow + 16 * j);
+        const float sraw = on ? srow[j >> 1] : 0.0f;
+        const float sj = sraw * scale;  // exact: a power-of-two scaling
+        const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
         float v[16];
+        int sum = 0;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            v[i] = (float)(int8_t)(ws[i >> 2] >> (8 * (i & 3))) * sj;
-            // v is the fp32-rounded product: without this barrier the compiler
-            // fuses multiply and fp16 conversion (one rounding), and hi can then
-            // differ by one ulp from the hi that lo is measured against when the
-            // fp32 product sits on an fp16 rounding tie.
-            asm volatile("" : "+v"(v[i]));
+            const int c = (int8_t)(ws[i >> 2] >> (8 * (i & 3)));
+            sum += c;
+            v[i] = (float)c * sj;
         }
+        sum += __shfl_xor(sum, 1);  // lanes 2m, 2m+1 hold the two halves of one block
+        if (on && (j & 1) == 0) {
+            const float u = -0.5f * sraw * (float)sum;
+            ush[w][j >> 1] = u;
+            umax = fmaxf(umax, fabsf(u));
+        }
+        if (!on) continue;
         if constexpr (P == 1) {
             half8_t h0, h1;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
+                asm volatile("" : "+v"(v[i]), "+v"(v[8 + i]));
                 h0[i] = (_Float16)v[i];
                 h1[i] = (_Float16)v[8 + i];
             }
@@ -131,15 +152,42 @@ __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict_
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const _Float16 hi = (_Float16)v[8 * h + i];
+                    _Float16 hi, lo;
+                    split_hi_lo(v[8 * h + i], hi, lo);
                     g[2 * h][i] = hi;
-                    g[2 * h + 1][i] = (_Float16)(v[8 * h + i] - (float)hi);
+                    g[2 * h + 1][i] = lo;
                 }
             // block j/2, value groups 2*(j%2) and 2*(j%2)+1: 64 contiguous bytes
             half8_t* dst = reinterpret_cast<half8_t*>(out + row * (int64_t)cols * 2 + 32 * j);
 #pragma unroll
             for (int t = 0; t < 4; ++t) dst[t] = g[t];
         }
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) umax = fmaxf(umax, __shfl_xor(umax, o));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // offset operand: lane g < 4*nch writes value group g (blocks 8g..8g+7)
+    int eu = 0;
+    if (umax > 0.0f) frexpf(umax, &eu);  // |u| * 2^-eu < 1
+    eu = eu < -100 ? -100 : eu;           // keeps 2^-eu finite
+    const float dn = ldexpf(1.0f, -eu);
+    if (lane == 0) umult[row] = ldexpf(1.0f, eu);
+    if (lane < 4 * nch) {
+        half8_t hi, lo;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int b = 8 * lane + t;
+            const float un = b < nb ? ush[w][b] * dn : 0.0f;  // exact: a power-of-two scaling
+            _Float16 h, l;
+            split_hi_lo(un, h, l);
+            hi[t] = h;
+            lo[t] = l;
+        }
+        half8_t* dst = reinterpret_cast<half8_t*>(uop + row * (int64_t)nch * 64 + 16 * lane);
+        dst[0] = hi;
+        dst[1] = lo;
     }
 }
 
@@ -148,52 +196,33 @@ __global__ void fill_zero_kernel(float* __restrict__ p, int64_t count) {
     if (g < count) p[g] = 0.0f;
 }
 
-// u = -0.5 * s * (sum of the block's codes) for given int8 codes and scales.
-__global__ void block_correction_kernel(const int8_t* __restrict__ q, const float* __restrict__ s, int64_t nblocks,
-                                        float* __restrict__ u) {
-    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (g >= nblocks) return;
-    int sum = 0;
-    for (int i = 0; i < kBlock; ++i) sum += q[g * kBlock + i];
-    u[g] = -0.5f * s[g] * (float)sum;
-}
-
 inline unsigned grid_for(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
 
 }  // namespace
 
-hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q8, float* s, float* u,
-                           hipStream_t st) {
+hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q8, float* s, hipStream_t st) {
     const int64_t n4 = rows * cols / 4;
     if (n4 > 0)
         hipLaunchKernelGGL(quantize_kernel, dim3(grid_for(n4, 256)), dim3(256), 0, st,
-                           reinterpret_cast<const float4*>(v), n4, q8, s, u);
+                           reinterpret_cast<const float4*>(v), n4, q8, s);
     return hipGetLastError();
 }
 
 hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_t cols, int parts, _Float16* out,
-                           float* mult, hipStream_t st) {
+                           float* mult, _Float16* uop, float* umult, hipStream_t st) {
     if (rows > 0) {
         if (parts == 2)
             hipLaunchKernelGGL(prescale_kernel<2>, dim3(grid_for(rows, 4)), dim3(256), 0, st, q, s, rows, cols, out,
-                               mult);
+                               mult, uop, umult);
         else
             hipLaunchKernelGGL(prescale_kernel<1>, dim3(grid_for(rows, 4)), dim3(256), 0, st, q, s, rows, cols, out,
-                               mult);
+                               mult, uop, umult);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t st) {
     if (count > 0) hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(count, 256)), dim3(256), 0, st, p, count);
-    return hipGetLastError();
-}
-
-hipError_t launch_block_correction(const int8_t* q, const float* s, int64_t rows, int32_t cols, float* u,
-                                   hipStream_t st) {
-    const int64_t nb = rows * (cols / kBlock);
-    if (nb > 0)
-        hipLaunchKernelGGL(block_correction_kernel, dim3(grid_for(nb, 256)), dim3(256), 0, st, q, s, nb, u);
     return hipGetLastError();
 }
 

@@ -119,9 +119,10 @@ struct Buffers {
     float* p;
     int8_t* xq;
     float* xs;
-    float* xu;
     _Float16* xb;
     float* xe;
+    _Float16* xuop;
+    float* xum;
     int32_t* hist;
     int32_t* base;
     int32_t* offsets;
@@ -133,16 +134,17 @@ struct Buffers {
     float* prow;
     int8_t* hq;
     float* hs;
-    float* hu;
     _Float16* hb;
     float* he;
+    _Float16* huop;
+    float* hum;
     float* dm;
     int64_t tiles_cap;
 };
 
 struct Offsets {
-    size_t logits, ids, p, xq, xs, xu, xb, xe, hist, base, offsets, tiles, ntiles, err, src, slot, prow, hq, hs, hu, hb,
-        he, dm, total;
+    size_t logits, ids, p, xq, xs, xb, xe, xuop, xum, hist, base, offsets, tiles, ntiles, err, src, slot, prow, hq, hs,
+        hb, he, huop, hum, dm, total;
     int64_t tiles_cap;
 };
 
@@ -157,9 +159,10 @@ Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I) {
     o.p = L.take<float>(n);
     o.xq = L.take<int8_t>(T * H);
     o.xs = L.take<float>(T * (H / kBlock));
-    o.xu = L.take<float>(T * (H / kBlock));
     o.xb = L.take<_Float16>(2 * T * H);
     o.xe = L.take<float>(T);
+    o.xuop = L.take<_Float16>(T * offset_operand_halves(H));
+    o.xum = L.take<float>(T);
     o.hist = L.take<int32_t>(nchunks * E);
     o.base = L.take<int32_t>(nchunks * E);
     o.offsets = L.take<int32_t>(E + 1);
@@ -171,9 +174,10 @@ Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I) {
     o.prow = L.take<float>(n);
     o.hq = L.take<int8_t>(n * I);
     o.hs = L.take<float>(n * (I / kBlock));
-    o.hu = L.take<float>(n * (I / kBlock));
     o.hb = L.take<_Float16>(n * I);
     o.he = L.take<float>(n);
+    o.huop = L.take<_Float16>(n * offset_operand_halves(I));
+    o.hum = L.take<float>(n);
     o.dm = L.take<float>(n * H);
     o.total = L.off;
     return o;
@@ -186,9 +190,10 @@ Buffers carve(char* ws, const Offsets& o) {
     b.p = (float*)(ws + o.p);
     b.xq = (int8_t*)(ws + o.xq);
     b.xs = (float*)(ws + o.xs);
-    b.xu = (float*)(ws + o.xu);
     b.xb = (_Float16*)(ws + o.xb);
     b.xe = (float*)(ws + o.xe);
+    b.xuop = (_Float16*)(ws + o.xuop);
+    b.xum = (float*)(ws + o.xum);
     b.hist = (int32_t*)(ws + o.hist);
     b.base = (int32_t*)(ws + o.base);
     b.offsets = (int32_t*)(ws + o.offsets);
@@ -200,9 +205,10 @@ Buffers carve(char* ws, const Offsets& o) {
     b.prow = (float*)(ws + o.prow);
     b.hq = (int8_t*)(ws + o.hq);
     b.hs = (float*)(ws + o.hs);
-    b.hu = (float*)(ws + o.hu);
     b.hb = (_Float16*)(ws + o.hb);
     b.he = (float*)(ws + o.he);
+    b.huop = (_Float16*)(ws + o.huop);
+    b.hum = (float*)(ws + o.hum);
     b.dm = (float*)(ws + o.dm);
     b.tiles_cap = o.tiles_cap;
     return b;
@@ -311,8 +317,8 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     Buffers b = carve(ws, o);
     CallTimer tm(st);
     tm.begin(kQuantize);
-    HIP_TRY(launch_quantize(x, T, H, b.xq, b.xs, b.xu, st), "quantize launch");
-    HIP_TRY(launch_prescale(b.xq, b.xs, T, H, 2, b.xb, b.xe, st), "prescale launch");
+    HIP_TRY(launch_quantize(x, T, H, b.xq, b.xs, st), "quantize launch");
+    HIP_TRY(launch_prescale(b.xq, b.xs, T, H, 2, b.xb, b.xe, b.xuop, b.xum, st), "prescale launch");
     tm.end(kQuantize);
     tm.begin(kRouter);
     HIP_TRY(launch_router_logits(x, wr, ex->router_bias, T, H, E, b.logits, st), "router launch");
@@ -328,15 +334,15 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     tm.end(kGroup);
     tm.begin(kGateUp);
     HIP_TRY(launch_gate_up((const uint8_t*)ex->gate_up, ex->gate_up_stride, b.tiles, b.ntiles, b.tiles_cap, b.src,
-                           b.xb, T, b.xe, b.xu, H, I, b.hq, b.hs, b.hu, st),
+                           b.xb, T, b.xe, b.xuop, b.xum, H, I, b.hq, b.hs, st),
             "gate/up launch");
     tm.end(kGateUp);
     tm.begin(kPrescaleH);
-    HIP_TRY(launch_prescale(b.hq, b.hs, n, I, 1, b.hb, b.he, st), "prescale launch");
+    HIP_TRY(launch_prescale(b.hq, b.hs, n, I, 1, b.hb, b.he, b.huop, b.hum, st), "prescale launch");
     tm.end(kPrescaleH);
     tm.begin(kDown);
     HIP_TRY(launch_down((const uint8_t*)ex->down, ex->down_stride, b.tiles, b.ntiles, b.tiles_cap, b.src, b.prow,
-                        b.hb, n, b.he, b.hu, H, I, b.dm, st),
+                        b.hb, n, b.he, b.huop, b.hum, H, I, b.dm, st),
             "down launch");
     tm.end(kDown);
     tm.begin(kCombine);
@@ -538,7 +544,7 @@ int strata_moe_quantize(const float* v, int64_t rows, int32_t cols, int8_t* code
     if (!v || !codes || !scales) return fail(STRATA_MOE_EINVAL, "null pointer");
     if (!aligned(v, 16) || !aligned(codes, 4)) return fail(STRATA_MOE_EINVAL, "v must be 16-, codes 4-byte aligned");
     TRY(check_device());
-    HIP_TRY(launch_quantize(v, rows, cols, codes, scales, nullptr, (hipStream_t)stream), "quantize launch");
+    HIP_TRY(launch_quantize(v, rows, cols, codes, scales, (hipStream_t)stream), "quantize launch");
     return 0;
 }
 
@@ -555,20 +561,19 @@ int strata_moe_gate_up(const int8_t* qx, const float* sx, const int32_t* offsets
     const int32_t E = experts->n_expert, H = experts->hidden, I = experts->ffn;
     const int64_t n = T * K;
     Layout L;
-    const size_t o_xb = L.take<_Float16>(2 * T * H), o_xe = L.take<float>(T), o_xu = L.take<float>(T * (H / kBlock));
+    const size_t o_xb = L.take<_Float16>(2 * T * H), o_xe = L.take<float>(T);
+    const size_t o_xuop = L.take<_Float16>(T * offset_operand_halves(H)), o_xum = L.take<float>(T);
     const size_t o_tiles = L.take<Tile>(max_tiles(n, E)), o_nt = L.take<int32_t>(1);
-    const size_t o_hu = L.take<float>(n * (I / kBlock));
     char* ws = nullptr;
     TRY(get_workspace(L.off, &ws));
     _Float16* xb = (_Float16*)(ws + o_xb);
     float* xe = (float*)(ws + o_xe);
-    float* xu = (float*)(ws + o_xu);
-    HIP_TRY(launch_prescale(qx, sx, T, H, 2, xb, xe, st), "prescale launch");
-    HIP_TRY(launch_block_correction(qx, sx, T, H, xu, st), "correction launch");
+    _Float16* xuop = (_Float16*)(ws + o_xuop);
+    float* xum = (float*)(ws + o_xum);
+    HIP_TRY(launch_prescale(qx, sx, T, H, 2, xb, xe, xuop, xum, st), "prescale launch");
     HIP_TRY(launch_tiles_from_offsets(offsets, E, (Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), st), "tiles launch");
     HIP_TRY(launch_gate_up((const uint8_t*)experts->gate_up, experts->gate_up_stride, (Tile*)(ws + o_tiles),
-                           (int32_t*)(ws + o_nt), max_tiles(n, E), src, xb, T, xe, xu, H, I, qh, sh,
-                           (float*)(ws + o_hu), st),
+                           (int32_t*)(ws + o_nt), max_tiles(n, E), src, xb, T, xe, xuop, xum, H, I, qh, sh, st),
             "gate/up launch");
     return 0;
 }
@@ -587,22 +592,23 @@ int strata_moe_down(const int8_t* qh, const float* sh, const int32_t* offsets, c
     const int32_t E = experts->n_expert, H = experts->hidden, I = experts->ffn;
     const int64_t n = T * K;
     Layout L;
-    const size_t o_hb = L.take<_Float16>(n * I), o_he = L.take<float>(n), o_hu = L.take<float>(n * (I / kBlock));
+    const size_t o_hb = L.take<_Float16>(n * I), o_he = L.take<float>(n);
+    const size_t o_huop = L.take<_Float16>(n * offset_operand_halves(I)), o_hum = L.take<float>(n);
     const size_t o_tiles = L.take<Tile>(max_tiles(n, E)), o_nt = L.take<int32_t>(1), o_prow = L.take<float>(n);
     const size_t o_dm = L.take<float>(n * H);
     char* ws = nullptr;
     TRY(get_workspace(L.off, &ws));
     _Float16* hb = (_Float16*)(ws + o_hb);
     float* he = (float*)(ws + o_he);
-    float* hu = (float*)(ws + o_hu);
+    _Float16* huop = (_Float16*)(ws + o_huop);
+    float* hum = (float*)(ws + o_hum);
     float* prow = (float*)(ws + o_prow);
     float* dm = (float*)(ws + o_dm);
-    HIP_TRY(launch_prescale(qh, sh, n, I, 1, hb, he, st), "prescale launch");
-    HIP_TRY(launch_block_correction(qh, sh, n, I, hu, st), "correction launch");
+    HIP_TRY(launch_prescale(qh, sh, n, I, 1, hb, he, huop, hum, st), "prescale launch");
     HIP_TRY(launch_tiles_from_offsets(offsets, E, (Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), st), "tiles launch");
     HIP_TRY(launch_row_weights(slot, p, n, prow, st), "weights launch");
     HIP_TRY(launch_down((const uint8_t*)experts->down, experts->down_stride, (Tile*)(ws + o_tiles),
-                        (int32_t*)(ws + o_nt), max_tiles(n, E), src, prow, hb, n, he, hu, H, I, dm, st),
+                        (int32_t*)(ws + o_nt), max_tiles(n, E), src, prow, hb, n, he, huop, hum, H, I, dm, st),
             "down launch");
     HIP_TRY(launch_combine(dm, slot, T, K, H, out, st), "combine launch");
     return 0;
