@@ -43,10 +43,22 @@ hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_
                            float* mult, _Float16* uop, float* umult, hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t st);
 
-hipError_t launch_router_logits(const float* x, const float* wr, const float* bias, int64_t T, int32_t H, int32_t E,
-                                float* logits, hipStream_t st);
-hipError_t launch_topk(const float* logits, const float* x, const float* wr, const float* bias, int64_t T, int32_t H,
-                       int32_t E, int32_t K, int32_t* ids, float* p, hipStream_t st);
+// Router scratch: wt [E][H] fp32 (transposed weight, also read by the top-K
+// re-score), wb [E][H][2] fp16 (its hi/lo form), wm [E], xm [T] (input row
+// multipliers, used when the caller passes none).
+struct RouterScratch {
+    float* wt;
+    _Float16* wb;
+    float* wm;
+    float* xm;
+};
+// logits [T][E]; xm: the input rows' power-of-two multipliers (the prescale's
+// row multipliers of the same rows) or nullptr to compute them.
+hipError_t launch_router(const float* x, const float* xm, const float* wr, const float* bias, int64_t T, int32_t H,
+                         int32_t E, const RouterScratch& rs, float* logits, hipStream_t st);
+// amb: scratch of T+1 ints (the list of tokens with a near-tie); wt from the router scratch.
+hipError_t launch_topk(const float* logits, const float* x, const float* wt, const float* bias, int64_t T, int32_t H,
+                       int32_t E, int32_t K, int32_t* amb, int32_t* ids, float* p, hipStream_t st);
 
 hipError_t launch_group(const int32_t* ids, const float* p, int64_t n, int32_t K, int32_t E, int32_t* hist,
                         int32_t* base, int32_t* offsets, Tile* tiles, int32_t* ntiles, int32_t* src, int32_t* slot,

@@ -6,13 +6,17 @@
 // the K largest logits in rank order (equal logits: lower expert index first)
 // and the softmax over those K logits as the weights.
 //
-// Exactness of the selection.  The logits are computed in fp32; near a tie the
-// fp32 order may differ from the real one.  Every token whose K-th/(K+1)-th
-// gap, or any gap between consecutive selected logits, is below
-// delta = kTieRel * max(1, |l_K|) is re-scored: all experts within delta of
-// the K-th value are recomputed as fp64 dot products and re-ranked.  With
-// delta above twice the fp32 error, the result equals the ranking of the exact
-// logits.
+// Exactness of the selection.  The logits carry an error of the order of an
+// fp32 dot product's (see the router kernel below); near a tie their order
+// may differ from the real one.  For a token where some gap
+// between consecutive ranks 0..K (fp32 order) is below
+// delta = kTieRel * max(1, |l_K|), the experts whose order is in doubt (the
+// ranks next to such a gap, and every expert within delta below the K-th
+// value) are recomputed as fp64 dot products and everything within delta of
+// the K-th value is re-ranked.  With delta above twice the fp32 error, the
+// result equals the ranking of the exact logits (at the synthetic workloads'
+// scale the largest deviation from fp64 logits is about 3e-5 against a delta
+// of about 1e-3).
 #include "internal.h"
 
 #include <cfloat>
@@ -25,98 +29,254 @@ namespace {
 constexpr float kTieRel = 1.0f / 1024.0f;
 
 // ---------------------------------------------------------------- logits
-// logits[T][E] = x[T][H] . wr[H][E] (+ bias), 64x64 tiles, 4x4 per thread.
-__global__ void __launch_bounds__(256) router_gemm_kernel(const float* __restrict__ x, const float* __restrict__ wr,
-                                                          const float* __restrict__ bias, int64_t T, int32_t H,
-                                                          int32_t E, float* __restrict__ out) {
-    __shared__ float As[16][64 + 4];
-    __shared__ float Bs[16][64 + 4];
-    const int tid = threadIdx.x;
-    const int tx = tid & 15, ty = tid >> 4;
-    const int64_t m0 = (int64_t)blockIdx.y * 64;
-    const int n0 = blockIdx.x * 64;
-    float acc[4][4] = {};
-    for (int k0 = 0; k0 < H; k0 += 16) {
-        {
-            const int ar = tid >> 2, ac = (tid & 3) * 4;
-            float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (m0 + ar < T) a = *reinterpret_cast<const float4*>(x + (m0 + ar) * H + k0 + ac);
-            As[ac + 0][ar] = a.x;
-            As[ac + 1][ar] = a.y;
-            As[ac + 2][ar] = a.z;
-            As[ac + 3][ar] = a.w;
-            const int br = tid >> 4, bc = (tid & 15) * 4;
-            const float* wrow = wr + (int64_t)(k0 + br) * E;
+// logits[T][E] = x[T][H] . wr[H][E] (+ bias) on the MFMA unit.  Each fp32
+// operand is written as hi + lo fp16 (lo = fp16(v - hi), about 22 bits)
+// after a power-of-two scaling that puts the row's (token's) or column's
+// (expert's) largest magnitude in [2^14, 2^15); the product keeps
+// hi*hi + hi*lo + lo*hi (three MFMAs, fp32 accumulation), which leaves an
+// error of the order of an fp32 dot product's, and the scalings are undone
+// exactly in the epilogue.
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void split_hi_lo(float v, _Float16& hi, _Float16& lo) {
+    asm volatile("" : "+v"(v));  // v stays the fp32 value (no fused multiply-convert)
+    hi = (_Float16)v;
+    lo = (_Float16)(v - (float)hi);
+}
+
+// 2^(ex - 15) for a row whose largest magnitude is m: m * 2^(15 - ex) lies in
+// [2^14, 2^15).  1 for an all-zero row.
+__device__ __forceinline__ float row_multiplier(float m) {
+    if (!(m > 0.0f)) return 1.0f;
+    int ex = 0;
+    frexpf(m, &ex);
+    ex = ex < -96 ? -96 : ex;
+    return ldexpf(1.0f, ex - 15);
+}
+
+// xm[t] = row multiplier of x[t] (one wave per row).
+__global__ void __launch_bounds__(256) row_scale_kernel(const float* __restrict__ x, int64_t T, int32_t H,
+                                                        float* __restrict__ xm) {
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int lane = threadIdx.x & 63;
+    float m = 0.0f;
+    for (int h = lane; h < H; h += 64) m = fmaxf(m, fabsf(x[t * H + h]));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Bs[br][bc + i] = (n0 + bc + i < E) ? wrow[n0 + bc + i] : 0.f;
+    for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (lane == 0) xm[t] = row_multiplier(m);
+}
+
+// From wt [E][H] (the transposed router weight): wb [E][H/8][hi 8, lo 8] of
+// wt * 2^-ew and wm[e] = 2^ew (one wave per expert).
+__global__ void __launch_bounds__(256) router_prep_kernel(const float* __restrict__ wt, int32_t H, int32_t E,
+                                                          _Float16* __restrict__ wb, float* __restrict__ wm) {
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (e >= E) return;
+    const int lane = threadIdx.x & 63;
+    const float* row = wt + (int64_t)e * H;
+    float m = 0.0f;
+    for (int h = lane; h < H; h += 64) m = fmaxf(m, fabsf(row[h]));
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    const float mult = row_multiplier(m), inv = 1.0f / mult;  // exact: powers of two
+    if (lane == 0) wm[e] = mult;
+    for (int j = lane; j < H / 8; j += 64) {
+        half8_t hi, lo;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            _Float16 h, l;
+            split_hi_lo(row[8 * j + i] * inv, h, l);
+            hi[i] = h;
+            lo[i] = l;
         }
-        __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-            const float4 a = *reinterpret_cast<const float4*>(&As[kk][ty * 4]);
-            const float4 b = *reinterpret_cast<const float4*>(&Bs[kk][tx * 4]);
-            const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t m = m0 + ty * 4 + i;
-        if (m >= T) continue;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n = n0 + tx * 4 + j;
-            if (n < E) out[m * E + n] = acc[i][j] + (bias ? bias[n] : 0.f);
-        }
+        half8_t* dst = reinterpret_cast<half8_t*>(wb + ((int64_t)e * H + 8 * j) * 2);
+        dst[0] = hi;
+        dst[1] = lo;
     }
 }
 
+// 64 tokens x 128 experts per workgroup; wave w takes experts 32w..32w+31 of
+// the tile (two 16-wide MFMA columns) against all 64 tokens (four 16-row
+// tiles).  Per 32-wide k block: the workgroup converts its 64 x 32 input
+// block to hi/lo fp16 into LDS (each thread 8 values), one barrier, then each
+// wave reads the 4 x 2 A fragments and runs 4 x 2 x 3 MFMAs.  Input values
+// and B fragments are loaded two k blocks ahead (H / 32 is even).
+constexpr int kRtM = 64, kRtN = 128;
+
+struct RouterStage {
+    float4 x0, x1;          // this thread's 8 input values of one k block
+    half8_t b[2][2];        // [expert tile][hi, lo]
+};
+
+__global__ void __launch_bounds__(256, 2) router_mfma_kernel(const float* __restrict__ x,
+                                                             const float* __restrict__ xm,
+                                                             const _Float16* __restrict__ wb,
+                                                             const float* __restrict__ wm,
+                                                             const float* __restrict__ bias, int64_t T, int32_t H,
+                                                             int32_t E, float* __restrict__ out) {
+    __shared__ half8_t a_lds[2][4][2][64];  // [buffer][token tile][hi, lo][lane]
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, kg = lane >> 4;
+    const int n0 = blockIdx.x * kRtN;
+    const int64_t m0 = (int64_t)blockIdx.y * kRtM;
+    const int nk = H / 32;
+
+    // staging role: token row sr of the tile, value group sk (8 values) of the k block
+    const int sr = tid >> 2, sk = tid & 3;
+    const bool srow_ok = m0 + sr < T;
+    const float sinv = srow_ok ? 1.0f / xm[m0 + sr] : 0.0f;  // exact: a power of two
+    const float* xs = x + (srow_ok ? m0 + sr : 0) * (int64_t)H + 8 * sk;
+    const int slane = sk * 16 + (sr & 15), stile = sr >> 4;
+
+    // B role: expert tiles et = 0, 1 of this wave; experts >= E read expert 0 (never stored)
+    const _Float16* wbp[2];
+#pragma unroll
+    for (int et = 0; et < 2; ++et) {
+        const int e = n0 + 32 * wave + 16 * et + r16;
+        wbp[et] = wb + ((int64_t)(e < E ? e : 0) * H + 8 * kg) * 2;
+    }
+
+    auto load = [&](int kb, RouterStage& S) {
+        kb = kb < nk ? kb : nk - 1;
+        S.x0 = *reinterpret_cast<const float4*>(xs + 32 * kb);
+        S.x1 = *reinterpret_cast<const float4*>(xs + 32 * kb + 4);
+#pragma unroll
+        for (int et = 0; et < 2; ++et) {
+            const half8_t* bp = reinterpret_cast<const half8_t*>(wbp[et] + 64 * kb);
+            S.b[et][0] = bp[0];
+            S.b[et][1] = bp[1];
+        }
+    };
+    auto stage = [&](int kb, const RouterStage& S) {
+        const float v[8] = {S.x0.x, S.x0.y, S.x0.z, S.x0.w, S.x1.x, S.x1.y, S.x1.z, S.x1.w};
+        half8_t hi, lo;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            _Float16 h, l;
+            split_hi_lo(v[i] * sinv, h, l);
+            hi[i] = h;
+            lo[i] = l;
+        }
+        a_lds[kb & 1][stile][0][slane] = hi;
+        a_lds[kb & 1][stile][1][slane] = lo;
+    };
+    float4_t acc[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int et = 0; et < 2; ++et) acc[mt][et] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    auto products = [&](int kb, const RouterStage& S) {
+        half8_t a[4][2];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            a[mt][0] = a_lds[kb & 1][mt][0][lane];
+            a[mt][1] = a_lds[kb & 1][mt][1][lane];
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int et = 0; et < 2; ++et) {
+                acc[mt][et] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][0], S.b[et][0], acc[mt][et], 0, 0, 0);
+                acc[mt][et] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][0], S.b[et][1], acc[mt][et], 0, 0, 0);
+                acc[mt][et] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][1], S.b[et][0], acc[mt][et], 0, 0, 0);
+            }
+    };
+
+    RouterStage s0, s1;
+    load(0, s0);
+    load(1, s1);
+    for (int kb = 0; kb < nk; kb += 2) {
+        stage(kb, s0);
+        __syncthreads();
+        products(kb, s0);
+        load(kb + 2, s0);
+        stage(kb + 1, s1);
+        __syncthreads();
+        products(kb + 1, s1);
+        load(kb + 3, s1);
+    }
+
+#pragma unroll
+    for (int et = 0; et < 2; ++et) {
+        const int e = n0 + 32 * wave + 16 * et + r16;
+        if (e >= E) continue;
+        const float we = wm[e], be = bias ? bias[e] : 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t t = m0 + 16 * mt + 4 * kg + v;
+                if (t < T) out[t * E + e] = acc[mt][et][v] * xm[t] * we + be;
+            }
+    }
+}
+
+__global__ void fill_i32_kernel(int32_t* __restrict__ p, int32_t count, int32_t value) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count) p[i] = value;
+}
+
+// wt[E][H] = wr[H][E]: the re-score reads one expert's weights as a
+// contiguous row.  32x32 tiles through LDS.
+__global__ void __launch_bounds__(256) transpose_kernel(const float* __restrict__ in, int32_t R, int32_t C,
+                                                        float* __restrict__ out) {
+    __shared__ float tile[32][33];
+    const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+#pragma unroll
+    for (int k = 0; k < 32; k += 8)
+        if (r0 + ty + k < R && c0 + tx < C) tile[ty + k][tx] = in[(int64_t)(r0 + ty + k) * C + c0 + tx];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 32; k += 8)
+        if (c0 + ty + k < C && r0 + tx < R) out[(int64_t)(c0 + ty + k) * R + r0 + tx] = tile[tx][ty + k];
+}
+
 // ------------------------------------------------------------------ top-K
-// One wave per token; lane l holds experts l, l+64, ... (at most 16).
-constexpr int kWaves = 4;
 constexpr int kPerLane = kMaxExperts / 64;
+constexpr int kBatch = 8;  // re-scored dot products computed together
 
 __device__ __forceinline__ bool better(float v, int e, float bv, int be) { return v > bv || (v == bv && e < be); }
 __device__ __forceinline__ bool better_d(double v, int e, double bv, int be) {
     return v > bv || (v == bv && e < be);
 }
 
-__global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, const float* __restrict__ x,
-                                                   const float* __restrict__ wr, const float* __restrict__ bias,
-                                                   int64_t T, int32_t H, int32_t E, int32_t K,
-                                                   int32_t* __restrict__ ids, float* __restrict__ p_out) {
-    __shared__ int cidx_s[kWaves][kMaxExperts];
-    __shared__ double cval_s[kWaves][kMaxExperts];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * kWaves + wave;
-    if (t >= T) return;  // whole wave; this kernel has no block-level barrier
-    const float* l = logits + t * E;
+// The wave-wide selection of one token (every lane ends with the same
+// results): lane l holds logits l, l+64, ... in v; selv/seli get ranks
+// 0..rounds-1 (K+1 rounds, K when K == E) by larger value, then lower index;
+// `loose` has bit k (k < K) set when rank k is within delta of a neighbouring
+// rank, i.e. its exact order is in doubt.
+struct Selection {
     float v[kPerLane];
+    float selv[kMaxTopK + 1];
+    int seli[kMaxTopK + 1];
+    int rounds;
+    float vK, delta;
+    uint32_t loose;
+};
+
+__device__ __forceinline__ void select_token(const float* __restrict__ l, int32_t E, int32_t K, int lane,
+                                             Selection& S) {
 #pragma unroll
     for (int i = 0; i < kPerLane; ++i) {
         const int e = lane + 64 * i;
-        v[i] = e < E ? l[e] : -FLT_MAX;
+        S.v[i] = e < E ? l[e] : -FLT_MAX;
     }
-    // K + 1 rounds of a wave-wide argmax (larger value, then lower index).
-    float selv[kMaxTopK + 1];
-    int seli[kMaxTopK + 1];
     uint32_t taken = 0;
-    const int rounds = K < E ? K + 1 : K;
+    S.rounds = K < E ? K + 1 : K;
 #pragma unroll
     for (int k = 0; k <= kMaxTopK; ++k) {
-        selv[k] = -FLT_MAX;
-        seli[k] = INT_MAX;
-        if (k >= rounds) continue;
+        S.selv[k] = -FLT_MAX;
+        S.seli[k] = INT_MAX;
+        if (k >= S.rounds) continue;
         float bv = -FLT_MAX;
         int bi = INT_MAX;
 #pragma unroll
         for (int i = 0; i < kPerLane; ++i) {
             const int e = lane + 64 * i;
-            if (e < E && !((taken >> i) & 1u) && better(v[i], e, bv, bi)) bv = v[i], bi = e;
+            if (e < E && !((taken >> i) & 1u) && better(S.v[i], e, bv, bi)) bv = S.v[i], bi = e;
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) {
@@ -124,88 +284,27 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
             const int oi = __shfl_xor(bi, off);
             if (better(ov, oi, bv, bi)) bv = ov, bi = oi;
         }
-        selv[k] = bv;
-        seli[k] = bi;
+        S.selv[k] = bv;
+        S.seli[k] = bi;
         if (bi < E && (bi & 63) == lane) taken |= 1u << (bi >> 6);
     }
-    float vK = -FLT_MAX;
+    S.vK = -FLT_MAX;
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k)
-        if (k == K - 1) vK = selv[k];
-    const float delta = kTieRel * fmaxf(1.0f, fabsf(vK));
-    bool amb = false;
+        if (k == K - 1) S.vK = S.selv[k];
+    S.delta = kTieRel * fmaxf(1.0f, fabsf(S.vK));
+    S.loose = 0;
 #pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k)
-        if (k + 1 < rounds && selv[k] - selv[k + 1] < delta) amb = true;
-
-    double lv[kMaxTopK];
-    int li[kMaxTopK];
-#pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k) lv[k] = (double)selv[k], li[k] = seli[k];
-
-    if (amb) {
-        // Candidates: every expert within delta below the K-th value.
-        int* cidx = cidx_s[wave];
-        double* cval = cval_s[wave];
-        const float thr = vK - delta;
-        int nc = 0;
-#pragma unroll
-        for (int i = 0; i < kPerLane; ++i) {
-            const int e = lane + 64 * i;
-            const bool cand = e < E && v[i] >= thr;
-            const uint64_t m = __ballot(cand);
-            if (cand) cidx[nc + __popcll(m & ((1ull << lane) - 1ull))] = e;
-            nc += __popcll(m);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        // fp64 re-score of each candidate, the wave splitting the hidden dim.
-        const float* xr = x + t * H;
-        for (int c = 0; c < nc; ++c) {
-            const int e = cidx[c];
-            double acc = 0.0;
-            for (int h = lane; h < H; h += 64) acc = fma((double)xr[h], (double)wr[(int64_t)h * E + e], acc);
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-            if (bias) acc += (double)bias[e];
-            if (lane == 0) cval[c] = acc;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        // Re-rank the candidates (larger fp64 value, then lower index).
-        double cv[kPerLane];
-        int ci[kPerLane];
-#pragma unroll
-        for (int i = 0; i < kPerLane; ++i) {
-            const int c = lane + 64 * i;
-            cv[i] = c < nc ? cval[c] : -DBL_MAX;
-            ci[i] = c < nc ? cidx[c] : INT_MAX;
-        }
-        uint32_t tk = 0;
-#pragma unroll
-        for (int k = 0; k < kMaxTopK; ++k) {
-            if (k >= K) continue;
-            double bv = -DBL_MAX;
-            int bi = INT_MAX, bslot = -1;
-#pragma unroll
-            for (int i = 0; i < kPerLane; ++i)
-                if (!((tk >> i) & 1u) && ci[i] != INT_MAX && better_d(cv[i], ci[i], bv, bi))
-                    bv = cv[i], bi = ci[i], bslot = i;
-            int bl = bslot >= 0 ? lane : 64;
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) {
-                const double ov = __shfl_xor(bv, off);
-                const int oi = __shfl_xor(bi, off);
-                const int os = __shfl_xor(bslot, off);
-                const int ol = __shfl_xor(bl, off);
-                if (better_d(ov, oi, bv, bi)) bv = ov, bi = oi, bslot = os, bl = ol;
-            }
-            lv[k] = bv;
-            li[k] = bi;
-            if (bl == lane && bslot >= 0) tk |= 1u << bslot;
-        }
+    for (int k = 0; k < kMaxTopK; ++k) {
+        const bool up = k > 0 && k < S.rounds && S.selv[k - 1] - S.selv[k] < S.delta;
+        const bool dn = k + 1 < S.rounds && S.selv[k] - S.selv[k + 1] < S.delta;
+        if (k < K && (up || dn)) S.loose |= 1u << k;
     }
-    // Softmax over the K selected logits, in double.
+}
+
+// ids / p of one token from its ranked values (softmax over the K, in double).
+__device__ __forceinline__ void write_token(const double (&lv)[kMaxTopK], const int (&li)[kMaxTopK], int32_t K,
+                                            int lane, int64_t t, int32_t* __restrict__ ids, float* __restrict__ p_out) {
     const double m = lv[0];
     double z = 0.0;
 #pragma unroll
@@ -219,21 +318,181 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
         }
 }
 
+// One wave per token: tokens without a near-tie are finished here; the others
+// are appended to `amb` (amb[0] = count, then token ids) for the resolve pass.
+constexpr int kWaves = 4;
+__global__ void __launch_bounds__(256) topk_select_kernel(const float* __restrict__ logits, int64_t T, int32_t E,
+                                                          int32_t K, int32_t* __restrict__ amb,
+                                                          int32_t* __restrict__ ids, float* __restrict__ p_out) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * kWaves + wave;
+    if (t >= T) return;  // whole wave; this kernel has no block-level barrier
+    Selection S;
+    select_token(logits + t * E, E, K, lane, S);
+    if (S.loose) {
+        if (lane == 0) {
+            const int slot = atomicAdd(amb, 1);
+            amb[1 + slot] = (int32_t)t;
+        }
+        return;
+    }
+    double lv[kMaxTopK];
+    int li[kMaxTopK];
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) lv[k] = (double)S.selv[k], li[k] = S.seli[k];
+    write_token(lv, li, K, lane, t, ids, p_out);
+}
+
+// One workgroup per listed token (grid-stride over the list).  Candidates:
+// every expert within delta below the K-th value (this includes all K
+// selected).  Selected ranks outside every near-tie keep their fp32 value:
+// each is at least delta away from any value that is re-scored, so the merged
+// order is the exact one.  The others are re-scored as fp64 dot products by
+// all 256 threads, up to kBatch at a time (each thread takes H/256 products of
+// each), then wave 0 re-ranks the candidates.
+__global__ void __launch_bounds__(256) topk_resolve_kernel(const float* __restrict__ logits,
+                                                           const float* __restrict__ x, const float* __restrict__ wt,
+                                                           const float* __restrict__ bias, int32_t H, int32_t E,
+                                                           int32_t K, const int32_t* __restrict__ amb,
+                                                           int32_t* __restrict__ ids, float* __restrict__ p_out) {
+    __shared__ int cidx[kMaxExperts];
+    __shared__ double cval[kMaxExperts];
+    __shared__ int jobs[kMaxExperts];
+    __shared__ double part[kWaves][kBatch];
+    __shared__ int counts[2];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n = amb[0];
+    for (int it = blockIdx.x; it < n; it += gridDim.x) {  // uniform over the workgroup
+        const int64_t t = amb[1 + it];
+        Selection S;
+        if (wave == 0) {
+            select_token(logits + t * E, E, K, lane, S);
+            const float thr = S.vK - S.delta;
+            int nc = 0, nj = 0;
+#pragma unroll
+            for (int i = 0; i < kPerLane; ++i) {
+                const int e = lane + 64 * i;
+                const bool cand = e < E && S.v[i] >= thr;
+                bool stable = false;
+#pragma unroll
+                for (int k = 0; k < kMaxTopK; ++k)
+                    if (k < K && !((S.loose >> k) & 1u) && S.seli[k] == e) stable = true;
+                const uint64_t m = __ballot(cand);
+                const uint64_t mj = __ballot(cand && !stable);
+                if (cand) {
+                    const int c = nc + __popcll(m & ((1ull << lane) - 1ull));
+                    cidx[c] = e;
+                    cval[c] = (double)S.v[i];
+                    if (!stable) jobs[nj + __popcll(mj & ((1ull << lane) - 1ull))] = c;
+                }
+                nc += __popcll(m);
+                nj += __popcll(mj);
+            }
+            if (lane == 0) counts[0] = nc, counts[1] = nj;
+        }
+        __syncthreads();
+        const int nj = counts[1];
+        const float* xr = x + t * H;
+        for (int j0 = 0; j0 < nj; j0 += kBatch) {  // uniform
+            double acc[kBatch];
+            int ej[kBatch];
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                acc[b] = 0.0;
+                ej[b] = j0 + b < nj ? cidx[jobs[j0 + b]] : -1;
+            }
+            for (int h = tid; h < H; h += 256) {
+                const double xv = (double)xr[h];
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b)
+                    if (ej[b] >= 0) acc[b] = fma(xv, (double)wt[(int64_t)ej[b] * H + h], acc[b]);
+            }
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) acc[b] += __shfl_xor(acc[b], off);
+                if (lane == 0) part[wave][b] = acc[b];
+            }
+            __syncthreads();
+            if (tid < kBatch && j0 + tid < nj) {
+                double v = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]);
+                const int c = jobs[j0 + tid];
+                if (bias) v += (double)bias[cidx[c]];
+                cval[c] = v;
+            }
+            __syncthreads();
+        }
+        if (wave == 0) {
+            const int nc = counts[0];
+            double cv[kPerLane];
+            int ci[kPerLane];
+#pragma unroll
+            for (int i = 0; i < kPerLane; ++i) {
+                const int c = lane + 64 * i;
+                cv[i] = c < nc ? cval[c] : -DBL_MAX;
+                ci[i] = c < nc ? cidx[c] : INT_MAX;
+            }
+            double lv[kMaxTopK];
+            int li[kMaxTopK];
+            uint32_t tk = 0;
+#pragma unroll
+            for (int k = 0; k < kMaxTopK; ++k) {
+                lv[k] = -DBL_MAX;
+                li[k] = INT_MAX;
+                if (k >= K) continue;
+                double bv = -DBL_MAX;
+                int bi = INT_MAX, bslot = -1;
+#pragma unroll
+                for (int i = 0; i < kPerLane; ++i)
+                    if (!((tk >> i) & 1u) && ci[i] != INT_MAX && better_d(cv[i], ci[i], bv, bi))
+                        bv = cv[i], bi = ci[i], bslot = i;
+                int bl = bslot >= 0 ? lane : 64;
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) {
+                    const double ov = __shfl_xor(bv, off);
+                    const int oi = __shfl_xor(bi, off);
+                    const int os = __shfl_xor(bslot, off);
+                    const int ol = __shfl_xor(bl, off);
+                    if (better_d(ov, oi, bv, bi)) bv = ov, bi = oi, bslot = os, bl = ol;
+                }
+                lv[k] = bv;
+                li[k] = bi;
+                if (bl == lane && bslot >= 0) tk |= 1u << bslot;
+            }
+            write_token(lv, li, K, lane, t, ids, p_out);
+        }
+        __syncthreads();  // cidx / cval / counts are reused by the next token
+    }
+}
+
 }  // namespace
 
-hipError_t launch_router_logits(const float* x, const float* wr, const float* bias, int64_t T, int32_t H, int32_t E,
-                                float* logits, hipStream_t st) {
-    if (T > 0)
-        hipLaunchKernelGGL(router_gemm_kernel, dim3((E + 63) / 64, (unsigned)((T + 63) / 64)), dim3(256), 0, st, x,
-                           wr, bias, T, H, E, logits);
+hipError_t launch_router(const float* x, const float* xm, const float* wr, const float* bias, int64_t T, int32_t H,
+                         int32_t E, const RouterScratch& rs, float* logits, hipStream_t st) {
+    if (T <= 0) return hipGetLastError();
+    hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)((E + 31) / 32), (unsigned)((H + 31) / 32)), dim3(256), 0, st,
+                       wr, H, E, rs.wt);
+    hipLaunchKernelGGL(router_prep_kernel, dim3((unsigned)((E + 3) / 4)), dim3(256), 0, st, rs.wt, H, E, rs.wb,
+                       rs.wm);
+    if (!xm) {
+        hipLaunchKernelGGL(row_scale_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, x, T, H, rs.xm);
+        xm = rs.xm;
+    }
+    hipLaunchKernelGGL(router_mfma_kernel, dim3((unsigned)((E + kRtN - 1) / kRtN), (unsigned)((T + kRtM - 1) / kRtM)),
+                       dim3(256), 0, st, x, xm, rs.wb, rs.wm, bias, T, H, E, logits);
     return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* logits, const float* x, const float* wr, const float* bias, int64_t T, int32_t H,
-                       int32_t E, int32_t K, int32_t* ids, float* p, hipStream_t st) {
-    if (T > 0)
-        hipLaunchKernelGGL(topk_kernel, dim3((unsigned)((T + kWaves - 1) / kWaves)), dim3(64 * kWaves), 0, st,
-                           logits, x, wr, bias, T, H, E, K, ids, p);
+hipError_t launch_topk(const float* logits, const float* x, const float* wt, const float* bias, int64_t T, int32_t H,
+                       int32_t E, int32_t K, int32_t* amb, int32_t* ids, float* p, hipStream_t st) {
+    if (T > 0) {
+        hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, amb, 1, 0);
+        hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)((T + kWaves - 1) / kWaves)), dim3(64 * kWaves), 0, st,
+                           logits, T, E, K, amb, ids, p);
+        const unsigned grid = (unsigned)(T < 2048 ? T : 2048);
+        hipLaunchKernelGGL(topk_resolve_kernel, dim3(grid), dim3(256), 0, st, logits, x, wt, bias, H, E, K, amb, ids,
+                           p);
+    }
     return hipGetLastError();
 }
 

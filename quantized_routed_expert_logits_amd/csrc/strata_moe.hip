@@ -115,6 +115,10 @@ struct Layout {
 
 struct Buffers {
     float* logits;
+    float* wt;
+    _Float16* wb;
+    float* wm;
+    int32_t* amb;
     int32_t* ids;
     float* p;
     int8_t* xq;
@@ -143,7 +147,7 @@ struct Buffers {
 };
 
 struct Offsets {
-    size_t logits, ids, p, xq, xs, xb, xe, xuop, xum, hist, base, offsets, tiles, ntiles, err, src, slot, prow, hq, hs,
+    size_t logits, wt, wb, wm, amb, ids, p, xq, xs, xb, xe, xuop, xum, hist, base, offsets, tiles, ntiles, err, src, slot, prow, hq, hs,
         hb, he, huop, hum, dm, total;
     int64_t tiles_cap;
 };
@@ -155,6 +159,10 @@ Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I) {
     Offsets o;
     o.tiles_cap = max_tiles(n, E);
     o.logits = L.take<float>(T * E);
+    o.wt = L.take<float>((int64_t)E * H);
+    o.wb = L.take<_Float16>((int64_t)E * H * 2);
+    o.wm = L.take<float>(E);
+    o.amb = L.take<int32_t>(T + 1);
     o.ids = L.take<int32_t>(n);
     o.p = L.take<float>(n);
     o.xq = L.take<int8_t>(T * H);
@@ -186,6 +194,10 @@ Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I) {
 Buffers carve(char* ws, const Offsets& o) {
     Buffers b;
     b.logits = (float*)(ws + o.logits);
+    b.wt = (float*)(ws + o.wt);
+    b.wb = (_Float16*)(ws + o.wb);
+    b.wm = (float*)(ws + o.wm);
+    b.amb = (int32_t*)(ws + o.amb);
     b.ids = (int32_t*)(ws + o.ids);
     b.p = (float*)(ws + o.p);
     b.xq = (int8_t*)(ws + o.xq);
@@ -321,10 +333,12 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     HIP_TRY(launch_prescale(b.xq, b.xs, T, H, 2, b.xb, b.xe, b.xuop, b.xum, st), "prescale launch");
     tm.end(kQuantize);
     tm.begin(kRouter);
-    HIP_TRY(launch_router_logits(x, wr, ex->router_bias, T, H, E, b.logits, st), "router launch");
+    HIP_TRY(launch_router(x, b.xe, wr, ex->router_bias, T, H, E, RouterScratch{b.wt, b.wb, b.wm, nullptr}, b.logits,
+                          st),
+            "router launch");
     tm.end(kRouter);
     tm.begin(kTopK);
-    HIP_TRY(launch_topk(b.logits, x, wr, ex->router_bias, T, H, E, K, b.ids, b.p, st), "top-K launch");
+    HIP_TRY(launch_topk(b.logits, x, b.wt, ex->router_bias, T, H, E, K, b.amb, b.ids, b.p, st), "top-K launch");
     tm.end(kTopK);
     tm.begin(kGroup);
     HIP_TRY(launch_fill_zero((float*)b.err, 1, st), "fill launch");
@@ -501,12 +515,15 @@ int strata_moe_route(const float* x, const float* router_w, const float* bias, i
     TRY(check_device());
     hipStream_t st = (hipStream_t)stream;
     Layout L;
-    const size_t lo = L.take<float>(T * E);
+    const size_t lo = L.take<float>(T * E), o_wt = L.take<float>((int64_t)E * H), o_amb = L.take<int32_t>(T + 1);
+    const size_t o_wb = L.take<_Float16>((int64_t)E * H * 2), o_wm = L.take<float>(E), o_xm = L.take<float>(T);
     char* ws = nullptr;
     TRY(get_workspace(L.off, &ws));
     float* logits = (float*)(ws + lo);
-    HIP_TRY(launch_router_logits(x, router_w, bias, T, H, E, logits, st), "router launch");
-    HIP_TRY(launch_topk(logits, x, router_w, bias, T, H, E, K, ids, p, st), "top-K launch");
+    float* wt = (float*)(ws + o_wt);
+    const RouterScratch rs{wt, (_Float16*)(ws + o_wb), (float*)(ws + o_wm), (float*)(ws + o_xm)};
+    HIP_TRY(launch_router(x, nullptr, router_w, bias, T, H, E, rs, logits, st), "router launch");
+    HIP_TRY(launch_topk(logits, x, wt, bias, T, H, E, K, (int32_t*)(ws + o_amb), ids, p, st), "top-K launch");
     return 0;
 }
 
