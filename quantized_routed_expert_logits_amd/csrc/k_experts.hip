@@ -109,9 +109,9 @@ struct GemmArgs {
 // of the slab's record into LDS buffer b&1 (and the two scales into the
 // offset-pass matrix), one barrier, then the wave's NT tiles x 8 fragments x
 // P parts of MFMAs, fragment-major.
-// Two register sets hold the prefetched next block (record dword and scales,
-// activation fragments), alternating, so the loop body has no copies and each
-// load has a block of compute to land.
+// Records are prefetched several blocks ahead in a register ring and
+// activation fragments one block ahead in two alternating register sets, so
+// the loop body has no copies.
 template <int P>
 struct BlockLoop {
     __amdgpu_buffer_rsrc_t rec;  // this slab's records (nblk x 1280 bytes)
@@ -177,38 +177,37 @@ struct BlockLoop {
                     acc[f][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[f], bf[i][h], acc[f][i], 0, 0, 0);
     }
 
-    // nblk is even (H is a multiple of 128, I of 64): two blocks per
-    // iteration, no exit in between.  Records (from HBM) are loaded two blocks
-    // ahead, activation fragments (mostly from L2) one block ahead; each load
-    // goes out right after the barrier that frees its registers.
-    template <int NT>
+    // One step per block: unpack the block's record into LDS, one barrier,
+    // issue the loads of later blocks, then the block's MFMAs.  Records (from
+    // HBM) run D blocks ahead in a register ring (5 bytes per thread and
+    // block), activation fragments (mostly from L2) one block ahead in two
+    // register sets.  D divides nblk, so the unrolled body has no exit in the
+    // middle and every ring index is a compile-time constant.
+    template <int NT, int D>
     __device__ __forceinline__ void run(const int64_t (&arow)[kTilesPerWave],
                                         float4_t (&acc)[kFrags][kTilesPerWave]) const {
-        uint32_t xw0, sw0, xw1, sw1;
-        half8_t bf0[kTilesPerWave][P], bf1[kTilesPerWave][P];
+        static_assert(D % 2 == 0, "activation sets alternate per block");
+        uint32_t xw[D], sw[D];
+        half8_t bf[2][kTilesPerWave][P];
         // Issue order matters: each unpack waits for its record with a vmcnt
-        // that counts the loads issued after it.  Records first here, as in
-        // the loop (a record is always followed by exactly one block of
-        // activation loads and one record), so the loop header's count holds
-        // on entry too; otherwise the header waits for every load in flight.
-        load_record(0, xw0, sw0);
-        load_record(1, xw1, sw1);
+        // that counts the loads issued after it, and the loop header merges
+        // the entry path with the back edge.  Records first, as in the loop.
+#pragma unroll
+        for (int j = 0; j < D; ++j) load_record(j, xw[j], sw[j]);
         __builtin_amdgcn_sched_barrier(0);
-        load_act<NT>(0, arow, bf0);
+        load_act<NT>(0, arow, bf[0]);
         __builtin_amdgcn_sched_barrier(0);
-        for (int b = 0; b < nblk; b += 2) {
-            unpack(b, xw0, sw0);
-            __syncthreads();
-            load_act<NT>(b + 1, arow, bf1);
-            load_record(b + 2, xw0, sw0);
-            __builtin_amdgcn_sched_barrier(0);  // loads go out before the MFMAs
-            products<NT>(b, bf0, acc);
-            unpack(b + 1, xw1, sw1);
-            __syncthreads();
-            load_act<NT>(b + 2, arow, bf0);
-            load_record(b + 3, xw1, sw1);
-            __builtin_amdgcn_sched_barrier(0);
-            products<NT>(b + 1, bf1, acc);
+        for (int b = 0; b < nblk; b += D) {
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                const int blk = b + j;
+                unpack(blk, xw[j], sw[j]);
+                __syncthreads();
+                load_record(blk + D, xw[j], sw[j]);
+                load_act<NT>(blk + 1, arow, bf[(j + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);  // loads go out before the MFMAs
+                products<NT>(blk, bf[j & 1], acc);
+            }
         }
     }
 };
@@ -262,11 +261,22 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_kernel(GemmArgs g) {
                    __builtin_amdgcn_make_buffer_rsrc((void*)g.act, (short)0, (int)(g.act_rows * g.Kd * 2 * P),
                                                      kBufferWord3),
                    g.Kd, nblk, dstride, tau, lane, r16, kg, p, d_lds, a_lds};
-    switch (ntw) {  // wave-uniform: the block loop is straight-line code for 1..3 tiles
-        case 1: L.template run<1>(arow, acc); break;
-        case 2: L.template run<2>(arow, acc); break;
-        case 3: L.template run<3>(arow, acc); break;
-        default: L.template run<0>(arow, acc); break;  // no tiles: still unpack and meet every barrier
+    // wave-uniform: the block loop is straight-line code for 1..3 tiles; the
+    // record ring is 8 deep when 8 divides the block count (H = 2560, I = 1024)
+    if (nblk % 8 == 0) {
+        switch (ntw) {
+            case 1: L.template run<1, 8>(arow, acc); break;
+            case 2: L.template run<2, 8>(arow, acc); break;
+            case 3: L.template run<3, 8>(arow, acc); break;
+            default: L.template run<0, 8>(arow, acc); break;  // no tiles: still unpack and meet every barrier
+        }
+    } else {
+        switch (ntw) {
+            case 1: L.template run<1, 2>(arow, acc); break;
+            case 2: L.template run<2, 2>(arow, acc); break;
+            case 3: L.template run<3, 2>(arow, acc); break;
+            default: L.template run<0, 2>(arow, acc); break;
+        }
     }
     __syncthreads();  // every d of the slab is in LDS
 
