@@ -47,9 +47,10 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="chunk_8k")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-tokens", type=int, default=256, help="tokens in the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=4096, help="tokens in the CPU-oracle sample (0 = skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="also run one plain device copy of this many MiB (counter calibration)")
+                    help="also run one plain device copy of this many MiB after flushing the Infinity Cache "
+                         "(counter calibration)")
     return ap.parse_args()
 
 
@@ -121,6 +122,7 @@ def main() -> int:
 
     for _ in range(args.warmup):
         qm.strata_moe_prefill(x, wr, experts, s.K, out)
+    dbg_ids = qm.strata_moe_prefill_debug(x, wr, experts, s.K, out)["ids"]  # routing of this chunk (hit experts)
     torch.cuda.synchronize()
 
     log(f"timing {args.steps} steps")
@@ -143,20 +145,34 @@ def main() -> int:
         + ", ".join(f"{k} {v:.3f}" for k, v in kernel_ms.items()))
 
     if args.copy_probe_mib:
-        a = torch.ones((args.copy_probe_mib << 20) // 4, dtype=torch.float32, device=dev)
+        a = torch.empty((args.copy_probe_mib << 20) // 4, dtype=torch.float32, device=dev).uniform_()
         b = torch.empty_like(a)
+        flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
+        flush.fill_(1.0)  # 512 MiB written: evicts the 256 MiB Infinity Cache
+        torch.cuda.synchronize()
         torch.neg(a, out=b)  # reads and writes copy_probe_mib MiB
         torch.cuda.synchronize()
+        del flush
         log(f"copy probe: {args.copy_probe_mib} MiB")
 
     n = s.T * s.K
     flops = {"gate_up": 2.0 * n * 2 * s.I * s.H, "down": 2.0 * n * s.H * s.I}
     dominant = max(kernel_ms, key=kernel_ms.get)
-    if dominant in flops:
+    traffic = measured_traffic(dominant, s.name) if dominant in flops else None
+    if dominant in flops and n / s.E >= 64:
+        # many rows per expert: the grouped GEMM is a dense contraction
         achieved = flops[dominant] / (kernel_ms[dominant] * 1e-3) / 1e12
-        traffic = measured_traffic(dominant, s.name)
         roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic}
+    elif dominant in flops:
+        # few rows per expert: the GEMM streams the hit experts' packed weights once
+        hit = int((torch.bincount(dbg_ids.reshape(-1).long(), minlength=s.E) > 0).sum())
+        rows = 2 * s.I if dominant == "gate_up" else s.H
+        kd = s.H if dominant == "gate_up" else s.I
+        wbytes = hit * rows * kd * (2 / 8 + 2 / 32)
+        achieved = wbytes / (kernel_ms[dominant] * 1e-3) / 1e9
+        roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
     else:
         roofline = {"kernel": dominant, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": None, "traffic": None}
