@@ -153,28 +153,31 @@ struct BlockLoop {
         unpack_dword(xw, d0, d1, a0, a1);
         a_lds[blk & 1][2 * p][lane] = a0;
         a_lds[blk & 1][2 * p + 1][lane] = a1;
-        if (kg == 0) {
-            d_lds[(32 * p + r16) * dstride + blk] = d0;
-            d_lds[(32 * p + 16 + r16) * dstride + blk] = d1;
-        }
+        // the 4 lanes of a row (kg = 0..3) hold the same scales: all write, no branch,
+        // so the unpack can interleave with the MFMAs of the previous block
+        d_lds[(32 * p + r16) * dstride + blk] = d0;
+        d_lds[(32 * p + 16 + r16) * dstride + blk] = d1;
     }
 
     template <int NT>
     __device__ __forceinline__ void products(int blk, const half8_t (&bf)[kTilesPerWave][P],
                                              float4_t (&acc)[kFrags][kTilesPerWave]) const {
-        // all A fragments of the block first: the MFMA stream then waits on
-        // LDS only until each fragment lands, never between fragments
-        half8_t a[kFrags];
+        // A fragments in two groups of four (registers are tight: the next
+        // block's unpack interleaves with these MFMAs)
 #pragma unroll
-        for (int f = 0; f < kFrags; ++f) a[f] = a_lds[blk & 1][f][lane];
-        __builtin_amdgcn_sched_barrier(0);
+        for (int g = 0; g < 2; ++g) {
+            half8_t a[kFrags / 2];
 #pragma unroll
-        for (int f = 0; f < kFrags; ++f)
+            for (int f = 0; f < kFrags / 2; ++f) a[f] = a_lds[blk & 1][4 * g + f][lane];
 #pragma unroll
-            for (int h = 0; h < P; ++h)
+            for (int f = 0; f < kFrags / 2; ++f)
 #pragma unroll
-                for (int i = 0; i < NT; ++i)
-                    acc[f][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[f], bf[i][h], acc[f][i], 0, 0, 0);
+                for (int h = 0; h < P; ++h)
+#pragma unroll
+                    for (int i = 0; i < NT; ++i)
+                        acc[4 * g + f][i] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_f16(a[f], bf[i][h], acc[4 * g + f][i], 0, 0, 0);
+        }
     }
 
     // One step per block: unpack the block's record into LDS, one barrier,
