@@ -52,6 +52,9 @@ constexpr int kWaves = 4;
 constexpr int kFrags = kSlabRows / 16;                               // 8
 constexpr int kTilesPerWave = kChunkRows / (16 * kWaves);            // 3
 constexpr int kParkStride = kSlabRows + 4;                           // floats per parked output row
+constexpr int kSmallRows = 48;       // chunks of at most this many rows take the small-chunk kernel
+constexpr int kSmallTiles = 2;       // 16-row tiles per pass of the small-chunk kernel
+constexpr int kDlStride = 40;        // fp16 per row of a small-chunk wave's d buffer (32 blocks + pad)
 constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3 for raw dword loads on gfx9 (gfx950)
 
 __device__ __forceinline__ _Float16 lo_half(uint32_t w) { return __builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
@@ -59,17 +62,37 @@ __device__ __forceinline__ _Float16 hi_half(uint32_t w) { return __builtin_bit_c
 
 // One packed dword (16 codes) -> two A fragments of 8 fp16 values d*(q-1).
 // Pair m (0..7) of the dword fills fragment m/4, elements 2(m%4) and
-// 2(m%4)+1; its codes sit at bits [2m, 2m+1] and [16+2m, 17+2m].  OR-ing a
-// code into the mantissa of 1024.0 (0x6400) gives 1024 + q exactly; minus
-// 1025 gives q - 1; times d is exact.
-__device__ __forceinline__ void unpack_dword(uint32_t x, _Float16 d0, _Float16 d1, half8_t& a0, half8_t& a1) {
+// 2(m%4)+1; its codes sit at bits [2m, 2m+1] and [16+2m, 17+2m].  A code at
+// mantissa bits [2j, 2j+1] of an fp16 whose exponent gives those bits the
+// weight 1 (2^10, 2^8, 2^6, 2^4, 2^2 for j = 0..4) reads as 2^(10-2j) + q
+// exactly, so one AND-OR per pair places both codes (pairs 5..7 after one
+// shift of the dword by 10); subtracting 2^(10-2j) + 1 gives q - 1 and the
+// product with d is exact.  The five exponent patterns live in VGPRs (the
+// AND-OR takes the mask as its one scalar operand).
+struct UnpackMagic {
+    uint32_t m[5];
+    __device__ __forceinline__ UnpackMagic() {
+#pragma unroll
+        for (int j = 0; j < 5; ++j) {
+            uint32_t v = (uint32_t)(0x6400u - 0x0800u * j) * 0x00010001u;
+            asm("" : "+v"(v));  // keep the pattern in a VGPR
+            m[j] = v;
+        }
+    }
+};
+
+__device__ __forceinline__ void unpack_dword(uint32_t x, _Float16 d0, _Float16 d1, const UnpackMagic& mg,
+                                             half8_t& a0, half8_t& a1) {
 #pragma clang fp contract(off)
-    const half2_t bias = {(_Float16)1025.0f, (_Float16)1025.0f};
     const half2_t s0 = {d0, d0}, s1 = {d1, d1};
+    const uint32_t y = x >> 10;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-        const uint32_t y = ((x >> (2 * m)) & 0x00030003u) | 0x64006400u;
-        const half2_t h = (__builtin_bit_cast(half2_t, y) - bias) * (m < 4 ? s0 : s1);
+        const int j = m < 5 ? m : m - 5;
+        const uint32_t w = ((m < 5 ? x : y) & (0x00030003u << (2 * j))) | mg.m[j];
+        const _Float16 c = (_Float16)(float)((1 << (10 - 2 * j)) + 1);
+        const half2_t bias = {c, c};
+        const half2_t h = (__builtin_bit_cast(half2_t, w) - bias) * (m < 4 ? s0 : s1);
         if (m < 4) {
             a0[2 * (m & 3)] = h[0];
             a0[2 * (m & 3) + 1] = h[1];
@@ -120,6 +143,7 @@ struct BlockLoop {
     int tau, lane, r16, kg, p;
     _Float16* d_lds;
     half8_t (*a_lds)[kFrags][64];
+    UnpackMagic mg;
 
     // Buffer loads: per-lane offsets are loop-invariant, the block enters as a
     // scalar offset.  A block beyond the last re-reads the last one.
@@ -150,7 +174,7 @@ struct BlockLoop {
     __device__ __forceinline__ void unpack(int blk, uint32_t xw, uint32_t sw) const {
         half8_t a0, a1;
         const _Float16 d0 = lo_half(sw), d1 = hi_half(sw);
-        unpack_dword(xw, d0, d1, a0, a1);
+        unpack_dword(xw, d0, d1, mg, a0, a1);
         a_lds[blk & 1][2 * p][lane] = a0;
         a_lds[blk & 1][2 * p + 1][lane] = a1;
         // the 4 lanes of a row (kg = 0..3) hold the same scales: all write, no branch,
@@ -215,6 +239,83 @@ struct BlockLoop {
     }
 };
 
+
+// Gate/up epilogue of one 16-row tile of routed rows (column r16 of this lane,
+// grouped row r of the chunk) against one slab: fragments 0..3 are the gate
+// rows 64*slab + 16f + 4kg + v, fragments 4..7 the up rows of the same j.
+// SwiGLU, then the two 32-wide H blocks of the slab rounded to int8 with their
+// scales (the max over a block spans the 4 lanes kg of the row).
+__device__ __forceinline__ void gate_up_store(const GemmArgs& g, const Tile& tl, int slab, int r, int kg,
+                                              const float4_t (&a)[kFrags]) {
+    const int nbi = g.I / kBlock;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+        float h[2][4];
+        float amax = 0.f;
+#pragma unroll
+        for (int ff = 0; ff < 2; ++ff)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float gt = a[2 * hb + ff][v], up = a[4 + 2 * hb + ff][v];
+                // silu(gate) * up; hardware exp and reciprocal (about 2 ulp),
+                // far inside the rounding-tie tolerance of the int8 H codes
+                h[ff][v] = gt * up * __builtin_amdgcn_rcpf(1.0f + __expf(-gt));
+                amax = fmaxf(amax, fabsf(h[ff][v]));
+            }
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        const float sh = amax / 127.0f;
+        float q[2][4];
+#pragma unroll
+        for (int ff = 0; ff < 2; ++ff)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) q[ff][v] = sh != 0.0f ? round_half_away(h[ff][v] / sh) : 0.0f;
+        if (r < tl.nrows) {
+            const int64_t row = tl.row0 + r;
+            int8_t* dst = g.hq + row * g.I + 64 * slab + 32 * hb + 4 * kg;
+#pragma unroll
+            for (int ff = 0; ff < 2; ++ff) {
+                const uint32_t packed = (uint32_t)(uint8_t)(int8_t)(int)q[ff][0] |
+                                        (uint32_t)(uint8_t)(int8_t)(int)q[ff][1] << 8 |
+                                        (uint32_t)(uint8_t)(int8_t)(int)q[ff][2] << 16 |
+                                        (uint32_t)(uint8_t)(int8_t)(int)q[ff][3] << 24;
+                *reinterpret_cast<uint32_t*>(dst + 16 * ff) = packed;
+            }
+            if (kg == 0) g.hs[row * nbi + 2 * slab + hb] = sh;
+        }
+    }
+}
+
+// Down epilogue of one 16-row tile (chunk rows 16*tt .. 16*tt + 15) against one
+// slab: each routed row's outputs times its routing weight w, written to its
+// grouped row of dm [n][H] (the rows the combine reads).  The wave parks the
+// 16 rows x 128 outputs in its LDS area `park` and stores them row by row,
+// 512 contiguous bytes per row.
+__device__ __forceinline__ void down_store(const GemmArgs& g, const Tile& tl, int slab, int tt, int lane, float w,
+                                           const float4_t (&a)[kFrags], float* park) {
+    const int r16 = lane & 15, kg = lane >> 4;
+#pragma unroll
+    for (int f = 0; f < kFrags; ++f) {
+        const float4 v4 = make_float4(w * a[f][0], w * a[f][1], w * a[f][2], w * a[f][3]);
+        *reinterpret_cast<float4*>(park + r16 * kParkStride + 16 * f + 4 * kg) = v4;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // float4 (j*64 + lane): row (j*64 + lane) / 32 of the tile, outputs 4*((j*64 + lane) % 32)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int flat = j * 64 + lane;
+        const int rr = flat >> 5, c4 = flat & 31;
+        const int r = 16 * tt + rr;
+        if (r < tl.nrows) {
+            const float4 v4 = *reinterpret_cast<const float4*>(park + rr * kParkStride + 4 * c4);
+            *reinterpret_cast<float4*>(g.y + (int64_t)(tl.row0 + r) * g.H + kSlabRows * slab + 4 * c4) = v4;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
 // kGateUp: activation rows are tokens (through src), epilogue SwiGLU + int8 H.
 // Otherwise: activation rows are the grouped rows, epilogue weighted row stores.
 template <bool kGateUp>
@@ -229,6 +330,7 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_kernel(GemmArgs g) {
     const int slab = local % g.nslab;
     if (chunk >= *g.nchunks) return;  // uniform over the workgroup, before any barrier
     const Tile tl = g.chunks[chunk];
+    if (tl.nrows <= kSmallRows) return;  // the small-chunk kernel's
 
     const int tau = threadIdx.x, lane = tau & 63, r16 = lane & 15, kg = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tau >> 6);
@@ -263,7 +365,7 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_kernel(GemmArgs g) {
     BlockLoop<P> L{__builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, nblk * kRecordBytes, kBufferWord3),
                    __builtin_amdgcn_make_buffer_rsrc((void*)g.act, (short)0, (int)(g.act_rows * g.Kd * 2 * P),
                                                      kBufferWord3),
-                   g.Kd, nblk, dstride, tau, lane, r16, kg, p, d_lds, a_lds};
+                   g.Kd, nblk, dstride, tau, lane, r16, kg, p, d_lds, a_lds, UnpackMagic()};
     // wave-uniform: the block loop is straight-line code for 1..3 tiles; the
     // record ring is 8 deep when 8 divides the block count (H = 2560, I = 1024)
     if (nblk % 8 == 0) {
@@ -331,81 +433,233 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_kernel(GemmArgs g) {
     }
 
     if constexpr (kGateUp) {
-        // fragments 0..3: gate rows 64*slab + 16f + 4kg + v; 4..7: the up rows of the same j
-        const int nbi = g.I / kBlock;
 #pragma unroll
         for (int i = 0; i < kTilesPerWave; ++i) {
             if (i >= ntw) continue;
-            const int r = 16 * (wave + kWaves * i) + r16;
+            float4_t a[kFrags];
 #pragma unroll
-            for (int hb = 0; hb < 2; ++hb) {
-                float h[2][4];
-                float amax = 0.f;
-#pragma unroll
-                for (int ff = 0; ff < 2; ++ff)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const float gt = acc[2 * hb + ff][i][v], up = acc[4 + 2 * hb + ff][i][v];
-                        // silu(gate) * up; hardware exp and reciprocal (about 2 ulp),
-                        // far inside the rounding-tie tolerance of the int8 H codes
-                        h[ff][v] = gt * up * __builtin_amdgcn_rcpf(1.0f + __expf(-gt));
-                        amax = fmaxf(amax, fabsf(h[ff][v]));
-                    }
-                amax = fmaxf(amax, __shfl_xor(amax, 16));
-                amax = fmaxf(amax, __shfl_xor(amax, 32));
-                const float sh = amax / 127.0f;
-                float q[2][4];
-#pragma unroll
-                for (int ff = 0; ff < 2; ++ff)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) q[ff][v] = sh != 0.0f ? round_half_away(h[ff][v] / sh) : 0.0f;
-                if (r < tl.nrows) {
-                    const int64_t row = tl.row0 + r;
-                    int8_t* dst = g.hq + row * g.I + 64 * slab + 32 * hb + 4 * kg;
-#pragma unroll
-                    for (int ff = 0; ff < 2; ++ff) {
-                        const uint32_t packed = (uint32_t)(uint8_t)(int8_t)(int)q[ff][0] |
-                                                (uint32_t)(uint8_t)(int8_t)(int)q[ff][1] << 8 |
-                                                (uint32_t)(uint8_t)(int8_t)(int)q[ff][2] << 16 |
-                                                (uint32_t)(uint8_t)(int8_t)(int)q[ff][3] << 24;
-                        *reinterpret_cast<uint32_t*>(dst + 16 * ff) = packed;
-                    }
-                    if (kg == 0) g.hs[row * nbi + 2 * slab + hb] = sh;
-                }
-            }
+            for (int f = 0; f < kFrags; ++f) a[f] = acc[f][i];
+            gate_up_store(g, tl, slab, 16 * (wave + kWaves * i) + r16, kg, a);
         }
     } else {
-        // Each routed row's output times its routing weight, written to its
-        // grouped row of dm [n][H] (the rows the combine reads).  Per tile the
-        // wave parks its 16 rows x 128 outputs in LDS and stores them row by
-        // row, 512 contiguous bytes per row.
         float* park = reinterpret_cast<float*>(d_lds + kSlabRows * dstride) + wave * 16 * kParkStride;
 #pragma unroll
         for (int i = 0; i < kTilesPerWave; ++i) {
             if (i >= ntw) continue;
-            const float w = arow[i] >= 0 ? g.prow[arow[i]] : 0.f;
+            float4_t a[kFrags];
 #pragma unroll
-            for (int f = 0; f < kFrags; ++f) {
-                const float4 v4 = make_float4(w * acc[f][i][0], w * acc[f][i][1], w * acc[f][i][2], w * acc[f][i][3]);
-                *reinterpret_cast<float4*>(park + r16 * kParkStride + 16 * f + 4 * kg) = v4;
+            for (int f = 0; f < kFrags; ++f) a[f] = acc[f][i];
+            down_store(g, tl, slab, wave + kWaves * i, lane, arow[i] >= 0 ? g.prow[arow[i]] : 0.f, a, park);
+        }
+    }
+}
+
+
+// Small-chunk kernel (chunks of at most kSmallRows routed rows, the common
+// case when a prompt chunk gives each expert only a few rows).  There the
+// 4-wave kernel above leaves most of its waves without a tile, and its
+// per-block barrier is paid for very few MFMAs.  Here each wave streams one
+// slab on its own: per block a lane loads the four dwords of its (r16, kg)
+// position (fragments 0..7) and the scales of its rows, unpacks them in
+// registers and runs the MFMAs of every tile of the chunk (at most two per
+// pass; a three-tile chunk takes two passes).  A workgroup holds four waves on
+// four consecutive slabs of one chunk, so the activation fragments they all
+// read come from the CU's L1.  No workgroup barrier: each wave keeps the d of
+// its rows for the offset pass in its own LDS area, 32 blocks at a time, and
+// runs that pass every 32 blocks, adding it with the ratio of the two row
+// multipliers (powers of two) before the final multiply.
+template <int P, int NT>
+struct SlabPass {
+    __amdgpu_buffer_rsrc_t rec, act;
+    int32_t Kd, nblk;
+    int lane, r16, kg;
+    _Float16* dl;  // [kSlabRows][kDlStride]
+    UnpackMagic mg;
+
+    __device__ __forceinline__ void load_record(int blk, uint32_t (&xw)[4], uint32_t (&sw)[4]) const {
+        blk = blk < nblk ? blk : nblk - 1;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            xw[p] = __builtin_amdgcn_raw_buffer_load_b32(rec, (64 * p + lane) * 4, blk * kRecordBytes, 0);
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            sw[p] = __builtin_amdgcn_raw_buffer_load_b32(rec, kRecordCodeBytes + (16 * p + r16) * 4,
+                                                         blk * kRecordBytes, 0);
+    }
+
+    __device__ __forceinline__ void load_act(int blk, const int64_t (&arow)[NT], half8_t (&bf)[NT][P]) const {
+        blk = blk < nblk ? blk : nblk - 1;
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            const int r = arow[i] >= 0 ? (int)arow[i] : 0;
+            const int voff = r * Kd * 2 * P + kg * 16 * P;
+#pragma unroll
+            for (int h = 0; h < P; ++h)
+                bf[i][h] = __builtin_bit_cast(
+                    half8_t, __builtin_amdgcn_raw_buffer_load_b128(act, voff + 16 * h, blk * kBlock * 2 * P, 0));
+        }
+    }
+
+    // One block: per dword p, unpack fragments 2p and 2p+1, park their scales
+    // for the offset pass (the 4 lanes kg of a row write the same value), MFMAs.
+    __device__ __forceinline__ void block(int blk, const uint32_t (&xw)[4], const uint32_t (&sw)[4],
+                                          const half8_t (&bf)[NT][P], float4_t (&acc)[kFrags][NT]) const {
+        const int col = blk & 31;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            half8_t a0, a1;
+            const _Float16 d0 = lo_half(sw[p]), d1 = hi_half(sw[p]);
+            unpack_dword(xw[p], d0, d1, mg, a0, a1);
+            dl[(32 * p + r16) * kDlStride + col] = d0;
+            dl[(32 * p + 16 + r16) * kDlStride + col] = d1;
+#pragma unroll
+            for (int h = 0; h < P; ++h)
+#pragma unroll
+                for (int i = 0; i < NT; ++i) {
+                    acc[2 * p][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bf[i][h], acc[2 * p][i], 0, 0, 0);
+                    acc[2 * p + 1][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bf[i][h], acc[2 * p + 1][i], 0, 0, 0);
+                }
+            __builtin_amdgcn_sched_barrier(0);  // one dword's fragments live at a time
+        }
+    }
+
+    // Offset pass of 32-block chunk c: acc += (um / am) * sum_b d[row][b] u'[col][b].
+    __device__ __forceinline__ void offset(int c, int nch, const _Float16* uop, const int64_t (&arow)[NT],
+                                           const float (&ratio)[NT], float4_t (&acc)[kFrags][NT]) const {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        half8_t ub[NT][2];
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            const int64_t ar = arow[i] >= 0 ? arow[i] : 0;
+            const half8_t* urow = reinterpret_cast<const half8_t*>(uop + ar * nch * 64) + 2 * kg + 8 * c;
+            ub[i][0] = urow[0];
+            ub[i][1] = urow[1];
+        }
+#pragma unroll
+        for (int f = 0; f < kFrags; ++f) {
+            const half8_t da = *reinterpret_cast<const half8_t*>(&dl[(16 * f + r16) * kDlStride + 8 * kg]);
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                float4_t t = __builtin_amdgcn_mfma_f32_16x16x32_f16(da, ub[i][0], (float4_t){0.f, 0.f, 0.f, 0.f},
+                                                                    0, 0, 0);
+                t = __builtin_amdgcn_mfma_f32_16x16x32_f16(da, ub[i][1], t, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[f][i][v] = fmaf(t[v], ratio[i], acc[f][i][v]);
             }
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            const int tt = wave + kWaves * i;
-            // float4 (j*64 + lane): row (j*64 + lane) / 32 of the tile, outputs 4*((j*64 + lane) % 32)
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+    // Records run D blocks ahead in a register ring (8 dwords per block),
+    // activation fragments one block ahead in two alternating sets.
+    template <int D>
+    __device__ __forceinline__ void run(int nch, const _Float16* uop, const int64_t (&arow)[NT],
+                                        const float (&ratio)[NT], float4_t (&acc)[kFrags][NT]) const {
+        uint32_t xw[D][4], sw[D][4];
+        half8_t bf[2][NT][P];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int flat = j * 64 + lane;
-                const int rr = flat >> 5, c4 = flat & 31;
-                const int r = 16 * tt + rr;
-                if (r < tl.nrows) {
-                    const float4 v4 = *reinterpret_cast<const float4*>(park + rr * kParkStride + 4 * c4);
-                    *reinterpret_cast<float4*>(g.y + (int64_t)(tl.row0 + r) * g.H + kSlabRows * slab + 4 * c4) = v4;
+        for (int j = 0; j < D; ++j) load_record(j, xw[j], sw[j]);
+        __builtin_amdgcn_sched_barrier(0);
+        load_act(0, arow, bf[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        for (int c = 0; c < nch; ++c) {
+            const int bend = nblk < 32 * c + 32 ? nblk : 32 * c + 32;
+            for (int b = 32 * c; b < bend; b += D) {
+#pragma unroll
+                for (int j = 0; j < D; ++j) {
+                    const int blk = b + j;
+                    load_act(blk + 1, arow, bf[(j + 1) & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    block(blk, xw[j], sw[j], bf[j & 1], acc);
+                    load_record(blk + D, xw[j], sw[j]);
                 }
             }
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            __builtin_amdgcn_wave_barrier();
+            offset(c, nch, uop, arow, ratio, acc);
         }
+    }
+};
+
+template <bool kGateUp, int NT>
+__device__ __forceinline__ void small_chunk_pass(const GemmArgs& g, const Tile& tl, int slab, int t0, int lane,
+                                                 _Float16* dl) {
+    constexpr int P = kGateUp ? 2 : 1;
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int nblk = g.Kd / kBlock, nch = (nblk + 31) / 32;
+
+    // zero the d buffer: blocks past the last of a partial chunk meet u = 0
+    for (int o = lane; o < kSlabRows * kDlStride / 8; o += 64)
+        reinterpret_cast<half8_t*>(dl)[o] = (half8_t){0, 0, 0, 0, 0, 0, 0, 0};
+
+    int64_t arow[NT];
+    float ratio[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const int r = 16 * (t0 + i) + r16;
+        arow[i] = -1;
+        if (r < tl.nrows) arow[i] = kGateUp ? (int64_t)g.src[tl.row0 + r] : (int64_t)(tl.row0 + r);
+        ratio[i] = arow[i] >= 0 ? g.um[arow[i]] / g.am[arow[i]] : 0.f;
+    }
+    float4_t acc[kFrags][NT];
+#pragma unroll
+    for (int f = 0; f < kFrags; ++f)
+#pragma unroll
+        for (int i = 0; i < NT; ++i) acc[f][i] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+    const uint8_t* rec = g.blobs + (int64_t)tl.e * g.stride + (int64_t)slab * nblk * kRecordBytes;
+    SlabPass<P, NT> L{__builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, nblk * kRecordBytes, kBufferWord3),
+                      __builtin_amdgcn_make_buffer_rsrc((void*)g.act, (short)0, (int)(g.act_rows * g.Kd * 2 * P),
+                                                        kBufferWord3),
+                      g.Kd, nblk, lane, r16, kg, dl, UnpackMagic()};
+    if (nblk % 4 == 0)
+        L.template run<4>(nch, g.uop, arow, ratio, acc);
+    else
+        L.template run<2>(nch, g.uop, arow, ratio, acc);
+
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const float mult = arow[i] >= 0 ? g.am[arow[i]] : 0.f;
+        float4_t a[kFrags];
+#pragma unroll
+        for (int f = 0; f < kFrags; ++f)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) a[f][v] = acc[f][i][v] * mult;
+        if constexpr (kGateUp)
+            gate_up_store(g, tl, slab, 16 * (t0 + i) + r16, kg, a);
+        else  // the d buffer is free after the last offset pass
+            down_store(g, tl, slab, t0 + i, lane, arow[i] >= 0 ? g.prow[arow[i]] : 0.f, a,
+                       reinterpret_cast<float*>(dl));
+    }
+}
+
+template <bool kGateUp>
+__global__ void __launch_bounds__(256, 3) expert_gemm_small_kernel(GemmArgs g) {
+    __shared__ _Float16 dl_all[kWaves][kSlabRows * kDlStride];
+    static_assert(kSlabRows * kDlStride * sizeof(_Float16) >= 16 * kParkStride * sizeof(float),
+                  "a wave's d buffer also parks one output tile");
+
+    // workgroup -> (chunk, group of 4 slabs), all groups of a chunk on one XCD
+    const int ngroups = (g.nslab + kWaves - 1) / kWaves;
+    const int id = blockIdx.x;
+    const int local = id >> 3;
+    const int chunk = (local / ngroups) * 8 + (id & 7);
+    const int group = local % ngroups;
+    if (chunk >= *g.nchunks) return;
+    const Tile tl = g.chunks[chunk];
+    if (tl.nrows > kSmallRows) return;  // the 4-wave kernel's
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int slab = kWaves * group + wave;
+    if (slab >= g.nslab) return;  // waves are independent: no workgroup barrier follows
+    const int lane = threadIdx.x & 63;
+    const int nt = (tl.nrows + 15) / 16;
+    for (int t0 = 0; t0 < nt; t0 += kSmallTiles) {
+        if (nt - t0 >= 2)
+            small_chunk_pass<kGateUp, 2>(g, tl, slab, t0, lane, dl_all[wave]);
+        else
+            small_chunk_pass<kGateUp, 1>(g, tl, slab, t0, lane, dl_all[wave]);
     }
 }
 
@@ -452,8 +706,12 @@ hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const Tile* chun
     GemmArgs g{blobs, stride, chunks, nchunks, 2 * I / kSlabRows, H, src, nullptr, xb, act_rows, xe, xuop, xum, I, H,
                hq, hs, nullptr};
     if (chunks_cap > 0)
+    {
         hipLaunchKernelGGL(expert_gemm_kernel<true>, dim3(grid_of(chunks_cap, g.nslab)), dim3(256),
                            dynamic_lds_bytes(H, false), st, g);
+        hipLaunchKernelGGL(expert_gemm_small_kernel<true>, dim3(grid_of(chunks_cap, (g.nslab + kWaves - 1) / kWaves)),
+                           dim3(256), 0, st, g);
+    }
     return hipGetLastError();
 }
 
@@ -464,8 +722,12 @@ hipError_t launch_down(const uint8_t* blobs, int64_t stride, const Tile* chunks,
     GemmArgs g{blobs, stride, chunks, nchunks, H / kSlabRows, I, src, prow, hb, act_rows, he, huop, hum, I, H, nullptr,
                nullptr, dm};
     if (chunks_cap > 0)
+    {
         hipLaunchKernelGGL(expert_gemm_kernel<false>, dim3(grid_of(chunks_cap, g.nslab)), dim3(256),
                            dynamic_lds_bytes(I, true), st, g);
+        hipLaunchKernelGGL(expert_gemm_small_kernel<false>,
+                           dim3(grid_of(chunks_cap, (g.nslab + kWaves - 1) / kWaves)), dim3(256), 0, st, g);
+    }
     return hipGetLastError();
 }
 
