@@ -29,6 +29,19 @@ inline int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 // Upper bound of the chunk count of n grouped rows over E experts.
 inline int64_t max_tiles(int64_t n, int32_t E) { return n / kChunkRows + E; }
 
+constexpr int kSmallRows = 48;  // chunks of at most this many rows go to the small-chunk GEMM kernel
+
+// The GEMMs' work lists, written on the GPU by the grouping (or from given
+// offsets): tiles[0, cap) the chunks of more than kSmallRows rows, tiles[cap,
+// 2 cap) the others; sched[0], sched[1] their counts.
+constexpr int kSchedInts = 2;
+struct ChunkLists {
+    Tile* tiles;     // [2 * cap]
+    int32_t* sched;  // [kSchedInts]
+    int64_t cap;
+};
+inline int64_t chunk_list_cap(int64_t n, int32_t E) { return max_tiles(n, E); }
+
 // fp16 values per row of the offset-pass operand of a reduction length Kd:
 // 32-block chunks, hi and lo per block.
 inline int64_t offset_operand_halves(int32_t Kd) { return (int64_t)((Kd / kBlock + 31) / 32) * 64; }
@@ -61,25 +74,24 @@ hipError_t launch_topk(const float* logits, const float* x, const float* wt, con
                        int32_t E, int32_t K, int32_t* amb, int32_t* ids, float* p, hipStream_t st);
 
 hipError_t launch_group(const int32_t* ids, const float* p, int64_t n, int32_t K, int32_t E, int32_t* hist,
-                        int32_t* base, int32_t* offsets, Tile* tiles, int32_t* ntiles, int32_t* src, int32_t* slot,
+                        int32_t* base, int32_t* offsets, const ChunkLists& cl, int32_t* src, int32_t* slot,
                         float* prow, int32_t* err, hipStream_t st);
-hipError_t launch_tiles_from_offsets(const int32_t* offsets, int32_t E, Tile* tiles, int32_t* ntiles,
-                                     hipStream_t st);
+hipError_t launch_chunks_from_offsets(const int32_t* offsets, int32_t E, const ChunkLists& cl, hipStream_t st);
 hipError_t launch_row_weights(const int32_t* slot, const float* p, int64_t n, float* prow, hipStream_t st);
 
 // gate/up: xb = prescaled input rows (parts 2), xe = their multipliers,
 // xuop / xum = offset-pass operand and multipliers; writes int8 H codes hq and
 // scales hs.
-hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const Tile* tiles, const int32_t* ntiles,
-                          int64_t tiles_cap, const int32_t* src, const _Float16* xb, int64_t act_rows, const float* xe,
+// n = routed rows, E = experts (bounds of the two chunk lists' lengths).
+hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const ChunkLists& cl, int64_t n, int32_t E,
+                          const int32_t* src, const _Float16* xb, int64_t act_rows, const float* xe,
                           const _Float16* xuop, const float* xum, int32_t H, int32_t I, int8_t* hq, float* hs,
                           hipStream_t st);
 // down: hb = prescaled H rows (parts 1), he = their multipliers, huop / hum =
 // offset-pass operand and multipliers; writes the weighted rows dm.
-hipError_t launch_down(const uint8_t* blobs, int64_t stride, const Tile* tiles, const int32_t* ntiles,
-                       int64_t tiles_cap, const int32_t* src, const float* prow, const _Float16* hb, int64_t act_rows,
-                       const float* he, const _Float16* huop, const float* hum, int32_t H, int32_t I, float* dm,
-                       hipStream_t st);
+hipError_t launch_down(const uint8_t* blobs, int64_t stride, const ChunkLists& cl, int64_t n, int32_t E,
+                       const int32_t* src, const float* prow, const _Float16* hb, int64_t act_rows, const float* he,
+                       const _Float16* huop, const float* hum, int32_t H, int32_t I, float* dm, hipStream_t st);
 hipError_t launch_combine(const float* dm, const int32_t* slot, int64_t T, int32_t K, int32_t H, float* y,
                           hipStream_t st);
 

@@ -52,7 +52,6 @@ constexpr int kWaves = 4;
 constexpr int kFrags = kSlabRows / 16;                               // 8
 constexpr int kTilesPerWave = kChunkRows / (16 * kWaves);            // 3
 constexpr int kParkStride = kSlabRows + 4;                           // floats per parked output row
-constexpr int kSmallRows = 48;       // chunks of at most this many rows take the small-chunk kernel
 constexpr int kSmallTiles = 2;       // 16-row tiles per pass of the small-chunk kernel
 constexpr int kDlStride = 40;        // fp16 per row of a small-chunk wave's d buffer (32 blocks + pad)
 constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3 for raw dword loads on gfx9 (gfx950)
@@ -111,8 +110,8 @@ __device__ __forceinline__ float round_half_away(float t) {
 struct GemmArgs {
     const uint8_t* blobs;  // packed matrices, one per expert
     int64_t stride;        // bytes between experts
-    const Tile* chunks;    // chunks of grouped rows
-    const int32_t* nchunks;
+    const Tile* chunks;    // this kernel's list of chunks of grouped rows
+    const int32_t* nchunks;  // its length
     int32_t nslab;         // 128-row slabs of the packed matrix
     int32_t Kd;            // reduction length (H for gate/up, I for down)
     const int32_t* src;    // token of each grouped row
@@ -150,7 +149,7 @@ struct BlockLoop {
     __device__ __forceinline__ void load_record(int blk, uint32_t& xw, uint32_t& sw) const {
         blk = blk < nblk ? blk : nblk - 1;
         xw = __builtin_amdgcn_raw_buffer_load_b32(rec, tau * 4, blk * kRecordBytes, 0);
-        sw = __builtin_amdgcn_raw_buffer_load_b32(rec, kRecordCodeBytes + (p * 16 + r16) * 4, blk * kRecordBytes, 0);
+        sw = __builtin_amdgcn_raw_buffer_load_b32(rec, kRecordCodeBytes + (tau & 63) * 4, blk * kRecordBytes, 0);
     }
 
     // Activation fragments of a block: lane (r16, kg) takes values 8kg..8kg+7
@@ -171,16 +170,20 @@ struct BlockLoop {
         }
     }
 
+    // Thread tau unpacks dword tau of the record: fragments 2p and 2p+1 of
+    // MFMA lane tau / 4 (p = tau % 4), stored at lane slot (tau / 4) ^ 2p so
+    // that the four pairs of one lane fall in different LDS banks.
     __device__ __forceinline__ void unpack(int blk, uint32_t xw, uint32_t sw) const {
         half8_t a0, a1;
         const _Float16 d0 = lo_half(sw), d1 = hi_half(sw);
         unpack_dword(xw, d0, d1, mg, a0, a1);
-        a_lds[blk & 1][2 * p][lane] = a0;
-        a_lds[blk & 1][2 * p + 1][lane] = a1;
-        // the 4 lanes of a row (kg = 0..3) hold the same scales: all write, no branch,
-        // so the unpack can interleave with the MFMAs of the previous block
-        d_lds[(32 * p + r16) * dstride + blk] = d0;
-        d_lds[(32 * p + 16 + r16) * dstride + blk] = d1;
+        const int ul = tau >> 2, ur16 = ul & 15;
+        a_lds[blk & 1][2 * p][ul ^ (2 * p)] = a0;
+        a_lds[blk & 1][2 * p + 1][ul ^ (2 * p)] = a1;
+        // the 4 waves hold the same scales of a row: all write, no branch, so
+        // the unpack can interleave with the MFMAs of the previous block
+        d_lds[(32 * p + ur16) * dstride + blk] = d0;
+        d_lds[(32 * p + 16 + ur16) * dstride + blk] = d1;
     }
 
     template <int NT>
@@ -192,7 +195,7 @@ struct BlockLoop {
         for (int g = 0; g < 2; ++g) {
             half8_t a[kFrags / 2];
 #pragma unroll
-            for (int f = 0; f < kFrags / 2; ++f) a[f] = a_lds[blk & 1][4 * g + f][lane];
+            for (int f = 0; f < kFrags / 2; ++f) a[f] = a_lds[blk & 1][4 * g + f][lane ^ ((4 * g + f) & ~1)];
 #pragma unroll
             for (int f = 0; f < kFrags / 2; ++f)
 #pragma unroll
@@ -318,20 +321,10 @@ __device__ __forceinline__ void down_store(const GemmArgs& g, const Tile& tl, in
 
 // kGateUp: activation rows are tokens (through src), epilogue SwiGLU + int8 H.
 // Otherwise: activation rows are the grouped rows, epilogue weighted row stores.
+// One work item of the 4-wave kernel: chunk tl against slab `slab`.
 template <bool kGateUp>
-__global__ void __launch_bounds__(256, 2) expert_gemm_kernel(GemmArgs g) {
-    __shared__ half8_t a_lds[2][kFrags][64];
-    extern __shared__ _Float16 d_lds[];  // [kSlabRows][dstride]: d of every row and block (offset pass)
-
-    // workgroup -> (chunk, slab), all slabs of a chunk on one XCD
-    const int id = blockIdx.x;
-    const int local = id >> 3;
-    const int chunk = (local / g.nslab) * 8 + (id & 7);
-    const int slab = local % g.nslab;
-    if (chunk >= *g.nchunks) return;  // uniform over the workgroup, before any barrier
-    const Tile tl = g.chunks[chunk];
-    if (tl.nrows <= kSmallRows) return;  // the small-chunk kernel's
-
+__device__ __forceinline__ void big_chunk_item(const GemmArgs& g, const Tile tl, int slab,
+                                               half8_t (*a_lds)[kFrags][64], _Float16* d_lds) {
     const int tau = threadIdx.x, lane = tau & 63, r16 = lane & 15, kg = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tau >> 6);
     const int nblk = g.Kd / kBlock;
@@ -354,7 +347,7 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_kernel(GemmArgs g) {
     }
 
     const uint8_t* rec = g.blobs + (int64_t)tl.e * g.stride + (int64_t)slab * nblk * kRecordBytes;
-    const int p = wave;  // fragment pair this thread unpacks: fragments 2p, 2p+1
+    const int p = tau & 3;  // fragment pair this thread unpacks: fragments 2p, 2p+1 of MFMA lane tau / 4
 
     float4_t acc[kFrags][kTilesPerWave];
 #pragma unroll
@@ -455,6 +448,21 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_kernel(GemmArgs g) {
 }
 
 
+// One workgroup per (chunk, slab); the id -> (chunk, slab) map keeps every
+// slab of a chunk on one XCD (workgroups are dealt round-robin to the 8
+// XCDs), so that chunk's activation rows are fetched into one L2 only.
+template <bool kGateUp>
+__global__ void __launch_bounds__(256, 2) expert_gemm_kernel(GemmArgs g) {
+    __shared__ half8_t a_lds[2][kFrags][64];
+    extern __shared__ _Float16 d_lds[];  // [kSlabRows][dstride]: d of every row and block (offset pass)
+    const int id = blockIdx.x;
+    const int local = id >> 3;
+    const int chunk = (local / g.nslab) * 8 + (id & 7);
+    if (chunk >= *g.nchunks) return;  // uniform over the workgroup, before any barrier
+    const Tile tl = g.chunks[chunk];   // a copy: read once, before any store
+    big_chunk_item<kGateUp>(g, tl, local % g.nslab, a_lds, d_lds);
+}
+
 // Small-chunk kernel (chunks of at most kSmallRows routed rows, the common
 // case when a prompt chunk gives each expert only a few rows).  There the
 // 4-wave kernel above leaves most of its waves without a tile, and its
@@ -476,15 +484,17 @@ struct SlabPass {
     _Float16* dl;  // [kSlabRows][kDlStride]
     UnpackMagic mg;
 
+    // A lane's four code dwords (fragments 0..7 at its position) and the 8
+    // scales of its row are 16 contiguous bytes each.
     __device__ __forceinline__ void load_record(int blk, uint32_t (&xw)[4], uint32_t (&sw)[4]) const {
         blk = blk < nblk ? blk : nblk - 1;
+        const auto c = __builtin_amdgcn_raw_buffer_load_b128(rec, lane * 16, blk * kRecordBytes, 0);
+        const auto d = __builtin_amdgcn_raw_buffer_load_b128(rec, kRecordCodeBytes + r16 * 16, blk * kRecordBytes, 0);
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-            xw[p] = __builtin_amdgcn_raw_buffer_load_b32(rec, (64 * p + lane) * 4, blk * kRecordBytes, 0);
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-            sw[p] = __builtin_amdgcn_raw_buffer_load_b32(rec, kRecordCodeBytes + (16 * p + r16) * 4,
-                                                         blk * kRecordBytes, 0);
+        for (int p = 0; p < 4; ++p) {
+            xw[p] = c[p];
+            sw[p] = d[p];
+        }
     }
 
     __device__ __forceinline__ void load_act(int blk, const int64_t (&arow)[NT], half8_t (&bf)[NT][P]) const {
@@ -500,26 +510,48 @@ struct SlabPass {
         }
     }
 
-    // One block: per dword p, unpack fragments 2p and 2p+1, park their scales
-    // for the offset pass (the 4 lanes kg of a row write the same value), MFMAs.
+    // Unpack dword p (fragments 2p, 2p+1) and park its scales for the offset
+    // pass (the 4 lanes kg of a row write the same value).
+    __device__ __forceinline__ void prepare(int p, int col, const uint32_t (&xw)[4], const uint32_t (&sw)[4],
+                                            half8_t (&a)[2]) const {
+        const _Float16 d0 = lo_half(sw[p]), d1 = hi_half(sw[p]);
+        unpack_dword(xw[p], d0, d1, mg, a[0], a[1]);
+        dl[(32 * p + r16) * kDlStride + col] = d0;
+        dl[(32 * p + 16 + r16) * kDlStride + col] = d1;
+    }
+
+    // One block, software-pipelined over the four dwords: the MFMAs of dword
+    // p issue interleaved with the unpack of dword p + 1 (one MFMA, then a
+    // few VALU instructions), so the matrix unit and the vector ALU of the
+    // wave work side by side.
     __device__ __forceinline__ void block(int blk, const uint32_t (&xw)[4], const uint32_t (&sw)[4],
                                           const half8_t (&bf)[NT][P], float4_t (&acc)[kFrags][NT]) const {
+        constexpr int kMfmas = 2 * NT * P;                  // per dword
+        constexpr int kValuPer = (26 + kMfmas - 1) / kMfmas;  // unpack instructions per MFMA slot
         const int col = blk & 31;
+        half8_t a[2][2];
+        prepare(0, col, xw, sw, a[0]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            half8_t a0, a1;
-            const _Float16 d0 = lo_half(sw[p]), d1 = hi_half(sw[p]);
-            unpack_dword(xw[p], d0, d1, mg, a0, a1);
-            dl[(32 * p + r16) * kDlStride + col] = d0;
-            dl[(32 * p + 16 + r16) * kDlStride + col] = d1;
+            if (p < 3) prepare(p + 1, col, xw, sw, a[(p + 1) & 1]);
 #pragma unroll
             for (int h = 0; h < P; ++h)
 #pragma unroll
                 for (int i = 0; i < NT; ++i) {
-                    acc[2 * p][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bf[i][h], acc[2 * p][i], 0, 0, 0);
-                    acc[2 * p + 1][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bf[i][h], acc[2 * p + 1][i], 0, 0, 0);
+                    acc[2 * p][i] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_f16(a[p & 1][0], bf[i][h], acc[2 * p][i], 0, 0, 0);
+                    acc[2 * p + 1][i] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_f16(a[p & 1][1], bf[i][h], acc[2 * p + 1][i], 0, 0, 0);
                 }
-            __builtin_amdgcn_sched_barrier(0);  // one dword's fragments live at a time
+            if (p < 3) {
+#pragma unroll
+                for (int k = 0; k < kMfmas; ++k) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);  // then unpack VALU
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
@@ -614,10 +646,7 @@ __device__ __forceinline__ void small_chunk_pass(const GemmArgs& g, const Tile& 
                       __builtin_amdgcn_make_buffer_rsrc((void*)g.act, (short)0, (int)(g.act_rows * g.Kd * 2 * P),
                                                         kBufferWord3),
                       g.Kd, nblk, lane, r16, kg, dl, UnpackMagic()};
-    if (nblk % 4 == 0)
-        L.template run<4>(nch, g.uop, arow, ratio, acc);
-    else
-        L.template run<2>(nch, g.uop, arow, ratio, acc);
+    L.template run<2>(nch, g.uop, arow, ratio, acc);
 
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
@@ -640,18 +669,15 @@ __global__ void __launch_bounds__(256, 3) expert_gemm_small_kernel(GemmArgs g) {
     __shared__ _Float16 dl_all[kWaves][kSlabRows * kDlStride];
     static_assert(kSlabRows * kDlStride * sizeof(_Float16) >= 16 * kParkStride * sizeof(float),
                   "a wave's d buffer also parks one output tile");
-
     // workgroup -> (chunk, group of 4 slabs), all groups of a chunk on one XCD
     const int ngroups = (g.nslab + kWaves - 1) / kWaves;
     const int id = blockIdx.x;
     const int local = id >> 3;
     const int chunk = (local / ngroups) * 8 + (id & 7);
-    const int group = local % ngroups;
     if (chunk >= *g.nchunks) return;
     const Tile tl = g.chunks[chunk];
-    if (tl.nrows > kSmallRows) return;  // the 4-wave kernel's
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int slab = kWaves * group + wave;
+    const int slab = kWaves * (local % ngroups) + wave;
     if (slab >= g.nslab) return;  // waves are independent: no workgroup barrier follows
     const int lane = threadIdx.x & 63;
     const int nt = (tl.nrows + 15) / 16;
@@ -693,41 +719,55 @@ inline size_t dynamic_lds_bytes(int32_t Kd, bool park) {
     return b;
 }
 
-inline unsigned grid_of(int64_t chunks_cap, int32_t nslab) {
-    return (unsigned)(8 * ((chunks_cap + 7) / 8) * nslab);
+inline unsigned grid_of(int64_t chunks_cap, int32_t per_chunk) {
+    return (unsigned)(8 * ((chunks_cap + 7) / 8) * per_chunk);
+}
+
+// Both kernels over their own lists.  List bounds known on the host: a big
+// chunk holds more than kSmallRows of the n rows; an expert has at most one
+// small chunk.
+void launch_gemms(GemmArgs g, const ChunkLists& cl, int64_t n, int32_t E, size_t big_lds, bool gate_up,
+                  hipStream_t st) {
+    const int64_t cap_big = cl.cap < n / (kSmallRows + 1) ? cl.cap : n / (kSmallRows + 1);
+    const int64_t cap_small = cl.cap < E ? cl.cap : E;
+    g.chunks = cl.tiles;
+    g.nchunks = cl.sched;
+    if (cap_big > 0) {
+        const unsigned gb = grid_of(cap_big, g.nslab);
+        if (gate_up)
+            hipLaunchKernelGGL(expert_gemm_kernel<true>, dim3(gb), dim3(256), big_lds, st, g);
+        else
+            hipLaunchKernelGGL(expert_gemm_kernel<false>, dim3(gb), dim3(256), big_lds, st, g);
+    }
+    g.chunks = cl.tiles + cl.cap;
+    g.nchunks = cl.sched + 1;
+    if (cap_small > 0) {
+        const unsigned gs = grid_of(cap_small, (g.nslab + kWaves - 1) / kWaves);
+        if (gate_up)
+            hipLaunchKernelGGL(expert_gemm_small_kernel<true>, dim3(gs), dim3(256), 0, st, g);
+        else
+            hipLaunchKernelGGL(expert_gemm_small_kernel<false>, dim3(gs), dim3(256), 0, st, g);
+    }
 }
 
 }  // namespace
 
-hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const Tile* chunks, const int32_t* nchunks,
-                          int64_t chunks_cap, const int32_t* src, const _Float16* xb, int64_t act_rows, const float* xe,
+hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const ChunkLists& cl, int64_t n, int32_t E,
+                          const int32_t* src, const _Float16* xb, int64_t act_rows, const float* xe,
                           const _Float16* xuop, const float* xum, int32_t H, int32_t I, int8_t* hq, float* hs,
                           hipStream_t st) {
-    GemmArgs g{blobs, stride, chunks, nchunks, 2 * I / kSlabRows, H, src, nullptr, xb, act_rows, xe, xuop, xum, I, H,
+    GemmArgs g{blobs, stride, nullptr, nullptr, 2 * I / kSlabRows, H, src, nullptr, xb, act_rows, xe, xuop, xum, I, H,
                hq, hs, nullptr};
-    if (chunks_cap > 0)
-    {
-        hipLaunchKernelGGL(expert_gemm_kernel<true>, dim3(grid_of(chunks_cap, g.nslab)), dim3(256),
-                           dynamic_lds_bytes(H, false), st, g);
-        hipLaunchKernelGGL(expert_gemm_small_kernel<true>, dim3(grid_of(chunks_cap, (g.nslab + kWaves - 1) / kWaves)),
-                           dim3(256), 0, st, g);
-    }
+    launch_gemms(g, cl, n, E, dynamic_lds_bytes(H, false), true, st);
     return hipGetLastError();
 }
 
-hipError_t launch_down(const uint8_t* blobs, int64_t stride, const Tile* chunks, const int32_t* nchunks,
-                       int64_t chunks_cap, const int32_t* src, const float* prow, const _Float16* hb, int64_t act_rows,
-                       const float* he, const _Float16* huop, const float* hum, int32_t H, int32_t I, float* dm,
-                       hipStream_t st) {
-    GemmArgs g{blobs, stride, chunks, nchunks, H / kSlabRows, I, src, prow, hb, act_rows, he, huop, hum, I, H, nullptr,
-               nullptr, dm};
-    if (chunks_cap > 0)
-    {
-        hipLaunchKernelGGL(expert_gemm_kernel<false>, dim3(grid_of(chunks_cap, g.nslab)), dim3(256),
-                           dynamic_lds_bytes(I, true), st, g);
-        hipLaunchKernelGGL(expert_gemm_small_kernel<false>,
-                           dim3(grid_of(chunks_cap, (g.nslab + kWaves - 1) / kWaves)), dim3(256), 0, st, g);
-    }
+hipError_t launch_down(const uint8_t* blobs, int64_t stride, const ChunkLists& cl, int64_t n, int32_t E,
+                       const int32_t* src, const float* prow, const _Float16* hb, int64_t act_rows, const float* he,
+                       const _Float16* huop, const float* hum, int32_t H, int32_t I, float* dm, hipStream_t st) {
+    GemmArgs g{blobs, stride, nullptr, nullptr, H / kSlabRows, I, src, prow, hb, act_rows, he, huop, hum, I, H,
+               nullptr, nullptr, dm};
+    launch_gemms(g, cl, n, E, dynamic_lds_bytes(I, true), false, st);
     return hipGetLastError();
 }
 

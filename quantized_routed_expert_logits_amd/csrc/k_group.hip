@@ -2,7 +2,7 @@
 //
 // Strata compare v0.1.35...v0.1.37 page, include/strata/prefill/moe_fused.hpp,
 // group: from the router's ids, per expert its rows (counts, offsets, the list
-// of 64-row tiles; here chunks of up to 256 rows), slot[i] = the row of pair
+// of 64-row tiles; here chunks of up to kChunkRows rows), slot[i] = the row of pair
 // i and src[row] = its token
 // i / K, without a host wait.  The order of rows within an expert is left open
 // there; these kernels produce the stable order (ascending pair index) of the
@@ -12,11 +12,14 @@
 // Three launches, none of which waits on the host:
 //   hist    one workgroup per chunk of 2048 pairs: LDS histogram of its ids;
 //   scan    one workgroup: per expert the exclusive prefix over chunks, the
-//           counts' exclusive scan over experts (offsets), and the list of
-//           row chunks (at most 256 rows of one expert each) the GEMMs walk;
-//   scatter one wave per chunk: pairs in order, 64 at a time; each lane's rank
-//           among the lanes of the same expert comes from ballots over the id
-//           bits (multi-split), so rows are assigned in pair order.
+//           counts' exclusive scan over experts (offsets), and the two lists
+//           of row chunks (at most kChunkRows rows of one expert each) the
+//           GEMMs walk: chunks of more than kSmallRows rows and the others;
+//   scatter one workgroup of 8 waves per chunk, 256 pairs per wave: each
+//           lane's rank among the lanes of the same expert comes from ballots
+//           over the id bits (multi-split); a first pass counts per wave and
+//           expert, a scan over the waves gives each wave's first rows, and a
+//           second pass assigns the rows in pair order.
 #include "internal.h"
 
 namespace strata_moe {
@@ -86,11 +89,41 @@ __device__ int block_exclusive_scan(int v, int* total) {
     return r;
 }
 
+// Expert e's nt chunks (rows off.. off+cnt, `per` rows each, the last one
+// shorter) into the two lists at the expert's offsets in each.
+__device__ void emit_chunks(const ChunkLists& cl, int e, int off, int cnt, int nt, int per, int bpos, int spos) {
+    for (int i = 0; i < nt; ++i) {
+        Tile tl;
+        tl.e = e;
+        tl.row0 = off + i * per;
+        tl.nrows = cnt - i * per < per ? cnt - i * per : per;
+        tl.pad = 0;
+        if (tl.nrows > kSmallRows)
+            cl.tiles[bpos++] = tl;
+        else
+            cl.tiles[cl.cap + spos++] = tl;
+    }
+}
+
+// Chunks of expert e with at most kSmallRows rows (the others are big).
+__device__ int small_chunks(int cnt, int nt, int per) {
+    int ns = 0;
+    for (int i = 0; i < nt; ++i) ns += (cnt - i * per < per ? cnt - i * per : per) <= kSmallRows;
+    return ns;
+}
+
+// The list counts (one thread).
+__device__ void finish_lists(const ChunkLists& cl, int nbig, int nsmall) {
+    if (threadIdx.x == 0) {
+        cl.sched[0] = nbig;
+        cl.sched[1] = nsmall;
+    }
+}
+
 __global__ void __launch_bounds__(1024) group_scan_kernel(const int32_t* __restrict__ hist, int64_t nchunks, int64_t n,
                                                           int32_t E, int32_t* __restrict__ base,
-                                                          int32_t* __restrict__ offsets, Tile* __restrict__ tiles,
-                                                          int32_t* __restrict__ ntiles) {
-    __shared__ int total_rows, total_tiles;
+                                                          int32_t* __restrict__ offsets, ChunkLists cl) {
+    __shared__ int total_rows, total_big, total_small;
     const int e = threadIdx.x;
     int cnt = 0;
     if (e < E) {
@@ -115,51 +148,72 @@ __global__ void __launch_bounds__(1024) group_scan_kernel(const int32_t* __restr
     const int off = block_exclusive_scan(e < E ? cnt : 0, &total_rows);
     int per = 0;
     const int nt = e < E ? chunk_split(cnt, &per) : 0;
-    const int toff = block_exclusive_scan(nt, &total_tiles);
+    const int ns = small_chunks(cnt, nt, per);
+    const int bpos = block_exclusive_scan(nt - ns, &total_big);
+    const int spos = block_exclusive_scan(ns, &total_small);
     if (e < E) {
         offsets[e] = off;
-        for (int i = 0; i < nt; ++i) {
-            Tile tl;
-            tl.e = e;
-            tl.row0 = off + i * per;
-            tl.nrows = cnt - i * per < per ? cnt - i * per : per;
-            tl.pad = 0;
-            tiles[toff + i] = tl;
-        }
+        emit_chunks(cl, e, off, cnt, nt, per, bpos, spos);
     }
-    if (e == 0) {
-        offsets[E] = (int32_t)n;
-        *ntiles = total_tiles;
-    }
+    if (e == 0) offsets[E] = (int32_t)n;
+    finish_lists(cl, total_big, total_small);
 }
 
-__global__ void __launch_bounds__(64) group_scatter_kernel(const int32_t* __restrict__ ids, const float* __restrict__ p,
-                                                           int64_t n, int32_t K, int32_t E,
-                                                           const int32_t* __restrict__ base,
-                                                           const int32_t* __restrict__ offsets,
-                                                           int32_t* __restrict__ src, int32_t* __restrict__ slot,
-                                                           float* __restrict__ prow) {
-    __shared__ int32_t next[kMaxExperts];
-    const int lane = threadIdx.x;
-    for (int e = lane; e < E; e += 64) next[e] = offsets[e] + base[(int64_t)blockIdx.x * E + e];
+constexpr int kScatterWaves = kGroupChunk / 256;  // 8 waves of 256 pairs per chunk
+
+// The lanes of this wave whose id equals this lane's (all lanes with a valid
+// id take part in the ballots); 0 for an invalid id.
+__device__ __forceinline__ uint64_t same_expert_lanes(int32_t e, bool ok, int nbits) {
+    uint64_t same = __ballot(ok);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = ok && ((e >> b) & 1);
+        const uint64_t m = __ballot(bit);
+        same &= bit ? m : ~m;
+    }
+    return ok ? same : 0ull;
+}
+
+__global__ void __launch_bounds__(64 * kScatterWaves) group_scatter_kernel(
+    const int32_t* __restrict__ ids, const float* __restrict__ p, int64_t n, int32_t K, int32_t E,
+    const int32_t* __restrict__ base, const int32_t* __restrict__ offsets, int32_t* __restrict__ src,
+    int32_t* __restrict__ slot, float* __restrict__ prow) {
+    __shared__ int32_t next[kScatterWaves][kMaxExperts];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < kScatterWaves * E; i += blockDim.x) next[i / E][i % E] = 0;
     __syncthreads();
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
-    const int64_t i0 = (int64_t)blockIdx.x * kGroupChunk;
+    const int64_t i0 = (int64_t)blockIdx.x * kGroupChunk + 256 * w;
     const uint64_t below = (1ull << lane) - 1ull;
-    for (int step = 0; step < kGroupChunk / 64; ++step) {
+    // pass 1: this wave's count per expert (the highest lane of each expert adds)
+    for (int step = 0; step < 4; ++step) {
         const int64_t i = i0 + step * 64 + lane;
         const int32_t e = i < n ? ids[i] : -1;
         const bool ok = e >= 0 && e < E;
-        uint64_t same = __ballot(ok);
-        for (int b = 0; b < nbits; ++b) {
-            const bool bit = ok && ((e >> b) & 1);
-            const uint64_t m = __ballot(bit);
-            same &= bit ? m : ~m;
+        const uint64_t same = same_expert_lanes(e, ok, nbits);
+        if (ok && (same >> lane) == 1ull) next[w][e] += __popcll(same);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();
+    // each wave's first row per expert: the chunk's first row, then the waves before it
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        int run = offsets[e] + base[(int64_t)blockIdx.x * E + e];
+        for (int ww = 0; ww < kScatterWaves; ++ww) {
+            const int t = next[ww][e];
+            next[ww][e] = run;
+            run += t;
         }
-        if (!ok) same = 0;
+    }
+    __syncthreads();
+    // pass 2: rows in pair order
+    for (int step = 0; step < 4; ++step) {
+        const int64_t i = i0 + step * 64 + lane;
+        const int32_t e = i < n ? ids[i] : -1;
+        const bool ok = e >= 0 && e < E;
+        const uint64_t same = same_expert_lanes(e, ok, nbits);
         const int rank = __popcll(same & below);
-        const int first = ok ? next[e] : 0;
+        const int first = ok ? next[w][e] : 0;
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
         if (ok) {
@@ -167,33 +221,26 @@ __global__ void __launch_bounds__(64) group_scatter_kernel(const int32_t* __rest
             slot[i] = row;
             src[row] = (int32_t)(i / K);
             if (prow) prow[row] = p[i];
-            if ((same >> lane) == 1ull) next[e] = first + __popcll(same);  // the highest lane of this expert
+            if ((same >> lane) == 1ull) next[w][e] = first + __popcll(same);  // the highest lane of this expert
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
     }
 }
 
-// The tile list of a given grouping (offsets from the caller).
-__global__ void __launch_bounds__(1024) tiles_from_offsets_kernel(const int32_t* __restrict__ offsets, int32_t E,
-                                                                  Tile* __restrict__ tiles,
-                                                                  int32_t* __restrict__ ntiles) {
-    __shared__ int total_tiles;
+// The chunk lists of a given grouping (offsets from the caller).
+__global__ void __launch_bounds__(1024) chunks_from_offsets_kernel(const int32_t* __restrict__ offsets, int32_t E,
+                                                                   ChunkLists cl) {
+    __shared__ int total_big, total_small;
     const int e = threadIdx.x;
     const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
     int per = 0;
     const int nt = chunk_split(cnt, &per);
-    const int toff = block_exclusive_scan(nt, &total_tiles);
-    if (e < E)
-        for (int i = 0; i < nt; ++i) {
-            Tile tl;
-            tl.e = e;
-            tl.row0 = offsets[e] + i * per;
-            tl.nrows = cnt - i * per < per ? cnt - i * per : per;
-            tl.pad = 0;
-            tiles[toff + i] = tl;
-        }
-    if (e == 0) *ntiles = total_tiles;
+    const int ns = small_chunks(cnt, nt, per);
+    const int bpos = block_exclusive_scan(nt - ns, &total_big);
+    const int spos = block_exclusive_scan(ns, &total_small);
+    if (e < E) emit_chunks(cl, e, offsets[e], cnt, nt, per, bpos, spos);
+    finish_lists(cl, total_big, total_small);
 }
 
 __global__ void row_weights_kernel(const int32_t* __restrict__ slot, const float* __restrict__ p, int64_t n,
@@ -205,25 +252,23 @@ __global__ void row_weights_kernel(const int32_t* __restrict__ slot, const float
 }  // namespace
 
 hipError_t launch_group(const int32_t* ids, const float* p, int64_t n, int32_t K, int32_t E, int32_t* hist,
-                        int32_t* base, int32_t* offsets, Tile* tiles, int32_t* ntiles, int32_t* src, int32_t* slot,
+                        int32_t* base, int32_t* offsets, const ChunkLists& cl, int32_t* src, int32_t* slot,
                         float* prow, int32_t* err, hipStream_t st) {
     const int64_t nchunks = (n + kGroupChunk - 1) / kGroupChunk;
     if (nchunks > 0) {
         hipLaunchKernelGGL(group_hist_kernel, dim3((unsigned)nchunks), dim3(256), 0, st, ids, n, E, hist, err);
-        hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(1024), 0, st, hist, nchunks, n, E, base, offsets,
-                           tiles, ntiles);
-        hipLaunchKernelGGL(group_scatter_kernel, dim3((unsigned)nchunks), dim3(64), 0, st, ids, p, n, K, E, base,
-                           offsets, src, slot, prow);
+        hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(1024), 0, st, hist, nchunks, n, E, base, offsets, cl);
+        hipLaunchKernelGGL(group_scatter_kernel, dim3((unsigned)nchunks), dim3(64 * kScatterWaves), 0, st, ids, p,
+                           n, K, E, base, offsets, src, slot, prow);
     } else {
         hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(1024), 0, st, hist, (int64_t)0, (int64_t)0, E, base,
-                           offsets, tiles, ntiles);
+                           offsets, cl);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_tiles_from_offsets(const int32_t* offsets, int32_t E, Tile* tiles, int32_t* ntiles,
-                                     hipStream_t st) {
-    hipLaunchKernelGGL(tiles_from_offsets_kernel, dim3(1), dim3(1024), 0, st, offsets, E, tiles, ntiles);
+hipError_t launch_chunks_from_offsets(const int32_t* offsets, int32_t E, const ChunkLists& cl, hipStream_t st) {
+    hipLaunchKernelGGL(chunks_from_offsets_kernel, dim3(1), dim3(1024), 0, st, offsets, E, cl);
     return hipGetLastError();
 }
 

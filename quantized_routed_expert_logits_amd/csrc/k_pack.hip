@@ -4,15 +4,17 @@
 // The pages pass each expert to the fused kernels as one blob in its own
 // (Q2_0 / GGUF) layout, 16-byte aligned (Strata compare v0.1.35...v0.1.37
 // page, moe_fused.hpp, Batch).  This layout is this library's own: a
-// workgroup streams one 1280-byte record per 32-wide block of the reduction
-// dimension for its 128-row slab, which its 256 threads unpack one dword each.
+// GEMM work item streams one 1280-byte record per 32-wide block of the
+// reduction dimension for its 128-row slab (256 code dwords and 128 scales).
 //
 // For an M x Kd matrix (reduction over Kd), slab s (128 rows = 8 MFMA
 // fragments of 16 rows), block b, the record at ((s * Kd/32) + b) * 1280:
-//   codes  [4 fragment pairs p][64 lanes l] u32 -- 16 codes of fragments 2p
+//   codes  [64 lanes l][4 fragment pairs p] u32 -- 16 codes of fragments 2p
 //          and 2p+1 for row r = l % 16 and k = 32b + 8*(l/16) + i (i < 8);
 //          element m' = 8*(f - 2p) + i sits at bits 16*(m' % 2) + 2*(m' / 2);
-//   scales [4 pairs p][16 rows r][2] fp16 -- d of fragment 2p + w, row r.
+//          so one lane's four dwords (all 8 fragments) are 16 contiguous bytes;
+//   scales [16 rows r][4 pairs p][2] fp16 -- d of fragment 2p + w, row r; so
+//          the 8 scales a lane of row r needs are 16 contiguous bytes.
 // Row map: gate/up (M = 2I, slab = 64 gate + 64 up rows): fragment f < 4 is
 // gate row 64s + 16f + r, f >= 4 is up row I + 64s + 16(f-4) + r; down
 // (M = H): row 128s + 16f + r.
@@ -27,8 +29,8 @@ __device__ __forceinline__ int row_of(int f, int r, int s, int gate_up_I) {
     return kSlabRows * s + 16 * f + r;
 }
 
-// One thread per (expert, slab, block, pair, lane): one code dword, and the
-// 2 scales of (pair, row) for lanes < 16.
+// One thread per (expert, slab, block, lane, pair): one code dword, and the
+// 2 scales of (row, pair) for lanes < 16.
 __global__ void pack_kernel(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int32_t nexp,
                             int32_t M, int32_t Kd, int32_t gate_up_I, uint8_t* __restrict__ dst, int64_t stride) {
     const int nslab = M / kSlabRows, nblk = Kd / kBlock;
@@ -41,7 +43,7 @@ __global__ void pack_kernel(const uint8_t* __restrict__ codes, const uint16_t* _
     rest /= nblk;
     const int s = (int)(rest % nslab);
     const int64_t e = rest / nslab;
-    const int p = tau >> 6, lane = tau & 63, r16 = lane & 15, kg = lane >> 4;
+    const int p = tau & 3, lane = tau >> 2, r16 = lane & 15, kg = lane >> 4;
     uint32_t w = 0u;
 #pragma unroll
     for (int mp = 0; mp < 16; ++mp) {
@@ -53,7 +55,7 @@ __global__ void pack_kernel(const uint8_t* __restrict__ codes, const uint16_t* _
     uint8_t* rec = dst + e * stride + ((int64_t)s * nblk + b) * kRecordBytes;
     reinterpret_cast<uint32_t*>(rec)[tau] = w;
     if (kg == 0) {
-        uint16_t* sc = reinterpret_cast<uint16_t*>(rec + kRecordCodeBytes) + (p * 16 + r16) * 2;
+        uint16_t* sc = reinterpret_cast<uint16_t*>(rec + kRecordCodeBytes) + (r16 * 4 + p) * 2;
         sc[0] = scales[(e * M + row_of(2 * p, r16, s, gate_up_I)) * nblk + b];
         sc[1] = scales[(e * M + row_of(2 * p + 1, r16, s, gate_up_I)) * nblk + b];
     }
@@ -71,7 +73,7 @@ __global__ void unpack_kernel(const uint8_t* __restrict__ src, int64_t stride, i
     rest /= nblk;
     const int s = (int)(rest % nslab);
     const int64_t e = rest / nslab;
-    const int p = tau >> 6, lane = tau & 63, r16 = lane & 15, kg = lane >> 4;
+    const int p = tau & 3, lane = tau >> 2, r16 = lane & 15, kg = lane >> 4;
     const uint8_t* rec = src + e * stride + ((int64_t)s * nblk + b) * kRecordBytes;
     const uint32_t w = reinterpret_cast<const uint32_t*>(rec)[tau];
 #pragma unroll
@@ -82,7 +84,7 @@ __global__ void unpack_kernel(const uint8_t* __restrict__ src, int64_t stride, i
         codes[(e * M + row) * Kd + k] = (uint8_t)((w >> (16 * (mp & 1) + 2 * (mp >> 1))) & 3u);
     }
     if (kg == 0) {
-        const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec + kRecordCodeBytes) + (p * 16 + r16) * 2;
+        const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec + kRecordCodeBytes) + (r16 * 4 + p) * 2;
         scales[(e * M + row_of(2 * p, r16, s, gate_up_I)) * nblk + b] = sc[0];
         scales[(e * M + row_of(2 * p + 1, r16, s, gate_up_I)) * nblk + b] = sc[1];
     }

@@ -157,7 +157,7 @@ Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I) {
     const int64_t nchunks = (n + kGroupChunk - 1) / kGroupChunk;
     Layout L;
     Offsets o;
-    o.tiles_cap = max_tiles(n, E);
+    o.tiles_cap = chunk_list_cap(n, E);
     o.logits = L.take<float>(T * E);
     o.wt = L.take<float>((int64_t)E * H);
     o.wb = L.take<_Float16>((int64_t)E * H * 2);
@@ -174,8 +174,8 @@ Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I) {
     o.hist = L.take<int32_t>(nchunks * E);
     o.base = L.take<int32_t>(nchunks * E);
     o.offsets = L.take<int32_t>(E + 1);
-    o.tiles = L.take<Tile>(o.tiles_cap);
-    o.ntiles = L.take<int32_t>(1);
+    o.tiles = L.take<Tile>(2 * o.tiles_cap);
+    o.ntiles = L.take<int32_t>(kSchedInts);
     o.err = L.take<int32_t>(1);
     o.src = L.take<int32_t>(n);
     o.slot = L.take<int32_t>(n);
@@ -342,21 +342,21 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     tm.end(kTopK);
     tm.begin(kGroup);
     HIP_TRY(launch_fill_zero((float*)b.err, 1, st), "fill launch");
-    HIP_TRY(launch_group(b.ids, b.p, n, K, E, b.hist, b.base, b.offsets, b.tiles, b.ntiles, b.src, b.slot, b.prow,
-                         b.err, st),
+    const ChunkLists cl{b.tiles, b.ntiles, b.tiles_cap};
+    HIP_TRY(launch_group(b.ids, b.p, n, K, E, b.hist, b.base, b.offsets, cl, b.src, b.slot, b.prow, b.err, st),
             "group launch");
     tm.end(kGroup);
     tm.begin(kGateUp);
-    HIP_TRY(launch_gate_up((const uint8_t*)ex->gate_up, ex->gate_up_stride, b.tiles, b.ntiles, b.tiles_cap, b.src,
-                           b.xb, T, b.xe, b.xuop, b.xum, H, I, b.hq, b.hs, st),
+    HIP_TRY(launch_gate_up((const uint8_t*)ex->gate_up, ex->gate_up_stride, cl, n, E, b.src, b.xb, T, b.xe, b.xuop, b.xum, H,
+                           I, b.hq, b.hs, st),
             "gate/up launch");
     tm.end(kGateUp);
     tm.begin(kPrescaleH);
     HIP_TRY(launch_prescale(b.hq, b.hs, n, I, 1, b.hb, b.he, b.huop, b.hum, st), "prescale launch");
     tm.end(kPrescaleH);
     tm.begin(kDown);
-    HIP_TRY(launch_down((const uint8_t*)ex->down, ex->down_stride, b.tiles, b.ntiles, b.tiles_cap, b.src, b.prow,
-                        b.hb, n, b.he, b.huop, b.hum, H, I, b.dm, st),
+    HIP_TRY(launch_down((const uint8_t*)ex->down, ex->down_stride, cl, n, E, b.src, b.prow, b.hb, n, b.he, b.huop, b.hum,
+                        H, I, b.dm, st),
             "down launch");
     tm.end(kDown);
     tm.begin(kCombine);
@@ -539,13 +539,14 @@ int strata_moe_group(const int32_t* ids, int64_t T, int32_t K, int32_t E, int32_
     const int64_t nchunks = (n + kGroupChunk - 1) / kGroupChunk;
     Layout L;
     const size_t o_hist = L.take<int32_t>(nchunks * E), o_base = L.take<int32_t>(nchunks * E);
-    const size_t o_tiles = L.take<Tile>(max_tiles(n, E)), o_nt = L.take<int32_t>(1), o_err = L.take<int32_t>(1);
+    const int64_t cap = chunk_list_cap(n, E);
+    const size_t o_tiles = L.take<Tile>(2 * cap), o_nt = L.take<int32_t>(kSchedInts), o_err = L.take<int32_t>(1);
     char* ws = nullptr;
     TRY(get_workspace(L.off, &ws));
     int32_t* err = (int32_t*)(ws + o_err);
     HIP_TRY(launch_fill_zero((float*)err, 1, st), "fill launch");
     HIP_TRY(launch_group(ids, nullptr, n, K, E, (int32_t*)(ws + o_hist), (int32_t*)(ws + o_base), offsets,
-                         (Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), src, slot, nullptr, err, st),
+                         ChunkLists{(Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), cap}, src, slot, nullptr, err, st),
             "group launch");
     int32_t herr = 0;
     HIP_TRY(hipMemcpyAsync(&herr, err, 4, hipMemcpyDeviceToHost, st), "hipMemcpyAsync");
@@ -580,17 +581,19 @@ int strata_moe_gate_up(const int8_t* qx, const float* sx, const int32_t* offsets
     Layout L;
     const size_t o_xb = L.take<_Float16>(2 * T * H), o_xe = L.take<float>(T);
     const size_t o_xuop = L.take<_Float16>(T * offset_operand_halves(H)), o_xum = L.take<float>(T);
-    const size_t o_tiles = L.take<Tile>(max_tiles(n, E)), o_nt = L.take<int32_t>(1);
+    const int64_t cap = chunk_list_cap(n, E);
+    const size_t o_tiles = L.take<Tile>(2 * cap), o_nt = L.take<int32_t>(kSchedInts);
     char* ws = nullptr;
     TRY(get_workspace(L.off, &ws));
+    const ChunkLists cl{(Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), cap};
     _Float16* xb = (_Float16*)(ws + o_xb);
     float* xe = (float*)(ws + o_xe);
     _Float16* xuop = (_Float16*)(ws + o_xuop);
     float* xum = (float*)(ws + o_xum);
     HIP_TRY(launch_prescale(qx, sx, T, H, 2, xb, xe, xuop, xum, st), "prescale launch");
-    HIP_TRY(launch_tiles_from_offsets(offsets, E, (Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), st), "tiles launch");
-    HIP_TRY(launch_gate_up((const uint8_t*)experts->gate_up, experts->gate_up_stride, (Tile*)(ws + o_tiles),
-                           (int32_t*)(ws + o_nt), max_tiles(n, E), src, xb, T, xe, xuop, xum, H, I, qh, sh, st),
+    HIP_TRY(launch_chunks_from_offsets(offsets, E, cl, st), "chunk list launch");
+    HIP_TRY(launch_gate_up((const uint8_t*)experts->gate_up, experts->gate_up_stride, cl, n, E, src, xb, T, xe, xuop, xum,
+                           H, I, qh, sh, st),
             "gate/up launch");
     return 0;
 }
@@ -611,10 +614,12 @@ int strata_moe_down(const int8_t* qh, const float* sh, const int32_t* offsets, c
     Layout L;
     const size_t o_hb = L.take<_Float16>(n * I), o_he = L.take<float>(n);
     const size_t o_huop = L.take<_Float16>(n * offset_operand_halves(I)), o_hum = L.take<float>(n);
-    const size_t o_tiles = L.take<Tile>(max_tiles(n, E)), o_nt = L.take<int32_t>(1), o_prow = L.take<float>(n);
+    const int64_t cap = chunk_list_cap(n, E);
+    const size_t o_tiles = L.take<Tile>(2 * cap), o_nt = L.take<int32_t>(kSchedInts), o_prow = L.take<float>(n);
     const size_t o_dm = L.take<float>(n * H);
     char* ws = nullptr;
     TRY(get_workspace(L.off, &ws));
+    const ChunkLists cl{(Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), cap};
     _Float16* hb = (_Float16*)(ws + o_hb);
     float* he = (float*)(ws + o_he);
     _Float16* huop = (_Float16*)(ws + o_huop);
@@ -622,10 +627,10 @@ int strata_moe_down(const int8_t* qh, const float* sh, const int32_t* offsets, c
     float* prow = (float*)(ws + o_prow);
     float* dm = (float*)(ws + o_dm);
     HIP_TRY(launch_prescale(qh, sh, n, I, 1, hb, he, huop, hum, st), "prescale launch");
-    HIP_TRY(launch_tiles_from_offsets(offsets, E, (Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), st), "tiles launch");
+    HIP_TRY(launch_chunks_from_offsets(offsets, E, cl, st), "chunk list launch");
     HIP_TRY(launch_row_weights(slot, p, n, prow, st), "weights launch");
-    HIP_TRY(launch_down((const uint8_t*)experts->down, experts->down_stride, (Tile*)(ws + o_tiles),
-                        (int32_t*)(ws + o_nt), max_tiles(n, E), src, prow, hb, n, he, huop, hum, H, I, dm, st),
+    HIP_TRY(launch_down((const uint8_t*)experts->down, experts->down_stride, cl, n, E, src, prow, hb, n, he, huop, hum, H,
+                        I, dm, st),
             "down launch");
     HIP_TRY(launch_combine(dm, slot, T, K, H, out, st), "combine launch");
     return 0;
