@@ -236,7 +236,6 @@ __global__ void __launch_bounds__(256) transpose_kernel(const float* __restrict_
 
 // ------------------------------------------------------------------ top-K
 constexpr int kPerLane = kMaxExperts / 64;
-constexpr int kBatch = 8;  // re-scored dot products computed together
 
 __device__ __forceinline__ bool better(float v, int e, float bv, int be) { return v > bv || (v == bv && e < be); }
 __device__ __forceinline__ bool better_d(double v, int e, double bv, int be) {
@@ -302,19 +301,23 @@ __device__ __forceinline__ void select_token(const float* __restrict__ l, int32_
     }
 }
 
-// ids / p of one token from its ranked values (softmax over the K, in double).
-__device__ __forceinline__ void write_token(const double (&lv)[kMaxTopK], const int (&li)[kMaxTopK], int32_t K,
-                                            int lane, int64_t t, int32_t* __restrict__ ids, float* __restrict__ p_out) {
-    const double m = lv[0];
-    double z = 0.0;
+// ids / p of one token from its ranked values: the softmax over the K, in
+// fp32 (values relative to the largest, each term in (0, 1]).
+template <typename V>
+__device__ __forceinline__ void write_token(const V (&lv)[kMaxTopK], const int (&li)[kMaxTopK], int32_t K, int lane,
+                                            int64_t t, int32_t* __restrict__ ids, float* __restrict__ p_out) {
+    float ev[kMaxTopK];
+    float z = 0.0f;
 #pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k)
-        if (k < K) z += exp(lv[k] - m);
+    for (int k = 0; k < kMaxTopK; ++k) {
+        ev[k] = k < K ? expf((float)(lv[k] - lv[0])) : 0.0f;
+        z += ev[k];
+    }
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k)
         if (k < K && lane == k) {
             ids[t * K + k] = li[k];
-            p_out[t * K + k] = (float)(exp(lv[k] - m) / z);
+            p_out[t * K + k] = ev[k] / z;
         }
 }
 
@@ -336,132 +339,104 @@ __global__ void __launch_bounds__(256) topk_select_kernel(const float* __restric
         }
         return;
     }
-    double lv[kMaxTopK];
+    float lv[kMaxTopK];
     int li[kMaxTopK];
 #pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k) lv[k] = (double)S.selv[k], li[k] = S.seli[k];
+    for (int k = 0; k < kMaxTopK; ++k) lv[k] = S.selv[k], li[k] = S.seli[k];
     write_token(lv, li, K, lane, t, ids, p_out);
 }
 
-// One workgroup per listed token (grid-stride over the list).  Candidates:
-// every expert within delta below the K-th value (this includes all K
-// selected).  Selected ranks outside every near-tie keep their fp32 value:
-// each is at least delta away from any value that is re-scored, so the merged
-// order is the exact one.  The others are re-scored as fp64 dot products by
-// all 256 threads, up to kBatch at a time (each thread takes H/256 products of
-// each), then wave 0 re-ranks the candidates.
+// The fp64 dot product x[0..H) . w[0..H) over one wave (every lane ends with
+// the sum); lane l takes elements l, l + 64, ... (H a multiple of 64).
+__device__ __forceinline__ double wave_dot_fp64(const float* __restrict__ x, const float* __restrict__ w, int32_t H,
+                                                int lane) {
+    double acc = 0.0;
+    int h = lane;
+    for (; h + 64 * 7 < H; h += 64 * 8) {  // 8 independent loads of each operand in flight
+        float xv[8], wv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xv[j] = x[h + 64 * j], wv[j] = w[h + 64 * j];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc = fma((double)xv[j], (double)wv[j], acc);
+    }
+    for (; h < H; h += 64) acc = fma((double)x[h], (double)w[h], acc);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    return acc;
+}
+
+// One wave per listed token (grid-stride over the list), no workgroup
+// barrier.  Candidates: every expert within delta below the K-th value (this
+// includes all K selected).  Selected ranks outside every near-tie keep their
+// fp32 value: each is at least delta away from any value that is re-scored,
+// so the merged order is the exact one.  The others are re-scored one at a
+// time as wave-wide fp64 dot products; then the candidates are re-ranked.
+// Lane l keeps the candidates among experts l, l + 64, ... in registers.
 __global__ void __launch_bounds__(256) topk_resolve_kernel(const float* __restrict__ logits,
                                                            const float* __restrict__ x, const float* __restrict__ wt,
                                                            const float* __restrict__ bias, int32_t H, int32_t E,
                                                            int32_t K, const int32_t* __restrict__ amb,
                                                            int32_t* __restrict__ ids, float* __restrict__ p_out) {
-    __shared__ int cidx[kMaxExperts];
-    __shared__ double cval[kMaxExperts];
-    __shared__ int jobs[kMaxExperts];
-    __shared__ double part[kWaves][kBatch];
-    __shared__ int counts[2];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = amb[0];
-    for (int it = blockIdx.x; it < n; it += gridDim.x) {  // uniform over the workgroup
+    for (int it = blockIdx.x * kWaves + wave; it < n; it += gridDim.x * kWaves) {  // uniform over the wave
         const int64_t t = amb[1 + it];
         Selection S;
-        if (wave == 0) {
-            select_token(logits + t * E, E, K, lane, S);
-            const float thr = S.vK - S.delta;
-            int nc = 0, nj = 0;
+        select_token(logits + t * E, E, K, lane, S);
+        const float thr = S.vK - S.delta;
+        double cv[kPerLane];
+        uint32_t cand = 0, todo = 0;
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i) {
+            const int e = lane + 64 * i;
+            const bool c = e < E && S.v[i] >= thr;
+            bool stable = false;
+#pragma unroll
+            for (int k = 0; k < kMaxTopK; ++k)
+                if (k < K && !((S.loose >> k) & 1u) && S.seli[k] == e) stable = true;
+            cv[i] = (double)S.v[i];
+            cand |= (uint32_t)c << i;
+            todo |= (uint32_t)(c && !stable) << i;
+        }
+        const float* xr = x + t * H;
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i) {
+            uint64_t m = __ballot((todo >> i) & 1u);
+            while (m) {  // uniform over the wave
+                const int l = __ffsll((unsigned long long)m) - 1;
+                m &= m - 1ull;
+                const int e = l + 64 * i;
+                double v = wave_dot_fp64(xr, wt + (int64_t)e * H, H, lane);
+                if (bias) v += (double)bias[e];
+                if (lane == l) cv[i] = v;
+            }
+        }
+        double lv[kMaxTopK];
+        int li[kMaxTopK];
+        uint32_t tk = 0;
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k) {
+            lv[k] = -DBL_MAX;
+            li[k] = INT_MAX;
+            if (k >= K) continue;
+            double bv = -DBL_MAX;
+            int bi = INT_MAX;
 #pragma unroll
             for (int i = 0; i < kPerLane; ++i) {
                 const int e = lane + 64 * i;
-                const bool cand = e < E && S.v[i] >= thr;
-                bool stable = false;
-#pragma unroll
-                for (int k = 0; k < kMaxTopK; ++k)
-                    if (k < K && !((S.loose >> k) & 1u) && S.seli[k] == e) stable = true;
-                const uint64_t m = __ballot(cand);
-                const uint64_t mj = __ballot(cand && !stable);
-                if (cand) {
-                    const int c = nc + __popcll(m & ((1ull << lane) - 1ull));
-                    cidx[c] = e;
-                    cval[c] = (double)S.v[i];
-                    if (!stable) jobs[nj + __popcll(mj & ((1ull << lane) - 1ull))] = c;
-                }
-                nc += __popcll(m);
-                nj += __popcll(mj);
+                if (((cand & ~tk) >> i) & 1u && better_d(cv[i], e, bv, bi)) bv = cv[i], bi = e;
             }
-            if (lane == 0) counts[0] = nc, counts[1] = nj;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                const double ov = __shfl_xor(bv, off);
+                const int oi = __shfl_xor(bi, off);
+                if (better_d(ov, oi, bv, bi)) bv = ov, bi = oi;
+            }
+            lv[k] = bv;
+            li[k] = bi;
+            if (bi < E && (bi & 63) == lane) tk |= 1u << (bi >> 6);
         }
-        __syncthreads();
-        const int nj = counts[1];
-        const float* xr = x + t * H;
-        for (int j0 = 0; j0 < nj; j0 += kBatch) {  // uniform
-            double acc[kBatch];
-            int ej[kBatch];
-#pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
-                acc[b] = 0.0;
-                ej[b] = j0 + b < nj ? cidx[jobs[j0 + b]] : -1;
-            }
-            for (int h = tid; h < H; h += 256) {
-                const double xv = (double)xr[h];
-#pragma unroll
-                for (int b = 0; b < kBatch; ++b)
-                    if (ej[b] >= 0) acc[b] = fma(xv, (double)wt[(int64_t)ej[b] * H + h], acc[b]);
-            }
-#pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
-#pragma unroll
-                for (int off = 32; off > 0; off >>= 1) acc[b] += __shfl_xor(acc[b], off);
-                if (lane == 0) part[wave][b] = acc[b];
-            }
-            __syncthreads();
-            if (tid < kBatch && j0 + tid < nj) {
-                double v = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]);
-                const int c = jobs[j0 + tid];
-                if (bias) v += (double)bias[cidx[c]];
-                cval[c] = v;
-            }
-            __syncthreads();
-        }
-        if (wave == 0) {
-            const int nc = counts[0];
-            double cv[kPerLane];
-            int ci[kPerLane];
-#pragma unroll
-            for (int i = 0; i < kPerLane; ++i) {
-                const int c = lane + 64 * i;
-                cv[i] = c < nc ? cval[c] : -DBL_MAX;
-                ci[i] = c < nc ? cidx[c] : INT_MAX;
-            }
-            double lv[kMaxTopK];
-            int li[kMaxTopK];
-            uint32_t tk = 0;
-#pragma unroll
-            for (int k = 0; k < kMaxTopK; ++k) {
-                lv[k] = -DBL_MAX;
-                li[k] = INT_MAX;
-                if (k >= K) continue;
-                double bv = -DBL_MAX;
-                int bi = INT_MAX, bslot = -1;
-#pragma unroll
-                for (int i = 0; i < kPerLane; ++i)
-                    if (!((tk >> i) & 1u) && ci[i] != INT_MAX && better_d(cv[i], ci[i], bv, bi))
-                        bv = cv[i], bi = ci[i], bslot = i;
-                int bl = bslot >= 0 ? lane : 64;
-#pragma unroll
-                for (int off = 32; off > 0; off >>= 1) {
-                    const double ov = __shfl_xor(bv, off);
-                    const int oi = __shfl_xor(bi, off);
-                    const int os = __shfl_xor(bslot, off);
-                    const int ol = __shfl_xor(bl, off);
-                    if (better_d(ov, oi, bv, bi)) bv = ov, bi = oi, bslot = os, bl = ol;
-                }
-                lv[k] = bv;
-                li[k] = bi;
-                if (bl == lane && bslot >= 0) tk |= 1u << bslot;
-            }
-            write_token(lv, li, K, lane, t, ids, p_out);
-        }
-        __syncthreads();  // cidx / cval / counts are reused by the next token
+        write_token(lv, li, K, lane, t, ids, p_out);
     }
 }
 
@@ -489,7 +464,7 @@ hipError_t launch_topk(const float* logits, const float* x, const float* wt, con
         hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, amb, 1, 0);
         hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)((T + kWaves - 1) / kWaves)), dim3(64 * kWaves), 0, st,
                            logits, T, E, K, amb, ids, p);
-        const unsigned grid = (unsigned)(T < 2048 ? T : 2048);
+        const unsigned grid = (unsigned)((T < 8192 ? T : 8192) + kWaves - 1) / kWaves;
         hipLaunchKernelGGL(topk_resolve_kernel, dim3(grid), dim3(256), 0, st, logits, x, wt, bias, H, E, K, amb, ids,
                            p);
     }
