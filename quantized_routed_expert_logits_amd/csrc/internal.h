@@ -49,7 +49,7 @@ inline int64_t offset_operand_halves(int32_t Kd) { return (int64_t)((Kd / kBlock
 // ---- launchers; each returns hipGetLastError() after its launches.
 hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q8, float* s, hipStream_t st);
 // fp16 GEMM operand q * s * 2^-e_r of int8 rows (parts 1: one fp16; 2: hi and
-// lo fp16 per value, block-interleaved) and the row multipliers 2^e_r; plus
+// lo fp16 per value: per 32-wide block its 32 hi then its 32 lo values) and the row multipliers 2^e_r; plus
 // the offset-pass operand (u per block, hi/lo, [rows][offset_operand_halves])
 // and its row multipliers.
 hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_t cols, int parts, _Float16* out,
@@ -58,12 +58,14 @@ hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t st);
 
 // Router scratch: wt [E][H] fp32 (transposed weight, also read by the top-K
 // re-score), wb [E][H][2] fp16 (its hi/lo form), wm [E], xm [T] (input row
-// multipliers, used when the caller passes none).
+// multipliers, used when the caller passes none), pmax [H/32][E] (column
+// maxima of 32-row tiles of the weight).
 struct RouterScratch {
     float* wt;
     _Float16* wb;
     float* wm;
     float* xm;
+    float* pmax;
 };
 // logits [T][E]; xm: the input rows' power-of-two multipliers (the prescale's
 // row multipliers of the same rows) or nullptr to compute them.

@@ -107,6 +107,30 @@ __device__ __forceinline__ float round_half_away(float t) {
     return copysignf(fminf(r, 127.0f), t);
 }
 
+// Activation (B operand) fragments are read coalesced, then moved into the
+// MFMA layout.  In the MFMA layout lane d holds column (routed row) d % 16 and
+// value group d / 16 of a block, so consecutive lanes would read 16 different
+// rows, one L1 access each.  Instead loader lane L = 16a + 4c + k reads tile
+// row 4c + a, group k: four consecutive lanes read one row's 64 contiguous
+// bytes of a part.  Lane d then takes (ds_bpermute) the loader lane of its
+// row and group, L = 16 (r % 4) + 4 (r / 4) + g for r = d % 16, g = d / 16:
+// an exchange of lane-index bits {0,1} and {4,5}.
+__device__ __forceinline__ int loader_row(int lane) { return 4 * ((lane >> 2) & 3) + (lane >> 4); }
+
+__device__ __forceinline__ int mfma_source_addr(int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    return 4 * (16 * (r & 3) + 4 * (r >> 2) + g);  // byte address of the source lane
+}
+
+__device__ __forceinline__ half8_t to_mfma_layout(half8_t v, int addr) {
+    uint4 u = __builtin_bit_cast(uint4, v);
+    u.x = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)u.x);
+    u.y = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)u.y);
+    u.z = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)u.z);
+    u.w = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)u.w);
+    return __builtin_bit_cast(half8_t, u);
+}
+
 struct GemmArgs {
     const uint8_t* blobs;  // packed matrices, one per expert
     int64_t stride;        // bytes between experts
@@ -139,7 +163,7 @@ struct BlockLoop {
     __amdgpu_buffer_rsrc_t rec;  // this slab's records (nblk x 1280 bytes)
     __amdgpu_buffer_rsrc_t act;  // prescaled activations [rows][Kd x P] fp16
     int32_t Kd, nblk, dstride;
-    int tau, lane, r16, kg, p;
+    int tau, lane, r16, kg, p, paddr;
     _Float16* d_lds;
     half8_t (*a_lds)[kFrags][64];
     UnpackMagic mg;
@@ -152,22 +176,19 @@ struct BlockLoop {
         sw = __builtin_amdgcn_raw_buffer_load_b32(rec, kRecordCodeBytes + (tau & 63) * 4, blk * kRecordBytes, 0);
     }
 
-    // Activation fragments of a block: lane (r16, kg) takes values 8kg..8kg+7
-    // of its row (P x 16 contiguous bytes).  Padding rows (arow < 0) read row
-    // 0; their results are never stored.
+    // Activation fragments of a block in the loader layout (see loader_row):
+    // lvoff[i] is this lane's byte offset of its loader row and group in tile
+    // i; a block holds P parts of 64 bytes per row.
     template <int NT>
-    __device__ __forceinline__ void load_act(int blk, const int64_t (&arow)[kTilesPerWave],
+    __device__ __forceinline__ void load_act(int blk, const int (&lvoff)[kTilesPerWave],
                                              half8_t (&bf)[kTilesPerWave][P]) const {
         blk = blk < nblk ? blk : nblk - 1;
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
-            const int r = arow[i] >= 0 ? (int)arow[i] : 0;
-            const int voff = r * Kd * 2 * P + kg * 16 * P;
+        for (int i = 0; i < NT; ++i)
 #pragma unroll
             for (int h = 0; h < P; ++h)
                 bf[i][h] = __builtin_bit_cast(
-                    half8_t, __builtin_amdgcn_raw_buffer_load_b128(act, voff + 16 * h, blk * kBlock * 2 * P, 0));
-        }
+                    half8_t, __builtin_amdgcn_raw_buffer_load_b128(act, lvoff[i] + 64 * h, blk * kBlock * 2 * P, 0));
     }
 
     // Thread tau unpacks dword tau of the record: fragments 2p and 2p+1 of
@@ -187,8 +208,13 @@ struct BlockLoop {
     }
 
     template <int NT>
-    __device__ __forceinline__ void products(int blk, const half8_t (&bf)[kTilesPerWave][P],
+    __device__ __forceinline__ void products(int blk, const half8_t (&raw)[kTilesPerWave][P],
                                              float4_t (&acc)[kFrags][kTilesPerWave]) const {
+        half8_t bf[kTilesPerWave][P];
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int h = 0; h < P; ++h) bf[i][h] = to_mfma_layout(raw[i][h], paddr);
         // A fragments in two groups of four (registers are tight: the next
         // block's unpack interleaves with these MFMAs)
 #pragma unroll
@@ -214,7 +240,7 @@ struct BlockLoop {
     // register sets.  D divides nblk, so the unrolled body has no exit in the
     // middle and every ring index is a compile-time constant.
     template <int NT, int D>
-    __device__ __forceinline__ void run(const int64_t (&arow)[kTilesPerWave],
+    __device__ __forceinline__ void run(const int (&lvoff)[kTilesPerWave],
                                         float4_t (&acc)[kFrags][kTilesPerWave]) const {
         static_assert(D % 2 == 0, "activation sets alternate per block");
         uint32_t xw[D], sw[D];
@@ -225,7 +251,7 @@ struct BlockLoop {
 #pragma unroll
         for (int j = 0; j < D; ++j) load_record(j, xw[j], sw[j]);
         __builtin_amdgcn_sched_barrier(0);
-        load_act<NT>(0, arow, bf[0]);
+        load_act<NT>(0, lvoff, bf[0]);
         __builtin_amdgcn_sched_barrier(0);
         for (int b = 0; b < nblk; b += D) {
 #pragma unroll
@@ -234,7 +260,7 @@ struct BlockLoop {
                 unpack(blk, xw[j], sw[j]);
                 __syncthreads();
                 load_record(blk + D, xw[j], sw[j]);
-                load_act<NT>(blk + 1, arow, bf[(j + 1) & 1]);
+                load_act<NT>(blk + 1, lvoff, bf[(j + 1) & 1]);
                 __builtin_amdgcn_sched_barrier(0);  // loads go out before the MFMAs
                 products<NT>(blk, bf[j & 1], acc);
             }
@@ -334,16 +360,24 @@ __device__ __forceinline__ void big_chunk_item(const GemmArgs& g, const Tile tl,
     // zero the padding blocks of the offset-pass matrix: two threads per row
     for (int c = nblk + (tau & 1); c < nch * 32; c += 2) d_lds[(tau >> 1) * dstride + c] = (_Float16)0.0f;
 
-    // this wave's tiles
+    // this wave's tiles: arow = activation row of this lane's MFMA column,
+    // lvoff = byte offset of its loader row and group (padding rows read row 0
+    // and are never stored)
+    constexpr int P = kGateUp ? 2 : 1;
     int64_t arow[kTilesPerWave];
+    int lvoff[kTilesPerWave];
     int ntw = 0;
+    const int tw = wave;
 #pragma unroll
     for (int i = 0; i < kTilesPerWave; ++i) {
-        const int tt = wave + kWaves * i;
-        const int r = 16 * tt + r16;
+        const int tt = tw + kWaves * i;
+        const int r = 16 * tt + r16, lr = 16 * tt + loader_row(lane);
         if (16 * tt < tl.nrows) ntw = i + 1;  // wave-uniform
         arow[i] = -1;
         if (r < tl.nrows) arow[i] = kGateUp ? (int64_t)g.src[tl.row0 + r] : (int64_t)(tl.row0 + r);
+        int64_t la = 0;
+        if (lr < tl.nrows) la = kGateUp ? (int64_t)g.src[tl.row0 + lr] : (int64_t)(tl.row0 + lr);
+        lvoff[i] = (int)la * g.Kd * 2 * P + 16 * (lane & 3);
     }
 
     const uint8_t* rec = g.blobs + (int64_t)tl.e * g.stride + (int64_t)slab * nblk * kRecordBytes;
@@ -354,26 +388,26 @@ __device__ __forceinline__ void big_chunk_item(const GemmArgs& g, const Tile tl,
     for (int f = 0; f < kFrags; ++f)
 #pragma unroll
         for (int i = 0; i < kTilesPerWave; ++i) acc[f][i] = (float4_t){0.f, 0.f, 0.f, 0.f};
-    constexpr int P = kGateUp ? 2 : 1;
     BlockLoop<P> L{__builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, nblk * kRecordBytes, kBufferWord3),
                    __builtin_amdgcn_make_buffer_rsrc((void*)g.act, (short)0, (int)(g.act_rows * g.Kd * 2 * P),
                                                      kBufferWord3),
-                   g.Kd, nblk, dstride, tau, lane, r16, kg, p, d_lds, a_lds, UnpackMagic()};
+                   g.Kd, nblk, dstride, tau, lane, r16, kg, p, mfma_source_addr(lane), d_lds, a_lds,
+                   UnpackMagic()};
     // wave-uniform: the block loop is straight-line code for 1..3 tiles; the
     // record ring is 8 deep when 8 divides the block count (H = 2560, I = 1024)
     if (nblk % 8 == 0) {
         switch (ntw) {
-            case 1: L.template run<1, 8>(arow, acc); break;
-            case 2: L.template run<2, 8>(arow, acc); break;
-            case 3: L.template run<3, 8>(arow, acc); break;
-            default: L.template run<0, 8>(arow, acc); break;  // no tiles: still unpack and meet every barrier
+            case 1: L.template run<1, 8>(lvoff, acc); break;
+            case 2: L.template run<2, 8>(lvoff, acc); break;
+            case 3: L.template run<3, 8>(lvoff, acc); break;
+            default: L.template run<0, 8>(lvoff, acc); break;  // no tiles: still unpack and meet every barrier
         }
     } else {
         switch (ntw) {
-            case 1: L.template run<1, 2>(arow, acc); break;
-            case 2: L.template run<2, 2>(arow, acc); break;
-            case 3: L.template run<3, 2>(arow, acc); break;
-            default: L.template run<0, 2>(arow, acc); break;
+            case 1: L.template run<1, 2>(lvoff, acc); break;
+            case 2: L.template run<2, 2>(lvoff, acc); break;
+            case 3: L.template run<3, 2>(lvoff, acc); break;
+            default: L.template run<0, 2>(lvoff, acc); break;
         }
     }
     __syncthreads();  // every d of the slab is in LDS
@@ -432,7 +466,7 @@ __device__ __forceinline__ void big_chunk_item(const GemmArgs& g, const Tile tl,
             float4_t a[kFrags];
 #pragma unroll
             for (int f = 0; f < kFrags; ++f) a[f] = acc[f][i];
-            gate_up_store(g, tl, slab, 16 * (wave + kWaves * i) + r16, kg, a);
+            gate_up_store(g, tl, slab, 16 * (tw + kWaves * i) + r16, kg, a);
         }
     } else {
         float* park = reinterpret_cast<float*>(d_lds + kSlabRows * dstride) + wave * 16 * kParkStride;
@@ -442,7 +476,7 @@ __device__ __forceinline__ void big_chunk_item(const GemmArgs& g, const Tile tl,
             float4_t a[kFrags];
 #pragma unroll
             for (int f = 0; f < kFrags; ++f) a[f] = acc[f][i];
-            down_store(g, tl, slab, wave + kWaves * i, lane, arow[i] >= 0 ? g.prow[arow[i]] : 0.f, a, park);
+            down_store(g, tl, slab, tw + kWaves * i, lane, arow[i] >= 0 ? g.prow[arow[i]] : 0.f, a, park);
         }
     }
 }
@@ -480,7 +514,7 @@ template <int P, int NT>
 struct SlabPass {
     __amdgpu_buffer_rsrc_t rec, act;
     int32_t Kd, nblk;
-    int lane, r16, kg;
+    int lane, r16, kg, paddr;
     _Float16* dl;  // [kSlabRows][kDlStride]
     UnpackMagic mg;
 
@@ -497,17 +531,15 @@ struct SlabPass {
         }
     }
 
-    __device__ __forceinline__ void load_act(int blk, const int64_t (&arow)[NT], half8_t (&bf)[NT][P]) const {
+    // Activation fragments of a block in the loader layout (see loader_row).
+    __device__ __forceinline__ void load_act(int blk, const int (&lvoff)[NT], half8_t (&bf)[NT][P]) const {
         blk = blk < nblk ? blk : nblk - 1;
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
-            const int r = arow[i] >= 0 ? (int)arow[i] : 0;
-            const int voff = r * Kd * 2 * P + kg * 16 * P;
+        for (int i = 0; i < NT; ++i)
 #pragma unroll
             for (int h = 0; h < P; ++h)
                 bf[i][h] = __builtin_bit_cast(
-                    half8_t, __builtin_amdgcn_raw_buffer_load_b128(act, voff + 16 * h, blk * kBlock * 2 * P, 0));
-        }
+                    half8_t, __builtin_amdgcn_raw_buffer_load_b128(act, lvoff[i] + 64 * h, blk * kBlock * 2 * P, 0));
     }
 
     // Unpack dword p (fragments 2p, 2p+1) and park its scales for the offset
@@ -525,10 +557,15 @@ struct SlabPass {
     // few VALU instructions), so the matrix unit and the vector ALU of the
     // wave work side by side.
     __device__ __forceinline__ void block(int blk, const uint32_t (&xw)[4], const uint32_t (&sw)[4],
-                                          const half8_t (&bf)[NT][P], float4_t (&acc)[kFrags][NT]) const {
+                                          const half8_t (&raw)[NT][P], float4_t (&acc)[kFrags][NT]) const {
         constexpr int kMfmas = 2 * NT * P;                  // per dword
         constexpr int kValuPer = (26 + kMfmas - 1) / kMfmas;  // unpack instructions per MFMA slot
         const int col = blk & 31;
+        half8_t bf[NT][P];
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int h = 0; h < P; ++h) bf[i][h] = to_mfma_layout(raw[i][h], paddr);
         half8_t a[2][2];
         prepare(0, col, xw, sw, a[0]);
         __builtin_amdgcn_sched_barrier(0);
@@ -590,13 +627,14 @@ struct SlabPass {
     // activation fragments one block ahead in two alternating sets.
     template <int D>
     __device__ __forceinline__ void run(int nch, const _Float16* uop, const int64_t (&arow)[NT],
-                                        const float (&ratio)[NT], float4_t (&acc)[kFrags][NT]) const {
+                                        const int (&lvoff)[NT], const float (&ratio)[NT],
+                                        float4_t (&acc)[kFrags][NT]) const {
         uint32_t xw[D][4], sw[D][4];
         half8_t bf[2][NT][P];
 #pragma unroll
         for (int j = 0; j < D; ++j) load_record(j, xw[j], sw[j]);
         __builtin_amdgcn_sched_barrier(0);
-        load_act(0, arow, bf[0]);
+        load_act(0, lvoff, bf[0]);
         __builtin_amdgcn_sched_barrier(0);
         for (int c = 0; c < nch; ++c) {
             const int bend = nblk < 32 * c + 32 ? nblk : 32 * c + 32;
@@ -604,7 +642,7 @@ struct SlabPass {
 #pragma unroll
                 for (int j = 0; j < D; ++j) {
                     const int blk = b + j;
-                    load_act(blk + 1, arow, bf[(j + 1) & 1]);
+                    load_act(blk + 1, lvoff, bf[(j + 1) & 1]);
                     __builtin_amdgcn_sched_barrier(0);
                     block(blk, xw[j], sw[j], bf[j & 1], acc);
                     load_record(blk + D, xw[j], sw[j]);
@@ -627,13 +665,17 @@ __device__ __forceinline__ void small_chunk_pass(const GemmArgs& g, const Tile& 
         reinterpret_cast<half8_t*>(dl)[o] = (half8_t){0, 0, 0, 0, 0, 0, 0, 0};
 
     int64_t arow[NT];
+    int lvoff[NT];
     float ratio[NT];
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-        const int r = 16 * (t0 + i) + r16;
+        const int r = 16 * (t0 + i) + r16, lr = 16 * (t0 + i) + loader_row(lane);
         arow[i] = -1;
         if (r < tl.nrows) arow[i] = kGateUp ? (int64_t)g.src[tl.row0 + r] : (int64_t)(tl.row0 + r);
         ratio[i] = arow[i] >= 0 ? g.um[arow[i]] / g.am[arow[i]] : 0.f;
+        int64_t la = 0;
+        if (lr < tl.nrows) la = kGateUp ? (int64_t)g.src[tl.row0 + lr] : (int64_t)(tl.row0 + lr);
+        lvoff[i] = (int)la * g.Kd * 2 * P + 16 * (lane & 3);
     }
     float4_t acc[kFrags][NT];
 #pragma unroll
@@ -645,8 +687,8 @@ __device__ __forceinline__ void small_chunk_pass(const GemmArgs& g, const Tile& 
     SlabPass<P, NT> L{__builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, nblk * kRecordBytes, kBufferWord3),
                       __builtin_amdgcn_make_buffer_rsrc((void*)g.act, (short)0, (int)(g.act_rows * g.Kd * 2 * P),
                                                         kBufferWord3),
-                      g.Kd, nblk, lane, r16, kg, dl, UnpackMagic()};
-    L.template run<2>(nch, g.uop, arow, ratio, acc);
+                      g.Kd, nblk, lane, r16, kg, mfma_source_addr(lane), dl, UnpackMagic()};
+    L.template run<2>(nch, g.uop, arow, lvoff, ratio, acc);
 
 #pragma unroll
     for (int i = 0; i < NT; ++i) {

@@ -24,9 +24,9 @@
 //   parts = 2: hi as above and lo = fp16(v - hi), v = fp32(q * s * 2^-e), so
 //              hi + lo carries about 22 bits (the gate/up GEMM, whose output
 //              is rounded to int8 and must not move the rounding points).
-// parts = 2 layout per row: per 32-wide block, 4 groups of 8 values, each
-// stored as 8 hi then 8 lo (128 bytes per block), so the 32 bytes one MFMA
-// lane needs for a block (its 8 values, hi and lo) are contiguous.
+// parts = 2 layout per row: per 32-wide block, its 32 hi values then its 32
+// lo values (128 bytes per block), so each part of a block is 64 contiguous
+// bytes (four lanes of a GEMM's coalesced fragment load).
 //
 // The same kernel writes the operand of the GEMMs' offset pass: per block,
 // u = -0.5 * s * (sum of the block's codes) (the 2-bit weight offset's share,
@@ -147,20 +147,22 @@ __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict_
             dst[0] = h0;
             dst[1] = h1;
         } else {
-            half8_t g[4];
+            half8_t hi[2], lo[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    _Float16 hi, lo;
-                    split_hi_lo(v[8 * h + i], hi, lo);
-                    g[2 * h][i] = hi;
-                    g[2 * h + 1][i] = lo;
+                    _Float16 a, b;
+                    split_hi_lo(v[8 * h + i], a, b);
+                    hi[h][i] = a;
+                    lo[h][i] = b;
                 }
-            // block j/2, value groups 2*(j%2) and 2*(j%2)+1: 64 contiguous bytes
-            half8_t* dst = reinterpret_cast<half8_t*>(out + row * (int64_t)cols * 2 + 32 * j);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) dst[t] = g[t];
+            // block j/2, values 16*(j%2) .. +15: 32 bytes of its hi part and 32 of its lo part
+            _Float16* blk = out + row * (int64_t)cols * 2 + 64 * (j >> 1) + 16 * (j & 1);
+            reinterpret_cast<half8_t*>(blk)[0] = hi[0];
+            reinterpret_cast<half8_t*>(blk)[1] = hi[1];
+            reinterpret_cast<half8_t*>(blk + 32)[0] = lo[0];
+            reinterpret_cast<half8_t*>(blk + 32)[1] = lo[1];
         }
     }
 #pragma unroll

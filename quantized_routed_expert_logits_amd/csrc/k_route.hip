@@ -69,32 +69,49 @@ __global__ void __launch_bounds__(256) row_scale_kernel(const float* __restrict_
     if (lane == 0) xm[t] = row_multiplier(m);
 }
 
-// From wt [E][H] (the transposed router weight): wb [E][H/8][hi 8, lo 8] of
-// wt * 2^-ew and wm[e] = 2^ew (one wave per expert).
-__global__ void __launch_bounds__(256) router_prep_kernel(const float* __restrict__ wt, int32_t H, int32_t E,
+// From wt [E][H] (the transposed router weight) and the column maxima of its
+// 32-row tiles pmax [H/32][E]: wb [E][H/8][hi 8, lo 8] of wt * 2^-ew and
+// wm[e] = 2^ew (one wave per expert).
+__global__ void __launch_bounds__(256) router_prep_kernel(const float* __restrict__ wt,
+                                                          const float* __restrict__ pmax, int32_t H, int32_t E,
                                                           _Float16* __restrict__ wb, float* __restrict__ wm) {
     const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (e >= E) return;
     const int lane = threadIdx.x & 63;
-    const float* row = wt + (int64_t)e * H;
     float m = 0.0f;
-    for (int h = lane; h < H; h += 64) m = fmaxf(m, fabsf(row[h]));
+    for (int i = lane; i < H / 32; i += 64) m = fmaxf(m, pmax[(int64_t)i * E + e]);
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
     const float mult = row_multiplier(m), inv = 1.0f / mult;  // exact: powers of two
     if (lane == 0) wm[e] = mult;
-    for (int j = lane; j < H / 8; j += 64) {
-        half8_t hi, lo;
+    const float4* row = reinterpret_cast<const float4*>(wt + (int64_t)e * H);
+    half8_t* dst = reinterpret_cast<half8_t*>(wb + (int64_t)e * H * 2);
+    for (int j0 = 0; j0 < H / 8; j0 += 256) {  // 4 groups of 8 values per lane in flight
+        float4 v[4][2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            _Float16 h, l;
-            split_hi_lo(row[8 * j + i] * inv, h, l);
-            hi[i] = h;
-            lo[i] = l;
+        for (int u = 0; u < 4; ++u) {
+            const int j = j0 + 64 * u + lane;
+            if (j < H / 8) {
+                v[u][0] = row[2 * j];
+                v[u][1] = row[2 * j + 1];
+            }
         }
-        half8_t* dst = reinterpret_cast<half8_t*>(wb + ((int64_t)e * H + 8 * j) * 2);
-        dst[0] = hi;
-        dst[1] = lo;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = j0 + 64 * u + lane;
+            if (j >= H / 8) continue;
+            const float f[8] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w, v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
+            half8_t hi, lo;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                _Float16 h, l;
+                split_hi_lo(f[i] * inv, h, l);
+                hi[i] = h;
+                lo[i] = l;
+            }
+            dst[2 * j] = hi;
+            dst[2 * j + 1] = lo;
+        }
     }
 }
 
@@ -218,10 +235,11 @@ __global__ void fill_i32_kernel(int32_t* __restrict__ p, int32_t count, int32_t 
     if (i < count) p[i] = value;
 }
 
-// wt[E][H] = wr[H][E]: the re-score reads one expert's weights as a
-// contiguous row.  32x32 tiles through LDS.
+// wt[E][H] = wr[H][E] (the re-score reads one expert's weights as a
+// contiguous row), 32x32 tiles through LDS; and pmax[tile row][e] = the
+// largest |wr| of expert e in the tile's 32 rows.
 __global__ void __launch_bounds__(256) transpose_kernel(const float* __restrict__ in, int32_t R, int32_t C,
-                                                        float* __restrict__ out) {
+                                                        float* __restrict__ out, float* __restrict__ pmax) {
     __shared__ float tile[32][33];
     const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
     const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
@@ -232,6 +250,11 @@ __global__ void __launch_bounds__(256) transpose_kernel(const float* __restrict_
 #pragma unroll
     for (int k = 0; k < 32; k += 8)
         if (c0 + ty + k < C && r0 + tx < R) out[(int64_t)(c0 + ty + k) * R + r0 + tx] = tile[tx][ty + k];
+    if (ty == 0 && c0 + tx < C) {
+        float m = 0.0f;
+        for (int r = 0; r < 32 && r0 + r < R; ++r) m = fmaxf(m, fabsf(tile[r][tx]));
+        pmax[(int64_t)blockIdx.y * C + c0 + tx] = m;
+    }
 }
 
 // ------------------------------------------------------------------ top-K
@@ -446,9 +469,9 @@ hipError_t launch_router(const float* x, const float* xm, const float* wr, const
                          int32_t E, const RouterScratch& rs, float* logits, hipStream_t st) {
     if (T <= 0) return hipGetLastError();
     hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)((E + 31) / 32), (unsigned)((H + 31) / 32)), dim3(256), 0, st,
-                       wr, H, E, rs.wt);
-    hipLaunchKernelGGL(router_prep_kernel, dim3((unsigned)((E + 3) / 4)), dim3(256), 0, st, rs.wt, H, E, rs.wb,
-                       rs.wm);
+                       wr, H, E, rs.wt, rs.pmax);
+    hipLaunchKernelGGL(router_prep_kernel, dim3((unsigned)((E + 3) / 4)), dim3(256), 0, st, rs.wt, rs.pmax, H, E,
+                       rs.wb, rs.wm);
     if (!xm) {
         hipLaunchKernelGGL(row_scale_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, x, T, H, rs.xm);
         xm = rs.xm;

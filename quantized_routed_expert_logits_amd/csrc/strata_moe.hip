@@ -118,6 +118,7 @@ struct Buffers {
     float* wt;
     _Float16* wb;
     float* wm;
+    float* pmax;
     int32_t* amb;
     int32_t* ids;
     float* p;
@@ -147,7 +148,7 @@ struct Buffers {
 };
 
 struct Offsets {
-    size_t logits, wt, wb, wm, amb, ids, p, xq, xs, xb, xe, xuop, xum, hist, base, offsets, tiles, ntiles, err, src, slot, prow, hq, hs,
+    size_t logits, wt, wb, wm, pmax, amb, ids, p, xq, xs, xb, xe, xuop, xum, hist, base, offsets, tiles, ntiles, err, src, slot, prow, hq, hs,
         hb, he, huop, hum, dm, total;
     int64_t tiles_cap;
 };
@@ -162,6 +163,7 @@ Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I) {
     o.wt = L.take<float>((int64_t)E * H);
     o.wb = L.take<_Float16>((int64_t)E * H * 2);
     o.wm = L.take<float>(E);
+    o.pmax = L.take<float>((int64_t)((H + 31) / 32) * E);
     o.amb = L.take<int32_t>(T + 1);
     o.ids = L.take<int32_t>(n);
     o.p = L.take<float>(n);
@@ -197,6 +199,7 @@ Buffers carve(char* ws, const Offsets& o) {
     b.wt = (float*)(ws + o.wt);
     b.wb = (_Float16*)(ws + o.wb);
     b.wm = (float*)(ws + o.wm);
+    b.pmax = (float*)(ws + o.pmax);
     b.amb = (int32_t*)(ws + o.amb);
     b.ids = (int32_t*)(ws + o.ids);
     b.p = (float*)(ws + o.p);
@@ -333,7 +336,7 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     HIP_TRY(launch_prescale(b.xq, b.xs, T, H, 2, b.xb, b.xe, b.xuop, b.xum, st), "prescale launch");
     tm.end(kQuantize);
     tm.begin(kRouter);
-    HIP_TRY(launch_router(x, b.xe, wr, ex->router_bias, T, H, E, RouterScratch{b.wt, b.wb, b.wm, nullptr}, b.logits,
+    HIP_TRY(launch_router(x, b.xe, wr, ex->router_bias, T, H, E, RouterScratch{b.wt, b.wb, b.wm, nullptr, b.pmax}, b.logits,
                           st),
             "router launch");
     tm.end(kRouter);
@@ -517,11 +520,12 @@ int strata_moe_route(const float* x, const float* router_w, const float* bias, i
     Layout L;
     const size_t lo = L.take<float>(T * E), o_wt = L.take<float>((int64_t)E * H), o_amb = L.take<int32_t>(T + 1);
     const size_t o_wb = L.take<_Float16>((int64_t)E * H * 2), o_wm = L.take<float>(E), o_xm = L.take<float>(T);
+    const size_t o_pm = L.take<float>((int64_t)((H + 31) / 32) * E);
     char* ws = nullptr;
     TRY(get_workspace(L.off, &ws));
     float* logits = (float*)(ws + lo);
     float* wt = (float*)(ws + o_wt);
-    const RouterScratch rs{wt, (_Float16*)(ws + o_wb), (float*)(ws + o_wm), (float*)(ws + o_xm)};
+    const RouterScratch rs{wt, (_Float16*)(ws + o_wb), (float*)(ws + o_wm), (float*)(ws + o_xm), (float*)(ws + o_pm)};
     HIP_TRY(launch_router(x, nullptr, router_w, bias, T, H, E, rs, logits, st), "router launch");
     HIP_TRY(launch_topk(logits, x, wt, bias, T, H, E, K, (int32_t*)(ws + o_amb), ids, p, st), "top-K launch");
     return 0;
