@@ -265,6 +265,85 @@ __device__ __forceinline__ bool better_d(double v, int e, double bv, int be) {
     return v > bv || (v == bv && e < be);
 }
 
+// Wave-wide best (largest value, then lowest index) in every lane, on the
+// vector ALU: quad exchanges (lane ^ 1, lane ^ 2), the mirror within each 8
+// and within each 16 lanes (DPP), then the 16-lane and 32-lane row swaps.
+// After each step a lane holds the best of twice as many lanes.
+template <int kCtrl>
+__device__ __forceinline__ int dpp(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xF, 0xF, false);
+}
+
+template <typename V>
+struct Best {
+    V v;
+    int i;
+};
+
+__device__ __forceinline__ void take_better(Best<float>& a, float v, int i) {
+    if (better(v, i, a.v, a.i)) a.v = v, a.i = i;
+}
+__device__ __forceinline__ void take_better(Best<double>& a, double v, int i) {
+    if (better_d(v, i, a.v, a.i)) a.v = v, a.i = i;
+}
+
+template <int kCtrl>
+__device__ __forceinline__ void best_step(Best<float>& a) {
+    const float v = __builtin_bit_cast(float, dpp<kCtrl>(__builtin_bit_cast(int, a.v)));
+    const int i = dpp<kCtrl>(a.i);
+    take_better(a, v, i);
+}
+template <int kCtrl>
+__device__ __forceinline__ void best_step(Best<double>& a) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, a.v);
+    const uint32_t lo = (uint32_t)dpp<kCtrl>((int)(uint32_t)u), hi = (uint32_t)dpp<kCtrl>((int)(uint32_t)(u >> 32));
+    const int i = dpp<kCtrl>(a.i);
+    take_better(a, __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo), i);
+}
+
+// Each swap returns the row pair's two halves in two registers: lane l holds
+// one of them in each, so one comparison combines the pair.
+__device__ __forceinline__ uint32_t pair_first(uint32_t a, uint32_t b, bool wide, uint32_t* second) {
+    if (wide) {
+        const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+        *second = r[1];
+        return r[0];
+    }
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    *second = r[1];
+    return r[0];
+}
+
+__device__ __forceinline__ void best_swap(Best<float>& a, bool wide) {
+    uint32_t v1, i1;
+    const uint32_t v0 = pair_first(__builtin_bit_cast(uint32_t, a.v), __builtin_bit_cast(uint32_t, a.v), wide, &v1);
+    const uint32_t i0 = pair_first((uint32_t)a.i, (uint32_t)a.i, wide, &i1);
+    a.v = __builtin_bit_cast(float, v0);
+    a.i = (int)i0;
+    take_better(a, __builtin_bit_cast(float, v1), (int)i1);
+}
+__device__ __forceinline__ void best_swap(Best<double>& a, bool wide) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, a.v);
+    uint32_t lo1, hi1, i1;
+    const uint32_t lo0 = pair_first((uint32_t)u, (uint32_t)u, wide, &lo1);
+    const uint32_t hi0 = pair_first((uint32_t)(u >> 32), (uint32_t)(u >> 32), wide, &hi1);
+    const uint32_t i0 = pair_first((uint32_t)a.i, (uint32_t)a.i, wide, &i1);
+    a.v = __builtin_bit_cast(double, ((uint64_t)hi0 << 32) | lo0);
+    a.i = (int)i0;
+    take_better(a, __builtin_bit_cast(double, ((uint64_t)hi1 << 32) | lo1), (int)i1);
+}
+
+template <typename V>
+__device__ __forceinline__ Best<V> wave_best(Best<V> a) {
+    best_step<0xB1>(a);   // quad_perm [1,0,3,2]: lane ^ 1
+    best_step<0x4E>(a);   // quad_perm [2,3,0,1]: lane ^ 2
+    best_step<0x141>(a);  // mirror within 8 lanes: the other quad
+    best_step<0x140>(a);  // mirror within 16 lanes: the other 8
+    best_swap(a, false);  // rows 0/1 and 2/3
+    best_swap(a, true);   // halves 0-31 / 32-63
+    return a;
+}
+
 // The wave-wide selection of one token (every lane ends with the same
 // results): lane l holds logits l, l+64, ... in v; selv/seli get ranks
 // 0..rounds-1 (K+1 rounds, K when K == E) by larger value, then lower index;
@@ -293,20 +372,15 @@ __device__ __forceinline__ void select_token(const float* __restrict__ l, int32_
         S.selv[k] = -FLT_MAX;
         S.seli[k] = INT_MAX;
         if (k >= S.rounds) continue;
-        float bv = -FLT_MAX;
-        int bi = INT_MAX;
+        Best<float> b{-FLT_MAX, INT_MAX};
 #pragma unroll
         for (int i = 0; i < kPerLane; ++i) {
             const int e = lane + 64 * i;
-            if (e < E && !((taken >> i) & 1u) && better(S.v[i], e, bv, bi)) bv = S.v[i], bi = e;
+            if (e < E && !((taken >> i) & 1u)) take_better(b, S.v[i], e);
         }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(bv, off);
-            const int oi = __shfl_xor(bi, off);
-            if (better(ov, oi, bv, bi)) bv = ov, bi = oi;
-        }
-        S.selv[k] = bv;
+        b = wave_best(b);
+        const int bi = b.i;
+        S.selv[k] = b.v;
         S.seli[k] = bi;
         if (bi < E && (bi & 63) == lane) taken |= 1u << (bi >> 6);
     }
@@ -370,19 +444,32 @@ __global__ void __launch_bounds__(256) topk_select_kernel(const float* __restric
 }
 
 // The fp64 dot product x[0..H) . w[0..H) over one wave (every lane ends with
-// the sum); lane l takes elements l, l + 64, ... (H a multiple of 64).
+// the same sum).  Lane l takes 4 consecutive elements of every 256, up to
+// kDotBatch such groups of loads in flight at once; a tail of H % 256
+// elements goes one per lane.
+constexpr int kDotBatch = 10;
 __device__ __forceinline__ double wave_dot_fp64(const float* __restrict__ x, const float* __restrict__ w, int32_t H,
                                                 int lane) {
     double acc = 0.0;
-    int h = lane;
-    for (; h + 64 * 7 < H; h += 64 * 8) {  // 8 independent loads of each operand in flight
-        float xv[8], wv[8];
+    const int n4 = H / 256;
+    for (int c0 = 0; c0 < n4; c0 += kDotBatch) {
+        float4 xv[kDotBatch], wv[kDotBatch];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) xv[j] = x[h + 64 * j], wv[j] = w[h + 64 * j];
+        for (int j = 0; j < kDotBatch; ++j)
+            if (c0 + j < n4) {
+                xv[j] = reinterpret_cast<const float4*>(x)[64 * (c0 + j) + lane];
+                wv[j] = reinterpret_cast<const float4*>(w)[64 * (c0 + j) + lane];
+            }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc = fma((double)xv[j], (double)wv[j], acc);
+        for (int j = 0; j < kDotBatch; ++j)
+            if (c0 + j < n4) {
+                acc = fma((double)xv[j].x, (double)wv[j].x, acc);
+                acc = fma((double)xv[j].y, (double)wv[j].y, acc);
+                acc = fma((double)xv[j].z, (double)wv[j].z, acc);
+                acc = fma((double)xv[j].w, (double)wv[j].w, acc);
+            }
     }
-    for (; h < H; h += 64) acc = fma((double)x[h], (double)w[h], acc);
+    for (int h = 256 * n4 + lane; h < H; h += 64) acc = fma((double)x[h], (double)w[h], acc);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     return acc;
@@ -442,20 +529,13 @@ __global__ void __launch_bounds__(256) topk_resolve_kernel(const float* __restri
             lv[k] = -DBL_MAX;
             li[k] = INT_MAX;
             if (k >= K) continue;
-            double bv = -DBL_MAX;
-            int bi = INT_MAX;
+            Best<double> b{-DBL_MAX, INT_MAX};
 #pragma unroll
-            for (int i = 0; i < kPerLane; ++i) {
-                const int e = lane + 64 * i;
-                if (((cand & ~tk) >> i) & 1u && better_d(cv[i], e, bv, bi)) bv = cv[i], bi = e;
-            }
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) {
-                const double ov = __shfl_xor(bv, off);
-                const int oi = __shfl_xor(bi, off);
-                if (better_d(ov, oi, bv, bi)) bv = ov, bi = oi;
-            }
-            lv[k] = bv;
+            for (int i = 0; i < kPerLane; ++i)
+                if (((cand & ~tk) >> i) & 1u) take_better(b, cv[i], lane + 64 * i);
+            b = wave_best(b);
+            const int bi = b.i;
+            lv[k] = b.v;
             li[k] = bi;
             if (bi < E && (bi & 63) == lane) tk |= 1u << (bi >> 6);
         }
