@@ -57,9 +57,10 @@ hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_
 hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t st);
 
 // Router scratch: wt [E][H] fp32 (transposed weight, also read by the top-K
-// re-score), wb [E][H][2] fp16 (its hi/lo form), wm [E], xm [T] (input row
-// multipliers, used when the caller passes none), pmax [H/32][E] (column
-// maxima of 32-row tiles of the weight).
+// re-score), wb [Ep][H][2] fp16 (its hi/lo form in MFMA fragment order, Ep =
+// router_padded_experts(E)), wm [Ep], xm [T] (input row multipliers, used when
+// the caller passes none), pmax [H/32][E] (column maxima of 32-row tiles of
+// the weight).
 struct RouterScratch {
     float* wt;
     _Float16* wb;
@@ -67,8 +68,20 @@ struct RouterScratch {
     float* xm;
     float* pmax;
 };
-// logits [T][E]; xm: the input rows' power-of-two multipliers (the prescale's
-// row multipliers of the same rows) or nullptr to compute them.
+// The router GEMM splits the reduction over H into router_splits() ranges
+// when a chunk is short (too few workgroups otherwise); logits then holds
+// that many partial [T][E] arrays, which the top-K adds in order.
+inline int router_splits(int64_t T, int32_t H, int32_t E) {
+    const int64_t nk = H / 32, wgs = ((T + 63) / 64) * ((E + 127) / 128);
+    int s = 1;
+    while (s < 4 && wgs * s < 512 && nk % (4 * s) == 0) s *= 2;
+    return s;
+}
+inline int64_t router_logit_floats(int64_t T, int32_t H, int32_t E) { return router_splits(T, H, E) * T * E; }
+inline int64_t router_padded_experts(int32_t E) { return round_up(E, 16); }
+
+// logits [splits][T][E]; xm: the input rows' power-of-two multipliers (the
+// prescale's row multipliers of the same rows) or nullptr to compute them.
 hipError_t launch_router(const float* x, const float* xm, const float* wr, const float* bias, int64_t T, int32_t H,
                          int32_t E, const RouterScratch& rs, float* logits, hipStream_t st);
 // amb: scratch of T+1 ints (the list of tokens with a near-tie); wt from the router scratch.

@@ -70,35 +70,43 @@ __global__ void __launch_bounds__(256) row_scale_kernel(const float* __restrict_
 }
 
 // From wt [E][H] (the transposed router weight) and the column maxima of its
-// 32-row tiles pmax [H/32][E]: wb [E][H/8][hi 8, lo 8] of wt * 2^-ew and
-// wm[e] = 2^ew (one wave per expert).
+// 32-row tiles pmax [H/32][E]: wb, the hi/lo fp16 form of wt * 2^-ew in MFMA
+// fragment order, and wm[e] = 2^ew (one wave per expert; padding experts up
+// to a multiple of 16 get zeros and wm = 1).  Fragment order: per 16-expert
+// tile and 32-wide k block, the hi fragment then the lo fragment, each 64
+// lanes x 8 values with lane r + 16 g holding expert r of the tile, values
+// 8g..8g+7 of the block; so a wave reads a fragment as 1 KB in one load.
 __global__ void __launch_bounds__(256) router_prep_kernel(const float* __restrict__ wt,
                                                           const float* __restrict__ pmax, int32_t H, int32_t E,
-                                                          _Float16* __restrict__ wb, float* __restrict__ wm) {
+                                                          int32_t Ep, _Float16* __restrict__ wb,
+                                                          float* __restrict__ wm) {
     const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (e >= E) return;
+    if (e >= Ep) return;
     const int lane = threadIdx.x & 63;
+    const int nk = H / 32;
     float m = 0.0f;
-    for (int i = lane; i < H / 32; i += 64) m = fmaxf(m, pmax[(int64_t)i * E + e]);
+    if (e < E)
+        for (int i = lane; i < H / 32; i += 64) m = fmaxf(m, pmax[(int64_t)i * E + e]);
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
     const float mult = row_multiplier(m), inv = 1.0f / mult;  // exact: powers of two
     if (lane == 0) wm[e] = mult;
-    const float4* row = reinterpret_cast<const float4*>(wt + (int64_t)e * H);
-    half8_t* dst = reinterpret_cast<half8_t*>(wb + (int64_t)e * H * 2);
+    const float4* row = reinterpret_cast<const float4*>(wt + (int64_t)(e < E ? e : 0) * H);
+    _Float16* tile = wb + (int64_t)(e >> 4) * nk * 1024;
     for (int j0 = 0; j0 < H / 8; j0 += 256) {  // 4 groups of 8 values per lane in flight
         float4 v[4][2];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int j = j0 + 64 * u + lane;
-            if (j < H / 8) {
+            v[u][0] = v[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (j < H / 8 && e < E) {
                 v[u][0] = row[2 * j];
                 v[u][1] = row[2 * j + 1];
             }
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int j = j0 + 64 * u + lane;
+            const int j = j0 + 64 * u + lane;  // value group j: block j / 4, group j % 4
             if (j >= H / 8) continue;
             const float f[8] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w, v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
             half8_t hi, lo;
@@ -109,8 +117,9 @@ __global__ void __launch_bounds__(256) router_prep_kernel(const float* __restric
                 hi[i] = h;
                 lo[i] = l;
             }
-            dst[2 * j] = hi;
-            dst[2 * j + 1] = lo;
+            half8_t* dst = reinterpret_cast<half8_t*>(tile + (int64_t)(j >> 2) * 1024) + (e & 15) + 16 * (j & 3);
+            dst[0] = hi;
+            dst[64] = lo;
         }
     }
 }
@@ -120,7 +129,10 @@ __global__ void __launch_bounds__(256) router_prep_kernel(const float* __restric
 // tiles).  Per 32-wide k block: the workgroup converts its 64 x 32 input
 // block to hi/lo fp16 into LDS (each thread 8 values), one barrier, then each
 // wave reads the 4 x 2 A fragments and runs 4 x 2 x 3 MFMAs.  Input values
-// and B fragments are loaded two k blocks ahead (H / 32 is even).
+// and B fragments (1 KB loads in fragment order) are loaded two k blocks
+// ahead.  Workgroup z of gridDim.z takes the z-th of gridDim.z equal ranges
+// of k blocks (each of even length) and writes its partial logits to slice z
+// (the bias goes into slice 0).
 constexpr int kRtM = 64, kRtN = 128;
 
 struct RouterStage {
@@ -133,12 +145,12 @@ __global__ void __launch_bounds__(256, 2) router_mfma_kernel(const float* __rest
                                                              const _Float16* __restrict__ wb,
                                                              const float* __restrict__ wm,
                                                              const float* __restrict__ bias, int64_t T, int32_t H,
-                                                             int32_t E, float* __restrict__ out) {
+                                                             int32_t E, int32_t Ep, float* __restrict__ out) {
     __shared__ half8_t a_lds[2][4][2][64];  // [buffer][token tile][hi, lo][lane]
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, kg = lane >> 4;
     const int n0 = blockIdx.x * kRtN;
     const int64_t m0 = (int64_t)blockIdx.y * kRtM;
-    const int nk = H / 32;
+    const int nk = H / 32, kper = nk / gridDim.z, kb0 = blockIdx.z * kper, kb1 = kb0 + kper;
 
     // staging role: token row sr of the tile, value group sk (8 values) of the k block
     const int sr = tid >> 2, sk = tid & 3;
@@ -147,23 +159,24 @@ __global__ void __launch_bounds__(256, 2) router_mfma_kernel(const float* __rest
     const float* xs = x + (srow_ok ? m0 + sr : 0) * (int64_t)H + 8 * sk;
     const int slane = sk * 16 + (sr & 15), stile = sr >> 4;
 
-    // B role: expert tiles et = 0, 1 of this wave; experts >= E read expert 0 (never stored)
-    const _Float16* wbp[2];
+    // B role: expert tiles et = 0, 1 of this wave; tiles past the padded
+    // experts read the last tile (never stored)
+    const half8_t* wbp[2];
 #pragma unroll
     for (int et = 0; et < 2; ++et) {
-        const int e = n0 + 32 * wave + 16 * et + r16;
-        wbp[et] = wb + ((int64_t)(e < E ? e : 0) * H + 8 * kg) * 2;
+        int te = (n0 >> 4) + 2 * wave + et;
+        te = te < Ep / 16 ? te : Ep / 16 - 1;
+        wbp[et] = reinterpret_cast<const half8_t*>(wb + (int64_t)te * nk * 1024) + lane;
     }
 
     auto load = [&](int kb, RouterStage& S) {
-        kb = kb < nk ? kb : nk - 1;
+        kb = kb < kb1 ? kb : kb1 - 1;
         S.x0 = *reinterpret_cast<const float4*>(xs + 32 * kb);
         S.x1 = *reinterpret_cast<const float4*>(xs + 32 * kb + 4);
 #pragma unroll
         for (int et = 0; et < 2; ++et) {
-            const half8_t* bp = reinterpret_cast<const half8_t*>(wbp[et] + 64 * kb);
-            S.b[et][0] = bp[0];
-            S.b[et][1] = bp[1];
+            S.b[et][0] = wbp[et][128 * kb];
+            S.b[et][1] = wbp[et][128 * kb + 64];
         }
     };
     auto stage = [&](int kb, const RouterStage& S) {
@@ -202,9 +215,9 @@ __global__ void __launch_bounds__(256, 2) router_mfma_kernel(const float* __rest
     };
 
     RouterStage s0, s1;
-    load(0, s0);
-    load(1, s1);
-    for (int kb = 0; kb < nk; kb += 2) {
+    load(kb0, s0);
+    load(kb0 + 1, s1);
+    for (int kb = kb0; kb < kb1; kb += 2) {
         stage(kb, s0);
         __syncthreads();
         products(kb, s0);
@@ -215,17 +228,18 @@ __global__ void __launch_bounds__(256, 2) router_mfma_kernel(const float* __rest
         load(kb + 3, s1);
     }
 
+    float* part = out + (int64_t)blockIdx.z * T * E;
 #pragma unroll
     for (int et = 0; et < 2; ++et) {
         const int e = n0 + 32 * wave + 16 * et + r16;
         if (e >= E) continue;
-        const float we = wm[e], be = bias ? bias[e] : 0.0f;
+        const float we = wm[e], be = bias && blockIdx.z == 0 ? bias[e] : 0.0f;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int64_t t = m0 + 16 * mt + 4 * kg + v;
-                if (t < T) out[t * E + e] = acc[mt][et][v] * xm[t] * we + be;
+                if (t < T) part[t * E + e] = acc[mt][et][v] * xm[t] * we + be;
             }
     }
 }
@@ -358,12 +372,19 @@ struct Selection {
     uint32_t loose;
 };
 
-__device__ __forceinline__ void select_token(const float* __restrict__ l, int32_t E, int32_t K, int lane,
-                                             Selection& S) {
+// l: the token's row of the first partial logits slice; nsplit slices
+// `sstride` floats apart are added in order.
+__device__ __forceinline__ void select_token(const float* __restrict__ l, int nsplit, int64_t sstride, int32_t E,
+                                             int32_t K, int lane, Selection& S) {
 #pragma unroll
     for (int i = 0; i < kPerLane; ++i) {
         const int e = lane + 64 * i;
-        S.v[i] = e < E ? l[e] : -FLT_MAX;
+        float v = -FLT_MAX;
+        if (e < E) {
+            v = l[e];
+            for (int z = 1; z < nsplit; ++z) v += l[z * sstride + e];
+        }
+        S.v[i] = v;
     }
     uint32_t taken = 0;
     S.rounds = K < E ? K + 1 : K;
@@ -421,14 +442,14 @@ __device__ __forceinline__ void write_token(const V (&lv)[kMaxTopK], const int (
 // One wave per token: tokens without a near-tie are finished here; the others
 // are appended to `amb` (amb[0] = count, then token ids) for the resolve pass.
 constexpr int kWaves = 4;
-__global__ void __launch_bounds__(256) topk_select_kernel(const float* __restrict__ logits, int64_t T, int32_t E,
-                                                          int32_t K, int32_t* __restrict__ amb,
+__global__ void __launch_bounds__(256) topk_select_kernel(const float* __restrict__ logits, int nsplit, int64_t T,
+                                                          int32_t E, int32_t K, int32_t* __restrict__ amb,
                                                           int32_t* __restrict__ ids, float* __restrict__ p_out) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * kWaves + wave;
     if (t >= T) return;  // whole wave; this kernel has no block-level barrier
     Selection S;
-    select_token(logits + t * E, E, K, lane, S);
+    select_token(logits + t * E, nsplit, T * E, E, K, lane, S);
     if (S.loose) {
         if (lane == 0) {
             const int slot = atomicAdd(amb, 1);
@@ -482,8 +503,9 @@ __device__ __forceinline__ double wave_dot_fp64(const float* __restrict__ x, con
 // so the merged order is the exact one.  The others are re-scored one at a
 // time as wave-wide fp64 dot products; then the candidates are re-ranked.
 // Lane l keeps the candidates among experts l, l + 64, ... in registers.
-__global__ void __launch_bounds__(256) topk_resolve_kernel(const float* __restrict__ logits,
-                                                           const float* __restrict__ x, const float* __restrict__ wt,
+__global__ void __launch_bounds__(256) topk_resolve_kernel(const float* __restrict__ logits, int nsplit,
+                                                           int64_t T, const float* __restrict__ x,
+                                                           const float* __restrict__ wt,
                                                            const float* __restrict__ bias, int32_t H, int32_t E,
                                                            int32_t K, const int32_t* __restrict__ amb,
                                                            int32_t* __restrict__ ids, float* __restrict__ p_out) {
@@ -492,7 +514,7 @@ __global__ void __launch_bounds__(256) topk_resolve_kernel(const float* __restri
     for (int it = blockIdx.x * kWaves + wave; it < n; it += gridDim.x * kWaves) {  // uniform over the wave
         const int64_t t = amb[1 + it];
         Selection S;
-        select_token(logits + t * E, E, K, lane, S);
+        select_token(logits + t * E, nsplit, T * E, E, K, lane, S);
         const float thr = S.vK - S.delta;
         double cv[kPerLane];
         uint32_t cand = 0, todo = 0;
@@ -550,14 +572,17 @@ hipError_t launch_router(const float* x, const float* xm, const float* wr, const
     if (T <= 0) return hipGetLastError();
     hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)((E + 31) / 32), (unsigned)((H + 31) / 32)), dim3(256), 0, st,
                        wr, H, E, rs.wt, rs.pmax);
-    hipLaunchKernelGGL(router_prep_kernel, dim3((unsigned)((E + 3) / 4)), dim3(256), 0, st, rs.wt, rs.pmax, H, E,
+    const int32_t Ep = (int32_t)router_padded_experts(E);
+    hipLaunchKernelGGL(router_prep_kernel, dim3((unsigned)((Ep + 3) / 4)), dim3(256), 0, st, rs.wt, rs.pmax, H, E, Ep,
                        rs.wb, rs.wm);
     if (!xm) {
         hipLaunchKernelGGL(row_scale_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, x, T, H, rs.xm);
         xm = rs.xm;
     }
-    hipLaunchKernelGGL(router_mfma_kernel, dim3((unsigned)((E + kRtN - 1) / kRtN), (unsigned)((T + kRtM - 1) / kRtM)),
-                       dim3(256), 0, st, x, xm, rs.wb, rs.wm, bias, T, H, E, logits);
+    hipLaunchKernelGGL(router_mfma_kernel,
+                       dim3((unsigned)((E + kRtN - 1) / kRtN), (unsigned)((T + kRtM - 1) / kRtM),
+                            (unsigned)router_splits(T, H, E)),
+                       dim3(256), 0, st, x, xm, rs.wb, rs.wm, bias, T, H, E, Ep, logits);
     return hipGetLastError();
 }
 
@@ -565,11 +590,12 @@ hipError_t launch_topk(const float* logits, const float* x, const float* wt, con
                        int32_t E, int32_t K, int32_t* amb, int32_t* ids, float* p, hipStream_t st) {
     if (T > 0) {
         hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, amb, 1, 0);
+        const int ns = router_splits(T, H, E);
         hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)((T + kWaves - 1) / kWaves)), dim3(64 * kWaves), 0, st,
-                           logits, T, E, K, amb, ids, p);
+                           logits, ns, T, E, K, amb, ids, p);
         const unsigned grid = (unsigned)((T < 8192 ? T : 8192) + kWaves - 1) / kWaves;
-        hipLaunchKernelGGL(topk_resolve_kernel, dim3(grid), dim3(256), 0, st, logits, x, wt, bias, H, E, K, amb, ids,
-                           p);
+        hipLaunchKernelGGL(topk_resolve_kernel, dim3(grid), dim3(256), 0, st, logits, ns, T, x, wt, bias, H, E, K,
+                           amb, ids, p);
     }
     return hipGetLastError();
 }

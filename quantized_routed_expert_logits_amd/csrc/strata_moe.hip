@@ -159,10 +159,10 @@ Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I) {
     Layout L;
     Offsets o;
     o.tiles_cap = chunk_list_cap(n, E);
-    o.logits = L.take<float>(T * E);
+    o.logits = L.take<float>(router_logit_floats(T, H, E));
     o.wt = L.take<float>((int64_t)E * H);
-    o.wb = L.take<_Float16>((int64_t)E * H * 2);
-    o.wm = L.take<float>(E);
+    o.wb = L.take<_Float16>(router_padded_experts(E) * H * 2);
+    o.wm = L.take<float>(router_padded_experts(E));
     o.pmax = L.take<float>((int64_t)((H + 31) / 32) * E);
     o.amb = L.take<int32_t>(T + 1);
     o.ids = L.take<int32_t>(n);
@@ -518,8 +518,10 @@ int strata_moe_route(const float* x, const float* router_w, const float* bias, i
     TRY(check_device());
     hipStream_t st = (hipStream_t)stream;
     Layout L;
-    const size_t lo = L.take<float>(T * E), o_wt = L.take<float>((int64_t)E * H), o_amb = L.take<int32_t>(T + 1);
-    const size_t o_wb = L.take<_Float16>((int64_t)E * H * 2), o_wm = L.take<float>(E), o_xm = L.take<float>(T);
+    const size_t lo = L.take<float>(router_logit_floats(T, H, E)), o_wt = L.take<float>((int64_t)E * H);
+    const size_t o_amb = L.take<int32_t>(T + 1);
+    const size_t o_wb = L.take<_Float16>(router_padded_experts(E) * H * 2);
+    const size_t o_wm = L.take<float>(router_padded_experts(E)), o_xm = L.take<float>(T);
     const size_t o_pm = L.take<float>((int64_t)((H + 31) / 32) * E);
     char* ws = nullptr;
     TRY(get_workspace(L.off, &ws));
