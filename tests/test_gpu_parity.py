@@ -245,4 +245,6 @@ def test_full_layer_sampled(qm, name):
     ref = oracle.layer_tokens(x, wr, bias, getter(s), s.K, tok)
     assert np.array_equal(g["ids"][tok], ref["ids"])
     assert np.array_equal(g["qx"][tok], ref["qx"])
-    assert rel_err(y[tok], ref["y"]) <= Y_TOL
+    err = rel_err(y[tok], ref["y"])
+    print(f"{name}: {len(tok)} sampled tokens, max|dy|/max|y| = {err:.2e}")
+    assert err <= Y_TOL
