@@ -71,10 +71,11 @@ struct RouterScratch {
 // The router GEMM splits the reduction over H into router_splits() ranges
 // when a chunk is short (too few workgroups otherwise); logits then holds
 // that many partial [T][E] arrays, which the top-K adds in order.
+constexpr int kMaxRouterSplits = 4;
 inline int router_splits(int64_t T, int32_t H, int32_t E) {
     const int64_t nk = H / 32, wgs = ((T + 63) / 64) * ((E + 127) / 128);
     int s = 1;
-    while (s < 4 && wgs * s < 512 && nk % (4 * s) == 0) s *= 2;
+    while (s < kMaxRouterSplits && wgs * s < 512 && nk % (4 * s) == 0) s *= 2;
     return s;
 }
 inline int64_t router_logit_floats(int64_t T, int32_t H, int32_t E) { return router_splits(T, H, E) * T * E; }

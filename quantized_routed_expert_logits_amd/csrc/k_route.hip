@@ -347,6 +347,32 @@ __device__ __forceinline__ void best_swap(Best<double>& a, bool wide) {
     take_better(a, __builtin_bit_cast(double, ((uint64_t)hi1 << 32) | lo1), (int)i1);
 }
 
+// Wave-wide fp64 sum in every lane, by the same exchange steps (fp addition
+// is commutative, so the lanes of a pair compute the same value and every
+// lane ends with the same sum).
+template <int kCtrl>
+__device__ __forceinline__ double dpp_d(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)dpp<kCtrl>((int)(uint32_t)u), hi = (uint32_t)dpp<kCtrl>((int)(uint32_t)(u >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double swap_add(double v, bool wide) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    uint32_t lo1, hi1;
+    const uint32_t lo0 = pair_first((uint32_t)u, (uint32_t)u, wide, &lo1);
+    const uint32_t hi0 = pair_first((uint32_t)(u >> 32), (uint32_t)(u >> 32), wide, &hi1);
+    return __builtin_bit_cast(double, ((uint64_t)hi0 << 32) | lo0) +
+           __builtin_bit_cast(double, ((uint64_t)hi1 << 32) | lo1);
+}
+__device__ __forceinline__ double wave_sum(double v) {
+    v += dpp_d<0xB1>(v);
+    v += dpp_d<0x4E>(v);
+    v += dpp_d<0x141>(v);
+    v += dpp_d<0x140>(v);
+    v = swap_add(v, false);
+    return swap_add(v, true);
+}
+
 template <typename V>
 __device__ __forceinline__ Best<V> wave_best(Best<V> a) {
     best_step<0xB1>(a);   // quad_perm [1,0,3,2]: lane ^ 1
@@ -363,8 +389,9 @@ __device__ __forceinline__ Best<V> wave_best(Best<V> a) {
 // 0..rounds-1 (K+1 rounds, K when K == E) by larger value, then lower index;
 // `loose` has bit k (k < K) set when rank k is within delta of a neighbouring
 // rank, i.e. its exact order is in doubt.
+template <int kSlots>
 struct Selection {
-    float v[kPerLane];
+    float v[kSlots];  // lane l: logits of experts l, l + 64, ...
     float selv[kMaxTopK + 1];
     int seli[kMaxTopK + 1];
     int rounds;
@@ -372,38 +399,92 @@ struct Selection {
     uint32_t loose;
 };
 
-// l: the token's row of the first partial logits slice; nsplit slices
-// `sstride` floats apart are added in order.
-__device__ __forceinline__ void select_token(const float* __restrict__ l, int nsplit, int64_t sstride, int32_t E,
-                                             int32_t K, int lane, Selection& S) {
-#pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
-        const int e = lane + 64 * i;
-        float v = -FLT_MAX;
-        if (e < E) {
-            v = l[e];
-            for (int z = 1; z < nsplit; ++z) v += l[z * sstride + e];
-        }
-        S.v[i] = v;
+// The 19-comparator sorting network for 8 values (descending by value, then
+// ascending index), applied to one lane's values.
+__device__ __forceinline__ void cas(float (&v)[8], int (&e)[8], int a, int b) {
+    if (better(v[b], e[b], v[a], e[a])) {
+        const float tv = v[a];
+        const int te = e[a];
+        v[a] = v[b], e[a] = e[b];
+        v[b] = tv, e[b] = te;
     }
-    uint32_t taken = 0;
+}
+__device__ __forceinline__ void sort8(float (&v)[8], int (&e)[8]) {
+    cas(v, e, 0, 2), cas(v, e, 1, 3), cas(v, e, 4, 6), cas(v, e, 5, 7);
+    cas(v, e, 0, 4), cas(v, e, 1, 5), cas(v, e, 2, 6), cas(v, e, 3, 7);
+    cas(v, e, 0, 1), cas(v, e, 2, 3), cas(v, e, 4, 5), cas(v, e, 6, 7);
+    cas(v, e, 2, 4), cas(v, e, 3, 5);
+    cas(v, e, 1, 4), cas(v, e, 3, 6);
+    cas(v, e, 1, 2), cas(v, e, 3, 4), cas(v, e, 5, 6);
+}
+
+// l: the token's row of the first partial logits slice; nsplit slices
+// `sstride` floats apart are added in order.  kSlots = 8 needs E <= 512.
+template <int kSlots>
+__device__ __forceinline__ void select_token(const float* __restrict__ l, int nsplit, int64_t sstride, int32_t E,
+                                             int32_t K, int lane, Selection<kSlots>& S) {
+    // all loads first (the slices are independent), then the sums in slice order
+    float part[kMaxRouterSplits][kSlots];
+#pragma unroll
+    for (int z = 0; z < kMaxRouterSplits; ++z)
+        if (z < nsplit)  // uniform
+#pragma unroll
+            for (int i = 0; i < kSlots; ++i) {
+                const int e = lane + 64 * i;
+                part[z][i] = e < E ? l[z * sstride + e] : 0.0f;
+            }
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i) {
+        float v = part[0][i];
+#pragma unroll
+        for (int z = 1; z < kMaxRouterSplits; ++z)
+            if (z < nsplit) v += part[z][i];
+        S.v[i] = lane + 64 * i < E ? v : -FLT_MAX;
+    }
     S.rounds = K < E ? K + 1 : K;
 #pragma unroll
-    for (int k = 0; k <= kMaxTopK; ++k) {
-        S.selv[k] = -FLT_MAX;
-        S.seli[k] = INT_MAX;
-        if (k >= S.rounds) continue;
-        Best<float> b{-FLT_MAX, INT_MAX};
+    for (int k = 0; k <= kMaxTopK; ++k) S.selv[k] = -FLT_MAX, S.seli[k] = INT_MAX;
+    if constexpr (kSlots == 8) {
+        // each lane sorts its 8 values once; a round offers every lane's head,
+        // and the winning lane moves its list up by one
+        float hv[8];
+        int he[8];
 #pragma unroll
-        for (int i = 0; i < kPerLane; ++i) {
-            const int e = lane + 64 * i;
-            if (e < E && !((taken >> i) & 1u)) take_better(b, S.v[i], e);
+        for (int i = 0; i < 8; ++i) hv[i] = S.v[i], he[i] = lane + 64 * i < E ? lane + 64 * i : INT_MAX;
+        sort8(hv, he);
+#pragma unroll
+        for (int k = 0; k <= kMaxTopK; ++k) {
+            if (k >= S.rounds) continue;
+            Best<float> b{hv[0], he[0]};
+            b = wave_best(b);
+            S.selv[k] = b.v;
+            S.seli[k] = b.i;
+            const bool win = he[0] == b.i;
+#pragma unroll
+            for (int i = 0; i < 7; ++i) {
+                hv[i] = win ? hv[i + 1] : hv[i];
+                he[i] = win ? he[i + 1] : he[i];
+            }
+            hv[7] = win ? -FLT_MAX : hv[7];
+            he[7] = win ? INT_MAX : he[7];
         }
-        b = wave_best(b);
-        const int bi = b.i;
-        S.selv[k] = b.v;
-        S.seli[k] = bi;
-        if (bi < E && (bi & 63) == lane) taken |= 1u << (bi >> 6);
+    } else {
+        uint32_t taken = 0;
+#pragma unroll
+        for (int k = 0; k <= kMaxTopK; ++k) {
+            if (k >= S.rounds) continue;
+            Best<float> b{-FLT_MAX, INT_MAX};
+#pragma unroll
+            for (int i = 0; i < kSlots; ++i) {
+                const int e = lane + 64 * i;
+                if (e < E && !((taken >> i) & 1u)) take_better(b, S.v[i], e);
+            }
+            b = wave_best(b);
+            const int bi = b.i;
+            S.selv[k] = b.v;
+            S.seli[k] = bi;
+            if (bi < E && (bi & 63) == lane) taken |= 1u << (bi >> 6);
+        }
     }
     S.vK = -FLT_MAX;
 #pragma unroll
@@ -419,36 +500,51 @@ __device__ __forceinline__ void select_token(const float* __restrict__ l, int ns
     }
 }
 
+// Wave-wide fp32 sum in every lane (the exchange steps of wave_best).
+__device__ __forceinline__ float wave_sum_f(float v) {
+    v += __builtin_bit_cast(float, dpp<0xB1>(__builtin_bit_cast(int, v)));
+    v += __builtin_bit_cast(float, dpp<0x4E>(__builtin_bit_cast(int, v)));
+    v += __builtin_bit_cast(float, dpp<0x141>(__builtin_bit_cast(int, v)));
+    v += __builtin_bit_cast(float, dpp<0x140>(__builtin_bit_cast(int, v)));
+    uint32_t b;
+    float a = __builtin_bit_cast(float, pair_first(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v),
+                                                   false, &b));
+    v = a + __builtin_bit_cast(float, b);
+    a = __builtin_bit_cast(float, pair_first(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v), true,
+                                             &b));
+    return a + __builtin_bit_cast(float, b);
+}
+
 // ids / p of one token from its ranked values: the softmax over the K, in
-// fp32 (values relative to the largest, each term in (0, 1]).
+// fp32 (values relative to the largest, each term in (0, 1]); lane k < K
+// takes rank k.
 template <typename V>
 __device__ __forceinline__ void write_token(const V (&lv)[kMaxTopK], const int (&li)[kMaxTopK], int32_t K, int lane,
                                             int64_t t, int32_t* __restrict__ ids, float* __restrict__ p_out) {
-    float ev[kMaxTopK];
-    float z = 0.0f;
+    V mine = lv[0];
+    int mi = li[0];
 #pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k) {
-        ev[k] = k < K ? expf((float)(lv[k] - lv[0])) : 0.0f;
-        z += ev[k];
+    for (int k = 1; k < kMaxTopK; ++k)
+        if (lane == k) mine = lv[k], mi = li[k];
+    const float ev = lane < K ? expf((float)(mine - lv[0])) : 0.0f;
+    const float z = wave_sum_f(ev);
+    if (lane < K) {
+        ids[t * K + lane] = mi;
+        p_out[t * K + lane] = ev / z;
     }
-#pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k)
-        if (k < K && lane == k) {
-            ids[t * K + k] = li[k];
-            p_out[t * K + k] = ev[k] / z;
-        }
 }
 
 // One wave per token: tokens without a near-tie are finished here; the others
 // are appended to `amb` (amb[0] = count, then token ids) for the resolve pass.
 constexpr int kWaves = 4;
+template <int kSlots>
 __global__ void __launch_bounds__(256) topk_select_kernel(const float* __restrict__ logits, int nsplit, int64_t T,
                                                           int32_t E, int32_t K, int32_t* __restrict__ amb,
                                                           int32_t* __restrict__ ids, float* __restrict__ p_out) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * kWaves + wave;
     if (t >= T) return;  // whole wave; this kernel has no block-level barrier
-    Selection S;
+    Selection<kSlots> S;
     select_token(logits + t * E, nsplit, T * E, E, K, lane, S);
     if (S.loose) {
         if (lane == 0) {
@@ -491,9 +587,7 @@ __device__ __forceinline__ double wave_dot_fp64(const float* __restrict__ x, con
             }
     }
     for (int h = 256 * n4 + lane; h < H; h += 64) acc = fma((double)x[h], (double)w[h], acc);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    return acc;
+    return wave_sum(acc);
 }
 
 // One wave per listed token (grid-stride over the list), no workgroup
@@ -503,6 +597,7 @@ __device__ __forceinline__ double wave_dot_fp64(const float* __restrict__ x, con
 // so the merged order is the exact one.  The others are re-scored one at a
 // time as wave-wide fp64 dot products; then the candidates are re-ranked.
 // Lane l keeps the candidates among experts l, l + 64, ... in registers.
+template <int kSlots>
 __global__ void __launch_bounds__(256) topk_resolve_kernel(const float* __restrict__ logits, int nsplit,
                                                            int64_t T, const float* __restrict__ x,
                                                            const float* __restrict__ wt,
@@ -513,13 +608,13 @@ __global__ void __launch_bounds__(256) topk_resolve_kernel(const float* __restri
     const int n = amb[0];
     for (int it = blockIdx.x * kWaves + wave; it < n; it += gridDim.x * kWaves) {  // uniform over the wave
         const int64_t t = amb[1 + it];
-        Selection S;
+        Selection<kSlots> S;
         select_token(logits + t * E, nsplit, T * E, E, K, lane, S);
         const float thr = S.vK - S.delta;
-        double cv[kPerLane];
+        double cv[kSlots];
         uint32_t cand = 0, todo = 0;
 #pragma unroll
-        for (int i = 0; i < kPerLane; ++i) {
+        for (int i = 0; i < kSlots; ++i) {
             const int e = lane + 64 * i;
             const bool c = e < E && S.v[i] >= thr;
             bool stable = false;
@@ -532,7 +627,7 @@ __global__ void __launch_bounds__(256) topk_resolve_kernel(const float* __restri
         }
         const float* xr = x + t * H;
 #pragma unroll
-        for (int i = 0; i < kPerLane; ++i) {
+        for (int i = 0; i < kSlots; ++i) {
             uint64_t m = __ballot((todo >> i) & 1u);
             while (m) {  // uniform over the wave
                 const int l = __ffsll((unsigned long long)m) - 1;
@@ -553,7 +648,7 @@ __global__ void __launch_bounds__(256) topk_resolve_kernel(const float* __restri
             if (k >= K) continue;
             Best<double> b{-DBL_MAX, INT_MAX};
 #pragma unroll
-            for (int i = 0; i < kPerLane; ++i)
+            for (int i = 0; i < kSlots; ++i)
                 if (((cand & ~tk) >> i) & 1u) take_better(b, cv[i], lane + 64 * i);
             b = wave_best(b);
             const int bi = b.i;
@@ -591,11 +686,19 @@ hipError_t launch_topk(const float* logits, const float* x, const float* wt, con
     if (T > 0) {
         hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, amb, 1, 0);
         const int ns = router_splits(T, H, E);
-        hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)((T + kWaves - 1) / kWaves)), dim3(64 * kWaves), 0, st,
-                           logits, ns, T, E, K, amb, ids, p);
+        const dim3 sg((unsigned)((T + kWaves - 1) / kWaves));
+        if (E <= 512)
+            hipLaunchKernelGGL(topk_select_kernel<8>, sg, dim3(64 * kWaves), 0, st, logits, ns, T, E, K, amb, ids, p);
+        else
+            hipLaunchKernelGGL(topk_select_kernel<kPerLane>, sg, dim3(64 * kWaves), 0, st, logits, ns, T, E, K, amb,
+                               ids, p);
         const unsigned grid = (unsigned)((T < 8192 ? T : 8192) + kWaves - 1) / kWaves;
-        hipLaunchKernelGGL(topk_resolve_kernel, dim3(grid), dim3(256), 0, st, logits, ns, T, x, wt, bias, H, E, K,
-                           amb, ids, p);
+        if (E <= 512)
+            hipLaunchKernelGGL(topk_resolve_kernel<8>, dim3(grid), dim3(256), 0, st, logits, ns, T, x, wt, bias, H, E,
+                               K, amb, ids, p);
+        else
+            hipLaunchKernelGGL(topk_resolve_kernel<kPerLane>, dim3(grid), dim3(256), 0, st, logits, ns, T, x, wt, bias,
+                               H, E, K, amb, ids, p);
     }
     return hipGetLastError();
 }

@@ -83,6 +83,14 @@ def test_route_matches_oracle(qm, name):
     _route_case(qm, S.activations(s), S.router_weight(s), S.router_bias(s), s.K)
 
 
+def test_route_many_experts(qm):
+    """More than 512 experts: the selection keeps 16 logits per lane."""
+    s = S.custom(T=200, H=256, E=1000, K=12, I=32)
+    x, wr = S.activations(s, 6), S.router_weight(s, 6)
+    wr[:, 777] = wr[:, 5]           # an exact tie across the two halves of the expert range
+    _route_case(qm, x, wr, None, s.K)
+
+
 def test_route_exact_ties_and_zero_router(qm):
     s = S.custom(T=300, H=512, E=40, K=7, I=32)
     x, wr = S.activations(s, 3), S.router_weight(s, 3)
