@@ -512,6 +512,12 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_kernel(GemmArgs g) {
 // multipliers (powers of two) before the final multiply.
 template <int P, int NT>
 struct SlabPass {
+    // With one part (down) the activation fragments are read straight in the
+    // MFMA layout: at one 16-byte load per tile and block the L1 keeps up with
+    // 16 rows per load, and the lane exchange costs more than it saves.  Two
+    // parts (gate/up) read twice as much and keep the coalesced read plus
+    // exchange.
+    static constexpr bool kDirect = P == 1;
     __amdgpu_buffer_rsrc_t rec, act;
     int32_t Kd, nblk;
     int lane, r16, kg, paddr;
@@ -531,7 +537,8 @@ struct SlabPass {
         }
     }
 
-    // Activation fragments of a block in the loader layout (see loader_row).
+    // Activation fragments of a block, in the loader layout (see loader_row) or,
+    // with kDirect, in the MFMA layout.
     __device__ __forceinline__ void load_act(int blk, const int (&lvoff)[NT], half8_t (&bf)[NT][P]) const {
         blk = blk < nblk ? blk : nblk - 1;
 #pragma unroll
@@ -542,14 +549,19 @@ struct SlabPass {
                     half8_t, __builtin_amdgcn_raw_buffer_load_b128(act, lvoff[i] + 64 * h, blk * kBlock * 2 * P, 0));
     }
 
-    // Unpack dword p (fragments 2p, 2p+1) and park its scales for the offset
-    // pass (the 4 lanes kg of a row write the same value).
-    __device__ __forceinline__ void prepare(int p, int col, const uint32_t (&xw)[4], const uint32_t (&sw)[4],
+    // Unpack dword p (fragments 2p, 2p+1).
+    __device__ __forceinline__ void prepare(int p, const uint32_t (&xw)[4], const uint32_t (&sw)[4],
                                             half8_t (&a)[2]) const {
-        const _Float16 d0 = lo_half(sw[p]), d1 = hi_half(sw[p]);
-        unpack_dword(xw[p], d0, d1, mg, a[0], a[1]);
-        dl[(32 * p + r16) * kDlStride + col] = d0;
-        dl[(32 * p + 16 + r16) * kDlStride + col] = d1;
+        unpack_dword(xw[p], lo_half(sw[p]), hi_half(sw[p]), mg, a[0], a[1]);
+    }
+
+    // Park the block's scales for the offset pass.  The four lanes kg of a
+    // row hold the same 8 scales (fragments 0..7); lane kg writes those of
+    // fragments 2kg and 2kg+1 only.
+    __device__ __forceinline__ void park_scales(int col, const uint32_t (&sw)[4]) const {
+        const uint32_t s = kg == 0 ? sw[0] : kg == 1 ? sw[1] : kg == 2 ? sw[2] : sw[3];
+        dl[(32 * kg + r16) * kDlStride + col] = lo_half(s);
+        dl[(32 * kg + 16 + r16) * kDlStride + col] = hi_half(s);
     }
 
     // One block, software-pipelined over the four dwords: the MFMAs of dword
@@ -565,13 +577,14 @@ struct SlabPass {
 #pragma unroll
         for (int i = 0; i < NT; ++i)
 #pragma unroll
-            for (int h = 0; h < P; ++h) bf[i][h] = to_mfma_layout(raw[i][h], paddr);
+            for (int h = 0; h < P; ++h) bf[i][h] = kDirect ? raw[i][h] : to_mfma_layout(raw[i][h], paddr);
         half8_t a[2][2];
-        prepare(0, col, xw, sw, a[0]);
+        prepare(0, xw, sw, a[0]);
+        park_scales(col, sw);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            if (p < 3) prepare(p + 1, col, xw, sw, a[(p + 1) & 1]);
+            if (p < 3) prepare(p + 1, xw, sw, a[(p + 1) & 1]);
 #pragma unroll
             for (int h = 0; h < P; ++h)
 #pragma unroll
@@ -675,7 +688,9 @@ __device__ __forceinline__ void small_chunk_pass(const GemmArgs& g, const Tile& 
         ratio[i] = arow[i] >= 0 ? g.um[arow[i]] / g.am[arow[i]] : 0.f;
         int64_t la = 0;
         if (lr < tl.nrows) la = kGateUp ? (int64_t)g.src[tl.row0 + lr] : (int64_t)(tl.row0 + lr);
-        lvoff[i] = (int)la * g.Kd * 2 * P + 16 * (lane & 3);
+        if constexpr (SlabPass<P, NT>::kDirect)  // MFMA layout: column r16, group kg
+            la = arow[i] >= 0 ? arow[i] : 0;
+        lvoff[i] = (int)la * g.Kd * 2 * P + (SlabPass<P, NT>::kDirect ? 16 * kg : 16 * (lane & 3));
     }
     float4_t acc[kFrags][NT];
 #pragma unroll
