@@ -47,7 +47,12 @@ inline int64_t chunk_list_cap(int64_t n, int32_t E) { return max_tiles(n, E); }
 inline int64_t offset_operand_halves(int32_t Kd) { return (int64_t)((Kd / kBlock + 31) / 32) * 64; }
 
 // ---- launchers; each returns hipGetLastError() after its launches.
-hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q8, float* s, hipStream_t st);
+// Up to two int32 words the quantize kernel sets to 0 (a call's flags), or null.
+struct ZeroWords {
+    int32_t* p[2];
+};
+hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q8, float* s, hipStream_t st,
+                           ZeroWords z = ZeroWords{{nullptr, nullptr}});
 // fp16 GEMM operand q * s * 2^-e_r of int8 rows (parts 1: one fp16; 2: hi and
 // lo fp16 per value: per 32-wide block its 32 hi then its 32 lo values) and the row multipliers 2^e_r; plus
 // the offset-pass operand (u per block, hi/lo, [rows][offset_operand_halves])
@@ -85,9 +90,11 @@ inline int64_t router_padded_experts(int32_t E) { return round_up(E, 16); }
 // prescale's row multipliers of the same rows) or nullptr to compute them.
 hipError_t launch_router(const float* x, const float* xm, const float* wr, const float* bias, int64_t T, int32_t H,
                          int32_t E, const RouterScratch& rs, float* logits, hipStream_t st);
-// amb: scratch of T+1 ints (the list of tokens with a near-tie); wt from the router scratch.
+// amb: scratch of T+1 ints (the list of tokens with a near-tie), amb[0] set to
+// 0 here unless the caller already did (amb_zeroed); wt from the router scratch.
 hipError_t launch_topk(const float* logits, const float* x, const float* wt, const float* bias, int64_t T, int32_t H,
-                       int32_t E, int32_t K, int32_t* amb, int32_t* ids, float* p, hipStream_t st);
+                       int32_t E, int32_t K, int32_t* amb, int32_t* ids, float* p, hipStream_t st,
+                       bool amb_zeroed = false);
 
 hipError_t launch_group(const int32_t* ids, const float* p, int64_t n, int32_t K, int32_t E, int32_t* hist,
                         int32_t* base, int32_t* offsets, const ChunkLists& cl, int32_t* src, int32_t* slot,

@@ -809,11 +809,17 @@ inline unsigned grid_of(int64_t chunks_cap, int32_t per_chunk) {
 }
 
 // Both kernels over their own lists.  List bounds known on the host: a big
-// chunk holds more than kSmallRows of the n rows; an expert has at most one
-// small chunk.
+// chunk holds more than kSmallRows of the n rows; an expert with c rows has
+// at most ceil(c / kChunkRows) <= c / kChunkRows + 1 chunks, and at most
+// n / (kSmallRows + 1) experts have a big one; an expert has at most one
+// small chunk.  Workgroups past the list's length exit at once, so a tight
+// bound saves their launches.
 void launch_gemms(GemmArgs g, const ChunkLists& cl, int64_t n, int32_t E, size_t big_lds, bool gate_up,
                   hipStream_t st) {
-    const int64_t cap_big = cl.cap < n / (kSmallRows + 1) ? cl.cap : n / (kSmallRows + 1);
+    const int64_t by_rows = n / (kSmallRows + 1);
+    const int64_t by_experts = n / kChunkRows + (E < by_rows ? E : by_rows);
+    int64_t cap_big = cl.cap < by_rows ? cl.cap : by_rows;
+    cap_big = cap_big < by_experts ? cap_big : by_experts;
     const int64_t cap_small = cl.cap < E ? cl.cap : E;
     g.chunks = cl.tiles;
     g.nchunks = cl.sched;

@@ -47,8 +47,10 @@ __device__ __forceinline__ float round_half_away(float t) {
 }
 
 __global__ void __launch_bounds__(256) quantize_kernel(const float4* __restrict__ v, int64_t n4,
-                                                       int8_t* __restrict__ q8, float* __restrict__ s_out) {
+                                                       int8_t* __restrict__ q8, float* __restrict__ s_out,
+                                                       ZeroWords z) {
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g < 2 && z.p[g]) *z.p[g] = 0;  // the call's flag words (saves a launch)
     const bool valid = g < n4;
     const float4 x = valid ? v[g] : make_float4(0.f, 0.f, 0.f, 0.f);
     float a = fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
@@ -202,11 +204,12 @@ inline unsigned grid_for(int64_t n, int threads) { return (unsigned)((n + thread
 
 }  // namespace
 
-hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q8, float* s, hipStream_t st) {
+hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q8, float* s, hipStream_t st,
+                           ZeroWords z) {
     const int64_t n4 = rows * cols / 4;
     if (n4 > 0)
         hipLaunchKernelGGL(quantize_kernel, dim3(grid_for(n4, 256)), dim3(256), 0, st,
-                           reinterpret_cast<const float4*>(v), n4, q8, s);
+                           reinterpret_cast<const float4*>(v), n4, q8, s, z);
     return hipGetLastError();
 }
 

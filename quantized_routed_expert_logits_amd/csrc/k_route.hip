@@ -682,9 +682,10 @@ hipError_t launch_router(const float* x, const float* xm, const float* wr, const
 }
 
 hipError_t launch_topk(const float* logits, const float* x, const float* wt, const float* bias, int64_t T, int32_t H,
-                       int32_t E, int32_t K, int32_t* amb, int32_t* ids, float* p, hipStream_t st) {
+                       int32_t E, int32_t K, int32_t* amb, int32_t* ids, float* p, hipStream_t st,
+                       bool amb_zeroed) {
     if (T > 0) {
-        hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, amb, 1, 0);
+        if (!amb_zeroed) hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, amb, 1, 0);
         const int ns = router_splits(T, H, E);
         const dim3 sg((unsigned)((T + kWaves - 1) / kWaves));
         if (E <= 512)

@@ -332,7 +332,8 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     Buffers b = carve(ws, o);
     CallTimer tm(st);
     tm.begin(kQuantize);
-    HIP_TRY(launch_quantize(x, T, H, b.xq, b.xs, st), "quantize launch");
+    // the quantize kernel also clears the top-K near-tie count and the id error flag
+    HIP_TRY(launch_quantize(x, T, H, b.xq, b.xs, st, ZeroWords{{b.amb, b.err}}), "quantize launch");
     HIP_TRY(launch_prescale(b.xq, b.xs, T, H, 2, b.xb, b.xe, b.xuop, b.xum, st), "prescale launch");
     tm.end(kQuantize);
     tm.begin(kRouter);
@@ -341,10 +342,10 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
             "router launch");
     tm.end(kRouter);
     tm.begin(kTopK);
-    HIP_TRY(launch_topk(b.logits, x, b.wt, ex->router_bias, T, H, E, K, b.amb, b.ids, b.p, st), "top-K launch");
+    HIP_TRY(launch_topk(b.logits, x, b.wt, ex->router_bias, T, H, E, K, b.amb, b.ids, b.p, st, true),
+            "top-K launch");
     tm.end(kTopK);
     tm.begin(kGroup);
-    HIP_TRY(launch_fill_zero((float*)b.err, 1, st), "fill launch");
     const ChunkLists cl{b.tiles, b.ntiles, b.tiles_cap};
     HIP_TRY(launch_group(b.ids, b.p, n, K, E, b.hist, b.base, b.offsets, cl, b.src, b.slot, b.prow, b.err, st),
             "group launch");
