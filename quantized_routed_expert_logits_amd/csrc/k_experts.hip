@@ -15,12 +15,19 @@
 //     d * sum (q - 1.5) * (s a) = sum [d (q - 1)] * (s a) + d * u,
 //     u = -0.5 * s * sum(a)  (one value per activation block).
 // The first sum runs on v_mfma_f32_16x16x32_f16 (K = 32 = one block): the A
-// operand d*(q-1) is exact in fp16 (q - 1 in {-1, 0, 1, 2}); the B operand is
-// the prescaled activation s*a*2^-e of the row (one fp16 for down, a hi and a
-// lo fp16 for gate/up, two MFMAs into the same accumulator), so the block
-// scale needs no vector-ALU multiply and the accumulators run over the whole
-// reduction.  After the loop the results are multiplied by the row's 2^e
-// (exact).  The d*u terms of all blocks form a small matrix product over the
+// operand d*(q-1) is exact in fp16 (q - 1 in {-1, 0, 1, 2}).  Two forms of the
+// B operand:
+//   prescaled: the activation s*a*2^-e of the row (one fp16 for down, a hi
+//     and a lo fp16 for gate/up, two MFMAs into the same accumulator), so the
+//     block scale needs no vector-ALU multiply and the accumulators run over
+//     the whole reduction; after the loop the results are multiplied by the
+//     row's 2^e (exact);
+//   rescaled (gate/up, chunks of more than kSmallRows rows): the codes a
+//     themselves (exact in fp16).  One MFMA per block gives d * sum (q-1) a
+//     exactly (an integer times d: at most 24 significant bits), and one fp32
+//     FMA per output adds it times the block's s.  Half the MFMAs and half the
+//     activation bytes of the hi/lo form, for 4 FMAs per MFMA on the vector
+//     ALU, and the sum is more precise.  The d*u terms of all blocks form a small matrix product over the
 // block index (K = Kd/32), done after the block loop on the MFMA unit: A = d
 // (exact in fp16), B = u of each row scaled by a power of two to [-1, 1] and
 // split into a high and a low fp16 part (22 bits).
@@ -141,7 +148,9 @@ struct GemmArgs {
     const int32_t* src;    // token of each grouped row
     const float* prow;     // routing weight of each grouped row (down)
     const _Float16* act;   // prescaled activations [rows][Kd x parts]
-    int64_t act_rows;      // rows of act / am / uop / um
+    int64_t act_rows;      // rows of act / am / uop / um (and act1 / ascale)
+    const _Float16* act1;  // rescaled form (gate/up, 4-wave kernel): codes as fp16 [rows][Kd]
+    const float* ascale;   // ... and their block scales [rows][Kd / 32]
     const float* am;       // row multipliers 2^e [rows]
     const _Float16* uop;   // offset-pass operand [rows][nch x 32 blocks x 2] (hi, lo)
     const float* um;       // its row multipliers [rows]
@@ -158,10 +167,12 @@ struct GemmArgs {
 // Records are prefetched several blocks ahead in a register ring and
 // activation fragments one block ahead in two alternating register sets, so
 // the loop body has no copies.
-template <int P>
+template <int P, bool kRescale>
 struct BlockLoop {
+    static_assert(!kRescale || P == 1, "the rescaled form has one part");
     __amdgpu_buffer_rsrc_t rec;  // this slab's records (nblk x 1280 bytes)
-    __amdgpu_buffer_rsrc_t act;  // prescaled activations [rows][Kd x P] fp16
+    __amdgpu_buffer_rsrc_t act;  // activations [rows][Kd x P] fp16 (prescaled, or codes with kRescale)
+    __amdgpu_buffer_rsrc_t scl;  // kRescale: block scales [rows][nblk] fp32
     int32_t Kd, nblk, dstride;
     int tau, lane, r16, kg, p, paddr;
     _Float16* d_lds;
@@ -191,6 +202,17 @@ struct BlockLoop {
                     half8_t, __builtin_amdgcn_raw_buffer_load_b128(act, lvoff[i] + 64 * h, blk * kBlock * 2 * P, 0));
     }
 
+    // kRescale: the block scale of this lane's MFMA column in each tile;
+    // soff[i] is the byte offset of that row's scales.
+    template <int NT>
+    __device__ __forceinline__ void load_scales(int blk, const int (&soff)[kTilesPerWave],
+                                                float (&sv)[kTilesPerWave]) const {
+        blk = blk < nblk ? blk : nblk - 1;
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+            sv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(scl, soff[i], blk * 4, 0));
+    }
+
     // Thread tau unpacks dword tau of the record: fragments 2p and 2p+1 of
     // MFMA lane tau / 4 (p = tau % 4), stored at lane slot (tau / 4) ^ 2p so
     // that the four pairs of one lane fall in different LDS banks.
@@ -209,6 +231,7 @@ struct BlockLoop {
 
     template <int NT>
     __device__ __forceinline__ void products(int blk, const half8_t (&raw)[kTilesPerWave][P],
+                                             const float (&sv)[kTilesPerWave],
                                              float4_t (&acc)[kFrags][kTilesPerWave]) const {
         half8_t bf[kTilesPerWave][P];
 #pragma unroll
@@ -222,14 +245,26 @@ struct BlockLoop {
             half8_t a[kFrags / 2];
 #pragma unroll
             for (int f = 0; f < kFrags / 2; ++f) a[f] = a_lds[blk & 1][4 * g + f][lane ^ ((4 * g + f) & ~1)];
+            if constexpr (kRescale) {
 #pragma unroll
-            for (int f = 0; f < kFrags / 2; ++f)
+                for (int f = 0; f < kFrags / 2; ++f)
 #pragma unroll
-                for (int h = 0; h < P; ++h)
+                    for (int i = 0; i < NT; ++i) {
+                        const float4_t t = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            a[f], bf[i][0], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-                    for (int i = 0; i < NT; ++i)
-                        acc[4 * g + f][i] =
-                            __builtin_amdgcn_mfma_f32_16x16x32_f16(a[f], bf[i][h], acc[4 * g + f][i], 0, 0, 0);
+                        for (int v = 0; v < 4; ++v) acc[4 * g + f][i][v] = fmaf(t[v], sv[i], acc[4 * g + f][i][v]);
+                    }
+            } else {
+#pragma unroll
+                for (int f = 0; f < kFrags / 2; ++f)
+#pragma unroll
+                    for (int h = 0; h < P; ++h)
+#pragma unroll
+                        for (int i = 0; i < NT; ++i)
+                            acc[4 * g + f][i] =
+                                __builtin_amdgcn_mfma_f32_16x16x32_f16(a[f], bf[i][h], acc[4 * g + f][i], 0, 0, 0);
+            }
         }
     }
 
@@ -240,11 +275,12 @@ struct BlockLoop {
     // register sets.  D divides nblk, so the unrolled body has no exit in the
     // middle and every ring index is a compile-time constant.
     template <int NT, int D>
-    __device__ __forceinline__ void run(const int (&lvoff)[kTilesPerWave],
+    __device__ __forceinline__ void run(const int (&lvoff)[kTilesPerWave], const int (&soff)[kTilesPerWave],
                                         float4_t (&acc)[kFrags][kTilesPerWave]) const {
         static_assert(D % 2 == 0, "activation sets alternate per block");
         uint32_t xw[D], sw[D];
         half8_t bf[2][kTilesPerWave][P];
+        float sv[2][kTilesPerWave] = {};
         // Issue order matters: each unpack waits for its record with a vmcnt
         // that counts the loads issued after it, and the loop header merges
         // the entry path with the back edge.  Records first, as in the loop.
@@ -252,6 +288,7 @@ struct BlockLoop {
         for (int j = 0; j < D; ++j) load_record(j, xw[j], sw[j]);
         __builtin_amdgcn_sched_barrier(0);
         load_act<NT>(0, lvoff, bf[0]);
+        if constexpr (kRescale) load_scales<NT>(0, soff, sv[0]);
         __builtin_amdgcn_sched_barrier(0);
         for (int b = 0; b < nblk; b += D) {
 #pragma unroll
@@ -261,8 +298,9 @@ struct BlockLoop {
                 __syncthreads();
                 load_record(blk + D, xw[j], sw[j]);
                 load_act<NT>(blk + 1, lvoff, bf[(j + 1) & 1]);
+                if constexpr (kRescale) load_scales<NT>(blk + 1, soff, sv[(j + 1) & 1]);
                 __builtin_amdgcn_sched_barrier(0);  // loads go out before the MFMAs
-                products<NT>(blk, bf[j & 1], acc);
+                products<NT>(blk, bf[j & 1], sv[j & 1], acc);
             }
         }
     }
@@ -361,11 +399,14 @@ __device__ __forceinline__ void big_chunk_item(const GemmArgs& g, const Tile tl,
     for (int c = nblk + (tau & 1); c < nch * 32; c += 2) d_lds[(tau >> 1) * dstride + c] = (_Float16)0.0f;
 
     // this wave's tiles: arow = activation row of this lane's MFMA column,
-    // lvoff = byte offset of its loader row and group (padding rows read row 0
-    // and are never stored)
-    constexpr int P = kGateUp ? 2 : 1;
+    // lvoff = byte offset of its loader row and group, soff = byte offset of
+    // the column's block scales (rescaled form; padding rows read row 0 and
+    // are never stored).  gate/up takes the rescaled form, down the
+    // prescaled one with one part.
+    constexpr bool kRescale = kGateUp;
+    constexpr int P = 1;
     int64_t arow[kTilesPerWave];
-    int lvoff[kTilesPerWave];
+    int lvoff[kTilesPerWave], soff[kTilesPerWave];
     int ntw = 0;
     const int tw = wave;
 #pragma unroll
@@ -378,6 +419,7 @@ __device__ __forceinline__ void big_chunk_item(const GemmArgs& g, const Tile tl,
         int64_t la = 0;
         if (lr < tl.nrows) la = kGateUp ? (int64_t)g.src[tl.row0 + lr] : (int64_t)(tl.row0 + lr);
         lvoff[i] = (int)la * g.Kd * 2 * P + 16 * (lane & 3);
+        soff[i] = (int)(arow[i] >= 0 ? arow[i] : 0) * nblk * 4;
     }
 
     const uint8_t* rec = g.blobs + (int64_t)tl.e * g.stride + (int64_t)slab * nblk * kRecordBytes;
@@ -388,34 +430,36 @@ __device__ __forceinline__ void big_chunk_item(const GemmArgs& g, const Tile tl,
     for (int f = 0; f < kFrags; ++f)
 #pragma unroll
         for (int i = 0; i < kTilesPerWave; ++i) acc[f][i] = (float4_t){0.f, 0.f, 0.f, 0.f};
-    BlockLoop<P> L{__builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, nblk * kRecordBytes, kBufferWord3),
-                   __builtin_amdgcn_make_buffer_rsrc((void*)g.act, (short)0, (int)(g.act_rows * g.Kd * 2 * P),
-                                                     kBufferWord3),
-                   g.Kd, nblk, dstride, tau, lane, r16, kg, p, mfma_source_addr(lane), d_lds, a_lds,
-                   UnpackMagic()};
+    BlockLoop<P, kRescale> L{
+        __builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, nblk * kRecordBytes, kBufferWord3),
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kRescale ? g.act1 : g.act), (short)0,
+                                          (int)(g.act_rows * g.Kd * 2 * P), kBufferWord3),
+        __builtin_amdgcn_make_buffer_rsrc((void*)g.ascale, (short)0, kRescale ? (int)(g.act_rows * nblk * 4) : 0,
+                                          kBufferWord3),
+        g.Kd, nblk, dstride, tau, lane, r16, kg, p, mfma_source_addr(lane), d_lds, a_lds, UnpackMagic()};
     // wave-uniform: the block loop is straight-line code for 1..3 tiles; the
     // record ring is 8 deep when 8 divides the block count (H = 2560, I = 1024)
     if (nblk % 8 == 0) {
         switch (ntw) {
-            case 1: L.template run<1, 8>(lvoff, acc); break;
-            case 2: L.template run<2, 8>(lvoff, acc); break;
-            case 3: L.template run<3, 8>(lvoff, acc); break;
-            default: L.template run<0, 8>(lvoff, acc); break;  // no tiles: still unpack and meet every barrier
+            case 1: L.template run<1, 8>(lvoff, soff, acc); break;
+            case 2: L.template run<2, 8>(lvoff, soff, acc); break;
+            case 3: L.template run<3, 8>(lvoff, soff, acc); break;
+            default: L.template run<0, 8>(lvoff, soff, acc); break;  // no tiles: still unpack and meet every barrier
         }
     } else {
         switch (ntw) {
-            case 1: L.template run<1, 2>(lvoff, acc); break;
-            case 2: L.template run<2, 2>(lvoff, acc); break;
-            case 3: L.template run<3, 2>(lvoff, acc); break;
-            default: L.template run<0, 2>(lvoff, acc); break;
+            case 1: L.template run<1, 2>(lvoff, soff, acc); break;
+            case 2: L.template run<2, 2>(lvoff, soff, acc); break;
+            case 3: L.template run<3, 2>(lvoff, soff, acc); break;
+            default: L.template run<0, 2>(lvoff, soff, acc); break;
         }
     }
     __syncthreads();  // every d of the slab is in LDS
 
-    // undo the rows' power-of-two prescaling
+    // undo the rows' power-of-two prescaling (the rescaled form has none)
 #pragma unroll
     for (int i = 0; i < kTilesPerWave; ++i) {
-        if (i >= ntw) continue;
+        if (kRescale || i >= ntw) continue;
         const float mult = arow[i] >= 0 ? g.am[arow[i]] : 0.f;
 #pragma unroll
         for (int f = 0; f < kFrags; ++f)
@@ -845,10 +889,10 @@ void launch_gemms(GemmArgs g, const ChunkLists& cl, int64_t n, int32_t E, size_t
 
 hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const ChunkLists& cl, int64_t n, int32_t E,
                           const int32_t* src, const _Float16* xb, int64_t act_rows, const float* xe,
-                          const _Float16* xuop, const float* xum, int32_t H, int32_t I, int8_t* hq, float* hs,
-                          hipStream_t st) {
-    GemmArgs g{blobs, stride, nullptr, nullptr, 2 * I / kSlabRows, H, src, nullptr, xb, act_rows, xe, xuop, xum, I, H,
-               hq, hs, nullptr};
+                          const _Float16* xa, const float* xs, const _Float16* xuop, const float* xum, int32_t H,
+                          int32_t I, int8_t* hq, float* hs, hipStream_t st) {
+    GemmArgs g{blobs, stride, nullptr, nullptr, 2 * I / kSlabRows, H, src, nullptr, xb, act_rows, xa, xs, xe, xuop,
+               xum, I, H, hq, hs, nullptr};
     launch_gemms(g, cl, n, E, dynamic_lds_bytes(H, false), true, st);
     return hipGetLastError();
 }
@@ -856,7 +900,8 @@ hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const ChunkLists
 hipError_t launch_down(const uint8_t* blobs, int64_t stride, const ChunkLists& cl, int64_t n, int32_t E,
                        const int32_t* src, const float* prow, const _Float16* hb, int64_t act_rows, const float* he,
                        const _Float16* huop, const float* hum, int32_t H, int32_t I, float* dm, hipStream_t st) {
-    GemmArgs g{blobs, stride, nullptr, nullptr, H / kSlabRows, I, src, prow, hb, act_rows, he, huop, hum, I, H,
+    GemmArgs g{blobs, stride, nullptr, nullptr, H / kSlabRows, I, src, prow, hb, act_rows, nullptr, nullptr, he, huop,
+               hum, I, H,
                nullptr, nullptr, dm};
     launch_gemms(g, cl, n, E, dynamic_lds_bytes(I, true), false, st);
     return hipGetLastError();

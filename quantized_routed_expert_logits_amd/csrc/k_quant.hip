@@ -28,6 +28,10 @@
 // lo values (128 bytes per block), so each part of a block is 64 contiguous
 // bytes (four lanes of a GEMM's coalesced fragment load).
 //
+// With parts = 2 the kernel can also write the codes themselves as fp16
+// (exact), the operand of the large-chunk gate/up kernel, which applies the
+// block scales in fp32 after each block's products.
+//
 // The same kernel writes the operand of the GEMMs' offset pass: per block,
 // u = -0.5 * s * (sum of the block's codes) (the 2-bit weight offset's share,
 // see k_experts.hip), the row's u scaled by a power of two into (-1, 1) and
@@ -89,7 +93,7 @@ template <int P>
 __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict__ q, const float* __restrict__ s,
                                                        int64_t rows, int32_t cols, _Float16* __restrict__ out,
                                                        float* __restrict__ mult, _Float16* __restrict__ uop,
-                                                       float* __restrict__ umult) {
+                                                       float* __restrict__ umult, _Float16* __restrict__ codes16) {
     __shared__ float ush[4][kMaxOffsetChunks * 32];
     const int w = threadIdx.x >> 6;
     const int64_t row = (int64_t)blockIdx.x * 4 + w;
@@ -123,12 +127,14 @@ __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict_
         const float sj = sraw * scale;  // exact: a power-of-two scaling
         const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
         float v[16];
+        half8_t cq[2];
         int sum = 0;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int c = (int8_t)(ws[i >> 2] >> (8 * (i & 3)));
             sum += c;
             v[i] = (float)c * sj;
+            cq[i >> 3][i & 7] = (_Float16)c;  // exact: |c| <= 127
         }
         sum += __shfl_xor(sum, 1);  // lanes 2m, 2m+1 hold the two halves of one block
         if (on && (j & 1) == 0) {
@@ -165,6 +171,11 @@ __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict_
             reinterpret_cast<half8_t*>(blk)[1] = hi[1];
             reinterpret_cast<half8_t*>(blk + 32)[0] = lo[0];
             reinterpret_cast<half8_t*>(blk + 32)[1] = lo[1];
+            if (codes16) {
+                half8_t* dst = reinterpret_cast<half8_t*>(codes16 + row * cols + 16 * j);
+                dst[0] = cq[0];
+                dst[1] = cq[1];
+            }
         }
     }
 #pragma unroll
@@ -214,14 +225,14 @@ hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q
 }
 
 hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_t cols, int parts, _Float16* out,
-                           float* mult, _Float16* uop, float* umult, hipStream_t st) {
+                           float* mult, _Float16* uop, float* umult, hipStream_t st, _Float16* codes16) {
     if (rows > 0) {
         if (parts == 2)
             hipLaunchKernelGGL(prescale_kernel<2>, dim3(grid_for(rows, 4)), dim3(256), 0, st, q, s, rows, cols, out,
-                               mult, uop, umult);
+                               mult, uop, umult, codes16);
         else
             hipLaunchKernelGGL(prescale_kernel<1>, dim3(grid_for(rows, 4)), dim3(256), 0, st, q, s, rows, cols, out,
-                               mult, uop, umult);
+                               mult, uop, umult, (_Float16*)nullptr);
     }
     return hipGetLastError();
 }
