@@ -53,13 +53,12 @@ struct ZeroWords {
 };
 hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q8, float* s, hipStream_t st,
                            ZeroWords z = ZeroWords{{nullptr, nullptr}});
-// fp16 GEMM operand q * s * 2^-e_r of int8 rows (parts 1: one fp16; 2: hi and
-// lo fp16 per value: per 32-wide block its 32 hi then its 32 lo values) and the row multipliers 2^e_r; plus
-// the offset-pass operand (u per block, hi/lo, [rows][offset_operand_halves])
-// and its row multipliers; with parts 2 and codes16 non-null also the codes
-// as fp16 [rows][cols] (exact).
+// fp16 GEMM operand of int8 rows, [rows][cols]: parts 1: q * s * 2^-e_r;
+// parts 0: the codes q themselves (exact).  Both: the row multipliers 2^e_r
+// in mult (if non-null), and the offset-pass operand (u per block, hi/lo,
+// [rows][offset_operand_halves]) and its row multipliers.
 hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_t cols, int parts, _Float16* out,
-                           float* mult, _Float16* uop, float* umult, hipStream_t st, _Float16* codes16 = nullptr);
+                           float* mult, _Float16* uop, float* umult, hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t st);
 
 // Router scratch: wt [E][H] fp32 (transposed weight, also read by the top-K
@@ -103,15 +102,14 @@ hipError_t launch_group(const int32_t* ids, const float* p, int64_t n, int32_t K
 hipError_t launch_chunks_from_offsets(const int32_t* offsets, int32_t E, const ChunkLists& cl, hipStream_t st);
 hipError_t launch_row_weights(const int32_t* slot, const float* p, int64_t n, float* prow, hipStream_t st);
 
-// gate/up: xb = prescaled input rows (parts 2), xe = their multipliers (the
-// small-chunk kernel); xa = the input codes as fp16 and xs = their block
-// scales (the large-chunk kernel); xuop / xum = offset-pass operand and
+// gate/up: xa = the input codes as fp16 (prescale parts 0) and xs = their
+// block scales, act_rows rows each; xuop / xum = offset-pass operand and
 // multipliers; writes int8 H codes hq and scales hs.
 // n = routed rows, E = experts (bounds of the two chunk lists' lengths).
 hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const ChunkLists& cl, int64_t n, int32_t E,
-                          const int32_t* src, const _Float16* xb, int64_t act_rows, const float* xe,
-                          const _Float16* xa, const float* xs, const _Float16* xuop, const float* xum, int32_t H,
-                          int32_t I, int8_t* hq, float* hs, hipStream_t st);
+                          const int32_t* src, const _Float16* xa, const float* xs, int64_t act_rows,
+                          const _Float16* xuop, const float* xum, int32_t H, int32_t I, int8_t* hq, float* hs,
+                          hipStream_t st);
 // down: hb = prescaled H rows (parts 1), he = their multipliers, huop / hum =
 // offset-pass operand and multipliers; writes the weighted rows dm.
 hipError_t launch_down(const uint8_t* blobs, int64_t stride, const ChunkLists& cl, int64_t n, int32_t E,

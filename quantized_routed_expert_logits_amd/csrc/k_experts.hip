@@ -17,17 +17,16 @@
 // The first sum runs on v_mfma_f32_16x16x32_f16 (K = 32 = one block): the A
 // operand d*(q-1) is exact in fp16 (q - 1 in {-1, 0, 1, 2}).  Two forms of the
 // B operand:
-//   prescaled: the activation s*a*2^-e of the row (one fp16 for down, a hi
-//     and a lo fp16 for gate/up, two MFMAs into the same accumulator), so the
-//     block scale needs no vector-ALU multiply and the accumulators run over
-//     the whole reduction; after the loop the results are multiplied by the
-//     row's 2^e (exact);
-//   rescaled (gate/up, chunks of more than kSmallRows rows): the codes a
-//     themselves (exact in fp16).  One MFMA per block gives d * sum (q-1) a
-//     exactly (an integer times d: at most 24 significant bits), and one fp32
-//     FMA per output adds it times the block's s.  Half the MFMAs and half the
-//     activation bytes of the hi/lo form, for 4 FMAs per MFMA on the vector
-//     ALU, and the sum is more precise.  The d*u terms of all blocks form a small matrix product over the
+//   rescaled (gate/up): the codes a themselves (exact in fp16).  One MFMA per
+//     block with a zero accumulator gives d * sum (q-1) a exactly (an integer
+//     below 2^13 times d: at most 24 significant bits), and one fp32 FMA per
+//     output adds it times the block's s.  gate/up needs more than fp16's 11
+//     bits of the activations (its output is rounded to int8 again); this
+//     form keeps them all for 4 vector FMAs per MFMA;
+//   prescaled (down): the activation s*a*2^-e of the row as one fp16, so the
+//     block scale rides inside the MFMA and the accumulators run over the
+//     whole reduction; after the loop the results are multiplied by the row's
+//     2^e (exact).  The d*u terms of all blocks form a small matrix product over the
 // block index (K = Kd/32), done after the block loop on the MFMA unit: A = d
 // (exact in fp16), B = u of each row scaled by a power of two to [-1, 1] and
 // split into a high and a low fp16 part (22 bits).
@@ -147,11 +146,10 @@ struct GemmArgs {
     int32_t Kd;            // reduction length (H for gate/up, I for down)
     const int32_t* src;    // token of each grouped row
     const float* prow;     // routing weight of each grouped row (down)
-    const _Float16* act;   // prescaled activations [rows][Kd x parts]
-    int64_t act_rows;      // rows of act / am / uop / um (and act1 / ascale)
-    const _Float16* act1;  // rescaled form (gate/up, 4-wave kernel): codes as fp16 [rows][Kd]
-    const float* ascale;   // ... and their block scales [rows][Kd / 32]
-    const float* am;       // row multipliers 2^e [rows]
+    const _Float16* act;   // activations [rows][Kd] fp16: gate/up the codes, down prescaled
+    int64_t act_rows;      // rows of act / ascale / am / uop / um
+    const float* ascale;   // gate/up: block scales of act [rows][Kd / 32]
+    const float* am;       // down: row multipliers 2^e of act [rows]
     const _Float16* uop;   // offset-pass operand [rows][nch x 32 blocks x 2] (hi, lo)
     const float* um;       // its row multipliers [rows]
     int32_t I, H;
@@ -162,16 +160,15 @@ struct GemmArgs {
 
 // The K loop over 32-wide blocks.  Per block: every thread unpacks its dword
 // of the slab's record into LDS buffer b&1 (and the two scales into the
-// offset-pass matrix), one barrier, then the wave's NT tiles x 8 fragments x
-// P parts of MFMAs, fragment-major.
+// offset-pass matrix), one barrier, then the wave's NT tiles x 8 fragments of
+// MFMAs, fragment-major.
 // Records are prefetched several blocks ahead in a register ring and
 // activation fragments one block ahead in two alternating register sets, so
 // the loop body has no copies.
-template <int P, bool kRescale>
+template <bool kRescale>
 struct BlockLoop {
-    static_assert(!kRescale || P == 1, "the rescaled form has one part");
     __amdgpu_buffer_rsrc_t rec;  // this slab's records (nblk x 1280 bytes)
-    __amdgpu_buffer_rsrc_t act;  // activations [rows][Kd x P] fp16 (prescaled, or codes with kRescale)
+    __amdgpu_buffer_rsrc_t act;  // activations [rows][Kd] fp16: codes (kRescale) or prescaled
     __amdgpu_buffer_rsrc_t scl;  // kRescale: block scales [rows][nblk] fp32
     int32_t Kd, nblk, dstride;
     int tau, lane, r16, kg, p, paddr;
@@ -189,17 +186,15 @@ struct BlockLoop {
 
     // Activation fragments of a block in the loader layout (see loader_row):
     // lvoff[i] is this lane's byte offset of its loader row and group in tile
-    // i; a block holds P parts of 64 bytes per row.
+    // i; a block is 64 bytes of a row.
     template <int NT>
     __device__ __forceinline__ void load_act(int blk, const int (&lvoff)[kTilesPerWave],
-                                             half8_t (&bf)[kTilesPerWave][P]) const {
+                                             half8_t (&bf)[kTilesPerWave]) const {
         blk = blk < nblk ? blk : nblk - 1;
 #pragma unroll
         for (int i = 0; i < NT; ++i)
-#pragma unroll
-            for (int h = 0; h < P; ++h)
-                bf[i][h] = __builtin_bit_cast(
-                    half8_t, __builtin_amdgcn_raw_buffer_load_b128(act, lvoff[i] + 64 * h, blk * kBlock * 2 * P, 0));
+            bf[i] = __builtin_bit_cast(half8_t,
+                                       __builtin_amdgcn_raw_buffer_load_b128(act, lvoff[i], blk * kBlock * 2, 0));
     }
 
     // kRescale: the block scale of this lane's MFMA column in each tile;
@@ -230,14 +225,12 @@ struct BlockLoop {
     }
 
     template <int NT>
-    __device__ __forceinline__ void products(int blk, const half8_t (&raw)[kTilesPerWave][P],
+    __device__ __forceinline__ void products(int blk, const half8_t (&raw)[kTilesPerWave],
                                              const float (&sv)[kTilesPerWave],
                                              float4_t (&acc)[kFrags][kTilesPerWave]) const {
-        half8_t bf[kTilesPerWave][P];
+        half8_t bf[kTilesPerWave];
 #pragma unroll
-        for (int i = 0; i < NT; ++i)
-#pragma unroll
-            for (int h = 0; h < P; ++h) bf[i][h] = to_mfma_layout(raw[i][h], paddr);
+        for (int i = 0; i < NT; ++i) bf[i] = to_mfma_layout(raw[i], paddr);
         // A fragments in two groups of four (registers are tight: the next
         // block's unpack interleaves with these MFMAs)
 #pragma unroll
@@ -251,7 +244,7 @@ struct BlockLoop {
 #pragma unroll
                     for (int i = 0; i < NT; ++i) {
                         const float4_t t = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            a[f], bf[i][0], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                            a[f], bf[i], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
                         for (int v = 0; v < 4; ++v) acc[4 * g + f][i][v] = fmaf(t[v], sv[i], acc[4 * g + f][i][v]);
                     }
@@ -259,11 +252,9 @@ struct BlockLoop {
 #pragma unroll
                 for (int f = 0; f < kFrags / 2; ++f)
 #pragma unroll
-                    for (int h = 0; h < P; ++h)
-#pragma unroll
-                        for (int i = 0; i < NT; ++i)
-                            acc[4 * g + f][i] =
-                                __builtin_amdgcn_mfma_f32_16x16x32_f16(a[f], bf[i][h], acc[4 * g + f][i], 0, 0, 0);
+                    for (int i = 0; i < NT; ++i)
+                        acc[4 * g + f][i] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_f16(a[f], bf[i], acc[4 * g + f][i], 0, 0, 0);
             }
         }
     }
@@ -279,7 +270,7 @@ struct BlockLoop {
                                         float4_t (&acc)[kFrags][kTilesPerWave]) const {
         static_assert(D % 2 == 0, "activation sets alternate per block");
         uint32_t xw[D], sw[D];
-        half8_t bf[2][kTilesPerWave][P];
+        half8_t bf[2][kTilesPerWave];
         float sv[2][kTilesPerWave] = {};
         // Issue order matters: each unpack waits for its record with a vmcnt
         // that counts the loads issued after it, and the loop header merges
@@ -402,9 +393,8 @@ __device__ __forceinline__ void big_chunk_item(const GemmArgs& g, const Tile tl,
     // lvoff = byte offset of its loader row and group, soff = byte offset of
     // the column's block scales (rescaled form; padding rows read row 0 and
     // are never stored).  gate/up takes the rescaled form, down the
-    // prescaled one with one part.
+    // prescaled one.
     constexpr bool kRescale = kGateUp;
-    constexpr int P = 1;
     int64_t arow[kTilesPerWave];
     int lvoff[kTilesPerWave], soff[kTilesPerWave];
     int ntw = 0;
@@ -418,7 +408,7 @@ __device__ __forceinline__ void big_chunk_item(const GemmArgs& g, const Tile tl,
         if (r < tl.nrows) arow[i] = kGateUp ? (int64_t)g.src[tl.row0 + r] : (int64_t)(tl.row0 + r);
         int64_t la = 0;
         if (lr < tl.nrows) la = kGateUp ? (int64_t)g.src[tl.row0 + lr] : (int64_t)(tl.row0 + lr);
-        lvoff[i] = (int)la * g.Kd * 2 * P + 16 * (lane & 3);
+        lvoff[i] = (int)la * g.Kd * 2 + 16 * (lane & 3);
         soff[i] = (int)(arow[i] >= 0 ? arow[i] : 0) * nblk * 4;
     }
 
@@ -430,10 +420,9 @@ __device__ __forceinline__ void big_chunk_item(const GemmArgs& g, const Tile tl,
     for (int f = 0; f < kFrags; ++f)
 #pragma unroll
         for (int i = 0; i < kTilesPerWave; ++i) acc[f][i] = (float4_t){0.f, 0.f, 0.f, 0.f};
-    BlockLoop<P, kRescale> L{
+    BlockLoop<kRescale> L{
         __builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, nblk * kRecordBytes, kBufferWord3),
-        __builtin_amdgcn_make_buffer_rsrc((void*)(kRescale ? g.act1 : g.act), (short)0,
-                                          (int)(g.act_rows * g.Kd * 2 * P), kBufferWord3),
+        __builtin_amdgcn_make_buffer_rsrc((void*)g.act, (short)0, (int)(g.act_rows * g.Kd * 2), kBufferWord3),
         __builtin_amdgcn_make_buffer_rsrc((void*)g.ascale, (short)0, kRescale ? (int)(g.act_rows * nblk * 4) : 0,
                                           kBufferWord3),
         g.Kd, nblk, dstride, tau, lane, r16, kg, p, mfma_source_addr(lane), d_lds, a_lds, UnpackMagic()};
@@ -554,17 +543,14 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_kernel(GemmArgs g) {
 // its rows for the offset pass in its own LDS area, 32 blocks at a time, and
 // runs that pass every 32 blocks, adding it with the ratio of the two row
 // multipliers (powers of two) before the final multiply.
-template <int P, int NT>
+// The activation fragments are read straight in the MFMA layout: at one
+// 16-byte load per tile and block the L1 keeps up with 16 rows per load, and
+// the lane exchange of the 4-wave kernel costs more than it saves here.
+template <int NT, bool kRescale>
 struct SlabPass {
-    // With one part (down) the activation fragments are read straight in the
-    // MFMA layout: at one 16-byte load per tile and block the L1 keeps up with
-    // 16 rows per load, and the lane exchange costs more than it saves.  Two
-    // parts (gate/up) read twice as much and keep the coalesced read plus
-    // exchange.
-    static constexpr bool kDirect = P == 1;
-    __amdgpu_buffer_rsrc_t rec, act;
+    __amdgpu_buffer_rsrc_t rec, act, scl;
     int32_t Kd, nblk;
-    int lane, r16, kg, paddr;
+    int lane, r16, kg;
     _Float16* dl;  // [kSlabRows][kDlStride]
     UnpackMagic mg;
 
@@ -581,16 +567,20 @@ struct SlabPass {
         }
     }
 
-    // Activation fragments of a block, in the loader layout (see loader_row) or,
-    // with kDirect, in the MFMA layout.
-    __device__ __forceinline__ void load_act(int blk, const int (&lvoff)[NT], half8_t (&bf)[NT][P]) const {
+    // Activation fragments of a block (lvoff: this lane's byte offset of its
+    // column's row and group); with kRescale also the block scale of the
+    // lane's column in each tile (soff: byte offset of that row's scales).
+    __device__ __forceinline__ void load_act(int blk, const int (&lvoff)[NT], const int (&soff)[NT],
+                                             half8_t (&bf)[NT], float (&sv)[NT]) const {
         blk = blk < nblk ? blk : nblk - 1;
 #pragma unroll
         for (int i = 0; i < NT; ++i)
+            bf[i] = __builtin_bit_cast(half8_t,
+                                       __builtin_amdgcn_raw_buffer_load_b128(act, lvoff[i], blk * kBlock * 2, 0));
+        if constexpr (kRescale)
 #pragma unroll
-            for (int h = 0; h < P; ++h)
-                bf[i][h] = __builtin_bit_cast(
-                    half8_t, __builtin_amdgcn_raw_buffer_load_b128(act, lvoff[i] + 64 * h, blk * kBlock * 2 * P, 0));
+            for (int i = 0; i < NT; ++i)
+                sv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(scl, soff[i], blk * 4, 0));
     }
 
     // Unpack dword p (fragments 2p, 2p+1).
@@ -613,15 +603,12 @@ struct SlabPass {
     // few VALU instructions), so the matrix unit and the vector ALU of the
     // wave work side by side.
     __device__ __forceinline__ void block(int blk, const uint32_t (&xw)[4], const uint32_t (&sw)[4],
-                                          const half8_t (&raw)[NT][P], float4_t (&acc)[kFrags][NT]) const {
-        constexpr int kMfmas = 2 * NT * P;                  // per dword
-        constexpr int kValuPer = (26 + kMfmas - 1) / kMfmas;  // unpack instructions per MFMA slot
+                                          const half8_t (&bf)[NT], const float (&sv)[NT],
+                                          float4_t (&acc)[kFrags][NT]) const {
+        constexpr int kMfmas = 2 * NT;                                // per dword
+        constexpr int kValu = 26 + (kRescale ? 4 * kMfmas : 0);       // unpack (+ rescale FMAs) per dword
+        constexpr int kValuPer = (kValu + kMfmas - 1) / kMfmas;       // VALU instructions per MFMA slot
         const int col = blk & 31;
-        half8_t bf[NT][P];
-#pragma unroll
-        for (int i = 0; i < NT; ++i)
-#pragma unroll
-            for (int h = 0; h < P; ++h) bf[i][h] = kDirect ? raw[i][h] : to_mfma_layout(raw[i][h], paddr);
         half8_t a[2][2];
         prepare(0, xw, sw, a[0]);
         park_scales(col, sw);
@@ -629,15 +616,26 @@ struct SlabPass {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             if (p < 3) prepare(p + 1, xw, sw, a[(p + 1) & 1]);
-#pragma unroll
-            for (int h = 0; h < P; ++h)
+            if constexpr (kRescale) {
 #pragma unroll
                 for (int i = 0; i < NT; ++i) {
-                    acc[2 * p][i] =
-                        __builtin_amdgcn_mfma_f32_16x16x32_f16(a[p & 1][0], bf[i][h], acc[2 * p][i], 0, 0, 0);
-                    acc[2 * p + 1][i] =
-                        __builtin_amdgcn_mfma_f32_16x16x32_f16(a[p & 1][1], bf[i][h], acc[2 * p + 1][i], 0, 0, 0);
+                    const float4_t z = {0.f, 0.f, 0.f, 0.f};
+                    const float4_t t0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[p & 1][0], bf[i], z, 0, 0, 0);
+                    const float4_t t1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[p & 1][1], bf[i], z, 0, 0, 0);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        acc[2 * p][i][v] = fmaf(t0[v], sv[i], acc[2 * p][i][v]);
+                        acc[2 * p + 1][i][v] = fmaf(t1[v], sv[i], acc[2 * p + 1][i][v]);
+                    }
                 }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NT; ++i) {
+                    acc[2 * p][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[p & 1][0], bf[i], acc[2 * p][i], 0, 0, 0);
+                    acc[2 * p + 1][i] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_f16(a[p & 1][1], bf[i], acc[2 * p + 1][i], 0, 0, 0);
+                }
+            }
             if (p < 3) {
 #pragma unroll
                 for (int k = 0; k < kMfmas; ++k) {
@@ -684,14 +682,15 @@ struct SlabPass {
     // activation fragments one block ahead in two alternating sets.
     template <int D>
     __device__ __forceinline__ void run(int nch, const _Float16* uop, const int64_t (&arow)[NT],
-                                        const int (&lvoff)[NT], const float (&ratio)[NT],
+                                        const int (&lvoff)[NT], const int (&soff)[NT], const float (&ratio)[NT],
                                         float4_t (&acc)[kFrags][NT]) const {
         uint32_t xw[D][4], sw[D][4];
-        half8_t bf[2][NT][P];
+        half8_t bf[2][NT];
+        float sv[2][NT] = {};
 #pragma unroll
         for (int j = 0; j < D; ++j) load_record(j, xw[j], sw[j]);
         __builtin_amdgcn_sched_barrier(0);
-        load_act(0, lvoff, bf[0]);
+        load_act(0, lvoff, soff, bf[0], sv[0]);
         __builtin_amdgcn_sched_barrier(0);
         for (int c = 0; c < nch; ++c) {
             const int bend = nblk < 32 * c + 32 ? nblk : 32 * c + 32;
@@ -699,9 +698,9 @@ struct SlabPass {
 #pragma unroll
                 for (int j = 0; j < D; ++j) {
                     const int blk = b + j;
-                    load_act(blk + 1, lvoff, bf[(j + 1) & 1]);
+                    load_act(blk + 1, lvoff, soff, bf[(j + 1) & 1], sv[(j + 1) & 1]);
                     __builtin_amdgcn_sched_barrier(0);
-                    block(blk, xw[j], sw[j], bf[j & 1], acc);
+                    block(blk, xw[j], sw[j], bf[j & 1], sv[j & 1], acc);
                     load_record(blk + D, xw[j], sw[j]);
                 }
             }
@@ -713,7 +712,8 @@ struct SlabPass {
 template <bool kGateUp, int NT>
 __device__ __forceinline__ void small_chunk_pass(const GemmArgs& g, const Tile& tl, int slab, int t0, int lane,
                                                  _Float16* dl) {
-    constexpr int P = kGateUp ? 2 : 1;
+    constexpr bool kRescale = kGateUp;  // gate/up: codes and block scales; down: prescaled H
+    using Pass = SlabPass<NT, kRescale>;
     const int r16 = lane & 15, kg = lane >> 4;
     const int nblk = g.Kd / kBlock, nch = (nblk + 31) / 32;
 
@@ -722,19 +722,17 @@ __device__ __forceinline__ void small_chunk_pass(const GemmArgs& g, const Tile& 
         reinterpret_cast<half8_t*>(dl)[o] = (half8_t){0, 0, 0, 0, 0, 0, 0, 0};
 
     int64_t arow[NT];
-    int lvoff[NT];
-    float ratio[NT];
+    int lvoff[NT], soff[NT];
+    float ratio[NT];  // offset pass against main products: um / am (rescaled form: um, there is no am)
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-        const int r = 16 * (t0 + i) + r16, lr = 16 * (t0 + i) + loader_row(lane);
+        const int r = 16 * (t0 + i) + r16;
         arow[i] = -1;
         if (r < tl.nrows) arow[i] = kGateUp ? (int64_t)g.src[tl.row0 + r] : (int64_t)(tl.row0 + r);
-        ratio[i] = arow[i] >= 0 ? g.um[arow[i]] / g.am[arow[i]] : 0.f;
-        int64_t la = 0;
-        if (lr < tl.nrows) la = kGateUp ? (int64_t)g.src[tl.row0 + lr] : (int64_t)(tl.row0 + lr);
-        if constexpr (SlabPass<P, NT>::kDirect)  // MFMA layout: column r16, group kg
-            la = arow[i] >= 0 ? arow[i] : 0;
-        lvoff[i] = (int)la * g.Kd * 2 * P + (SlabPass<P, NT>::kDirect ? 16 * kg : 16 * (lane & 3));
+        ratio[i] = arow[i] >= 0 ? (kRescale ? g.um[arow[i]] : g.um[arow[i]] / g.am[arow[i]]) : 0.f;
+        const int64_t ar = arow[i] >= 0 ? arow[i] : 0;  // padding columns read row 0, never stored
+        lvoff[i] = (int)ar * g.Kd * 2 + 16 * kg;        // MFMA layout: column r16, group kg
+        soff[i] = (int)ar * nblk * 4;
     }
     float4_t acc[kFrags][NT];
 #pragma unroll
@@ -743,15 +741,16 @@ __device__ __forceinline__ void small_chunk_pass(const GemmArgs& g, const Tile& 
         for (int i = 0; i < NT; ++i) acc[f][i] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
     const uint8_t* rec = g.blobs + (int64_t)tl.e * g.stride + (int64_t)slab * nblk * kRecordBytes;
-    SlabPass<P, NT> L{__builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, nblk * kRecordBytes, kBufferWord3),
-                      __builtin_amdgcn_make_buffer_rsrc((void*)g.act, (short)0, (int)(g.act_rows * g.Kd * 2 * P),
-                                                        kBufferWord3),
-                      g.Kd, nblk, lane, r16, kg, mfma_source_addr(lane), dl, UnpackMagic()};
-    L.template run<2>(nch, g.uop, arow, lvoff, ratio, acc);
+    Pass L{__builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, nblk * kRecordBytes, kBufferWord3),
+           __builtin_amdgcn_make_buffer_rsrc((void*)g.act, (short)0, (int)(g.act_rows * g.Kd * 2), kBufferWord3),
+           __builtin_amdgcn_make_buffer_rsrc((void*)g.ascale, (short)0, kRescale ? (int)(g.act_rows * nblk * 4) : 0,
+                                             kBufferWord3),
+           g.Kd, nblk, lane, r16, kg, dl, UnpackMagic()};
+    L.template run<2>(nch, g.uop, arow, lvoff, soff, ratio, acc);
 
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-        const float mult = arow[i] >= 0 ? g.am[arow[i]] : 0.f;
+        const float mult = arow[i] >= 0 ? (kRescale ? 1.0f : g.am[arow[i]]) : 0.f;
         float4_t a[kFrags];
 #pragma unroll
         for (int f = 0; f < kFrags; ++f)
@@ -766,7 +765,7 @@ __device__ __forceinline__ void small_chunk_pass(const GemmArgs& g, const Tile& 
 }
 
 template <bool kGateUp>
-__global__ void __launch_bounds__(256, 3) expert_gemm_small_kernel(GemmArgs g) {
+__global__ void __launch_bounds__(256, 2) expert_gemm_small_kernel(GemmArgs g) {
     __shared__ _Float16 dl_all[kWaves][kSlabRows * kDlStride];
     static_assert(kSlabRows * kDlStride * sizeof(_Float16) >= 16 * kParkStride * sizeof(float),
                   "a wave's d buffer also parks one output tile");
@@ -888,10 +887,10 @@ void launch_gemms(GemmArgs g, const ChunkLists& cl, int64_t n, int32_t E, size_t
 }  // namespace
 
 hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const ChunkLists& cl, int64_t n, int32_t E,
-                          const int32_t* src, const _Float16* xb, int64_t act_rows, const float* xe,
-                          const _Float16* xa, const float* xs, const _Float16* xuop, const float* xum, int32_t H,
-                          int32_t I, int8_t* hq, float* hs, hipStream_t st) {
-    GemmArgs g{blobs, stride, nullptr, nullptr, 2 * I / kSlabRows, H, src, nullptr, xb, act_rows, xa, xs, xe, xuop,
+                          const int32_t* src, const _Float16* xa, const float* xs, int64_t act_rows,
+                          const _Float16* xuop, const float* xum, int32_t H, int32_t I, int8_t* hq, float* hs,
+                          hipStream_t st) {
+    GemmArgs g{blobs, stride, nullptr, nullptr, 2 * I / kSlabRows, H, src, nullptr, xa, act_rows, xs, nullptr, xuop,
                xum, I, H, hq, hs, nullptr};
     launch_gemms(g, cl, n, E, dynamic_lds_bytes(H, false), true, st);
     return hipGetLastError();
@@ -900,8 +899,8 @@ hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const ChunkLists
 hipError_t launch_down(const uint8_t* blobs, int64_t stride, const ChunkLists& cl, int64_t n, int32_t E,
                        const int32_t* src, const float* prow, const _Float16* hb, int64_t act_rows, const float* he,
                        const _Float16* huop, const float* hum, int32_t H, int32_t I, float* dm, hipStream_t st) {
-    GemmArgs g{blobs, stride, nullptr, nullptr, H / kSlabRows, I, src, prow, hb, act_rows, nullptr, nullptr, he, huop,
-               hum, I, H,
+    GemmArgs g{blobs, stride, nullptr, nullptr, H / kSlabRows, I, src, prow, hb, act_rows, nullptr, he, huop, hum, I,
+               H,
                nullptr, nullptr, dm};
     launch_gemms(g, cl, n, E, dynamic_lds_bytes(I, true), false, st);
     return hipGetLastError();

@@ -12,25 +12,16 @@
 // wave reads 1 KiB of contiguous input per instruction.  Outputs per block:
 // the int8 codes and the scale.
 //
-// Prescale: the expert GEMMs take each activation value q * s as an fp16
-// operand, so the per-block scale rides inside the MFMA and no per-block
-// multiply is left on the vector ALU.  A row r is first scaled by 2^-e_r,
-// chosen so that the row's largest possible |q * s| (127 * max s) lands in
-// [2^14, 2^15): fp16 cannot overflow and small values keep their bits.  The
-// row multiplier 2^e_r is written beside the operand; the GEMM multiplies its
-// fp32 results by it (exact).  Two forms:
-//   parts = 1: hi = fp16(q * s * 2^-e), 11 significant bits (the down GEMM,
-//              whose output is not rounded to int8 again);
-//   parts = 2: hi as above and lo = fp16(v - hi), v = fp32(q * s * 2^-e), so
-//              hi + lo carries about 22 bits (the gate/up GEMM, whose output
-//              is rounded to int8 and must not move the rounding points).
-// parts = 2 layout per row: per 32-wide block, its 32 hi values then its 32
-// lo values (128 bytes per block), so each part of a block is 64 contiguous
-// bytes (four lanes of a GEMM's coalesced fragment load).
-//
-// With parts = 2 the kernel can also write the codes themselves as fp16
-// (exact), the operand of the large-chunk gate/up kernel, which applies the
-// block scales in fp32 after each block's products.
+// Prescale: the fp16 operand of the expert GEMMs, [rows][cols].  Two forms:
+//   parts = 1 (the down GEMM): fp16(q * s * 2^-e_r), 11 significant bits, so
+//     the per-block scale rides inside the MFMA.  A row r is first scaled by
+//     2^-e_r, chosen so that the row's largest possible |q * s| (127 * max s)
+//     lands in [2^14, 2^15): fp16 cannot overflow and small values keep their
+//     bits.  The row multiplier 2^e_r is written beside the operand; the GEMM
+//     multiplies its fp32 results by it (exact).  The down output is not
+//     rounded to int8 again, so 11 bits suffice.
+//   parts = 0 (the gate/up GEMM): the codes q themselves (exact); the GEMM
+//     applies the block scales in fp32 after each block's products.
 //
 // The same kernel writes the operand of the GEMMs' offset pass: per block,
 // u = -0.5 * s * (sum of the block's codes) (the 2-bit weight offset's share,
@@ -93,7 +84,7 @@ template <int P>
 __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict__ q, const float* __restrict__ s,
                                                        int64_t rows, int32_t cols, _Float16* __restrict__ out,
                                                        float* __restrict__ mult, _Float16* __restrict__ uop,
-                                                       float* __restrict__ umult, _Float16* __restrict__ codes16) {
+                                                       float* __restrict__ umult) {
     __shared__ float ush[4][kMaxOffsetChunks * 32];
     const int w = threadIdx.x >> 6;
     const int64_t row = (int64_t)blockIdx.x * 4 + w;
@@ -102,6 +93,9 @@ __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict_
     const int nb = cols / kBlock;
     const int nch = (nb + 31) / 32;
     const float* srow = s + row * nb;
+    // the row multiplier 2^e (written for both forms when mult is given: the
+    // router takes the input rows' multipliers from here); parts 1 scales by
+    // its inverse
     float m = 0.0f;
     for (int b = lane; b < nb; b += 64) m = fmaxf(m, srow[b]);
 #pragma unroll
@@ -115,7 +109,7 @@ __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict_
         scale = ldexpf(1.0f, 15 - ex);
         back = ldexpf(1.0f, ex - 15);
     }
-    if (lane == 0) mult[row] = back;
+    if (mult && lane == 0) mult[row] = back;
     const int8_t* qrow = q + row * cols;
     float umax = 0.0f;
     for (int j0 = 0; j0 < cols / 16; j0 += 64) {  // uniform trip count: the shuffle below sees whole waves
@@ -143,6 +137,7 @@ __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict_
             umax = fmaxf(umax, fabsf(u));
         }
         if (!on) continue;
+        half8_t* dst = reinterpret_cast<half8_t*>(out + row * cols + 16 * j);
         if constexpr (P == 1) {
             half8_t h0, h1;
 #pragma unroll
@@ -151,31 +146,11 @@ __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict_
                 h0[i] = (_Float16)v[i];
                 h1[i] = (_Float16)v[8 + i];
             }
-            half8_t* dst = reinterpret_cast<half8_t*>(out + row * cols + 16 * j);
             dst[0] = h0;
             dst[1] = h1;
         } else {
-            half8_t hi[2], lo[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    _Float16 a, b;
-                    split_hi_lo(v[8 * h + i], a, b);
-                    hi[h][i] = a;
-                    lo[h][i] = b;
-                }
-            // block j/2, values 16*(j%2) .. +15: 32 bytes of its hi part and 32 of its lo part
-            _Float16* blk = out + row * (int64_t)cols * 2 + 64 * (j >> 1) + 16 * (j & 1);
-            reinterpret_cast<half8_t*>(blk)[0] = hi[0];
-            reinterpret_cast<half8_t*>(blk)[1] = hi[1];
-            reinterpret_cast<half8_t*>(blk + 32)[0] = lo[0];
-            reinterpret_cast<half8_t*>(blk + 32)[1] = lo[1];
-            if (codes16) {
-                half8_t* dst = reinterpret_cast<half8_t*>(codes16 + row * cols + 16 * j);
-                dst[0] = cq[0];
-                dst[1] = cq[1];
-            }
+            dst[0] = cq[0];
+            dst[1] = cq[1];
         }
     }
 #pragma unroll
@@ -225,14 +200,14 @@ hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q
 }
 
 hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_t cols, int parts, _Float16* out,
-                           float* mult, _Float16* uop, float* umult, hipStream_t st, _Float16* codes16) {
+                           float* mult, _Float16* uop, float* umult, hipStream_t st) {
     if (rows > 0) {
-        if (parts == 2)
-            hipLaunchKernelGGL(prescale_kernel<2>, dim3(grid_for(rows, 4)), dim3(256), 0, st, q, s, rows, cols, out,
-                               mult, uop, umult, codes16);
+        if (parts == 0)
+            hipLaunchKernelGGL(prescale_kernel<0>, dim3(grid_for(rows, 4)), dim3(256), 0, st, q, s, rows, cols, out,
+                               mult, uop, umult);
         else
             hipLaunchKernelGGL(prescale_kernel<1>, dim3(grid_for(rows, 4)), dim3(256), 0, st, q, s, rows, cols, out,
-                               mult, uop, umult, (_Float16*)nullptr);
+                               mult, uop, umult);
     }
     return hipGetLastError();
 }

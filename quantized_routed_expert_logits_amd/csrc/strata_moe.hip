@@ -124,7 +124,6 @@ struct Buffers {
     float* p;
     int8_t* xq;
     float* xs;
-    _Float16* xb;
     _Float16* xa;
     float* xe;
     _Float16* xuop;
@@ -149,7 +148,7 @@ struct Buffers {
 };
 
 struct Offsets {
-    size_t logits, wt, wb, wm, pmax, amb, ids, p, xq, xs, xb, xa, xe, xuop, xum, hist, base, offsets, tiles, ntiles, err, src, slot, prow, hq, hs,
+    size_t logits, wt, wb, wm, pmax, amb, ids, p, xq, xs, xa, xe, xuop, xum, hist, base, offsets, tiles, ntiles, err, src, slot, prow, hq, hs,
         hb, he, huop, hum, dm, total;
     int64_t tiles_cap;
 };
@@ -170,7 +169,6 @@ Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I) {
     o.p = L.take<float>(n);
     o.xq = L.take<int8_t>(T * H);
     o.xs = L.take<float>(T * (H / kBlock));
-    o.xb = L.take<_Float16>(2 * T * H);
     o.xa = L.take<_Float16>(T * H);
     o.xe = L.take<float>(T);
     o.xuop = L.take<_Float16>(T * offset_operand_halves(H));
@@ -207,7 +205,6 @@ Buffers carve(char* ws, const Offsets& o) {
     b.p = (float*)(ws + o.p);
     b.xq = (int8_t*)(ws + o.xq);
     b.xs = (float*)(ws + o.xs);
-    b.xb = (_Float16*)(ws + o.xb);
     b.xa = (_Float16*)(ws + o.xa);
     b.xe = (float*)(ws + o.xe);
     b.xuop = (_Float16*)(ws + o.xuop);
@@ -337,7 +334,7 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     tm.begin(kQuantize);
     // the quantize kernel also clears the top-K near-tie count and the id error flag
     HIP_TRY(launch_quantize(x, T, H, b.xq, b.xs, st, ZeroWords{{b.amb, b.err}}), "quantize launch");
-    HIP_TRY(launch_prescale(b.xq, b.xs, T, H, 2, b.xb, b.xe, b.xuop, b.xum, st, b.xa), "prescale launch");
+    HIP_TRY(launch_prescale(b.xq, b.xs, T, H, 0, b.xa, b.xe, b.xuop, b.xum, st), "prescale launch");
     tm.end(kQuantize);
     tm.begin(kRouter);
     HIP_TRY(launch_router(x, b.xe, wr, ex->router_bias, T, H, E, RouterScratch{b.wt, b.wb, b.wm, nullptr, b.pmax}, b.logits,
@@ -354,8 +351,8 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
             "group launch");
     tm.end(kGroup);
     tm.begin(kGateUp);
-    HIP_TRY(launch_gate_up((const uint8_t*)ex->gate_up, ex->gate_up_stride, cl, n, E, b.src, b.xb, T, b.xe, b.xa, b.xs,
-                           b.xuop, b.xum, H, I, b.hq, b.hs, st),
+    HIP_TRY(launch_gate_up((const uint8_t*)ex->gate_up, ex->gate_up_stride, cl, n, E, b.src, b.xa, b.xs, T, b.xuop,
+                           b.xum, H, I, b.hq, b.hs, st),
             "gate/up launch");
     tm.end(kGateUp);
     tm.begin(kPrescaleH);
@@ -589,22 +586,20 @@ int strata_moe_gate_up(const int8_t* qx, const float* sx, const int32_t* offsets
     const int32_t E = experts->n_expert, H = experts->hidden, I = experts->ffn;
     const int64_t n = T * K;
     Layout L;
-    const size_t o_xb = L.take<_Float16>(2 * T * H), o_xa = L.take<_Float16>(T * H), o_xe = L.take<float>(T);
+    const size_t o_xa = L.take<_Float16>(T * H);
     const size_t o_xuop = L.take<_Float16>(T * offset_operand_halves(H)), o_xum = L.take<float>(T);
     const int64_t cap = chunk_list_cap(n, E);
     const size_t o_tiles = L.take<Tile>(2 * cap), o_nt = L.take<int32_t>(kSchedInts);
     char* ws = nullptr;
     TRY(get_workspace(L.off, &ws));
     const ChunkLists cl{(Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), cap};
-    _Float16* xb = (_Float16*)(ws + o_xb);
     _Float16* xa = (_Float16*)(ws + o_xa);
-    float* xe = (float*)(ws + o_xe);
     _Float16* xuop = (_Float16*)(ws + o_xuop);
     float* xum = (float*)(ws + o_xum);
-    HIP_TRY(launch_prescale(qx, sx, T, H, 2, xb, xe, xuop, xum, st, xa), "prescale launch");
+    HIP_TRY(launch_prescale(qx, sx, T, H, 0, xa, nullptr, xuop, xum, st), "prescale launch");
     HIP_TRY(launch_chunks_from_offsets(offsets, E, cl, st), "chunk list launch");
-    HIP_TRY(launch_gate_up((const uint8_t*)experts->gate_up, experts->gate_up_stride, cl, n, E, src, xb, T, xe, xa, sx,
-                           xuop, xum, H, I, qh, sh, st),
+    HIP_TRY(launch_gate_up((const uint8_t*)experts->gate_up, experts->gate_up_stride, cl, n, E, src, xa, sx, T, xuop,
+                           xum, H, I, qh, sh, st),
             "gate/up launch");
     return 0;
 }
