@@ -590,6 +590,43 @@ __device__ __forceinline__ double wave_dot_fp64(const float* __restrict__ x, con
     return wave_sum(acc);
 }
 
+// Two such dot products, x . w1 and x . w2, with the loads of both in flight
+// together; each sum is formed in the same order as wave_dot_fp64's.
+__device__ __forceinline__ void wave_dot2_fp64(const float* __restrict__ x, const float* __restrict__ w1,
+                                               const float* __restrict__ w2, int32_t H, int lane, double& v1,
+                                               double& v2) {
+    double a1 = 0.0, a2 = 0.0;
+    const int n4 = H / 256;
+    for (int c0 = 0; c0 < n4; c0 += kDotBatch) {
+        float4 xv[kDotBatch], p[kDotBatch], q[kDotBatch];
+#pragma unroll
+        for (int j = 0; j < kDotBatch; ++j)
+            if (c0 + j < n4) {
+                xv[j] = reinterpret_cast<const float4*>(x)[64 * (c0 + j) + lane];
+                p[j] = reinterpret_cast<const float4*>(w1)[64 * (c0 + j) + lane];
+                q[j] = reinterpret_cast<const float4*>(w2)[64 * (c0 + j) + lane];
+            }
+#pragma unroll
+        for (int j = 0; j < kDotBatch; ++j)
+            if (c0 + j < n4) {
+                a1 = fma((double)xv[j].x, (double)p[j].x, a1);
+                a1 = fma((double)xv[j].y, (double)p[j].y, a1);
+                a1 = fma((double)xv[j].z, (double)p[j].z, a1);
+                a1 = fma((double)xv[j].w, (double)p[j].w, a1);
+                a2 = fma((double)xv[j].x, (double)q[j].x, a2);
+                a2 = fma((double)xv[j].y, (double)q[j].y, a2);
+                a2 = fma((double)xv[j].z, (double)q[j].z, a2);
+                a2 = fma((double)xv[j].w, (double)q[j].w, a2);
+            }
+    }
+    for (int h = 256 * n4 + lane; h < H; h += 64) {
+        a1 = fma((double)x[h], (double)w1[h], a1);
+        a2 = fma((double)x[h], (double)w2[h], a2);
+    }
+    v1 = wave_sum(a1);
+    v2 = wave_sum(a2);
+}
+
 // One wave per listed token (grid-stride over the list), no workgroup
 // barrier.  Candidates: every expert within delta below the K-th value (this
 // includes all K selected).  Selected ranks outside every near-tie keep their
@@ -626,16 +663,38 @@ __global__ void __launch_bounds__(256) topk_resolve_kernel(const float* __restri
             todo |= (uint32_t)(c && !stable) << i;
         }
         const float* xr = x + t * H;
+        // the experts to re-score, two at a time (uniform over the wave): each
+        // round takes the next two set bits of the slots' candidate masks
+        uint64_t m[kSlots];
 #pragma unroll
-        for (int i = 0; i < kSlots; ++i) {
-            uint64_t m = __ballot((todo >> i) & 1u);
-            while (m) {  // uniform over the wave
-                const int l = __ffsll((unsigned long long)m) - 1;
-                m &= m - 1ull;
-                const int e = l + 64 * i;
-                double v = wave_dot_fp64(xr, wt + (int64_t)e * H, H, lane);
-                if (bias) v += (double)bias[e];
-                if (lane == l) cv[i] = v;
+        for (int i = 0; i < kSlots; ++i) m[i] = __ballot((todo >> i) & 1u);
+        for (;;) {
+            int e1 = -1, e2 = -1;
+#pragma unroll
+            for (int i = 0; i < kSlots; ++i) {
+                if (e1 < 0 && m[i]) {
+                    e1 = (__ffsll((unsigned long long)m[i]) - 1) + 64 * i;
+                    m[i] &= m[i] - 1ull;
+                }
+                if (e1 >= 0 && e2 < 0 && m[i]) {
+                    e2 = (__ffsll((unsigned long long)m[i]) - 1) + 64 * i;
+                    m[i] &= m[i] - 1ull;
+                }
+            }
+            if (e1 < 0) break;
+            double v1, v2 = 0.0;
+            if (e2 >= 0)
+                wave_dot2_fp64(xr, wt + (int64_t)e1 * H, wt + (int64_t)e2 * H, H, lane, v1, v2);
+            else
+                v1 = wave_dot_fp64(xr, wt + (int64_t)e1 * H, H, lane);
+            if (bias) {
+                v1 += (double)bias[e1];
+                if (e2 >= 0) v2 += (double)bias[e2];
+            }
+#pragma unroll
+            for (int i = 0; i < kSlots; ++i) {
+                const int e = lane + 64 * i;
+                cv[i] = e == e1 ? v1 : e == e2 ? v2 : cv[i];
             }
         }
         double lv[kMaxTopK];
