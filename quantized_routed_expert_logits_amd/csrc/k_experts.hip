@@ -593,7 +593,11 @@ struct SlabPass {
     // row hold the same 8 scales (fragments 0..7); lane kg writes those of
     // fragments 2kg and 2kg+1 only.
     __device__ __forceinline__ void park_scales(int col, const uint32_t (&sw)[4]) const {
-        const uint32_t s = kg == 0 ? sw[0] : kg == 1 ? sw[1] : kg == 2 ? sw[2] : sw[3];
+        // a bitwise select: a conditional chain here became a divergent branch
+        // that split the block's schedule
+        uint32_t s = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s |= sw[j] & (0u - (uint32_t)(kg == j));
         dl[(32 * kg + r16) * kDlStride + col] = lo_half(s);
         dl[(32 * kg + 16 + r16) * kDlStride + col] = hi_half(s);
     }
@@ -601,7 +605,9 @@ struct SlabPass {
     // One block, software-pipelined over the four dwords: the MFMAs of dword
     // p issue interleaved with the unpack of dword p + 1 (one MFMA, then a
     // few VALU instructions), so the matrix unit and the vector ALU of the
-    // wave work side by side.
+    // wave work side by side.  kRescale: the FMAs that scale dword p's
+    // products run one dword later, beside dword p + 1's MFMAs (the products
+    // are ready by then).
     __device__ __forceinline__ void block(int blk, const uint32_t (&xw)[4], const uint32_t (&sw)[4],
                                           const half8_t (&bf)[NT], const float (&sv)[NT],
                                           float4_t (&acc)[kFrags][NT]) const {
@@ -610,6 +616,7 @@ struct SlabPass {
         constexpr int kValuPer = (kValu + kMfmas - 1) / kMfmas;       // VALU instructions per MFMA slot
         const int col = blk & 31;
         half8_t a[2][2];
+        float4_t t[2][2][NT];  // kRescale: products of the last two dwords (fragment pair, tile)
         prepare(0, xw, sw, a[0]);
         park_scales(col, sw);
         __builtin_amdgcn_sched_barrier(0);
@@ -617,17 +624,13 @@ struct SlabPass {
         for (int p = 0; p < 4; ++p) {
             if (p < 3) prepare(p + 1, xw, sw, a[(p + 1) & 1]);
             if constexpr (kRescale) {
+                const float4_t z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int i = 0; i < NT; ++i) {
-                    const float4_t z = {0.f, 0.f, 0.f, 0.f};
-                    const float4_t t0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[p & 1][0], bf[i], z, 0, 0, 0);
-                    const float4_t t1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[p & 1][1], bf[i], z, 0, 0, 0);
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        acc[2 * p][i][v] = fmaf(t0[v], sv[i], acc[2 * p][i][v]);
-                        acc[2 * p + 1][i][v] = fmaf(t1[v], sv[i], acc[2 * p + 1][i][v]);
-                    }
+                    t[p & 1][0][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[p & 1][0], bf[i], z, 0, 0, 0);
+                    t[p & 1][1][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[p & 1][1], bf[i], z, 0, 0, 0);
                 }
+                if (p > 0) scale_products(p - 1, t[(p - 1) & 1], sv, acc);
             } else {
 #pragma unroll
                 for (int i = 0; i < NT; ++i) {
@@ -636,15 +639,28 @@ struct SlabPass {
                         __builtin_amdgcn_mfma_f32_16x16x32_f16(a[p & 1][1], bf[i], acc[2 * p + 1][i], 0, 0, 0);
                 }
             }
-            if (p < 3) {
+            if (p < 3 || kRescale) {
 #pragma unroll
                 for (int k = 0; k < kMfmas; ++k) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);  // then unpack VALU
+                    __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);  // then VALU
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (kRescale) scale_products(3, t[1], sv, acc);
+    }
+
+    // kRescale: acc of fragments 2p, 2p+1 += block scale * products.
+    __device__ __forceinline__ void scale_products(int p, const float4_t (&tp)[2][NT], const float (&sv)[NT],
+                                                   float4_t (&acc)[kFrags][NT]) const {
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                acc[2 * p][i][v] = fmaf(tp[0][i][v], sv[i], acc[2 * p][i][v]);
+                acc[2 * p + 1][i][v] = fmaf(tp[1][i][v], sv[i], acc[2 * p + 1][i][v]);
+            }
     }
 
     // Offset pass of 32-block chunk c: acc += (um / am) * sum_b d[row][b] u'[col][b].
