@@ -59,6 +59,12 @@ hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q
 // [rows][offset_operand_halves]) and its row multipliers.
 hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_t cols, int parts, _Float16* out,
                            float* mult, _Float16* uop, float* umult, hipStream_t st);
+// The layer input in one pass: launch_quantize's outputs (q8, s) and
+// launch_prescale's with parts 0 (codes16, mult, uop, umult), bit-identical to
+// the two launches; also clears the ZeroWords.
+hipError_t launch_quantize_prescale(const float* x, int64_t rows, int32_t cols, int8_t* q8, float* s,
+                                   _Float16* codes16, float* mult, _Float16* uop, float* umult, hipStream_t st,
+                                   ZeroWords z);
 hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t st);
 
 // Router scratch: wt [E][H] fp32 (transposed weight, also read by the top-K

@@ -181,6 +181,105 @@ __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict_
     }
 }
 
+// The layer input in one pass: quantize_kernel's int8 codes and scales and
+// prescale_kernel<0>'s outputs (fp16 codes, row multiplier, offset operand)
+// from the fp32 rows, one wave per row.  Lane pairs own a 32-value block, 16
+// values each (four float4 loads: the wave reads 4 KiB of the row per step);
+// the arithmetic of each output is that of the two separate kernels.
+__global__ void __launch_bounds__(256) quantize_prescale_kernel(const float* __restrict__ x, int64_t rows,
+                                                                int32_t cols, int8_t* __restrict__ q8,
+                                                                float* __restrict__ s_out, _Float16* __restrict__ out,
+                                                                float* __restrict__ mult, _Float16* __restrict__ uop,
+                                                                float* __restrict__ umult, ZeroWords z) {
+    __shared__ float ush[4][kMaxOffsetChunks * 32];
+    if (blockIdx.x == 0 && threadIdx.x < 2 && z.p[threadIdx.x]) *z.p[threadIdx.x] = 0;  // the call's flag words
+    const int w = threadIdx.x >> 6;
+    const int64_t row = (int64_t)blockIdx.x * 4 + w;
+    if (row >= rows) return;  // wave-uniform; only wave-level synchronisation below
+    const int lane = threadIdx.x & 63;
+    const int nb = cols / kBlock;
+    const int nch = (nb + 31) / 32;
+    const float* xrow = x + row * cols;
+    float smax = 0.0f, umax = 0.0f;
+    for (int j0 = 0; j0 < cols / 16; j0 += 64) {  // uniform trip count: the shuffles see whole waves
+        const int j = j0 + lane;                  // 16-value group j: block j / 2, half j % 2
+        const bool on = j < cols / 16;
+        float v[16];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            const float4 x4 = on ? reinterpret_cast<const float4*>(xrow + 16 * j)[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+            v[4 * f] = x4.x, v[4 * f + 1] = x4.y, v[4 * f + 2] = x4.z, v[4 * f + 3] = x4.w;
+        }
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(v[i]));
+        a = fmaxf(a, __shfl_xor(a, 1));
+        const float s = a / 127.0f;
+        int sum = 0;
+        uint32_t packed[4] = {0, 0, 0, 0};
+        half8_t cq[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float qf = s != 0.0f ? round_half_away(v[i] / s) : 0.0f;
+            const int c = (int)qf;
+            sum += c;
+            packed[i >> 2] |= (uint32_t)(uint8_t)(int8_t)c << (8 * (i & 3));
+            cq[i >> 3][i & 7] = (_Float16)c;  // exact: |c| <= 127
+        }
+        sum += __shfl_xor(sum, 1);
+        if (!on) continue;
+        smax = fmaxf(smax, s);
+        *reinterpret_cast<uint4*>(q8 + row * cols + 16 * j) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        half8_t* dst = reinterpret_cast<half8_t*>(out + row * cols + 16 * j);
+        dst[0] = cq[0];
+        dst[1] = cq[1];
+        if ((j & 1) == 0) {
+            s_out[row * nb + (j >> 1)] = s;
+            const float u = -0.5f * s * (float)sum;
+            ush[w][j >> 1] = u;
+            umax = fmaxf(umax, fabsf(u));
+        }
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        smax = fmaxf(smax, __shfl_xor(smax, o));
+        umax = fmaxf(umax, __shfl_xor(umax, o));
+    }
+    // the row multiplier, as prescale_kernel computes it from the block scales
+    const float bound = 127.0f * smax;
+    float back = 1.0f;
+    if (bound > 0.0f) {
+        int ex = 0;
+        frexpf(bound, &ex);
+        ex = ex < -96 ? -96 : ex;
+        back = ldexpf(1.0f, ex - 15);
+    }
+    if (lane == 0) mult[row] = back;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int eu = 0;
+    if (umax > 0.0f) frexpf(umax, &eu);
+    eu = eu < -100 ? -100 : eu;
+    const float dn = ldexpf(1.0f, -eu);
+    if (lane == 0) umult[row] = ldexpf(1.0f, eu);
+    if (lane < 4 * nch) {
+        half8_t hi, lo;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int b = 8 * lane + t;
+            const float un = b < nb ? ush[w][b] * dn : 0.0f;
+            _Float16 h, l;
+            split_hi_lo(un, h, l);
+            hi[t] = h;
+            lo[t] = l;
+        }
+        half8_t* dst = reinterpret_cast<half8_t*>(uop + row * (int64_t)nch * 64 + 16 * lane);
+        dst[0] = hi;
+        dst[1] = lo;
+    }
+}
+
 __global__ void fill_zero_kernel(float* __restrict__ p, int64_t count) {
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (g < count) p[g] = 0.0f;
@@ -209,6 +308,15 @@ hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_
             hipLaunchKernelGGL(prescale_kernel<1>, dim3(grid_for(rows, 4)), dim3(256), 0, st, q, s, rows, cols, out,
                                mult, uop, umult);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_prescale(const float* x, int64_t rows, int32_t cols, int8_t* q8, float* s,
+                                   _Float16* codes16, float* mult, _Float16* uop, float* umult, hipStream_t st,
+                                   ZeroWords z) {
+    if (rows > 0)
+        hipLaunchKernelGGL(quantize_prescale_kernel, dim3(grid_for(rows, 4)), dim3(256), 0, st, x, rows, cols, q8, s,
+                           codes16, mult, uop, umult, z);
     return hipGetLastError();
 }
 

@@ -332,9 +332,10 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     Buffers b = carve(ws, o);
     CallTimer tm(st);
     tm.begin(kQuantize);
-    // the quantize kernel also clears the top-K near-tie count and the id error flag
-    HIP_TRY(launch_quantize(x, T, H, b.xq, b.xs, st, ZeroWords{{b.amb, b.err}}), "quantize launch");
-    HIP_TRY(launch_prescale(b.xq, b.xs, T, H, 0, b.xa, b.xe, b.xuop, b.xum, st), "prescale launch");
+    // one pass over x: int8 codes and scales, their fp16 copy, row multipliers and
+    // offset operand; it also clears the top-K near-tie count and the id error flag
+    HIP_TRY(launch_quantize_prescale(x, T, H, b.xq, b.xs, b.xa, b.xe, b.xuop, b.xum, st, ZeroWords{{b.amb, b.err}}),
+            "quantize launch");
     tm.end(kQuantize);
     tm.begin(kRouter);
     HIP_TRY(launch_router(x, b.xe, wr, ex->router_bias, T, H, E, RouterScratch{b.wt, b.wb, b.wm, nullptr, b.pmax}, b.logits,
