@@ -55,7 +55,7 @@ extern "C" {
 /* Weight format: 2-bit codes q in {0,1,2,3} with one fp16 scale d per 32
  * consecutive codes along the reduction dimension; w = d * (q - 1.5).  The
  * pages' own Q2_0 packs use w = d * (q - 1) (moe_fused.hpp header comment);
- * this build's layer uses the symmetric map. */
+ * this library's layer uses the symmetric map. */
 #define STRATA_MOE_Q2_SYM 1
 
 /* A layer's experts, resident in device memory.  The blobs are written by

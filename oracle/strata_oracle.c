@@ -18,7 +18,7 @@
  *                  the epilogue; down into per-slot rows; a combine that reads
  *                  those rows.
  * Readings where the pages leave a step open are stated at each step; the
- * 2-bit weight map is the symmetric one used by this build, w = d*(q - 1.5)
+ * 2-bit weight map is the symmetric one, w = d*(q - 1.5)
  * with an fp16 d per 32 codes along the reduction dimension (the pages' own
  * Q2_0 pack uses w = d*(q - 1), moe_fused.hpp header comment).
  *

@@ -7,8 +7,8 @@ two sides see bit-identical arrays.
 
 Shapes follow the layer the Strata pages describe (Winery-Strata prefill.cpp
 page, the constants at the top of the file: hidden N = 2560, NE = 512 routed
-experts, K = 10 per token) with the expert FFN width used for this build
-(I = 1024), plus a tiny layer for fast checks.  The pages measure on private
+experts, K = 10 per token) with an expert FFN width of I = 1024, plus a tiny
+layer for fast checks.  The pages measure on private
 prompts and a trained GGUF pack; neither is available, so these seeded
 synthetic arrays stand in for them at the same shapes.
 
@@ -60,7 +60,7 @@ class LayerShape:
         return self.T * self.K
 
 
-# The five layers this build is checked and measured on.
+# The five layers the layer is checked and measured on.
 SHAPES = {
     "tiny": LayerShape("tiny", T=64, H=256, E=16, K=2, I=128),
     "stream_all_1k": LayerShape("stream_all_1k", T=1024, H=2560, E=512, K=10, I=1024),

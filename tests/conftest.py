@@ -16,8 +16,8 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are skipped (not failed) where no GPU is visible; on a GPU machine
-    # they run and a missing library is an error there, not a skip.
+    # GPU tests are skipped (not failed) where no GPU is visible; on a machine
+    # with a GPU they run and a missing library is an error there, not a skip.
     try:
         import torch
         have_gpu = torch.cuda.is_available()
