@@ -3,8 +3,9 @@
 
 A step is one strata_moe_prefill call -- router, top-K, grouping, int8
 quantization, gate/up + SwiGLU + int8 H, down + weighted scatter-add -- over a
-chunk of T tokens whose inputs and packed experts are already resident in
-HBM.  Default workload: T = 8192, H = 2560, E = 512 experts, top-10, expert FFN
+chunk of T tokens whose inputs, packed experts and prepared router matrix
+(strata_moe_prepare_router, once, like the packing; --router-per-call prepares
+it inside every step instead) are already resident in HBM.  Default workload: T = 8192, H = 2560, E = 512 experts, top-10, expert FFN
 I = 1024, seeded synthetic inputs (the pages' own prompts and trained pack are
 not available).
 
@@ -47,6 +48,8 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="chunk_8k")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--router-per-call", action="store_true",
+                    help="prepare the router matrix inside every layer call instead of once with the experts")
     ap.add_argument("--cpu-tokens", type=int, default=4096, help="tokens in the CPU-oracle sample (0 = skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB after flushing the Infinity Cache "
@@ -114,6 +117,8 @@ def main() -> int:
     x_np, wr_np = S.activations(s, args.seed), S.router_weight(s, args.seed)
     x = torch.from_numpy(x_np).to(dev)
     wr = torch.from_numpy(wr_np).to(dev)
+    if not args.router_per_call:  # a layer parameter, prepared once like the packed experts
+        experts = experts.with_prepared_router(wr)
     out = torch.empty_like(x)
     ws = torch.empty(qm.strata_moe_workspace_bytes(s.T, s.K, experts), dtype=torch.uint8, device=dev)
     qm.strata_moe_set_workspace(ws)
@@ -205,7 +210,8 @@ def main() -> int:
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": s.name, "T": s.T, "H": s.H, "E": s.E, "K": s.K, "I": s.I,
-                   "weights": "2-bit codes, fp16 scale per 32", "activations": "int8, fp32 scale per 32"},
+                   "weights": "2-bit codes, fp16 scale per 32", "activations": "int8, fp32 scale per 32",
+                   "router_matrix": "prepared per call" if args.router_per_call else "prepared once"},
         "kernel_ms": {k: round(v, 4) for k, v in kernel_ms.items()},
         "int8_ops_per_step": 2.0 * n * 3 * s.H * s.I,
         "roofline": roofline,

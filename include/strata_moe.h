@@ -65,7 +65,11 @@ extern "C" {
  *            over H), from which expert e's SwiGLU input is computed.
  *   down:    E blobs of down_stride bytes (H rows x I, reduction over I).
  *   router_bias: [E] fp32 added to the router logits before the top-K and
- *            the softmax, or NULL. */
+ *            the softmax, or NULL.
+ *   router_prepared: strata_moe_prepare_router()'s output for the router_w
+ *            that the layer calls pass, or NULL (then the layer prepares
+ *            router_w on every call).  Added after the fields above; code
+ *            that zero-initialises the struct keeps the per-call path. */
 typedef struct strata_moe_experts {
     int32_t n_expert; /* E */
     int32_t hidden;   /* H */
@@ -76,6 +80,7 @@ typedef struct strata_moe_experts {
     const void* down;
     int64_t down_stride;
     const float* router_bias;
+    const void* router_prepared;
 } strata_moe_experts;
 
 /* Optional intermediate outputs of strata_moe_prefill_debug (each may be
@@ -131,6 +136,20 @@ int strata_moe_pack(const uint8_t* codes_gu, const uint16_t* scales_gu, const ui
 int strata_moe_unpack(const void* gate_up, int64_t gate_up_stride, const void* down, int64_t down_stride, int32_t e0,
                       int32_t e1, int32_t hidden, int32_t ffn, uint8_t* codes_gu, uint16_t* scales_gu,
                       uint8_t* codes_d, uint16_t* scales_d, void* stream);
+
+/* Device bytes of a prepared router matrix of H x E.  Errors: EINVAL for H
+ * not a multiple of 128 in [128, 4096] or E outside [1, 1024]. */
+int strata_moe_router_prepared_bytes(int32_t hidden, int32_t n_expert, size_t* bytes);
+
+/* The router matrix's per-call forms, computed once (Winery-Strata
+ * prefill.cpp page, the router step: the logits are x . W_r; the layer builds
+ * from W_r a transposed fp32 copy for the fp64 re-score of near-ties and the
+ * hi/lo fp16 MFMA operand).  router_w [H][E] fp32 (device); prepared:
+ * caller-owned device memory of strata_moe_router_prepared_bytes() bytes,
+ * 256-byte aligned.  Point experts->router_prepared at it and pass the same
+ * router_w to the layer calls; prepare again whenever router_w changes (the
+ * layer does not check).  Asynchronous on `stream`. */
+int strata_moe_prepare_router(const float* router_w, int32_t hidden, int32_t n_expert, void* prepared, void* stream);
 
 /* ------------------------------------------------------------- the layer */
 

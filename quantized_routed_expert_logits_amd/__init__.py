@@ -45,7 +45,7 @@ _i64, _i32 = ctypes.c_int64, ctypes.c_int32
 class ExpertsStruct(ctypes.Structure):
     _fields_ = [("n_expert", _i32), ("hidden", _i32), ("ffn", _i32), ("format", _i32),
                 ("gate_up", _P), ("gate_up_stride", _i64), ("down", _P), ("down_stride", _i64),
-                ("router_bias", _P)]
+                ("router_bias", _P), ("router_prepared", _P)]
 
 
 class DebugStruct(ctypes.Structure):
@@ -64,6 +64,8 @@ _sig("strata_moe_last_error", [], ctypes.c_char_p)
 _sig("strata_moe_packed_bytes", [_i32, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)])
 _sig("strata_moe_workspace_bytes", [_i64, _i32, ctypes.POINTER(ExpertsStruct), ctypes.POINTER(ctypes.c_size_t)])
 _sig("strata_moe_set_workspace", [_P, ctypes.c_size_t])
+_sig("strata_moe_router_prepared_bytes", [_i32, _i32, ctypes.POINTER(ctypes.c_size_t)])
+_sig("strata_moe_prepare_router", [_P, _i32, _i32, _P, _P])
 _sig("strata_moe_pack", [_P, _P, _P, _P, _i32, _i32, _i32, _i32, _P, _i64, _P, _i64, _P])
 _sig("strata_moe_unpack", [_P, _i64, _P, _i64, _i32, _i32, _i32, _i32, _P, _P, _P, _P, _P])
 _sig("strata_moe_prefill", [_P, _P, ctypes.POINTER(ExpertsStruct), _i64, _i32, _P, _P])
@@ -81,7 +83,8 @@ _sig("strata_moe_timing_read", [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(
 
 EXPORTED = [
     "strata_moe_device_supported", "strata_moe_last_error", "strata_moe_packed_bytes",
-    "strata_moe_workspace_bytes", "strata_moe_set_workspace", "strata_moe_pack", "strata_moe_unpack",
+    "strata_moe_workspace_bytes", "strata_moe_set_workspace", "strata_moe_router_prepared_bytes",
+    "strata_moe_prepare_router", "strata_moe_pack", "strata_moe_unpack",
     "strata_moe_prefill", "strata_moe_prefill_debug", "strata_moe_route", "strata_moe_group",
     "strata_moe_quantize", "strata_moe_gate_up", "strata_moe_down", "strata_moe_timing",
     "strata_moe_timing_kinds", "strata_moe_timing_name", "strata_moe_timing_read",
@@ -132,6 +135,22 @@ def strata_moe_packed_bytes(hidden: int, ffn: int) -> tuple[int, int]:
     return gu.value, dn.value
 
 
+def strata_moe_router_prepared_bytes(hidden: int, n_expert: int) -> int:
+    b = ctypes.c_size_t()
+    _check(_lib.strata_moe_router_prepared_bytes(hidden, n_expert, ctypes.byref(b)), "strata_moe_router_prepared_bytes")
+    return b.value
+
+
+def strata_moe_prepare_router(router_w: torch.Tensor, stream=None) -> torch.Tensor:
+    """router_w [H][E] fp32 on the device -> its prepared form (a uint8 device tensor)."""
+    _dtype(router_w, torch.float32, "router_w")
+    H, E = router_w.shape
+    prepared = torch.empty(strata_moe_router_prepared_bytes(H, E), dtype=torch.uint8, device=router_w.device)
+    _check(_lib.strata_moe_prepare_router(_ptr(router_w), H, E, _ptr(prepared), _stream(stream)),
+           "strata_moe_prepare_router")
+    return prepared
+
+
 def strata_moe_set_workspace(buf: torch.Tensor | None) -> None:
     if buf is None:
         _check(_lib.strata_moe_set_workspace(None, 0), "strata_moe_set_workspace")
@@ -151,9 +170,14 @@ class Experts:
         self.down = torch.empty(n_expert * self.down_stride, dtype=torch.uint8, device=device)
         _dtype(router_bias, torch.float32, "router_bias")
         self.router_bias = router_bias
-        self.struct = ExpertsStruct(n_expert, hidden, ffn, Q2_SYM, self.gate_up.data_ptr(), self.gate_up_stride,
-                                    self.down.data_ptr(), self.down_stride,
-                                    None if router_bias is None else router_bias.data_ptr())
+        self.router_prepared = None
+        self._restruct()
+
+    def _restruct(self):
+        self.struct = ExpertsStruct(self.n_expert, self.hidden, self.ffn, Q2_SYM, self.gate_up.data_ptr(),
+                                    self.gate_up_stride, self.down.data_ptr(), self.down_stride,
+                                    None if self.router_bias is None else self.router_bias.data_ptr(),
+                                    None if self.router_prepared is None else self.router_prepared.data_ptr())
 
     def with_router_bias(self, router_bias: torch.Tensor | None) -> "Experts":
         """The same blobs with another router bias (or none)."""
@@ -162,9 +186,17 @@ class Experts:
         _dtype(router_bias, torch.float32, "router_bias")
         other = copy.copy(self)
         other.router_bias = router_bias
-        other.struct = ExpertsStruct(self.n_expert, self.hidden, self.ffn, Q2_SYM, self.gate_up.data_ptr(),
-                                     self.gate_up_stride, self.down.data_ptr(), self.down_stride,
-                                     None if router_bias is None else router_bias.data_ptr())
+        other._restruct()
+        return other
+
+    def with_prepared_router(self, router_w: torch.Tensor | None, stream=None) -> "Experts":
+        """The same blobs with router_w prepared once (strata_moe_prepare_router);
+        the layer calls must then pass the same router_w.  None: prepare per call."""
+        import copy
+
+        other = copy.copy(self)
+        other.router_prepared = None if router_w is None else strata_moe_prepare_router(router_w, stream)
+        other._restruct()
         return other
 
     def pack(self, e0: int, codes_gu, scales_gu, codes_d, scales_d, stream=None):

@@ -94,8 +94,34 @@ inline int64_t router_padded_experts(int32_t E) { return round_up(E, 16); }
 
 // logits [splits][T][E]; xm: the input rows' power-of-two multipliers (the
 // prescale's row multipliers of the same rows) or nullptr to compute them.
+// wr == nullptr: rs.wt / rs.wb / rs.wm already hold wr's prepared forms
+// (launch_router_prep); otherwise they are prepared here (rs.pmax: scratch of
+// H/32 x E floats).
 hipError_t launch_router(const float* x, const float* xm, const float* wr, const float* bias, int64_t T, int32_t H,
                          int32_t E, const RouterScratch& rs, float* logits, hipStream_t st);
+// The router matrix's per-call forms: the transposed fp32 copy rs.wt [E][H]
+// and the hi/lo fp16 operand rs.wb / rs.wm (rs.pmax: scratch).
+hipError_t launch_router_prep(const float* wr, int32_t H, int32_t E, const RouterScratch& rs, hipStream_t st);
+// Byte offsets of the prepared router matrix's parts in one buffer.
+struct RouterPrepared {
+    size_t wt, wb, wm, pmax, total;
+};
+inline RouterPrepared router_prepared_layout(int32_t H, int32_t E) {
+    RouterPrepared r;
+    const int64_t Ep = router_padded_experts(E);
+    auto take = [](size_t& off, size_t bytes) {
+        const size_t at = off;
+        off += (bytes + 255) / 256 * 256;
+        return at;
+    };
+    size_t off = 0;
+    r.wt = take(off, (size_t)E * H * sizeof(float));
+    r.wb = take(off, (size_t)Ep * H * 2 * sizeof(_Float16));
+    r.wm = take(off, (size_t)Ep * sizeof(float));
+    r.pmax = take(off, (size_t)((H + 31) / 32) * E * sizeof(float));
+    r.total = off;
+    return r;
+}
 // amb: scratch of T+1 ints (the list of tokens with a near-tie), amb[0] set to
 // 0 here unless the caller already did (amb_zeroed); wt from the router scratch.
 hipError_t launch_topk(const float* logits, const float* x, const float* wt, const float* bias, int64_t T, int32_t H,

@@ -721,14 +721,20 @@ __global__ void __launch_bounds__(256) topk_resolve_kernel(const float* __restri
 
 }  // namespace
 
-hipError_t launch_router(const float* x, const float* xm, const float* wr, const float* bias, int64_t T, int32_t H,
-                         int32_t E, const RouterScratch& rs, float* logits, hipStream_t st) {
-    if (T <= 0) return hipGetLastError();
+hipError_t launch_router_prep(const float* wr, int32_t H, int32_t E, const RouterScratch& rs, hipStream_t st) {
     hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)((E + 31) / 32), (unsigned)((H + 31) / 32)), dim3(256), 0, st,
                        wr, H, E, rs.wt, rs.pmax);
     const int32_t Ep = (int32_t)router_padded_experts(E);
     hipLaunchKernelGGL(router_prep_kernel, dim3((unsigned)((Ep + 3) / 4)), dim3(256), 0, st, rs.wt, rs.pmax, H, E, Ep,
                        rs.wb, rs.wm);
+    return hipGetLastError();
+}
+
+hipError_t launch_router(const float* x, const float* xm, const float* wr, const float* bias, int64_t T, int32_t H,
+                         int32_t E, const RouterScratch& rs, float* logits, hipStream_t st) {
+    if (T <= 0) return hipGetLastError();
+    if (wr) launch_router_prep(wr, H, E, rs, st);
+    const int32_t Ep = (int32_t)router_padded_experts(E);
     if (!xm) {
         hipLaunchKernelGGL(row_scale_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, x, T, H, rs.xm);
         xm = rs.xm;

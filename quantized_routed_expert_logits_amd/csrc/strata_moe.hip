@@ -293,6 +293,8 @@ int check_experts(const strata_moe_experts* ex) {
                     (long long)ex->gate_up_stride, (long long)ex->down_stride, (long long)gu, (long long)dn);
     if (ex->gate_up_stride % 256 || ex->down_stride % 256 || !aligned(ex->gate_up, 256) || !aligned(ex->down, 256))
         return fail(STRATA_MOE_EINVAL, "expert blobs and strides must be 256-byte aligned");
+    if (ex->router_prepared && !aligned(ex->router_prepared, 256))
+        return fail(STRATA_MOE_EINVAL, "router_prepared must be 256-byte aligned");
     return 0;
 }
 
@@ -338,12 +340,19 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
             "quantize launch");
     tm.end(kQuantize);
     tm.begin(kRouter);
-    HIP_TRY(launch_router(x, b.xe, wr, ex->router_bias, T, H, E, RouterScratch{b.wt, b.wb, b.wm, nullptr, b.pmax}, b.logits,
-                          st),
+    // the router matrix's MFMA operand and transposed copy: prepared once by the
+    // caller (experts->router_prepared) or here on every call
+    RouterScratch rs{b.wt, b.wb, b.wm, nullptr, b.pmax};
+    if (ex->router_prepared) {
+        const RouterPrepared rp = router_prepared_layout(H, E);
+        char* base = (char*)ex->router_prepared;
+        rs = RouterScratch{(float*)(base + rp.wt), (_Float16*)(base + rp.wb), (float*)(base + rp.wm), nullptr, nullptr};
+    }
+    HIP_TRY(launch_router(x, b.xe, ex->router_prepared ? nullptr : wr, ex->router_bias, T, H, E, rs, b.logits, st),
             "router launch");
     tm.end(kRouter);
     tm.begin(kTopK);
-    HIP_TRY(launch_topk(b.logits, x, b.wt, ex->router_bias, T, H, E, K, b.amb, b.ids, b.p, st, true),
+    HIP_TRY(launch_topk(b.logits, x, rs.wt, ex->router_bias, T, H, E, K, b.amb, b.ids, b.p, st, true),
             "top-K launch");
     tm.end(kTopK);
     tm.begin(kGroup);
@@ -391,6 +400,31 @@ int strata_moe_packed_bytes(int32_t hidden, int32_t ffn, int64_t* gate_up_bytes,
     TRY(check_dims(hidden, ffn));
     *gate_up_bytes = round_up(packed_matrix_bytes(2LL * ffn, hidden), 256);
     *down_bytes = round_up(packed_matrix_bytes(hidden, ffn), 256);
+    return 0;
+}
+
+int strata_moe_router_prepared_bytes(int32_t hidden, int32_t n_expert, size_t* bytes) {
+    g_err.clear();
+    if (!bytes) return fail(STRATA_MOE_EINVAL, "bytes is NULL");
+    if (hidden < 128 || hidden % 128 || hidden > 4096)
+        return fail(STRATA_MOE_EINVAL, "hidden %d is not a multiple of 128 in [128, 4096]", hidden);
+    if (n_expert < 1 || n_expert > kMaxExperts)
+        return fail(STRATA_MOE_EINVAL, "n_expert %d outside [1, %d]", n_expert, kMaxExperts);
+    *bytes = router_prepared_layout(hidden, n_expert).total;
+    return 0;
+}
+
+int strata_moe_prepare_router(const float* router_w, int32_t hidden, int32_t n_expert, void* prepared, void* stream) {
+    size_t bytes = 0;
+    TRY(strata_moe_router_prepared_bytes(hidden, n_expert, &bytes));
+    if (!router_w || !prepared) return fail(STRATA_MOE_EINVAL, "null pointer");
+    if (!aligned(prepared, 256)) return fail(STRATA_MOE_EINVAL, "prepared must be 256-byte aligned");
+    TRY(check_device());
+    const RouterPrepared rp = router_prepared_layout(hidden, n_expert);
+    char* base = (char*)prepared;
+    const RouterScratch rs{(float*)(base + rp.wt), (_Float16*)(base + rp.wb), (float*)(base + rp.wm), nullptr,
+                           (float*)(base + rp.pmax)};
+    HIP_TRY(launch_router_prep(router_w, hidden, n_expert, rs, (hipStream_t)stream), "router prep launch");
     return 0;
 }
 

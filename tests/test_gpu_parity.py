@@ -209,6 +209,22 @@ def test_layer_zero_input_and_repeat(qm):
     assert torch.equal(a, b)  # the combine adds each token's rows in a fixed order
 
 
+@pytest.mark.parametrize("s", [S.shape("tiny"), S.custom(T=300, H=256, E=12, K=3, I=128),
+                               S.custom(T=129, H=256, E=8, K=4, I=64, skewed=True)], ids=lambda s: s.name)
+def test_layer_prepared_router_is_identical(qm, s):
+    # the router matrix prepared once (strata_moe_prepare_router) gives the
+    # same bits as preparing it in every call; a later call with the other
+    # form in between checks that neither leaves state behind
+    ex = gpu_experts(s)
+    wr = _t(S.router_weight(s))
+    x = _t(S.activations(s))
+    exp = ex.with_prepared_router(wr)
+    a = qm.strata_moe_prefill(x, wr, ex, s.K, torch.empty_like(x)).clone()
+    b = qm.strata_moe_prefill(x, wr, exp, s.K, torch.empty_like(x)).clone()
+    c = qm.strata_moe_prefill(x, wr, ex, s.K, torch.empty_like(x))
+    assert torch.equal(a, b) and torch.equal(a, c)
+
+
 def test_layer_zero_tokens(qm):
     s = S.shape("tiny")
     ex = gpu_experts(s)
