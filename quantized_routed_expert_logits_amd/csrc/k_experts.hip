@@ -175,13 +175,17 @@ struct BlockLoop {
     _Float16* d_lds;
     half8_t (*a_lds)[kFrags][64];
     UnpackMagic mg;
+    int dw0;  // the first record dword this thread unpacks (a multiple of 64 plus its lane)
 
     // Buffer loads: per-lane offsets are loop-invariant, the block enters as a
-    // scalar offset.  A block beyond the last re-reads the last one.
-    __device__ __forceinline__ void load_record(int blk, uint32_t& xw, uint32_t& sw) const {
+    // scalar offset.  A block beyond the last re-reads the last one.  Dwords
+    // dw0 and dw0 + 64 share their scale dword (the lane's).
+    template <int KW>
+    __device__ __forceinline__ void load_record(int blk, uint32_t& xw, uint32_t& xw2, uint32_t& sw) const {
         blk = blk < nblk ? blk : nblk - 1;
-        xw = __builtin_amdgcn_raw_buffer_load_b32(rec, tau * 4, blk * kRecordBytes, 0);
-        sw = __builtin_amdgcn_raw_buffer_load_b32(rec, kRecordCodeBytes + (tau & 63) * 4, blk * kRecordBytes, 0);
+        xw = __builtin_amdgcn_raw_buffer_load_b32(rec, dw0 * 4, blk * kRecordBytes, 0);
+        if constexpr (KW == 2) xw2 = __builtin_amdgcn_raw_buffer_load_b32(rec, dw0 * 4 + 256, blk * kRecordBytes, 0);
+        sw = __builtin_amdgcn_raw_buffer_load_b32(rec, kRecordCodeBytes + lane * 4, blk * kRecordBytes, 0);
     }
 
     // Activation fragments of a block in the loader layout (see loader_row):
@@ -208,18 +212,19 @@ struct BlockLoop {
             sv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(scl, soff[i], blk * 4, 0));
     }
 
-    // Thread tau unpacks dword tau of the record: fragments 2p and 2p+1 of
-    // MFMA lane tau / 4 (p = tau % 4), stored at lane slot (tau / 4) ^ 2p so
-    // that the four pairs of one lane fall in different LDS banks.
-    __device__ __forceinline__ void unpack(int blk, uint32_t xw, uint32_t sw) const {
+    // Record dword dw holds fragments 2p and 2p+1 of MFMA lane dw / 4
+    // (p = dw % 4, the thread's lane % 4), stored at lane slot (dw / 4) ^ 2p
+    // so that the four pairs of one lane fall in different LDS banks.
+    __device__ __forceinline__ void unpack(int blk, int dw, uint32_t xw, uint32_t sw) const {
         half8_t a0, a1;
         const _Float16 d0 = lo_half(sw), d1 = hi_half(sw);
         unpack_dword(xw, d0, d1, mg, a0, a1);
-        const int ul = tau >> 2, ur16 = ul & 15;
+        const int ul = dw >> 2, ur16 = ul & 15;
         a_lds[blk & 1][2 * p][ul ^ (2 * p)] = a0;
         a_lds[blk & 1][2 * p + 1][ul ^ (2 * p)] = a1;
-        // the 4 waves hold the same scales of a row: all write, no branch, so
-        // the unpack can interleave with the MFMAs of the previous block
+        // every unpacking wave holds the same scales of a row: all write, no
+        // branch, so the unpack can interleave with the MFMAs of the previous
+        // block
         d_lds[(32 * p + ur16) * dstride + blk] = d0;
         d_lds[(32 * p + 16 + ur16) * dstride + blk] = d1;
     }
@@ -265,18 +270,20 @@ struct BlockLoop {
     // block), activation fragments (mostly from L2) one block ahead in two
     // register sets.  D divides nblk, so the unrolled body has no exit in the
     // middle and every ring index is a compile-time constant.
-    template <int NT, int D>
+    // KW: record dwords this thread unpacks per block (0, 1 or 2).
+    template <int NT, int D, int KW>
     __device__ __forceinline__ void run(const int (&lvoff)[kTilesPerWave], const int (&soff)[kTilesPerWave],
                                         float4_t (&acc)[kFrags][kTilesPerWave]) const {
         static_assert(D % 2 == 0, "activation sets alternate per block");
-        uint32_t xw[D], sw[D];
+        uint32_t xw[D], xw2[D], sw[D];
         half8_t bf[2][kTilesPerWave];
         float sv[2][kTilesPerWave] = {};
         // Issue order matters: each unpack waits for its record with a vmcnt
         // that counts the loads issued after it, and the loop header merges
         // the entry path with the back edge.  Records first, as in the loop.
 #pragma unroll
-        for (int j = 0; j < D; ++j) load_record(j, xw[j], sw[j]);
+        for (int j = 0; j < D; ++j)
+            if constexpr (KW > 0) load_record<KW>(j, xw[j], xw2[j], sw[j]);
         __builtin_amdgcn_sched_barrier(0);
         load_act<NT>(0, lvoff, bf[0]);
         if constexpr (kRescale) load_scales<NT>(0, soff, sv[0]);
@@ -285,9 +292,10 @@ struct BlockLoop {
 #pragma unroll
             for (int j = 0; j < D; ++j) {
                 const int blk = b + j;
-                unpack(blk, xw[j], sw[j]);
+                if constexpr (KW > 0) unpack(blk, dw0, xw[j], sw[j]);
+                if constexpr (KW == 2) unpack(blk, dw0 + 64, xw2[j], sw[j]);
                 __syncthreads();
-                load_record(blk + D, xw[j], sw[j]);
+                if constexpr (KW > 0) load_record<KW>(blk + D, xw[j], xw2[j], sw[j]);
                 load_act<NT>(blk + 1, lvoff, bf[(j + 1) & 1]);
                 if constexpr (kRescale) load_scales<NT>(blk + 1, soff, sv[(j + 1) & 1]);
                 __builtin_amdgcn_sched_barrier(0);  // loads go out before the MFMAs
@@ -374,6 +382,27 @@ __device__ __forceinline__ void down_store(const GemmArgs& g, const Tile& tl, in
     __builtin_amdgcn_wave_barrier();
 }
 
+// The block loop of one wave's shape (wave-uniform): ntw tiles, kw record
+// dwords unpacked per thread and block.
+template <int D, typename Loop>
+__device__ __forceinline__ void run_shape(const Loop& L, int ntw, int kw, const int (&lvoff)[kTilesPerWave],
+                                          const int (&soff)[kTilesPerWave], float4_t (&acc)[kFrags][kTilesPerWave]) {
+    switch (3 * ntw + kw) {
+        case 0: L.template run<0, D, 0>(lvoff, soff, acc); break;
+        case 1: L.template run<0, D, 1>(lvoff, soff, acc); break;  // no tiles: still unpack, meet every barrier
+        case 2: L.template run<0, D, 2>(lvoff, soff, acc); break;
+        case 3: L.template run<1, D, 0>(lvoff, soff, acc); break;
+        case 4: L.template run<1, D, 1>(lvoff, soff, acc); break;
+        case 5: L.template run<1, D, 2>(lvoff, soff, acc); break;
+        case 6: L.template run<2, D, 0>(lvoff, soff, acc); break;
+        case 7: L.template run<2, D, 1>(lvoff, soff, acc); break;
+        case 8: L.template run<2, D, 2>(lvoff, soff, acc); break;
+        case 9: L.template run<3, D, 0>(lvoff, soff, acc); break;
+        case 10: L.template run<3, D, 1>(lvoff, soff, acc); break;
+        default: L.template run<3, D, 2>(lvoff, soff, acc); break;
+    }
+}
+
 // kGateUp: activation rows are tokens (through src), epilogue SwiGLU + int8 H.
 // Otherwise: activation rows are the grouped rows, epilogue weighted row stores.
 // One work item of the 4-wave kernel: chunk tl against slab `slab`.
@@ -425,24 +454,21 @@ __device__ __forceinline__ void big_chunk_item(const GemmArgs& g, const Tile tl,
         __builtin_amdgcn_make_buffer_rsrc((void*)g.act, (short)0, (int)(g.act_rows * g.Kd * 2), kBufferWord3),
         __builtin_amdgcn_make_buffer_rsrc((void*)g.ascale, (short)0, kRescale ? (int)(g.act_rows * nblk * 4) : 0,
                                           kBufferWord3),
-        g.Kd, nblk, dstride, tau, lane, r16, kg, p, mfma_source_addr(lane), d_lds, a_lds, UnpackMagic()};
+        g.Kd, nblk, dstride, tau, lane, r16, kg, p, mfma_source_addr(lane), d_lds, a_lds, UnpackMagic(), 0};
+    // The record's 256 dwords are unpacked by the waves with fewer tiles where
+    // the chunk's tiles do not split evenly (nt = 4q + r; waves 0..r-1 hold
+    // q + 1 tiles): r = 1: dwords per lane (0, 2, 1, 1); r = 2: (0, 0, 2, 2);
+    // else one each.  The busiest waves then skip the unpack.
+    const int rem = ((tl.nrows + 15) / 16) & 3;
+    const int kw = rem == 1 ? (wave == 0 ? 0 : wave == 1 ? 2 : 1) : rem == 2 ? (wave < 2 ? 0 : 2) : 1;
+    const int kw_before = rem == 1 ? (wave == 0 ? 0 : wave == 1 ? 0 : wave) : rem == 2 ? (wave < 3 ? 0 : 2) : wave;
+    L.dw0 = 64 * kw_before + lane;
     // wave-uniform: the block loop is straight-line code for 1..3 tiles; the
     // record ring is 8 deep when 8 divides the block count (H = 2560, I = 1024)
-    if (nblk % 8 == 0) {
-        switch (ntw) {
-            case 1: L.template run<1, 8>(lvoff, soff, acc); break;
-            case 2: L.template run<2, 8>(lvoff, soff, acc); break;
-            case 3: L.template run<3, 8>(lvoff, soff, acc); break;
-            default: L.template run<0, 8>(lvoff, soff, acc); break;  // no tiles: still unpack and meet every barrier
-        }
-    } else {
-        switch (ntw) {
-            case 1: L.template run<1, 2>(lvoff, soff, acc); break;
-            case 2: L.template run<2, 2>(lvoff, soff, acc); break;
-            case 3: L.template run<3, 2>(lvoff, soff, acc); break;
-            default: L.template run<0, 2>(lvoff, soff, acc); break;
-        }
-    }
+    if (nblk % 8 == 0)
+        run_shape<8>(L, ntw, kw, lvoff, soff, acc);
+    else
+        run_shape<2>(L, ntw, kw, lvoff, soff, acc);
     __syncthreads();  // every d of the slab is in LDS
 
     // undo the rows' power-of-two prescaling (the rescaled form has none)
