@@ -421,8 +421,8 @@ __device__ __forceinline__ void sort8(float (&v)[8], int (&e)[8]) {
 // l: the token's row of the first partial logits slice; nsplit slices
 // `sstride` floats apart are added in order.  kSlots = 8 needs E <= 512.
 template <int kSlots>
-__device__ __forceinline__ void select_token(const float* __restrict__ l, int nsplit, int64_t sstride, int32_t E,
-                                             int32_t K, int lane, Selection<kSlots>& S) {
+__device__ __forceinline__ void load_logits(const float* __restrict__ l, int nsplit, int64_t sstride, int32_t E,
+                                            int lane, Selection<kSlots>& S) {
     // all loads first (the slices are independent), then the sums in slice order
     float part[kMaxRouterSplits][kSlots];
 #pragma unroll
@@ -441,6 +441,12 @@ __device__ __forceinline__ void select_token(const float* __restrict__ l, int ns
             if (z < nsplit) v += part[z][i];
         S.v[i] = lane + 64 * i < E ? v : -FLT_MAX;
     }
+}
+
+template <int kSlots>
+__device__ __forceinline__ void select_token(const float* __restrict__ l, int nsplit, int64_t sstride, int32_t E,
+                                             int32_t K, int lane, Selection<kSlots>& S) {
+    load_logits(l, nsplit, sstride, E, lane, S);
     S.rounds = K < E ? K + 1 : K;
 #pragma unroll
     for (int k = 0; k <= kMaxTopK; ++k) S.selv[k] = -FLT_MAX, S.seli[k] = INT_MAX;
@@ -535,18 +541,28 @@ __device__ __forceinline__ void write_token(const V (&lv)[kMaxTopK], const int (
 }
 
 // One wave per token: tokens without a near-tie are finished here; the others
-// are appended to `amb` (amb[0] = count, then token ids) for the resolve pass.
+// are appended to `amb` (amb[0] = count, then token ids) for the resolve pass,
+// with their fp32 ranking in `sel` (kSelWords per token: the ranked expert
+// ids, the loose-rank mask, the K-th value), which that pass then reuses.
 constexpr int kWaves = 4;
 template <int kSlots>
 __global__ void __launch_bounds__(256) topk_select_kernel(const float* __restrict__ logits, int nsplit, int64_t T,
                                                           int32_t E, int32_t K, int32_t* __restrict__ amb,
-                                                          int32_t* __restrict__ ids, float* __restrict__ p_out) {
+                                                          int32_t* __restrict__ sel, int32_t* __restrict__ ids,
+                                                          float* __restrict__ p_out) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * kWaves + wave;
     if (t >= T) return;  // whole wave; this kernel has no block-level barrier
     Selection<kSlots> S;
     select_token(logits + t * E, nsplit, T * E, E, K, lane, S);
     if (S.loose) {
+        int word = 0;
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k)
+            if (lane == k) word = S.seli[k];
+        if (lane == kMaxTopK) word = (int)S.loose;
+        if (lane == kMaxTopK + 1) word = __builtin_bit_cast(int, S.vK);
+        if (lane < kSelWords) sel[t * kSelWords + lane] = word;
         if (lane == 0) {
             const int slot = atomicAdd(amb, 1);
             amb[1 + slot] = (int32_t)t;
@@ -640,13 +656,20 @@ __global__ void __launch_bounds__(256) topk_resolve_kernel(const float* __restri
                                                            const float* __restrict__ wt,
                                                            const float* __restrict__ bias, int32_t H, int32_t E,
                                                            int32_t K, const int32_t* __restrict__ amb,
+                                                           const int32_t* __restrict__ sel,
                                                            int32_t* __restrict__ ids, float* __restrict__ p_out) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = amb[0];
     for (int it = blockIdx.x * kWaves + wave; it < n; it += gridDim.x * kWaves) {  // uniform over the wave
         const int64_t t = amb[1 + it];
-        Selection<kSlots> S;
-        select_token(logits + t * E, nsplit, T * E, E, K, lane, S);
+        Selection<kSlots> S;  // the select pass's ranking of this token, and its logits
+        load_logits(logits + t * E, nsplit, T * E, E, lane, S);
+        const int32_t* sm = sel + t * kSelWords;
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k) S.seli[k] = sm[k];
+        S.loose = (uint32_t)sm[kMaxTopK];
+        S.vK = __builtin_bit_cast(float, sm[kMaxTopK + 1]);
+        S.delta = kTieRel * fmaxf(1.0f, fabsf(S.vK));
         const float thr = S.vK - S.delta;
         double cv[kSlots];
         uint32_t cand = 0, todo = 0;
@@ -747,24 +770,25 @@ hipError_t launch_router(const float* x, const float* xm, const float* wr, const
 }
 
 hipError_t launch_topk(const float* logits, const float* x, const float* wt, const float* bias, int64_t T, int32_t H,
-                       int32_t E, int32_t K, int32_t* amb, int32_t* ids, float* p, hipStream_t st,
+                       int32_t E, int32_t K, int32_t* amb, int32_t* sel, int32_t* ids, float* p, hipStream_t st,
                        bool amb_zeroed) {
     if (T > 0) {
         if (!amb_zeroed) hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, amb, 1, 0);
         const int ns = router_splits(T, H, E);
         const dim3 sg((unsigned)((T + kWaves - 1) / kWaves));
         if (E <= 512)
-            hipLaunchKernelGGL(topk_select_kernel<8>, sg, dim3(64 * kWaves), 0, st, logits, ns, T, E, K, amb, ids, p);
+            hipLaunchKernelGGL(topk_select_kernel<8>, sg, dim3(64 * kWaves), 0, st, logits, ns, T, E, K, amb, sel,
+                               ids, p);
         else
             hipLaunchKernelGGL(topk_select_kernel<kPerLane>, sg, dim3(64 * kWaves), 0, st, logits, ns, T, E, K, amb,
-                               ids, p);
+                               sel, ids, p);
         const unsigned grid = (unsigned)((T < 8192 ? T : 8192) + kWaves - 1) / kWaves;
         if (E <= 512)
             hipLaunchKernelGGL(topk_resolve_kernel<8>, dim3(grid), dim3(256), 0, st, logits, ns, T, x, wt, bias, H, E,
-                               K, amb, ids, p);
+                               K, amb, sel, ids, p);
         else
             hipLaunchKernelGGL(topk_resolve_kernel<kPerLane>, dim3(grid), dim3(256), 0, st, logits, ns, T, x, wt, bias,
-                               H, E, K, amb, ids, p);
+                               H, E, K, amb, sel, ids, p);
     }
     return hipGetLastError();
 }

@@ -120,6 +120,7 @@ struct Buffers {
     float* wm;
     float* pmax;
     int32_t* amb;
+    int32_t* sel;
     int32_t* ids;
     float* p;
     int8_t* xq;
@@ -148,7 +149,7 @@ struct Buffers {
 };
 
 struct Offsets {
-    size_t logits, wt, wb, wm, pmax, amb, ids, p, xq, xs, xa, xe, xuop, xum, hist, base, offsets, tiles, ntiles, err, src, slot, prow, hq, hs,
+    size_t logits, wt, wb, wm, pmax, amb, sel, ids, p, xq, xs, xa, xe, xuop, xum, hist, base, offsets, tiles, ntiles, err, src, slot, prow, hq, hs,
         hb, he, huop, hum, dm, total;
     int64_t tiles_cap;
 };
@@ -165,6 +166,7 @@ Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I) {
     o.wm = L.take<float>(router_padded_experts(E));
     o.pmax = L.take<float>((int64_t)((H + 31) / 32) * E);
     o.amb = L.take<int32_t>(T + 1);
+    o.sel = L.take<int32_t>(T * kSelWords);
     o.ids = L.take<int32_t>(n);
     o.p = L.take<float>(n);
     o.xq = L.take<int8_t>(T * H);
@@ -201,6 +203,7 @@ Buffers carve(char* ws, const Offsets& o) {
     b.wm = (float*)(ws + o.wm);
     b.pmax = (float*)(ws + o.pmax);
     b.amb = (int32_t*)(ws + o.amb);
+    b.sel = (int32_t*)(ws + o.sel);
     b.ids = (int32_t*)(ws + o.ids);
     b.p = (float*)(ws + o.p);
     b.xq = (int8_t*)(ws + o.xq);
@@ -352,7 +355,7 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
             "router launch");
     tm.end(kRouter);
     tm.begin(kTopK);
-    HIP_TRY(launch_topk(b.logits, x, rs.wt, ex->router_bias, T, H, E, K, b.amb, b.ids, b.p, st, true),
+    HIP_TRY(launch_topk(b.logits, x, rs.wt, ex->router_bias, T, H, E, K, b.amb, b.sel, b.ids, b.p, st, true),
             "top-K launch");
     tm.end(kTopK);
     tm.begin(kGroup);
@@ -555,7 +558,7 @@ int strata_moe_route(const float* x, const float* router_w, const float* bias, i
     hipStream_t st = (hipStream_t)stream;
     Layout L;
     const size_t lo = L.take<float>(router_logit_floats(T, H, E)), o_wt = L.take<float>((int64_t)E * H);
-    const size_t o_amb = L.take<int32_t>(T + 1);
+    const size_t o_amb = L.take<int32_t>(T + 1), o_sel = L.take<int32_t>(T * kSelWords);
     const size_t o_wb = L.take<_Float16>(router_padded_experts(E) * H * 2);
     const size_t o_wm = L.take<float>(router_padded_experts(E)), o_xm = L.take<float>(T);
     const size_t o_pm = L.take<float>((int64_t)((H + 31) / 32) * E);
@@ -565,7 +568,8 @@ int strata_moe_route(const float* x, const float* router_w, const float* bias, i
     float* wt = (float*)(ws + o_wt);
     const RouterScratch rs{wt, (_Float16*)(ws + o_wb), (float*)(ws + o_wm), (float*)(ws + o_xm), (float*)(ws + o_pm)};
     HIP_TRY(launch_router(x, nullptr, router_w, bias, T, H, E, rs, logits, st), "router launch");
-    HIP_TRY(launch_topk(logits, x, wt, bias, T, H, E, K, (int32_t*)(ws + o_amb), ids, p, st), "top-K launch");
+    HIP_TRY(launch_topk(logits, x, wt, bias, T, H, E, K, (int32_t*)(ws + o_amb), (int32_t*)(ws + o_sel), ids, p, st),
+            "top-K launch");
     return 0;
 }
 
