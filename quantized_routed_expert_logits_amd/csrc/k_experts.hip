@@ -832,51 +832,30 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_small_kernel(GemmArgs g) {
 }
 
 // The combine: y[t] = sum_k dm[slot[t*K + k]] (rows already weighted), k in
-// order, so the result does not depend on scheduling.  One workgroup of
-// kCombineThreads per token row; thread j takes float4 groups j, j + 128,
-// ... of the row (up to kCombineGroups of them), two rows' loads in flight.
-constexpr int kCombineThreads = 128, kCombineGroups = 8;  // H <= 4096
+// order, so the result does not depend on scheduling.  A workgroup covers
+// kCombineThreads float4 columns of one token row (blockIdx.y picks the
+// column range): each thread issues the loads of all K rows at once (the
+// row slots are wave-uniform scalar loads), then adds them in k order.  The
+// rows are read once, so the loads and the store bypass cache retention.
+constexpr int kCombineThreads = 256;
 __global__ void __launch_bounds__(kCombineThreads) combine_kernel(const float* __restrict__ dm,
                                                                   const int32_t* __restrict__ slot, int64_t T,
                                                                   int32_t K, int32_t H, float* __restrict__ y) {
     const int64_t t = blockIdx.x;
-    const int j = threadIdx.x, n4 = H / 4;
-    float4 acc[kCombineGroups];
+    const int c = blockIdx.y * kCombineThreads + threadIdx.x, n4 = H / 4;
+    if (c >= n4) return;
+    const int32_t* sl = slot + t * K;
+    float4_t v[kMaxTopK];
 #pragma unroll
-    for (int g = 0; g < kCombineGroups; ++g) acc[g] = make_float4(0.f, 0.f, 0.f, 0.f);
-    int k = 0;
-    for (; k + 2 <= K; k += 2) {
-        const float4* r0 = reinterpret_cast<const float4*>(dm + (int64_t)slot[t * K + k] * H);
-        const float4* r1 = reinterpret_cast<const float4*>(dm + (int64_t)slot[t * K + k + 1] * H);
-        float4 v0[kCombineGroups], v1[kCombineGroups];
+    for (int k = 0; k < kMaxTopK; ++k)
+        if (k < K) v[k] = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(dm + (int64_t)sl[k] * H) + c);
+    float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int g = 0; g < kCombineGroups; ++g) {
-            const int c = j + kCombineThreads * g;
-            if (c < n4) v0[g] = r0[c], v1[g] = r1[c];
-        }
+    for (int k = 0; k < kMaxTopK; ++k)
+        if (k < K)
 #pragma unroll
-        for (int g = 0; g < kCombineGroups; ++g) {
-            acc[g].x += v0[g].x, acc[g].y += v0[g].y, acc[g].z += v0[g].z, acc[g].w += v0[g].w;
-            acc[g].x += v1[g].x, acc[g].y += v1[g].y, acc[g].z += v1[g].z, acc[g].w += v1[g].w;
-        }
-    }
-    if (k < K) {
-        const float4* r0 = reinterpret_cast<const float4*>(dm + (int64_t)slot[t * K + k] * H);
-#pragma unroll
-        for (int g = 0; g < kCombineGroups; ++g) {
-            const int c = j + kCombineThreads * g;
-            if (c < n4) {
-                const float4 v = r0[c];
-                acc[g].x += v.x, acc[g].y += v.y, acc[g].z += v.z, acc[g].w += v.w;
-            }
-        }
-    }
-    float4* yr = reinterpret_cast<float4*>(y + t * H);
-#pragma unroll
-    for (int g = 0; g < kCombineGroups; ++g) {
-        const int c = j + kCombineThreads * g;
-        if (c < n4) yr[c] = acc[g];
-    }
+            for (int e = 0; e < 4; ++e) acc[e] += v[k][e];
+    __builtin_nontemporal_store(acc, reinterpret_cast<float4_t*>(y + t * H) + c);
 }
 
 // Dynamic LDS: the offset-pass matrix d [128][dstride] fp16, then (down only)
@@ -951,7 +930,8 @@ hipError_t launch_down(const uint8_t* blobs, int64_t stride, const ChunkLists& c
 hipError_t launch_combine(const float* dm, const int32_t* slot, int64_t T, int32_t K, int32_t H, float* y,
                           hipStream_t st) {
     if (T > 0)
-        hipLaunchKernelGGL(combine_kernel, dim3((unsigned)T), dim3(kCombineThreads), 0, st, dm, slot, T, K, H, y);
+        hipLaunchKernelGGL(combine_kernel, dim3((unsigned)T, (unsigned)((H / 4 + kCombineThreads - 1) / kCombineThreads)),
+                           dim3(kCombineThreads), 0, st, dm, slot, T, K, H, y);
     return hipGetLastError();
 }
 
