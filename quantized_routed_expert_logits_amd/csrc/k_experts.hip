@@ -212,6 +212,19 @@ struct BlockLoop {
             sv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(scl, soff[i], blk * 4, 0));
     }
 
+    // The same for blocks blk .. blk + 3 (blk a multiple of 4, 4 | nblk): one
+    // 16-byte load per tile.  The 16 columns of a tile are 16 different rows,
+    // so a per-block load touches 16 cache lines for 64 useful bytes; four
+    // blocks per load cut those accesses fourfold.
+    template <int NT>
+    __device__ __forceinline__ void load_scales4(int blk, const int (&soff)[kTilesPerWave],
+                                                 float4_t (&sq)[kTilesPerWave]) const {
+        blk = blk < nblk ? blk : nblk - 4;
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+            sq[i] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(scl, soff[i], blk * 4, 0));
+    }
+
     // Record dword dw holds fragments 2p and 2p+1 of MFMA lane dw / 4
     // (p = dw % 4, the thread's lane % 4), stored at lane slot (dw / 4) ^ 2p
     // so that the four pairs of one lane fall in different LDS banks.
@@ -275,9 +288,13 @@ struct BlockLoop {
     __device__ __forceinline__ void run(const int (&lvoff)[kTilesPerWave], const int (&soff)[kTilesPerWave],
                                         float4_t (&acc)[kFrags][kTilesPerWave]) const {
         static_assert(D % 2 == 0, "activation sets alternate per block");
+        // kRescale with 8 | D: block scales in 4-block batches (two sets,
+        // batch (blk / 4) & 1 = j / 4), the next batch loaded one block ahead
+        constexpr bool kBatch = kRescale && D % 8 == 0;
         uint32_t xw[D], xw2[D], sw[D];
         half8_t bf[2][kTilesPerWave];
         float sv[2][kTilesPerWave] = {};
+        float4_t sq[2][kTilesPerWave] = {};
         // Issue order matters: each unpack waits for its record with a vmcnt
         // that counts the loads issued after it, and the loop header merges
         // the entry path with the back edge.  Records first, as in the loop.
@@ -286,7 +303,10 @@ struct BlockLoop {
             if constexpr (KW > 0) load_record<KW>(j, xw[j], xw2[j], sw[j]);
         __builtin_amdgcn_sched_barrier(0);
         load_act<NT>(0, lvoff, bf[0]);
-        if constexpr (kRescale) load_scales<NT>(0, soff, sv[0]);
+        if constexpr (kBatch)
+            load_scales4<NT>(0, soff, sq[0]);
+        else if constexpr (kRescale)
+            load_scales<NT>(0, soff, sv[0]);
         __builtin_amdgcn_sched_barrier(0);
         for (int b = 0; b < nblk; b += D) {
 #pragma unroll
@@ -297,9 +317,20 @@ struct BlockLoop {
                 __syncthreads();
                 if constexpr (KW > 0) load_record<KW>(blk + D, xw[j], xw2[j], sw[j]);
                 load_act<NT>(blk + 1, lvoff, bf[(j + 1) & 1]);
-                if constexpr (kRescale) load_scales<NT>(blk + 1, soff, sv[(j + 1) & 1]);
+                if constexpr (kBatch) {
+                    if ((j & 3) == 3) load_scales4<NT>(blk + 1, soff, sq[((j >> 2) + 1) & 1]);
+                } else if constexpr (kRescale) {
+                    load_scales<NT>(blk + 1, soff, sv[(j + 1) & 1]);
+                }
                 __builtin_amdgcn_sched_barrier(0);  // loads go out before the MFMAs
-                products<NT>(blk, bf[j & 1], sv[j & 1], acc);
+                if constexpr (kBatch) {
+                    float s[kTilesPerWave];
+#pragma unroll
+                    for (int i = 0; i < kTilesPerWave; ++i) s[i] = sq[(j >> 2) & 1][i][j & 3];
+                    products<NT>(blk, bf[j & 1], s, acc);
+                } else {
+                    products<NT>(blk, bf[j & 1], sv[j & 1], acc);
+                }
             }
         }
     }
@@ -597,16 +628,25 @@ struct SlabPass {
     // column's row and group); with kRescale also the block scale of the
     // lane's column in each tile (soff: byte offset of that row's scales).
     __device__ __forceinline__ void load_act(int blk, const int (&lvoff)[NT], const int (&soff)[NT],
-                                             half8_t (&bf)[NT], float (&sv)[NT]) const {
+                                             half8_t (&bf)[NT], float (&sv)[NT], bool scales) const {
         blk = blk < nblk ? blk : nblk - 1;
 #pragma unroll
         for (int i = 0; i < NT; ++i)
             bf[i] = __builtin_bit_cast(half8_t,
                                        __builtin_amdgcn_raw_buffer_load_b128(act, lvoff[i], blk * kBlock * 2, 0));
-        if constexpr (kRescale)
+        if (kRescale && scales)
 #pragma unroll
             for (int i = 0; i < NT; ++i)
                 sv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(scl, soff[i], blk * 4, 0));
+    }
+
+    // kRescale: the scales of blocks blk .. blk + 3 (blk a multiple of 4,
+    // 4 | nblk), one 16-byte load per tile instead of four gathered ones.
+    __device__ __forceinline__ void load_scales4(int blk, const int (&soff)[NT], float4_t (&sq)[NT]) const {
+        blk = blk < nblk ? blk : nblk - 4;
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+            sq[i] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(scl, soff[i], blk * 4, 0));
     }
 
     // Unpack dword p (fragments 2p, 2p+1).
@@ -721,29 +761,45 @@ struct SlabPass {
     }
 
     // Records run D blocks ahead in a register ring (8 dwords per block),
-    // activation fragments one block ahead in two alternating sets.
-    template <int D>
+    // activation fragments one block ahead in two alternating sets.  The
+    // body is unrolled U blocks (D | U, U | each 32-block chunk's length);
+    // with kRescale and U = 8 the block scales come in 4-block batches (two
+    // sets, batch (blk / 4) & 1 = j / 4), the next batch one block ahead.
+    template <int D, int U>
     __device__ __forceinline__ void run(int nch, const _Float16* uop, const int64_t (&arow)[NT],
                                         const int (&lvoff)[NT], const int (&soff)[NT], const float (&ratio)[NT],
                                         float4_t (&acc)[kFrags][NT]) const {
+        static_assert(U % D == 0 && U % 2 == 0, "ring slots and activation sets are compile-time per body");
+        constexpr bool kBatch = kRescale && U % 8 == 0;
         uint32_t xw[D][4], sw[D][4];
         half8_t bf[2][NT];
         float sv[2][NT] = {};
+        float4_t sq[2][NT] = {};
 #pragma unroll
         for (int j = 0; j < D; ++j) load_record(j, xw[j], sw[j]);
         __builtin_amdgcn_sched_barrier(0);
-        load_act(0, lvoff, soff, bf[0], sv[0]);
+        load_act(0, lvoff, soff, bf[0], sv[0], !kBatch);
+        if constexpr (kBatch) load_scales4(0, soff, sq[0]);
         __builtin_amdgcn_sched_barrier(0);
         for (int c = 0; c < nch; ++c) {
             const int bend = nblk < 32 * c + 32 ? nblk : 32 * c + 32;
-            for (int b = 32 * c; b < bend; b += D) {
+            for (int b = 32 * c; b < bend; b += U) {
 #pragma unroll
-                for (int j = 0; j < D; ++j) {
+                for (int j = 0; j < U; ++j) {
                     const int blk = b + j;
-                    load_act(blk + 1, lvoff, soff, bf[(j + 1) & 1], sv[(j + 1) & 1]);
+                    load_act(blk + 1, lvoff, soff, bf[(j + 1) & 1], sv[(j + 1) & 1], !kBatch);
+                    if constexpr (kBatch)
+                        if ((j & 3) == 3) load_scales4(blk + 1, soff, sq[((j >> 2) + 1) & 1]);
                     __builtin_amdgcn_sched_barrier(0);
-                    block(blk, xw[j], sw[j], bf[j & 1], sv[j & 1], acc);
-                    load_record(blk + D, xw[j], sw[j]);
+                    if constexpr (kBatch) {
+                        float s[NT];
+#pragma unroll
+                        for (int i = 0; i < NT; ++i) s[i] = sq[(j >> 2) & 1][i][j & 3];
+                        block(blk, xw[j % D], sw[j % D], bf[j & 1], s, acc);
+                    } else {
+                        block(blk, xw[j % D], sw[j % D], bf[j & 1], sv[j & 1], acc);
+                    }
+                    load_record(blk + D, xw[j % D], sw[j % D]);
                 }
             }
             offset(c, nch, uop, arow, ratio, acc);
@@ -788,7 +844,10 @@ __device__ __forceinline__ void small_chunk_pass(const GemmArgs& g, const Tile& 
            __builtin_amdgcn_make_buffer_rsrc((void*)g.ascale, (short)0, kRescale ? (int)(g.act_rows * nblk * 4) : 0,
                                              kBufferWord3),
            g.Kd, nblk, lane, r16, kg, dl, UnpackMagic()};
-    L.template run<2>(nch, g.uop, arow, lvoff, soff, ratio, acc);
+    if (kRescale && nblk % 8 == 0)  // 8 | every chunk's block count: 4-block scale batches
+        L.template run<2, 8>(nch, g.uop, arow, lvoff, soff, ratio, acc);
+    else
+        L.template run<2, 2>(nch, g.uop, arow, lvoff, soff, ratio, acc);
 
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
