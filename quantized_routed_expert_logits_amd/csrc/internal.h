@@ -19,8 +19,10 @@ constexpr int kRecordBytes = kRecordCodeBytes + 256;      // ... plus its 128 fp
 constexpr int kMaxOffsetChunks = 4;                       // reduction length <= 4 * 32 blocks = 4096
 
 // One chunk of grouped rows: rows [row0, row0 + nrows) all belong to expert e.
+// tile0: the chunk's first 16-row tile in the tiled row space (each expert's
+// rows start on a whole tile there), where the down GEMM's activations live.
 struct Tile {
-    int32_t e, row0, nrows, pad;
+    int32_t e, row0, nrows, tile0;
 };
 
 // Packed blob bytes of an M x Kd matrix (2 bits per weight + one fp16 per 32).
@@ -34,14 +36,23 @@ constexpr int kSmallRows = 48;  // chunks of at most this many rows go to the sm
 
 // The GEMMs' work lists, written on the GPU by the grouping (or from given
 // offsets): tiles[0, cap) the chunks of more than kSmallRows rows, tiles[cap,
-// 2 cap) the others; sched[0], sched[1] their counts.
-constexpr int kSchedInts = 2;
+// 2 cap) the others; sched[0], sched[1] their counts; sched[2] the number of
+// 16-row tiles of the tiled row space, trows[t] tile t's grouped rows.
+constexpr int kSchedInts = 3;
+struct TileRows {
+    int32_t row0, nrows;  // grouped rows [row0, row0 + nrows), nrows <= 16
+};
 struct ChunkLists {
-    Tile* tiles;     // [2 * cap]
-    int32_t* sched;  // [kSchedInts]
+    Tile* tiles;      // [2 * cap]
+    int32_t* sched;   // [kSchedInts]
     int64_t cap;
+    TileRows* trows;  // [tiled_rows_cap / 16]
 };
 inline int64_t chunk_list_cap(int64_t n, int32_t E) { return max_tiles(n, E); }
+
+// Rows of the tiled row space: every expert's rows rounded up to whole 16-row
+// tiles, so at most n + 15 E (a multiple of 16 after rounding up).
+inline int64_t tiled_rows_cap(int64_t n, int32_t E) { return (n + 15 * (int64_t)E + 15) / 16 * 16; }
 
 // fp16 values per row of the offset-pass operand of a reduction length Kd:
 // 32-block chunks, hi and lo per block.
@@ -60,6 +71,15 @@ hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q
 // [rows][offset_operand_halves]) and its row multipliers.
 hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_t cols, int parts, _Float16* out,
                            float* mult, _Float16* uop, float* umult, hipStream_t st);
+// The parts-1 operand of the grouped rows in the tiled layout: tile t of the
+// chunk lists' tile table holds grouped rows trows[t], stored as
+// [tile][block][group g of 8 values][row within the tile][8] (one MFMA
+// fragment of a tile and block is 1 KiB in MFMA lane order; rows past a
+// tile's nrows are zero).  mult, uop, umult as launch_prescale, per grouped
+// row.  tiles_cap bounds the tile count (the grid).
+hipError_t launch_prescale_tiled(const int8_t* q, const float* s, const ChunkLists& cl, int64_t tiles_cap,
+                                 int32_t cols, _Float16* out, float* mult, _Float16* uop, float* umult,
+                                 hipStream_t st);
 // The layer input in one pass: launch_quantize's outputs (q8, s) and
 // launch_prescale's with parts 0 (codes16, mult, uop, umult), bit-identical to
 // the two launches; also clears the ZeroWords.
@@ -133,7 +153,8 @@ hipError_t launch_topk(const float* logits, const float* x, const float* wt, con
 hipError_t launch_group(const int32_t* ids, const float* p, int64_t n, int32_t K, int32_t E, int32_t* hist,
                         int32_t* base, int32_t* offsets, const ChunkLists& cl, int32_t* src, int32_t* slot,
                         float* prow, int32_t* err, hipStream_t st);
-hipError_t launch_chunks_from_offsets(const int32_t* offsets, int32_t E, const ChunkLists& cl, hipStream_t st);
+hipError_t launch_chunks_from_offsets(const int32_t* offsets, int32_t E, int64_t n, const ChunkLists& cl,
+                                      hipStream_t st);
 hipError_t launch_row_weights(const int32_t* slot, const float* p, int64_t n, float* prow, hipStream_t st);
 
 // gate/up: xa = the input codes as fp16 (prescale parts 0) and xs = their

@@ -113,6 +113,12 @@ __device__ __forceinline__ float round_half_away(float t) {
     return copysignf(fminf(r, 127.0f), t);
 }
 
+// Bytes between consecutive blocks of one activation fragment: 64 in the
+// row-major gate/up input [rows][Kd], 1 KiB in the tiled down operand
+// [tile][block][group][16 rows][8] (a tile's fragment of a block is 1 KiB in
+// MFMA lane order: lane 16 g + r reads row r, group g, 16 contiguous bytes).
+constexpr int kRowBlockBytes = kBlock * 2, kTiledBlockBytes = 16 * kBlock * 2;
+
 // Activation (B operand) fragments are read coalesced, then moved into the
 // MFMA layout.  In the MFMA layout lane d holds column (routed row) d % 16 and
 // value group d / 16 of a block, so consecutive lanes would read 16 different
@@ -146,8 +152,8 @@ struct GemmArgs {
     int32_t Kd;            // reduction length (H for gate/up, I for down)
     const int32_t* src;    // token of each grouped row
     const float* prow;     // routing weight of each grouped row (down)
-    const _Float16* act;   // activations [rows][Kd] fp16: gate/up the codes, down prescaled
-    int64_t act_rows;      // rows of act / ascale / am / uop / um
+    const _Float16* act;   // activations fp16: gate/up the codes [rows][Kd], down prescaled, tiled
+    int64_t act_rows;      // rows of act (down: tiled rows) and ascale
     const float* ascale;   // gate/up: block scales of act [rows][Kd / 32]
     const float* am;       // down: row multipliers 2^e of act [rows]
     const _Float16* uop;   // offset-pass operand [rows][nch x 32 blocks x 2] (hi, lo)
@@ -195,10 +201,10 @@ struct BlockLoop {
     __device__ __forceinline__ void load_act(int blk, const int (&lvoff)[kTilesPerWave],
                                              half8_t (&bf)[kTilesPerWave]) const {
         blk = blk < nblk ? blk : nblk - 1;
+        constexpr int kStride = kRescale ? kRowBlockBytes : kTiledBlockBytes;
 #pragma unroll
         for (int i = 0; i < NT; ++i)
-            bf[i] = __builtin_bit_cast(half8_t,
-                                       __builtin_amdgcn_raw_buffer_load_b128(act, lvoff[i], blk * kBlock * 2, 0));
+            bf[i] = __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(act, lvoff[i], blk * kStride, 0));
     }
 
     // kRescale: the block scale of this lane's MFMA column in each tile;
@@ -246,9 +252,9 @@ struct BlockLoop {
     __device__ __forceinline__ void products(int blk, const half8_t (&raw)[kTilesPerWave],
                                              const float (&sv)[kTilesPerWave],
                                              float4_t (&acc)[kFrags][kTilesPerWave]) const {
-        half8_t bf[kTilesPerWave];
+        half8_t bf[kTilesPerWave];  // gate/up: loader layout to MFMA layout; down: tiled, already there
 #pragma unroll
-        for (int i = 0; i < NT; ++i) bf[i] = to_mfma_layout(raw[i], paddr);
+        for (int i = 0; i < NT; ++i) bf[i] = kRescale ? to_mfma_layout(raw[i], paddr) : raw[i];
         // A fragments in two groups of four (registers are tight: the next
         // block's unpack interleaves with these MFMAs)
 #pragma unroll
@@ -466,9 +472,12 @@ __device__ __forceinline__ void big_chunk_item(const GemmArgs& g, const Tile tl,
         if (16 * tt < tl.nrows) ntw = i + 1;  // wave-uniform
         arow[i] = -1;
         if (r < tl.nrows) arow[i] = kGateUp ? (int64_t)g.src[tl.row0 + r] : (int64_t)(tl.row0 + r);
-        int64_t la = 0;
-        if (lr < tl.nrows) la = kGateUp ? (int64_t)g.src[tl.row0 + lr] : (int64_t)(tl.row0 + lr);
-        lvoff[i] = (int)la * g.Kd * 2 + 16 * (lane & 3);
+        if constexpr (kGateUp) {
+            const int64_t la = lr < tl.nrows ? (int64_t)g.src[tl.row0 + lr] : 0;
+            lvoff[i] = (int)la * g.Kd * 2 + 16 * (lane & 3);
+        } else {  // tile tt of the chunk in the tiled operand (its padding rows are never stored)
+            lvoff[i] = (tl.tile0 + tt) * nblk * kTiledBlockBytes + 16 * lane;
+        }
         soff[i] = (int)(arow[i] >= 0 ? arow[i] : 0) * nblk * 4;
     }
 
@@ -630,10 +639,10 @@ struct SlabPass {
     __device__ __forceinline__ void load_act(int blk, const int (&lvoff)[NT], const int (&soff)[NT],
                                              half8_t (&bf)[NT], float (&sv)[NT], bool scales) const {
         blk = blk < nblk ? blk : nblk - 1;
+        constexpr int kStride = kRescale ? kRowBlockBytes : kTiledBlockBytes;
 #pragma unroll
         for (int i = 0; i < NT; ++i)
-            bf[i] = __builtin_bit_cast(half8_t,
-                                       __builtin_amdgcn_raw_buffer_load_b128(act, lvoff[i], blk * kBlock * 2, 0));
+            bf[i] = __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(act, lvoff[i], blk * kStride, 0));
         if (kRescale && scales)
 #pragma unroll
             for (int i = 0; i < NT; ++i)
@@ -829,7 +838,10 @@ __device__ __forceinline__ void small_chunk_pass(const GemmArgs& g, const Tile& 
         if (r < tl.nrows) arow[i] = kGateUp ? (int64_t)g.src[tl.row0 + r] : (int64_t)(tl.row0 + r);
         ratio[i] = arow[i] >= 0 ? (kRescale ? g.um[arow[i]] : g.um[arow[i]] / g.am[arow[i]]) : 0.f;
         const int64_t ar = arow[i] >= 0 ? arow[i] : 0;  // padding columns read row 0, never stored
-        lvoff[i] = (int)ar * g.Kd * 2 + 16 * kg;        // MFMA layout: column r16, group kg
+        if constexpr (kGateUp)
+            lvoff[i] = (int)ar * g.Kd * 2 + 16 * kg;  // MFMA layout: column r16, group kg
+        else  // tile t0 + i of the chunk in the tiled operand (padding rows never stored)
+            lvoff[i] = (tl.tile0 + t0 + i) * nblk * kTiledBlockBytes + 16 * lane;
         soff[i] = (int)ar * nblk * 4;
     }
     float4_t acc[kFrags][NT];

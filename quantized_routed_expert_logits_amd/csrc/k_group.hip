@@ -90,18 +90,23 @@ __device__ int block_exclusive_scan(int v, int* total) {
 }
 
 // Expert e's nt chunks (rows off.. off+cnt, `per` rows each, the last one
-// shorter) into the two lists at the expert's offsets in each.
-__device__ void emit_chunks(const ChunkLists& cl, int e, int off, int cnt, int nt, int per, int bpos, int spos) {
+// shorter) into the two lists at the expert's offsets in each; toff: the
+// expert's first row in the tiled row space (a multiple of 16), where its
+// rows follow in order (per is a multiple of 16, so every chunk starts a tile).
+__device__ void emit_chunks(const ChunkLists& cl, int e, int off, int cnt, int nt, int per, int bpos, int spos,
+                            int toff) {
     for (int i = 0; i < nt; ++i) {
         Tile tl;
         tl.e = e;
         tl.row0 = off + i * per;
         tl.nrows = cnt - i * per < per ? cnt - i * per : per;
-        tl.pad = 0;
+        tl.tile0 = (toff + i * per) / 16;
         if (tl.nrows > kSmallRows)
             cl.tiles[bpos++] = tl;
         else
             cl.tiles[cl.cap + spos++] = tl;
+        for (int r = 0; r < tl.nrows; r += 16)
+            cl.trows[tl.tile0 + r / 16] = TileRows{tl.row0 + r, tl.nrows - r < 16 ? tl.nrows - r : 16};
     }
 }
 
@@ -112,18 +117,19 @@ __device__ int small_chunks(int cnt, int nt, int per) {
     return ns;
 }
 
-// The list counts (one thread).
-__device__ void finish_lists(const ChunkLists& cl, int nbig, int nsmall) {
+// The list counts and the tile count (one thread).
+__device__ void finish_lists(const ChunkLists& cl, int nbig, int nsmall, int tiled_rows) {
     if (threadIdx.x == 0) {
         cl.sched[0] = nbig;
         cl.sched[1] = nsmall;
+        cl.sched[2] = tiled_rows / 16;
     }
 }
 
 __global__ void __launch_bounds__(1024) group_scan_kernel(const int32_t* __restrict__ hist, int64_t nchunks, int64_t n,
                                                           int32_t E, int32_t* __restrict__ base,
                                                           int32_t* __restrict__ offsets, ChunkLists cl) {
-    __shared__ int total_rows, total_big, total_small;
+    __shared__ int total_rows, total_tiled, total_big, total_small;
     const int e = threadIdx.x;
     int cnt = 0;
     if (e < E) {
@@ -146,6 +152,7 @@ __global__ void __launch_bounds__(1024) group_scan_kernel(const int32_t* __restr
         }
     }
     const int off = block_exclusive_scan(e < E ? cnt : 0, &total_rows);
+    const int toff = block_exclusive_scan(e < E ? (cnt + 15) / 16 * 16 : 0, &total_tiled);
     int per = 0;
     const int nt = e < E ? chunk_split(cnt, &per) : 0;
     const int ns = small_chunks(cnt, nt, per);
@@ -153,10 +160,10 @@ __global__ void __launch_bounds__(1024) group_scan_kernel(const int32_t* __restr
     const int spos = block_exclusive_scan(ns, &total_small);
     if (e < E) {
         offsets[e] = off;
-        emit_chunks(cl, e, off, cnt, nt, per, bpos, spos);
+        emit_chunks(cl, e, off, cnt, nt, per, bpos, spos, toff);
     }
     if (e == 0) offsets[E] = (int32_t)n;
-    finish_lists(cl, total_big, total_small);
+    finish_lists(cl, total_big, total_small, total_tiled);
 }
 
 constexpr int kScatterWaves = kGroupChunk / 256;  // 8 waves of 256 pairs per chunk
@@ -228,19 +235,23 @@ __global__ void __launch_bounds__(64 * kScatterWaves) group_scatter_kernel(
     }
 }
 
-// The chunk lists of a given grouping (offsets from the caller).
+// The chunk lists of a given grouping (offsets from the caller).  An expert
+// whose rows are not inside [0, n) gets none: the lists and tiled rows never
+// index past their buffers, whatever the offsets hold.
 __global__ void __launch_bounds__(1024) chunks_from_offsets_kernel(const int32_t* __restrict__ offsets, int32_t E,
-                                                                   ChunkLists cl) {
-    __shared__ int total_big, total_small;
+                                                                   int64_t n, ChunkLists cl) {
+    __shared__ int total_tiled, total_big, total_small;
     const int e = threadIdx.x;
-    const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
+    int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
+    if (e < E && (offsets[e] < 0 || cnt < 0 || offsets[e + 1] > n)) cnt = 0;
+    const int toff = block_exclusive_scan((cnt + 15) / 16 * 16, &total_tiled);
     int per = 0;
     const int nt = chunk_split(cnt, &per);
     const int ns = small_chunks(cnt, nt, per);
     const int bpos = block_exclusive_scan(nt - ns, &total_big);
     const int spos = block_exclusive_scan(ns, &total_small);
-    if (e < E) emit_chunks(cl, e, offsets[e], cnt, nt, per, bpos, spos);
-    finish_lists(cl, total_big, total_small);
+    if (e < E) emit_chunks(cl, e, offsets[e], cnt, nt, per, bpos, spos, toff);
+    finish_lists(cl, total_big, total_small, total_tiled);
 }
 
 __global__ void row_weights_kernel(const int32_t* __restrict__ slot, const float* __restrict__ p, int64_t n,
@@ -267,8 +278,9 @@ hipError_t launch_group(const int32_t* ids, const float* p, int64_t n, int32_t K
     return hipGetLastError();
 }
 
-hipError_t launch_chunks_from_offsets(const int32_t* offsets, int32_t E, const ChunkLists& cl, hipStream_t st) {
-    hipLaunchKernelGGL(chunks_from_offsets_kernel, dim3(1), dim3(1024), 0, st, offsets, E, cl);
+hipError_t launch_chunks_from_offsets(const int32_t* offsets, int32_t E, int64_t n, const ChunkLists& cl,
+                                      hipStream_t st) {
+    hipLaunchKernelGGL(chunks_from_offsets_kernel, dim3(1), dim3(1024), 0, st, offsets, E, n, cl);
     return hipGetLastError();
 }
 

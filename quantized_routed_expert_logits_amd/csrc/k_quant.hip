@@ -181,6 +181,142 @@ __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict_
     }
 }
 
+// prescale_kernel<1> for grouped rows, written in the tiled layout: one
+// workgroup per 16-row tile of the tile table.  The tile's rows are
+// consecutive grouped rows: their codes and scales are read coalesced into
+// LDS, kStageCols columns at a time (rows padded by 8 bytes / 1 float against
+// bank conflicts), then lane 16 g + r of a wave takes tile row r, value group
+// g (8 codes) of a block, so each block's fragment is one contiguous 1 KiB
+// store; wave w takes blocks w, w + 4, ...  The per-row quantities
+// (multiplier from the block scales, offset operand from the block sums)
+// follow prescale_kernel's arithmetic exactly.  Wider rows than kStageCols
+// are staged twice (once per pass).
+constexpr int kStageCols = 2048;
+inline size_t prescale_tiles_lds_bytes(int32_t cols) {
+    const int sc = cols < kStageCols ? cols : kStageCols;
+    return (size_t)16 * (sc + 8) + (size_t)16 * (sc / kBlock + 1) * sizeof(float);
+}
+
+__global__ void __launch_bounds__(256) prescale_tiles_kernel(const int8_t* __restrict__ q,
+                                                             const float* __restrict__ s,
+                                                             const TileRows* __restrict__ trows,
+                                                             const int32_t* __restrict__ ntiles, int32_t cols,
+                                                             _Float16* __restrict__ out, float* __restrict__ mult,
+                                                             _Float16* __restrict__ uop,
+                                                             float* __restrict__ umult) {
+    extern __shared__ __align__(16) unsigned char lds[];  // codes [16][sc + 8], scales [16][sc / 32 + 1]
+    __shared__ float ush[16][kMaxOffsetChunks * 32];      // u of each row and block
+    __shared__ float smx[4][16], umx[4][16];              // per wave: max block scale, max |u| of each row
+    const int64_t t = blockIdx.x;
+    if (t >= *ntiles) return;  // uniform over the workgroup, before any barrier
+    const TileRows tr = trows[t];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+    const int nb = cols / kBlock, nch = (nb + 31) / 32;
+    const int sc = cols < kStageCols ? cols : kStageCols, sb = sc / kBlock;
+    const int qstride = sc + 8, sstride = sb + 1;
+    float* sl = reinterpret_cast<float*>(lds + (size_t)16 * qstride);
+    // columns [c0, c0 + sc) of the tile's rows into LDS; rows past nrows as zeros
+    auto stage = [&](int c0) {
+        const int pieces = sc / 16;
+        for (int i = tid; i < 16 * pieces; i += 256) {
+            const int rr = i / pieces, c = i - rr * pieces;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (rr < tr.nrows && c0 + 16 * c < cols)
+                v = *reinterpret_cast<const uint4*>(q + ((int64_t)tr.row0 + rr) * cols + c0 + 16 * c);
+            *reinterpret_cast<uint2*>(lds + rr * qstride + 16 * c) = make_uint2(v.x, v.y);
+            *reinterpret_cast<uint2*>(lds + rr * qstride + 16 * c + 8) = make_uint2(v.z, v.w);
+        }
+        for (int i = tid; i < 16 * sb; i += 256) {
+            const int rr = i / sb, b = i - rr * sb, bg = c0 / kBlock + b;
+            sl[rr * sstride + b] = rr < tr.nrows && bg < nb ? s[((int64_t)tr.row0 + rr) * nb + bg] : 0.0f;
+        }
+    };
+    const bool valid = r < tr.nrows;
+    const int64_t row = (int64_t)tr.row0 + r;
+    // pass 1: block sums -> u, the row's largest block scale and |u|
+    float m = 0.0f, umax = 0.0f;
+    for (int c0 = 0; c0 < cols; c0 += sc) {
+        if (c0 > 0) __syncthreads();  // the previous slice is read
+        stage(c0);
+        __syncthreads();
+        const int b1 = (cols - c0) / kBlock < sb ? (cols - c0) / kBlock : sb;
+        for (int b = w; b < b1; b += 4) {  // uniform trip count: the shuffles see whole waves
+            const uint2 c8 = *reinterpret_cast<const uint2*>(lds + r * qstride + kBlock * b + 8 * g);
+            const float sraw = sl[r * sstride + b];
+            int sum = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sum += (int)(int8_t)(c8.x >> (8 * i)) + (int)(int8_t)(c8.y >> (8 * i));
+            sum += __shfl_xor(sum, 16);
+            sum += __shfl_xor(sum, 32);
+            const float u = -0.5f * sraw * (float)sum;
+            if (g == 0) ush[r][c0 / kBlock + b] = u;
+            m = fmaxf(m, sraw);
+            umax = fmaxf(umax, fabsf(u));
+        }
+    }
+    if (g == 0) smx[w][r] = m, umx[w][r] = umax;
+    __syncthreads();
+    m = fmaxf(fmaxf(smx[0][r], smx[1][r]), fmaxf(smx[2][r], smx[3][r]));
+    umax = fmaxf(fmaxf(umx[0][r], umx[1][r]), fmaxf(umx[2][r], umx[3][r]));
+    const float bound = 127.0f * m;  // >= every |q * s| of the row
+    float scale = 1.0f, back = 1.0f;
+    if (bound > 0.0f) {
+        int ex = 0;
+        frexpf(bound, &ex);
+        ex = ex < -96 ? -96 : ex;
+        scale = ldexpf(1.0f, 15 - ex);
+        back = ldexpf(1.0f, ex - 15);
+    }
+    int eu = 0;
+    if (umax > 0.0f) frexpf(umax, &eu);
+    eu = eu < -100 ? -100 : eu;
+    const float dn = ldexpf(1.0f, -eu);
+    if (valid && w == 0 && g == 0) {
+        mult[row] = back;
+        umult[row] = ldexpf(1.0f, eu);
+    }
+    // offset operand: value group G (blocks 8G .. 8G + 7) of row r, hi then lo
+    if (valid)
+        for (int G = 4 * w + g; G < 4 * nch; G += 16) {
+            half8_t hi, lo;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int b = 8 * G + i;
+                const float un = b < nb ? ush[r][b] * dn : 0.0f;  // exact: a power-of-two scaling
+                _Float16 h, l;
+                split_hi_lo(un, h, l);
+                hi[i] = h;
+                lo[i] = l;
+            }
+            half8_t* dst = reinterpret_cast<half8_t*>(uop + row * (int64_t)nch * 64 + 16 * G);
+            dst[0] = hi;
+            dst[1] = lo;
+        }
+    // pass 2: the prescaled values, one 1 KiB fragment store per block
+    half8_t* tile = reinterpret_cast<half8_t*>(out) + t * nb * 64;
+    for (int c0 = 0; c0 < cols; c0 += sc) {
+        if (sc < cols) {  // more than one slice: stage this one again
+            __syncthreads();
+            stage(c0);
+            __syncthreads();
+        }
+        const int b1 = (cols - c0) / kBlock < sb ? (cols - c0) / kBlock : sb;
+        for (int b = w; b < b1; b += 4) {
+            const uint2 c8 = *reinterpret_cast<const uint2*>(lds + r * qstride + kBlock * b + 8 * g);
+            const float sj = sl[r * sstride + b] * scale;  // exact: a power-of-two scaling
+            half8_t h;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int c = (int8_t)((i < 4 ? c8.x : c8.y) >> (8 * (i & 3)));
+                float v = (float)c * sj;
+                asm volatile("" : "+v"(v));
+                h[i] = (_Float16)v;  // rows past nrows: zero codes and scale, so zeros
+            }
+            tile[(c0 / kBlock + b) * 64 + lane] = h;
+        }
+    }
+}
+
 // The layer input in one pass: quantize_kernel's int8 codes and scales and
 // prescale_kernel<0>'s outputs (fp16 codes, row multiplier, offset operand)
 // from the fp32 rows, one wave per row.  Lane pairs own a 32-value block, 16
@@ -308,6 +444,15 @@ hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_
             hipLaunchKernelGGL(prescale_kernel<1>, dim3(grid_for(rows, 4)), dim3(256), 0, st, q, s, rows, cols, out,
                                mult, uop, umult);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_prescale_tiled(const int8_t* q, const float* s, const ChunkLists& cl, int64_t tiles_cap,
+                                 int32_t cols, _Float16* out, float* mult, _Float16* uop, float* umult,
+                                 hipStream_t st) {
+    if (tiles_cap > 0)
+        hipLaunchKernelGGL(prescale_tiles_kernel, dim3((unsigned)tiles_cap), dim3(256), prescale_tiles_lds_bytes(cols),
+                           st, q, s, cl.trows, cl.sched + 2, cols, out, mult, uop, umult);
     return hipGetLastError();
 }
 

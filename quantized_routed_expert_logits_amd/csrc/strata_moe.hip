@@ -140,6 +140,7 @@ struct Buffers {
     float* prow;
     int8_t* hq;
     float* hs;
+    TileRows* trows;
     _Float16* hb;
     float* he;
     _Float16* huop;
@@ -150,7 +151,7 @@ struct Buffers {
 
 struct Offsets {
     size_t logits, wt, wb, wm, pmax, amb, sel, ids, p, xq, xs, xa, xe, xuop, xum, hist, base, offsets, tiles, ntiles, err, src, slot, prow, hq, hs,
-        hb, he, huop, hum, dm, total;
+        trows, hb, he, huop, hum, dm, total;
     int64_t tiles_cap;
 };
 
@@ -186,7 +187,8 @@ Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I) {
     o.prow = L.take<float>(n);
     o.hq = L.take<int8_t>(n * I);
     o.hs = L.take<float>(n * (I / kBlock));
-    o.hb = L.take<_Float16>(n * I);
+    o.trows = L.take<TileRows>(tiled_rows_cap(n, E) / 16);
+    o.hb = L.take<_Float16>(tiled_rows_cap(n, E) * I);
     o.he = L.take<float>(n);
     o.huop = L.take<_Float16>(n * offset_operand_halves(I));
     o.hum = L.take<float>(n);
@@ -223,6 +225,7 @@ Buffers carve(char* ws, const Offsets& o) {
     b.prow = (float*)(ws + o.prow);
     b.hq = (int8_t*)(ws + o.hq);
     b.hs = (float*)(ws + o.hs);
+    b.trows = (TileRows*)(ws + o.trows);
     b.hb = (_Float16*)(ws + o.hb);
     b.he = (float*)(ws + o.he);
     b.huop = (_Float16*)(ws + o.huop);
@@ -301,11 +304,11 @@ int check_experts(const strata_moe_experts* ex) {
     return 0;
 }
 
-// The GEMMs address activations with 32-bit buffer offsets: the prescaled
-// input ([T][H], hi and lo fp16) and H ([T*K][I], fp16) must each stay below
-// 2 GiB.
-int check_buffers(int64_t T, int32_t K, int32_t H, int32_t I) {
-    if (T * (int64_t)H * 4 >= ((int64_t)1 << 31) || T * (int64_t)K * I * 2 >= ((int64_t)1 << 31))
+// The GEMMs address activations with 32-bit buffer offsets: the input's fp16
+// codes ([T][H]) and the tiled H operand (T*K rows and up to 15 padding rows
+// per expert, [.][I] fp16) must each stay below 2 GiB.
+int check_buffers(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I) {
+    if (T * (int64_t)H * 4 >= ((int64_t)1 << 31) || tiled_rows_cap(T * K, E) * I * 2 >= ((int64_t)1 << 31))
         return fail(STRATA_MOE_EINVAL, "T = %lld too large for one call at H = %d, I = %d, K = %d", (long long)T, H, I,
                     K);
     return 0;
@@ -359,7 +362,7 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
             "top-K launch");
     tm.end(kTopK);
     tm.begin(kGroup);
-    const ChunkLists cl{b.tiles, b.ntiles, b.tiles_cap};
+    const ChunkLists cl{b.tiles, b.ntiles, b.tiles_cap, b.trows};
     HIP_TRY(launch_group(b.ids, b.p, n, K, E, b.hist, b.base, b.offsets, cl, b.src, b.slot, b.prow, b.err, st),
             "group launch");
     tm.end(kGroup);
@@ -369,11 +372,12 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
             "gate/up launch");
     tm.end(kGateUp);
     tm.begin(kPrescaleH);
-    HIP_TRY(launch_prescale(b.hq, b.hs, n, I, 1, b.hb, b.he, b.huop, b.hum, st), "prescale launch");
+    HIP_TRY(launch_prescale_tiled(b.hq, b.hs, cl, tiled_rows_cap(n, E) / 16, I, b.hb, b.he, b.huop, b.hum, st),
+            "prescale launch");
     tm.end(kPrescaleH);
     tm.begin(kDown);
-    HIP_TRY(launch_down((const uint8_t*)ex->down, ex->down_stride, cl, n, E, b.src, b.prow, b.hb, n, b.he, b.huop, b.hum,
-                        H, I, b.dm, st),
+    HIP_TRY(launch_down((const uint8_t*)ex->down, ex->down_stride, cl, n, E, b.src, b.prow, b.hb, tiled_rows_cap(n, E),
+                        b.he, b.huop, b.hum, H, I, b.dm, st),
             "down launch");
     tm.end(kDown);
     tm.begin(kCombine);
@@ -436,7 +440,7 @@ int strata_moe_workspace_bytes(int64_t T, int32_t K, const strata_moe_experts* e
     if (!bytes) return fail(STRATA_MOE_EINVAL, "bytes is NULL");
     TRY(check_experts(experts));
     TRY(check_tk(T, K, experts->n_expert));
-    TRY(check_buffers(T, K, experts->hidden, experts->ffn));
+    TRY(check_buffers(T, K, experts->n_expert, experts->hidden, experts->ffn));
     *bytes = plan(T, K, experts->n_expert, experts->hidden, experts->ffn).total;
     return 0;
 }
@@ -504,7 +508,7 @@ int strata_moe_prefill(const float* x, const float* router_w, const strata_moe_e
     g_err.clear();
     TRY(check_experts(experts));
     TRY(check_tk(T, K, experts->n_expert));
-    TRY(check_buffers(T, K, experts->hidden, experts->ffn));
+    TRY(check_buffers(T, K, experts->n_expert, experts->hidden, experts->ffn));
     if (T == 0) return 0;
     if (!x || !router_w || !out) return fail(STRATA_MOE_EINVAL, "null x / router_w / out");
     if (!aligned(x, 16) || !aligned(out, 16)) return fail(STRATA_MOE_EINVAL, "x and out must be 16-byte aligned");
@@ -518,7 +522,7 @@ int strata_moe_prefill_debug(const float* x, const float* router_w, const strata
     g_err.clear();
     TRY(check_experts(experts));
     TRY(check_tk(T, K, experts->n_expert));
-    TRY(check_buffers(T, K, experts->hidden, experts->ffn));
+    TRY(check_buffers(T, K, experts->n_expert, experts->hidden, experts->ffn));
     if (T == 0) return 0;
     if (!x || !router_w || !out || !dbg) return fail(STRATA_MOE_EINVAL, "null x / router_w / out / dbg");
     if (!aligned(x, 16) || !aligned(out, 16)) return fail(STRATA_MOE_EINVAL, "x and out must be 16-byte aligned");
@@ -587,12 +591,14 @@ int strata_moe_group(const int32_t* ids, int64_t T, int32_t K, int32_t E, int32_
     const size_t o_hist = L.take<int32_t>(nchunks * E), o_base = L.take<int32_t>(nchunks * E);
     const int64_t cap = chunk_list_cap(n, E);
     const size_t o_tiles = L.take<Tile>(2 * cap), o_nt = L.take<int32_t>(kSchedInts), o_err = L.take<int32_t>(1);
+    const size_t o_trows = L.take<TileRows>(tiled_rows_cap(n, E) / 16);
     char* ws = nullptr;
     TRY(get_workspace(L.off, &ws));
     int32_t* err = (int32_t*)(ws + o_err);
     HIP_TRY(launch_fill_zero((float*)err, 1, st), "fill launch");
     HIP_TRY(launch_group(ids, nullptr, n, K, E, (int32_t*)(ws + o_hist), (int32_t*)(ws + o_base), offsets,
-                         ChunkLists{(Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), cap}, src, slot, nullptr, err, st),
+                         ChunkLists{(Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), cap, (TileRows*)(ws + o_trows)}, src,
+                         slot, nullptr, err, st),
             "group launch");
     int32_t herr = 0;
     HIP_TRY(hipMemcpyAsync(&herr, err, 4, hipMemcpyDeviceToHost, st), "hipMemcpyAsync");
@@ -617,7 +623,7 @@ int strata_moe_gate_up(const int8_t* qx, const float* sx, const int32_t* offsets
     g_err.clear();
     TRY(check_experts(experts));
     TRY(check_tk(T, K, experts->n_expert));
-    TRY(check_buffers(T, K, experts->hidden, experts->ffn));
+    TRY(check_buffers(T, K, experts->n_expert, experts->hidden, experts->ffn));
     if (T == 0) return 0;
     if (!qx || !sx || !offsets || !src || !qh || !sh) return fail(STRATA_MOE_EINVAL, "null pointer");
     TRY(check_device());
@@ -628,15 +634,16 @@ int strata_moe_gate_up(const int8_t* qx, const float* sx, const int32_t* offsets
     const size_t o_xa = L.take<_Float16>(T * H);
     const size_t o_xuop = L.take<_Float16>(T * offset_operand_halves(H)), o_xum = L.take<float>(T);
     const int64_t cap = chunk_list_cap(n, E);
-    const size_t o_tiles = L.take<Tile>(2 * cap), o_nt = L.take<int32_t>(kSchedInts);
+    const size_t o_tiles = L.take<Tile>(2 * cap), o_nt = L.take<int32_t>(kSchedInts),
+                 o_trows = L.take<TileRows>(tiled_rows_cap(n, E) / 16);
     char* ws = nullptr;
     TRY(get_workspace(L.off, &ws));
-    const ChunkLists cl{(Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), cap};
+    const ChunkLists cl{(Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), cap, (TileRows*)(ws + o_trows)};
     _Float16* xa = (_Float16*)(ws + o_xa);
     _Float16* xuop = (_Float16*)(ws + o_xuop);
     float* xum = (float*)(ws + o_xum);
     HIP_TRY(launch_prescale(qx, sx, T, H, 0, xa, nullptr, xuop, xum, st), "prescale launch");
-    HIP_TRY(launch_chunks_from_offsets(offsets, E, cl, st), "chunk list launch");
+    HIP_TRY(launch_chunks_from_offsets(offsets, E, n, cl, st), "chunk list launch");
     HIP_TRY(launch_gate_up((const uint8_t*)experts->gate_up, experts->gate_up_stride, cl, n, E, src, xa, sx, T, xuop,
                            xum, H, I, qh, sh, st),
             "gate/up launch");
@@ -649,7 +656,7 @@ int strata_moe_down(const int8_t* qh, const float* sh, const int32_t* offsets, c
     g_err.clear();
     TRY(check_experts(experts));
     TRY(check_tk(T, K, experts->n_expert));
-    TRY(check_buffers(T, K, experts->hidden, experts->ffn));
+    TRY(check_buffers(T, K, experts->n_expert, experts->hidden, experts->ffn));
     if (T == 0) return 0;
     if (!qh || !sh || !offsets || !src || !slot || !p || !out) return fail(STRATA_MOE_EINVAL, "null pointer");
     TRY(check_device());
@@ -657,25 +664,25 @@ int strata_moe_down(const int8_t* qh, const float* sh, const int32_t* offsets, c
     const int32_t E = experts->n_expert, H = experts->hidden, I = experts->ffn;
     const int64_t n = T * K;
     Layout L;
-    const size_t o_hb = L.take<_Float16>(n * I), o_he = L.take<float>(n);
+    const size_t o_hb = L.take<_Float16>(tiled_rows_cap(n, E) * I), o_he = L.take<float>(n);
     const size_t o_huop = L.take<_Float16>(n * offset_operand_halves(I)), o_hum = L.take<float>(n);
     const int64_t cap = chunk_list_cap(n, E);
     const size_t o_tiles = L.take<Tile>(2 * cap), o_nt = L.take<int32_t>(kSchedInts), o_prow = L.take<float>(n);
-    const size_t o_dm = L.take<float>(n * H);
+    const size_t o_dm = L.take<float>(n * H), o_trows = L.take<TileRows>(tiled_rows_cap(n, E) / 16);
     char* ws = nullptr;
     TRY(get_workspace(L.off, &ws));
-    const ChunkLists cl{(Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), cap};
+    const ChunkLists cl{(Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), cap, (TileRows*)(ws + o_trows)};
     _Float16* hb = (_Float16*)(ws + o_hb);
     float* he = (float*)(ws + o_he);
     _Float16* huop = (_Float16*)(ws + o_huop);
     float* hum = (float*)(ws + o_hum);
     float* prow = (float*)(ws + o_prow);
     float* dm = (float*)(ws + o_dm);
-    HIP_TRY(launch_prescale(qh, sh, n, I, 1, hb, he, huop, hum, st), "prescale launch");
-    HIP_TRY(launch_chunks_from_offsets(offsets, E, cl, st), "chunk list launch");
+    HIP_TRY(launch_chunks_from_offsets(offsets, E, n, cl, st), "chunk list launch");  // and the tile table
+    HIP_TRY(launch_prescale_tiled(qh, sh, cl, tiled_rows_cap(n, E) / 16, I, hb, he, huop, hum, st), "prescale launch");
     HIP_TRY(launch_row_weights(slot, p, n, prow, st), "weights launch");
-    HIP_TRY(launch_down((const uint8_t*)experts->down, experts->down_stride, cl, n, E, src, prow, hb, n, he, huop, hum, H,
-                        I, dm, st),
+    HIP_TRY(launch_down((const uint8_t*)experts->down, experts->down_stride, cl, n, E, src, prow, hb,
+                        tiled_rows_cap(n, E), he, huop, hum, H, I, dm, st),
             "down launch");
     HIP_TRY(launch_combine(dm, slot, T, K, H, out, st), "combine launch");
     return 0;
