@@ -263,15 +263,25 @@ struct BlockLoop {
 #pragma unroll
             for (int f = 0; f < kFrags / 2; ++f) a[f] = a_lds[blk & 1][4 * g + f][lane ^ ((4 * g + f) & ~1)];
             if constexpr (kRescale) {
+                // the FMAs that scale a product run kLag MFMAs later, beside
+                // the MFMAs in between (issued as one MFMA, then four FMAs),
+                // so the wave does not wait for each product in turn
+                constexpr int kLag = 2, kN = kFrags / 2 * NT;
+                float4_t tq[kLag + 1];
 #pragma unroll
-                for (int f = 0; f < kFrags / 2; ++f)
+                for (int k = 0; k < kN + kLag; ++k) {
+                    if (k < kN)
+                        tq[k % (kLag + 1)] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            a[k / NT], bf[k % NT], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    if (k >= kLag) {
+                        const int kp = k - kLag, f = kp / NT, i = kp % NT;
 #pragma unroll
-                    for (int i = 0; i < NT; ++i) {
-                        const float4_t t = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            a[f], bf[i], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) acc[4 * g + f][i][v] = fmaf(t[v], sv[i], acc[4 * g + f][i][v]);
+                        for (int v = 0; v < 4; ++v)
+                            acc[4 * g + f][i][v] = fmaf(tq[kp % (kLag + 1)][v], sv[i], acc[4 * g + f][i][v]);
                     }
+                    if (k < kN) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    if (k >= kLag) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // then its FMAs
+                }
             } else {
 #pragma unroll
                 for (int f = 0; f < kFrags / 2; ++f)
