@@ -41,6 +41,7 @@ constexpr int kSmallRows = 48;  // chunks of at most this many rows go to the sm
 constexpr int kSchedInts = 3;
 struct TileRows {
     int32_t row0, nrows;  // grouped rows [row0, row0 + nrows), nrows <= 16
+    int32_t big;          // 1 if the tile's chunk has more than kSmallRows rows
 };
 struct ChunkLists {
     Tile* tiles;      // [2 * cap]
@@ -65,23 +66,34 @@ struct ZeroWords {
 };
 hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q8, float* s, hipStream_t st,
                            ZeroWords z = ZeroWords{{nullptr, nullptr}});
-// fp16 GEMM operand of int8 rows, [rows][cols]: parts 1: q * s * 2^-e_r;
-// parts 0: the codes q themselves (exact).  Both: the row multipliers 2^e_r
-// in mult (if non-null), and the offset-pass operand (u per block, hi/lo,
-// [rows][offset_operand_halves]) and its row multipliers.
-hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_t cols, int parts, _Float16* out,
-                           float* mult, _Float16* uop, float* umult, hipStream_t st);
-// The parts-1 operand of the grouped rows in the tiled layout: tile t of the
-// chunk lists' tile table holds grouped rows trows[t], stored as
+// Per int8 row: the codes q themselves as fp16 (exact), [rows][cols], if out
+// is non-null; the row multipliers 2^e_r (127 * the row's largest
+// block scale in [2^14, 2^15) after scaling by 2^-e_r) in mult if non-null;
+// the offset-pass operand (u per block, hi/lo, [rows][offset_operand_halves])
+// and its row multipliers.
+hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_t cols, _Float16* out, float* mult,
+                           _Float16* uop, float* umult, hipStream_t st);
+// The down GEMM operand q * s * 2^-e_r (fp16) of the grouped rows in the
+// tiled layout: tile t of the chunk lists' tile table holds grouped rows
+// trows[t], stored as
 // [tile][block][group g of 8 values][row within the tile][8] (one MFMA
 // fragment of a tile and block is 1 KiB in MFMA lane order; rows past a
 // tile's nrows are zero).  mult, uop, umult as launch_prescale, per grouped
-// row.  tiles_cap bounds the tile count (the grid).
+// row (all written).  tiles_cap bounds the tile count (the grid).
+// The 4-wave gate/up kernel's operand in the tiled layout: tile t of the
+// chunk lists' tile table (tiles of chunks of more than kSmallRows rows only)
+// holds grouped rows trows[t], each the token src[row] of the int8 rows q
+// [tokens][cols] with block scales s; out = [tile][block][group g of 8
+// values][row within the tile][8] fp16 codes (exact), sout = [tile][block /
+// 4][row within the tile][4] block scales; rows past a tile's nrows are
+// zeros.  tiles_cap bounds the tile count.
+hipError_t launch_gather_tiles(const int8_t* q, const float* s, const int32_t* src, const ChunkLists& cl,
+                               int64_t tiles_cap, int32_t cols, _Float16* out, float* sout, hipStream_t st);
 hipError_t launch_prescale_tiled(const int8_t* q, const float* s, const ChunkLists& cl, int64_t tiles_cap,
                                  int32_t cols, _Float16* out, float* mult, _Float16* uop, float* umult,
                                  hipStream_t st);
 // The layer input in one pass: launch_quantize's outputs (q8, s) and
-// launch_prescale's with parts 0 (codes16, mult, uop, umult), bit-identical to
+// launch_prescale's (codes16, mult, uop, umult), bit-identical to
 // the two launches; also clears the ZeroWords.
 hipError_t launch_quantize_prescale(const float* x, int64_t rows, int32_t cols, int8_t* q8, float* s,
                                    _Float16* codes16, float* mult, _Float16* uop, float* umult, hipStream_t st,
@@ -157,15 +169,18 @@ hipError_t launch_chunks_from_offsets(const int32_t* offsets, int32_t E, int64_t
                                       hipStream_t st);
 hipError_t launch_row_weights(const int32_t* slot, const float* p, int64_t n, float* prow, hipStream_t st);
 
-// gate/up: xa = the input codes as fp16 (prescale parts 0) and xs = their
-// block scales, act_rows rows each; xuop / xum = offset-pass operand and
-// multipliers; writes int8 H codes hq and scales hs.
+// gate/up: xt / xst = the tiled codes and scales (launch_gather_tiles,
+// tiled_rows rows) for the 4-wave kernel; xa = the input codes as fp16
+// (launch_prescale) and xs = their block scales, T rows each, for the small-
+// chunk kernel; xuop / xum = offset-pass operand and multipliers; writes int8
+// H codes hq and scales hs.
 // n = routed rows, E = experts (bounds of the two chunk lists' lengths).
 hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const ChunkLists& cl, int64_t n, int32_t E,
-                          const int32_t* src, const _Float16* xa, const float* xs, int64_t act_rows,
-                          const _Float16* xuop, const float* xum, int32_t H, int32_t I, int8_t* hq, float* hs,
-                          hipStream_t st);
-// down: hb = prescaled H rows (parts 1), he = their multipliers, huop / hum =
+                          const int32_t* src, const _Float16* xt, const float* xst, int64_t tiled_rows,
+                          const _Float16* xa, const float* xs, int64_t T, const _Float16* xuop, const float* xum,
+                          int32_t H, int32_t I, int8_t* hq, float* hs, hipStream_t st);
+// down: hb = the tiled prescaled H (launch_prescale_tiled; act_rows = its
+// rows), he = the row multipliers, huop / hum =
 // offset-pass operand and multipliers; writes the weighted rows dm.
 hipError_t launch_down(const uint8_t* blobs, int64_t stride, const ChunkLists& cl, int64_t n, int32_t E,
                        const int32_t* src, const float* prow, const _Float16* hb, int64_t act_rows, const float* he,

@@ -113,35 +113,20 @@ __device__ __forceinline__ float round_half_away(float t) {
     return copysignf(fminf(r, 127.0f), t);
 }
 
-// Bytes between consecutive blocks of one activation fragment: 64 in the
-// row-major gate/up input [rows][Kd], 1 KiB in the tiled down operand
-// [tile][block][group][16 rows][8] (a tile's fragment of a block is 1 KiB in
-// MFMA lane order: lane 16 g + r reads row r, group g, 16 contiguous bytes).
-constexpr int kRowBlockBytes = kBlock * 2, kTiledBlockBytes = 16 * kBlock * 2;
-
-// Activation (B operand) fragments are read coalesced, then moved into the
-// MFMA layout.  In the MFMA layout lane d holds column (routed row) d % 16 and
-// value group d / 16 of a block, so consecutive lanes would read 16 different
-// rows, one L1 access each.  Instead loader lane L = 16a + 4c + k reads tile
-// row 4c + a, group k: four consecutive lanes read one row's 64 contiguous
-// bytes of a part.  Lane d then takes (ds_bpermute) the loader lane of its
-// row and group, L = 16 (r % 4) + 4 (r / 4) + g for r = d % 16, g = d / 16:
-// an exchange of lane-index bits {0,1} and {4,5}.
-__device__ __forceinline__ int loader_row(int lane) { return 4 * ((lane >> 2) & 3) + (lane >> 4); }
-
-__device__ __forceinline__ int mfma_source_addr(int lane) {
-    const int r = lane & 15, g = lane >> 4;
-    return 4 * (16 * (r & 3) + 4 * (r >> 2) + g);  // byte address of the source lane
-}
-
-__device__ __forceinline__ half8_t to_mfma_layout(half8_t v, int addr) {
-    uint4 u = __builtin_bit_cast(uint4, v);
-    u.x = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)u.x);
-    u.y = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)u.y);
-    u.z = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)u.z);
-    u.w = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)u.w);
-    return __builtin_bit_cast(half8_t, u);
-}
+// Both GEMMs read their activations (B operand) in the tiled layout of the
+// grouped rows: [tile][block][group g][16 rows][8] fp16, so the fragment of
+// one 16-row tile and block is 1 KiB in MFMA lane order (lane 16 g + r holds
+// row r, values 8g .. 8g + 7) and one coalesced 16-byte load per lane.  The
+// gate/up block scales are tiled alike: [tile][block / 4][16 rows][4] fp32.
+// For a tile's lane: activation offset tile * nblk * kTiledBlockBytes +
+// 16 * lane, plus blk * kTiledBlockBytes; scale offset tile * nblk * 64 +
+// 16 * r, plus tiled_scale_offset(blk).
+constexpr int kTiledBlockBytes = 16 * kBlock * 2;
+__device__ __forceinline__ int tiled_scale_offset(int blk) { return (blk >> 2) * 256 + (blk & 3) * 4; }
+// The small-chunk gate/up kernel reads its tokens' rows in place instead:
+// codes [tokens][Kd] fp16 (64 bytes per block of a row), scales
+// [tokens][Kd / 32] fp32.
+constexpr int kRowBlockBytes = kBlock * 2;
 
 struct GemmArgs {
     const uint8_t* blobs;  // packed matrices, one per expert
@@ -152,9 +137,10 @@ struct GemmArgs {
     int32_t Kd;            // reduction length (H for gate/up, I for down)
     const int32_t* src;    // token of each grouped row
     const float* prow;     // routing weight of each grouped row (down)
-    const _Float16* act;   // activations fp16: gate/up the codes [rows][Kd], down prescaled, tiled
-    int64_t act_rows;      // rows of act (down: tiled rows) and ascale
-    const float* ascale;   // gate/up: block scales of act [rows][Kd / 32]
+    const _Float16* act;   // activations fp16: gate/up the codes (4-wave kernel tiled, small-chunk
+                           // kernel [tokens][Kd]), down prescaled (tiled)
+    int64_t act_rows;      // rows of act and ascale
+    const float* ascale;   // gate/up: block scales of act (tiled [tile][Kd / 128][16][4], or [tokens][Kd / 32])
     const float* am;       // down: row multipliers 2^e of act [rows]
     const _Float16* uop;   // offset-pass operand [rows][nch x 32 blocks x 2] (hi, lo)
     const float* um;       // its row multipliers [rows]
@@ -177,7 +163,7 @@ struct BlockLoop {
     __amdgpu_buffer_rsrc_t act;  // activations [rows][Kd] fp16: codes (kRescale) or prescaled
     __amdgpu_buffer_rsrc_t scl;  // kRescale: block scales [rows][nblk] fp32
     int32_t Kd, nblk, dstride;
-    int tau, lane, r16, kg, p, paddr;
+    int tau, lane, r16, kg, p;
     _Float16* d_lds;
     half8_t (*a_lds)[kFrags][64];
     UnpackMagic mg;
@@ -194,41 +180,40 @@ struct BlockLoop {
         sw = __builtin_amdgcn_raw_buffer_load_b32(rec, kRecordCodeBytes + lane * 4, blk * kRecordBytes, 0);
     }
 
-    // Activation fragments of a block in the loader layout (see loader_row):
-    // lvoff[i] is this lane's byte offset of its loader row and group in tile
-    // i; a block is 64 bytes of a row.
+    // Activation fragments of a block (tiled): lvoff[i] is this lane's byte
+    // offset in tile i.
     template <int NT>
     __device__ __forceinline__ void load_act(int blk, const int (&lvoff)[kTilesPerWave],
                                              half8_t (&bf)[kTilesPerWave]) const {
         blk = blk < nblk ? blk : nblk - 1;
-        constexpr int kStride = kRescale ? kRowBlockBytes : kTiledBlockBytes;
 #pragma unroll
         for (int i = 0; i < NT; ++i)
-            bf[i] = __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(act, lvoff[i], blk * kStride, 0));
+            bf[i] = __builtin_bit_cast(half8_t,
+                                       __builtin_amdgcn_raw_buffer_load_b128(act, lvoff[i], blk * kTiledBlockBytes, 0));
     }
 
     // kRescale: the block scale of this lane's MFMA column in each tile;
-    // soff[i] is the byte offset of that row's scales.
+    // soff[i] is the byte offset of that row's scales (tiled).
     template <int NT>
     __device__ __forceinline__ void load_scales(int blk, const int (&soff)[kTilesPerWave],
                                                 float (&sv)[kTilesPerWave]) const {
         blk = blk < nblk ? blk : nblk - 1;
 #pragma unroll
         for (int i = 0; i < NT; ++i)
-            sv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(scl, soff[i], blk * 4, 0));
+            sv[i] = __builtin_bit_cast(float,
+                                       __builtin_amdgcn_raw_buffer_load_b32(scl, soff[i], tiled_scale_offset(blk), 0));
     }
 
     // The same for blocks blk .. blk + 3 (blk a multiple of 4, 4 | nblk): one
-    // 16-byte load per tile.  The 16 columns of a tile are 16 different rows,
-    // so a per-block load touches 16 cache lines for 64 useful bytes; four
-    // blocks per load cut those accesses fourfold.
+    // 16-byte load per tile and 4 blocks.
     template <int NT>
     __device__ __forceinline__ void load_scales4(int blk, const int (&soff)[kTilesPerWave],
                                                  float4_t (&sq)[kTilesPerWave]) const {
         blk = blk < nblk ? blk : nblk - 4;
 #pragma unroll
         for (int i = 0; i < NT; ++i)
-            sq[i] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(scl, soff[i], blk * 4, 0));
+            sq[i] = __builtin_bit_cast(float4_t,
+                                       __builtin_amdgcn_raw_buffer_load_b128(scl, soff[i], tiled_scale_offset(blk), 0));
     }
 
     // Record dword dw holds fragments 2p and 2p+1 of MFMA lane dw / 4
@@ -252,9 +237,7 @@ struct BlockLoop {
     __device__ __forceinline__ void products(int blk, const half8_t (&raw)[kTilesPerWave],
                                              const float (&sv)[kTilesPerWave],
                                              float4_t (&acc)[kFrags][kTilesPerWave]) const {
-        half8_t bf[kTilesPerWave];  // gate/up: loader layout to MFMA layout; down: tiled, already there
-#pragma unroll
-        for (int i = 0; i < NT; ++i) bf[i] = kRescale ? to_mfma_layout(raw[i], paddr) : raw[i];
+        const half8_t (&bf)[kTilesPerWave] = raw;  // tiled: already in the MFMA layout
         // A fragments in two groups of four (registers are tight: the next
         // block's unpack interleaves with these MFMAs)
 #pragma unroll
@@ -262,7 +245,7 @@ struct BlockLoop {
             half8_t a[kFrags / 2];
 #pragma unroll
             for (int f = 0; f < kFrags / 2; ++f) a[f] = a_lds[blk & 1][4 * g + f][lane ^ ((4 * g + f) & ~1)];
-            if constexpr (kRescale) {
+            if constexpr (kRescale && NT > 0) {
                 // the FMAs that scale a product run kLag MFMAs later, beside
                 // the MFMAs in between (issued as one MFMA, then four FMAs),
                 // so the wave does not wait for each product in turn
@@ -282,7 +265,7 @@ struct BlockLoop {
                     if (k < kN) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
                     if (k >= kLag) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // then its FMAs
                 }
-            } else {
+            } else if constexpr (!kRescale) {
 #pragma unroll
                 for (int f = 0; f < kFrags / 2; ++f)
 #pragma unroll
@@ -478,17 +461,13 @@ __device__ __forceinline__ void big_chunk_item(const GemmArgs& g, const Tile tl,
 #pragma unroll
     for (int i = 0; i < kTilesPerWave; ++i) {
         const int tt = tw + kWaves * i;
-        const int r = 16 * tt + r16, lr = 16 * tt + loader_row(lane);
+        const int r = 16 * tt + r16;
         if (16 * tt < tl.nrows) ntw = i + 1;  // wave-uniform
         arow[i] = -1;
         if (r < tl.nrows) arow[i] = kGateUp ? (int64_t)g.src[tl.row0 + r] : (int64_t)(tl.row0 + r);
-        if constexpr (kGateUp) {
-            const int64_t la = lr < tl.nrows ? (int64_t)g.src[tl.row0 + lr] : 0;
-            lvoff[i] = (int)la * g.Kd * 2 + 16 * (lane & 3);
-        } else {  // tile tt of the chunk in the tiled operand (its padding rows are never stored)
-            lvoff[i] = (tl.tile0 + tt) * nblk * kTiledBlockBytes + 16 * lane;
-        }
-        soff[i] = (int)(arow[i] >= 0 ? arow[i] : 0) * nblk * 4;
+        // tile tt of the chunk in the tiled operands (padding rows are zeros, never stored)
+        lvoff[i] = (tl.tile0 + tt) * nblk * kTiledBlockBytes + 16 * lane;
+        soff[i] = (tl.tile0 + tt) * nblk * 64 + 16 * r16;
     }
 
     const uint8_t* rec = g.blobs + (int64_t)tl.e * g.stride + (int64_t)slab * nblk * kRecordBytes;
@@ -504,7 +483,7 @@ __device__ __forceinline__ void big_chunk_item(const GemmArgs& g, const Tile tl,
         __builtin_amdgcn_make_buffer_rsrc((void*)g.act, (short)0, (int)(g.act_rows * g.Kd * 2), kBufferWord3),
         __builtin_amdgcn_make_buffer_rsrc((void*)g.ascale, (short)0, kRescale ? (int)(g.act_rows * nblk * 4) : 0,
                                           kBufferWord3),
-        g.Kd, nblk, dstride, tau, lane, r16, kg, p, mfma_source_addr(lane), d_lds, a_lds, UnpackMagic(), 0};
+        g.Kd, nblk, dstride, tau, lane, r16, kg, p, d_lds, a_lds, UnpackMagic(), 0};
     // The record's 256 dwords are unpacked by the waves with fewer tiles where
     // the chunk's tiles do not split evenly (nt = 4q + r; waves 0..r-1 hold
     // q + 1 tiles): r = 1: dwords per lane (0, 2, 1, 1); r = 2: (0, 0, 2, 2);
@@ -643,9 +622,10 @@ struct SlabPass {
         }
     }
 
-    // Activation fragments of a block (lvoff: this lane's byte offset of its
-    // column's row and group); with kRescale also the block scale of the
-    // lane's column in each tile (soff: byte offset of that row's scales).
+    // Activation fragments of a block (lvoff: this lane's byte offset; gate/up
+    // its column's row and group in place, down its place in the tiled
+    // operand); with kRescale also the block scale of the lane's column in
+    // each tile (soff: byte offset of that row's scales).
     __device__ __forceinline__ void load_act(int blk, const int (&lvoff)[NT], const int (&soff)[NT],
                                              half8_t (&bf)[NT], float (&sv)[NT], bool scales) const {
         blk = blk < nblk ? blk : nblk - 1;
@@ -660,7 +640,7 @@ struct SlabPass {
     }
 
     // kRescale: the scales of blocks blk .. blk + 3 (blk a multiple of 4,
-    // 4 | nblk), one 16-byte load per tile instead of four gathered ones.
+    // 4 | nblk), one 16-byte load per tile instead of four gathered dwords.
     __device__ __forceinline__ void load_scales4(int blk, const int (&soff)[NT], float4_t (&sq)[NT]) const {
         blk = blk < nblk ? blk : nblk - 4;
 #pragma unroll
@@ -850,7 +830,7 @@ __device__ __forceinline__ void small_chunk_pass(const GemmArgs& g, const Tile& 
         const int64_t ar = arow[i] >= 0 ? arow[i] : 0;  // padding columns read row 0, never stored
         if constexpr (kGateUp)
             lvoff[i] = (int)ar * g.Kd * 2 + 16 * kg;  // MFMA layout: column r16, group kg
-        else  // tile t0 + i of the chunk in the tiled operand (padding rows never stored)
+        else  // tile t0 + i of the chunk in the tiled operand (padding rows are zeros, never stored)
             lvoff[i] = (tl.tile0 + t0 + i) * nblk * kTiledBlockBytes + 16 * lane;
         soff[i] = (int)ar * nblk * 4;
     }
@@ -959,8 +939,9 @@ inline unsigned grid_of(int64_t chunks_cap, int32_t per_chunk) {
 // n / (kSmallRows + 1) experts have a big one; an expert has at most one
 // small chunk.  Workgroups past the list's length exit at once, so a tight
 // bound saves their launches.
-void launch_gemms(GemmArgs g, const ChunkLists& cl, int64_t n, int32_t E, size_t big_lds, bool gate_up,
-                  hipStream_t st) {
+// gs: the small-chunk kernel's arguments (its activations may differ).
+void launch_gemms(GemmArgs g, GemmArgs gs_args, const ChunkLists& cl, int64_t n, int32_t E, size_t big_lds,
+                  bool gate_up, hipStream_t st) {
     const int64_t by_rows = n / (kSmallRows + 1);
     const int64_t by_experts = n / kChunkRows + (E < by_rows ? E : by_rows);
     int64_t cap_big = cl.cap < by_rows ? cl.cap : by_rows;
@@ -975,26 +956,30 @@ void launch_gemms(GemmArgs g, const ChunkLists& cl, int64_t n, int32_t E, size_t
         else
             hipLaunchKernelGGL(expert_gemm_kernel<false>, dim3(gb), dim3(256), big_lds, st, g);
     }
-    g.chunks = cl.tiles + cl.cap;
-    g.nchunks = cl.sched + 1;
+    gs_args.chunks = cl.tiles + cl.cap;
+    gs_args.nchunks = cl.sched + 1;
     if (cap_small > 0) {
-        const unsigned gs = grid_of(cap_small, (g.nslab + kWaves - 1) / kWaves);
+        const unsigned gs = grid_of(cap_small, (gs_args.nslab + kWaves - 1) / kWaves);
         if (gate_up)
-            hipLaunchKernelGGL(expert_gemm_small_kernel<true>, dim3(gs), dim3(256), 0, st, g);
+            hipLaunchKernelGGL(expert_gemm_small_kernel<true>, dim3(gs), dim3(256), 0, st, gs_args);
         else
-            hipLaunchKernelGGL(expert_gemm_small_kernel<false>, dim3(gs), dim3(256), 0, st, g);
+            hipLaunchKernelGGL(expert_gemm_small_kernel<false>, dim3(gs), dim3(256), 0, st, gs_args);
     }
 }
 
 }  // namespace
 
 hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const ChunkLists& cl, int64_t n, int32_t E,
-                          const int32_t* src, const _Float16* xa, const float* xs, int64_t act_rows,
-                          const _Float16* xuop, const float* xum, int32_t H, int32_t I, int8_t* hq, float* hs,
-                          hipStream_t st) {
-    GemmArgs g{blobs, stride, nullptr, nullptr, 2 * I / kSlabRows, H, src, nullptr, xa, act_rows, xs, nullptr, xuop,
-               xum, I, H, hq, hs, nullptr};
-    launch_gemms(g, cl, n, E, dynamic_lds_bytes(H, false), true, st);
+                          const int32_t* src, const _Float16* xt, const float* xst, int64_t tiled_rows,
+                          const _Float16* xa, const float* xs, int64_t T, const _Float16* xuop, const float* xum,
+                          int32_t H, int32_t I, int8_t* hq, float* hs, hipStream_t st) {
+    const GemmArgs g{blobs, stride, nullptr, nullptr, 2 * I / kSlabRows, H, src, nullptr, xt, tiled_rows, xst,
+                     nullptr, xuop, xum, I, H, hq, hs, nullptr};
+    GemmArgs gs = g;
+    gs.act = xa;
+    gs.act_rows = T;
+    gs.ascale = xs;
+    launch_gemms(g, gs, cl, n, E, dynamic_lds_bytes(H, false), true, st);
     return hipGetLastError();
 }
 
@@ -1004,7 +989,7 @@ hipError_t launch_down(const uint8_t* blobs, int64_t stride, const ChunkLists& c
     GemmArgs g{blobs, stride, nullptr, nullptr, H / kSlabRows, I, src, prow, hb, act_rows, nullptr, he, huop, hum, I,
                H,
                nullptr, nullptr, dm};
-    launch_gemms(g, cl, n, E, dynamic_lds_bytes(I, true), false, st);
+    launch_gemms(g, g, cl, n, E, dynamic_lds_bytes(I, true), false, st);
     return hipGetLastError();
 }
 

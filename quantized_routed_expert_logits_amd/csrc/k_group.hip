@@ -106,7 +106,8 @@ __device__ void emit_chunks(const ChunkLists& cl, int e, int off, int cnt, int n
         else
             cl.tiles[cl.cap + spos++] = tl;
         for (int r = 0; r < tl.nrows; r += 16)
-            cl.trows[tl.tile0 + r / 16] = TileRows{tl.row0 + r, tl.nrows - r < 16 ? tl.nrows - r : 16};
+            cl.trows[tl.tile0 + r / 16] =
+                TileRows{tl.row0 + r, tl.nrows - r < 16 ? tl.nrows - r : 16, tl.nrows > kSmallRows ? 1 : 0};
     }
 }
 

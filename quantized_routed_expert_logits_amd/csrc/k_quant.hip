@@ -12,21 +12,22 @@
 // wave reads 1 KiB of contiguous input per instruction.  Outputs per block:
 // the int8 codes and the scale.
 //
-// Prescale: the fp16 operand of the expert GEMMs, [rows][cols].  Two forms:
-//   parts = 1 (the down GEMM): fp16(q * s * 2^-e_r), 11 significant bits, so
-//     the per-block scale rides inside the MFMA.  A row r is first scaled by
+// Prescale: the fp16 operands of the expert GEMMs.  Two forms:
+//   the down GEMM: fp16(q * s * 2^-e_r), 11 significant bits, so the
+//     per-block scale rides inside the MFMA.  A row r is first scaled by
 //     2^-e_r, chosen so that the row's largest possible |q * s| (127 * max s)
 //     lands in [2^14, 2^15): fp16 cannot overflow and small values keep their
 //     bits.  The row multiplier 2^e_r is written beside the operand; the GEMM
 //     multiplies its fp32 results by it (exact).  The down output is not
-//     rounded to int8 again, so 11 bits suffice.
-//   parts = 0 (the gate/up GEMM): the codes q themselves (exact); the GEMM
+//     rounded to int8 again, so 11 bits suffice.  Written in the tiled layout
+//     (prescale_tiles_kernel).
+//   the gate/up GEMM: the codes q themselves (exact), [rows][cols]; the GEMM
 //     applies the block scales in fp32 after each block's products.
 //
-// The same kernel writes the operand of the GEMMs' offset pass: per block,
+// Both kernels write the operand of the GEMMs' offset pass: per block,
 // u = -0.5 * s * (sum of the block's codes) (the 2-bit weight offset's share,
 // see k_experts.hip), the row's u scaled by a power of two into (-1, 1) and
-// split hi/lo, in the parts = 2 layout over the block index (padded with
+// split hi/lo, in a hi 8 / lo 8 layout over the block index (padded with
 // zeros to a multiple of 32 blocks), plus that power of two.
 #include "internal.h"
 
@@ -78,9 +79,9 @@ __device__ __forceinline__ void split_hi_lo(float v, _Float16& hi, _Float16& lo)
 }
 
 // One wave per row: the row multiplier from the block scales, then 16 codes
-// per lane per step (16 contiguous bytes in, 32 or 64 contiguous bytes out);
-// the block sums go through LDS to the lanes that write the offset operand.
-template <int P>
+// per lane per step (16 contiguous bytes in, 32 contiguous bytes of fp16
+// codes out); the block sums go through LDS to the lanes that write the
+// offset operand.
 __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict__ q, const float* __restrict__ s,
                                                        int64_t rows, int32_t cols, _Float16* __restrict__ out,
                                                        float* __restrict__ mult, _Float16* __restrict__ uop,
@@ -93,20 +94,18 @@ __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict_
     const int nb = cols / kBlock;
     const int nch = (nb + 31) / 32;
     const float* srow = s + row * nb;
-    // the row multiplier 2^e (written for both forms when mult is given: the
-    // router takes the input rows' multipliers from here); parts 1 scales by
-    // its inverse
+    // the row multiplier 2^e, written when mult is given (the router takes the
+    // input rows' multipliers from here)
     float m = 0.0f;
     for (int b = lane; b < nb; b += 64) m = fmaxf(m, srow[b]);
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
     const float bound = 127.0f * m;  // >= every |q * s| of the row
-    float scale = 1.0f, back = 1.0f;
+    float back = 1.0f;
     if (bound > 0.0f) {
         int ex = 0;
-        frexpf(bound, &ex);          // bound in [2^(ex-1), 2^ex)
-        ex = ex < -96 ? -96 : ex;    // keeps 2^(15-ex) finite
-        scale = ldexpf(1.0f, 15 - ex);
+        frexpf(bound, &ex);        // bound in [2^(ex-1), 2^ex)
+        ex = ex < -96 ? -96 : ex;  // keeps 2^(ex-15) a normal float
         back = ldexpf(1.0f, ex - 15);
     }
     if (mult && lane == 0) mult[row] = back;
@@ -118,16 +117,13 @@ __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict_
         uint4 wv = make_uint4(0, 0, 0, 0);
         if (on) wv = *reinterpret_cast<const uint4*>(qrow + 16 * j);
         const float sraw = on ? srow[j >> 1] : 0.0f;
-        const float sj = sraw * scale;  // exact: a power-of-two scaling
         const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
-        float v[16];
         half8_t cq[2];
         int sum = 0;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int c = (int8_t)(ws[i >> 2] >> (8 * (i & 3)));
             sum += c;
-            v[i] = (float)c * sj;
             cq[i >> 3][i & 7] = (_Float16)c;  // exact: |c| <= 127
         }
         sum += __shfl_xor(sum, 1);  // lanes 2m, 2m+1 hold the two halves of one block
@@ -137,18 +133,8 @@ __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict_
             umax = fmaxf(umax, fabsf(u));
         }
         if (!on) continue;
-        half8_t* dst = reinterpret_cast<half8_t*>(out + row * cols + 16 * j);
-        if constexpr (P == 1) {
-            half8_t h0, h1;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                asm volatile("" : "+v"(v[i]), "+v"(v[8 + i]));
-                h0[i] = (_Float16)v[i];
-                h1[i] = (_Float16)v[8 + i];
-            }
-            dst[0] = h0;
-            dst[1] = h1;
-        } else {
+        if (out) {
+            half8_t* dst = reinterpret_cast<half8_t*>(out + row * cols + 16 * j);
             dst[0] = cq[0];
             dst[1] = cq[1];
         }
@@ -181,16 +167,18 @@ __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict_
     }
 }
 
-// prescale_kernel<1> for grouped rows, written in the tiled layout: one
-// workgroup per 16-row tile of the tile table.  The tile's rows are
+// The down operand of grouped rows in the tiled layout: q * s * 2^-e_r as
+// fp16, with 2^e_r the row multiplier (127 * the row's largest block scale
+// lies in [2^14, 2^15) after the scaling), plus the offset operand as
+// prescale_kernel builds it.  One workgroup per 16-row tile of the tile
+// table.  The tile's rows are
 // consecutive grouped rows: their codes and scales are read coalesced into
 // LDS, kStageCols columns at a time (rows padded by 8 bytes / 1 float against
 // bank conflicts), then lane 16 g + r of a wave takes tile row r, value group
 // g (8 codes) of a block, so each block's fragment is one contiguous 1 KiB
-// store; wave w takes blocks w, w + 4, ...  The per-row quantities
-// (multiplier from the block scales, offset operand from the block sums)
-// follow prescale_kernel's arithmetic exactly.  Wider rows than kStageCols
-// are staged twice (once per pass).
+// store; wave w takes blocks w, w + 4, ...  The per-row multiplier and
+// offset operand use prescale_kernel's arithmetic.  Wider rows than
+// kStageCols are staged twice (once per pass).
 constexpr int kStageCols = 2048;
 inline size_t prescale_tiles_lds_bytes(int32_t cols) {
     const int sc = cols < kStageCols ? cols : kStageCols;
@@ -216,15 +204,24 @@ __global__ void __launch_bounds__(256) prescale_tiles_kernel(const int8_t* __res
     const int qstride = sc + 8, sstride = sb + 1;
     float* sl = reinterpret_cast<float*>(lds + (size_t)16 * qstride);
     // columns [c0, c0 + sc) of the tile's rows into LDS; rows past nrows as zeros
-    auto stage = [&](int c0) {
+    auto stage = [&](int c0) {  // all of a thread's loads first, then its LDS stores
         const int pieces = sc / 16;
-        for (int i = tid; i < 16 * pieces; i += 256) {
-            const int rr = i / pieces, c = i - rr * pieces;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (rr < tr.nrows && c0 + 16 * c < cols)
-                v = *reinterpret_cast<const uint4*>(q + ((int64_t)tr.row0 + rr) * cols + c0 + 16 * c);
-            *reinterpret_cast<uint2*>(lds + rr * qstride + 16 * c) = make_uint2(v.x, v.y);
-            *reinterpret_cast<uint2*>(lds + rr * qstride + 16 * c + 8) = make_uint2(v.z, v.w);
+        constexpr int kPer = 16 * (kStageCols / 16) / 256;
+        uint4 v[kPer];
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int i = tid + 256 * k, rr = i / pieces, c = i - rr * pieces;
+            v[k] = make_uint4(0, 0, 0, 0);
+            if (i < 16 * pieces && rr < tr.nrows && c0 + 16 * c < cols)
+                v[k] = *reinterpret_cast<const uint4*>(q + ((int64_t)tr.row0 + rr) * cols + c0 + 16 * c);
+        }
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int i = tid + 256 * k, rr = i / pieces, c = i - rr * pieces;
+            if (i < 16 * pieces) {
+                *reinterpret_cast<uint2*>(lds + rr * qstride + 16 * c) = make_uint2(v[k].x, v[k].y);
+                *reinterpret_cast<uint2*>(lds + rr * qstride + 16 * c + 8) = make_uint2(v[k].z, v[k].w);
+            }
         }
         for (int i = tid; i < 16 * sb; i += 256) {
             const int rr = i / sb, b = i - rr * sb, bg = c0 / kBlock + b;
@@ -317,8 +314,79 @@ __global__ void __launch_bounds__(256) prescale_tiles_kernel(const int8_t* __res
     }
 }
 
+// The 4-wave gate/up kernel's operand in the tiled layout: tile t of the
+// tile table (if its chunk is big) holds grouped rows trows[t], each the
+// token src[row]; its int8
+// codes become fp16 (exact) in [tile][block][group g][row within the tile][8]
+// and its block scales [tile][block / 4][row within the tile][4] (one 16-byte
+// load per lane and 4 blocks).  One workgroup per tile: the 16 token rows'
+// codes are staged in LDS with coalesced loads (kStageCols columns at a time,
+// rows padded by 8 bytes), then lane 16 g + r of a wave writes row r, group
+// g of a block, so each block's fragment is one contiguous 1 KiB store; wave
+// w takes blocks w, w + 4, ...  Rows past a tile's nrows are zeros.
+constexpr int kGatherCols = 2560;                         // columns staged per slice
+constexpr int kGatherPer = 16 * (kGatherCols / 16) / 256;  // 16-byte pieces per thread and slice
+inline size_t gather_tiles_lds_bytes(int32_t cols) {
+    const int sc = cols < kGatherCols ? cols : kGatherCols;
+    return (size_t)16 * (sc + 8);
+}
+
+__global__ void __launch_bounds__(256) gather_tiles_kernel(const int8_t* __restrict__ q, const float* __restrict__ s,
+                                                           const int32_t* __restrict__ src,
+                                                           const TileRows* __restrict__ trows,
+                                                           const int32_t* __restrict__ ntiles, int32_t cols,
+                                                           _Float16* __restrict__ out, float* __restrict__ sout) {
+    extern __shared__ __align__(16) unsigned char lds[];  // codes [16][sc + 8]
+    const int64_t t = blockIdx.x;
+    if (t >= *ntiles) return;  // uniform over the workgroup, before any barrier
+    const TileRows tr = trows[t];
+    if (!tr.big) return;  // the small-chunk kernel reads its rows in place
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+    const int nb = cols / kBlock;
+    const int sc = cols < kGatherCols ? cols : kGatherCols, sb = sc / kBlock, qstride = sc + 8;
+    // block scales: thread i takes row i / (nb / 4), 4-block group i % (nb / 4)
+    const int nq = nb / 4;
+    for (int i = tid; i < 16 * nq; i += 256) {
+        const int rr = i / nq, qb = i - rr * nq;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (rr < tr.nrows) v = *reinterpret_cast<const float4*>(s + (int64_t)src[tr.row0 + rr] * nb + 4 * qb);
+        *reinterpret_cast<float4*>(sout + ((t * nq + qb) * 16 + rr) * 4) = v;
+    }
+    half8_t* tile = reinterpret_cast<half8_t*>(out) + t * nb * 64;
+    for (int c0 = 0; c0 < cols; c0 += sc) {
+        if (c0 > 0) __syncthreads();  // the previous slice is read
+        // all of a thread's loads first, then its LDS stores
+        const int pieces = sc / 16;
+        uint4 v[kGatherPer];
+#pragma unroll
+        for (int k = 0; k < kGatherPer; ++k) {
+            const int i = tid + 256 * k, rr = i / pieces, c = i - rr * pieces;
+            v[k] = make_uint4(0, 0, 0, 0);
+            if (i < 16 * pieces && rr < tr.nrows && c0 + 16 * c < cols)
+                v[k] = *reinterpret_cast<const uint4*>(q + (int64_t)src[tr.row0 + rr] * cols + c0 + 16 * c);
+        }
+#pragma unroll
+        for (int k = 0; k < kGatherPer; ++k) {
+            const int i = tid + 256 * k, rr = i / pieces, c = i - rr * pieces;
+            if (i < 16 * pieces) {
+                *reinterpret_cast<uint2*>(lds + rr * qstride + 16 * c) = make_uint2(v[k].x, v[k].y);
+                *reinterpret_cast<uint2*>(lds + rr * qstride + 16 * c + 8) = make_uint2(v[k].z, v[k].w);
+            }
+        }
+        __syncthreads();
+        const int b1 = (cols - c0) / kBlock < sb ? (cols - c0) / kBlock : sb;
+        for (int b = w; b < b1; b += 4) {
+            const uint2 c8 = *reinterpret_cast<const uint2*>(lds + r * qstride + kBlock * b + 8 * g);
+            half8_t h;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) h[i] = (_Float16)(int8_t)((i < 4 ? c8.x : c8.y) >> (8 * (i & 3)));  // exact
+            tile[(c0 / kBlock + b) * 64 + lane] = h;
+        }
+    }
+}
+
 // The layer input in one pass: quantize_kernel's int8 codes and scales and
-// prescale_kernel<0>'s outputs (fp16 codes, row multiplier, offset operand)
+// prescale_kernel's outputs (fp16 codes, row multiplier, offset operand)
 // from the fp32 rows, one wave per row.  Lane pairs own a 32-value block, 16
 // values each (four float4 loads: the wave reads 4 KiB of the row per step);
 // the arithmetic of each output is that of the two separate kernels.
@@ -366,9 +434,11 @@ __global__ void __launch_bounds__(256) quantize_prescale_kernel(const float* __r
         if (!on) continue;
         smax = fmaxf(smax, s);
         *reinterpret_cast<uint4*>(q8 + row * cols + 16 * j) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-        half8_t* dst = reinterpret_cast<half8_t*>(out + row * cols + 16 * j);
-        dst[0] = cq[0];
-        dst[1] = cq[1];
+        if (out) {
+            half8_t* dst = reinterpret_cast<half8_t*>(out + row * cols + 16 * j);
+            dst[0] = cq[0];
+            dst[1] = cq[1];
+        }
         if ((j & 1) == 0) {
             s_out[row * nb + (j >> 1)] = s;
             const float u = -0.5f * s * (float)sum;
@@ -434,16 +504,19 @@ hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q
     return hipGetLastError();
 }
 
-hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_t cols, int parts, _Float16* out,
-                           float* mult, _Float16* uop, float* umult, hipStream_t st) {
-    if (rows > 0) {
-        if (parts == 0)
-            hipLaunchKernelGGL(prescale_kernel<0>, dim3(grid_for(rows, 4)), dim3(256), 0, st, q, s, rows, cols, out,
-                               mult, uop, umult);
-        else
-            hipLaunchKernelGGL(prescale_kernel<1>, dim3(grid_for(rows, 4)), dim3(256), 0, st, q, s, rows, cols, out,
-                               mult, uop, umult);
-    }
+hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_t cols, _Float16* out, float* mult,
+                           _Float16* uop, float* umult, hipStream_t st) {
+    if (rows > 0)
+        hipLaunchKernelGGL(prescale_kernel, dim3(grid_for(rows, 4)), dim3(256), 0, st, q, s, rows, cols, out, mult,
+                           uop, umult);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_tiles(const int8_t* q, const float* s, const int32_t* src, const ChunkLists& cl,
+                               int64_t tiles_cap, int32_t cols, _Float16* out, float* sout, hipStream_t st) {
+    if (tiles_cap > 0)
+        hipLaunchKernelGGL(gather_tiles_kernel, dim3((unsigned)tiles_cap), dim3(256), gather_tiles_lds_bytes(cols), st,
+                           q, s, src, cl.trows, cl.sched + 2, cols, out, sout);
     return hipGetLastError();
 }
 

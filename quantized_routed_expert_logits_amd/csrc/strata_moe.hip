@@ -125,7 +125,9 @@ struct Buffers {
     float* p;
     int8_t* xq;
     float* xs;
-    _Float16* xa;
+    _Float16* xa;  // the input codes as fp16 [T][H] (small-chunk gate/up kernel)
+    _Float16* xt;  // tiled gate/up operand of big chunks' rows: fp16 codes
+    float* xst;    // and their tiled block scales
     float* xe;
     _Float16* xuop;
     float* xum;
@@ -150,7 +152,7 @@ struct Buffers {
 };
 
 struct Offsets {
-    size_t logits, wt, wb, wm, pmax, amb, sel, ids, p, xq, xs, xa, xe, xuop, xum, hist, base, offsets, tiles, ntiles, err, src, slot, prow, hq, hs,
+    size_t logits, wt, wb, wm, pmax, amb, sel, ids, p, xq, xs, xa, xt, xst, xe, xuop, xum, hist, base, offsets, tiles, ntiles, err, src, slot, prow, hq, hs,
         trows, hb, he, huop, hum, dm, total;
     int64_t tiles_cap;
 };
@@ -172,7 +174,6 @@ Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I) {
     o.p = L.take<float>(n);
     o.xq = L.take<int8_t>(T * H);
     o.xs = L.take<float>(T * (H / kBlock));
-    o.xa = L.take<_Float16>(T * H);
     o.xe = L.take<float>(T);
     o.xuop = L.take<_Float16>(T * offset_operand_halves(H));
     o.xum = L.take<float>(T);
@@ -188,6 +189,9 @@ Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I) {
     o.hq = L.take<int8_t>(n * I);
     o.hs = L.take<float>(n * (I / kBlock));
     o.trows = L.take<TileRows>(tiled_rows_cap(n, E) / 16);
+    o.xa = L.take<_Float16>(T * H);
+    o.xt = L.take<_Float16>(tiled_rows_cap(n, E) * H);
+    o.xst = L.take<float>(tiled_rows_cap(n, E) * (H / kBlock));
     o.hb = L.take<_Float16>(tiled_rows_cap(n, E) * I);
     o.he = L.take<float>(n);
     o.huop = L.take<_Float16>(n * offset_operand_halves(I));
@@ -211,6 +215,8 @@ Buffers carve(char* ws, const Offsets& o) {
     b.xq = (int8_t*)(ws + o.xq);
     b.xs = (float*)(ws + o.xs);
     b.xa = (_Float16*)(ws + o.xa);
+    b.xt = (_Float16*)(ws + o.xt);
+    b.xst = (float*)(ws + o.xst);
     b.xe = (float*)(ws + o.xe);
     b.xuop = (_Float16*)(ws + o.xuop);
     b.xum = (float*)(ws + o.xum);
@@ -304,11 +310,12 @@ int check_experts(const strata_moe_experts* ex) {
     return 0;
 }
 
-// The GEMMs address activations with 32-bit buffer offsets: the input's fp16
-// codes ([T][H]) and the tiled H operand (T*K rows and up to 15 padding rows
-// per expert, [.][I] fp16) must each stay below 2 GiB.
+// The GEMMs address activations with 32-bit buffer offsets: their tiled
+// operands (T*K rows and up to 15 padding rows per expert, [.][H] and [.][I]
+// fp16) must each stay below 2 GiB; so must x.
 int check_buffers(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I) {
-    if (T * (int64_t)H * 4 >= ((int64_t)1 << 31) || tiled_rows_cap(T * K, E) * I * 2 >= ((int64_t)1 << 31))
+    const int64_t rows = tiled_rows_cap(T * K, E), lim = (int64_t)1 << 31;
+    if (T * (int64_t)H * 4 >= lim || rows * H * 2 >= lim || rows * I * 2 >= lim)
         return fail(STRATA_MOE_EINVAL, "T = %lld too large for one call at H = %d, I = %d, K = %d", (long long)T, H, I,
                     K);
     return 0;
@@ -365,10 +372,13 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     const ChunkLists cl{b.tiles, b.ntiles, b.tiles_cap, b.trows};
     HIP_TRY(launch_group(b.ids, b.p, n, K, E, b.hist, b.base, b.offsets, cl, b.src, b.slot, b.prow, b.err, st),
             "group launch");
+    // the big chunks' input codes and scales, gathered into the tiled layout
+    HIP_TRY(launch_gather_tiles(b.xq, b.xs, b.src, cl, tiled_rows_cap(n, E) / 16, H, b.xt, b.xst, st),
+            "gather launch");
     tm.end(kGroup);
     tm.begin(kGateUp);
-    HIP_TRY(launch_gate_up((const uint8_t*)ex->gate_up, ex->gate_up_stride, cl, n, E, b.src, b.xa, b.xs, T, b.xuop,
-                           b.xum, H, I, b.hq, b.hs, st),
+    HIP_TRY(launch_gate_up((const uint8_t*)ex->gate_up, ex->gate_up_stride, cl, n, E, b.src, b.xt, b.xst,
+                           tiled_rows_cap(n, E), b.xa, b.xs, T, b.xuop, b.xum, H, I, b.hq, b.hs, st),
             "gate/up launch");
     tm.end(kGateUp);
     tm.begin(kPrescaleH);
@@ -631,7 +641,8 @@ int strata_moe_gate_up(const int8_t* qx, const float* sx, const int32_t* offsets
     const int32_t E = experts->n_expert, H = experts->hidden, I = experts->ffn;
     const int64_t n = T * K;
     Layout L;
-    const size_t o_xa = L.take<_Float16>(T * H);
+    const size_t o_xa = L.take<_Float16>(T * H), o_xt = L.take<_Float16>(tiled_rows_cap(n, E) * H);
+    const size_t o_xst = L.take<float>(tiled_rows_cap(n, E) * (H / kBlock));
     const size_t o_xuop = L.take<_Float16>(T * offset_operand_halves(H)), o_xum = L.take<float>(T);
     const int64_t cap = chunk_list_cap(n, E);
     const size_t o_tiles = L.take<Tile>(2 * cap), o_nt = L.take<int32_t>(kSchedInts),
@@ -640,12 +651,15 @@ int strata_moe_gate_up(const int8_t* qx, const float* sx, const int32_t* offsets
     TRY(get_workspace(L.off, &ws));
     const ChunkLists cl{(Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), cap, (TileRows*)(ws + o_trows)};
     _Float16* xa = (_Float16*)(ws + o_xa);
+    _Float16* xt = (_Float16*)(ws + o_xt);
+    float* xst = (float*)(ws + o_xst);
     _Float16* xuop = (_Float16*)(ws + o_xuop);
     float* xum = (float*)(ws + o_xum);
-    HIP_TRY(launch_prescale(qx, sx, T, H, 0, xa, nullptr, xuop, xum, st), "prescale launch");
-    HIP_TRY(launch_chunks_from_offsets(offsets, E, n, cl, st), "chunk list launch");
-    HIP_TRY(launch_gate_up((const uint8_t*)experts->gate_up, experts->gate_up_stride, cl, n, E, src, xa, sx, T, xuop,
-                           xum, H, I, qh, sh, st),
+    HIP_TRY(launch_prescale(qx, sx, T, H, xa, nullptr, xuop, xum, st), "prescale launch");
+    HIP_TRY(launch_chunks_from_offsets(offsets, E, n, cl, st), "chunk list launch");  // and the tile table
+    HIP_TRY(launch_gather_tiles(qx, sx, src, cl, tiled_rows_cap(n, E) / 16, H, xt, xst, st), "gather launch");
+    HIP_TRY(launch_gate_up((const uint8_t*)experts->gate_up, experts->gate_up_stride, cl, n, E, src, xt, xst,
+                           tiled_rows_cap(n, E), xa, sx, T, xuop, xum, H, I, qh, sh, st),
             "gate/up launch");
     return 0;
 }
