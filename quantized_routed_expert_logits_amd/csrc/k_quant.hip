@@ -316,16 +316,16 @@ __global__ void __launch_bounds__(256) prescale_tiles_kernel(const int8_t* __res
 
 // The 4-wave gate/up kernel's operand in the tiled layout: tile t of the
 // tile table (if its chunk is big) holds grouped rows trows[t], each the
-// token src[row]; its int8
-// codes become fp16 (exact) in [tile][block][group g][row within the tile][8]
-// and its block scales [tile][block / 4][row within the tile][4] (one 16-byte
-// load per lane and 4 blocks).  One workgroup per tile: the 16 token rows'
-// codes are staged in LDS with coalesced loads (kStageCols columns at a time,
-// rows padded by 8 bytes), then lane 16 g + r of a wave writes row r, group
-// g of a block, so each block's fragment is one contiguous 1 KiB store; wave
-// w takes blocks w, w + 4, ...  Rows past a tile's nrows are zeros.
-constexpr int kGatherCols = 2560;                         // columns staged per slice
-constexpr int kGatherPer = 16 * (kGatherCols / 16) / 256;  // 16-byte pieces per thread and slice
+// token src[row]; its int8 codes become fp16 (exact) in [tile][block][group
+// g][row within the tile][8] and its block scales [tile][block / 4][row
+// within the tile][4] (one 16-byte load per lane and 4 blocks).  One
+// workgroup per tile and slice of kGatherCols columns (grid y): the 16 token
+// rows' codes of the slice are staged in LDS with coalesced loads (rows
+// padded by 8 bytes), then lane 16 g + r of a wave writes row r, group g of
+// a block, so each block's fragment is one contiguous 1 KiB store; wave w
+// takes blocks w, w + 4, ...  Rows past a tile's nrows are zeros.
+constexpr int kGatherCols = 640;                               // columns per slice (20 blocks, 5 scale groups)
+constexpr int kGatherPer = (16 * (kGatherCols / 16) + 255) / 256;  // 16-byte pieces per thread
 inline size_t gather_tiles_lds_bytes(int32_t cols) {
     const int sc = cols < kGatherCols ? cols : kGatherCols;
     return (size_t)16 * (sc + 8);
@@ -343,45 +343,44 @@ __global__ void __launch_bounds__(256) gather_tiles_kernel(const int8_t* __restr
     if (!tr.big) return;  // the small-chunk kernel reads its rows in place
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
     const int nb = cols / kBlock;
-    const int sc = cols < kGatherCols ? cols : kGatherCols, sb = sc / kBlock, qstride = sc + 8;
-    // block scales: thread i takes row i / (nb / 4), 4-block group i % (nb / 4)
-    const int nq = nb / 4;
-    for (int i = tid; i < 16 * nq; i += 256) {
-        const int rr = i / nq, qb = i - rr * nq;
+    const int sc = cols < kGatherCols ? cols : kGatherCols, qstride = sc + 8;
+    const int c0 = blockIdx.y * sc;                                     // the slice's first column
+    const int b0 = c0 / kBlock, b1 = (cols - c0 < sc ? cols - c0 : sc) / kBlock;  // its blocks [b0, b0 + b1)
+    // block scales of the slice's 4-block groups: thread i takes row i / ng, group i % ng
+    const int nq = nb / 4, ng = (b1 + 3) / 4;
+    for (int i = tid; i < 16 * ng; i += 256) {
+        const int rr = i / ng, qb = b0 / 4 + i - rr * ng;
+        if (qb >= nq) continue;
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
         if (rr < tr.nrows) v = *reinterpret_cast<const float4*>(s + (int64_t)src[tr.row0 + rr] * nb + 4 * qb);
         *reinterpret_cast<float4*>(sout + ((t * nq + qb) * 16 + rr) * 4) = v;
     }
+    // all of a thread's loads first, then its LDS stores
+    const int pieces = sc / 16;
+    uint4 v[kGatherPer];
+#pragma unroll
+    for (int k = 0; k < kGatherPer; ++k) {
+        const int i = tid + 256 * k, rr = i / pieces, c = i - rr * pieces;
+        v[k] = make_uint4(0, 0, 0, 0);
+        if (i < 16 * pieces && rr < tr.nrows && c0 + 16 * c < cols)
+            v[k] = *reinterpret_cast<const uint4*>(q + (int64_t)src[tr.row0 + rr] * cols + c0 + 16 * c);
+    }
+#pragma unroll
+    for (int k = 0; k < kGatherPer; ++k) {
+        const int i = tid + 256 * k, rr = i / pieces, c = i - rr * pieces;
+        if (i < 16 * pieces) {
+            *reinterpret_cast<uint2*>(lds + rr * qstride + 16 * c) = make_uint2(v[k].x, v[k].y);
+            *reinterpret_cast<uint2*>(lds + rr * qstride + 16 * c + 8) = make_uint2(v[k].z, v[k].w);
+        }
+    }
+    __syncthreads();
     half8_t* tile = reinterpret_cast<half8_t*>(out) + t * nb * 64;
-    for (int c0 = 0; c0 < cols; c0 += sc) {
-        if (c0 > 0) __syncthreads();  // the previous slice is read
-        // all of a thread's loads first, then its LDS stores
-        const int pieces = sc / 16;
-        uint4 v[kGatherPer];
+    for (int b = w; b < b1; b += 4) {
+        const uint2 c8 = *reinterpret_cast<const uint2*>(lds + r * qstride + kBlock * b + 8 * g);
+        half8_t h;
 #pragma unroll
-        for (int k = 0; k < kGatherPer; ++k) {
-            const int i = tid + 256 * k, rr = i / pieces, c = i - rr * pieces;
-            v[k] = make_uint4(0, 0, 0, 0);
-            if (i < 16 * pieces && rr < tr.nrows && c0 + 16 * c < cols)
-                v[k] = *reinterpret_cast<const uint4*>(q + (int64_t)src[tr.row0 + rr] * cols + c0 + 16 * c);
-        }
-#pragma unroll
-        for (int k = 0; k < kGatherPer; ++k) {
-            const int i = tid + 256 * k, rr = i / pieces, c = i - rr * pieces;
-            if (i < 16 * pieces) {
-                *reinterpret_cast<uint2*>(lds + rr * qstride + 16 * c) = make_uint2(v[k].x, v[k].y);
-                *reinterpret_cast<uint2*>(lds + rr * qstride + 16 * c + 8) = make_uint2(v[k].z, v[k].w);
-            }
-        }
-        __syncthreads();
-        const int b1 = (cols - c0) / kBlock < sb ? (cols - c0) / kBlock : sb;
-        for (int b = w; b < b1; b += 4) {
-            const uint2 c8 = *reinterpret_cast<const uint2*>(lds + r * qstride + kBlock * b + 8 * g);
-            half8_t h;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) h[i] = (_Float16)(int8_t)((i < 4 ? c8.x : c8.y) >> (8 * (i & 3)));  // exact
-            tile[(c0 / kBlock + b) * 64 + lane] = h;
-        }
+        for (int i = 0; i < 8; ++i) h[i] = (_Float16)(int8_t)((i < 4 ? c8.x : c8.y) >> (8 * (i & 3)));  // exact
+        tile[(b0 + b) * 64 + lane] = h;
     }
 }
 
@@ -515,8 +514,9 @@ hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_
 hipError_t launch_gather_tiles(const int8_t* q, const float* s, const int32_t* src, const ChunkLists& cl,
                                int64_t tiles_cap, int32_t cols, _Float16* out, float* sout, hipStream_t st) {
     if (tiles_cap > 0)
-        hipLaunchKernelGGL(gather_tiles_kernel, dim3((unsigned)tiles_cap), dim3(256), gather_tiles_lds_bytes(cols), st,
-                           q, s, src, cl.trows, cl.sched + 2, cols, out, sout);
+        hipLaunchKernelGGL(gather_tiles_kernel,
+                           dim3((unsigned)tiles_cap, (unsigned)((cols + kGatherCols - 1) / kGatherCols)), dim3(256),
+                           gather_tiles_lds_bytes(cols), st, q, s, src, cl.trows, cl.sched + 2, cols, out, sout);
     return hipGetLastError();
 }
 
