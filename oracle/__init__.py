@@ -57,9 +57,9 @@ def _load():
     lib.oracle_group.argtypes = [P, i64, i32, i32, P, P, P]
     lib.oracle_group.restype = ctypes.c_int
     lib.oracle_quantize.argtypes = [P, i64, i32, P, P]
-    lib.oracle_expert_rows.argtypes = [P, P, P, P, i32, i32, i64, P, P, P, P, P, P]
+    lib.oracle_expert_rows.argtypes = [P, P, P, P, i32, i32, ctypes.c_double, i64, P, P, P, P, P, P]
     lib.oracle_combine.argtypes = [P, P, P, i64, i32, i32, P]
-    lib.oracle_rows_multi.argtypes = [P, P, P, P, P, i32, i32, i64, P, P, P, P, P]
+    lib.oracle_rows_multi.argtypes = [P, P, P, P, P, i32, i32, ctypes.c_double, i64, P, P, P, P, P]
     lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_half_to_double.restype = ctypes.c_double
     lib.oracle_num_threads.restype = ctypes.c_int
@@ -130,11 +130,19 @@ def quantize(v):
     return q, s
 
 
-def expert_rows(ex, qx, sx, want_h: bool = False):
+def code_zero(fmt: str) -> float:
+    """The 2-bit map's offset z in w = d * (q - z): 1.5 for the symmetric map,
+    1 for the pages' Q2_0 packs (Strata compare page, moe_fused.hpp header
+    comment)."""
+    return {"q2_sym": 1.5, "q2_0": 1.0}[fmt]
+
+
+def expert_rows(ex, qx, sx, want_h: bool = False, fmt: str = "q2_sym"):
     """c5..c7 for one expert's routed rows.
 
     ex: an object with codes_gu [2I][H], scales_gu, codes_d [H][I], scales_d
-    (``synthetic.Expert``).  Returns (h or None, qh, sh, D)."""
+    (``synthetic.Expert``); fmt: the weight map (code_zero).  Returns
+    (h or None, qh, sh, D)."""
     cgu = _c(ex.codes_gu, np.uint8)
     sgu = _c(ex.scales_gu, np.uint16)
     cd = _c(ex.codes_d, np.uint8)
@@ -149,7 +157,7 @@ def expert_rows(ex, qx, sx, want_h: bool = False):
     sh = np.empty((n, I // BLOCK), np.float32)
     D = np.empty((n, H), np.float64)
     if n:
-        _load().oracle_expert_rows(_p(cgu), _p(sgu), _p(cd), _p(sd), H, I, n, _p(qx), _p(sx),
+        _load().oracle_expert_rows(_p(cgu), _p(sgu), _p(cd), _p(sd), H, I, code_zero(fmt), n, _p(qx), _p(sx),
                                    _p(h), _p(qh), _p(sh), _p(D))
     return h, qh, sh, D
 
@@ -166,7 +174,7 @@ def combine(D, p, slot):
     return y
 
 
-def layer(x, wr, bias, get_expert, E: int, K: int, want_h: bool = False) -> dict:
+def layer(x, wr, bias, get_expert, E: int, K: int, want_h: bool = False, fmt: str = "q2_sym") -> dict:
     """The whole layer on every token, all intermediates returned.
 
     get_expert(e) returns expert e's canonical arrays.  Steps in the pages'
@@ -190,7 +198,7 @@ def layer(x, wr, bias, get_expert, E: int, K: int, want_h: bool = False) -> dict
         if r1 == r0:
             continue
         rows = src[r0:r1]
-        he, qhe, she, De = expert_rows(get_expert(e), qx[rows], sx[rows], want_h)
+        he, qhe, she, De = expert_rows(get_expert(e), qx[rows], sx[rows], want_h, fmt)
         qh[r0:r1], sh[r0:r1], D[r0:r1] = qhe, she, De
         if want_h:
             h[r0:r1] = he
@@ -199,7 +207,7 @@ def layer(x, wr, bias, get_expert, E: int, K: int, want_h: bool = False) -> dict
                 qh=qh, sh=sh, h=h, D=D, y=y)
 
 
-def rows_multi(experts: list, which, qx, sx):
+def rows_multi(experts: list, which, qx, sx, fmt: str = "q2_sym"):
     """c5..c7 for rows of several experts: row r goes through experts[which[r]].
     Returns (qh, sh, D)."""
     keep = [(_c(e.codes_gu, np.uint8), _c(e.scales_gu, np.uint16), _c(e.codes_d, np.uint8),
@@ -215,12 +223,13 @@ def rows_multi(experts: list, which, qx, sx):
     sh = np.empty((n, I // BLOCK), np.float32)
     D = np.empty((n, H), np.float64)
     if n:
-        _load().oracle_rows_multi(tables[0], tables[1], tables[2], tables[3], _p(which), H, I, n, _p(qx), _p(sx),
+        _load().oracle_rows_multi(tables[0], tables[1], tables[2], tables[3], _p(which), H, I, code_zero(fmt), n,
+                                  _p(qx), _p(sx),
                                   _p(qh), _p(sh), _p(D))
     return qh, sh, D
 
 
-def layer_tokens(x, wr, bias, get_expert, K: int, tokens) -> dict:
+def layer_tokens(x, wr, bias, get_expert, K: int, tokens, fmt: str = "q2_sym") -> dict:
     """The layer's output for a sample of tokens only.
 
     Every step of the layer is independent across tokens except the grouping,
@@ -240,7 +249,7 @@ def layer_tokens(x, wr, bias, get_expert, K: int, tokens) -> dict:
     which = np.array([slot_of[int(e)] for e in ids.reshape(-1)], np.int32)
     # pairs token-major: row s*K + k is token s through its k-th expert
     rows = np.repeat(np.arange(S), K)
-    qh, sh, D = rows_multi([get_expert(e) for e in used], which, qx[rows], sx[rows])
+    qh, sh, D = rows_multi([get_expert(e) for e in used], which, qx[rows], sx[rows], fmt)
     I = qh.shape[1]
     # c8 with the pairs laid out token-major: row s*K + k holds D of (s, k)
     y = combine(D, p, np.arange(S * K, dtype=np.int32))

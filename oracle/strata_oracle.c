@@ -206,12 +206,13 @@ void oracle_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q, floa
 /* ----------------------------------------- c5..c7 one expert's routed rows
  * [moe_fused] per routed row (token t of expert e): gate and up from the int8
  * activations of t, SwiGLU, H rounded to int8 per 32 values, then down.
- * With the 2-bit map w = d*(q - 1.5):
- *   G[j] = sum_b dg[j][b] * sx[b] * sum_{i in b} (qg[j][i] - 1.5) * qx[i]
+ * With the 2-bit map w = d*(q - z), z = 1.5 (the symmetric map) or z = 1
+ * (the pages' Q2_0 packs, moe_fused.hpp header comment):
+ *   G[j] = sum_b dg[j][b] * sx[b] * sum_{i in b} (qg[j][i] - z) * qx[i]
  *   U[j] likewise with the up rows (rows I + j of the stacked gate/up matrix)
  *   h[j] = G[j] / (1 + exp(-G[j])) * U[j]            (SwiGLU = silu(gate)*up)
  *   qh, sh = the int8 rounding of RN32(h) per 32 values along I (as c4)
- *   D[o] = sum_b dd[o][b] * sh[b] * sum_{i in b} (qd[o][i] - 1.5) * qh[i]
+ *   D[o] = sum_b dd[o][b] * sh[b] * sum_{i in b} (qd[o][i] - z) * qh[i]
  * Each per-block term is exact in double (a half-integer below 2^13 times an
  * 11-bit and a 24-bit significand); only the sums over blocks round.
  * Inputs: one expert's canonical arrays cgu [2I][H] (uint8 codes), sgu
@@ -219,8 +220,8 @@ void oracle_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q, floa
  * qx [nrows][H], sx [nrows][H/32].  Outputs (any may be NULL except D):
  * h [nrows][I] double, qh [nrows][I], sh [nrows][I/32], D [nrows][H] double. */
 void oracle_expert_rows(const uint8_t* cgu, const uint16_t* sgu, const uint8_t* cd, const uint16_t* sd,
-                        int32_t H, int32_t I, int64_t nrows, const int8_t* qx, const float* sx, double* h_out,
-                        int8_t* qh_out, float* sh_out, double* D) {
+                        int32_t H, int32_t I, double z, int64_t nrows, const int8_t* qx, const float* sx,
+                        double* h_out, int8_t* qh_out, float* sh_out, double* D) {
     const int32_t nbh = H / QBLOCK, nbi = I / QBLOCK;
 #pragma omp parallel
     {
@@ -237,8 +238,8 @@ void oracle_expert_rows(const uint8_t* cgu, const uint16_t* sgu, const uint8_t* 
                 for (int32_t b = 0; b < nbh; ++b) {
                     double ig = 0.0, iu = 0.0;
                     for (int32_t i = b * QBLOCK; i < (b + 1) * QBLOCK; ++i) {
-                        ig += ((double)cgu[(int64_t)j * H + i] - 1.5) * (double)xr[i];
-                        iu += ((double)cgu[(int64_t)(I + j) * H + i] - 1.5) * (double)xr[i];
+                        ig += ((double)cgu[(int64_t)j * H + i] - z) * (double)xr[i];
+                        iu += ((double)cgu[(int64_t)(I + j) * H + i] - z) * (double)xr[i];
                     }
                     G += half_bits_to_double(sgu[(int64_t)j * nbh + b]) * (double)sxr[b] * ig;
                     U += half_bits_to_double(sgu[(int64_t)(I + j) * nbh + b]) * (double)sxr[b] * iu;
@@ -252,7 +253,7 @@ void oracle_expert_rows(const uint8_t* cgu, const uint16_t* sgu, const uint8_t* 
                 for (int32_t b = 0; b < nbi; ++b) {
                     double id = 0.0;
                     for (int32_t i = b * QBLOCK; i < (b + 1) * QBLOCK; ++i)
-                        id += ((double)cd[(int64_t)o * I + i] - 1.5) * (double)qh[i];
+                        id += ((double)cd[(int64_t)o * I + i] - z) * (double)qh[i];
                     acc += half_bits_to_double(sd[(int64_t)o * nbi + b]) * (double)sh[b] * id;
                 }
                 D[r * H + o] = acc;
@@ -272,12 +273,12 @@ void oracle_expert_rows(const uint8_t* cgu, const uint16_t* sgu, const uint8_t* 
  * pointer tables (the same per-row computation as oracle_expert_rows, with
  * the loop over rows spread across threads). */
 void oracle_rows_multi(const uint8_t* const* cgu, const uint16_t* const* sgu, const uint8_t* const* cd,
-                       const uint16_t* const* sd, const int32_t* which, int32_t H, int32_t I, int64_t nrows,
-                       const int8_t* qx, const float* sx, int8_t* qh_out, float* sh_out, double* D) {
+                       const uint16_t* const* sd, const int32_t* which, int32_t H, int32_t I, double z,
+                       int64_t nrows, const int8_t* qx, const float* sx, int8_t* qh_out, float* sh_out, double* D) {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < nrows; ++r) {
         const int32_t w = which[r];
-        oracle_expert_rows(cgu[w], sgu[w], cd[w], sd[w], H, I, 1, qx + r * H, sx + r * (H / QBLOCK), NULL,
+        oracle_expert_rows(cgu[w], sgu[w], cd[w], sd[w], H, I, z, 1, qx + r * H, sx + r * (H / QBLOCK), NULL,
                            qh_out ? qh_out + r * I : NULL, sh_out ? sh_out + r * (I / QBLOCK) : NULL, D + r * H);
     }
 }

@@ -54,6 +54,7 @@ class LayerShape:
     K: int   # experts per token
     I: int   # expert FFN width
     skewed: bool = False  # add the Zipf router bias
+    fmt: str = "q2_sym"   # weight map label: "q2_sym" or "q2_0" (the pages' own packs)
 
     @property
     def n(self) -> int:
@@ -69,14 +70,21 @@ SHAPES = {
     "skewed_4k": LayerShape("skewed_4k", T=4096, H=2560, E=512, K=10, I=1024, skewed=True),
 }
 
+# The pages' own expert geometry and weight map (I = 640, Q2_0), at a 2048-token
+# chunk: a further check and benchmark of the same layer.
+EXTRA_SHAPES = {
+    "pages_q2_0_2k": LayerShape("pages_q2_0_2k", T=2048, H=2560, E=512, K=10, I=640, fmt="q2_0"),
+}
+
 
 def shape(name: str) -> LayerShape:
-    return SHAPES[name]
+    return SHAPES[name] if name in SHAPES else EXTRA_SHAPES[name]
 
 
-def custom(T: int, H: int, E: int, K: int, I: int, skewed: bool = False) -> LayerShape:
+def custom(T: int, H: int, E: int, K: int, I: int, skewed: bool = False, fmt: str = "q2_sym") -> LayerShape:
     """A layer of arbitrary (test) size."""
-    return LayerShape(f"T{T}_H{H}_E{E}_K{K}_I{I}" + ("_skew" if skewed else ""), T, H, E, K, I, skewed)
+    name = f"T{T}_H{H}_E{E}_K{K}_I{I}" + ("_skew" if skewed else "") + ("" if fmt == "q2_sym" else "_" + fmt)
+    return LayerShape(name, T, H, E, K, I, skewed, fmt)
 
 
 def _rng(*tag: int) -> np.random.Generator:

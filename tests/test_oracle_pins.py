@@ -257,23 +257,30 @@ def test_quantize_error_bound():
 
 
 # ------------------------------------------------------ c5..c8 experts, combine
-def _dense(ex):
-    """Independent dense dequantization: W = d * (q - 1.5) as float64 matrices."""
+# the 2-bit maps: w = d * (q - 1.5) (symmetric) and the pages' Q2_0 packs'
+# w = d * (q - 1) (Strata compare page, moe_fused.hpp header comment)
+ZERO = {"q2_sym": 1.5, "q2_0": 1.0}
+
+
+def _dense(ex, fmt="q2_sym"):
+    """Independent dense dequantization: W = d * (q - z) as float64 matrices."""
+    z = ZERO[fmt]
     I2, H = ex.codes_gu.shape
     d_gu = np.repeat(ex.scales_gu.view(np.float16).astype(np.float64), 32, axis=1)
-    W_gu = d_gu * (ex.codes_gu.astype(np.float64) - 1.5)
+    W_gu = d_gu * (ex.codes_gu.astype(np.float64) - z)
     d_d = np.repeat(ex.scales_d.view(np.float16).astype(np.float64), 32, axis=1)
-    W_d = d_d * (ex.codes_d.astype(np.float64) - 1.5)
+    W_d = d_d * (ex.codes_d.astype(np.float64) - z)
     return W_gu[: I2 // 2], W_gu[I2 // 2:], W_d
 
 
-def test_expert_rows_match_dense_brute_force():
+@pytest.mark.parametrize("fmt", ["q2_sym", "q2_0"])
+def test_expert_rows_match_dense_brute_force(fmt):
     for s in [S.shape("tiny"), S.custom(T=4, H=64, E=4, K=2, I=32), S.custom(T=3, H=96, E=2, K=1, I=160)]:
         ex = S.expert(s, 1, seed=7)
         x = S.activations(s, 7)
         qx, sx = oracle.quantize(x)
-        h, qh, sh, D = oracle.expert_rows(ex, qx, sx, want_h=True)
-        Wg, Wu, Wd = _dense(ex)
+        h, qh, sh, D = oracle.expert_rows(ex, qx, sx, want_h=True, fmt=fmt)
+        Wg, Wu, Wd = _dense(ex, fmt)
         xd = qx.astype(np.float64) * np.repeat(sx.astype(np.float64), 32, axis=1)
         G, U = xd @ Wg.T, xd @ Wu.T
         h_ref = G / (1 + np.exp(-G)) * U
@@ -294,7 +301,7 @@ def test_silu_of_zero_and_zero_input():
     assert np.all(h == 0) and np.all(qh == 0) and np.all(sh == 0) and np.all(D == 0)
 
 
-def _layer_dense(x, wr, bias, exps, K):
+def _layer_dense(x, wr, bias, exps, K, fmt="q2_sym"):
     """Fully independent numpy layer: dense weights, per-token loop."""
     logits = x.astype(np.float64) @ wr.astype(np.float64)
     if bias is not None:
@@ -306,7 +313,7 @@ def _layer_dense(x, wr, bias, exps, K):
     p = w / w.sum(1, keepdims=True)
     qx, sx = oracle.quantize(x)
     xd = qx.astype(np.float64) * np.repeat(sx.astype(np.float64), 32, axis=1)
-    dense = [_dense(ex) for ex in exps]
+    dense = [_dense(ex, fmt) for ex in exps]
     y = np.zeros((T, H))
     for t in range(T):
         for k in range(K):
@@ -318,13 +325,13 @@ def _layer_dense(x, wr, bias, exps, K):
     return ids, p, y
 
 
-@pytest.mark.parametrize("skewed", [False, True])
-def test_layer_matches_independent_dense_layer(skewed):
-    s = S.custom(T=24, H=96, E=6, K=3, I=64, skewed=skewed)
+@pytest.mark.parametrize("skewed,fmt", [(False, "q2_sym"), (True, "q2_sym"), (False, "q2_0")])
+def test_layer_matches_independent_dense_layer(skewed, fmt):
+    s = S.custom(T=24, H=96, E=6, K=3, I=64, skewed=skewed, fmt=fmt)
     x, wr, bias = S.activations(s), S.router_weight(s), S.router_bias(s)
     exps = [S.expert(s, e) for e in range(s.E)]
-    out = oracle.layer(x, wr, bias, lambda e: exps[e], s.E, s.K)
-    ids, p, y = _layer_dense(x, wr, bias, exps, s.K)
+    out = oracle.layer(x, wr, bias, lambda e: exps[e], s.E, s.K, fmt=s.fmt)
+    ids, p, y = _layer_dense(x, wr, bias, exps, s.K, fmt)
     assert np.array_equal(out["ids"], ids)
     assert np.abs(out["p"] - p).max() < 1e-14
     assert np.abs(out["y"] - y).max() <= 1e-10 * np.abs(y).max()
@@ -374,3 +381,17 @@ def test_geometry_golden_matches_the_layer_shapes():
     for name in ("stream_all_1k", "chunk_8k", "long_32k", "skewed_4k"):
         s = S.shape(name)
         assert (s.H, s.K, s.E) == (g["hidden"], g["topk"], g["experts"])
+
+
+def test_q2_0_code_one_is_zero_weight():
+    """Under Q2_0, w = d * (q - 1): codes all 1 give zero weights, so the expert
+    output is exactly zero; under the symmetric map the same codes give
+    w = -d / 2, which is not."""
+    s = S.custom(T=5, H=64, E=1, K=1, I=32)
+    ex = S.expert(s, 0)
+    ones = S.Expert(np.ones_like(ex.codes_gu), ex.scales_gu, np.ones_like(ex.codes_d), ex.scales_d)
+    qx, sx = oracle.quantize(S.activations(s))
+    h, qh, sh, D = oracle.expert_rows(ones, qx, sx, want_h=True, fmt="q2_0")
+    assert np.all(h == 0) and np.all(qh == 0) and np.all(D == 0)
+    h_sym, _, _, _ = oracle.expert_rows(ones, qx, sx, want_h=True, fmt="q2_sym")
+    assert np.abs(h_sym).max() > 0
