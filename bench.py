@@ -103,7 +103,7 @@ def main() -> int:
     log(f"workload {s.name}: T={s.T} H={s.H} E={s.E} K={s.K} I={s.I}; generating and packing experts")
     t_gen = time.time()
     canon = {}
-    experts = qm.Experts(s.E, s.H, s.I, device=dev)
+    experts = qm.Experts(s.E, s.H, s.I, device=dev, fmt=s.fmt)
     chunk = 32
     for e0 in range(0, s.E, chunk):
         parts = [S.expert(s, e, args.seed) for e in range(e0, min(s.E, e0 + chunk))]
@@ -190,7 +190,7 @@ def main() -> int:
         tok = np.sort(rng.choice(s.T, min(args.cpu_tokens, s.T), replace=False))
         log(f"CPU oracle on {len(tok)} sampled tokens")
         t0 = time.perf_counter()
-        oracle.layer_tokens(x_np, wr_np, bias_np, lambda e: canon[e], s.K, tok)
+        oracle.layer_tokens(x_np, wr_np, bias_np, lambda e: canon[e], s.K, tok, fmt=s.fmt)
         dt = time.perf_counter() - t0
         cpu = {"value": round(len(tok) / dt, 2), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
                "sample": f"{len(tok)} random tokens of the {s.name} layer, full layer per token "
@@ -210,7 +210,8 @@ def main() -> int:
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": s.name, "T": s.T, "H": s.H, "E": s.E, "K": s.K, "I": s.I,
-                   "weights": "2-bit codes, fp16 scale per 32", "activations": "int8, fp32 scale per 32",
+                   "weights": "2-bit codes, fp16 scale per 32, " + ("w = d(q-1)" if s.fmt == "q2_0" else "w = d(q-1.5)"),
+                   "activations": "int8, fp32 scale per 32",
                    "router_matrix": "prepared per call" if args.router_per_call else "prepared once"},
         "kernel_ms": {k: round(v, 4) for k, v in kernel_ms.items()},
         "int8_ops_per_step": 2.0 * n * 3 * s.H * s.I,

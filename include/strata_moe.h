@@ -52,11 +52,15 @@ extern "C" {
 #define STRATA_MOE_EHIP (-4)         /* a HIP runtime call or launch failed */
 #define STRATA_MOE_EDATA (-5)        /* a routed expert id out of range (strata_moe_group) */
 
-/* Weight format: 2-bit codes q in {0,1,2,3} with one fp16 scale d per 32
- * consecutive codes along the reduction dimension; w = d * (q - 1.5).  The
- * pages' own Q2_0 packs use w = d * (q - 1) (moe_fused.hpp header comment);
- * this library's layer uses the symmetric map. */
+/* Weight formats: 2-bit codes q in {0,1,2,3} with one fp16 scale d per 32
+ * consecutive codes along the reduction dimension.
+ *   STRATA_MOE_Q2_SYM: w = d * (q - 1.5), the symmetric map.
+ *   STRATA_MOE_Q2_0:   w = d * (q - 1), the map of the pages' own Q2_0 packs
+ *                      (Strata compare page, moe_fused.hpp header comment).
+ * Both use the same packed layout (strata_moe_pack); the format only changes
+ * the arithmetic of the layer. */
 #define STRATA_MOE_Q2_SYM 1
+#define STRATA_MOE_Q2_0 2
 
 /* A layer's experts, resident in device memory.  The blobs are written by
  * strata_moe_pack() in the kernels' own layout (not a GGUF layout).
@@ -74,7 +78,7 @@ typedef struct strata_moe_experts {
     int32_t n_expert; /* E */
     int32_t hidden;   /* H */
     int32_t ffn;      /* I */
-    int32_t format;   /* STRATA_MOE_Q2_SYM */
+    int32_t format;   /* STRATA_MOE_Q2_SYM or STRATA_MOE_Q2_0 */
     const void* gate_up;
     int64_t gate_up_stride;
     const void* down;

@@ -24,7 +24,9 @@ EUNSUPPORTED = -2
 ENOMEM = -3
 EHIP = -4
 EDATA = -5
-Q2_SYM = 1
+Q2_SYM = 1  # w = d * (q - 1.5)
+Q2_0 = 2    # w = d * (q - 1), the pages' Q2_0 packs
+FORMATS = {"q2_sym": Q2_SYM, "q2_0": Q2_0}
 
 
 class StrataMoeError(RuntimeError):
@@ -163,8 +165,10 @@ class Experts:
     """A layer's packed experts in device memory (blobs owned by torch)."""
 
     def __init__(self, n_expert: int, hidden: int, ffn: int, router_bias: torch.Tensor | None = None,
-                 device: str | torch.device = "cuda"):
-        self.n_expert, self.hidden, self.ffn = n_expert, hidden, ffn
+                 device: str | torch.device = "cuda", fmt: str = "q2_sym"):
+        if fmt not in FORMATS:
+            raise ValueError(f"unknown weight format {fmt!r}; one of {sorted(FORMATS)}")
+        self.n_expert, self.hidden, self.ffn, self.format = n_expert, hidden, ffn, FORMATS[fmt]
         self.gate_up_stride, self.down_stride = strata_moe_packed_bytes(hidden, ffn)
         self.gate_up = torch.empty(n_expert * self.gate_up_stride, dtype=torch.uint8, device=device)
         self.down = torch.empty(n_expert * self.down_stride, dtype=torch.uint8, device=device)
@@ -174,7 +178,7 @@ class Experts:
         self._restruct()
 
     def _restruct(self):
-        self.struct = ExpertsStruct(self.n_expert, self.hidden, self.ffn, Q2_SYM, self.gate_up.data_ptr(),
+        self.struct = ExpertsStruct(self.n_expert, self.hidden, self.ffn, self.format, self.gate_up.data_ptr(),
                                     self.gate_up_stride, self.down.data_ptr(), self.down_stride,
                                     None if self.router_bias is None else self.router_bias.data_ptr(),
                                     None if self.router_prepared is None else self.router_prepared.data_ptr())

@@ -69,10 +69,12 @@ hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q
 // Per int8 row: the codes q themselves as fp16 (exact), [rows][cols], if out
 // is non-null; the row multipliers 2^e_r (127 * the row's largest
 // block scale in [2^14, 2^15) after scaling by 2^-e_r) in mult if non-null;
-// the offset-pass operand (u per block, hi/lo, [rows][offset_operand_halves])
-// and its row multipliers.
-hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_t cols, _Float16* out, float* mult,
-                           _Float16* uop, float* umult, hipStream_t st);
+// the offset-pass operand (u = -uoff * s * (block code sum) per block, hi/lo,
+// [rows][offset_operand_halves]) and its row multipliers.  uoff = 0.5 for
+// the symmetric weight map w = d (q - 1.5), 0 for Q2_0's w = d (q - 1): the
+// GEMMs multiply by d (q - 1), the offset pass adds the rest.
+hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_t cols, float uoff, _Float16* out,
+                           float* mult, _Float16* uop, float* umult, hipStream_t st);
 // The down GEMM operand q * s * 2^-e_r (fp16) of the grouped rows in the
 // tiled layout: tile t of the chunk lists' tile table holds grouped rows
 // trows[t], stored as
@@ -90,12 +92,12 @@ hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_
 hipError_t launch_gather_tiles(const int8_t* q, const float* s, const int32_t* src, const ChunkLists& cl,
                                int64_t tiles_cap, int32_t cols, _Float16* out, float* sout, hipStream_t st);
 hipError_t launch_prescale_tiled(const int8_t* q, const float* s, const ChunkLists& cl, int64_t tiles_cap,
-                                 int32_t cols, _Float16* out, float* mult, _Float16* uop, float* umult,
+                                 int32_t cols, float uoff, _Float16* out, float* mult, _Float16* uop, float* umult,
                                  hipStream_t st);
 // The layer input in one pass: launch_quantize's outputs (q8, s) and
 // launch_prescale's (codes16, mult, uop, umult), bit-identical to
 // the two launches; also clears the ZeroWords.
-hipError_t launch_quantize_prescale(const float* x, int64_t rows, int32_t cols, int8_t* q8, float* s,
+hipError_t launch_quantize_prescale(const float* x, int64_t rows, int32_t cols, float uoff, int8_t* q8, float* s,
                                    _Float16* codes16, float* mult, _Float16* uop, float* umult, hipStream_t st,
                                    ZeroWords z);
 hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t st);

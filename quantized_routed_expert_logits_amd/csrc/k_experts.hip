@@ -14,6 +14,8 @@
 // scale s.  Their contribution to an output is
 //     d * sum (q - 1.5) * (s a) = sum [d (q - 1)] * (s a) + d * u,
 //     u = -0.5 * s * sum(a)  (one value per activation block).
+// With the pages' Q2_0 map w = d * (q - 1) the same GEMM runs with u = 0
+// (the activation prescale writes it; the offset pass then adds zeros).
 // The first sum runs on v_mfma_f32_16x16x32_f16 (K = 32 = one block): the A
 // operand d*(q-1) is exact in fp16 (q - 1 in {-1, 0, 1, 2}).  Two forms of the
 // B operand:

@@ -24,9 +24,10 @@
 //   the gate/up GEMM: the codes q themselves (exact), [rows][cols]; the GEMM
 //     applies the block scales in fp32 after each block's products.
 //
-// Both kernels write the operand of the GEMMs' offset pass: per block,
-// u = -0.5 * s * (sum of the block's codes) (the 2-bit weight offset's share,
-// see k_experts.hip), the row's u scaled by a power of two into (-1, 1) and
+// The kernels also write the operand of the GEMMs' offset pass: per block,
+// u = -uoff * s * (sum of the block's codes) (the 2-bit weight offset's share
+// beyond the GEMM's q - 1: uoff = 0.5 for w = d (q - 1.5), 0 for the pages'
+// Q2_0 map w = d (q - 1); see k_experts.hip), the row's u scaled by a power of two into (-1, 1) and
 // split hi/lo, in a hi 8 / lo 8 layout over the block index (padded with
 // zeros to a multiple of 32 blocks), plus that power of two.
 #include "internal.h"
@@ -83,9 +84,9 @@ __device__ __forceinline__ void split_hi_lo(float v, _Float16& hi, _Float16& lo)
 // codes out); the block sums go through LDS to the lanes that write the
 // offset operand.
 __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict__ q, const float* __restrict__ s,
-                                                       int64_t rows, int32_t cols, _Float16* __restrict__ out,
-                                                       float* __restrict__ mult, _Float16* __restrict__ uop,
-                                                       float* __restrict__ umult) {
+                                                       int64_t rows, int32_t cols, float uoff,
+                                                       _Float16* __restrict__ out, float* __restrict__ mult,
+                                                       _Float16* __restrict__ uop, float* __restrict__ umult) {
     __shared__ float ush[4][kMaxOffsetChunks * 32];
     const int w = threadIdx.x >> 6;
     const int64_t row = (int64_t)blockIdx.x * 4 + w;
@@ -128,7 +129,7 @@ __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict_
         }
         sum += __shfl_xor(sum, 1);  // lanes 2m, 2m+1 hold the two halves of one block
         if (on && (j & 1) == 0) {
-            const float u = -0.5f * sraw * (float)sum;
+            const float u = -uoff * sraw * (float)sum;
             ush[w][j >> 1] = u;
             umax = fmaxf(umax, fabsf(u));
         }
@@ -189,8 +190,8 @@ __global__ void __launch_bounds__(256) prescale_tiles_kernel(const int8_t* __res
                                                              const float* __restrict__ s,
                                                              const TileRows* __restrict__ trows,
                                                              const int32_t* __restrict__ ntiles, int32_t cols,
-                                                             _Float16* __restrict__ out, float* __restrict__ mult,
-                                                             _Float16* __restrict__ uop,
+                                                             float uoff, _Float16* __restrict__ out,
+                                                             float* __restrict__ mult, _Float16* __restrict__ uop,
                                                              float* __restrict__ umult) {
     extern __shared__ __align__(16) unsigned char lds[];  // codes [16][sc + 8], scales [16][sc / 32 + 1]
     __shared__ float ush[16][kMaxOffsetChunks * 32];      // u of each row and block
@@ -245,7 +246,7 @@ __global__ void __launch_bounds__(256) prescale_tiles_kernel(const int8_t* __res
             for (int i = 0; i < 4; ++i) sum += (int)(int8_t)(c8.x >> (8 * i)) + (int)(int8_t)(c8.y >> (8 * i));
             sum += __shfl_xor(sum, 16);
             sum += __shfl_xor(sum, 32);
-            const float u = -0.5f * sraw * (float)sum;
+            const float u = -uoff * sraw * (float)sum;
             if (g == 0) ush[r][c0 / kBlock + b] = u;
             m = fmaxf(m, sraw);
             umax = fmaxf(umax, fabsf(u));
@@ -390,7 +391,7 @@ __global__ void __launch_bounds__(256) gather_tiles_kernel(const int8_t* __restr
 // values each (four float4 loads: the wave reads 4 KiB of the row per step);
 // the arithmetic of each output is that of the two separate kernels.
 __global__ void __launch_bounds__(256) quantize_prescale_kernel(const float* __restrict__ x, int64_t rows,
-                                                                int32_t cols, int8_t* __restrict__ q8,
+                                                                int32_t cols, float uoff, int8_t* __restrict__ q8,
                                                                 float* __restrict__ s_out, _Float16* __restrict__ out,
                                                                 float* __restrict__ mult, _Float16* __restrict__ uop,
                                                                 float* __restrict__ umult, ZeroWords z) {
@@ -440,7 +441,7 @@ __global__ void __launch_bounds__(256) quantize_prescale_kernel(const float* __r
         }
         if ((j & 1) == 0) {
             s_out[row * nb + (j >> 1)] = s;
-            const float u = -0.5f * s * (float)sum;
+            const float u = -uoff * s * (float)sum;
             ush[w][j >> 1] = u;
             umax = fmaxf(umax, fabsf(u));
         }
@@ -503,11 +504,11 @@ hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q
     return hipGetLastError();
 }
 
-hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_t cols, _Float16* out, float* mult,
-                           _Float16* uop, float* umult, hipStream_t st) {
+hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_t cols, float uoff, _Float16* out,
+                           float* mult, _Float16* uop, float* umult, hipStream_t st) {
     if (rows > 0)
-        hipLaunchKernelGGL(prescale_kernel, dim3(grid_for(rows, 4)), dim3(256), 0, st, q, s, rows, cols, out, mult,
-                           uop, umult);
+        hipLaunchKernelGGL(prescale_kernel, dim3(grid_for(rows, 4)), dim3(256), 0, st, q, s, rows, cols, uoff, out,
+                           mult, uop, umult);
     return hipGetLastError();
 }
 
@@ -521,20 +522,20 @@ hipError_t launch_gather_tiles(const int8_t* q, const float* s, const int32_t* s
 }
 
 hipError_t launch_prescale_tiled(const int8_t* q, const float* s, const ChunkLists& cl, int64_t tiles_cap,
-                                 int32_t cols, _Float16* out, float* mult, _Float16* uop, float* umult,
+                                 int32_t cols, float uoff, _Float16* out, float* mult, _Float16* uop, float* umult,
                                  hipStream_t st) {
     if (tiles_cap > 0)
         hipLaunchKernelGGL(prescale_tiles_kernel, dim3((unsigned)tiles_cap), dim3(256), prescale_tiles_lds_bytes(cols),
-                           st, q, s, cl.trows, cl.sched + 2, cols, out, mult, uop, umult);
+                           st, q, s, cl.trows, cl.sched + 2, cols, uoff, out, mult, uop, umult);
     return hipGetLastError();
 }
 
-hipError_t launch_quantize_prescale(const float* x, int64_t rows, int32_t cols, int8_t* q8, float* s,
+hipError_t launch_quantize_prescale(const float* x, int64_t rows, int32_t cols, float uoff, int8_t* q8, float* s,
                                    _Float16* codes16, float* mult, _Float16* uop, float* umult, hipStream_t st,
                                    ZeroWords z) {
     if (rows > 0)
-        hipLaunchKernelGGL(quantize_prescale_kernel, dim3(grid_for(rows, 4)), dim3(256), 0, st, x, rows, cols, q8, s,
-                           codes16, mult, uop, umult, z);
+        hipLaunchKernelGGL(quantize_prescale_kernel, dim3(grid_for(rows, 4)), dim3(256), 0, st, x, rows, cols, uoff,
+                           q8, s, codes16, mult, uop, umult, z);
     return hipGetLastError();
 }
 

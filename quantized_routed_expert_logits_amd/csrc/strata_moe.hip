@@ -293,7 +293,8 @@ int check_dims(int32_t hidden, int32_t ffn) {
 
 int check_experts(const strata_moe_experts* ex) {
     if (!ex) return fail(STRATA_MOE_EINVAL, "experts is NULL");
-    if (ex->format != STRATA_MOE_Q2_SYM) return fail(STRATA_MOE_EUNSUPPORTED, "unknown weight format %d", ex->format);
+    if (ex->format != STRATA_MOE_Q2_SYM && ex->format != STRATA_MOE_Q2_0)
+        return fail(STRATA_MOE_EUNSUPPORTED, "unknown weight format %d", ex->format);
     if (ex->n_expert < 1 || ex->n_expert > kMaxExperts)
         return fail(STRATA_MOE_EINVAL, "n_expert %d outside [1, %d]", ex->n_expert, kMaxExperts);
     TRY(check_dims(ex->hidden, ex->ffn));
@@ -309,6 +310,11 @@ int check_experts(const strata_moe_experts* ex) {
         return fail(STRATA_MOE_EINVAL, "router_prepared must be 256-byte aligned");
     return 0;
 }
+
+// The GEMMs multiply by d (q - 1); the offset pass adds -uoff * d * s * (block
+// code sum) for the rest of the weight map's offset: 0.5 for w = d (q - 1.5),
+// 0 for Q2_0's w = d (q - 1).
+float code_offset(const strata_moe_experts* ex) { return ex->format == STRATA_MOE_Q2_0 ? 0.0f : 0.5f; }
 
 // The GEMMs address activations with 32-bit buffer offsets: their tiled
 // operands (T*K rows and up to 15 padding rows per expert, [.][H] and [.][I]
@@ -349,7 +355,8 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     tm.begin(kQuantize);
     // one pass over x: int8 codes and scales, their fp16 copy, row multipliers and
     // offset operand; it also clears the top-K near-tie count and the id error flag
-    HIP_TRY(launch_quantize_prescale(x, T, H, b.xq, b.xs, b.xa, b.xe, b.xuop, b.xum, st, ZeroWords{{b.amb, b.err}}),
+    HIP_TRY(launch_quantize_prescale(x, T, H, code_offset(ex), b.xq, b.xs, b.xa, b.xe, b.xuop, b.xum, st,
+                                     ZeroWords{{b.amb, b.err}}),
             "quantize launch");
     tm.end(kQuantize);
     tm.begin(kRouter);
@@ -382,7 +389,8 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
             "gate/up launch");
     tm.end(kGateUp);
     tm.begin(kPrescaleH);
-    HIP_TRY(launch_prescale_tiled(b.hq, b.hs, cl, tiled_rows_cap(n, E) / 16, I, b.hb, b.he, b.huop, b.hum, st),
+    HIP_TRY(launch_prescale_tiled(b.hq, b.hs, cl, tiled_rows_cap(n, E) / 16, I, code_offset(ex), b.hb, b.he, b.huop,
+                                  b.hum, st),
             "prescale launch");
     tm.end(kPrescaleH);
     tm.begin(kDown);
@@ -655,7 +663,7 @@ int strata_moe_gate_up(const int8_t* qx, const float* sx, const int32_t* offsets
     float* xst = (float*)(ws + o_xst);
     _Float16* xuop = (_Float16*)(ws + o_xuop);
     float* xum = (float*)(ws + o_xum);
-    HIP_TRY(launch_prescale(qx, sx, T, H, xa, nullptr, xuop, xum, st), "prescale launch");
+    HIP_TRY(launch_prescale(qx, sx, T, H, code_offset(experts), xa, nullptr, xuop, xum, st), "prescale launch");
     HIP_TRY(launch_chunks_from_offsets(offsets, E, n, cl, st), "chunk list launch");  // and the tile table
     HIP_TRY(launch_gather_tiles(qx, sx, src, cl, tiled_rows_cap(n, E) / 16, H, xt, xst, st), "gather launch");
     HIP_TRY(launch_gate_up((const uint8_t*)experts->gate_up, experts->gate_up_stride, cl, n, E, src, xt, xst,
@@ -693,7 +701,9 @@ int strata_moe_down(const int8_t* qh, const float* sh, const int32_t* offsets, c
     float* prow = (float*)(ws + o_prow);
     float* dm = (float*)(ws + o_dm);
     HIP_TRY(launch_chunks_from_offsets(offsets, E, n, cl, st), "chunk list launch");  // and the tile table
-    HIP_TRY(launch_prescale_tiled(qh, sh, cl, tiled_rows_cap(n, E) / 16, I, hb, he, huop, hum, st), "prescale launch");
+    HIP_TRY(launch_prescale_tiled(qh, sh, cl, tiled_rows_cap(n, E) / 16, I, code_offset(experts), hb, he, huop, hum,
+                                  st),
+            "prescale launch");
     HIP_TRY(launch_row_weights(slot, p, n, prow, st), "weights launch");
     HIP_TRY(launch_down((const uint8_t*)experts->down, experts->down_stride, cl, n, E, src, prow, hb,
                         tiled_rows_cap(n, E), he, huop, hum, H, I, dm, st),

@@ -4,6 +4,7 @@ from __future__ import annotations
 
 import numpy as np
 
+import oracle
 import synthetic as S
 
 _expert_cache: dict = {}
@@ -29,10 +30,10 @@ def gpu_experts(s: S.LayerShape, seed: int = 0, chunk: int = 32):
 
     import quantized_routed_expert_logits_amd as qm
 
-    key = (s.E, s.H, s.I, seed)
+    key = (s.E, s.H, s.I, seed, s.fmt)
     base = _gpu_experts.get(key)
     if base is None:
-        base = qm.Experts(s.E, s.H, s.I, device="cuda")
+        base = qm.Experts(s.E, s.H, s.I, device="cuda", fmt=s.fmt)
         for e0 in range(0, s.E, chunk):
             e1 = min(s.E, e0 + chunk)
             parts = [canonical_expert(s, e, seed) for e in range(e0, e1)]
@@ -95,7 +96,7 @@ def down_error_bound(s: S.LayerShape, ref: dict, seed: int = 0) -> np.ndarray:
             continue
         ex = canonical_expert(s, e, seed)
         d = ex.scales_d.view(np.float16).astype(np.float64)
-        w_abs = np.abs(np.repeat(d, 32, axis=1) * (ex.codes_d.astype(np.float64) - 1.5))
+        w_abs = np.abs(np.repeat(d, 32, axis=1) * (ex.codes_d.astype(np.float64) - oracle.code_zero(s.fmt)))
         contrib = h_abs[o0:o1] @ w_abs.T                      # [rows][H]
         # grouped row g is routed pair slot^-1(g): token src[g], weight p at that pair
         inv = np.empty(n, np.int64)

@@ -149,11 +149,13 @@ def test_group_rejects_out_of_range_ids(qm):
 # ------------------------------------------------------------ expert stages
 def _stage_ref(s):
     x, wr = S.activations(s), S.router_weight(s)
-    return x, wr, oracle.layer(x, wr, S.router_bias(s), getter(s), s.E, s.K, want_h=True)
+    return x, wr, oracle.layer(x, wr, S.router_bias(s), getter(s), s.E, s.K, want_h=True, fmt=s.fmt)
 
 
 STAGE_SHAPES = [S.shape("tiny"), S.custom(T=300, H=256, E=12, K=3, I=128), S.custom(T=70, H=640, E=5, K=2, I=192),
-                S.custom(T=2000, H=384, E=3, K=2, I=64)]
+                S.custom(T=2000, H=384, E=3, K=2, I=64),
+                # the pages' Q2_0 map, and its FFN width 640 (20 blocks: not a multiple of 8)
+                S.custom(T=300, H=256, E=12, K=3, I=128, fmt="q2_0"), S.custom(T=160, H=512, E=6, K=2, I=640, fmt="q2_0")]
 
 
 @pytest.mark.parametrize("s", STAGE_SHAPES, ids=lambda s: s.name)
@@ -247,7 +249,7 @@ def _check_grouping_props(g, T, K, E):
     assert np.all(inner > 0)  # ascending tokens within each expert
 
 
-@pytest.mark.parametrize("name", ["stream_all_1k", "chunk_8k", "skewed_4k", "long_32k"])
+@pytest.mark.parametrize("name", ["stream_all_1k", "chunk_8k", "skewed_4k", "long_32k", "pages_q2_0_2k"])
 def test_full_layer_sampled(qm, name):
     s = S.shape(name)
     ex = gpu_experts(s)
@@ -266,7 +268,7 @@ def test_full_layer_sampled(qm, name):
         rows = g["src"][g["offsets"][busiest]:g["offsets"][busiest + 1]]
         tok += list(rows[-8:])
     tok = np.unique(tok)
-    ref = oracle.layer_tokens(x, wr, bias, getter(s), s.K, tok)
+    ref = oracle.layer_tokens(x, wr, bias, getter(s), s.K, tok, fmt=s.fmt)
     assert np.array_equal(g["ids"][tok], ref["ids"])
     assert np.array_equal(g["qx"][tok], ref["qx"])
     err = rel_err(y[tok], ref["y"])
