@@ -886,6 +886,13 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_small_kernel(GemmArgs g) {
     if (slab >= g.nslab) return;  // waves are independent: no workgroup barrier follows
     const int lane = threadIdx.x & 63;
     const int nt = (tl.nrows + 15) / 16;
+    // gate/up: a 3-tile chunk in one pass (the weights are unpacked once; 256
+    // VGPRs, still 2 waves per SIMD).  Down keeps two passes (2 tiles, then
+    // 1): a 3-tile down pass would cost the kernel its third wave per SIMD.
+    if (kGateUp && nt == 3) {
+        small_chunk_pass<kGateUp, 3>(g, tl, slab, 0, lane, dl_all[wave]);
+        return;
+    }
     for (int t0 = 0; t0 < nt; t0 += kSmallTiles) {
         if (nt - t0 >= 2)
             small_chunk_pass<kGateUp, 2>(g, tl, slab, t0, lane, dl_all[wave]);

@@ -155,7 +155,9 @@ def _stage_ref(s):
 STAGE_SHAPES = [S.shape("tiny"), S.custom(T=300, H=256, E=12, K=3, I=128), S.custom(T=70, H=640, E=5, K=2, I=192),
                 S.custom(T=2000, H=384, E=3, K=2, I=64),
                 # the pages' Q2_0 map, and its FFN width 640 (20 blocks: not a multiple of 8)
-                S.custom(T=300, H=256, E=12, K=3, I=128, fmt="q2_0"), S.custom(T=160, H=512, E=6, K=2, I=640, fmt="q2_0")]
+                S.custom(T=300, H=256, E=12, K=3, I=128, fmt="q2_0"), S.custom(T=160, H=512, E=6, K=2, I=640, fmt="q2_0"),
+                # about 40 rows per expert: 3-tile chunks in the small-chunk kernel
+                S.custom(T=200, H=256, E=10, K=2, I=128)]
 
 
 @pytest.mark.parametrize("s", STAGE_SHAPES, ids=lambda s: s.name)
