@@ -70,10 +70,12 @@ SHAPES = {
     "skewed_4k": LayerShape("skewed_4k", T=4096, H=2560, E=512, K=10, I=1024, skewed=True),
 }
 
-# The pages' own expert geometry and weight map (I = 640, Q2_0), at a 2048-token
-# chunk: a further check and benchmark of the same layer.
+# Further workloads of the same layer: the pages' own expert geometry and weight
+# map (I = 640, Q2_0) at a 2048-token chunk, and a 256-token chunk.
 EXTRA_SHAPES = {
     "pages_q2_0_2k": LayerShape("pages_q2_0_2k", T=2048, H=2560, E=512, K=10, I=640, fmt="q2_0"),
+    # a short chunk (about 5 rows per expert): the small-T end of the range
+    "short_256": LayerShape("short_256", T=256, H=2560, E=512, K=10, I=1024),
 }
 
 
