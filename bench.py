@@ -103,10 +103,11 @@ def main() -> int:
     log(f"workload {s.name}: T={s.T} H={s.H} E={s.E} K={s.K} I={s.I}; generating and packing experts")
     t_gen = time.time()
     canon = {}
-    experts = qm.Experts(s.E, s.H, s.I, device=dev, fmt=s.fmt)
+    experts = qm.Experts(s.E, s.H, s.I, device=dev, fmt=s.fmt, shared=s.shared)
     chunk = 32
-    for e0 in range(0, s.E, chunk):
-        parts = [S.expert(s, e, args.seed) for e in range(e0, min(s.E, e0 + chunk))]
+    nb = s.E + s.shared  # a shared expert is the last blob
+    for e0 in range(0, nb, chunk):
+        parts = [S.expert(s, e, args.seed) for e in range(e0, min(nb, e0 + chunk))]
         for i, p in enumerate(parts):
             canon[e0 + i] = p
         experts.pack(e0, np.stack([p.codes_gu for p in parts]), np.stack([p.scales_gu for p in parts]),
@@ -114,6 +115,9 @@ def main() -> int:
     bias_np = S.router_bias(s, args.seed)
     bias = None if bias_np is None else torch.from_numpy(bias_np).to(dev)
     experts = experts.with_router_bias(bias)
+    wg_np = S.shared_gate_weight(s, args.seed) if s.shared else None
+    if s.shared:
+        experts = experts.with_shared_gate(torch.from_numpy(wg_np).to(dev))
     x_np, wr_np = S.activations(s, args.seed), S.router_weight(s, args.seed)
     x = torch.from_numpy(x_np).to(dev)
     wr = torch.from_numpy(wr_np).to(dev)
@@ -160,7 +164,7 @@ def main() -> int:
         del flush
         log(f"copy probe: {args.copy_probe_mib} MiB")
 
-    n = s.T * s.K
+    n = s.T * (s.K + s.shared)  # grouped rows: K routed pairs per token, plus the shared expert's
     flops = {"gate_up": 2.0 * n * 2 * s.I * s.H, "down": 2.0 * n * s.H * s.I}
     dominant = max(kernel_ms, key=kernel_ms.get)
     traffic = measured_traffic(dominant, s.name) if dominant in flops else None
@@ -171,7 +175,7 @@ def main() -> int:
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic}
     elif dominant in flops:
         # few rows per expert: the GEMM streams the hit experts' packed weights once
-        hit = int((torch.bincount(dbg_ids.reshape(-1).long(), minlength=s.E) > 0).sum())
+        hit = int((torch.bincount(dbg_ids.reshape(-1).long(), minlength=s.E + s.shared) > 0).sum())
         rows = 2 * s.I if dominant == "gate_up" else s.H
         kd = s.H if dominant == "gate_up" else s.I
         wbytes = hit * rows * kd * (2 / 8 + 2 / 32)
@@ -190,11 +194,12 @@ def main() -> int:
         tok = np.sort(rng.choice(s.T, min(args.cpu_tokens, s.T), replace=False))
         log(f"CPU oracle on {len(tok)} sampled tokens")
         t0 = time.perf_counter()
-        oracle.layer_tokens(x_np, wr_np, bias_np, lambda e: canon[e], s.K, tok, fmt=s.fmt)
+        oracle.layer_tokens(x_np, wr_np, bias_np, lambda e: canon[e], s.K, tok, fmt=s.fmt,
+                            shared=(canon[s.E], wg_np) if s.shared else None)
         dt = time.perf_counter() - t0
         cpu = {"value": round(len(tok) / dt, 2), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
                "sample": f"{len(tok)} random tokens of the {s.name} layer, full layer per token "
-                         f"(router, top-K, quantize, {s.K} expert FFNs, combine) in double; {dt:.2f} s"}
+                         f"(router, top-K, quantize, {s.K + s.shared} expert FFNs, combine) in double; {dt:.2f} s"}
 
     line = {
         "metric": METRIC,
@@ -212,7 +217,8 @@ def main() -> int:
         "config": {"workload": s.name, "T": s.T, "H": s.H, "E": s.E, "K": s.K, "I": s.I,
                    "weights": "2-bit codes, fp16 scale per 32, " + ("w = d(q-1)" if s.fmt == "q2_0" else "w = d(q-1.5)"),
                    "activations": "int8, fp32 scale per 32",
-                   "router_matrix": "prepared per call" if args.router_per_call else "prepared once"},
+                   "router_matrix": "prepared per call" if args.router_per_call else "prepared once",
+                   "shared_expert": bool(s.shared)},
         "kernel_ms": {k: round(v, 4) for k, v in kernel_ms.items()},
         "int8_ops_per_step": 2.0 * n * 3 * s.H * s.I,
         "roofline": roofline,

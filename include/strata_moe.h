@@ -73,7 +73,18 @@ extern "C" {
  *   router_prepared: strata_moe_prepare_router()'s output for the router_w
  *            that the layer calls pass, or NULL (then the layer prepares
  *            router_w on every call).  Added after the fields above; code
- *            that zero-initialises the struct keeps the per-call path. */
+ *            that zero-initialises the struct keeps the per-call path.
+ *   shared_gate: [H] fp32, or NULL for no shared expert.  When set, the
+ *            blobs hold E + 1 experts and the last one (index E) is the
+ *            layer's shared expert: every token also goes through it, and
+ *            its output is added with the token's scalar gate
+ *            g = sigmoid(x . shared_gate), computed in fp32 (the shared expert
+ *            and its scalar gate in the MoE half of Prefill::run, prefill.cpp
+ *            page; the pages do not print how the two outputs are combined,
+ *            and this is the sigmoid-gated sum).  The shared expert takes the
+ *            routed experts' path: int8 input, gate/up, SwiGLU, int8 H, down.
+ *            It is pair slot K of every token, so with it K <= 15 and
+ *            E <= 1023.  Code that zero-initialises the struct has none. */
 typedef struct strata_moe_experts {
     int32_t n_expert; /* E */
     int32_t hidden;   /* H */
@@ -85,11 +96,14 @@ typedef struct strata_moe_experts {
     int64_t down_stride;
     const float* router_bias;
     const void* router_prepared;
+    const float* shared_gate;
 } strata_moe_experts;
 
 /* Optional intermediate outputs of strata_moe_prefill_debug (each may be
  * NULL; all device pointers, sized for T tokens).  The library's own buffers
- * are copied into them after the layer has run. */
+ * are copied into them after the layer has run.  With a shared expert every
+ * K below reads K + 1 and E reads E + 1: pair slot K of token t is the shared
+ * expert (id E, p = its gate). */
 typedef struct strata_moe_debug {
     int32_t* ids;     /* [T][K] routed experts, rank order */
     float* p;         /* [T][K] routing weights */

@@ -7,9 +7,11 @@ the only module both sides read is ``synthetic`` (the seeded input draws).
 
 The arithmetic lives in ``strata_oracle.c`` (plain C, double precision, one
 function per step of the layer, each citing the passage of the Strata pages it
-follows); this wrapper only marshals numpy arrays and chains the steps in the
-order the pages give them (Winery-Strata prefill.cpp page, Prefill::run, MoE
-half: router -> route -> quantize -> group -> experts -> combine).
+follows); this wrapper marshals numpy arrays and chains the steps in the order
+the pages give them (Winery-Strata prefill.cpp page, Prefill::run, MoE half:
+router -> route -> quantize -> group -> experts -> combine).  The one step
+written here in numpy (double) is the shared expert's gate and weighted sum
+(s1, s2: the shared expert), built from the C steps.
 
 Parity is pinned by ``tests/test_oracle_pins.py`` (brute force, closed forms,
 invariants and exact round-trips); no function here is unpinned.
@@ -174,13 +176,34 @@ def combine(D, p, slot):
     return y
 
 
-def layer(x, wr, bias, get_expert, E: int, K: int, want_h: bool = False, fmt: str = "q2_sym") -> dict:
+def shared_gate(x, wg) -> np.ndarray:
+    """s1: the shared expert's scalar gate per token, g = sigmoid(x . wg), in
+    double (the dot is c1's compensated sum with wg as the one column).  The
+    pages compute this projection beside the shared expert in the MoE half of
+    Prefill::run (prefill.cpp page) but do not print how it is applied; the
+    reading here is the sigmoid-gated sum of s2."""
+    s = router_logits(x, np.asarray(wg, np.float32).reshape(-1, 1))[:, 0]
+    return 1.0 / (1.0 + np.exp(-s))
+
+
+def _shared_term(shared, qx, sx, x, want_h, fmt):
+    """s2: the shared expert's rows for every given token (the routed
+    experts' c5..c7 on the token's int8 input) and its gate; y gains g * D."""
+    ex, wg = shared
+    h, qh, sh, D = expert_rows(ex, qx, sx, want_h, fmt)
+    return dict(g=shared_gate(x, wg), qh=qh, sh=sh, h=h, D=D)
+
+
+def layer(x, wr, bias, get_expert, E: int, K: int, want_h: bool = False, fmt: str = "q2_sym",
+          shared=None) -> dict:
     """The whole layer on every token, all intermediates returned.
 
     get_expert(e) returns expert e's canonical arrays.  Steps in the pages'
     order: router logits, route (top-K + softmax), int8 activations once per
     token, grouping, per expert its rows (gate/up, SwiGLU, int8 H, down), and
-    the combine."""
+    the combine.  shared = (expert arrays, gate vector [H]) adds the shared
+    expert on every token, weighted by its scalar gate (s1, s2); its
+    intermediates come back under "shared"."""
     T, H = x.shape
     logits = router_logits(x, wr, bias)
     ids, p = topk_softmax(logits, K)
@@ -203,8 +226,12 @@ def layer(x, wr, bias, get_expert, E: int, K: int, want_h: bool = False, fmt: st
         if want_h:
             h[r0:r1] = he
     y = combine(D, p, slot)
+    sh_term = None
+    if shared is not None:
+        sh_term = _shared_term(shared, qx, sx, x, want_h, fmt)
+        y = y + sh_term["g"][:, None] * sh_term["D"]
     return dict(logits=logits, ids=ids, p=p, qx=qx, sx=sx, offsets=offsets, src=src, slot=slot,
-                qh=qh, sh=sh, h=h, D=D, y=y)
+                qh=qh, sh=sh, h=h, D=D, y=y, shared=sh_term)
 
 
 def rows_multi(experts: list, which, qx, sx, fmt: str = "q2_sym"):
@@ -229,7 +256,7 @@ def rows_multi(experts: list, which, qx, sx, fmt: str = "q2_sym"):
     return qh, sh, D
 
 
-def layer_tokens(x, wr, bias, get_expert, K: int, tokens, fmt: str = "q2_sym") -> dict:
+def layer_tokens(x, wr, bias, get_expert, K: int, tokens, fmt: str = "q2_sym", shared=None) -> dict:
     """The layer's output for a sample of tokens only.
 
     Every step of the layer is independent across tokens except the grouping,
@@ -256,4 +283,8 @@ def layer_tokens(x, wr, bias, get_expert, K: int, tokens, fmt: str = "q2_sym") -
     D = D.reshape(S, K, H)
     qh = qh.reshape(S, K, I)
     sh = sh.reshape(S, K, I // BLOCK)
-    return dict(tokens=tokens, logits=logits, ids=ids, p=p, qx=qx, sx=sx, qh=qh, sh=sh, D=D, y=y)
+    sh_term = None
+    if shared is not None:
+        sh_term = _shared_term(shared, qx, sx, xs, False, fmt)
+        y = y + sh_term["g"][:, None] * sh_term["D"]
+    return dict(tokens=tokens, logits=logits, ids=ids, p=p, qx=qx, sx=sx, qh=qh, sh=sh, D=D, y=y, shared=sh_term)

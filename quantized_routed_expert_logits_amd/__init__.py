@@ -47,7 +47,7 @@ _i64, _i32 = ctypes.c_int64, ctypes.c_int32
 class ExpertsStruct(ctypes.Structure):
     _fields_ = [("n_expert", _i32), ("hidden", _i32), ("ffn", _i32), ("format", _i32),
                 ("gate_up", _P), ("gate_up_stride", _i64), ("down", _P), ("down_stride", _i64),
-                ("router_bias", _P), ("router_prepared", _P)]
+                ("router_bias", _P), ("router_prepared", _P), ("shared_gate", _P)]
 
 
 class DebugStruct(ctypes.Structure):
@@ -162,26 +162,34 @@ def strata_moe_set_workspace(buf: torch.Tensor | None) -> None:
 
 # ------------------------------------------------------------------- experts
 class Experts:
-    """A layer's packed experts in device memory (blobs owned by torch)."""
+    """A layer's packed experts in device memory (blobs owned by torch).
+
+    shared=True adds a blob slot for the layer's shared expert at index
+    n_expert (pack it like a routed expert); the layer runs it once its scalar
+    gate vector is set (with_shared_gate)."""
 
     def __init__(self, n_expert: int, hidden: int, ffn: int, router_bias: torch.Tensor | None = None,
-                 device: str | torch.device = "cuda", fmt: str = "q2_sym"):
+                 device: str | torch.device = "cuda", fmt: str = "q2_sym", shared: bool = False):
         if fmt not in FORMATS:
             raise ValueError(f"unknown weight format {fmt!r}; one of {sorted(FORMATS)}")
         self.n_expert, self.hidden, self.ffn, self.format = n_expert, hidden, ffn, FORMATS[fmt]
+        self.shared = bool(shared)
+        nb = n_expert + self.shared
         self.gate_up_stride, self.down_stride = strata_moe_packed_bytes(hidden, ffn)
-        self.gate_up = torch.empty(n_expert * self.gate_up_stride, dtype=torch.uint8, device=device)
-        self.down = torch.empty(n_expert * self.down_stride, dtype=torch.uint8, device=device)
+        self.gate_up = torch.empty(nb * self.gate_up_stride, dtype=torch.uint8, device=device)
+        self.down = torch.empty(nb * self.down_stride, dtype=torch.uint8, device=device)
         _dtype(router_bias, torch.float32, "router_bias")
         self.router_bias = router_bias
         self.router_prepared = None
+        self.shared_gate = None
         self._restruct()
 
     def _restruct(self):
         self.struct = ExpertsStruct(self.n_expert, self.hidden, self.ffn, self.format, self.gate_up.data_ptr(),
                                     self.gate_up_stride, self.down.data_ptr(), self.down_stride,
                                     None if self.router_bias is None else self.router_bias.data_ptr(),
-                                    None if self.router_prepared is None else self.router_prepared.data_ptr())
+                                    None if self.router_prepared is None else self.router_prepared.data_ptr(),
+                                    None if self.shared_gate is None else self.shared_gate.data_ptr())
 
     def with_router_bias(self, router_bias: torch.Tensor | None) -> "Experts":
         """The same blobs with another router bias (or none)."""
@@ -190,6 +198,22 @@ class Experts:
         _dtype(router_bias, torch.float32, "router_bias")
         other = copy.copy(self)
         other.router_bias = router_bias
+        other._restruct()
+        return other
+
+    def with_shared_gate(self, gate: torch.Tensor | None) -> "Experts":
+        """The same blobs with the shared expert's scalar gate vector [H] fp32
+        (None: the layer runs the routed experts only)."""
+        import copy
+
+        if gate is not None:
+            if not self.shared:
+                raise ValueError("these experts have no shared-expert blob (Experts(..., shared=True))")
+            _dtype(gate, torch.float32, "shared_gate")
+            if tuple(gate.shape) != (self.hidden,) or not gate.is_contiguous():
+                raise ValueError(f"shared_gate must be a contiguous [{self.hidden}] tensor")
+        other = copy.copy(self)
+        other.shared_gate = gate
         other._restruct()
         return other
 
@@ -266,10 +290,12 @@ def strata_moe_prefill(x: torch.Tensor, router_w: torch.Tensor, experts: Experts
 def strata_moe_prefill_debug(x, router_w, experts: Experts, K: int, out, stream=None) -> dict:
     """The layer plus its intermediates (ids, p, offsets, src, slot, qx, sx, qh, sh) as device tensors."""
     T, H = x.shape
-    E, I, n = experts.n_expert, experts.ffn, x.shape[0] * K
+    sh = experts.shared_gate is not None  # the shared expert: pair slot K of each token, expert n_expert
+    Kg = K + sh
+    E, I, n = experts.n_expert + sh, experts.ffn, x.shape[0] * Kg
     dev = x.device
-    d = dict(ids=torch.empty((T, K), dtype=torch.int32, device=dev),
-             p=torch.empty((T, K), dtype=torch.float32, device=dev),
+    d = dict(ids=torch.empty((T, Kg), dtype=torch.int32, device=dev),
+             p=torch.empty((T, Kg), dtype=torch.float32, device=dev),
              offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
              src=torch.empty(n, dtype=torch.int32, device=dev),
              slot=torch.empty(n, dtype=torch.int32, device=dev),

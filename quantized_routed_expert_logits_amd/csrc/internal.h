@@ -164,6 +164,11 @@ hipError_t launch_topk(const float* logits, const float* x, const float* wt, con
                        int32_t E, int32_t K, int32_t* amb, int32_t* sel, int32_t* ids, float* p, hipStream_t st,
                        bool amb_zeroed = false);
 
+// The shared expert's pair slot: ids / p [T][K] copied to gids / gp [T][K+1]
+// with slot K = (E, sigmoid(x[t] . wg)).  x, wg 16-byte aligned; H % 128 == 0.
+hipError_t launch_shared_slot(const float* x, const float* wg, const int32_t* ids, const float* p, int64_t T,
+                              int32_t H, int32_t K, int32_t E, int32_t* gids, float* gp, hipStream_t st);
+
 hipError_t launch_group(const int32_t* ids, const float* p, int64_t n, int32_t K, int32_t E, int32_t* hist,
                         int32_t* base, int32_t* offsets, const ChunkLists& cl, int32_t* src, int32_t* slot,
                         float* prow, int32_t* err, hipStream_t st);

@@ -793,4 +793,50 @@ hipError_t launch_topk(const float* logits, const float* x, const float* wt, con
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------ shared expert
+// The shared expert joins the grouping as expert E, pair slot K of every
+// token, its weight the token's scalar gate g = sigmoid(x . wg) (the shared
+// expert and its scalar gate, MoE half of Prefill::run, prefill.cpp page).
+// One wave per token: the dot in fp32 (lane-strided float4 partial sums, then
+// a butterfly), the routed pairs copied to the K + 1 wide arrays beside it.
+constexpr int kSharedWaves = 4;
+
+__global__ void __launch_bounds__(64 * kSharedWaves)
+    shared_slot_kernel(const float* __restrict__ x, const float* __restrict__ wg, const int32_t* __restrict__ ids,
+                       const float* __restrict__ p, int64_t T, int32_t H, int32_t K, int32_t E,
+                       int32_t* __restrict__ gids, float* __restrict__ gp) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * kSharedWaves + (threadIdx.x >> 6);
+    if (t >= T) return;  // whole waves
+    const float4_t* xr = reinterpret_cast<const float4_t*>(x + t * H);
+    const float4_t* wr = reinterpret_cast<const float4_t*>(wg);
+    float acc = 0.f;
+    for (int c = lane; c < H / 4; c += 64) {
+        const float4_t a = xr[c], w = wr[c];
+        acc = fmaf(a[0], w[0], acc);
+        acc = fmaf(a[1], w[1], acc);
+        acc = fmaf(a[2], w[2], acc);
+        acc = fmaf(a[3], w[3], acc);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    const float g = 1.0f / (1.0f + expf(-acc));
+    const int32_t Kg = K + 1;
+    if (lane < K) {
+        gids[t * Kg + lane] = ids[t * K + lane];
+        gp[t * Kg + lane] = p[t * K + lane];
+    } else if (lane == K) {
+        gids[t * Kg + K] = E;
+        gp[t * Kg + K] = g;
+    }
+}
+
+hipError_t launch_shared_slot(const float* x, const float* wg, const int32_t* ids, const float* p, int64_t T,
+                              int32_t H, int32_t K, int32_t E, int32_t* gids, float* gp, hipStream_t st) {
+    if (T > 0)
+        hipLaunchKernelGGL(shared_slot_kernel, dim3((unsigned)((T + kSharedWaves - 1) / kSharedWaves)),
+                           dim3(64 * kSharedWaves), 0, st, x, wg, ids, p, T, H, K, E, gids, gp);
+    return hipGetLastError();
+}
+
 }  // namespace strata_moe

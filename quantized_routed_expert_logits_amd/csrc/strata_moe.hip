@@ -121,8 +121,10 @@ struct Buffers {
     float* pmax;
     int32_t* amb;
     int32_t* sel;
-    int32_t* ids;
+    int32_t* ids;   // the routing: [T][K]
     float* p;
+    int32_t* gids;  // the grouped pairs: [T][K+1] with a shared expert, else ids / p
+    float* gp;
     int8_t* xq;
     float* xs;
     _Float16* xa;  // the input codes as fp16 [T][H] (small-chunk gate/up kernel)
@@ -152,26 +154,33 @@ struct Buffers {
 };
 
 struct Offsets {
-    size_t logits, wt, wb, wm, pmax, amb, sel, ids, p, xq, xs, xa, xt, xst, xe, xuop, xum, hist, base, offsets, tiles, ntiles, err, src, slot, prow, hq, hs,
+    size_t logits, wt, wb, wm, pmax, amb, sel, ids, p, gids, gp, xq, xs, xa, xt, xst, xe, xuop, xum, hist, base, offsets, tiles, ntiles, err, src, slot, prow, hq, hs,
         trows, hb, he, huop, hum, dm, total;
     int64_t tiles_cap;
 };
 
-Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I) {
+// K, E: the routing's; with a shared expert the grouping and the expert GEMMs
+// run over K + 1 pairs per token and E + 1 experts.
+Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I, bool shared) {
+    const int64_t nr = T * K;
+    const int32_t Er = E;
+    if (shared) ++K, ++E;
     const int64_t n = T * K;
     const int64_t nchunks = (n + kGroupChunk - 1) / kGroupChunk;
     Layout L;
     Offsets o;
     o.tiles_cap = chunk_list_cap(n, E);
-    o.logits = L.take<float>(router_logit_floats(T, H, E));
-    o.wt = L.take<float>((int64_t)E * H);
-    o.wb = L.take<_Float16>(router_padded_experts(E) * H * 2);
-    o.wm = L.take<float>(router_padded_experts(E));
-    o.pmax = L.take<float>((int64_t)((H + 31) / 32) * E);
+    o.logits = L.take<float>(router_logit_floats(T, H, Er));
+    o.wt = L.take<float>((int64_t)Er * H);
+    o.wb = L.take<_Float16>(router_padded_experts(Er) * H * 2);
+    o.wm = L.take<float>(router_padded_experts(Er));
+    o.pmax = L.take<float>((int64_t)((H + 31) / 32) * Er);
     o.amb = L.take<int32_t>(T + 1);
     o.sel = L.take<int32_t>(T * kSelWords);
-    o.ids = L.take<int32_t>(n);
-    o.p = L.take<float>(n);
+    o.ids = L.take<int32_t>(nr);
+    o.p = L.take<float>(nr);
+    o.gids = shared ? L.take<int32_t>(n) : o.ids;
+    o.gp = shared ? L.take<float>(n) : o.p;
     o.xq = L.take<int8_t>(T * H);
     o.xs = L.take<float>(T * (H / kBlock));
     o.xe = L.take<float>(T);
@@ -212,6 +221,8 @@ Buffers carve(char* ws, const Offsets& o) {
     b.sel = (int32_t*)(ws + o.sel);
     b.ids = (int32_t*)(ws + o.ids);
     b.p = (float*)(ws + o.p);
+    b.gids = (int32_t*)(ws + o.gids);
+    b.gp = (float*)(ws + o.gp);
     b.xq = (int8_t*)(ws + o.xq);
     b.xs = (float*)(ws + o.xs);
     b.xa = (_Float16*)(ws + o.xa);
@@ -308,6 +319,11 @@ int check_experts(const strata_moe_experts* ex) {
         return fail(STRATA_MOE_EINVAL, "expert blobs and strides must be 256-byte aligned");
     if (ex->router_prepared && !aligned(ex->router_prepared, 256))
         return fail(STRATA_MOE_EINVAL, "router_prepared must be 256-byte aligned");
+    if (ex->shared_gate && !aligned(ex->shared_gate, 16))
+        return fail(STRATA_MOE_EINVAL, "shared_gate must be 16-byte aligned");
+    if (ex->shared_gate && ex->n_expert + 1 > kMaxExperts)
+        return fail(STRATA_MOE_EINVAL, "n_expert %d leaves no room for the shared expert (at most %d)", ex->n_expert,
+                    kMaxExperts - 1);
     return 0;
 }
 
@@ -335,6 +351,20 @@ int check_tk(int64_t T, int32_t K, int32_t E) {
     return 0;
 }
 
+// A layer call's sizes: the routing's K of E, then the grouped pairs (K + 1 of
+// E + 1 with a shared expert).
+int check_layer(int64_t T, int32_t K, const strata_moe_experts* ex) {
+    TRY(check_experts(ex));
+    TRY(check_tk(T, K, ex->n_expert));
+    const int32_t sh = ex->shared_gate ? 1 : 0;
+    if (K + sh > kMaxTopK)
+        return fail(STRATA_MOE_EINVAL, "K = %d leaves no pair slot for the shared expert (at most %d)", K,
+                    kMaxTopK - 1);
+    if (T * (int64_t)(K + sh) >= (int64_t)1 << 31)
+        return fail(STRATA_MOE_EINVAL, "T*(K+1) = %lld too large", (long long)(T * (K + sh)));
+    return check_buffers(T, K + sh, ex->n_expert + sh, ex->hidden, ex->ffn);
+}
+
 // The layer zeroes `out` before its router reads `x`: the two must not overlap.
 int check_no_overlap(const void* a, const void* b, int64_t bytes) {
     const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
@@ -345,9 +375,11 @@ int check_no_overlap(const void* a, const void* b, int64_t bytes) {
 
 int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int64_t T, int32_t K, float* out,
               hipStream_t st, Buffers* keep) {
+    const bool shared = ex->shared_gate != nullptr;
     const int32_t E = ex->n_expert, H = ex->hidden, I = ex->ffn;
-    const int64_t n = T * K;
-    const Offsets o = plan(T, K, E, H, I);
+    const int32_t Kg = K + shared, Eg = E + shared;  // the grouped pairs per token, the experts they go to
+    const int64_t n = T * Kg;
+    const Offsets o = plan(T, K, E, H, I, shared);
     char* ws = nullptr;
     TRY(get_workspace(o.total, &ws));
     Buffers b = carve(ws, o);
@@ -374,32 +406,34 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     tm.begin(kTopK);
     HIP_TRY(launch_topk(b.logits, x, rs.wt, ex->router_bias, T, H, E, K, b.amb, b.sel, b.ids, b.p, st, true),
             "top-K launch");
+    if (shared)
+        HIP_TRY(launch_shared_slot(x, ex->shared_gate, b.ids, b.p, T, H, K, E, b.gids, b.gp, st), "shared gate launch");
     tm.end(kTopK);
     tm.begin(kGroup);
     const ChunkLists cl{b.tiles, b.ntiles, b.tiles_cap, b.trows};
-    HIP_TRY(launch_group(b.ids, b.p, n, K, E, b.hist, b.base, b.offsets, cl, b.src, b.slot, b.prow, b.err, st),
+    HIP_TRY(launch_group(b.gids, b.gp, n, Kg, Eg, b.hist, b.base, b.offsets, cl, b.src, b.slot, b.prow, b.err, st),
             "group launch");
     // the big chunks' input codes and scales, gathered into the tiled layout
-    HIP_TRY(launch_gather_tiles(b.xq, b.xs, b.src, cl, tiled_rows_cap(n, E) / 16, H, b.xt, b.xst, st),
+    HIP_TRY(launch_gather_tiles(b.xq, b.xs, b.src, cl, tiled_rows_cap(n, Eg) / 16, H, b.xt, b.xst, st),
             "gather launch");
     tm.end(kGroup);
     tm.begin(kGateUp);
-    HIP_TRY(launch_gate_up((const uint8_t*)ex->gate_up, ex->gate_up_stride, cl, n, E, b.src, b.xt, b.xst,
-                           tiled_rows_cap(n, E), b.xa, b.xs, T, b.xuop, b.xum, H, I, b.hq, b.hs, st),
+    HIP_TRY(launch_gate_up((const uint8_t*)ex->gate_up, ex->gate_up_stride, cl, n, Eg, b.src, b.xt, b.xst,
+                           tiled_rows_cap(n, Eg), b.xa, b.xs, T, b.xuop, b.xum, H, I, b.hq, b.hs, st),
             "gate/up launch");
     tm.end(kGateUp);
     tm.begin(kPrescaleH);
-    HIP_TRY(launch_prescale_tiled(b.hq, b.hs, cl, tiled_rows_cap(n, E) / 16, I, code_offset(ex), b.hb, b.he, b.huop,
+    HIP_TRY(launch_prescale_tiled(b.hq, b.hs, cl, tiled_rows_cap(n, Eg) / 16, I, code_offset(ex), b.hb, b.he, b.huop,
                                   b.hum, st),
             "prescale launch");
     tm.end(kPrescaleH);
     tm.begin(kDown);
-    HIP_TRY(launch_down((const uint8_t*)ex->down, ex->down_stride, cl, n, E, b.src, b.prow, b.hb, tiled_rows_cap(n, E),
+    HIP_TRY(launch_down((const uint8_t*)ex->down, ex->down_stride, cl, n, Eg, b.src, b.prow, b.hb, tiled_rows_cap(n, Eg),
                         b.he, b.huop, b.hum, H, I, b.dm, st),
             "down launch");
     tm.end(kDown);
     tm.begin(kCombine);
-    HIP_TRY(launch_combine(b.dm, b.slot, T, K, H, out, st), "combine launch");
+    HIP_TRY(launch_combine(b.dm, b.slot, T, Kg, H, out, st), "combine launch");
     tm.end(kCombine);
     if (keep) *keep = b;
     return 0;
@@ -456,10 +490,8 @@ int strata_moe_prepare_router(const float* router_w, int32_t hidden, int32_t n_e
 int strata_moe_workspace_bytes(int64_t T, int32_t K, const strata_moe_experts* experts, size_t* bytes) {
     g_err.clear();
     if (!bytes) return fail(STRATA_MOE_EINVAL, "bytes is NULL");
-    TRY(check_experts(experts));
-    TRY(check_tk(T, K, experts->n_expert));
-    TRY(check_buffers(T, K, experts->n_expert, experts->hidden, experts->ffn));
-    *bytes = plan(T, K, experts->n_expert, experts->hidden, experts->ffn).total;
+    TRY(check_layer(T, K, experts));
+    *bytes = plan(T, K, experts->n_expert, experts->hidden, experts->ffn, experts->shared_gate != nullptr).total;
     return 0;
 }
 
@@ -524,9 +556,7 @@ int strata_moe_unpack(const void* gate_up, int64_t gate_up_stride, const void* d
 int strata_moe_prefill(const float* x, const float* router_w, const strata_moe_experts* experts, int64_t T,
                        int32_t K, float* out, void* stream) {
     g_err.clear();
-    TRY(check_experts(experts));
-    TRY(check_tk(T, K, experts->n_expert));
-    TRY(check_buffers(T, K, experts->n_expert, experts->hidden, experts->ffn));
+    TRY(check_layer(T, K, experts));
     if (T == 0) return 0;
     if (!x || !router_w || !out) return fail(STRATA_MOE_EINVAL, "null x / router_w / out");
     if (!aligned(x, 16) || !aligned(out, 16)) return fail(STRATA_MOE_EINVAL, "x and out must be 16-byte aligned");
@@ -538,9 +568,7 @@ int strata_moe_prefill(const float* x, const float* router_w, const strata_moe_e
 int strata_moe_prefill_debug(const float* x, const float* router_w, const strata_moe_experts* experts, int64_t T,
                              int32_t K, float* out, const strata_moe_debug* dbg, void* stream) {
     g_err.clear();
-    TRY(check_experts(experts));
-    TRY(check_tk(T, K, experts->n_expert));
-    TRY(check_buffers(T, K, experts->n_expert, experts->hidden, experts->ffn));
+    TRY(check_layer(T, K, experts));
     if (T == 0) return 0;
     if (!x || !router_w || !out || !dbg) return fail(STRATA_MOE_EINVAL, "null x / router_w / out / dbg");
     if (!aligned(x, 16) || !aligned(out, 16)) return fail(STRATA_MOE_EINVAL, "x and out must be 16-byte aligned");
@@ -549,14 +577,15 @@ int strata_moe_prefill_debug(const float* x, const float* router_w, const strata
     hipStream_t st = (hipStream_t)stream;
     Buffers b;
     TRY(run_layer(x, router_w, experts, T, K, out, st, &b));
-    const int32_t E = experts->n_expert, H = experts->hidden, I = experts->ffn;
-    const int64_t n = T * K;
+    const int32_t sh = experts->shared_gate ? 1 : 0;
+    const int32_t E = experts->n_expert + sh, H = experts->hidden, I = experts->ffn;
+    const int64_t n = T * (K + sh);
     auto cp = [&](void* dst, const void* src, size_t bytes) -> int {
         if (dst) HIP_TRY(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st), "hipMemcpyAsync");
         return 0;
     };
-    TRY(cp(dbg->ids, b.ids, n * 4));
-    TRY(cp(dbg->p, b.p, n * 4));
+    TRY(cp(dbg->ids, b.gids, n * 4));
+    TRY(cp(dbg->p, b.gp, n * 4));
     TRY(cp(dbg->offsets, b.offsets, (E + 1) * 4));
     TRY(cp(dbg->src, b.src, n * 4));
     TRY(cp(dbg->slot, b.slot, n * 4));

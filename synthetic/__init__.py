@@ -55,6 +55,7 @@ class LayerShape:
     I: int   # expert FFN width
     skewed: bool = False  # add the Zipf router bias
     fmt: str = "q2_sym"   # weight map label: "q2_sym" or "q2_0" (the pages' own packs)
+    shared: bool = False  # add a shared expert (index E) with its scalar gate vector
 
     @property
     def n(self) -> int:
@@ -76,6 +77,10 @@ EXTRA_SHAPES = {
     "pages_q2_0_2k": LayerShape("pages_q2_0_2k", T=2048, H=2560, E=512, K=10, I=640, fmt="q2_0"),
     # a short chunk (about 5 rows per expert): the small-T end of the range
     "short_256": LayerShape("short_256", T=256, H=2560, E=512, K=10, I=1024),
+    # the MoE half with its shared expert: the 8192-token chunk, and the pages'
+    # geometry (there the shared expert has the routed experts' width, 640)
+    "chunk_8k_shared": LayerShape("chunk_8k_shared", T=8192, H=2560, E=512, K=10, I=1024, shared=True),
+    "pages_shared_2k": LayerShape("pages_shared_2k", T=2048, H=2560, E=512, K=10, I=640, fmt="q2_0", shared=True),
 }
 
 
@@ -83,10 +88,12 @@ def shape(name: str) -> LayerShape:
     return SHAPES[name] if name in SHAPES else EXTRA_SHAPES[name]
 
 
-def custom(T: int, H: int, E: int, K: int, I: int, skewed: bool = False, fmt: str = "q2_sym") -> LayerShape:
+def custom(T: int, H: int, E: int, K: int, I: int, skewed: bool = False, fmt: str = "q2_sym",
+           shared: bool = False) -> LayerShape:
     """A layer of arbitrary (test) size."""
-    name = f"T{T}_H{H}_E{E}_K{K}_I{I}" + ("_skew" if skewed else "") + ("" if fmt == "q2_sym" else "_" + fmt)
-    return LayerShape(name, T, H, E, K, I, skewed, fmt)
+    name = (f"T{T}_H{H}_E{E}_K{K}_I{I}" + ("_skew" if skewed else "") + ("" if fmt == "q2_sym" else "_" + fmt)
+            + ("_shared" if shared else ""))
+    return LayerShape(name, T, H, E, K, I, skewed, fmt, shared)
 
 
 def _rng(*tag: int) -> np.random.Generator:
@@ -101,6 +108,12 @@ def activations(s: LayerShape, seed: int = 0) -> np.ndarray:
 def router_weight(s: LayerShape, seed: int = 0) -> np.ndarray:
     """W_r [H][E] fp32 (hidden-major: column e is expert e's router vector)."""
     return _rng(seed, 2).normal(0.0, 0.05, (s.H, s.E)).astype(np.float32)
+
+
+def shared_gate_weight(s: LayerShape, seed: int = 0) -> np.ndarray:
+    """The shared expert's scalar gate vector [H] fp32 (drawn like a router
+    column).  The shared expert's own arrays are expert(s, s.E, seed)."""
+    return _rng(seed, 4).normal(0.0, 0.05, s.H).astype(np.float32)
 
 
 def router_bias(s: LayerShape, seed: int = 0) -> np.ndarray | None:

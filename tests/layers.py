@@ -30,19 +30,35 @@ def gpu_experts(s: S.LayerShape, seed: int = 0, chunk: int = 32):
 
     import quantized_routed_expert_logits_amd as qm
 
-    key = (s.E, s.H, s.I, seed, s.fmt)
+    key = (s.E, s.H, s.I, seed, s.fmt, s.shared)
     base = _gpu_experts.get(key)
+    nb = s.E + s.shared  # the shared expert's blob is the last one
     if base is None:
-        base = qm.Experts(s.E, s.H, s.I, device="cuda", fmt=s.fmt)
-        for e0 in range(0, s.E, chunk):
-            e1 = min(s.E, e0 + chunk)
+        base = qm.Experts(s.E, s.H, s.I, device="cuda", fmt=s.fmt, shared=s.shared)
+        for e0 in range(0, nb, chunk):
+            e1 = min(nb, e0 + chunk)
             parts = [canonical_expert(s, e, seed) for e in range(e0, e1)]
             base.pack(e0, np.stack([p.codes_gu for p in parts]), np.stack([p.scales_gu for p in parts]),
                       np.stack([p.codes_d for p in parts]), np.stack([p.scales_d for p in parts]))
         torch.cuda.synchronize()
         _gpu_experts[key] = base
+    if s.shared:
+        base = base.with_shared_gate(torch.from_numpy(S.shared_gate_weight(s, seed)).cuda())
     bias = S.router_bias(s, seed)
     return base.with_router_bias(None if bias is None else torch.from_numpy(bias).cuda())
+
+
+def shared_args(s: S.LayerShape, seed: int = 0):
+    """The oracle's shared-expert argument for the layer (None without one)."""
+    return (canonical_expert(s, s.E, seed), S.shared_gate_weight(s, seed)) if s.shared else None
+
+
+def gate_bound(x, wg) -> np.ndarray:
+    """Per-token bound of |g_gpu - g| for the fp32 gate: the dot of H products
+    in fp32 is within (H + 6) 2^-24 sum|x w| of the exact one, sigmoid's slope
+    is at most 1/4, and exp, add and divide add a few units of 2^-24."""
+    H = x.shape[1]
+    return 0.25 * (H + 6) * 2.0 ** -24 * (np.abs(x.astype(np.float64)) @ np.abs(wg.astype(np.float64))) + 8 * 2.0 ** -24
 
 
 def check_h_codes(q_gpu, s_gpu, h_ref, q_ref, s_ref, tie_tol=2e-3):

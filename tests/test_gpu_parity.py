@@ -12,7 +12,8 @@ import torch
 
 import oracle
 import synthetic as S
-from layers import canonical_expert, check_h_codes, down_error_bound, getter, gpu_experts, rel_err
+from layers import (canonical_expert, check_h_codes, down_error_bound, gate_bound, getter, gpu_experts, rel_err,
+                    shared_args)
 
 pytestmark = pytest.mark.gpu
 
@@ -200,6 +201,40 @@ def test_layer_all_intermediates(qm, s):
     assert rel_err(g["out"], ref["y"]) <= Y_TOL
 
 
+SHARED_SHAPES = [S.custom(T=200, H=256, E=10, K=3, I=128, shared=True),
+                 S.custom(T=160, H=512, E=6, K=2, I=640, fmt="q2_0", shared=True),
+                 S.custom(T=129, H=256, E=8, K=4, I=64, skewed=True, shared=True)]
+
+
+@pytest.mark.parametrize("s", SHARED_SHAPES, ids=lambda s: s.name)
+def test_layer_with_shared_expert(qm, s):
+    # the shared expert is pair slot K of every token (expert E, weight its
+    # gate); the routed part keeps the routed-only grouping order
+    x, wr = S.activations(s), S.router_weight(s)
+    ref = oracle.layer(x, wr, S.router_bias(s), getter(s), s.E, s.K, want_h=True, fmt=s.fmt, shared=shared_args(s))
+    ex = gpu_experts(s)
+    out = torch.empty((s.T, s.H), dtype=torch.float32, device="cuda")
+    d = qm.strata_moe_prefill_debug(_t(x), _t(wr), ex, s.K, out)
+    g = {k: v.cpu().numpy() for k, v in d.items()}
+    T, K, E = s.T, s.K, s.E
+    assert np.array_equal(g["ids"][:, :K], ref["ids"]) and np.all(g["ids"][:, K] == E)
+    assert np.abs(g["p"][:, :K] - ref["p"]).max() <= P_TOL
+    assert np.all(np.abs(g["p"][:, K] - ref["shared"]["g"]) <= gate_bound(x, S.shared_gate_weight(s)))
+    _check_grouping_props(g, T, K + 1, E + 1)
+    o0 = int(g["offsets"][E])
+    assert np.array_equal(g["offsets"][:E + 1], ref["offsets"]) and np.array_equal(g["src"][:o0], ref["src"])
+    assert np.array_equal(g["src"][o0:], np.arange(T))  # the shared expert's rows: every token in order
+    for k in ("qx", "sx"):
+        assert np.array_equal(g[k], ref[k]), k
+    check_h_codes(g["qh"][:o0], g["sh"][:o0], ref["h"], ref["qh"], ref["sh"])
+    rs = ref["shared"]
+    check_h_codes(g["qh"][o0:], g["sh"][o0:], rs["h"], rs["qh"], rs["sh"])
+    assert rel_err(g["out"], ref["y"]) <= Y_TOL
+    # the plain entry point gives the same bits
+    y = qm.strata_moe_prefill(_t(x), _t(wr), ex, s.K, torch.empty_like(out))
+    assert torch.equal(y, out)
+
+
 def test_layer_zero_input_and_repeat(qm):
     s = S.shape("tiny")
     ex = gpu_experts(s)
@@ -251,7 +286,8 @@ def _check_grouping_props(g, T, K, E):
     assert np.all(inner > 0)  # ascending tokens within each expert
 
 
-@pytest.mark.parametrize("name", ["stream_all_1k", "chunk_8k", "skewed_4k", "long_32k", "pages_q2_0_2k"])
+@pytest.mark.parametrize("name", ["stream_all_1k", "chunk_8k", "skewed_4k", "long_32k", "pages_q2_0_2k",
+                                  "chunk_8k_shared", "pages_shared_2k"])
 def test_full_layer_sampled(qm, name):
     s = S.shape(name)
     ex = gpu_experts(s)
@@ -262,7 +298,7 @@ def test_full_layer_sampled(qm, name):
     y = out.cpu().numpy()
     d = qm.strata_moe_prefill_debug(xt, wt, ex, s.K, torch.empty_like(xt))
     g = {k: v.cpu().numpy() for k, v in d.items() if k in ("ids", "offsets", "src", "slot", "qx")}
-    _check_grouping_props(g, s.T, s.K, s.E)
+    _check_grouping_props(g, s.T, s.K + s.shared, s.E + s.shared)
     rng = np.random.default_rng(5)
     tok = [0, s.T - 1] + list(rng.choice(s.T, 30, replace=False))
     if s.skewed:  # tokens of the busiest expert (its tiles run last in their group)
@@ -270,8 +306,8 @@ def test_full_layer_sampled(qm, name):
         rows = g["src"][g["offsets"][busiest]:g["offsets"][busiest + 1]]
         tok += list(rows[-8:])
     tok = np.unique(tok)
-    ref = oracle.layer_tokens(x, wr, bias, getter(s), s.K, tok, fmt=s.fmt)
-    assert np.array_equal(g["ids"][tok], ref["ids"])
+    ref = oracle.layer_tokens(x, wr, bias, getter(s), s.K, tok, fmt=s.fmt, shared=shared_args(s))
+    assert np.array_equal(g["ids"][tok][:, :s.K], ref["ids"])
     assert np.array_equal(g["qx"][tok], ref["qx"])
     err = rel_err(y[tok], ref["y"])
     print(f"{name}: {len(tok)} sampled tokens, max|dy|/max|y| = {err:.2e}")

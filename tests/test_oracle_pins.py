@@ -317,12 +317,70 @@ def _layer_dense(x, wr, bias, exps, K, fmt="q2_sym"):
     y = np.zeros((T, H))
     for t in range(T):
         for k in range(K):
-            Wg, Wu, Wd = dense[ids[t, k]]
-            G, U = Wg @ xd[t], Wu @ xd[t]
-            hq, hs = oracle.quantize((G / (1 + np.exp(-G)) * U).astype(np.float32)[None, :])
-            hd = hq[0].astype(np.float64) * np.repeat(hs[0].astype(np.float64), 32)
-            y[t] += p[t, k] * (Wd @ hd)
+            y[t] += p[t, k] * _ffn_dense(dense[ids[t, k]], xd[t])
     return ids, p, y
+
+
+def _ffn_dense(W, xdt):
+    """One token through one expert with dense weights: SwiGLU, H rounded to
+    int8 per 32 (c4 on the fp32-rounded h), down."""
+    Wg, Wu, Wd = W
+    G, U = Wg @ xdt, Wu @ xdt
+    hq, hs = oracle.quantize((G / (1 + np.exp(-G)) * U).astype(np.float32)[None, :])
+    hd = hq[0].astype(np.float64) * np.repeat(hs[0].astype(np.float64), 32)
+    return Wd @ hd
+
+
+def test_shared_gate_closed_forms():
+    H = 64
+    x = S.activations(S.custom(T=5, H=H, E=2, K=1, I=32), 3)
+    assert np.all(oracle.shared_gate(x, np.zeros(H, np.float32)) == 0.5)  # sigmoid(0)
+    wg = np.zeros(H, np.float32)
+    wg[7] = 1.0
+    xs = np.zeros((4, H), np.float32)
+    xs[:, 7] = [np.log(3.0), -np.log(3.0), 40.0, -40.0]
+    g = oracle.shared_gate(xs, wg)
+    l3 = float(np.float32(np.log(3.0)))
+    assert abs(g[0] - 1.0 / (1.0 + np.exp(-l3))) < 1e-15 and abs(g[0] - 0.75) < 1e-7
+    assert abs(g[0] + g[1] - 1.0) < 1e-15  # sigmoid(-s) = 1 - sigmoid(s)
+    assert g[2] == 1.0 and 0 < g[3] < 1e-17  # sigmoid(40) rounds to 1 in double; sigmoid(-40) = 4.2e-18
+    # the gate is the sigmoid of the plain dot product
+    wr = S.shared_gate_weight(S.custom(T=5, H=H, E=2, K=1, I=32))
+    dot = x.astype(np.float64) @ wr.astype(np.float64)
+    assert np.abs(oracle.shared_gate(x, wr) - 1 / (1 + np.exp(-dot))).max() < 1e-15
+
+
+@pytest.mark.parametrize("fmt", ["q2_sym", "q2_0"])
+def test_layer_with_shared_expert_matches_independent_dense_layer(fmt):
+    s = S.custom(T=20, H=96, E=6, K=3, I=64, fmt=fmt, shared=True)
+    x, wr = S.activations(s), S.router_weight(s)
+    exps = [S.expert(s, e) for e in range(s.E + 1)]
+    wg = S.shared_gate_weight(s)
+    out = oracle.layer(x, wr, None, lambda e: exps[e], s.E, s.K, fmt=fmt, shared=(exps[s.E], wg))
+    ids, p, y = _layer_dense(x, wr, None, exps[: s.E], s.K, fmt)
+    qx, sx = oracle.quantize(x)
+    xd = qx.astype(np.float64) * np.repeat(sx.astype(np.float64), 32, axis=1)
+    W = _dense(exps[s.E], fmt)
+    g = 1 / (1 + np.exp(-(x.astype(np.float64) @ wg.astype(np.float64))))
+    for t in range(s.T):
+        y[t] += g[t] * _ffn_dense(W, xd[t])
+    assert np.array_equal(out["ids"], ids)
+    assert np.abs(out["shared"]["g"] - g).max() < 1e-14
+    assert np.abs(out["y"] - y).max() <= 1e-10 * np.abs(y).max()
+    # the sampled-token form gives the same rows
+    tok = np.array([0, 7, 19])
+    lt = oracle.layer_tokens(x, wr, None, lambda e: exps[e], s.K, tok, fmt=fmt, shared=(exps[s.E], wg))
+    assert np.abs(lt["y"] - out["y"][tok]).max() <= 1e-12 * np.abs(y).max()
+
+
+def test_shared_expert_with_zero_gate_vector_adds_half_its_output():
+    s = S.custom(T=9, H=64, E=4, K=2, I=32, shared=True)
+    x, wr = S.activations(s), S.router_weight(s)
+    exps = [S.expert(s, e) for e in range(s.E + 1)]
+    base = oracle.layer(x, wr, None, lambda e: exps[e], s.E, s.K)
+    out = oracle.layer(x, wr, None, lambda e: exps[e], s.E, s.K, shared=(exps[s.E], np.zeros(s.H, np.float32)))
+    _, _, _, D = oracle.expert_rows(exps[s.E], *oracle.quantize(x))
+    assert np.abs(out["y"] - (base["y"] + 0.5 * D)).max() <= 1e-14 * np.abs(out["y"]).max()
 
 
 @pytest.mark.parametrize("skewed,fmt", [(False, "q2_sym"), (True, "q2_sym"), (False, "q2_0")])
