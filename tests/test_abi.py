@@ -91,6 +91,29 @@ def test_prefill_rejects_bad_arguments_on_the_host(qm, K, T, fmt, H, I, E, code)
     assert qm.strata_moe_last_error() != ""
 
 
+def test_shared_expert_sizes_and_limits_on_the_host(qm):
+    # a shared expert widens the grouping to K + 1 pairs of E + 1 experts
+    lib = qm.library()
+    b = ctypes.c_size_t()
+    st = _experts_struct(qm)
+    assert lib.strata_moe_workspace_bytes(8192, 10, ctypes.byref(st), ctypes.byref(b)) == 0
+    plain = b.value
+    st.shared_gate = 1 << 12
+    assert lib.strata_moe_workspace_bytes(8192, 10, ctypes.byref(st), ctypes.byref(b)) == 0
+    assert b.value >= plain + 8192 * 1024 * 2  # at least one more row of H codes per token
+    for K, E in ((16, 512), (10, 1024)):  # no pair slot left; no expert index left
+        st = _experts_struct(qm, E=E)
+        st.shared_gate = 1 << 12
+        rc = lib.strata_moe_prefill(ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.byref(st), 8, K,
+                                    ctypes.c_void_p(16), None)
+        assert rc == qm.EINVAL and "shared" in qm.strata_moe_last_error()
+    st = _experts_struct(qm)
+    st.shared_gate = (1 << 12) + 4  # not 16-byte aligned
+    assert lib.strata_moe_workspace_bytes(8, 10, ctypes.byref(st), ctypes.byref(b)) == qm.EINVAL
+    # the C struct's last field: ctypes offset after the router_prepared pointer
+    assert qm.ExpertsStruct.shared_gate.offset == qm.ExpertsStruct.router_prepared.offset + ctypes.sizeof(ctypes.c_void_p)
+
+
 def test_prefill_rejects_short_strides_and_null(qm):
     lib = qm.library()
     st = _experts_struct(qm)
