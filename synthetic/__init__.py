@@ -77,6 +77,8 @@ EXTRA_SHAPES = {
     "pages_q2_0_2k": LayerShape("pages_q2_0_2k", T=2048, H=2560, E=512, K=10, I=640, fmt="q2_0"),
     # a short chunk (about 5 rows per expert): the small-T end of the range
     "short_256": LayerShape("short_256", T=256, H=2560, E=512, K=10, I=1024),
+    # a decode-sized window (320 pairs over 512 experts: mostly one row per hit expert)
+    "window_32": LayerShape("window_32", T=32, H=2560, E=512, K=10, I=1024),
     # the MoE half with its shared expert: the 8192-token chunk, and the pages'
     # geometry (there the shared expert has the routed experts' width, 640)
     "chunk_8k_shared": LayerShape("chunk_8k_shared", T=8192, H=2560, E=512, K=10, I=1024, shared=True),

@@ -287,7 +287,7 @@ def _check_grouping_props(g, T, K, E):
 
 
 @pytest.mark.parametrize("name", ["stream_all_1k", "chunk_8k", "skewed_4k", "long_32k", "pages_q2_0_2k",
-                                  "chunk_8k_shared", "pages_shared_2k"])
+                                  "chunk_8k_shared", "pages_shared_2k", "short_256", "window_32"])
 def test_full_layer_sampled(qm, name):
     s = S.shape(name)
     ex = gpu_experts(s)
