@@ -61,7 +61,7 @@ def _load():
     lib.oracle_quantize.argtypes = [P, i64, i32, P, P]
     lib.oracle_expert_rows.argtypes = [P, P, P, P, i32, i32, ctypes.c_double, i64, P, P, P, P, P, P]
     lib.oracle_combine.argtypes = [P, P, P, i64, i32, i32, P]
-    lib.oracle_rows_multi.argtypes = [P, P, P, P, P, i32, i32, ctypes.c_double, i64, P, P, P, P, P]
+    lib.oracle_rows_multi.argtypes = [P, P, P, P, P, i32, i32, ctypes.c_double, i64, P, P, P, P, P, P]
     lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_half_to_double.restype = ctypes.c_double
     lib.oracle_num_threads.restype = ctypes.c_int
@@ -234,9 +234,10 @@ def layer(x, wr, bias, get_expert, E: int, K: int, want_h: bool = False, fmt: st
                 qh=qh, sh=sh, h=h, D=D, y=y, shared=sh_term)
 
 
-def rows_multi(experts: list, which, qx, sx, fmt: str = "q2_sym"):
+def rows_multi(experts: list, which, qx, sx, fmt: str = "q2_sym", want_h: bool = False):
     """c5..c7 for rows of several experts: row r goes through experts[which[r]].
-    Returns (qh, sh, D)."""
+    Returns (qh, sh, D), plus h (the exact SwiGLU output, double) first if
+    want_h."""
     keep = [(_c(e.codes_gu, np.uint8), _c(e.scales_gu, np.uint16), _c(e.codes_d, np.uint8),
              _c(e.scales_d, np.uint16)) for e in experts]
     H = keep[0][0].shape[1]
@@ -249,11 +250,11 @@ def rows_multi(experts: list, which, qx, sx, fmt: str = "q2_sym"):
     qh = np.empty((n, I), np.int8)
     sh = np.empty((n, I // BLOCK), np.float32)
     D = np.empty((n, H), np.float64)
+    h = np.empty((n, I), np.float64) if want_h else None
     if n:
         _load().oracle_rows_multi(tables[0], tables[1], tables[2], tables[3], _p(which), H, I, code_zero(fmt), n,
-                                  _p(qx), _p(sx),
-                                  _p(qh), _p(sh), _p(D))
-    return qh, sh, D
+                                  _p(qx), _p(sx), _p(h), _p(qh), _p(sh), _p(D))
+    return (h, qh, sh, D) if want_h else (qh, sh, D)
 
 
 def layer_tokens(x, wr, bias, get_expert, K: int, tokens, fmt: str = "q2_sym", shared=None) -> dict:
@@ -263,7 +264,7 @@ def layer_tokens(x, wr, bias, get_expert, K: int, tokens, fmt: str = "q2_sym", s
     which only orders rows; so each sampled token is routed, quantized and
     pushed through its K experts on its own, and y[t] is exactly the full
     layer's y[t].  Returns per sampled token: ids, p, qx, sx, the K H-code
-    rows, their scales and y."""
+    rows, their scales, the exact SwiGLU outputs h they round and y."""
     tokens = np.asarray(tokens, dtype=np.int64)
     xs = x[tokens]
     logits = router_logits(xs, wr, bias)
@@ -276,15 +277,17 @@ def layer_tokens(x, wr, bias, get_expert, K: int, tokens, fmt: str = "q2_sym", s
     which = np.array([slot_of[int(e)] for e in ids.reshape(-1)], np.int32)
     # pairs token-major: row s*K + k is token s through its k-th expert
     rows = np.repeat(np.arange(S), K)
-    qh, sh, D = rows_multi([get_expert(e) for e in used], which, qx[rows], sx[rows], fmt)
+    h, qh, sh, D = rows_multi([get_expert(e) for e in used], which, qx[rows], sx[rows], fmt, want_h=True)
     I = qh.shape[1]
     # c8 with the pairs laid out token-major: row s*K + k holds D of (s, k)
     y = combine(D, p, np.arange(S * K, dtype=np.int32))
     D = D.reshape(S, K, H)
     qh = qh.reshape(S, K, I)
     sh = sh.reshape(S, K, I // BLOCK)
+    h = h.reshape(S, K, I)
     sh_term = None
     if shared is not None:
         sh_term = _shared_term(shared, qx, sx, xs, False, fmt)
         y = y + sh_term["g"][:, None] * sh_term["D"]
-    return dict(tokens=tokens, logits=logits, ids=ids, p=p, qx=qx, sx=sx, qh=qh, sh=sh, D=D, y=y, shared=sh_term)
+    return dict(tokens=tokens, logits=logits, ids=ids, p=p, qx=qx, sx=sx, qh=qh, sh=sh, h=h, D=D, y=y,
+                shared=sh_term)

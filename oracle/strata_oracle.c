@@ -131,39 +131,41 @@ void oracle_topk_softmax(const double* logits, int64_t T, int32_t E, int32_t K, 
 }
 
 /* -------------------------------------------------------------- c3 grouping
- * [prefill.cpp] the MMQ path's host grouping: count the pairs of each expert,
- * offsets by exclusive scan, then walk the pairs in order: slot[i] = the next
- * row of expert ids[i], src[row] = the token i / K.  [moe_fused] says the GPU
- * grouping may order rows within an expert freely; the reading taken is this
- * stable order (ascending pair index), which is also ascending token order.
- * Returns -1 (and writes nothing useful) if an id is out of range, as the
- * pages' "routed id out of range" check does.
+ * [moe_fused] group(): the routed pairs i = t*K + k are laid out expert by
+ * expert; slot[i] is the row pair i lands in and src[row] the token (i / K)
+ * that row reads.  The pages leave the order inside one expert open; the
+ * reading taken is ascending pair index (the order of the MMQ path's host
+ * grouping in [prefill.cpp], and ascending token order).  So the rows are the
+ * pairs sorted by the key (expert id, pair index), a total order: this
+ * function sorts the pair indices by that key and reads every table off the
+ * sorted list.  offsets[e] is the first row whose expert is >= e.  Returns -1
+ * if an id is outside [0, E), as the pages' "routed id out of range" check.
  * ids [T*K], offsets [E+1], src [T*K], slot [T*K]. */
+static int ascending_i64(const void* a, const void* b) {
+    const int64_t x = *(const int64_t*)a, y = *(const int64_t*)b;
+    return x < y ? -1 : (x > y ? 1 : 0);
+}
+
 int oracle_group(const int32_t* ids, int64_t T, int32_t K, int32_t E, int32_t* offsets, int32_t* src,
                  int32_t* slot) {
     const int64_t n = T * K;
-    int64_t* cnt = (int64_t*)calloc((size_t)E, sizeof(int64_t));
-    for (int64_t i = 0; i < n; ++i) {
-        if (ids[i] < 0 || ids[i] >= E) {
-            free(cnt);
-            return -1;
-        }
-        ++cnt[ids[i]];
+    for (int64_t i = 0; i < n; ++i)
+        if (ids[i] < 0 || ids[i] >= E) return -1;
+    /* the key (expert id, pair index) as one integer: id * 2^32 + i (i < 2^31) */
+    int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n > 0 ? n : 1));
+    for (int64_t i = 0; i < n; ++i) key[i] = (int64_t)ids[i] * ((int64_t)1 << 32) + i;
+    qsort(key, (size_t)n, sizeof(int64_t), ascending_i64);
+    int64_t row = 0;
+    for (int32_t e = 0; e <= E; ++e) {
+        while (row < n && key[row] / ((int64_t)1 << 32) < e) ++row;
+        offsets[e] = (int32_t)row;
     }
-    int64_t r = 0;
-    for (int32_t e = 0; e < E; ++e) {
-        offsets[e] = (int32_t)r;
-        r += cnt[e];
+    for (int64_t r = 0; r < n; ++r) {
+        const int64_t i = key[r] % ((int64_t)1 << 32); /* the pair in row r */
+        slot[i] = (int32_t)r;
+        src[r] = (int32_t)(i / K);
     }
-    offsets[E] = (int32_t)r;
-    int64_t* fill = cnt; /* reuse: next free row of each expert */
-    for (int32_t e = 0; e < E; ++e) fill[e] = offsets[e];
-    for (int64_t i = 0; i < n; ++i) {
-        const int64_t row = fill[ids[i]]++;
-        slot[i] = (int32_t)row;
-        src[row] = (int32_t)(i / K);
-    }
-    free(cnt);
+    free(key);
     return 0;
 }
 
@@ -274,12 +276,14 @@ void oracle_expert_rows(const uint8_t* cgu, const uint16_t* sgu, const uint8_t* 
  * the loop over rows spread across threads). */
 void oracle_rows_multi(const uint8_t* const* cgu, const uint16_t* const* sgu, const uint8_t* const* cd,
                        const uint16_t* const* sd, const int32_t* which, int32_t H, int32_t I, double z,
-                       int64_t nrows, const int8_t* qx, const float* sx, int8_t* qh_out, float* sh_out, double* D) {
+                       int64_t nrows, const int8_t* qx, const float* sx, double* h_out, int8_t* qh_out,
+                       float* sh_out, double* D) {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < nrows; ++r) {
         const int32_t w = which[r];
-        oracle_expert_rows(cgu[w], sgu[w], cd[w], sd[w], H, I, z, 1, qx + r * H, sx + r * (H / QBLOCK), NULL,
-                           qh_out ? qh_out + r * I : NULL, sh_out ? sh_out + r * (I / QBLOCK) : NULL, D + r * H);
+        oracle_expert_rows(cgu[w], sgu[w], cd[w], sd[w], H, I, z, 1, qx + r * H, sx + r * (H / QBLOCK),
+                           h_out ? h_out + r * I : NULL, qh_out ? qh_out + r * I : NULL,
+                           sh_out ? sh_out + r * (I / QBLOCK) : NULL, D + r * H);
     }
 }
 
