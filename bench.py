@@ -2,17 +2,27 @@
 """Benchmark of the routed-expert prompt MoE layer on one MI355X.
 
 A step is one strata_moe_prefill call -- router, top-K, grouping, int8
-quantization, gate/up + SwiGLU + int8 H, down + weighted scatter-add -- over a
+quantization, gate/up + SwiGLU + int8 H, down + the weighted combine -- over a
 chunk of T tokens whose inputs, packed experts and prepared router matrix
 (strata_moe_prepare_router, once, like the packing; --router-per-call prepares
-it inside every step instead) are already resident in HBM.  Default workload: T = 8192, H = 2560, E = 512 experts, top-10, expert FFN
-I = 1024, seeded synthetic inputs (the pages' own prompts and trained pack are
-not available).
+it inside every step instead) are already resident in HBM.  Default workload:
+T = 8192, H = 2560, E = 512 experts, top-10, expert FFN I = 1024, seeded
+synthetic inputs (the pages' own prompts and trained pack are not available).
+The same run also times the 1024-token chunk (the weight-streaming end) on the
+same experts and reports it in the same JSON line.
 
 Prints one JSON line on stdout (progress goes to stderr):
   value        tokens/s of the layer over the timed steps (one GPU)
-  roofline     the dominant kernel's achieved rate against its peak, measured
-               with HIP events on the launch stream over the timed steps
+  layer        whole-layer int8-equivalent TOPS against the int8 and fp16
+               MFMA peaks, median / min / cold-cache step times
+  roofline     the dominant kernel's achieved rate against the int8 peak
+               (its fp16 fraction beside it), measured with HIP events on the
+               launch stream over the timed steps
+  stream_all_1k  the 1024-token chunk: ms per step, the hit experts' weight
+               bytes per second against the 8 TB/s HBM peak
+  streamed     the same layer with every expert streamed from pinned host
+               memory through rings of 96, 384 and 512 device slots
+  mfma_measured  the matrix unit's rates measured on this device
   cpu_baseline the CPU oracle (double precision) timed on this host on a
                bounded sample of the same workload
 
@@ -25,6 +35,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -33,8 +44,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "MoE prefill layer tokens/s at T=8192 (512 exp, top-10); % int8 MFMA / HBM peak"
+PEAK_I8_TOPS = 5000.0     # MI355X dense int8 MFMA (5.0 POPS)
 PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
+SECOND = "stream_all_1k"  # the weight-streaming chunk reported beside the headline
 
 
 def log(msg: str) -> None:
@@ -50,6 +63,14 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--router-per-call", action="store_true",
                     help="prepare the router matrix inside every layer call instead of once with the experts")
+    ap.add_argument("--second-steps", type=int, default=200,
+                    help="timed steps of the 1024-token chunk (0 = skip it)")
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="steps timed after a 512 MiB scrub each (cold Infinity Cache; 0 = skip)")
+    ap.add_argument("--no-probe", action="store_true", help="skip the matrix-unit rate measurements")
+    ap.add_argument("--rings", default="96,384,512",
+                    help="ring sizes (slots) of the streamed-experts measurement, comma separated ('' = skip)")
+    ap.add_argument("--ring-steps", type=int, default=5, help="timed steps per ring size")
     ap.add_argument("--cpu-tokens", type=int, default=4096, help="tokens in the CPU-oracle sample (0 = skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB after flushing the Infinity Cache "
@@ -77,6 +98,49 @@ def measured_traffic(kernel: str, workload: str):
     if not m_sha or not m_b or m_sha.group(1) != kernel_source_sha():
         return None
     return float(m_b.group(1))
+
+
+def time_steps(qm, torch, s, x, wr, experts, out, steps: int, warmup: int, scrub=None):
+    """Runs warmup + steps layer calls; returns (ms per step over the whole
+    timed region, per-step ms list, per-kernel mean ms).  With scrub (a
+    device tensor), each timed step is preceded by a write of it (outside the
+    step's events), so the step starts with a cold Infinity Cache."""
+    for _ in range(warmup):
+        qm.strata_moe_prefill(x, wr, experts, s.K, out)
+    torch.cuda.synchronize()
+    qm.strata_moe_timing(True, steps)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        if scrub is not None:
+            scrub.fill_(float(i))
+        evs[i][0].record()
+        qm.strata_moe_prefill(x, wr, experts, s.K, out)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in evs]
+    kt = qm.strata_moe_timing_read()
+    qm.strata_moe_timing(False)
+    kernel_ms = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in kt.items()}
+    return per, kernel_ms
+
+
+def region_ms(qm, torch, s, x, wr, experts, out, steps: int):
+    """ms per step over one timed region of back-to-back steps, bracketed by
+    synchronisation and two events (the contract's timing)."""
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        qm.strata_moe_prefill(x, wr, experts, s.K, out)
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps, 1e3 * (time.perf_counter() - wall0) / steps
+
+
+def hit_experts(torch, ids, nexp: int) -> int:
+    return int((torch.bincount(ids.reshape(-1).long(), minlength=nexp) > 0).sum())
 
 
 def main() -> int:
@@ -112,6 +176,7 @@ def main() -> int:
             canon[e0 + i] = p
         experts.pack(e0, np.stack([p.codes_gu for p in parts]), np.stack([p.scales_gu for p in parts]),
                      np.stack([p.codes_d for p in parts]), np.stack([p.scales_d for p in parts]))
+    base_experts = experts
     bias_np = S.router_bias(s, args.seed)
     bias = None if bias_np is None else torch.from_numpy(bias_np).to(dev)
     experts = experts.with_router_bias(bias)
@@ -134,24 +199,21 @@ def main() -> int:
     dbg_ids = qm.strata_moe_prefill_debug(x, wr, experts, s.K, out)["ids"]  # routing of this chunk (hit experts)
     torch.cuda.synchronize()
 
+    # the contract's timed region: K back-to-back steps between two events
     log(f"timing {args.steps} steps")
-    qm.strata_moe_timing(True, args.steps)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        qm.strata_moe_prefill(x, wr, experts, s.K, out)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
-    kt = qm.strata_moe_timing_read()
-    qm.strata_moe_timing(False)
+    ms_per_step, wall_ms = region_ms(qm, torch, s, x, wr, experts, out, args.steps)
+    # the same steps again with events around every step and every kernel
+    per, kernel_ms = time_steps(qm, torch, s, x, wr, experts, out, args.steps, 0)
+    log(f"{ms_per_step:.3f} ms/step (wall {wall_ms:.3f}); per step median {statistics.median(per):.3f}, "
+        f"min {min(per):.3f}; per kernel " + ", ".join(f"{k} {v:.3f}" for k, v in kernel_ms.items()))
+    cold = None
+    if args.cold_steps > 0:
+        scrub = torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
+        per_cold, _ = time_steps(qm, torch, s, x, wr, experts, out, args.cold_steps, 0, scrub=scrub)
+        cold = statistics.median(per_cold)
+        del scrub
+        log(f"cold Infinity Cache: median {cold:.3f} ms/step over {args.cold_steps} steps")
     qm.strata_moe_set_workspace(None)
-    kernel_ms = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in kt.items()}
-    log(f"{ms_per_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}); per kernel "
-        + ", ".join(f"{k} {v:.3f}" for k, v in kernel_ms.items()))
 
     if args.copy_probe_mib:
         a = torch.empty((args.copy_probe_mib << 20) // 4, dtype=torch.float32, device=dev).uniform_()
@@ -161,30 +223,113 @@ def main() -> int:
         torch.cuda.synchronize()
         torch.neg(a, out=b)  # reads and writes copy_probe_mib MiB
         torch.cuda.synchronize()
-        del flush
+        del flush, a, b
         log(f"copy probe: {args.copy_probe_mib} MiB")
 
     n = s.T * (s.K + s.shared)  # grouped rows: K routed pairs per token, plus the shared expert's
-    flops = {"gate_up": 2.0 * n * 2 * s.I * s.H, "down": 2.0 * n * s.H * s.I}
+    ops = {"gate_up": 2.0 * n * 2 * s.I * s.H, "down": 2.0 * n * s.H * s.I}
+    layer_ops = 2.0 * n * 3 * s.H * s.I
+    expert_bytes = 3 * s.H * s.I * (2 / 8 + 2 / 32)  # packed gate, up and down of one expert
     dominant = max(kernel_ms, key=kernel_ms.get)
-    traffic = measured_traffic(dominant, s.name) if dominant in flops else None
-    if dominant in flops and n / s.E >= 64:
+    traffic = measured_traffic(dominant, s.name) if dominant in ops else None
+    if dominant in ops and n / s.E >= 64:
         # many rows per expert: the grouped GEMM is a dense contraction
-        achieved = flops[dominant] / (kernel_ms[dominant] * 1e-3) / 1e12
-        roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic}
-    elif dominant in flops:
+        achieved = ops[dominant] / (kernel_ms[dominant] * 1e-3) / 1e12
+        roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_I8_TOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_I8_TOPS, 4), "traffic": traffic,
+                    "peak_f16": PEAK_F16_TFLOPS, "frac_f16": round(achieved / PEAK_F16_TFLOPS, 4)}
+    elif dominant in ops:
         # few rows per expert: the GEMM streams the hit experts' packed weights once
-        hit = int((torch.bincount(dbg_ids.reshape(-1).long(), minlength=s.E + s.shared) > 0).sum())
-        rows = 2 * s.I if dominant == "gate_up" else s.H
-        kd = s.H if dominant == "gate_up" else s.I
-        wbytes = hit * rows * kd * (2 / 8 + 2 / 32)
-        achieved = wbytes / (kernel_ms[dominant] * 1e-3) / 1e9
+        hit = hit_experts(torch, dbg_ids, s.E + s.shared)
+        share = (2 / 3) if dominant == "gate_up" else (1 / 3)
+        achieved = hit * expert_bytes * share / (kernel_ms[dominant] * 1e-3) / 1e9
         roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
     else:
         roofline = {"kernel": dominant, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": None, "traffic": None}
+    layer_tops = layer_ops / (ms_per_step * 1e-3) / 1e12
+    layer = {"int8_ops_per_step": layer_ops, "tops": round(layer_tops, 2),
+             "frac_int8": round(layer_tops / PEAK_I8_TOPS, 4), "frac_f16": round(layer_tops / PEAK_F16_TFLOPS, 4),
+             "median_ms": round(statistics.median(per), 4), "min_ms": round(min(per), 4),
+             "cold_ms": None if cold is None else round(cold, 4),
+             "hit_experts": hit_experts(torch, dbg_ids, s.E + s.shared)}
+
+    second = None
+    if args.second_steps > 0 and s.name != SECOND:
+        s2 = S.shape(SECOND)
+        if (s2.E, s2.H, s2.I, s2.fmt) == (s.E, s.H, s.I, s.fmt) and not s.shared and not s.skewed:
+            x2 = torch.from_numpy(S.activations(s2, args.seed)).to(dev)
+            ex2 = base_experts if args.router_per_call else base_experts.with_prepared_router(wr)
+            out2 = torch.empty_like(x2)
+            ms2, _ = region_ms(qm, torch, s2, x2, wr, ex2, out2, 10)  # warm
+            ms2, _ = region_ms(qm, torch, s2, x2, wr, ex2, out2, args.second_steps)
+            per2, kms2 = time_steps(qm, torch, s2, x2, wr, ex2, out2, min(args.second_steps, 100), 0)
+            ids2 = qm.strata_moe_prefill_debug(x2, wr, ex2, s2.K, out2)["ids"]
+            torch.cuda.synchronize()
+            hit2 = hit_experts(torch, ids2, s2.E)
+            wbytes = hit2 * expert_bytes
+            second = {"workload": s2.name, "T": s2.T, "ms_per_step": round(ms2, 4),
+                      "median_ms": round(statistics.median(per2), 4), "min_ms": round(min(per2), 4),
+                      "tokens_per_s": round(s2.T / (ms2 * 1e-3), 1), "hit_experts": hit2,
+                      "weight_bytes": wbytes, "weight_gbs": round(wbytes / (ms2 * 1e-3) / 1e9, 1),
+                      "frac_hbm": round(wbytes / (ms2 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                      "kernel_ms": {k: round(v, 4) for k, v in kms2.items()}}
+            log(f"{s2.name}: {ms2:.3f} ms/step, hit experts' weights at {second['weight_gbs']} GB/s "
+                f"({100 * second['frac_hbm']:.1f}% of 8 TB/s)")
+
+    streamed = None
+    rings = [int(r) for r in args.rings.split(",") if r.strip()]
+    if rings and not s.shared:
+        # the same experts in pinned host memory, expert e's gate/up and down blobs
+        # side by side (one DMA each), copied from the resident blobs
+        host = qm.HostExperts(s.E, s.H, s.I, fmt=s.fmt)
+        hv = host.host.view(s.E, host.slot_bytes)
+        hv[:, :host.gate_up_bytes].copy_(base_experts.gate_up.view(s.E, -1)[:, :host.gate_up_bytes])
+        hv[:, host.gate_up_bytes:].copy_(base_experts.down.view(s.E, -1)[:, :host.slot_bytes - host.gate_up_bytes])
+        host = host.with_router_bias(bias)
+        if not args.router_per_call:
+            host = host.with_prepared_router(wr)
+        y_res = qm.strata_moe_prefill(x, wr, experts, s.K, torch.empty_like(x))
+        streamed = {"bytes_per_step": s.E * host.slot_bytes, "ms_per_step": {}, "host_to_device_gbs": {},
+                    "bitwise_equal_to_resident": True}
+        for R in rings:
+            ring = qm.Ring(R, s.H, s.I, device=dev)
+            ys = torch.empty_like(x)
+            for _ in range(2):
+                qm.strata_moe_prefill_streamed(x, wr, host, ring, s.K, ys)
+            torch.cuda.synchronize()
+            streamed["bitwise_equal_to_resident"] &= bool(torch.equal(ys, y_res))
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            for _ in range(args.ring_steps):
+                qm.strata_moe_prefill_streamed(x, wr, host, ring, s.K, ys)
+            ev1.record()
+            torch.cuda.synchronize()
+            ms = ev0.elapsed_time(ev1) / args.ring_steps
+            ring.close()
+            streamed["ms_per_step"][str(R)] = round(ms, 3)
+            streamed["host_to_device_gbs"][str(R)] = round(streamed["bytes_per_step"] / (ms * 1e-3) / 1e9, 1)
+            log(f"streamed experts, ring of {R} slots: {ms:.3f} ms/step "
+                f"({streamed['host_to_device_gbs'][str(R)]} GB/s of expert blobs over the host link)")
+        del host
+
+    mfma = None
+    if not args.no_probe:
+        from quantized_routed_expert_logits_amd import probe
+
+        mfma = {}
+        for kind in probe.KINDS:
+            rate, _ = probe.strata_probe_mfma_rate(kind)
+            mfma[kind] = round(rate / 1e12, 1)
+        f16_blocks, _ = probe.strata_probe_scaled_blocks(False)
+        i8_blocks, _ = probe.strata_probe_scaled_blocks(True)
+        mfma["unit"] = "TOP/s (2 M N K per MFMA, 8 chains per wave, all SIMDs)"
+        mfma["scaled_blocks_f16"] = round(f16_blocks / 1e12, 3)
+        mfma["scaled_blocks_i8"] = round(i8_blocks / 1e12, 3)
+        mfma["scaled_blocks_unit"] = "T output-blocks/s (32-wide block products, each scaled into fp32)"
+        log("MFMA rates (TOP/s): " + ", ".join(f"{k} {mfma[k]}" for k in probe.KINDS)
+            + f"; scaled blocks fp16 {mfma['scaled_blocks_f16']} vs int8 {mfma['scaled_blocks_i8']} T/s")
 
     cpu = None
     if args.cpu_tokens > 0:
@@ -220,8 +365,12 @@ def main() -> int:
                    "router_matrix": "prepared per call" if args.router_per_call else "prepared once",
                    "shared_expert": bool(s.shared)},
         "kernel_ms": {k: round(v, 4) for k, v in kernel_ms.items()},
-        "int8_ops_per_step": 2.0 * n * 3 * s.H * s.I,
+        "int8_ops_per_step": layer_ops,
+        "layer": layer,
         "roofline": roofline,
+        "stream_all_1k": second,
+        "streamed": streamed,
+        "mfma_measured": mfma,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -16,7 +16,9 @@
  *      int8 per 32 values, then down (moe_fused.hpp, experts);
  *   5. the combine of each token's K rows with its routing weights.
  *
- * Every expert stays resident in device memory (no streaming ring).
+ * The experts are either resident in device memory (strata_moe_prefill) or
+ * streamed from pinned host memory through a ring of device slots while the
+ * layer runs (strata_moe_prefill_streamed).
  *
  * Conventions for every entry point:
  *   - Pointers named in the argument lists are DEVICE pointers owned by the
@@ -29,7 +31,11 @@
  *     work was enqueued; strata_moe_last_error() then describes why.
  *   - Sizes: H a multiple of 128 and I a multiple of 64, both at most 4096;
  *     1 <= K <= 16, K <= E <= 1024, T * K < 2^31.  T = 0 is a no-op.  (The
- *     single-step route entry point only needs H a multiple of 64.)
+ *     single-step route entry point only needs H a multiple of 64.)  One call
+ *     also keeps its tiled fp16 GEMM operands below 2 GiB each:
+ *     (T * K + 15 * E) * max(H, I) * 2 bytes < 2^31 (and x below 2 GiB), which
+ *     at H = 2560, K = 10, E = 512 allows up to about 41,000 tokens; longer
+ *     prompts run as several chunks (the pages' prompt path is chunked too).
  *   - Thread safety: calls may come from several host threads; calls that
  *     share the library-owned workspace of one device (the default when no
  *     workspace was set) must not overlap on different streams.
@@ -188,33 +194,102 @@ int strata_moe_prefill_debug(const float* x, const float* router_w, const strata
 
 /* ------------------------------------------- single steps (parity checks) */
 
-/* Router logits and route(): ids [T][K] int32 in rank order (ties -> lower
- * expert index), p [T][K] fp32 = softmax over the K selected logits.  bias
- * [E] or NULL.  Near-ties are settled in fp64. */
+/* Router logits and route() (Winery-Strata prefill.cpp page, Prefill::run,
+ * MoE half: the router projection, then route(logits, ids, w); the body of
+ * route() is not printed, and the reading is the K largest logits with a
+ * softmax over them): ids [T][K] int32 in rank order (ties -> lower expert
+ * index), p [T][K] fp32 = softmax over the K selected logits.  x [T][H] fp32,
+ * router_w [H][E] fp32, bias [E] or NULL.  Near-ties are settled in fp64, so
+ * the ids are those of the exact logits.  Errors: EINVAL for sizes or NULL
+ * pointers, EHIP for a failed launch. */
 int strata_moe_route(const float* x, const float* router_w, const float* bias, int64_t T, int32_t H, int32_t E,
                      int32_t K, int32_t* ids, float* p, void* stream);
 
-/* Grouping of the (token, k) pairs by expert (stable: ascending pair index).
- * offsets [E+1], src [T*K], slot [T*K].  Synchronises `stream` to check the
- * ids; returns STRATA_MOE_EDATA if any id is outside [0, E). */
+/* Grouping of the (token, k) pairs by expert (Strata compare page,
+ * moe_fused.hpp, group(): slot[i] = the row of pair i, src[row] = its token,
+ * the rows of each expert contiguous; the order inside an expert, left open
+ * there, is ascending pair index here).  ids [T][K] int32 (device); offsets
+ * [E+1], src [T*K], slot [T*K] (device, written).  Synchronises `stream` to
+ * check the ids; returns STRATA_MOE_EDATA if any id is outside [0, E). */
 int strata_moe_group(const int32_t* ids, int64_t T, int32_t K, int32_t E, int32_t* offsets, int32_t* src,
                      int32_t* slot, void* stream);
 
-/* Per-32 int8 rounding of fp32 rows: codes [rows][cols], scales
- * [rows][cols/32]; s = max|v|/127 (fp32), q = round-half-away(v/s). */
+/* Per-32 int8 rounding of fp32 rows (Strata compare page, moe_fused.hpp,
+ * quantize_act: int8 codes with one scale per 32 values; the rounding rule,
+ * not printed there, is the reading below): v [rows][cols] fp32 (cols a
+ * multiple of 32, 16-byte aligned), codes [rows][cols] int8, scales
+ * [rows][cols/32] fp32; s = max|v|/127 (fp32), q = round-half-away(v/s),
+ * both divisions IEEE fp32.  Errors: EINVAL for sizes, alignment or NULL. */
 int strata_moe_quantize(const float* v, int64_t rows, int32_t cols, int8_t* codes, float* scales, void* stream);
 
-/* Gate/up + SwiGLU + int8 H for grouped rows: qx/sx from strata_moe_quantize
- * of the layer input, offsets/src from strata_moe_group; writes qh
- * [T*K][I] and sh [T*K][I/32]. */
+/* Gate/up + SwiGLU + int8 H for grouped rows (Strata compare page,
+ * moe_fused.hpp, experts(): gate/up on the int8 input rows of each expert
+ * through src, SwiGLU, H rounded to int8 per 32 values in the epilogue): qx
+ * [T][H] int8 / sx [T][H/32] fp32 from strata_moe_quantize of the layer
+ * input, offsets [E+1] / src [T*K] from strata_moe_group (all device); writes
+ * qh [T*K][I] int8 and sh [T*K][I/32] fp32 by grouped row.  Errors: those of
+ * strata_moe_prefill's size checks. */
 int strata_moe_gate_up(const int8_t* qx, const float* sx, const int32_t* offsets, const int32_t* src, int64_t T,
                        int32_t K, const strata_moe_experts* experts, int8_t* qh, float* sh, void* stream);
 
-/* Down + combine from given H codes: out [T][H] is overwritten with
- * sum_k p[t][k] * down(qh[slot[t*K+k]]).  p [T][K]. */
+/* Down + combine from given H codes (Strata compare page, moe_fused.hpp,
+ * experts(): down into the per-slot rows that the combine reads): qh
+ * [T*K][I] int8 / sh [T*K][I/32] fp32 by grouped row, offsets / src / slot
+ * from strata_moe_group, p [T][K] fp32 (all device); out [T][H] fp32 is
+ * overwritten with sum_k p[t][k] * down(qh[slot[t*K+k]]), k ascending.
+ * Errors: those of strata_moe_prefill's size checks. */
 int strata_moe_down(const int8_t* qh, const float* sh, const int32_t* offsets, const int32_t* src,
                     const int32_t* slot, const float* p, int64_t T, int32_t K, const strata_moe_experts* experts,
                     float* out, void* stream);
+
+/* ------------------------------------------------------ streamed experts */
+
+/* A ring of device slots through which a layer's experts stream from pinned
+ * host memory while the layer runs (Winery-Strata prefill.cpp page: the
+ * streamed ring described in the comments at the top of the file, and the
+ * fused batch loop in the MoE half of Prefill::run).  Entry k of the stream
+ * (counted across calls) lands in slot k % n_slots by a host-to-device copy
+ * on the ring's copy stream; a per-slot "copied" event gates the launches
+ * that read the slot, and a per-slot "used" event, recorded on the compute
+ * stream after them, gates the next copy into it.  Opaque; one ring serves
+ * one compute stream at a time (calls on it must not overlap). */
+typedef struct strata_moe_ring strata_moe_ring;
+
+/* Device bytes of a ring of n_slots expert slots for (H, I): n_slots times
+ * one expert's gate/up plus down blob (strata_moe_packed_bytes).  Errors:
+ * EINVAL for n_slots outside [1, 65536] or H, I as strata_moe_packed_bytes. */
+int strata_moe_ring_bytes(int32_t n_slots, int32_t hidden, int32_t ffn, size_t* bytes);
+
+/* A ring over caller-owned device memory `slots` (at least
+ * strata_moe_ring_bytes, 256-byte aligned; the caller frees it after
+ * strata_moe_ring_destroy).  copy_stream: a hipStream_t of its own (not
+ * NULL, not the compute stream; default priority), on which every expert DMA
+ * is enqueued.  The library owns the ring object and its 2 x n_slots events.
+ * Errors: EINVAL for bad sizes, pointers or a NULL stream; EHIP if an event
+ * cannot be created. */
+int strata_moe_ring_create(int32_t n_slots, int32_t hidden, int32_t ffn, void* slots, size_t slot_memory_bytes,
+                           void* copy_stream, strata_moe_ring** ring);
+
+/* Waits for the ring's last copy and use, then frees the ring object (not the
+ * slot memory).  NULL is a no-op. */
+int strata_moe_ring_destroy(strata_moe_ring* ring);
+
+/* The layer of strata_moe_prefill with every expert streamed through `ring`:
+ * experts->gate_up is pinned host memory (hipHostMalloc) holding expert e's
+ * gate/up blob at gate_up + e * S and its down blob right after it, at
+ * experts->down + e * S, with S = gate_up_stride = down_stride = one ring
+ * slot (gate/up bytes + down bytes of strata_moe_packed_bytes): the layout
+ * strata_moe_pack writes with those pointers and strides.  With a shared
+ * expert it is entry E.  The experts are walked in id order in batches of at
+ * most n_slots / 3 (at least 1): each batch's launches wait for its last
+ * copy, and up to n_slots later experts are in flight meanwhile.  The output
+ * is bitwise the resident layer's (the same kernels over the same chunks).
+ * Asynchronous on `stream` and the ring's copy stream; the host blobs must
+ * stay unchanged until the copies are done.  Errors: those of
+ * strata_moe_prefill, plus EINVAL for a ring of another device or shape, a
+ * host layout other than the one above, or blobs that are not pinned. */
+int strata_moe_prefill_streamed(const float* x, const float* router_w, const strata_moe_experts* experts,
+                                strata_moe_ring* ring, int64_t T, int32_t K, float* out, void* stream);
 
 /* ----------------------------------------------------------------- timing */
 

@@ -78,6 +78,10 @@ _sig("strata_moe_group", [_P, _i64, _i32, _i32, _P, _P, _P, _P])
 _sig("strata_moe_quantize", [_P, _i64, _i32, _P, _P, _P])
 _sig("strata_moe_gate_up", [_P, _P, _P, _P, _i64, _i32, ctypes.POINTER(ExpertsStruct), _P, _P, _P])
 _sig("strata_moe_down", [_P, _P, _P, _P, _P, _P, _i64, _i32, ctypes.POINTER(ExpertsStruct), _P, _P])
+_sig("strata_moe_ring_bytes", [_i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)])
+_sig("strata_moe_ring_create", [_i32, _i32, _i32, _P, ctypes.c_size_t, _P, ctypes.POINTER(_P)])
+_sig("strata_moe_ring_destroy", [_P])
+_sig("strata_moe_prefill_streamed", [_P, _P, ctypes.POINTER(ExpertsStruct), _P, _i64, _i32, _P, _P])
 _sig("strata_moe_timing", [ctypes.c_int, _i32])
 _sig("strata_moe_timing_kinds", [])
 _sig("strata_moe_timing_name", [ctypes.c_int], ctypes.c_char_p)
@@ -90,6 +94,7 @@ EXPORTED = [
     "strata_moe_prefill", "strata_moe_prefill_debug", "strata_moe_route", "strata_moe_group",
     "strata_moe_quantize", "strata_moe_gate_up", "strata_moe_down", "strata_moe_timing",
     "strata_moe_timing_kinds", "strata_moe_timing_name", "strata_moe_timing_read",
+    "strata_moe_ring_bytes", "strata_moe_ring_create", "strata_moe_ring_destroy", "strata_moe_prefill_streamed",
 ]
 
 
@@ -124,6 +129,46 @@ def _stream(stream):
 def _dtype(t, dt, name):
     if t is not None and t.dtype != dt:
         raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+
+
+def _expect(t, name: str, shape: tuple, dt):
+    """Host-side check of one tensor argument before the C call: the library
+    takes raw pointers and trusts the sizes it is given, so a tensor of the
+    wrong shape would send its kernels past the allocation."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    _dtype(t, dt, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _one_device(**tensors):
+    """Every given tensor is a CUDA (HIP) tensor, all on one device."""
+    devs = set()
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+        devs.add(t.device)
+    if len(devs) > 1:
+        raise ValueError(f"arguments are on different devices: {sorted(str(d) for d in devs)}")
+
+
+def _check_layer_args(x, router_w, experts: "Experts", out):
+    """x [T][H], router_w [H][E], out [T][H] (fp32), on the experts' device
+    (streamed experts: their parameters' device; the blobs are in host memory)."""
+    H, E = experts.hidden, experts.n_expert
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D [T][H] tensor")
+    T = x.shape[0]
+    _expect(x, "x", (T, H), torch.float32)
+    _expect(router_w, "router_w", (H, E), torch.float32)
+    _expect(out, "out", (T, H), torch.float32)
+    blobs = {} if getattr(experts, "streamed", False) else dict(gate_up=experts.gate_up, down=experts.down)
+    _one_device(x=x, router_w=router_w, out=out, router_bias=experts.router_bias,
+                router_prepared=experts.router_prepared, shared_gate=experts.shared_gate, **blobs)
+    return T
 
 
 # ------------------------------------------------------------------- queries
@@ -178,7 +223,8 @@ class Experts:
         self.gate_up_stride, self.down_stride = strata_moe_packed_bytes(hidden, ffn)
         self.gate_up = torch.empty(nb * self.gate_up_stride, dtype=torch.uint8, device=device)
         self.down = torch.empty(nb * self.down_stride, dtype=torch.uint8, device=device)
-        _dtype(router_bias, torch.float32, "router_bias")
+        if router_bias is not None:
+            _expect(router_bias, "router_bias", (n_expert,), torch.float32)
         self.router_bias = router_bias
         self.router_prepared = None
         self.shared_gate = None
@@ -195,7 +241,8 @@ class Experts:
         """The same blobs with another router bias (or none)."""
         import copy
 
-        _dtype(router_bias, torch.float32, "router_bias")
+        if router_bias is not None:
+            _expect(router_bias, "router_bias", (self.n_expert,), torch.float32)
         other = copy.copy(self)
         other.router_bias = router_bias
         other._restruct()
@@ -222,6 +269,8 @@ class Experts:
         the layer calls must then pass the same router_w.  None: prepare per call."""
         import copy
 
+        if router_w is not None:
+            _expect(router_w, "router_w", (self.hidden, self.n_expert), torch.float32)
         other = copy.copy(self)
         other.router_prepared = None if router_w is None else strata_moe_prepare_router(router_w, stream)
         other._restruct()
@@ -275,13 +324,104 @@ def strata_moe_workspace_bytes(T: int, K: int, experts: Experts) -> int:
     return b.value
 
 
+# ---------------------------------------------------------- streamed experts
+class HostExperts(Experts):
+    """A layer's packed experts in pinned host memory, for the streamed layer:
+    expert e's gate/up blob at e * S and its down blob right after it (S =
+    one ring slot), the layout strata_moe_prefill_streamed reads.  Packing
+    runs on `device` (the library's packer) and the result is copied here."""
+
+    streamed = True
+
+    def __init__(self, n_expert: int, hidden: int, ffn: int, router_bias: torch.Tensor | None = None,
+                 device: str | torch.device = "cuda", fmt: str = "q2_sym", shared: bool = False):
+        if fmt not in FORMATS:
+            raise ValueError(f"unknown weight format {fmt!r}; one of {sorted(FORMATS)}")
+        self.n_expert, self.hidden, self.ffn, self.format = n_expert, hidden, ffn, FORMATS[fmt]
+        self.shared = bool(shared)
+        self.device = torch.device(device)
+        gu, dn = strata_moe_packed_bytes(hidden, ffn)
+        self.gate_up_bytes, self.slot_bytes = gu, gu + dn
+        self.gate_up_stride = self.down_stride = self.slot_bytes
+        nb = n_expert + self.shared
+        self.host = torch.empty(nb * self.slot_bytes, dtype=torch.uint8, pin_memory=True)
+        self.gate_up = self.host
+        self.down = self.host[gu:]
+        if router_bias is not None:
+            _expect(router_bias, "router_bias", (n_expert,), torch.float32)
+        self.router_bias = router_bias
+        self.router_prepared = None
+        self.shared_gate = None
+        self._restruct()
+
+    def pack(self, e0: int, codes_gu, scales_gu, codes_d, scales_d, stream=None):
+        """Pack experts [e0, e0 + len(codes_gu)) from canonical arrays on the
+        device, then copy the blobs into their host places."""
+        ne = len(codes_gu)
+        staging = torch.empty(ne * self.slot_bytes, dtype=torch.uint8, device=self.device)
+
+        def to_dev(a, dt):
+            if isinstance(a, np.ndarray):
+                a = torch.from_numpy(np.ascontiguousarray(a))
+            return a.to(device=self.device, dtype=dt).contiguous()
+
+        as_i16 = lambda a: a.view(np.int16) if isinstance(a, np.ndarray) else a  # noqa: E731
+        cg, sg = to_dev(codes_gu, torch.uint8), to_dev(as_i16(scales_gu), torch.int16)
+        cd, sd = to_dev(codes_d, torch.uint8), to_dev(as_i16(scales_d), torch.int16)
+        assert cg.shape == (ne, 2 * self.ffn, self.hidden) and cd.shape == (ne, self.hidden, self.ffn)
+        strata_moe_pack(cg, sg, cd, sd, 0, ne, self.hidden, self.ffn, staging, self.slot_bytes,
+                        staging[self.gate_up_bytes:], self.slot_bytes, stream)
+        self.host[e0 * self.slot_bytes:(e0 + ne) * self.slot_bytes].copy_(staging)
+
+
+class Ring:
+    """A ring of n_slots device slots (torch memory) with a copy stream of its
+    own (default priority) and the library's ring object over them."""
+
+    def __init__(self, n_slots: int, hidden: int, ffn: int, device: str | torch.device = "cuda"):
+        b = ctypes.c_size_t()
+        _check(_lib.strata_moe_ring_bytes(n_slots, hidden, ffn, ctypes.byref(b)), "strata_moe_ring_bytes")
+        self.n_slots, self.hidden, self.ffn = n_slots, hidden, ffn
+        self.slots = torch.empty(b.value, dtype=torch.uint8, device=device)
+        self.copy_stream = torch.cuda.Stream(device=device)
+        h = _P()
+        _check(_lib.strata_moe_ring_create(n_slots, hidden, ffn, _ptr(self.slots), b.value,
+                                           ctypes.c_void_p(self.copy_stream.cuda_stream), ctypes.byref(h)),
+               "strata_moe_ring_create")
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            _lib.strata_moe_ring_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # pragma: no cover (interpreter shutdown)
+            pass
+
+
+def strata_moe_prefill_streamed(x: torch.Tensor, router_w: torch.Tensor, experts: HostExperts, ring: Ring, K: int,
+                                out: torch.Tensor, stream=None) -> torch.Tensor:
+    if not isinstance(experts, HostExperts):
+        raise TypeError("streamed experts live in pinned host memory: use HostExperts")
+    T = _check_layer_args(x, router_w, experts, out)
+    if ring.handle is None:
+        raise ValueError("the ring is closed")
+    if (ring.hidden, ring.ffn) != (experts.hidden, experts.ffn):
+        raise ValueError("the ring was made for other expert sizes")
+    if ring.slots.device != x.device:
+        raise ValueError("the ring is on another device")
+    _check(_lib.strata_moe_prefill_streamed(_ptr(x), _ptr(router_w), ctypes.byref(experts.struct), ring.handle, T, K,
+                                            _ptr(out), _stream(stream)), "strata_moe_prefill_streamed")
+    return out
+
+
 # --------------------------------------------------------------------- layer
 def strata_moe_prefill(x: torch.Tensor, router_w: torch.Tensor, experts: Experts, K: int, out: torch.Tensor,
                        stream=None) -> torch.Tensor:
-    _dtype(x, torch.float32, "x")
-    _dtype(router_w, torch.float32, "router_w")
-    _dtype(out, torch.float32, "out")
-    T = x.shape[0]
+    T = _check_layer_args(x, router_w, experts, out)
     _check(_lib.strata_moe_prefill(_ptr(x), _ptr(router_w), ctypes.byref(experts.struct), T, K, _ptr(out),
                                    _stream(stream)), "strata_moe_prefill")
     return out
@@ -289,6 +429,7 @@ def strata_moe_prefill(x: torch.Tensor, router_w: torch.Tensor, experts: Experts
 
 def strata_moe_prefill_debug(x, router_w, experts: Experts, K: int, out, stream=None) -> dict:
     """The layer plus its intermediates (ids, p, offsets, src, slot, qx, sx, qh, sh) as device tensors."""
+    _check_layer_args(x, router_w, experts, out)
     T, H = x.shape
     sh = experts.shared_gate is not None  # the shared expert: pair slot K of each token, expert n_expert
     Kg = K + sh
@@ -312,8 +453,19 @@ def strata_moe_prefill_debug(x, router_w, experts: Experts, K: int, out, stream=
 
 # -------------------------------------------------------------- single steps
 def strata_moe_route(x, router_w, bias, K: int, ids=None, p=None, stream=None):
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or not isinstance(router_w, torch.Tensor) or router_w.dim() != 2:
+        raise ValueError("x must be [T][H] and router_w [H][E]")
     T, H = x.shape
     E = router_w.shape[1]
+    _expect(x, "x", (T, H), torch.float32)
+    _expect(router_w, "router_w", (H, E), torch.float32)
+    if bias is not None:
+        _expect(bias, "bias", (E,), torch.float32)
+    if ids is not None:
+        _expect(ids, "ids", (T, K), torch.int32)
+    if p is not None:
+        _expect(p, "p", (T, K), torch.float32)
+    _one_device(x=x, router_w=router_w, bias=bias, ids=ids, p=p)
     ids = torch.empty((T, K), dtype=torch.int32, device=x.device) if ids is None else ids
     p = torch.empty((T, K), dtype=torch.float32, device=x.device) if p is None else p
     _check(_lib.strata_moe_route(_ptr(x), _ptr(router_w), _ptr(bias), T, H, E, K, _ptr(ids), _ptr(p),
@@ -322,7 +474,10 @@ def strata_moe_route(x, router_w, bias, K: int, ids=None, p=None, stream=None):
 
 
 def strata_moe_group(ids, E: int, stream=None):
+    if not isinstance(ids, torch.Tensor) or ids.dim() != 2:
+        raise ValueError("ids must be a 2-D [T][K] tensor")
     _dtype(ids, torch.int32, "ids")
+    _one_device(ids=ids)
     T, K = ids.shape
     dev = ids.device
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
@@ -334,7 +489,10 @@ def strata_moe_group(ids, E: int, stream=None):
 
 
 def strata_moe_quantize(v, stream=None):
+    if not isinstance(v, torch.Tensor) or v.dim() != 2:
+        raise ValueError("v must be a 2-D [rows][cols] tensor")
     _dtype(v, torch.float32, "v")
+    _one_device(v=v)
     rows, cols = v.shape
     codes = torch.empty((rows, cols), dtype=torch.int8, device=v.device)
     scales = torch.empty((rows, cols // 32), dtype=torch.float32, device=v.device)
@@ -344,8 +502,15 @@ def strata_moe_quantize(v, stream=None):
 
 
 def strata_moe_gate_up(qx, sx, offsets, src, K: int, experts: Experts, stream=None):
+    if not isinstance(qx, torch.Tensor) or qx.dim() != 2:
+        raise ValueError("qx must be a 2-D [T][H] tensor")
     T = qx.shape[0]
-    n, I = T * K, experts.ffn
+    n, I, H, E = T * K, experts.ffn, experts.hidden, experts.n_expert
+    _expect(qx, "qx", (T, H), torch.int8)
+    _expect(sx, "sx", (T, H // 32), torch.float32)
+    _expect(offsets, "offsets", (E + 1,), torch.int32)
+    _expect(src, "src", (n,), torch.int32)
+    _one_device(qx=qx, sx=sx, offsets=offsets, src=src, gate_up=experts.gate_up)
     qh = torch.empty((n, I), dtype=torch.int8, device=qx.device)
     sh = torch.empty((n, I // 32), dtype=torch.float32, device=qx.device)
     _check(_lib.strata_moe_gate_up(_ptr(qx), _ptr(sx), _ptr(offsets), _ptr(src), T, K, ctypes.byref(experts.struct),
@@ -354,7 +519,18 @@ def strata_moe_gate_up(qx, sx, offsets, src, K: int, experts: Experts, stream=No
 
 
 def strata_moe_down(qh, sh, offsets, src, slot, p, experts: Experts, out, stream=None):
+    if not isinstance(p, torch.Tensor) or p.dim() != 2:
+        raise ValueError("p must be a 2-D [T][K] tensor")
     T, K = p.shape
+    n, I, H, E = T * K, experts.ffn, experts.hidden, experts.n_expert
+    _expect(qh, "qh", (n, I), torch.int8)
+    _expect(sh, "sh", (n, I // 32), torch.float32)
+    _expect(offsets, "offsets", (E + 1,), torch.int32)
+    _expect(src, "src", (n,), torch.int32)
+    _expect(slot, "slot", (n,), torch.int32)
+    _expect(p, "p", (T, K), torch.float32)
+    _expect(out, "out", (T, H), torch.float32)
+    _one_device(qh=qh, sh=sh, offsets=offsets, src=src, slot=slot, p=p, out=out, down=experts.down)
     _check(_lib.strata_moe_down(_ptr(qh), _ptr(sh), _ptr(offsets), _ptr(src), _ptr(slot), _ptr(p), T, K,
                                 ctypes.byref(experts.struct), _ptr(out), _stream(stream)), "strata_moe_down")
     return out

@@ -48,12 +48,36 @@ struct ChunkLists {
     int32_t* sched;   // [kSchedInts]
     int64_t cap;
     TileRows* trows;  // [tiled_rows_cap / 16]
+    // [3][E + 1] or null: per expert e (and e = E: the totals) the index of
+    // its first chunk in the big list, in the small list, and its first tile
+    // of the tiled row space.  The lists and the tiles run in expert order,
+    // so experts [e0, e1) own entries [first[e0], first[e1]) of each.
+    int32_t* first;
+};
+inline int64_t first_table_ints(int32_t E) { return 3 * ((int64_t)E + 1); }
+
+// The experts one GEMM or tile launch covers: all of them (first == null),
+// or the range [e0, e1) through the ChunkLists first table of a grouping over
+// E experts; and where expert e's blob is: blobs + e * stride, or with
+// nring > 0 in slot (ring0 + e) % nring of a ring of streamed experts
+// (blobs + slot * stride).
+struct ExpertRange {
+    const int32_t* first = nullptr;
+    int32_t E = 0, e0 = 0, e1 = 0;
+    int64_t ring0 = 0;
+    int32_t nring = 0;
 };
 inline int64_t chunk_list_cap(int64_t n, int32_t E) { return max_tiles(n, E); }
 
 // Rows of the tiled row space: every expert's rows rounded up to whole 16-row
 // tiles, so at most n + 15 E (a multiple of 16 after rounding up).
 inline int64_t tiled_rows_cap(int64_t n, int32_t E) { return (n + 15 * (int64_t)E + 15) / 16 * 16; }
+
+// Floats of the down GEMM's tiled block scales (launch_tile_h): per 16-row
+// tile, ceil(I / 128) groups of 16 rows x 4 blocks.
+inline int64_t tiled_h_scale_floats(int64_t n, int32_t E, int32_t I) {
+    return tiled_rows_cap(n, E) * ((I / kBlock + 3) / 4) * 4;
+}
 
 // fp16 values per row of the offset-pass operand of a reduction length Kd:
 // 32-block chunks, hi and lo per block.
@@ -70,18 +94,24 @@ hipError_t launch_quantize(const float* v, int64_t rows, int32_t cols, int8_t* q
 // is non-null; the row multipliers 2^e_r (127 * the row's largest
 // block scale in [2^14, 2^15) after scaling by 2^-e_r) in mult if non-null;
 // the offset-pass operand (u = -uoff * s * (block code sum) per block, hi/lo,
-// [rows][offset_operand_halves]) and its row multipliers.  uoff = 0.5 for
-// the symmetric weight map w = d (q - 1.5), 0 for Q2_0's w = d (q - 1): the
-// GEMMs multiply by d (q - 1), the offset pass adds the rest.
+// [rows][offset_operand_halves]) and its row multipliers, if uop is non-null.
+// uoff = 0.5 for the symmetric weight map w = d (q - 1.5); Q2_0's
+// w = d (q - 1) has no offset operand (the GEMMs multiply by d (q - 1), the
+// offset pass adds the rest).
 hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_t cols, float uoff, _Float16* out,
                            float* mult, _Float16* uop, float* umult, hipStream_t st);
-// The down GEMM operand q * s * 2^-e_r (fp16) of the grouped rows in the
-// tiled layout: tile t of the chunk lists' tile table holds grouped rows
-// trows[t], stored as
-// [tile][block][group g of 8 values][row within the tile][8] (one MFMA
-// fragment of a tile and block is 1 KiB in MFMA lane order; rows past a
-// tile's nrows are zero).  mult, uop, umult as launch_prescale, per grouped
-// row (all written).  tiles_cap bounds the tile count (the grid).
+// The down GEMM operand of the grouped rows in the tiled layout: tile t of
+// the chunk lists' tile table holds grouped rows trows[t]; out = their int8
+// codes q as fp16 (exact) in [tile][block][group g of 8 values][row within
+// the tile][8] (one MFMA fragment of a tile and block is 1 KiB in MFMA lane
+// order; rows past a tile's nrows are zero), sout = their block scales
+// [tile][ceil(blocks / 4)][row within the tile][4] (zero padded).  uop, umult
+// as launch_prescale, per grouped row (skipped when uop is null).
+// tiles_cap bounds the tile count (the grid).
+// With rng.first set, only the tiles of experts [rng.e0, rng.e1).
+hipError_t launch_tile_h(const int8_t* q, const float* s, const ChunkLists& cl, int64_t tiles_cap, int32_t cols,
+                         float uoff, _Float16* out, float* sout, _Float16* uop, float* umult, hipStream_t st,
+                         const ExpertRange& rng = ExpertRange());
 // The 4-wave gate/up kernel's operand in the tiled layout: tile t of the
 // chunk lists' tile table (tiles of chunks of more than kSmallRows rows only)
 // holds grouped rows trows[t], each the token src[row] of the int8 rows q
@@ -91,27 +121,28 @@ hipError_t launch_prescale(const int8_t* q, const float* s, int64_t rows, int32_
 // zeros.  tiles_cap bounds the tile count.
 hipError_t launch_gather_tiles(const int8_t* q, const float* s, const int32_t* src, const ChunkLists& cl,
                                int64_t tiles_cap, int32_t cols, _Float16* out, float* sout, hipStream_t st);
-hipError_t launch_prescale_tiled(const int8_t* q, const float* s, const ChunkLists& cl, int64_t tiles_cap,
-                                 int32_t cols, float uoff, _Float16* out, float* mult, _Float16* uop, float* umult,
-                                 hipStream_t st);
 // The layer input in one pass: launch_quantize's outputs (q8, s) and
 // launch_prescale's (codes16, mult, uop, umult), bit-identical to
-// the two launches; also clears the ZeroWords.
+// the two launches, and each row's Euclidean norm xn (fp32); also clears the
+// ZeroWords.
 hipError_t launch_quantize_prescale(const float* x, int64_t rows, int32_t cols, float uoff, int8_t* q8, float* s,
-                                   _Float16* codes16, float* mult, _Float16* uop, float* umult, hipStream_t st,
-                                   ZeroWords z);
+                                   _Float16* codes16, float* mult, float* xn, _Float16* uop, float* umult,
+                                   hipStream_t st, ZeroWords z);
 hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t st);
 
 // Router scratch: wt [E][H] fp32 (transposed weight, also read by the top-K
 // re-score), wb [Ep][H][2] fp16 (its hi/lo form in MFMA fragment order, Ep =
-// router_padded_experts(E)), wm [Ep], xm [T] (input row multipliers, used when
-// the caller passes none), pmax [H/32][E] (column maxima of 32-row tiles of
-// the weight).
+// router_padded_experts(E)), wm [Ep], wnorm [1] (the largest Euclidean norm
+// of a router column), xm [T] and xn [T] (input row multipliers and norms,
+// used when the caller passes none), pmax [H/32][E] (column maxima of 32-row
+// tiles of the weight).
 struct RouterScratch {
     float* wt;
     _Float16* wb;
     float* wm;
+    float* wnorm;
     float* xm;
+    float* xn;
     float* pmax;
 };
 // The router GEMM splits the reduction over H into router_splits() ranges
@@ -132,6 +163,8 @@ inline int64_t router_padded_experts(int32_t E) { return round_up(E, 16); }
 // wr == nullptr: rs.wt / rs.wb / rs.wm already hold wr's prepared forms
 // (launch_router_prep); otherwise they are prepared here (rs.pmax: scratch of
 // H/32 x E floats).
+// When xm is null the rows' multipliers and norms are computed into rs.xm
+// and rs.xn.
 hipError_t launch_router(const float* x, const float* xm, const float* wr, const float* bias, int64_t T, int32_t H,
                          int32_t E, const RouterScratch& rs, float* logits, hipStream_t st);
 // The router matrix's per-call forms: the transposed fp32 copy rs.wt [E][H]
@@ -139,7 +172,7 @@ hipError_t launch_router(const float* x, const float* xm, const float* wr, const
 hipError_t launch_router_prep(const float* wr, int32_t H, int32_t E, const RouterScratch& rs, hipStream_t st);
 // Byte offsets of the prepared router matrix's parts in one buffer.
 struct RouterPrepared {
-    size_t wt, wb, wm, pmax, total;
+    size_t wt, wb, wm, wnorm, pmax, total;
 };
 inline RouterPrepared router_prepared_layout(int32_t H, int32_t E) {
     RouterPrepared r;
@@ -153,16 +186,18 @@ inline RouterPrepared router_prepared_layout(int32_t H, int32_t E) {
     r.wt = take(off, (size_t)E * H * sizeof(float));
     r.wb = take(off, (size_t)Ep * H * 2 * sizeof(_Float16));
     r.wm = take(off, (size_t)Ep * sizeof(float));
+    r.wnorm = take(off, sizeof(float));
     r.pmax = take(off, (size_t)((H + 31) / 32) * E * sizeof(float));
     r.total = off;
     return r;
 }
-// amb: scratch of T+1 ints (the list of tokens with a near-tie), amb[0] set to
+// xn: the input rows' Euclidean norms, wnorm: the router columns' largest
+// (the near-tie window's error bound).  amb: scratch of T+1 ints (the list of tokens with a near-tie), amb[0] set to
 // 0 here unless the caller already did (amb_zeroed); sel: scratch of
 // T * kSelWords ints; wt from the router scratch.
-hipError_t launch_topk(const float* logits, const float* x, const float* wt, const float* bias, int64_t T, int32_t H,
-                       int32_t E, int32_t K, int32_t* amb, int32_t* sel, int32_t* ids, float* p, hipStream_t st,
-                       bool amb_zeroed = false);
+hipError_t launch_topk(const float* logits, const float* x, const float* xn, const float* wt, const float* wnorm,
+                       const float* bias, int64_t T, int32_t H, int32_t E, int32_t K, int32_t* amb, int32_t* sel,
+                       int32_t* ids, float* p, hipStream_t st, bool amb_zeroed = false);
 
 // The shared expert's pair slot: ids / p [T][K] copied to gids / gp [T][K+1]
 // with slot K = (E, sigmoid(x[t] . wg)).  x, wg 16-byte aligned; H % 128 == 0.
@@ -179,19 +214,24 @@ hipError_t launch_row_weights(const int32_t* slot, const float* p, int64_t n, fl
 // gate/up: xt / xst = the tiled codes and scales (launch_gather_tiles,
 // tiled_rows rows) for the 4-wave kernel; xa = the input codes as fp16
 // (launch_prescale) and xs = their block scales, T rows each, for the small-
-// chunk kernel; xuop / xum = offset-pass operand and multipliers; writes int8
+// chunk kernel; xuop / xum = offset-pass operand and multipliers (xuop null:
+// none); writes int8
 // H codes hq and scales hs.
 // n = routed rows, E = experts (bounds of the two chunk lists' lengths).
 hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const ChunkLists& cl, int64_t n, int32_t E,
                           const int32_t* src, const _Float16* xt, const float* xst, int64_t tiled_rows,
                           const _Float16* xa, const float* xs, int64_t T, const _Float16* xuop, const float* xum,
-                          int32_t H, int32_t I, int8_t* hq, float* hs, hipStream_t st);
-// down: hb = the tiled prescaled H (launch_prescale_tiled; act_rows = its
-// rows), he = the row multipliers, huop / hum =
-// offset-pass operand and multipliers; writes the weighted rows dm.
+                          int32_t H, int32_t I, int8_t* hq, float* hs, hipStream_t st,
+                          const ExpertRange& rng = ExpertRange());
+// down: hb / hst = the tiled H codes and block scales (launch_tile_h) for
+// the 4-wave kernel (tiled_rows rows), hs = the grouped rows' block scales
+// [n][I/32] for the small-chunk kernel (which reads its codes from hb too),
+// huop / hum = offset-pass operand and multipliers (huop null: none); writes
+// the weighted rows dm.
 hipError_t launch_down(const uint8_t* blobs, int64_t stride, const ChunkLists& cl, int64_t n, int32_t E,
-                       const int32_t* src, const float* prow, const _Float16* hb, int64_t act_rows, const float* he,
-                       const _Float16* huop, const float* hum, int32_t H, int32_t I, float* dm, hipStream_t st);
+                       const int32_t* src, const float* prow, const _Float16* hb, const float* hst,
+                       int64_t tiled_rows, const float* hs, const _Float16* huop, const float* hum, int32_t H,
+                       int32_t I, float* dm, hipStream_t st, const ExpertRange& rng = ExpertRange());
 hipError_t launch_combine(const float* dm, const int32_t* slot, int64_t T, int32_t K, int32_t H, float* y,
                           hipStream_t st);
 

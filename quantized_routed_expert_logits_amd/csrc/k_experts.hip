@@ -12,34 +12,29 @@
 // Arithmetic.  One weight block is 32 codes q of one row with one fp16 scale
 // d, w = d * (q - 1.5); one activation block is 32 int8 codes a with an fp32
 // scale s.  Their contribution to an output is
-//     d * sum (q - 1.5) * (s a) = sum [d (q - 1)] * (s a) + d * u,
+//     d * sum (q - 1.5) * (s a) = s * [sum d (q - 1) * a] + d * u,
 //     u = -0.5 * s * sum(a)  (one value per activation block).
 // With the pages' Q2_0 map w = d * (q - 1) the same GEMM runs with u = 0
-// (the activation prescale writes it; the offset pass then adds zeros).
-// The first sum runs on v_mfma_f32_16x16x32_f16 (K = 32 = one block): the A
-// operand d*(q-1) is exact in fp16 (q - 1 in {-1, 0, 1, 2}).  Two forms of the
-// B operand:
-//   rescaled (gate/up): the codes a themselves (exact in fp16).  One MFMA per
-//     block with a zero accumulator gives d * sum (q-1) a exactly (an integer
-//     below 2^13 times d: at most 24 significant bits), and one fp32 FMA per
-//     output adds it times the block's s.  gate/up needs more than fp16's 11
-//     bits of the activations (its output is rounded to int8 again); this
-//     form keeps them all for 4 vector FMAs per MFMA;
-//   prescaled (down): the activation s*a*2^-e of the row as one fp16, so the
-//     block scale rides inside the MFMA and the accumulators run over the
-//     whole reduction; after the loop the results are multiplied by the row's
-//     2^e (exact).  The d*u terms of all blocks form a small matrix product over the
-// block index (K = Kd/32), done after the block loop on the MFMA unit: A = d
-// (exact in fp16), B = u of each row scaled by a power of two to [-1, 1] and
-// split into a high and a low fp16 part (22 bits).
+// (the offset pass is then skipped).
+// The bracket runs on v_mfma_f32_16x16x32_f16 (K = 32 = one block) with a
+// zero accumulator: the A operand d*(q-1) is exact in fp16 (q - 1 in
+// {-1, 0, 1, 2}), the B operand is the int8 codes a themselves (exact in
+// fp16), and the product is d times an integer below 2^13, at most 24
+// significant bits, so the block sum comes out of the MFMA exactly.  One fp32
+// FMA per output then adds it times the block's s.  Both GEMMs take this
+// form: gate/up on the layer input's codes, down on the int8 SwiGLU codes.
+// The d*u terms of all blocks form a small matrix product over the block
+// index (K = Kd/32), done after the block loop on the MFMA unit: A = d (exact
+// in fp16), B = u of each row scaled by a power of two to [-1, 1] and split
+// into a high and a low fp16 part (22 bits).
 //
-// Work split.  A workgroup (4 waves) takes one chunk of at most 256 grouped
+// Work split.  A workgroup (4 waves) takes one chunk of at most 192 grouped
 // rows of one expert and one 128-row weight slab (8 fragments of 16 rows).
 // Per 32-wide block each thread unpacks one dword of 16 codes into LDS, so the
 // slab's block is unpacked once and read by all 4 waves (double-buffered, one
 // barrier per block).  The chunk's rows form 16-row tiles; wave w owns tiles
-// w, w+4, w+8, w+12 and keeps their activation fragments in registers.  Lane
-// l of a 16x16 output holds routed row (column) l % 16 and weight rows
+// w, w+4, w+8 and keeps their activation fragments in registers.  Lane l of a
+// 16x16 output holds routed row (column) l % 16 and weight rows
 // 4*(l/16) + v, v = 0..3, so a row's scale is one value per lane.
 //
 // Mapping.  Workgroups are dealt round-robin to the 8 XCDs; the id ->
@@ -115,19 +110,22 @@ __device__ __forceinline__ float round_half_away(float t) {
     return copysignf(fminf(r, 127.0f), t);
 }
 
-// Both GEMMs read their activations (B operand) in the tiled layout of the
-// grouped rows: [tile][block][group g][16 rows][8] fp16, so the fragment of
-// one 16-row tile and block is 1 KiB in MFMA lane order (lane 16 g + r holds
-// row r, values 8g .. 8g + 7) and one coalesced 16-byte load per lane.  The
-// gate/up block scales are tiled alike: [tile][block / 4][16 rows][4] fp32.
-// For a tile's lane: activation offset tile * nblk * kTiledBlockBytes +
-// 16 * lane, plus blk * kTiledBlockBytes; scale offset tile * nblk * 64 +
+// The 4-wave kernel reads its activations (B operand) in the tiled layout of
+// the grouped rows: [tile][block][group g][16 rows][8] fp16 codes, so the
+// fragment of one 16-row tile and block is 1 KiB in MFMA lane order (lane
+// 16 g + r holds row r, values 8g .. 8g + 7) and one coalesced 16-byte load
+// per lane.  The block scales are tiled alike: [tile][block / 4][16 rows][4]
+// fp32 (blocks padded with zeros to a multiple of 4).  For a tile's lane:
+// activation offset tile * nblk * kTiledBlockBytes + 16 * lane, plus
+// blk * kTiledBlockBytes; scale offset tile * tiled_scale_stride(nblk) +
 // 16 * r, plus tiled_scale_offset(blk).
 constexpr int kTiledBlockBytes = 16 * kBlock * 2;
 __device__ __forceinline__ int tiled_scale_offset(int blk) { return (blk >> 2) * 256 + (blk & 3) * 4; }
-// The small-chunk gate/up kernel reads its tokens' rows in place instead:
-// codes [tokens][Kd] fp16 (64 bytes per block of a row), scales
-// [tokens][Kd / 32] fp32.
+__host__ __device__ __forceinline__ int tiled_scale_stride(int nblk) { return (nblk + 3) / 4 * 256; }
+// The small-chunk kernel reads its block scales as rows [rows][Kd / 32] fp32
+// (gate/up: the tokens' scales; down: the grouped rows' scales).  Its
+// gate/up codes are read in place too: [tokens][Kd] fp16 (64 bytes per block
+// of a row); its down codes come from the tiled layout above.
 constexpr int kRowBlockBytes = kBlock * 2;
 
 struct GemmArgs {
@@ -139,18 +137,37 @@ struct GemmArgs {
     int32_t Kd;            // reduction length (H for gate/up, I for down)
     const int32_t* src;    // token of each grouped row
     const float* prow;     // routing weight of each grouped row (down)
-    const _Float16* act;   // activations fp16: gate/up the codes (4-wave kernel tiled, small-chunk
-                           // kernel [tokens][Kd]), down prescaled (tiled)
-    int64_t act_rows;      // rows of act and ascale
-    const float* ascale;   // gate/up: block scales of act (tiled [tile][Kd / 128][16][4], or [tokens][Kd / 32])
-    const float* am;       // down: row multipliers 2^e of act [rows]
-    const _Float16* uop;   // offset-pass operand [rows][nch x 32 blocks x 2] (hi, lo)
+    const _Float16* act;   // activation codes fp16: tiled, or (small-chunk gate/up) [tokens][Kd]
+    int64_t act_rows;      // rows of act
+    const float* ascale;   // their block scales: tiled [tile][ceil(Kd / 128)][16][4] (4-wave kernel) or
+                           // [rows][Kd / 32] (small-chunk kernel)
+    int64_t scale_bytes;   // bytes of ascale
+    const _Float16* uop;   // offset-pass operand [rows][nch x 32 blocks x 2] (hi, lo), or null (no offset)
     const float* um;       // its row multipliers [rows]
     int32_t I, H;
     int8_t* hq;            // gate/up: H codes [n][I]
     float* hs;             // gate/up: H scales [n][I/32]
     float* y;              // down: weighted routed rows dm [n][H]
+    // the launch's chunks: all of the list, or (first != null) entries
+    // [first[e0], first[e1]) of it, the chunks of experts [e0, e1)
+    const int32_t* first;
+    int32_t e0, e1;
+    int64_t ring0;         // nring > 0: expert e's blob is in slot (ring0 + e) % nring
+    int32_t nring;
 };
+
+// Expert e's packed matrix: resident at blobs + e * stride, or in its slot of
+// the ring of streamed experts.
+__device__ __forceinline__ const uint8_t* expert_blob(const GemmArgs& g, int e) {
+    const int64_t slot = g.nring > 0 ? (g.ring0 + e) % g.nring : (int64_t)e;
+    return g.blobs + slot * g.stride;
+}
+
+// The launch's range of its chunk list: [*lo, *hi).
+__device__ __forceinline__ void chunk_range(const GemmArgs& g, int* lo, int* hi) {
+    *lo = g.first ? g.first[g.e0] : 0;
+    *hi = g.first ? g.first[g.e1] : *g.nchunks;
+}
 
 // The K loop over 32-wide blocks.  Per block: every thread unpacks its dword
 // of the slab's record into LDS buffer b&1 (and the two scales into the
@@ -159,11 +176,10 @@ struct GemmArgs {
 // Records are prefetched several blocks ahead in a register ring and
 // activation fragments one block ahead in two alternating register sets, so
 // the loop body has no copies.
-template <bool kRescale>
 struct BlockLoop {
     __amdgpu_buffer_rsrc_t rec;  // this slab's records (nblk x 1280 bytes)
-    __amdgpu_buffer_rsrc_t act;  // activations [rows][Kd] fp16: codes (kRescale) or prescaled
-    __amdgpu_buffer_rsrc_t scl;  // kRescale: block scales [rows][nblk] fp32
+    __amdgpu_buffer_rsrc_t act;  // activation codes fp16, tiled
+    __amdgpu_buffer_rsrc_t scl;  // their block scales fp32, tiled
     int32_t Kd, nblk, dstride;
     int tau, lane, r16, kg, p;
     _Float16* d_lds;
@@ -194,8 +210,8 @@ struct BlockLoop {
                                        __builtin_amdgcn_raw_buffer_load_b128(act, lvoff[i], blk * kTiledBlockBytes, 0));
     }
 
-    // kRescale: the block scale of this lane's MFMA column in each tile;
-    // soff[i] is the byte offset of that row's scales (tiled).
+    // The block scale of this lane's MFMA column in each tile; soff[i] is the
+    // byte offset of that row's scales (tiled).
     template <int NT>
     __device__ __forceinline__ void load_scales(int blk, const int (&soff)[kTilesPerWave],
                                                 float (&sv)[kTilesPerWave]) const {
@@ -247,7 +263,7 @@ struct BlockLoop {
             half8_t a[kFrags / 2];
 #pragma unroll
             for (int f = 0; f < kFrags / 2; ++f) a[f] = a_lds[blk & 1][4 * g + f][lane ^ ((4 * g + f) & ~1)];
-            if constexpr (kRescale && NT > 0) {
+            if constexpr (NT > 0) {
                 // the FMAs that scale a product run kLag MFMAs later, beside
                 // the MFMAs in between (issued as one MFMA, then four FMAs),
                 // so the wave does not wait for each product in turn
@@ -267,13 +283,6 @@ struct BlockLoop {
                     if (k < kN) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
                     if (k >= kLag) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // then its FMAs
                 }
-            } else if constexpr (!kRescale) {
-#pragma unroll
-                for (int f = 0; f < kFrags / 2; ++f)
-#pragma unroll
-                    for (int i = 0; i < NT; ++i)
-                        acc[4 * g + f][i] =
-                            __builtin_amdgcn_mfma_f32_16x16x32_f16(a[f], bf[i], acc[4 * g + f][i], 0, 0, 0);
             }
         }
     }
@@ -289,9 +298,9 @@ struct BlockLoop {
     __device__ __forceinline__ void run(const int (&lvoff)[kTilesPerWave], const int (&soff)[kTilesPerWave],
                                         float4_t (&acc)[kFrags][kTilesPerWave]) const {
         static_assert(D % 2 == 0, "activation sets alternate per block");
-        // kRescale with 8 | D: block scales in 4-block batches (two sets,
-        // batch (blk / 4) & 1 = j / 4), the next batch loaded one block ahead
-        constexpr bool kBatch = kRescale && D % 8 == 0;
+        // 8 | D: block scales in 4-block batches (two sets, batch (blk / 4) & 1
+        // = j / 4), the next batch loaded one block ahead
+        constexpr bool kBatch = D % 8 == 0;
         uint32_t xw[D], xw2[D], sw[D];
         half8_t bf[2][kTilesPerWave];
         float sv[2][kTilesPerWave] = {};
@@ -306,7 +315,7 @@ struct BlockLoop {
         load_act<NT>(0, lvoff, bf[0]);
         if constexpr (kBatch)
             load_scales4<NT>(0, soff, sq[0]);
-        else if constexpr (kRescale)
+        else
             load_scales<NT>(0, soff, sv[0]);
         __builtin_amdgcn_sched_barrier(0);
         for (int b = 0; b < nblk; b += D) {
@@ -320,7 +329,7 @@ struct BlockLoop {
                 load_act<NT>(blk + 1, lvoff, bf[(j + 1) & 1]);
                 if constexpr (kBatch) {
                     if ((j & 3) == 3) load_scales4<NT>(blk + 1, soff, sq[((j >> 2) + 1) & 1]);
-                } else if constexpr (kRescale) {
+                } else {
                     load_scales<NT>(blk + 1, soff, sv[(j + 1) & 1]);
                 }
                 __builtin_amdgcn_sched_barrier(0);  // loads go out before the MFMAs
@@ -450,12 +459,11 @@ __device__ __forceinline__ void big_chunk_item(const GemmArgs& g, const Tile tl,
     // zero the padding blocks of the offset-pass matrix: two threads per row
     for (int c = nblk + (tau & 1); c < nch * 32; c += 2) d_lds[(tau >> 1) * dstride + c] = (_Float16)0.0f;
 
-    // this wave's tiles: arow = activation row of this lane's MFMA column,
-    // lvoff = byte offset of its loader row and group, soff = byte offset of
-    // the column's block scales (rescaled form; padding rows read row 0 and
-    // are never stored).  gate/up takes the rescaled form, down the
-    // prescaled one.
-    constexpr bool kRescale = kGateUp;
+    // this wave's tiles: arow = activation row of this lane's MFMA column
+    // (gate/up: its token, down: its grouped row), lvoff = byte offset of its
+    // loader row and group, soff = byte offset of the column's block scales
+    // (padding rows are zeros in the tiled operands and are never stored)
+    const int sstride = tiled_scale_stride(nblk);
     int64_t arow[kTilesPerWave];
     int lvoff[kTilesPerWave], soff[kTilesPerWave];
     int ntw = 0;
@@ -469,10 +477,10 @@ __device__ __forceinline__ void big_chunk_item(const GemmArgs& g, const Tile tl,
         if (r < tl.nrows) arow[i] = kGateUp ? (int64_t)g.src[tl.row0 + r] : (int64_t)(tl.row0 + r);
         // tile tt of the chunk in the tiled operands (padding rows are zeros, never stored)
         lvoff[i] = (tl.tile0 + tt) * nblk * kTiledBlockBytes + 16 * lane;
-        soff[i] = (tl.tile0 + tt) * nblk * 64 + 16 * r16;
+        soff[i] = (tl.tile0 + tt) * sstride + 16 * r16;
     }
 
-    const uint8_t* rec = g.blobs + (int64_t)tl.e * g.stride + (int64_t)slab * nblk * kRecordBytes;
+    const uint8_t* rec = expert_blob(g, tl.e) + (int64_t)slab * nblk * kRecordBytes;
     const int p = tau & 3;  // fragment pair this thread unpacks: fragments 2p, 2p+1 of MFMA lane tau / 4
 
     float4_t acc[kFrags][kTilesPerWave];
@@ -480,11 +488,10 @@ __device__ __forceinline__ void big_chunk_item(const GemmArgs& g, const Tile tl,
     for (int f = 0; f < kFrags; ++f)
 #pragma unroll
         for (int i = 0; i < kTilesPerWave; ++i) acc[f][i] = (float4_t){0.f, 0.f, 0.f, 0.f};
-    BlockLoop<kRescale> L{
+    BlockLoop L{
         __builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, nblk * kRecordBytes, kBufferWord3),
         __builtin_amdgcn_make_buffer_rsrc((void*)g.act, (short)0, (int)(g.act_rows * g.Kd * 2), kBufferWord3),
-        __builtin_amdgcn_make_buffer_rsrc((void*)g.ascale, (short)0, kRescale ? (int)(g.act_rows * nblk * 4) : 0,
-                                          kBufferWord3),
+        __builtin_amdgcn_make_buffer_rsrc((void*)g.ascale, (short)0, (int)g.scale_bytes, kBufferWord3),
         g.Kd, nblk, dstride, tau, lane, r16, kg, p, d_lds, a_lds, UnpackMagic(), 0};
     // The record's 256 dwords are unpacked by the waves with fewer tiles where
     // the chunk's tiles do not split evenly (nt = 4q + r; waves 0..r-1 hold
@@ -502,23 +509,13 @@ __device__ __forceinline__ void big_chunk_item(const GemmArgs& g, const Tile tl,
         run_shape<2>(L, ntw, kw, lvoff, soff, acc);
     __syncthreads();  // every d of the slab is in LDS
 
-    // undo the rows' power-of-two prescaling (the rescaled form has none)
-#pragma unroll
-    for (int i = 0; i < kTilesPerWave; ++i) {
-        if (kRescale || i >= ntw) continue;
-        const float mult = arow[i] >= 0 ? g.am[arow[i]] : 0.f;
-#pragma unroll
-        for (int f = 0; f < kFrags; ++f)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) acc[f][i][v] *= mult;
-    }
-
     // offset pass: acc += 2^eu * sum_b d[row][b] * u'[row][b], 32 blocks per
     // MFMA, u' = u * 2^-eu as hi and lo fp16 (prepared with the activations,
     // zero-padded to whole chunks of 32 blocks, like the zeroed d padding).
+    // Without an offset operand (the Q2_0 map, u = 0) there is none.
 #pragma unroll
     for (int i = 0; i < kTilesPerWave; ++i) {
-        if (i >= ntw) continue;
+        if (i >= ntw || !g.uop) continue;
         const int64_t ar = arow[i] >= 0 ? arow[i] : 0;
         const half8_t* urow = reinterpret_cast<const half8_t*>(g.uop + ar * nch * 64) + 2 * kg;
         half8_t ub[kMaxOffsetChunks][2];
@@ -581,8 +578,10 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_kernel(GemmArgs g) {
     extern __shared__ _Float16 d_lds[];  // [kSlabRows][dstride]: d of every row and block (offset pass)
     const int id = blockIdx.x;
     const int local = id >> 3;
-    const int chunk = (local / g.nslab) * 8 + (id & 7);
-    if (chunk >= *g.nchunks) return;  // uniform over the workgroup, before any barrier
+    int lo, hi;
+    chunk_range(g, &lo, &hi);
+    const int chunk = lo + (local / g.nslab) * 8 + (id & 7);
+    if (chunk >= hi) return;  // uniform over the workgroup, before any barrier
     const Tile tl = g.chunks[chunk];   // a copy: read once, before any store
     big_chunk_item<kGateUp>(g, tl, local % g.nslab, a_lds, d_lds);
 }
@@ -603,7 +602,9 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_kernel(GemmArgs g) {
 // The activation fragments are read straight in the MFMA layout: at one
 // 16-byte load per tile and block the L1 keeps up with 16 rows per load, and
 // the lane exchange of the 4-wave kernel costs more than it saves here.
-template <int NT, bool kRescale>
+// kInPlace: the B codes are read from their rows in place (gate/up: the
+// tokens' codes [tokens][Kd]); otherwise from the tiled layout (down).
+template <int NT, bool kInPlace>
 struct SlabPass {
     __amdgpu_buffer_rsrc_t rec, act, scl;
     int32_t Kd, nblk;
@@ -626,23 +627,23 @@ struct SlabPass {
 
     // Activation fragments of a block (lvoff: this lane's byte offset; gate/up
     // its column's row and group in place, down its place in the tiled
-    // operand); with kRescale also the block scale of the lane's column in
-    // each tile (soff: byte offset of that row's scales).
+    // operand), and if `scales` the block scale of the lane's column in each
+    // tile (soff: byte offset of that row's scales).
     __device__ __forceinline__ void load_act(int blk, const int (&lvoff)[NT], const int (&soff)[NT],
                                              half8_t (&bf)[NT], float (&sv)[NT], bool scales) const {
         blk = blk < nblk ? blk : nblk - 1;
-        constexpr int kStride = kRescale ? kRowBlockBytes : kTiledBlockBytes;
+        constexpr int kStride = kInPlace ? kRowBlockBytes : kTiledBlockBytes;
 #pragma unroll
         for (int i = 0; i < NT; ++i)
             bf[i] = __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(act, lvoff[i], blk * kStride, 0));
-        if (kRescale && scales)
+        if (scales)
 #pragma unroll
             for (int i = 0; i < NT; ++i)
                 sv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(scl, soff[i], blk * 4, 0));
     }
 
-    // kRescale: the scales of blocks blk .. blk + 3 (blk a multiple of 4,
-    // 4 | nblk), one 16-byte load per tile instead of four gathered dwords.
+    // The scales of blocks blk .. blk + 3 (blk a multiple of 4, 4 | nblk),
+    // one 16-byte load per tile instead of four gathered dwords.
     __device__ __forceinline__ void load_scales4(int blk, const int (&soff)[NT], float4_t (&sq)[NT]) const {
         blk = blk < nblk ? blk : nblk - 4;
 #pragma unroll
@@ -672,53 +673,42 @@ struct SlabPass {
     // One block, software-pipelined over the four dwords: the MFMAs of dword
     // p issue interleaved with the unpack of dword p + 1 (one MFMA, then a
     // few VALU instructions), so the matrix unit and the vector ALU of the
-    // wave work side by side.  kRescale: the FMAs that scale dword p's
-    // products run one dword later, beside dword p + 1's MFMAs (the products
-    // are ready by then).
+    // wave work side by side.  The FMAs that scale dword p's products run one
+    // dword later, beside dword p + 1's MFMAs (the products are ready by
+    // then).
     __device__ __forceinline__ void block(int blk, const uint32_t (&xw)[4], const uint32_t (&sw)[4],
                                           const half8_t (&bf)[NT], const float (&sv)[NT],
                                           float4_t (&acc)[kFrags][NT]) const {
         constexpr int kMfmas = 2 * NT;                                // per dword
-        constexpr int kValu = 26 + (kRescale ? 4 * kMfmas : 0);       // unpack (+ rescale FMAs) per dword
+        constexpr int kValu = 26 + 4 * kMfmas;                        // unpack + rescale FMAs per dword
         constexpr int kValuPer = (kValu + kMfmas - 1) / kMfmas;       // VALU instructions per MFMA slot
         const int col = blk & 31;
         half8_t a[2][2];
-        float4_t t[2][2][NT];  // kRescale: products of the last two dwords (fragment pair, tile)
+        float4_t t[2][2][NT];  // products of the last two dwords (fragment pair, tile)
         prepare(0, xw, sw, a[0]);
         park_scales(col, sw);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             if (p < 3) prepare(p + 1, xw, sw, a[(p + 1) & 1]);
-            if constexpr (kRescale) {
-                const float4_t z = {0.f, 0.f, 0.f, 0.f};
+            const float4_t z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < NT; ++i) {
-                    t[p & 1][0][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[p & 1][0], bf[i], z, 0, 0, 0);
-                    t[p & 1][1][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[p & 1][1], bf[i], z, 0, 0, 0);
-                }
-                if (p > 0) scale_products(p - 1, t[(p - 1) & 1], sv, acc);
-            } else {
-#pragma unroll
-                for (int i = 0; i < NT; ++i) {
-                    acc[2 * p][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[p & 1][0], bf[i], acc[2 * p][i], 0, 0, 0);
-                    acc[2 * p + 1][i] =
-                        __builtin_amdgcn_mfma_f32_16x16x32_f16(a[p & 1][1], bf[i], acc[2 * p + 1][i], 0, 0, 0);
-                }
+            for (int i = 0; i < NT; ++i) {
+                t[p & 1][0][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[p & 1][0], bf[i], z, 0, 0, 0);
+                t[p & 1][1][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[p & 1][1], bf[i], z, 0, 0, 0);
             }
-            if (p < 3 || kRescale) {
+            if (p > 0) scale_products(p - 1, t[(p - 1) & 1], sv, acc);
 #pragma unroll
-                for (int k = 0; k < kMfmas; ++k) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);  // then VALU
-                }
+            for (int k = 0; k < kMfmas; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);  // then VALU
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (kRescale) scale_products(3, t[1], sv, acc);
+        scale_products(3, t[1], sv, acc);
     }
 
-    // kRescale: acc of fragments 2p, 2p+1 += block scale * products.
+    // acc of fragments 2p, 2p+1 += block scale * products.
     __device__ __forceinline__ void scale_products(int p, const float4_t (&tp)[2][NT], const float (&sv)[NT],
                                                    float4_t (&acc)[kFrags][NT]) const {
 #pragma unroll
@@ -730,7 +720,7 @@ struct SlabPass {
             }
     }
 
-    // Offset pass of 32-block chunk c: acc += (um / am) * sum_b d[row][b] u'[col][b].
+    // Offset pass of 32-block chunk c: acc += um * sum_b d[row][b] u'[col][b].
     __device__ __forceinline__ void offset(int c, int nch, const _Float16* uop, const int64_t (&arow)[NT],
                                            const float (&ratio)[NT], float4_t (&acc)[kFrags][NT]) const {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -764,14 +754,15 @@ struct SlabPass {
     // Records run D blocks ahead in a register ring (8 dwords per block),
     // activation fragments one block ahead in two alternating sets.  The
     // body is unrolled U blocks (D | U, U | each 32-block chunk's length);
-    // with kRescale and U = 8 the block scales come in 4-block batches (two
-    // sets, batch (blk / 4) & 1 = j / 4), the next batch one block ahead.
+    // with U = 8 the block scales come in 4-block batches (two sets, batch
+    // (blk / 4) & 1 = j / 4), the next batch one block ahead.  Without an
+    // offset operand (uop null: the Q2_0 map) there is no offset pass.
     template <int D, int U>
     __device__ __forceinline__ void run(int nch, const _Float16* uop, const int64_t (&arow)[NT],
                                         const int (&lvoff)[NT], const int (&soff)[NT], const float (&ratio)[NT],
                                         float4_t (&acc)[kFrags][NT]) const {
         static_assert(U % D == 0 && U % 2 == 0, "ring slots and activation sets are compile-time per body");
-        constexpr bool kBatch = kRescale && U % 8 == 0;
+        constexpr bool kBatch = U % 8 == 0;
         uint32_t xw[D][4], sw[D][4];
         half8_t bf[2][NT];
         float sv[2][NT] = {};
@@ -803,7 +794,7 @@ struct SlabPass {
                     load_record(blk + D, xw[j % D], sw[j % D]);
                 }
             }
-            offset(c, nch, uop, arow, ratio, acc);
+            if (uop) offset(c, nch, uop, arow, ratio, acc);
         }
     }
 };
@@ -811,8 +802,7 @@ struct SlabPass {
 template <bool kGateUp, int NT>
 __device__ __forceinline__ void small_chunk_pass(const GemmArgs& g, const Tile& tl, int slab, int t0, int lane,
                                                  _Float16* dl) {
-    constexpr bool kRescale = kGateUp;  // gate/up: codes and block scales; down: prescaled H
-    using Pass = SlabPass<NT, kRescale>;
+    using Pass = SlabPass<NT, kGateUp>;  // gate/up reads its tokens' codes in place, down the tiled H
     const int r16 = lane & 15, kg = lane >> 4;
     const int nblk = g.Kd / kBlock, nch = (nblk + 31) / 32;
 
@@ -822,19 +812,19 @@ __device__ __forceinline__ void small_chunk_pass(const GemmArgs& g, const Tile& 
 
     int64_t arow[NT];
     int lvoff[NT], soff[NT];
-    float ratio[NT];  // offset pass against main products: um / am (rescaled form: um, there is no am)
+    float ratio[NT];  // the offset pass's row multipliers um
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
         const int r = 16 * (t0 + i) + r16;
         arow[i] = -1;
         if (r < tl.nrows) arow[i] = kGateUp ? (int64_t)g.src[tl.row0 + r] : (int64_t)(tl.row0 + r);
-        ratio[i] = arow[i] >= 0 ? (kRescale ? g.um[arow[i]] : g.um[arow[i]] / g.am[arow[i]]) : 0.f;
+        ratio[i] = arow[i] >= 0 && g.uop ? g.um[arow[i]] : 0.f;
         const int64_t ar = arow[i] >= 0 ? arow[i] : 0;  // padding columns read row 0, never stored
         if constexpr (kGateUp)
             lvoff[i] = (int)ar * g.Kd * 2 + 16 * kg;  // MFMA layout: column r16, group kg
         else  // tile t0 + i of the chunk in the tiled operand (padding rows are zeros, never stored)
             lvoff[i] = (tl.tile0 + t0 + i) * nblk * kTiledBlockBytes + 16 * lane;
-        soff[i] = (int)ar * nblk * 4;
+        soff[i] = (int)ar * nblk * 4;  // scales as rows: gate/up the token's, down the grouped row's
     }
     float4_t acc[kFrags][NT];
 #pragma unroll
@@ -842,25 +832,21 @@ __device__ __forceinline__ void small_chunk_pass(const GemmArgs& g, const Tile& 
 #pragma unroll
         for (int i = 0; i < NT; ++i) acc[f][i] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-    const uint8_t* rec = g.blobs + (int64_t)tl.e * g.stride + (int64_t)slab * nblk * kRecordBytes;
+    const uint8_t* rec = expert_blob(g, tl.e) + (int64_t)slab * nblk * kRecordBytes;
     Pass L{__builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, nblk * kRecordBytes, kBufferWord3),
            __builtin_amdgcn_make_buffer_rsrc((void*)g.act, (short)0, (int)(g.act_rows * g.Kd * 2), kBufferWord3),
-           __builtin_amdgcn_make_buffer_rsrc((void*)g.ascale, (short)0, kRescale ? (int)(g.act_rows * nblk * 4) : 0,
-                                             kBufferWord3),
+           __builtin_amdgcn_make_buffer_rsrc((void*)g.ascale, (short)0, (int)g.scale_bytes, kBufferWord3),
            g.Kd, nblk, lane, r16, kg, dl, UnpackMagic()};
-    if (kRescale && nblk % 8 == 0)  // 8 | every chunk's block count: 4-block scale batches
+    if (nblk % 8 == 0)  // 8 | every chunk's block count: 4-block scale batches
         L.template run<2, 8>(nch, g.uop, arow, lvoff, soff, ratio, acc);
     else
         L.template run<2, 2>(nch, g.uop, arow, lvoff, soff, ratio, acc);
 
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-        const float mult = arow[i] >= 0 ? (kRescale ? 1.0f : g.am[arow[i]]) : 0.f;
         float4_t a[kFrags];
 #pragma unroll
-        for (int f = 0; f < kFrags; ++f)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) a[f][v] = acc[f][i][v] * mult;
+        for (int f = 0; f < kFrags; ++f) a[f] = acc[f][i];
         if constexpr (kGateUp)
             gate_up_store(g, tl, slab, 16 * (t0 + i) + r16, kg, a);
         else  // the d buffer is free after the last offset pass
@@ -878,18 +864,19 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_small_kernel(GemmArgs g) {
     const int ngroups = (g.nslab + kWaves - 1) / kWaves;
     const int id = blockIdx.x;
     const int local = id >> 3;
-    const int chunk = (local / ngroups) * 8 + (id & 7);
-    if (chunk >= *g.nchunks) return;
+    int lo, hi;
+    chunk_range(g, &lo, &hi);
+    const int chunk = lo + (local / ngroups) * 8 + (id & 7);
+    if (chunk >= hi) return;
     const Tile tl = g.chunks[chunk];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int slab = kWaves * (local % ngroups) + wave;
     if (slab >= g.nslab) return;  // waves are independent: no workgroup barrier follows
     const int lane = threadIdx.x & 63;
     const int nt = (tl.nrows + 15) / 16;
-    // gate/up: a 3-tile chunk in one pass (the weights are unpacked once; 256
-    // VGPRs, still 2 waves per SIMD).  Down keeps two passes (2 tiles, then
-    // 1): a 3-tile down pass would cost the kernel its third wave per SIMD.
-    if (kGateUp && nt == 3) {
+    // a 3-tile chunk in one pass (the weights are unpacked once; 256 VGPRs,
+    // still 2 waves per SIMD)
+    if (nt == 3) {
         small_chunk_pass<kGateUp, 3>(g, tl, slab, 0, lane, dl_all[wave]);
         return;
     }
@@ -949,13 +936,24 @@ inline unsigned grid_of(int64_t chunks_cap, int32_t per_chunk) {
 // small chunk.  Workgroups past the list's length exit at once, so a tight
 // bound saves their launches.
 // gs: the small-chunk kernel's arguments (its activations may differ).
+// rng: a range of experts (then the bounds count its experts only) and the
+// ring mapping of the blobs, or all experts resident.
 void launch_gemms(GemmArgs g, GemmArgs gs_args, const ChunkLists& cl, int64_t n, int32_t E, size_t big_lds,
-                  bool gate_up, hipStream_t st) {
+                  bool gate_up, hipStream_t st, const ExpertRange& rng) {
+    const int32_t ne = rng.first ? rng.e1 - rng.e0 : E;  // experts this launch covers
     const int64_t by_rows = n / (kSmallRows + 1);
-    const int64_t by_experts = n / kChunkRows + (E < by_rows ? E : by_rows);
+    const int64_t by_experts = n / kChunkRows + (ne < by_rows ? ne : by_rows);
     int64_t cap_big = cl.cap < by_rows ? cl.cap : by_rows;
     cap_big = cap_big < by_experts ? cap_big : by_experts;
-    const int64_t cap_small = cl.cap < E ? cl.cap : E;
+    const int64_t cap_small = cl.cap < ne ? cl.cap : ne;
+    for (GemmArgs* a : {&g, &gs_args}) {
+        a->e0 = rng.e0;
+        a->e1 = rng.e1;
+        a->ring0 = rng.ring0;
+        a->nring = rng.nring;
+    }
+    g.first = rng.first;                                                   // big list: row 0 of the table
+    gs_args.first = rng.first ? rng.first + ((int64_t)rng.E + 1) : nullptr;  // small list: row 1
     g.chunks = cl.tiles;
     g.nchunks = cl.sched;
     if (cap_big > 0) {
@@ -981,24 +979,30 @@ void launch_gemms(GemmArgs g, GemmArgs gs_args, const ChunkLists& cl, int64_t n,
 hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const ChunkLists& cl, int64_t n, int32_t E,
                           const int32_t* src, const _Float16* xt, const float* xst, int64_t tiled_rows,
                           const _Float16* xa, const float* xs, int64_t T, const _Float16* xuop, const float* xum,
-                          int32_t H, int32_t I, int8_t* hq, float* hs, hipStream_t st) {
+                          int32_t H, int32_t I, int8_t* hq, float* hs, hipStream_t st, const ExpertRange& rng) {
+    const int64_t tiled_scale_bytes = tiled_rows / 16 * tiled_scale_stride(H / kBlock);
     const GemmArgs g{blobs, stride, nullptr, nullptr, 2 * I / kSlabRows, H, src, nullptr, xt, tiled_rows, xst,
-                     nullptr, xuop, xum, I, H, hq, hs, nullptr};
+                     tiled_scale_bytes, xuop, xum, I, H, hq, hs, nullptr, nullptr, 0, 0, 0, 0};
     GemmArgs gs = g;
     gs.act = xa;
     gs.act_rows = T;
     gs.ascale = xs;
-    launch_gemms(g, gs, cl, n, E, dynamic_lds_bytes(H, false), true, st);
+    gs.scale_bytes = T * (H / kBlock) * 4;
+    launch_gemms(g, gs, cl, n, E, dynamic_lds_bytes(H, false), true, st, rng);
     return hipGetLastError();
 }
 
 hipError_t launch_down(const uint8_t* blobs, int64_t stride, const ChunkLists& cl, int64_t n, int32_t E,
-                       const int32_t* src, const float* prow, const _Float16* hb, int64_t act_rows, const float* he,
-                       const _Float16* huop, const float* hum, int32_t H, int32_t I, float* dm, hipStream_t st) {
-    GemmArgs g{blobs, stride, nullptr, nullptr, H / kSlabRows, I, src, prow, hb, act_rows, nullptr, he, huop, hum, I,
-               H,
-               nullptr, nullptr, dm};
-    launch_gemms(g, g, cl, n, E, dynamic_lds_bytes(I, true), false, st);
+                       const int32_t* src, const float* prow, const _Float16* hb, const float* hst,
+                       int64_t tiled_rows, const float* hs, const _Float16* huop, const float* hum, int32_t H,
+                       int32_t I, float* dm, hipStream_t st, const ExpertRange& rng) {
+    const int64_t tiled_scale_bytes = tiled_rows / 16 * tiled_scale_stride(I / kBlock);
+    const GemmArgs g{blobs, stride, nullptr, nullptr, H / kSlabRows, I, src, prow, hb, tiled_rows, hst,
+                     tiled_scale_bytes, huop, hum, I, H, nullptr, nullptr, dm, nullptr, 0, 0, 0, 0};
+    GemmArgs gs = g;  // the small-chunk kernel reads the grouped rows' scales as rows
+    gs.ascale = hs;
+    gs.scale_bytes = n * (I / kBlock) * 4;
+    launch_gemms(g, gs, cl, n, E, dynamic_lds_bytes(I, true), false, st, rng);
     return hipGetLastError();
 }
 

@@ -1,13 +1,15 @@
 // Grouping of the (token, k) pairs by expert, on the GPU.
 //
 // Strata compare v0.1.35...v0.1.37 page, include/strata/prefill/moe_fused.hpp,
-// group: from the router's ids, per expert its rows (counts, offsets, the list
-// of 64-row tiles; here chunks of up to kChunkRows rows), slot[i] = the row of pair
-// i and src[row] = its token
-// i / K, without a host wait.  The order of rows within an expert is left open
-// there; these kernels produce the stable order (ascending pair index) of the
-// MMQ path's host counting sort (Winery-Strata prefill.cpp page, Prefill::run,
-// MoE half), so the grouping is unique and can be compared exactly.
+// group: the fused path sorts the routed pairs by expert on the device,
+// straight from the router's output, so the host does not have to wait for
+// the routing.  Its tables: where each expert's rows start, which row each
+// pair lands in (slot) and which token each row reads (src); work lists of
+// row chunks (here at most kChunkRows rows each).  The pages leave the order
+// of one expert's rows open; these kernels keep pairs in ascending pair index,
+// the order the MMQ path's host counting sort gives (Winery-Strata prefill.cpp
+// page, Prefill::run, MoE half), which makes the tables unique and exactly
+// comparable.
 //
 // Three launches, none of which waits on the host:
 //   hist    one workgroup per chunk of 2048 pairs: LDS histogram of its ids;
@@ -118,12 +120,21 @@ __device__ int small_chunks(int cnt, int nt, int per) {
     return ns;
 }
 
+// Expert e's entries of the first table (the totals for e = E).
+__device__ void write_first(const ChunkLists& cl, int32_t E, int e, int bpos, int spos, int tile) {
+    if (!cl.first) return;
+    cl.first[e] = bpos;
+    cl.first[E + 1 + e] = spos;
+    cl.first[2 * (E + 1) + e] = tile;
+}
+
 // The list counts and the tile count (one thread).
-__device__ void finish_lists(const ChunkLists& cl, int nbig, int nsmall, int tiled_rows) {
+__device__ void finish_lists(const ChunkLists& cl, int32_t E, int nbig, int nsmall, int tiled_rows) {
     if (threadIdx.x == 0) {
         cl.sched[0] = nbig;
         cl.sched[1] = nsmall;
         cl.sched[2] = tiled_rows / 16;
+        write_first(cl, E, E, nbig, nsmall, tiled_rows / 16);
     }
 }
 
@@ -162,9 +173,10 @@ __global__ void __launch_bounds__(1024) group_scan_kernel(const int32_t* __restr
     if (e < E) {
         offsets[e] = off;
         emit_chunks(cl, e, off, cnt, nt, per, bpos, spos, toff);
+        write_first(cl, E, e, bpos, spos, toff / 16);
     }
     if (e == 0) offsets[E] = (int32_t)n;
-    finish_lists(cl, total_big, total_small, total_tiled);
+    finish_lists(cl, E, total_big, total_small, total_tiled);
 }
 
 constexpr int kScatterWaves = kGroupChunk / 256;  // 8 waves of 256 pairs per chunk
@@ -251,8 +263,11 @@ __global__ void __launch_bounds__(1024) chunks_from_offsets_kernel(const int32_t
     const int ns = small_chunks(cnt, nt, per);
     const int bpos = block_exclusive_scan(nt - ns, &total_big);
     const int spos = block_exclusive_scan(ns, &total_small);
-    if (e < E) emit_chunks(cl, e, offsets[e], cnt, nt, per, bpos, spos, toff);
-    finish_lists(cl, total_big, total_small, total_tiled);
+    if (e < E) {
+        emit_chunks(cl, e, offsets[e], cnt, nt, per, bpos, spos, toff);
+        write_first(cl, E, e, bpos, spos, toff / 16);
+    }
+    finish_lists(cl, E, total_big, total_small, total_tiled);
 }
 
 __global__ void row_weights_kernel(const int32_t* __restrict__ slot, const float* __restrict__ p, int64_t n,

@@ -1,28 +1,27 @@
 // Per-32 int8 rounding of fp32 rows (the layer input, once per token), the
-// prescaled fp16 GEMM operands built from int8 codes, and a fill helper.
+// fp16 code operands of the expert GEMMs built from int8 codes, and a fill
+// helper.
 //
 // Strata compare v0.1.35...v0.1.37 page, include/strata/prefill/moe_fused.hpp,
-// quantize_act: the activations are rounded to int8 once per token with one
-// scale per 32 values.  The rounding is not on the pages; the kernels take
-// s = max|v| / 127 and q = round-half-away-from-zero(v / s), both divisions
-// correctly rounded fp32 (IEEE), |q| <= 127, s = 0 and q = 0 for an all-zero
-// block.
+// header comment and quantize_act: on the fused path each token's input is
+// quantized a single time (not once per routed slot as on the MMQ path), to
+// int8 codes with one scale for every 32 consecutive values.  The pages do not
+// give the rounding; the kernels take s = max|v| / 127 and
+// q = round-half-away-from-zero(v / s), both divisions correctly rounded fp32
+// (IEEE), |q| <= 127, s = 0 and q = 0 for an all-zero block.
 //
 // Quantize layout: 8 lanes cover one block of 32 values, one float4 each, so a
 // wave reads 1 KiB of contiguous input per instruction.  Outputs per block:
 // the int8 codes and the scale.
 //
-// Prescale: the fp16 operands of the expert GEMMs.  Two forms:
-//   the down GEMM: fp16(q * s * 2^-e_r), 11 significant bits, so the
-//     per-block scale rides inside the MFMA.  A row r is first scaled by
-//     2^-e_r, chosen so that the row's largest possible |q * s| (127 * max s)
-//     lands in [2^14, 2^15): fp16 cannot overflow and small values keep their
-//     bits.  The row multiplier 2^e_r is written beside the operand; the GEMM
-//     multiplies its fp32 results by it (exact).  The down output is not
-//     rounded to int8 again, so 11 bits suffice.  Written in the tiled layout
-//     (prescale_tiles_kernel).
-//   the gate/up GEMM: the codes q themselves (exact), [rows][cols]; the GEMM
-//     applies the block scales in fp32 after each block's products.
+// Operands of the expert GEMMs: the int8 codes q themselves as fp16
+// (exact), either as rows [rows][cols] (the layer input, read in place by the
+// small-chunk gate/up kernel) or in the tiled layout of the grouped rows (the
+// gate/up input of big chunks, gathered through src, and the down input); the
+// GEMMs apply the block scales in fp32 after each block's products.  The
+// layer input also gets a row multiplier 2^e_r (127 * the row's largest block
+// scale in [2^14, 2^15) after scaling by 2^-e_r), which the router takes for
+// its fp16 operand.
 //
 // The kernels also write the operand of the GEMMs' offset pass: per block,
 // u = -uoff * s * (sum of the block's codes) (the 2-bit weight offset's share
@@ -142,6 +141,7 @@ __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict_
     }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) umax = fmaxf(umax, __shfl_xor(umax, o));
+    if (!uop) return;  // no offset operand (the Q2_0 map)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -168,42 +168,52 @@ __global__ void __launch_bounds__(256) prescale_kernel(const int8_t* __restrict_
     }
 }
 
-// The down operand of grouped rows in the tiled layout: q * s * 2^-e_r as
-// fp16, with 2^e_r the row multiplier (127 * the row's largest block scale
-// lies in [2^14, 2^15) after the scaling), plus the offset operand as
+// The down GEMM's operand of grouped rows in the tiled layout: the int8 H
+// codes as fp16 (exact) in [tile][block][group g][row within the tile][8],
+// their block scales in [tile][block / 4][row within the tile][4] (blocks
+// padded with zeros to a multiple of 4), plus the offset operand as
 // prescale_kernel builds it.  One workgroup per 16-row tile of the tile
-// table.  The tile's rows are
-// consecutive grouped rows: their codes and scales are read coalesced into
-// LDS, kStageCols columns at a time (rows padded by 8 bytes / 1 float against
-// bank conflicts), then lane 16 g + r of a wave takes tile row r, value group
-// g (8 codes) of a block, so each block's fragment is one contiguous 1 KiB
-// store; wave w takes blocks w, w + 4, ...  The per-row multiplier and
-// offset operand use prescale_kernel's arithmetic.  Wider rows than
-// kStageCols are staged twice (once per pass).
+// table.  The tile's rows are consecutive grouped rows: their codes and
+// scales are read coalesced into LDS, kStageCols columns at a time (rows
+// padded by 8 bytes / 1 float against bank conflicts), then lane 16 g + r of
+// a wave takes tile row r, value group g (8 codes) of a block, so each
+// block's fragment is one contiguous 1 KiB store; wave w takes blocks w,
+// w + 4, ...  Wider rows than kStageCols are staged twice (once per pass).
 constexpr int kStageCols = 2048;
-inline size_t prescale_tiles_lds_bytes(int32_t cols) {
+inline size_t tile_h_lds_bytes(int32_t cols) {
     const int sc = cols < kStageCols ? cols : kStageCols;
     return (size_t)16 * (sc + 8) + (size_t)16 * (sc / kBlock + 1) * sizeof(float);
 }
 
-__global__ void __launch_bounds__(256) prescale_tiles_kernel(const int8_t* __restrict__ q,
-                                                             const float* __restrict__ s,
-                                                             const TileRows* __restrict__ trows,
-                                                             const int32_t* __restrict__ ntiles, int32_t cols,
-                                                             float uoff, _Float16* __restrict__ out,
-                                                             float* __restrict__ mult, _Float16* __restrict__ uop,
-                                                             float* __restrict__ umult) {
+__global__ void __launch_bounds__(256) tile_h_kernel(const int8_t* __restrict__ q, const float* __restrict__ s,
+                                                     const TileRows* __restrict__ trows,
+                                                     const int32_t* __restrict__ ntiles, int32_t cols, float uoff,
+                                                     _Float16* __restrict__ out, float* __restrict__ sout,
+                                                     _Float16* __restrict__ uop, float* __restrict__ umult,
+                                                     const int32_t* __restrict__ first_tile, int32_t e0, int32_t e1) {
     extern __shared__ __align__(16) unsigned char lds[];  // codes [16][sc + 8], scales [16][sc / 32 + 1]
     __shared__ float ush[16][kMaxOffsetChunks * 32];      // u of each row and block
-    __shared__ float smx[4][16], umx[4][16];              // per wave: max block scale, max |u| of each row
-    const int64_t t = blockIdx.x;
-    if (t >= *ntiles) return;  // uniform over the workgroup, before any barrier
+    __shared__ float umx[4][16];                          // per wave: max |u| of each row
+    // all tiles, or (first_tile) those of experts [e0, e1)
+    const int64_t t = (first_tile ? first_tile[e0] : 0) + (int64_t)blockIdx.x;
+    if (t >= (first_tile ? first_tile[e1] : *ntiles)) return;  // uniform over the workgroup, before any barrier
     const TileRows tr = trows[t];
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
-    const int nb = cols / kBlock, nch = (nb + 31) / 32;
+    const int nb = cols / kBlock, nch = (nb + 31) / 32, nq = (nb + 3) / 4;
     const int sc = cols < kStageCols ? cols : kStageCols, sb = sc / kBlock;
     const int qstride = sc + 8, sstride = sb + 1;
     float* sl = reinterpret_cast<float*>(lds + (size_t)16 * qstride);
+    // block scales, tiled: thread i takes row i / nq, 4-block group i % nq
+    for (int i = tid; i < 16 * nq; i += 256) {
+        const int rr = i / nq, qb = i - rr * nq;
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int b = 4 * qb + j;
+            v[j] = rr < tr.nrows && b < nb ? s[((int64_t)tr.row0 + rr) * nb + b] : 0.0f;
+        }
+        *reinterpret_cast<float4*>(sout + ((t * nq + qb) * 16 + rr) * 4) = make_float4(v[0], v[1], v[2], v[3]);
+    }
     // columns [c0, c0 + sc) of the tile's rows into LDS; rows past nrows as zeros
     auto stage = [&](int c0) {  // all of a thread's loads first, then its LDS stores
         const int pieces = sc / 16;
@@ -231,8 +241,9 @@ __global__ void __launch_bounds__(256) prescale_tiles_kernel(const int8_t* __res
     };
     const bool valid = r < tr.nrows;
     const int64_t row = (int64_t)tr.row0 + r;
-    // pass 1: block sums -> u, the row's largest block scale and |u|
-    float m = 0.0f, umax = 0.0f;
+    half8_t* tile = reinterpret_cast<half8_t*>(out) + t * nb * 64;
+    // one pass per slice: the fp16 codes, and the block sums -> u, max |u|
+    float umax = 0.0f;
     for (int c0 = 0; c0 < cols; c0 += sc) {
         if (c0 > 0) __syncthreads();  // the previous slice is read
         stage(c0);
@@ -242,37 +253,30 @@ __global__ void __launch_bounds__(256) prescale_tiles_kernel(const int8_t* __res
             const uint2 c8 = *reinterpret_cast<const uint2*>(lds + r * qstride + kBlock * b + 8 * g);
             const float sraw = sl[r * sstride + b];
             int sum = 0;
+            half8_t h;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sum += (int)(int8_t)(c8.x >> (8 * i)) + (int)(int8_t)(c8.y >> (8 * i));
+            for (int i = 0; i < 8; ++i) {
+                const int c = (int8_t)((i < 4 ? c8.x : c8.y) >> (8 * (i & 3)));
+                sum += c;
+                h[i] = (_Float16)c;  // exact; rows past nrows: zero codes
+            }
+            tile[(c0 / kBlock + b) * 64 + lane] = h;
             sum += __shfl_xor(sum, 16);
             sum += __shfl_xor(sum, 32);
             const float u = -uoff * sraw * (float)sum;
             if (g == 0) ush[r][c0 / kBlock + b] = u;
-            m = fmaxf(m, sraw);
             umax = fmaxf(umax, fabsf(u));
         }
     }
-    if (g == 0) smx[w][r] = m, umx[w][r] = umax;
+    if (!uop) return;  // no offset operand (the Q2_0 map)
+    if (g == 0) umx[w][r] = umax;
     __syncthreads();
-    m = fmaxf(fmaxf(smx[0][r], smx[1][r]), fmaxf(smx[2][r], smx[3][r]));
     umax = fmaxf(fmaxf(umx[0][r], umx[1][r]), fmaxf(umx[2][r], umx[3][r]));
-    const float bound = 127.0f * m;  // >= every |q * s| of the row
-    float scale = 1.0f, back = 1.0f;
-    if (bound > 0.0f) {
-        int ex = 0;
-        frexpf(bound, &ex);
-        ex = ex < -96 ? -96 : ex;
-        scale = ldexpf(1.0f, 15 - ex);
-        back = ldexpf(1.0f, ex - 15);
-    }
     int eu = 0;
     if (umax > 0.0f) frexpf(umax, &eu);
     eu = eu < -100 ? -100 : eu;
     const float dn = ldexpf(1.0f, -eu);
-    if (valid && w == 0 && g == 0) {
-        mult[row] = back;
-        umult[row] = ldexpf(1.0f, eu);
-    }
+    if (valid && w == 0 && g == 0) umult[row] = ldexpf(1.0f, eu);
     // offset operand: value group G (blocks 8G .. 8G + 7) of row r, hi then lo
     if (valid)
         for (int G = 4 * w + g; G < 4 * nch; G += 16) {
@@ -290,29 +294,6 @@ __global__ void __launch_bounds__(256) prescale_tiles_kernel(const int8_t* __res
             dst[0] = hi;
             dst[1] = lo;
         }
-    // pass 2: the prescaled values, one 1 KiB fragment store per block
-    half8_t* tile = reinterpret_cast<half8_t*>(out) + t * nb * 64;
-    for (int c0 = 0; c0 < cols; c0 += sc) {
-        if (sc < cols) {  // more than one slice: stage this one again
-            __syncthreads();
-            stage(c0);
-            __syncthreads();
-        }
-        const int b1 = (cols - c0) / kBlock < sb ? (cols - c0) / kBlock : sb;
-        for (int b = w; b < b1; b += 4) {
-            const uint2 c8 = *reinterpret_cast<const uint2*>(lds + r * qstride + kBlock * b + 8 * g);
-            const float sj = sl[r * sstride + b] * scale;  // exact: a power-of-two scaling
-            half8_t h;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int c = (int8_t)((i < 4 ? c8.x : c8.y) >> (8 * (i & 3)));
-                float v = (float)c * sj;
-                asm volatile("" : "+v"(v));
-                h[i] = (_Float16)v;  // rows past nrows: zero codes and scale, so zeros
-            }
-            tile[(c0 / kBlock + b) * 64 + lane] = h;
-        }
-    }
 }
 
 // The 4-wave gate/up kernel's operand in the tiled layout: tile t of the
@@ -393,8 +374,9 @@ __global__ void __launch_bounds__(256) gather_tiles_kernel(const int8_t* __restr
 __global__ void __launch_bounds__(256) quantize_prescale_kernel(const float* __restrict__ x, int64_t rows,
                                                                 int32_t cols, float uoff, int8_t* __restrict__ q8,
                                                                 float* __restrict__ s_out, _Float16* __restrict__ out,
-                                                                float* __restrict__ mult, _Float16* __restrict__ uop,
-                                                                float* __restrict__ umult, ZeroWords z) {
+                                                                float* __restrict__ mult, float* __restrict__ xn,
+                                                                _Float16* __restrict__ uop, float* __restrict__ umult,
+                                                                ZeroWords z) {
     __shared__ float ush[4][kMaxOffsetChunks * 32];
     if (blockIdx.x == 0 && threadIdx.x < 2 && z.p[threadIdx.x]) *z.p[threadIdx.x] = 0;  // the call's flag words
     const int w = threadIdx.x >> 6;
@@ -404,7 +386,7 @@ __global__ void __launch_bounds__(256) quantize_prescale_kernel(const float* __r
     const int nb = cols / kBlock;
     const int nch = (nb + 31) / 32;
     const float* xrow = x + row * cols;
-    float smax = 0.0f, umax = 0.0f;
+    float smax = 0.0f, umax = 0.0f, sq = 0.0f;
     for (int j0 = 0; j0 < cols / 16; j0 += 64) {  // uniform trip count: the shuffles see whole waves
         const int j = j0 + lane;                  // 16-value group j: block j / 2, half j % 2
         const bool on = j < cols / 16;
@@ -416,7 +398,10 @@ __global__ void __launch_bounds__(256) quantize_prescale_kernel(const float* __r
         }
         float a = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(v[i]));
+        for (int i = 0; i < 16; ++i) {
+            a = fmaxf(a, fabsf(v[i]));
+            sq = fmaf(v[i], v[i], sq);  // zeros past the row
+        }
         a = fmaxf(a, __shfl_xor(a, 1));
         const float s = a / 127.0f;
         int sum = 0;
@@ -450,7 +435,9 @@ __global__ void __launch_bounds__(256) quantize_prescale_kernel(const float* __r
     for (int o = 1; o < 64; o <<= 1) {
         smax = fmaxf(smax, __shfl_xor(smax, o));
         umax = fmaxf(umax, __shfl_xor(umax, o));
+        sq += __shfl_xor(sq, o);
     }
+    if (lane == 0 && xn) xn[row] = sqrtf(sq);
     // the row multiplier, as prescale_kernel computes it from the block scales
     const float bound = 127.0f * smax;
     float back = 1.0f;
@@ -461,6 +448,7 @@ __global__ void __launch_bounds__(256) quantize_prescale_kernel(const float* __r
         back = ldexpf(1.0f, ex - 15);
     }
     if (lane == 0) mult[row] = back;
+    if (!uop) return;  // no offset operand (the Q2_0 map)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -521,21 +509,22 @@ hipError_t launch_gather_tiles(const int8_t* q, const float* s, const int32_t* s
     return hipGetLastError();
 }
 
-hipError_t launch_prescale_tiled(const int8_t* q, const float* s, const ChunkLists& cl, int64_t tiles_cap,
-                                 int32_t cols, float uoff, _Float16* out, float* mult, _Float16* uop, float* umult,
-                                 hipStream_t st) {
+hipError_t launch_tile_h(const int8_t* q, const float* s, const ChunkLists& cl, int64_t tiles_cap, int32_t cols,
+                         float uoff, _Float16* out, float* sout, _Float16* uop, float* umult, hipStream_t st,
+                         const ExpertRange& rng) {
+    const int32_t* first_tile = rng.first ? rng.first + 2 * ((int64_t)rng.E + 1) : nullptr;
     if (tiles_cap > 0)
-        hipLaunchKernelGGL(prescale_tiles_kernel, dim3((unsigned)tiles_cap), dim3(256), prescale_tiles_lds_bytes(cols),
-                           st, q, s, cl.trows, cl.sched + 2, cols, uoff, out, mult, uop, umult);
+        hipLaunchKernelGGL(tile_h_kernel, dim3((unsigned)tiles_cap), dim3(256), tile_h_lds_bytes(cols), st, q, s,
+                           cl.trows, cl.sched + 2, cols, uoff, out, sout, uop, umult, first_tile, rng.e0, rng.e1);
     return hipGetLastError();
 }
 
 hipError_t launch_quantize_prescale(const float* x, int64_t rows, int32_t cols, float uoff, int8_t* q8, float* s,
-                                   _Float16* codes16, float* mult, _Float16* uop, float* umult, hipStream_t st,
-                                   ZeroWords z) {
+                                   _Float16* codes16, float* mult, float* xn, _Float16* uop, float* umult,
+                                   hipStream_t st, ZeroWords z) {
     if (rows > 0)
         hipLaunchKernelGGL(quantize_prescale_kernel, dim3(grid_for(rows, 4)), dim3(256), 0, st, x, rows, cols, uoff,
-                           q8, s, codes16, mult, uop, umult, z);
+                           q8, s, codes16, mult, xn, uop, umult, z);
     return hipGetLastError();
 }
 

@@ -8,15 +8,26 @@
 //
 // Exactness of the selection.  The logits carry an error of the order of an
 // fp32 dot product's (see the router kernel below); near a tie their order
-// may differ from the real one.  For a token where some gap
-// between consecutive ranks 0..K (fp32 order) is below
-// delta = kTieRel * max(1, |l_K|), the experts whose order is in doubt (the
-// ranks next to such a gap, and every expert within delta below the K-th
-// value) are recomputed as fp64 dot products and everything within delta of
-// the K-th value is re-ranked.  With delta above twice the fp32 error, the
-// result equals the ranking of the exact logits (at the synthetic workloads'
-// scale the largest deviation from fp64 logits is about 3e-5 against a delta
-// of about 1e-3).
+// may differ from the real one.  For a token where some gap between
+// consecutive ranks 0..K (fp32 order) is below delta, the experts whose order
+// is in doubt (the ranks next to such a gap, and every expert within delta
+// below the K-th value) are recomputed as fp64 dot products and everything
+// within delta of the K-th value is re-ranked.  With delta above twice the
+// logits' error, the result equals the ranking of the exact logits.
+// delta = max(kTieRel * max(1, |l_K|), 2 * err_t), with err_t the token's
+// error bound.  Each term of the dot product is carried as three fp16
+// products (hi*hi + hi*lo + lo*hi of the two operands' halves: within
+// 2^-20 |x w| of x w), each exact in fp32.  v_mfma_f32_16x16x32_f16 sums its
+// 32 products in fp32-class arithmetic (at most 31 additions) and then adds
+// that sum to the accumulator, so a product passes through at most 31 + 3H/32
+// additions (3 H / 32 MFMAs in the accumulator chain), plus a few for the
+// split reduction and the bias; each addition is taken within 2^-23 of its
+// exact result (truncation as well as rounding), relative to at most
+// sum_h |x_h w_h| <= ||x||_2 ||w_e||_2 (Cauchy-Schwarz).  So
+//     err_t = ((3 H / 32 + 40) 2^-23 + 2^-20) ||x_t||_2 max_e ||w_e||_2.
+// At the synthetic workloads' scale the largest deviation from fp64 logits is
+// about 3e-5 and err_t about 5e-3; inputs with outlier channels raise err_t
+// with ||x_t||.
 #include "internal.h"
 
 #include <cfloat>
@@ -27,6 +38,11 @@ namespace strata_moe {
 namespace {
 
 constexpr float kTieRel = 1.0f / 1024.0f;
+
+// 2 err_t / (||x_t|| max_e ||w_e||), with 1% on top for the fp32 norms.
+__device__ __forceinline__ float tie_coeff(int32_t H) {
+    return 2.02f * ((3.0f * (float)(H / 32) + 40.0f) * 0x1p-23f + 0x1p-20f);
+}
 
 // ---------------------------------------------------------------- logits
 // logits[T][E] = x[T][H] . wr[H][E] (+ bias) on the MFMA unit.  Each fp32
@@ -56,17 +72,28 @@ __device__ __forceinline__ float row_multiplier(float m) {
     return ldexpf(1.0f, ex - 15);
 }
 
-// xm[t] = row multiplier of x[t] (one wave per row).
+// xm[t] = row multiplier of x[t], xn[t] = its Euclidean norm (fp32; one
+// wave per row).
 __global__ void __launch_bounds__(256) row_scale_kernel(const float* __restrict__ x, int64_t T, int32_t H,
-                                                        float* __restrict__ xm) {
+                                                        float* __restrict__ xm, float* __restrict__ xn) {
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     const int lane = threadIdx.x & 63;
-    float m = 0.0f;
-    for (int h = lane; h < H; h += 64) m = fmaxf(m, fabsf(x[t * H + h]));
+    float m = 0.0f, q = 0.0f;
+    for (int h = lane; h < H; h += 64) {
+        const float v = x[t * H + h];
+        m = fmaxf(m, fabsf(v));
+        q = fmaf(v, v, q);
+    }
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-    if (lane == 0) xm[t] = row_multiplier(m);
+    for (int o = 1; o < 64; o <<= 1) {
+        m = fmaxf(m, __shfl_xor(m, o));
+        q += __shfl_xor(q, o);
+    }
+    if (lane == 0) {
+        xm[t] = row_multiplier(m);
+        xn[t] = sqrtf(q);
+    }
 }
 
 // From wt [E][H] (the transposed router weight) and the column maxima of its
@@ -76,10 +103,12 @@ __global__ void __launch_bounds__(256) row_scale_kernel(const float* __restrict_
 // tile and 32-wide k block, the hi fragment then the lo fragment, each 64
 // lanes x 8 values with lane r + 16 g holding expert r of the tile, values
 // 8g..8g+7 of the block; so a wave reads a fragment as 1 KB in one load.
+// Also the largest Euclidean norm of a column, into *wnorm (zeroed before;
+// non-negative floats order like their bit patterns, so an integer maximum).
 __global__ void __launch_bounds__(256) router_prep_kernel(const float* __restrict__ wt,
                                                           const float* __restrict__ pmax, int32_t H, int32_t E,
                                                           int32_t Ep, _Float16* __restrict__ wb,
-                                                          float* __restrict__ wm) {
+                                                          float* __restrict__ wm, float* __restrict__ wnorm) {
     const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (e >= Ep) return;
     const int lane = threadIdx.x & 63;
@@ -93,6 +122,7 @@ __global__ void __launch_bounds__(256) router_prep_kernel(const float* __restric
     if (lane == 0) wm[e] = mult;
     const float4* row = reinterpret_cast<const float4*>(wt + (int64_t)(e < E ? e : 0) * H);
     _Float16* tile = wb + (int64_t)(e >> 4) * nk * 1024;
+    float q = 0.0f;
     for (int j0 = 0; j0 < H / 8; j0 += 256) {  // 4 groups of 8 values per lane in flight
         float4 v[4][2];
 #pragma unroll
@@ -116,12 +146,16 @@ __global__ void __launch_bounds__(256) router_prep_kernel(const float* __restric
                 split_hi_lo(f[i] * inv, h, l);
                 hi[i] = h;
                 lo[i] = l;
+                q = fmaf(f[i], f[i], q);
             }
             half8_t* dst = reinterpret_cast<half8_t*>(tile + (int64_t)(j >> 2) * 1024) + (e & 15) + 16 * (j & 3);
             dst[0] = hi;
             dst[64] = lo;
         }
     }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) q += __shfl_xor(q, o);
+    if (lane == 0 && e < E) atomicMax(reinterpret_cast<int*>(wnorm), __builtin_bit_cast(int, sqrtf(q)));
 }
 
 // 64 tokens x 128 experts per workgroup; wave w takes experts 32w..32w+31 of
@@ -443,9 +477,14 @@ __device__ __forceinline__ void load_logits(const float* __restrict__ l, int nsp
     }
 }
 
+// The near-tie window of a token: kTieRel of its K-th value, or twice its
+// logits' error bound, whichever is wider.  bnd = tie_coeff(H) * ||x_t|| *
+// max_e ||w_e||.
+__device__ __forceinline__ float tie_window(float vK, float bnd) { return fmaxf(kTieRel * fmaxf(1.0f, fabsf(vK)), bnd); }
+
 template <int kSlots>
 __device__ __forceinline__ void select_token(const float* __restrict__ l, int nsplit, int64_t sstride, int32_t E,
-                                             int32_t K, int lane, Selection<kSlots>& S) {
+                                             int32_t K, float bnd, int lane, Selection<kSlots>& S) {
     load_logits(l, nsplit, sstride, E, lane, S);
     S.rounds = K < E ? K + 1 : K;
 #pragma unroll
@@ -496,7 +535,7 @@ __device__ __forceinline__ void select_token(const float* __restrict__ l, int ns
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k)
         if (k == K - 1) S.vK = S.selv[k];
-    S.delta = kTieRel * fmaxf(1.0f, fabsf(S.vK));
+    S.delta = tie_window(S.vK, bnd);
     S.loose = 0;
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k) {
@@ -547,14 +586,16 @@ __device__ __forceinline__ void write_token(const V (&lv)[kMaxTopK], const int (
 constexpr int kWaves = 4;
 template <int kSlots>
 __global__ void __launch_bounds__(256) topk_select_kernel(const float* __restrict__ logits, int nsplit, int64_t T,
-                                                          int32_t E, int32_t K, int32_t* __restrict__ amb,
+                                                          int32_t H, int32_t E, int32_t K,
+                                                          const float* __restrict__ xn,
+                                                          const float* __restrict__ wnorm, int32_t* __restrict__ amb,
                                                           int32_t* __restrict__ sel, int32_t* __restrict__ ids,
                                                           float* __restrict__ p_out) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * kWaves + wave;
     if (t >= T) return;  // whole wave; this kernel has no block-level barrier
     Selection<kSlots> S;
-    select_token(logits + t * E, nsplit, T * E, E, K, lane, S);
+    select_token(logits + t * E, nsplit, T * E, E, K, tie_coeff(H) * xn[t] * *wnorm, lane, S);
     if (S.loose) {
         int word = 0;
 #pragma unroll
@@ -655,7 +696,9 @@ __global__ void __launch_bounds__(256) topk_resolve_kernel(const float* __restri
                                                            int64_t T, const float* __restrict__ x,
                                                            const float* __restrict__ wt,
                                                            const float* __restrict__ bias, int32_t H, int32_t E,
-                                                           int32_t K, const int32_t* __restrict__ amb,
+                                                           int32_t K, const float* __restrict__ xn,
+                                                           const float* __restrict__ wnorm,
+                                                           const int32_t* __restrict__ amb,
                                                            const int32_t* __restrict__ sel,
                                                            int32_t* __restrict__ ids, float* __restrict__ p_out) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -669,7 +712,7 @@ __global__ void __launch_bounds__(256) topk_resolve_kernel(const float* __restri
         for (int k = 0; k < kMaxTopK; ++k) S.seli[k] = sm[k];
         S.loose = (uint32_t)sm[kMaxTopK];
         S.vK = __builtin_bit_cast(float, sm[kMaxTopK + 1]);
-        S.delta = kTieRel * fmaxf(1.0f, fabsf(S.vK));
+        S.delta = tie_window(S.vK, tie_coeff(H) * xn[t] * *wnorm);  // as the select pass took it
         const float thr = S.vK - S.delta;
         double cv[kSlots];
         uint32_t cand = 0, todo = 0;
@@ -745,11 +788,12 @@ __global__ void __launch_bounds__(256) topk_resolve_kernel(const float* __restri
 }  // namespace
 
 hipError_t launch_router_prep(const float* wr, int32_t H, int32_t E, const RouterScratch& rs, hipStream_t st) {
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, reinterpret_cast<int32_t*>(rs.wnorm), 1, 0);
     hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)((E + 31) / 32), (unsigned)((H + 31) / 32)), dim3(256), 0, st,
                        wr, H, E, rs.wt, rs.pmax);
     const int32_t Ep = (int32_t)router_padded_experts(E);
     hipLaunchKernelGGL(router_prep_kernel, dim3((unsigned)((Ep + 3) / 4)), dim3(256), 0, st, rs.wt, rs.pmax, H, E, Ep,
-                       rs.wb, rs.wm);
+                       rs.wb, rs.wm, rs.wnorm);
     return hipGetLastError();
 }
 
@@ -758,8 +802,8 @@ hipError_t launch_router(const float* x, const float* xm, const float* wr, const
     if (T <= 0) return hipGetLastError();
     if (wr) launch_router_prep(wr, H, E, rs, st);
     const int32_t Ep = (int32_t)router_padded_experts(E);
-    if (!xm) {
-        hipLaunchKernelGGL(row_scale_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, x, T, H, rs.xm);
+    if (!xm) {  // the input rows' multipliers and norms
+        hipLaunchKernelGGL(row_scale_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, x, T, H, rs.xm, rs.xn);
         xm = rs.xm;
     }
     hipLaunchKernelGGL(router_mfma_kernel,
@@ -769,26 +813,26 @@ hipError_t launch_router(const float* x, const float* xm, const float* wr, const
     return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* logits, const float* x, const float* wt, const float* bias, int64_t T, int32_t H,
-                       int32_t E, int32_t K, int32_t* amb, int32_t* sel, int32_t* ids, float* p, hipStream_t st,
-                       bool amb_zeroed) {
+hipError_t launch_topk(const float* logits, const float* x, const float* xn, const float* wt, const float* wnorm,
+                       const float* bias, int64_t T, int32_t H, int32_t E, int32_t K, int32_t* amb, int32_t* sel,
+                       int32_t* ids, float* p, hipStream_t st, bool amb_zeroed) {
     if (T > 0) {
         if (!amb_zeroed) hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, amb, 1, 0);
         const int ns = router_splits(T, H, E);
         const dim3 sg((unsigned)((T + kWaves - 1) / kWaves));
         if (E <= 512)
-            hipLaunchKernelGGL(topk_select_kernel<8>, sg, dim3(64 * kWaves), 0, st, logits, ns, T, E, K, amb, sel,
-                               ids, p);
+            hipLaunchKernelGGL(topk_select_kernel<8>, sg, dim3(64 * kWaves), 0, st, logits, ns, T, H, E, K, xn, wnorm,
+                               amb, sel, ids, p);
         else
-            hipLaunchKernelGGL(topk_select_kernel<kPerLane>, sg, dim3(64 * kWaves), 0, st, logits, ns, T, E, K, amb,
-                               sel, ids, p);
+            hipLaunchKernelGGL(topk_select_kernel<kPerLane>, sg, dim3(64 * kWaves), 0, st, logits, ns, T, H, E, K, xn,
+                               wnorm, amb, sel, ids, p);
         const unsigned grid = (unsigned)((T < 8192 ? T : 8192) + kWaves - 1) / kWaves;
         if (E <= 512)
             hipLaunchKernelGGL(topk_resolve_kernel<8>, dim3(grid), dim3(256), 0, st, logits, ns, T, x, wt, bias, H, E,
-                               K, amb, sel, ids, p);
+                               K, xn, wnorm, amb, sel, ids, p);
         else
             hipLaunchKernelGGL(topk_resolve_kernel<kPerLane>, dim3(grid), dim3(256), 0, st, logits, ns, T, x, wt, bias,
-                               H, E, K, amb, sel, ids, p);
+                               H, E, K, xn, wnorm, amb, sel, ids, p);
     }
     return hipGetLastError();
 }

@@ -1,0 +1,265 @@
+// libstrata_probe: measurements of the matrix unit that the layer's design
+// and its error model rest on.  Not part of the layer (no layer entry point
+// calls into it); the benchmark and the tests load it beside libstrata_moe.
+//
+//   strata_probe_mfma_rate: the issue rate of one MFMA form (8 independent
+//     accumulator chains per wave, every SIMD busy), as ops per second.  This
+//     is the measured peak next to the published one.
+//   strata_probe_scaled_blocks: the rate of "per-32-block products, each
+//     scaled into an fp32 accumulator" on register-resident operands, in two
+//     formulations: fp16 MFMA with the weight scale inside the operand and
+//     one FMA per output (the layer's form), and int8 MFMA with both scales
+//     applied per output (convert, multiply, FMA).  Output-blocks per second.
+//   strata_probe_mfma_f16: one v_mfma_f32_16x16x32_f16 on given operands
+//     (row-major A [16][32], B [32][16], C [16][16]), to check how it rounds.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef int int4_t __attribute__((ext_vector_type(4)));
+typedef int int16v_t __attribute__((ext_vector_type(16)));
+
+namespace {
+
+constexpr int kChains = 8;
+constexpr int kWavesPerGroup = 4;
+
+enum Kind { kF16_16x16x32, kF16_32x32x16, kI8_16x16x64, kI8_32x32x32, kI8_16x16x32, kI8_32x32x16, kKinds };
+
+// 2 M N K of each form
+__host__ __device__ constexpr double kind_ops(int k) {
+    return k == kF16_16x16x32 ? 2.0 * 16 * 16 * 32
+         : k == kF16_32x32x16 ? 2.0 * 32 * 32 * 16
+         : k == kI8_16x16x64  ? 2.0 * 16 * 16 * 64
+         : k == kI8_32x32x32  ? 2.0 * 32 * 32 * 32
+         : k == kI8_16x16x32  ? 2.0 * 16 * 16 * 32
+                              : 2.0 * 32 * 32 * 16;
+}
+
+// seed: a value the host passes as 0 (operands stay data-dependent, so the
+// compiler keeps every MFMA); out receives one word per wave.
+template <int kKind>
+__global__ void __launch_bounds__(64 * kWavesPerGroup) mfma_rate_kernel(int32_t iters, int32_t seed,
+                                                                        float* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int s = seed + lane;
+    float r = 0.f;
+    if constexpr (kKind == kF16_16x16x32 || kKind == kF16_32x32x16) {
+        half8_t a, b;
+        for (int i = 0; i < 8; ++i) a[i] = (_Float16)(float)(s + i), b[i] = (_Float16)(float)(s - i);
+        if constexpr (kKind == kF16_16x16x32) {
+            float4_t c[kChains] = {};
+            for (int it = 0; it < iters; ++it)
+#pragma unroll
+                for (int j = 0; j < kChains; ++j) c[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c[j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < kChains; ++j) r += c[j][0];
+        } else {
+            float16_t c[kChains / 2] = {};
+            for (int it = 0; it < iters; ++it)
+#pragma unroll
+                for (int j = 0; j < kChains / 2; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c[j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < kChains / 2; ++j) r += c[j][0];
+        }
+    } else if constexpr (kKind == kI8_16x16x64 || kKind == kI8_32x32x32) {
+        const int4_t a = {s, s + 1, s + 2, s + 3}, b = {s ^ 5, s ^ 6, s ^ 7, s ^ 8};
+        if constexpr (kKind == kI8_16x16x64) {
+            int4_t c[kChains] = {};
+            for (int it = 0; it < iters; ++it)
+#pragma unroll
+                for (int j = 0; j < kChains; ++j) c[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c[j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < kChains; ++j) r += (float)c[j][0];
+        } else {
+            int16v_t c[kChains / 2] = {};
+            for (int it = 0; it < iters; ++it)
+#pragma unroll
+                for (int j = 0; j < kChains / 2; ++j) c[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c[j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < kChains / 2; ++j) r += (float)c[j][0];
+        }
+    } else {
+        const long a = (long)s * 0x0101010101010101L, b = (long)(s ^ 3) * 0x0101010101010101L;
+        if constexpr (kKind == kI8_16x16x32) {
+            int4_t c[kChains] = {};
+            for (int it = 0; it < iters; ++it)
+#pragma unroll
+                for (int j = 0; j < kChains; ++j) c[j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, c[j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < kChains; ++j) r += (float)c[j][0];
+        } else {
+            int16v_t c[kChains / 2] = {};
+            for (int it = 0; it < iters; ++it)
+#pragma unroll
+                for (int j = 0; j < kChains / 2; ++j) c[j] = __builtin_amdgcn_mfma_i32_32x32x16_i8(a, b, c[j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < kChains / 2; ++j) r += (float)c[j][0];
+        }
+    }
+    if (lane == 0) out[blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6)] = r;
+}
+
+// Scaled per-block products on register-resident operands: per block, the
+// wave forms the products of one 32-wide block for a 32 x 32 output tile and
+// adds them, scaled, into fp32 accumulators.
+//   kF16: four v_mfma_f32_16x16x32_f16 (A = the weight codes times d, exact
+//     in fp16; zero accumulator), then per output one FMA with the token's
+//     activation scale: 16 FMAs per lane.
+//   kI8: one v_mfma_i32_32x32x32_i8 (zero accumulator), then per output the
+//     int32 -> fp32 conversion, the product d_row * s_token and the FMA:
+//     16 x 3 VALU per lane.
+// The scales change every block (the per-32 format).
+template <bool kI8>
+__global__ void __launch_bounds__(64 * kWavesPerGroup) scaled_blocks_kernel(int32_t blocks, int32_t seed,
+                                                                            float* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int s = seed + lane;
+    float acc[16] = {};
+    float dsc[16];
+    for (int i = 0; i < 16; ++i) dsc[i] = 1.0f + (float)((s + i) & 7) * 0x1p-10f;
+    float ssc = 1.0f + (float)(s & 15) * 0x1p-12f;
+    if constexpr (kI8) {
+        int4_t a = {s, s + 1, s + 2, s + 3}, b = {s ^ 5, s ^ 6, s ^ 7, s ^ 8};
+#pragma unroll 2
+        for (int blk = 0; blk < blocks; ++blk) {
+            const int16v_t p = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, (int16v_t){}, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] = fmaf((float)p[i], dsc[i] * ssc, acc[i]);
+            a += 1;  // the next block's operands
+            ssc += 0x1p-20f;
+        }
+    } else {
+        half8_t a[4], b;
+        for (int f = 0; f < 4; ++f)
+            for (int i = 0; i < 8; ++i) a[f][i] = (_Float16)(float)((s + i + f) & 3);
+        for (int i = 0; i < 8; ++i) b[i] = (_Float16)(float)(s - i);
+        const half8_t one = {1, 1, 1, 1, 1, 1, 1, 1};
+#pragma unroll 2
+        for (int blk = 0; blk < blocks; ++blk) {
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                const float4_t p = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[f], b, (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[4 * f + v] = fmaf(p[v], ssc, acc[4 * f + v]);
+            }
+            b += one;  // the next block's operands
+            ssc += 0x1p-20f;
+        }
+    }
+    float r = 0.f;
+    for (int i = 0; i < 16; ++i) r += acc[i];
+    if (lane == 0) out[blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6)] = r;
+}
+
+// One 16x16x32 fp16 MFMA on row-major operands, one wave.  The lane layout
+// of the instruction: A lane l holds row l % 16, k = 8 (l / 16) .. + 7; B
+// lane l holds column l % 16, the same k; C/D lane l holds rows
+// 4 (l / 16) + v, column l % 16.
+__global__ void mfma_f16_kernel(const float* __restrict__ A, const float* __restrict__ B,
+                                const float* __restrict__ C, float* __restrict__ D) {
+    const int l = threadIdx.x, r = l & 15, g = l >> 4;
+    half8_t a, b;
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (_Float16)A[r * 32 + 8 * g + i];
+        b[i] = (_Float16)B[(8 * g + i) * 16 + r];
+    }
+    float4_t c;
+    for (int v = 0; v < 4; ++v) c[v] = C[(4 * g + v) * 16 + r];
+    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    for (int v = 0; v < 4; ++v) D[(4 * g + v) * 16 + r] = c[v];
+}
+
+int run_timed(void (*launch)(hipStream_t), double* ms) {
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return -4;
+    launch(nullptr);  // warm
+    (void)hipEventRecord(e0, nullptr);
+    launch(nullptr);
+    (void)hipEventRecord(e1, nullptr);
+    int rc = hipEventSynchronize(e1) == hipSuccess ? 0 : -4;
+    float t = 0.f;
+    if (rc == 0 && hipEventElapsedTime(&t, e0, e1) != hipSuccess) rc = -4;
+    *ms = t;
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (hipGetLastError() != hipSuccess) rc = -4;
+    return rc;
+}
+
+float* g_out = nullptr;
+int32_t g_iters = 0, g_groups = 0;
+
+template <int kKind>
+void launch_rate(hipStream_t st) {
+    hipLaunchKernelGGL(mfma_rate_kernel<kKind>, dim3(g_groups), dim3(64 * kWavesPerGroup), 0, st, g_iters, 0, g_out);
+}
+template <bool kI8>
+void launch_scaled(hipStream_t st) {
+    hipLaunchKernelGGL(scaled_blocks_kernel<kI8>, dim3(g_groups), dim3(64 * kWavesPerGroup), 0, st, g_iters, 0, g_out);
+}
+
+}  // namespace
+
+extern "C" {
+
+// Kinds: 0 f16 16x16x32, 1 f16 32x32x16, 2 i8 16x16x64, 3 i8 32x32x32,
+// 4 i8 16x16x32, 5 i8 32x32x16.  groups workgroups of 4 waves, iters rounds
+// of 8 accumulator chains' worth of MFMAs per wave.  Writes the rate in
+// ops/s (2 M N K per MFMA) and the kernel time.  Returns 0, -1 (arguments),
+// -4 (a HIP call failed).
+int strata_probe_mfma_rate(int kind, int32_t groups, int32_t iters, double* ops_per_s, double* ms) {
+    if (kind < 0 || kind >= kKinds || groups < 1 || iters < 1 || !ops_per_s || !ms) return -1;
+    if (hipMalloc(&g_out, sizeof(float) * groups * kWavesPerGroup) != hipSuccess) return -4;
+    g_iters = iters;
+    g_groups = groups;
+    void (*fns[kKinds])(hipStream_t) = {launch_rate<0>, launch_rate<1>, launch_rate<2>,
+                                        launch_rate<3>, launch_rate<4>, launch_rate<5>};
+    const int rc = run_timed(fns[kind], ms);
+    (void)hipFree(g_out);
+    g_out = nullptr;
+    // the 32x32 forms run kChains / 2 chains (each instruction is twice as long)
+    const bool wide = kind == kF16_32x32x16 || kind == kI8_32x32x32 || kind == kI8_32x32x16;
+    const double mfmas = (double)groups * kWavesPerGroup * iters * (wide ? kChains / 2 : kChains);
+    *ops_per_s = rc == 0 && *ms > 0 ? mfmas * kind_ops(kind) / (*ms * 1e-3) : 0.0;
+    return rc;
+}
+
+// i8 = 0: the fp16 formulation, 1: the int8 one.  Writes 32 x 32 x blocks
+// output-blocks per wave over the kernel time, per second.
+int strata_probe_scaled_blocks(int i8, int32_t groups, int32_t blocks, double* out_blocks_per_s, double* ms) {
+    if (groups < 1 || blocks < 1 || !out_blocks_per_s || !ms) return -1;
+    if (hipMalloc(&g_out, sizeof(float) * groups * kWavesPerGroup) != hipSuccess) return -4;
+    g_iters = blocks;
+    g_groups = groups;
+    const int rc = run_timed(i8 ? launch_scaled<true> : launch_scaled<false>, ms);
+    (void)hipFree(g_out);
+    g_out = nullptr;
+    const double n = (double)groups * kWavesPerGroup * blocks * 1024.0;
+    *out_blocks_per_s = rc == 0 && *ms > 0 ? n / (*ms * 1e-3) : 0.0;
+    return rc;
+}
+
+// D = A B + C for one v_mfma_f32_16x16x32_f16; host arrays A [16][32],
+// B [32][16] (values rounded to fp16 on the device), C, D [16][16] fp32.
+int strata_probe_mfma_f16(const float* A, const float* B, const float* C, float* D) {
+    if (!A || !B || !C || !D) return -1;
+    float* d = nullptr;
+    if (hipMalloc(&d, sizeof(float) * (512 + 512 + 256 + 256)) != hipSuccess) return -4;
+    int rc = 0;
+    if (hipMemcpy(d, A, 512 * 4, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(d + 512, B, 512 * 4, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(d + 1024, C, 256 * 4, hipMemcpyHostToDevice) != hipSuccess)
+        rc = -4;
+    if (rc == 0) {
+        hipLaunchKernelGGL(mfma_f16_kernel, dim3(1), dim3(64), 0, nullptr, d, d + 512, d + 1024, d + 1280);
+        if (hipMemcpy(D, d + 1280, 256 * 4, hipMemcpyDeviceToHost) != hipSuccess) rc = -4;
+    }
+    (void)hipFree(d);
+    return rc;
+}
+
+}  // extern "C"

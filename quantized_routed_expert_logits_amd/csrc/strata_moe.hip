@@ -24,6 +24,25 @@
 
 using namespace strata_moe;
 
+// A ring of device slots through which the experts of layer calls stream
+// from pinned host memory (Winery-Strata prefill.cpp page: the streamed
+// ring's commentary at the top of the file and the fused batch loop of
+// Prefill::run).  Entry k of the stream (a running count over calls) goes to
+// slot k % n_slots; copied[s] is recorded on the copy stream after the DMA
+// into slot s, used[s] on the compute stream after the last launch that
+// reads it, and a DMA into a slot waits for the slot's used event.
+struct strata_moe_ring {
+    int device = 0;
+    int32_t n_slots = 0, hidden = 0, ffn = 0;
+    int64_t slot_bytes = 0;  // one expert: gate/up blob, then down blob
+    int64_t gate_up_bytes = 0;
+    char* slots = nullptr;   // caller-owned device memory
+    hipStream_t copy = nullptr;
+    std::vector<hipEvent_t> copied, used;
+    std::vector<char> used_recorded;
+    int64_t next = 0;        // entries streamed by earlier calls
+};
+
 namespace {
 
 thread_local std::string g_err;
@@ -118,6 +137,7 @@ struct Buffers {
     float* wt;
     _Float16* wb;
     float* wm;
+    float* wnorm;
     float* pmax;
     int32_t* amb;
     int32_t* sel;
@@ -131,6 +151,7 @@ struct Buffers {
     _Float16* xt;  // tiled gate/up operand of big chunks' rows: fp16 codes
     float* xst;    // and their tiled block scales
     float* xe;
+    float* xn;     // the input rows' Euclidean norms (the router's near-tie window)
     _Float16* xuop;
     float* xum;
     int32_t* hist;
@@ -138,6 +159,7 @@ struct Buffers {
     int32_t* offsets;
     Tile* tiles;
     int32_t* ntiles;
+    int32_t* first;  // per-expert first chunk / tile table of the grouping
     int32_t* err;
     int32_t* src;
     int32_t* slot;
@@ -145,8 +167,8 @@ struct Buffers {
     int8_t* hq;
     float* hs;
     TileRows* trows;
-    _Float16* hb;
-    float* he;
+    _Float16* hb;   // tiled H codes (fp16) and their tiled block scales: the down GEMM's operand
+    float* hst;
     _Float16* huop;
     float* hum;
     float* dm;
@@ -154,8 +176,8 @@ struct Buffers {
 };
 
 struct Offsets {
-    size_t logits, wt, wb, wm, pmax, amb, sel, ids, p, gids, gp, xq, xs, xa, xt, xst, xe, xuop, xum, hist, base, offsets, tiles, ntiles, err, src, slot, prow, hq, hs,
-        trows, hb, he, huop, hum, dm, total;
+    size_t logits, wt, wb, wm, wnorm, pmax, amb, sel, ids, p, gids, gp, xq, xs, xa, xt, xst, xe, xn, xuop, xum, hist, base, offsets, tiles, ntiles, first, err, src, slot, prow, hq, hs,
+        trows, hb, hst, huop, hum, dm, total;
     int64_t tiles_cap;
 };
 
@@ -174,6 +196,7 @@ Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I, bool shared)
     o.wt = L.take<float>((int64_t)Er * H);
     o.wb = L.take<_Float16>(router_padded_experts(Er) * H * 2);
     o.wm = L.take<float>(router_padded_experts(Er));
+    o.wnorm = L.take<float>(1);
     o.pmax = L.take<float>((int64_t)((H + 31) / 32) * Er);
     o.amb = L.take<int32_t>(T + 1);
     o.sel = L.take<int32_t>(T * kSelWords);
@@ -184,6 +207,7 @@ Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I, bool shared)
     o.xq = L.take<int8_t>(T * H);
     o.xs = L.take<float>(T * (H / kBlock));
     o.xe = L.take<float>(T);
+    o.xn = L.take<float>(T);
     o.xuop = L.take<_Float16>(T * offset_operand_halves(H));
     o.xum = L.take<float>(T);
     o.hist = L.take<int32_t>(nchunks * E);
@@ -191,6 +215,7 @@ Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I, bool shared)
     o.offsets = L.take<int32_t>(E + 1);
     o.tiles = L.take<Tile>(2 * o.tiles_cap);
     o.ntiles = L.take<int32_t>(kSchedInts);
+    o.first = L.take<int32_t>(first_table_ints(E));
     o.err = L.take<int32_t>(1);
     o.src = L.take<int32_t>(n);
     o.slot = L.take<int32_t>(n);
@@ -202,7 +227,7 @@ Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I, bool shared)
     o.xt = L.take<_Float16>(tiled_rows_cap(n, E) * H);
     o.xst = L.take<float>(tiled_rows_cap(n, E) * (H / kBlock));
     o.hb = L.take<_Float16>(tiled_rows_cap(n, E) * I);
-    o.he = L.take<float>(n);
+    o.hst = L.take<float>(tiled_h_scale_floats(n, E, I));
     o.huop = L.take<_Float16>(n * offset_operand_halves(I));
     o.hum = L.take<float>(n);
     o.dm = L.take<float>(n * H);
@@ -216,6 +241,7 @@ Buffers carve(char* ws, const Offsets& o) {
     b.wt = (float*)(ws + o.wt);
     b.wb = (_Float16*)(ws + o.wb);
     b.wm = (float*)(ws + o.wm);
+    b.wnorm = (float*)(ws + o.wnorm);
     b.pmax = (float*)(ws + o.pmax);
     b.amb = (int32_t*)(ws + o.amb);
     b.sel = (int32_t*)(ws + o.sel);
@@ -229,6 +255,7 @@ Buffers carve(char* ws, const Offsets& o) {
     b.xt = (_Float16*)(ws + o.xt);
     b.xst = (float*)(ws + o.xst);
     b.xe = (float*)(ws + o.xe);
+    b.xn = (float*)(ws + o.xn);
     b.xuop = (_Float16*)(ws + o.xuop);
     b.xum = (float*)(ws + o.xum);
     b.hist = (int32_t*)(ws + o.hist);
@@ -236,6 +263,7 @@ Buffers carve(char* ws, const Offsets& o) {
     b.offsets = (int32_t*)(ws + o.offsets);
     b.tiles = (Tile*)(ws + o.tiles);
     b.ntiles = (int32_t*)(ws + o.ntiles);
+    b.first = (int32_t*)(ws + o.first);
     b.err = (int32_t*)(ws + o.err);
     b.src = (int32_t*)(ws + o.src);
     b.slot = (int32_t*)(ws + o.slot);
@@ -244,7 +272,7 @@ Buffers carve(char* ws, const Offsets& o) {
     b.hs = (float*)(ws + o.hs);
     b.trows = (TileRows*)(ws + o.trows);
     b.hb = (_Float16*)(ws + o.hb);
-    b.he = (float*)(ws + o.he);
+    b.hst = (float*)(ws + o.hst);
     b.huop = (_Float16*)(ws + o.huop);
     b.hum = (float*)(ws + o.hum);
     b.dm = (float*)(ws + o.dm);
@@ -253,9 +281,9 @@ Buffers carve(char* ws, const Offsets& o) {
 }
 
 // ----------------------------------------------------------------- timing
-enum Kind { kQuantize, kRouter, kTopK, kGroup, kGateUp, kPrescaleH, kDown, kCombine, kNumKinds };
-const char* const kKindNames[kNumKinds] = {"quantize", "router_gemm", "topk",  "group",
-                                           "gate_up",  "prescale_h",  "down",  "combine"};
+enum Kind { kQuantize, kRouter, kTopK, kGroup, kGateUp, kTileH, kDown, kCombine, kStreamed, kNumKinds };
+const char* const kKindNames[kNumKinds] = {"quantize", "router_gemm", "topk",    "group",           "gate_up",
+                                           "tile_h",   "down",        "combine", "streamed_experts"};
 
 struct Timing {
     bool on = false;
@@ -329,8 +357,9 @@ int check_experts(const strata_moe_experts* ex) {
 
 // The GEMMs multiply by d (q - 1); the offset pass adds -uoff * d * s * (block
 // code sum) for the rest of the weight map's offset: 0.5 for w = d (q - 1.5),
-// 0 for Q2_0's w = d (q - 1).
+// 0 for Q2_0's w = d (q - 1), which has no offset pass.
 float code_offset(const strata_moe_experts* ex) { return ex->format == STRATA_MOE_Q2_0 ? 0.0f : 0.5f; }
+bool has_offset(const strata_moe_experts* ex) { return code_offset(ex) != 0.0f; }
 
 // The GEMMs address activations with 32-bit buffer offsets: their tiled
 // operands (T*K rows and up to 15 padding rows per expert, [.][H] and [.][I]
@@ -373,8 +402,67 @@ int check_no_overlap(const void* a, const void* b, int64_t bytes) {
     return 0;
 }
 
+// The expert phase with every expert streamed through the ring: batches of
+// at most a third of the ring in expert id order; each batch waits for its
+// last DMA, runs gate/up, the tiled H and down on its experts' rows, and
+// gives its slots back (used events), which lets the next DMAs into them go.
+// All copies are on the ring's one copy stream, in order, so a batch's last
+// copied event covers the others.  Entry k of this call is expert k - G0.
+int run_streamed_experts(const strata_moe_experts* ex, strata_moe_ring* ring, const Buffers& b,
+                         const ChunkLists& cl, int64_t T, int64_t n, int32_t Eg, const _Float16* xuop,
+                         _Float16* huop, hipStream_t st) {
+    const int32_t H = ex->hidden, I = ex->ffn, R = ring->n_slots;
+    const int32_t per = R / 3 > 0 ? R / 3 : 1;
+    const int64_t G0 = ring->next, end = G0 + Eg;
+    int64_t issued = G0, consumed = G0;
+    const char* host = (const char*)ex->gate_up;
+    auto issue = [&](int64_t upto) -> int {  // enqueue the DMAs of entries [issued, upto)
+        for (; issued < upto; ++issued) {
+            const int s = (int)(issued % R);
+            if (ring->used_recorded[s]) HIP_TRY(hipStreamWaitEvent(ring->copy, ring->used[s], 0), "hipStreamWaitEvent");
+            HIP_TRY(hipMemcpyAsync(ring->slots + (int64_t)s * ring->slot_bytes, host + (issued - G0) * ring->slot_bytes,
+                                   ring->slot_bytes, hipMemcpyHostToDevice, ring->copy),
+                    "hipMemcpyAsync (expert DMA)");
+            HIP_TRY(hipEventRecord(ring->copied[s], ring->copy), "hipEventRecord");
+        }
+        return 0;
+    };
+    TRY(issue(end < consumed + R ? end : consumed + R));
+    for (int32_t e0 = 0; e0 < Eg;) {
+        const int32_t e1 = Eg - e0 < per ? Eg : e0 + per;
+        // every copy of the batch is enqueued: e1 - e0 <= per < R entries past `consumed`
+        HIP_TRY(hipStreamWaitEvent(st, ring->copied[(G0 + e1 - 1) % R], 0), "hipStreamWaitEvent");
+        ExpertRange rng;
+        rng.first = cl.first;
+        rng.E = Eg;
+        rng.e0 = e0;
+        rng.e1 = e1;
+        rng.ring0 = G0 % R;
+        rng.nring = R;
+        HIP_TRY(launch_gate_up((const uint8_t*)ring->slots, ring->slot_bytes, cl, n, Eg, b.src, b.xt, b.xst,
+                               tiled_rows_cap(n, Eg), b.xa, b.xs, T, xuop, b.xum, H, I, b.hq, b.hs, st, rng),
+                "gate/up launch");
+        HIP_TRY(launch_tile_h(b.hq, b.hs, cl, tiled_rows_cap(n, Eg) / 16, I, code_offset(ex), b.hb, b.hst, huop, b.hum,
+                              st, rng),
+                "tile launch");
+        HIP_TRY(launch_down((const uint8_t*)ring->slots + ring->gate_up_bytes, ring->slot_bytes, cl, n, Eg, b.src,
+                            b.prow, b.hb, b.hst, tiled_rows_cap(n, Eg), b.hs, huop, b.hum, H, I, b.dm, st, rng),
+                "down launch");
+        for (int64_t k = G0 + e0; k < G0 + e1; ++k) {
+            const int s = (int)(k % R);
+            HIP_TRY(hipEventRecord(ring->used[s], st), "hipEventRecord");
+            ring->used_recorded[s] = 1;
+        }
+        consumed = G0 + e1;
+        TRY(issue(end < consumed + R ? end : consumed + R));
+        e0 = e1;
+    }
+    ring->next = end;
+    return 0;
+}
+
 int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int64_t T, int32_t K, float* out,
-              hipStream_t st, Buffers* keep) {
+              hipStream_t st, Buffers* keep, strata_moe_ring* ring = nullptr) {
     const bool shared = ex->shared_gate != nullptr;
     const int32_t E = ex->n_expert, H = ex->hidden, I = ex->ffn;
     const int32_t Kg = K + shared, Eg = E + shared;  // the grouped pairs per token, the experts they go to
@@ -387,49 +475,62 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     tm.begin(kQuantize);
     // one pass over x: int8 codes and scales, their fp16 copy, row multipliers and
     // offset operand; it also clears the top-K near-tie count and the id error flag
-    HIP_TRY(launch_quantize_prescale(x, T, H, code_offset(ex), b.xq, b.xs, b.xa, b.xe, b.xuop, b.xum, st,
+    _Float16* xuop = has_offset(ex) ? b.xuop : nullptr;
+    _Float16* huop = has_offset(ex) ? b.huop : nullptr;
+    HIP_TRY(launch_quantize_prescale(x, T, H, code_offset(ex), b.xq, b.xs, b.xa, b.xe, b.xn, xuop, b.xum, st,
                                      ZeroWords{{b.amb, b.err}}),
             "quantize launch");
     tm.end(kQuantize);
     tm.begin(kRouter);
     // the router matrix's MFMA operand and transposed copy: prepared once by the
     // caller (experts->router_prepared) or here on every call
-    RouterScratch rs{b.wt, b.wb, b.wm, nullptr, b.pmax};
+    RouterScratch rs{b.wt, b.wb, b.wm, b.wnorm, nullptr, nullptr, b.pmax};
     if (ex->router_prepared) {
         const RouterPrepared rp = router_prepared_layout(H, E);
         char* base = (char*)ex->router_prepared;
-        rs = RouterScratch{(float*)(base + rp.wt), (_Float16*)(base + rp.wb), (float*)(base + rp.wm), nullptr, nullptr};
+        rs = RouterScratch{(float*)(base + rp.wt), (_Float16*)(base + rp.wb), (float*)(base + rp.wm),
+                           (float*)(base + rp.wnorm), nullptr, nullptr, nullptr};
     }
     HIP_TRY(launch_router(x, b.xe, ex->router_prepared ? nullptr : wr, ex->router_bias, T, H, E, rs, b.logits, st),
             "router launch");
     tm.end(kRouter);
     tm.begin(kTopK);
-    HIP_TRY(launch_topk(b.logits, x, rs.wt, ex->router_bias, T, H, E, K, b.amb, b.sel, b.ids, b.p, st, true),
+    HIP_TRY(launch_topk(b.logits, x, b.xn, rs.wt, rs.wnorm, ex->router_bias, T, H, E, K, b.amb, b.sel, b.ids, b.p, st,
+                        true),
             "top-K launch");
     if (shared)
         HIP_TRY(launch_shared_slot(x, ex->shared_gate, b.ids, b.p, T, H, K, E, b.gids, b.gp, st), "shared gate launch");
     tm.end(kTopK);
     tm.begin(kGroup);
-    const ChunkLists cl{b.tiles, b.ntiles, b.tiles_cap, b.trows};
+    const ChunkLists cl{b.tiles, b.ntiles, b.tiles_cap, b.trows, b.first};
     HIP_TRY(launch_group(b.gids, b.gp, n, Kg, Eg, b.hist, b.base, b.offsets, cl, b.src, b.slot, b.prow, b.err, st),
             "group launch");
     // the big chunks' input codes and scales, gathered into the tiled layout
     HIP_TRY(launch_gather_tiles(b.xq, b.xs, b.src, cl, tiled_rows_cap(n, Eg) / 16, H, b.xt, b.xst, st),
             "gather launch");
     tm.end(kGroup);
+    if (ring) {
+        tm.begin(kStreamed);
+        TRY(run_streamed_experts(ex, ring, b, cl, T, n, Eg, xuop, huop, st));
+        tm.end(kStreamed);
+        tm.begin(kCombine);
+        HIP_TRY(launch_combine(b.dm, b.slot, T, Kg, H, out, st), "combine launch");
+        tm.end(kCombine);
+        if (keep) *keep = b;
+        return 0;
+    }
     tm.begin(kGateUp);
     HIP_TRY(launch_gate_up((const uint8_t*)ex->gate_up, ex->gate_up_stride, cl, n, Eg, b.src, b.xt, b.xst,
-                           tiled_rows_cap(n, Eg), b.xa, b.xs, T, b.xuop, b.xum, H, I, b.hq, b.hs, st),
+                           tiled_rows_cap(n, Eg), b.xa, b.xs, T, xuop, b.xum, H, I, b.hq, b.hs, st),
             "gate/up launch");
     tm.end(kGateUp);
-    tm.begin(kPrescaleH);
-    HIP_TRY(launch_prescale_tiled(b.hq, b.hs, cl, tiled_rows_cap(n, Eg) / 16, I, code_offset(ex), b.hb, b.he, b.huop,
-                                  b.hum, st),
-            "prescale launch");
-    tm.end(kPrescaleH);
+    tm.begin(kTileH);
+    HIP_TRY(launch_tile_h(b.hq, b.hs, cl, tiled_rows_cap(n, Eg) / 16, I, code_offset(ex), b.hb, b.hst, huop, b.hum, st),
+            "tile launch");
+    tm.end(kTileH);
     tm.begin(kDown);
-    HIP_TRY(launch_down((const uint8_t*)ex->down, ex->down_stride, cl, n, Eg, b.src, b.prow, b.hb, tiled_rows_cap(n, Eg),
-                        b.he, b.huop, b.hum, H, I, b.dm, st),
+    HIP_TRY(launch_down((const uint8_t*)ex->down, ex->down_stride, cl, n, Eg, b.src, b.prow, b.hb, b.hst,
+                        tiled_rows_cap(n, Eg), b.hs, huop, b.hum, H, I, b.dm, st),
             "down launch");
     tm.end(kDown);
     tm.begin(kCombine);
@@ -481,8 +582,8 @@ int strata_moe_prepare_router(const float* router_w, int32_t hidden, int32_t n_e
     TRY(check_device());
     const RouterPrepared rp = router_prepared_layout(hidden, n_expert);
     char* base = (char*)prepared;
-    const RouterScratch rs{(float*)(base + rp.wt), (_Float16*)(base + rp.wb), (float*)(base + rp.wm), nullptr,
-                           (float*)(base + rp.pmax)};
+    const RouterScratch rs{(float*)(base + rp.wt), (_Float16*)(base + rp.wb), (float*)(base + rp.wm),
+                           (float*)(base + rp.wnorm), nullptr, nullptr, (float*)(base + rp.pmax)};
     HIP_TRY(launch_router_prep(router_w, hidden, n_expert, rs, (hipStream_t)stream), "router prep launch");
     return 0;
 }
@@ -596,6 +697,101 @@ int strata_moe_prefill_debug(const float* x, const float* router_w, const strata
     return 0;
 }
 
+int strata_moe_ring_bytes(int32_t n_slots, int32_t hidden, int32_t ffn, size_t* bytes) {
+    g_err.clear();
+    if (!bytes) return fail(STRATA_MOE_EINVAL, "bytes is NULL");
+    if (n_slots < 1 || n_slots > 65536) return fail(STRATA_MOE_EINVAL, "n_slots %d outside [1, 65536]", n_slots);
+    int64_t gu = 0, dn = 0;
+    TRY(strata_moe_packed_bytes(hidden, ffn, &gu, &dn));
+    *bytes = (size_t)n_slots * (size_t)(gu + dn);
+    return 0;
+}
+
+int strata_moe_ring_create(int32_t n_slots, int32_t hidden, int32_t ffn, void* slots, size_t slot_memory_bytes,
+                           void* copy_stream, strata_moe_ring** ring) {
+    g_err.clear();
+    if (!ring) return fail(STRATA_MOE_EINVAL, "ring is NULL");
+    *ring = nullptr;
+    size_t need = 0;
+    TRY(strata_moe_ring_bytes(n_slots, hidden, ffn, &need));
+    if (!slots || !aligned(slots, 256)) return fail(STRATA_MOE_EINVAL, "slot memory must be 256-byte aligned device memory");
+    if (slot_memory_bytes < need)
+        return fail(STRATA_MOE_EINVAL, "slot memory of %zu bytes, %zu needed", slot_memory_bytes, need);
+    if (!copy_stream) return fail(STRATA_MOE_EINVAL, "the ring needs a copy stream of its own");
+    TRY(check_device());
+    int64_t gu = 0, dn = 0;
+    TRY(strata_moe_packed_bytes(hidden, ffn, &gu, &dn));
+    strata_moe_ring* r = new strata_moe_ring();
+    HIP_TRY(hipGetDevice(&r->device), "hipGetDevice");
+    r->n_slots = n_slots;
+    r->hidden = hidden;
+    r->ffn = ffn;
+    r->gate_up_bytes = gu;
+    r->slot_bytes = gu + dn;
+    r->slots = (char*)slots;
+    r->copy = (hipStream_t)copy_stream;
+    r->copied.assign(n_slots, nullptr);
+    r->used.assign(n_slots, nullptr);
+    r->used_recorded.assign(n_slots, 0);
+    for (int i = 0; i < n_slots; ++i)
+        if (hipEventCreateWithFlags(&r->copied[i], hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&r->used[i], hipEventDisableTiming) != hipSuccess) {
+            strata_moe_ring_destroy(r);
+            return fail(STRATA_MOE_EHIP, "hipEventCreate failed");
+        }
+    *ring = r;
+    return 0;
+}
+
+int strata_moe_ring_destroy(strata_moe_ring* ring) {
+    g_err.clear();
+    if (!ring) return 0;
+    // the events may still be pending: wait for the ring's last DMA and use
+    for (size_t i = 0; i < ring->copied.size(); ++i) {
+        if (ring->copied[i]) (void)hipEventSynchronize(ring->copied[i]);
+        if (ring->used[i] && ring->used_recorded[i]) (void)hipEventSynchronize(ring->used[i]);
+    }
+    for (hipEvent_t e : ring->copied)
+        if (e) (void)hipEventDestroy(e);
+    for (hipEvent_t e : ring->used)
+        if (e) (void)hipEventDestroy(e);
+    delete ring;
+    return 0;
+}
+
+int strata_moe_prefill_streamed(const float* x, const float* router_w, const strata_moe_experts* experts,
+                                strata_moe_ring* ring, int64_t T, int32_t K, float* out, void* stream) {
+    g_err.clear();
+    if (!ring) return fail(STRATA_MOE_EINVAL, "ring is NULL");
+    if (!experts) return fail(STRATA_MOE_EINVAL, "experts is NULL");
+    // the host blobs: expert e's gate/up blob then its down blob, one slot's
+    // bytes per expert (so one DMA moves an expert)
+    if (experts->hidden != ring->hidden || experts->ffn != ring->ffn)
+        return fail(STRATA_MOE_EINVAL, "the ring was made for H = %d, I = %d", ring->hidden, ring->ffn);
+    if (experts->gate_up_stride != ring->slot_bytes || experts->down_stride != ring->slot_bytes ||
+        (const char*)experts->down != (const char*)experts->gate_up + ring->gate_up_bytes)
+        return fail(STRATA_MOE_EINVAL,
+                    "streamed experts must be interleaved: expert e at gate_up + e * %lld, its down blob %lld bytes "
+                    "after its gate/up blob",
+                    (long long)ring->slot_bytes, (long long)ring->gate_up_bytes);
+    TRY(check_layer(T, K, experts));
+    if (T == 0) return 0;
+    if (!x || !router_w || !out) return fail(STRATA_MOE_EINVAL, "null x / router_w / out");
+    if (!aligned(x, 16) || !aligned(out, 16)) return fail(STRATA_MOE_EINVAL, "x and out must be 16-byte aligned");
+    TRY(check_no_overlap(x, out, T * experts->hidden * 4));
+    TRY(check_device());
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+    if (dev != ring->device) return fail(STRATA_MOE_EINVAL, "the ring belongs to device %d", ring->device);
+    if ((hipStream_t)stream == ring->copy) return fail(STRATA_MOE_EINVAL, "the compute stream is the ring's copy stream");
+    hipPointerAttribute_t pa;
+    if (hipPointerGetAttributes(&pa, experts->gate_up) != hipSuccess || pa.type != hipMemoryTypeHost) {
+        (void)hipGetLastError();
+        return fail(STRATA_MOE_EINVAL, "streamed expert blobs must be pinned host memory (hipHostMalloc)");
+    }
+    return run_layer(x, router_w, experts, T, K, out, (hipStream_t)stream, nullptr, ring);
+}
+
 int strata_moe_route(const float* x, const float* router_w, const float* bias, int64_t T, int32_t H, int32_t E,
                      int32_t K, int32_t* ids, float* p, void* stream) {
     g_err.clear();
@@ -612,14 +808,17 @@ int strata_moe_route(const float* x, const float* router_w, const float* bias, i
     const size_t o_amb = L.take<int32_t>(T + 1), o_sel = L.take<int32_t>(T * kSelWords);
     const size_t o_wb = L.take<_Float16>(router_padded_experts(E) * H * 2);
     const size_t o_wm = L.take<float>(router_padded_experts(E)), o_xm = L.take<float>(T);
+    const size_t o_wn = L.take<float>(1), o_xn = L.take<float>(T);
     const size_t o_pm = L.take<float>((int64_t)((H + 31) / 32) * E);
     char* ws = nullptr;
     TRY(get_workspace(L.off, &ws));
     float* logits = (float*)(ws + lo);
     float* wt = (float*)(ws + o_wt);
-    const RouterScratch rs{wt, (_Float16*)(ws + o_wb), (float*)(ws + o_wm), (float*)(ws + o_xm), (float*)(ws + o_pm)};
+    const RouterScratch rs{wt, (_Float16*)(ws + o_wb), (float*)(ws + o_wm), (float*)(ws + o_wn), (float*)(ws + o_xm),
+                           (float*)(ws + o_xn), (float*)(ws + o_pm)};
     HIP_TRY(launch_router(x, nullptr, router_w, bias, T, H, E, rs, logits, st), "router launch");
-    HIP_TRY(launch_topk(logits, x, wt, bias, T, H, E, K, (int32_t*)(ws + o_amb), (int32_t*)(ws + o_sel), ids, p, st),
+    HIP_TRY(launch_topk(logits, x, rs.xn, wt, rs.wnorm, bias, T, H, E, K, (int32_t*)(ws + o_amb), (int32_t*)(ws + o_sel),
+                        ids, p, st),
             "top-K launch");
     return 0;
 }
@@ -692,6 +891,7 @@ int strata_moe_gate_up(const int8_t* qx, const float* sx, const int32_t* offsets
     float* xst = (float*)(ws + o_xst);
     _Float16* xuop = (_Float16*)(ws + o_xuop);
     float* xum = (float*)(ws + o_xum);
+    if (!has_offset(experts)) xuop = nullptr;
     HIP_TRY(launch_prescale(qx, sx, T, H, code_offset(experts), xa, nullptr, xuop, xum, st), "prescale launch");
     HIP_TRY(launch_chunks_from_offsets(offsets, E, n, cl, st), "chunk list launch");  // and the tile table
     HIP_TRY(launch_gather_tiles(qx, sx, src, cl, tiled_rows_cap(n, E) / 16, H, xt, xst, st), "gather launch");
@@ -715,7 +915,7 @@ int strata_moe_down(const int8_t* qh, const float* sh, const int32_t* offsets, c
     const int32_t E = experts->n_expert, H = experts->hidden, I = experts->ffn;
     const int64_t n = T * K;
     Layout L;
-    const size_t o_hb = L.take<_Float16>(tiled_rows_cap(n, E) * I), o_he = L.take<float>(n);
+    const size_t o_hb = L.take<_Float16>(tiled_rows_cap(n, E) * I), o_hst = L.take<float>(tiled_h_scale_floats(n, E, I));
     const size_t o_huop = L.take<_Float16>(n * offset_operand_halves(I)), o_hum = L.take<float>(n);
     const int64_t cap = chunk_list_cap(n, E);
     const size_t o_tiles = L.take<Tile>(2 * cap), o_nt = L.take<int32_t>(kSchedInts), o_prow = L.take<float>(n);
@@ -724,18 +924,18 @@ int strata_moe_down(const int8_t* qh, const float* sh, const int32_t* offsets, c
     TRY(get_workspace(L.off, &ws));
     const ChunkLists cl{(Tile*)(ws + o_tiles), (int32_t*)(ws + o_nt), cap, (TileRows*)(ws + o_trows)};
     _Float16* hb = (_Float16*)(ws + o_hb);
-    float* he = (float*)(ws + o_he);
+    float* hst = (float*)(ws + o_hst);
     _Float16* huop = (_Float16*)(ws + o_huop);
     float* hum = (float*)(ws + o_hum);
     float* prow = (float*)(ws + o_prow);
     float* dm = (float*)(ws + o_dm);
     HIP_TRY(launch_chunks_from_offsets(offsets, E, n, cl, st), "chunk list launch");  // and the tile table
-    HIP_TRY(launch_prescale_tiled(qh, sh, cl, tiled_rows_cap(n, E) / 16, I, code_offset(experts), hb, he, huop, hum,
-                                  st),
-            "prescale launch");
+    if (!has_offset(experts)) huop = nullptr;
+    HIP_TRY(launch_tile_h(qh, sh, cl, tiled_rows_cap(n, E) / 16, I, code_offset(experts), hb, hst, huop, hum, st),
+            "tile launch");
     HIP_TRY(launch_row_weights(slot, p, n, prow, st), "weights launch");
-    HIP_TRY(launch_down((const uint8_t*)experts->down, experts->down_stride, cl, n, E, src, prow, hb,
-                        tiled_rows_cap(n, E), he, huop, hum, H, I, dm, st),
+    HIP_TRY(launch_down((const uint8_t*)experts->down, experts->down_stride, cl, n, E, src, prow, hb, hst,
+                        tiled_rows_cap(n, E), sh, huop, hum, H, I, dm, st),
             "down launch");
     HIP_TRY(launch_combine(dm, slot, T, K, H, out, st), "combine launch");
     return 0;

@@ -94,18 +94,22 @@ def rel_err(y, ref) -> float:
 def down_error_bound(s: S.LayerShape, ref: dict, seed: int = 0) -> np.ndarray:
     """Per-output bound of |y_gpu - y| for the down GEMM and the combine.
 
-    The down GEMM takes each H value q*s (times a power of two per row) as one
-    fp16, so every operand carries a relative error of at most 2^-11 (fp16's
-    unit roundoff); the fp32 accumulation over I products, the routing-weight
-    product and the K-term combine add at most (I + K + 8) * 2^-23 relative to
-    the sum of absolute terms.  Hence
-        |dy[t, j]| <= (2^-11 + (I + K + 8) 2^-23) * sum_k p[t,k] sum_i |W_e[j,i]| |h[t,k,i]|.
+    The down GEMM takes each block's sum of (q - 1) d times the int8 H codes
+    exactly (an integer times an fp16 d, within fp32's 24 bits), then adds it
+    times the block's H scale with one fp32 FMA; the offset term of the
+    symmetric map adds sum_b d u_b with u split into two fp16 halves (22
+    bits); the routing-weight product and the K-term combine round in fp32 as
+    well.  Every rounding is relative to at most the sum of absolute terms,
+    and there are fewer than I / 32 + K + 8 of them on any output's path, so
+        |dy[t, j]| <= (I / 32 + K + 8) 2^-23 * sum_k p[t,k] sum_i |W_e[j,i]| |h[t,k,i]|.
     The absolute weights come from the codes and fp16 scales directly."""
     n = s.T * s.K
     h_abs = np.abs(ref["qh"].astype(np.float64) * np.repeat(ref["sh"].astype(np.float64), 32, axis=1))
     bound = np.zeros((s.T, s.H))
     off, src, slot = ref["offsets"], ref["src"], ref["slot"]
     p = ref["p"].reshape(-1)
+    inv = np.empty(n, np.int64)  # grouped row g holds routed pair inv[g]: token src[g], weight p at that pair
+    inv[slot] = np.arange(n)
     for e in range(s.E):
         o0, o1 = off[e], off[e + 1]
         if o1 == o0:
@@ -114,9 +118,6 @@ def down_error_bound(s: S.LayerShape, ref: dict, seed: int = 0) -> np.ndarray:
         d = ex.scales_d.view(np.float16).astype(np.float64)
         w_abs = np.abs(np.repeat(d, 32, axis=1) * (ex.codes_d.astype(np.float64) - oracle.code_zero(s.fmt)))
         contrib = h_abs[o0:o1] @ w_abs.T                      # [rows][H]
-        # grouped row g is routed pair slot^-1(g): token src[g], weight p at that pair
-        inv = np.empty(n, np.int64)
-        inv[slot] = np.arange(n)
         pairs = inv[o0:o1]
         np.add.at(bound, src[o0:o1], contrib * p[pairs][:, None])
-    return (2.0 ** -11 + (s.I + s.K + 8) * 2.0 ** -23) * bound
+    return (s.I / 32 + s.K + 8) * 2.0 ** -23 * bound

@@ -145,3 +145,77 @@ def test_timing_names(qm):
     n = lib.strata_moe_timing_kinds()
     names = [lib.strata_moe_timing_name(i).decode() for i in range(n)]
     assert "gate_up" in names and "down" in names
+
+
+def test_binding_rejects_mismatched_tensors_before_the_call(qm):
+    """The C entry points take raw pointers and sizes; the binding checks every
+    tensor's shape, dtype and device against the layer's sizes first and
+    raises before the C call (CPU tensors here: nothing reaches a device)."""
+    import torch
+
+    E, H, I, T, K = 8, 256, 128, 4, 2
+    ex = qm.Experts(E, H, I, device="cpu")
+    x = torch.zeros((T, H))
+    wr = torch.zeros((H, E))
+    out = torch.zeros((T, H))
+    bad_layer = [
+        (torch.zeros((T, 384)), wr, out),     # x wider than the experts' hidden size
+        (x, torch.zeros((H, E - 1)), out),    # router_w of another expert count
+        (x, torch.zeros((E, H)), out),        # router_w transposed
+        (x, wr, torch.zeros((T, I))),         # out of the wrong width
+        (x, wr, torch.zeros((T + 1, H))),     # out of another token count
+        (torch.zeros(T * H), wr, out),        # x not 2-D
+    ]
+    for xx, ww, oo in bad_layer:
+        with pytest.raises(ValueError):
+            qm.strata_moe_prefill(xx, ww, ex, K, oo)
+        with pytest.raises(ValueError):
+            qm.strata_moe_prefill_debug(xx, ww, ex, K, oo)
+    with pytest.raises(TypeError):
+        qm.strata_moe_prefill(x.double(), wr, ex, K, out)   # dtype
+    with pytest.raises(TypeError):
+        qm.strata_moe_prefill(x, wr, ex, K, out)            # right shapes, but not device tensors
+    with pytest.raises(ValueError):
+        ex.with_router_bias(torch.zeros(E + 1))
+    with pytest.raises(ValueError):
+        qm.strata_moe_route(x, wr, torch.zeros(E - 1), K)
+    with pytest.raises(ValueError):
+        qm.strata_moe_route(x, wr, None, K, ids=torch.zeros((T, K + 1), dtype=torch.int32))
+    n = T * K
+    qx, sx = torch.zeros((T, H), dtype=torch.int8), torch.zeros((T, H // 32))
+    offsets, src = torch.zeros(E + 1, dtype=torch.int32), torch.zeros(n, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        qm.strata_moe_gate_up(qx, torch.zeros((T, H // 16)), offsets, src, K, ex)
+    with pytest.raises(ValueError):
+        qm.strata_moe_gate_up(qx, sx, torch.zeros(E, dtype=torch.int32), src, K, ex)
+    with pytest.raises(ValueError):
+        qm.strata_moe_gate_up(qx, sx, offsets, torch.zeros(n - 1, dtype=torch.int32), K, ex)
+    qh, sh = torch.zeros((n, I), dtype=torch.int8), torch.zeros((n, I // 32))
+    slot, p = torch.zeros(n, dtype=torch.int32), torch.zeros((T, K))
+    with pytest.raises(ValueError):
+        qm.strata_moe_down(torch.zeros((n, H), dtype=torch.int8), sh, offsets, src, slot, p, ex, out)
+    with pytest.raises(ValueError):
+        qm.strata_moe_down(qh, sh, offsets, src, slot, p, ex, torch.zeros((T, I)))
+    with pytest.raises(TypeError):
+        qm.strata_moe_down(qh, sh, offsets, src, slot, p, ex, out)  # right shapes, CPU tensors
+
+
+def test_ring_sizes_and_host_checks(qm):
+    lib = qm.library()
+    b = ctypes.c_size_t()
+    assert lib.strata_moe_ring_bytes(96, 2560, 1024, ctypes.byref(b)) == 0
+    gu, dn = qm.strata_moe_packed_bytes(2560, 1024)
+    assert b.value == 96 * (gu + dn)  # one expert (gate/up + down) per slot
+    assert lib.strata_moe_ring_bytes(0, 2560, 1024, ctypes.byref(b)) == qm.EINVAL
+    h = ctypes.c_void_p()
+    # no copy stream; too little slot memory; misaligned memory: rejected before any device call
+    assert lib.strata_moe_ring_create(4, 256, 128, ctypes.c_void_p(1 << 20), 1 << 30, None, ctypes.byref(h)) \
+        == qm.EINVAL
+    assert lib.strata_moe_ring_create(4, 256, 128, ctypes.c_void_p(1 << 20), 256, ctypes.c_void_p(8),
+                                      ctypes.byref(h)) == qm.EINVAL
+    assert lib.strata_moe_ring_create(4, 256, 128, ctypes.c_void_p((1 << 20) + 8), 1 << 30, ctypes.c_void_p(8),
+                                      ctypes.byref(h)) == qm.EINVAL
+    assert lib.strata_moe_ring_destroy(None) == 0
+    st = _experts_struct(qm)
+    assert lib.strata_moe_prefill_streamed(ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.byref(st), None, 8, 10,
+                                           ctypes.c_void_p(16), None) == qm.EINVAL

@@ -3,7 +3,9 @@
 Bars: routing ids, grouping tables and the layer input's int8 codes and
 scales bit-exact; routing weights within 2e-5 absolute (fp32 logits: about
 4e-6 of logit error, far below); SwiGLU-output codes equal except at rounding
-ties of the oracle's exact quotient (then off by one); the layer output within
+ties of the oracle's exact quotient (then off by one), at a rate below 1e-3;
+the down stage fed the oracle's H codes within max|err| / max|ref| <= 1e-5
+(and a per-output fp32 rounding bound); the layer output within
 max|err| / max|ref| <= 2e-3.
 """
 import numpy as np
@@ -19,6 +21,8 @@ pytestmark = pytest.mark.gpu
 
 P_TOL = 2e-5
 Y_TOL = 2e-3
+DOWN_TOL = 1e-5   # the down stage alone, on the oracle's H codes
+H_RATE = 1e-3     # largest share of SwiGLU-output codes that may sit one step off at a rounding tie
 
 
 @pytest.fixture(scope="module")
@@ -78,12 +82,6 @@ def _route_case(qm, x, wr, bias, K):
     assert np.abs(p.astype(np.float64).sum(1) - 1).max() <= 1e-6
 
 
-@pytest.mark.parametrize("name", ["tiny", "stream_all_1k", "skewed_4k"])
-def test_route_matches_oracle(qm, name):
-    s = S.shape(name)
-    _route_case(qm, S.activations(s), S.router_weight(s), S.router_bias(s), s.K)
-
-
 def test_route_many_experts(qm):
     """More than 512 experts: the selection keeps 16 logits per lane."""
     s = S.custom(T=200, H=256, E=1000, K=12, I=32)
@@ -112,16 +110,71 @@ def test_route_near_ties_are_settled_exactly(qm):
     _route_case(qm, x, wr, None, s.K)
 
 
-@pytest.mark.parametrize("name", ["chunk_8k", "long_32k"])
-def test_route_full_size_sampled(qm, name):
+def boundary_gaps(logits, K):
+    """Per token, the exact logit gap between ranks K-1 and K (the smallest
+    change that would alter the selected set)."""
+    part = -np.partition(-logits, K, axis=1)[:, :K + 1]
+    part = -np.sort(-part, axis=1)
+    return part[:, K - 1] - part[:, K]
+
+
+@pytest.mark.parametrize("name", ["tiny", "stream_all_1k", "chunk_8k", "long_32k", "skewed_4k"])
+def test_route_all_tokens(qm, name):
+    """Every token of the five workloads: ids bit-exact, p within P_TOL.
+    Also reports the smallest exact boundary gap l_(K) - l_(K+1) over the
+    tokens and how many tokens sit below 1e-6 (the margin the near-tie
+    re-score has to settle)."""
     s = S.shape(name)
-    x, wr = S.activations(s), S.router_weight(s)
+    x, wr, bias = S.activations(s), S.router_weight(s), S.router_bias(s)
+    ids, p = qm.strata_moe_route(_t(x), _t(wr), None if bias is None else _t(bias), s.K)
+    logits = oracle.router_logits(x, wr, bias)
+    ids_r, p_r = oracle.topk_softmax(logits, s.K)
+    gap = boundary_gaps(logits, s.K)
+    ids, p = ids.cpu().numpy(), p.cpu().numpy()
+    print(f"{name}: {s.T} tokens, min boundary gap {gap.min():.3e}, tokens below 1e-6: {(gap < 1e-6).sum()}, "
+          f"mismatched tokens: {int((ids != ids_r).any(1).sum())}")
+    assert np.array_equal(ids, ids_r)
+    assert np.abs(p - p_r).max() <= P_TOL
+    assert np.abs(p.astype(np.float64).sum(1) - 1).max() <= 1e-6
+
+
+def router_error_bound(x, wr):
+    """Per-token bound of the GPU logits' error, as the routing kernels model
+    it: three fp16 products per term (hi and lo halves, 2^-20 of |x||w|
+    together), each passing through at most 31 additions inside an MFMA and
+    3 H / 32 accumulator additions, plus a few for the split reduction and the
+    bias, each within 2^-23 of its result; sum_h |x_h w_he| <=
+    ||x||_2 ||w_e||_2."""
+    H = x.shape[1]
+    c = (3 * H / 32 + 40) * 2.0 ** -23 + 2.0 ** -20
+    xn = np.linalg.norm(x.astype(np.float64), axis=1)
+    wn = np.linalg.norm(wr.astype(np.float64), axis=0).max()
+    return c * xn * wn
+
+
+def test_route_outlier_channels(qm):
+    """Heavy-tailed inputs with a few outlier channels (Student-t values, 8
+    channels scaled by 200): logits far above the synthetic scale, where a
+    window fixed by the logits' size alone would be too narrow.  Every token's
+    ids bit-exact; p within the softmax's response to the logit error bound."""
+    s = S.custom(T=2048, H=2560, E=512, K=10, I=32)
+    rng = np.random.default_rng(21)
+    x = rng.standard_t(3, (s.T, s.H))
+    x[:, rng.choice(s.H, 8, replace=False)] *= 200.0
+    x = x.astype(np.float32)
+    wr = S.router_weight(s, 21)
+    wr[:, 300] = wr[:, 299]            # an exact tie
+    wr[:, 301] = wr[:, 299]
+    wr[7, 301] = np.nextafter(wr[7, 299], np.float32(np.inf))  # and a one-ulp near tie
     ids, p = qm.strata_moe_route(_t(x), _t(wr), None, s.K)
-    rng = np.random.default_rng(11)
-    tok = np.unique(np.concatenate([[0, s.T - 1], rng.choice(s.T, 1022, replace=False)]))
-    ids_r, p_r = oracle.topk_softmax(oracle.router_logits(x[tok], wr), s.K)
-    assert np.array_equal(ids.cpu().numpy()[tok], ids_r)
-    assert np.abs(p.cpu().numpy()[tok] - p_r).max() <= P_TOL
+    logits = oracle.router_logits(x, wr)
+    ids_r, p_r = oracle.topk_softmax(logits, s.K)
+    ids, p = ids.cpu().numpy(), p.cpu().numpy()
+    print(f"outlier channels: logits up to {np.abs(logits).max():.1f}, min boundary gap "
+          f"{boundary_gaps(logits, s.K).min():.3e}, mismatched tokens {int((ids != ids_r).any(1).sum())}")
+    assert np.array_equal(ids, ids_r)
+    tol = 2.0 * router_error_bound(x, wr)[:, None] + 1e-6
+    assert np.all(np.abs(p - p_r) <= tol)
 
 
 # -------------------------------------------------------------------- group
@@ -158,7 +211,12 @@ STAGE_SHAPES = [S.shape("tiny"), S.custom(T=300, H=256, E=12, K=3, I=128), S.cus
                 # the pages' Q2_0 map, and its FFN width 640 (20 blocks: not a multiple of 8)
                 S.custom(T=300, H=256, E=12, K=3, I=128, fmt="q2_0"), S.custom(T=160, H=512, E=6, K=2, I=640, fmt="q2_0"),
                 # about 40 rows per expert: 3-tile chunks in the small-chunk kernel
-                S.custom(T=200, H=256, E=10, K=2, I=128)]
+                S.custom(T=200, H=256, E=10, K=2, I=128),
+                # the production widths H = 2560, I = 1024 at small T: three 32-block chunks
+                # of the offset pass, the 8-deep record ring; about 24 rows per expert (the
+                # small-chunk kernel) and about 107 (the 4-wave kernel, 7 tiles)
+                S.custom(T=48, H=2560, E=4, K=2, I=1024), S.custom(T=160, H=2560, E=3, K=2, I=1024),
+                S.custom(T=96, H=2560, E=4, K=2, I=640, fmt="q2_0")]
 
 
 @pytest.mark.parametrize("s", STAGE_SHAPES, ids=lambda s: s.name)
@@ -167,7 +225,8 @@ def test_gate_up_stage(qm, s):
     ex = gpu_experts(s)
     qh, sh = qm.strata_moe_gate_up(_t(ref["qx"]), _t(ref["sx"]), _t(ref["offsets"]), _t(ref["src"]), s.K, ex)
     rate = check_h_codes(qh.cpu().numpy(), sh.cpu().numpy(), ref["h"], ref["qh"], ref["sh"])
-    assert rate < 1e-3
+    print(f"{s.name}: H-code mismatch rate {rate:.2e}")
+    assert rate < H_RATE
 
 
 @pytest.mark.parametrize("s", STAGE_SHAPES, ids=lambda s: s.name)
@@ -180,7 +239,9 @@ def test_down_stage(qm, s):
     err = np.abs(out.cpu().numpy().astype(np.float64) - ref["y"])
     bound = down_error_bound(s, ref)
     assert np.all(err <= bound), f"max err/bound {np.max(err / np.maximum(bound, 1e-300)):.3f}"
-    assert rel_err(out.cpu().numpy(), ref["y"]) <= Y_TOL
+    rel = rel_err(out.cpu().numpy(), ref["y"])
+    print(f"{s.name}: down stage max|dy|/max|y| = {rel:.2e}")
+    assert rel <= DOWN_TOL
 
 
 # --------------------------------------------------------------- the layer
@@ -197,7 +258,7 @@ def test_layer_all_intermediates(qm, s):
     for k in ("ids", "offsets", "src", "slot", "qx", "sx"):
         assert np.array_equal(g[k], ref[k]), k
     assert np.abs(g["p"] - ref["p"]).max() <= P_TOL
-    check_h_codes(g["qh"], g["sh"], ref["h"], ref["qh"], ref["sh"])
+    assert check_h_codes(g["qh"], g["sh"], ref["h"], ref["qh"], ref["sh"]) < H_RATE
     assert rel_err(g["out"], ref["y"]) <= Y_TOL
 
 
@@ -226,9 +287,9 @@ def test_layer_with_shared_expert(qm, s):
     assert np.array_equal(g["src"][o0:], np.arange(T))  # the shared expert's rows: every token in order
     for k in ("qx", "sx"):
         assert np.array_equal(g[k], ref[k]), k
-    check_h_codes(g["qh"][:o0], g["sh"][:o0], ref["h"], ref["qh"], ref["sh"])
+    assert check_h_codes(g["qh"][:o0], g["sh"][:o0], ref["h"], ref["qh"], ref["sh"]) < H_RATE
     rs = ref["shared"]
-    check_h_codes(g["qh"][o0:], g["sh"][o0:], rs["h"], rs["qh"], rs["sh"])
+    assert check_h_codes(g["qh"][o0:], g["sh"][o0:], rs["h"], rs["qh"], rs["sh"]) < H_RATE
     assert rel_err(g["out"], ref["y"]) <= Y_TOL
     # the plain entry point gives the same bits
     y = qm.strata_moe_prefill(_t(x), _t(wr), ex, s.K, torch.empty_like(out))
@@ -297,7 +358,7 @@ def test_full_layer_sampled(qm, name):
     qm.strata_moe_prefill(xt, wt, ex, s.K, out)          # the launch the benchmark times
     y = out.cpu().numpy()
     d = qm.strata_moe_prefill_debug(xt, wt, ex, s.K, torch.empty_like(xt))
-    g = {k: v.cpu().numpy() for k, v in d.items() if k in ("ids", "offsets", "src", "slot", "qx")}
+    g = {k: v.cpu().numpy() for k, v in d.items() if k in ("ids", "p", "offsets", "src", "slot", "qx", "sx", "qh", "sh")}
     _check_grouping_props(g, s.T, s.K + s.shared, s.E + s.shared)
     rng = np.random.default_rng(5)
     tok = [0, s.T - 1] + list(rng.choice(s.T, 30, replace=False))
@@ -308,7 +369,15 @@ def test_full_layer_sampled(qm, name):
     tok = np.unique(tok)
     ref = oracle.layer_tokens(x, wr, bias, getter(s), s.K, tok, fmt=s.fmt, shared=shared_args(s))
     assert np.array_equal(g["ids"][tok][:, :s.K], ref["ids"])
-    assert np.array_equal(g["qx"][tok], ref["qx"])
+    assert np.abs(g["p"][tok][:, :s.K] - ref["p"]).max() <= P_TOL
+    assert np.array_equal(g["qx"][tok], ref["qx"]) and np.array_equal(g["sx"][tok], ref["sx"])
+    # the sampled tokens' routed rows: pair t*Kg + k sits in grouped row slot[t*Kg + k]
+    Kg = s.K + s.shared
+    rows = g["slot"].reshape(s.T, Kg)[tok][:, :s.K].reshape(-1)
+    I = s.I
+    rate = check_h_codes(g["qh"][rows], g["sh"][rows], ref["h"].reshape(-1, I), ref["qh"].reshape(-1, I),
+                         ref["sh"].reshape(-1, I // 32))
     err = rel_err(y[tok], ref["y"])
-    print(f"{name}: {len(tok)} sampled tokens, max|dy|/max|y| = {err:.2e}")
+    print(f"{name}: {len(tok)} sampled tokens, max|dy|/max|y| = {err:.2e}, H-code mismatch rate {rate:.2e}")
+    assert rate < H_RATE
     assert err <= Y_TOL
