@@ -187,6 +187,22 @@ int strata_moe_prepare_router(const float* router_w, int32_t hidden, int32_t n_e
 int strata_moe_prefill(const float* x, const float* router_w, const strata_moe_experts* experts, int64_t T,
                        int32_t K, float* out, void* stream);
 
+/* strata_moe_prefill for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The same launches as strata_moe_prefill, but the workspace is
+ * a fixed device array of STRATA_MOE_NOALLOC_SCRATCH_BYTES inside the
+ * library (one per GPU, held until the process ends), so the call allocates
+ * and frees nothing.  A call whose workspace (strata_moe_workspace_bytes)
+ * exceeds it fails with EINVAL and enqueues nothing: at H = 2560, I = 1024,
+ * E = 512, K = 10 that is above about 2,200 tokens.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other host threads) race and must not be made.  Nothing in the array needs
+ * to start at zero; the flags a call relies on are cleared by its own first
+ * kernel. */
+#define STRATA_MOE_NOALLOC_SCRATCH_BYTES ((size_t)512 << 20)
+int strata_moe_prefill_noalloc(const float* x, const float* router_w, const strata_moe_experts* experts, int64_t T,
+                               int32_t K, float* out, void* stream);
+
 /* strata_moe_prefill, then the intermediates copied into `dbg` (host struct
  * of device pointers). */
 int strata_moe_prefill_debug(const float* x, const float* router_w, const strata_moe_experts* experts, int64_t T,

@@ -71,6 +71,7 @@ _sig("strata_moe_prepare_router", [_P, _i32, _i32, _P, _P])
 _sig("strata_moe_pack", [_P, _P, _P, _P, _i32, _i32, _i32, _i32, _P, _i64, _P, _i64, _P])
 _sig("strata_moe_unpack", [_P, _i64, _P, _i64, _i32, _i32, _i32, _i32, _P, _P, _P, _P, _P])
 _sig("strata_moe_prefill", [_P, _P, ctypes.POINTER(ExpertsStruct), _i64, _i32, _P, _P])
+_sig("strata_moe_prefill_noalloc", [_P, _P, ctypes.POINTER(ExpertsStruct), _i64, _i32, _P, _P])
 _sig("strata_moe_prefill_debug", [_P, _P, ctypes.POINTER(ExpertsStruct), _i64, _i32, _P,
                                   ctypes.POINTER(DebugStruct), _P])
 _sig("strata_moe_route", [_P, _P, _P, _i64, _i32, _i32, _i32, _P, _P, _P])
@@ -95,7 +96,9 @@ EXPORTED = [
     "strata_moe_quantize", "strata_moe_gate_up", "strata_moe_down", "strata_moe_timing",
     "strata_moe_timing_kinds", "strata_moe_timing_name", "strata_moe_timing_read",
     "strata_moe_ring_bytes", "strata_moe_ring_create", "strata_moe_ring_destroy", "strata_moe_prefill_streamed",
+    "strata_moe_prefill_noalloc",
 ]
+NOALLOC_SCRATCH_BYTES = 512 << 20  # STRATA_MOE_NOALLOC_SCRATCH_BYTES
 
 
 def library() -> ctypes.CDLL:
@@ -424,6 +427,15 @@ def strata_moe_prefill(x: torch.Tensor, router_w: torch.Tensor, experts: Experts
     T = _check_layer_args(x, router_w, experts, out)
     _check(_lib.strata_moe_prefill(_ptr(x), _ptr(router_w), ctypes.byref(experts.struct), T, K, _ptr(out),
                                    _stream(stream)), "strata_moe_prefill")
+    return out
+
+
+def strata_moe_prefill_noalloc(x: torch.Tensor, router_w: torch.Tensor, experts: Experts, K: int, out: torch.Tensor,
+                               stream=None) -> torch.Tensor:
+    """strata_moe_prefill on the library's fixed scratch: no device allocation."""
+    T = _check_layer_args(x, router_w, experts, out)
+    _check(_lib.strata_moe_prefill_noalloc(_ptr(x), _ptr(router_w), ctypes.byref(experts.struct), T, K, _ptr(out),
+                                           _stream(stream)), "strata_moe_prefill_noalloc")
     return out
 
 

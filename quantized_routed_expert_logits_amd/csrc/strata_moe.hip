@@ -461,15 +461,25 @@ int run_streamed_experts(const strata_moe_experts* ex, strata_moe_ring* ring, co
     return 0;
 }
 
+// fixed_ws: a caller-provided workspace of fixed_bytes (then nothing is
+// allocated), or null for the library's workspace.
 int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int64_t T, int32_t K, float* out,
-              hipStream_t st, Buffers* keep, strata_moe_ring* ring = nullptr) {
+              hipStream_t st, Buffers* keep, strata_moe_ring* ring = nullptr, char* fixed_ws = nullptr,
+              size_t fixed_bytes = 0) {
     const bool shared = ex->shared_gate != nullptr;
     const int32_t E = ex->n_expert, H = ex->hidden, I = ex->ffn;
     const int32_t Kg = K + shared, Eg = E + shared;  // the grouped pairs per token, the experts they go to
     const int64_t n = T * Kg;
     const Offsets o = plan(T, K, E, H, I, shared);
-    char* ws = nullptr;
-    TRY(get_workspace(o.total, &ws));
+    char* ws = fixed_ws;
+    if (fixed_ws) {
+        if (o.total > fixed_bytes)
+            return fail(STRATA_MOE_EINVAL,
+                        "this call needs %zu bytes of scratch; the fixed scratch holds %zu (fewer tokens per call)",
+                        o.total, fixed_bytes);
+    } else {
+        TRY(get_workspace(o.total, &ws));
+    }
     Buffers b = carve(ws, o);
     CallTimer tm(st);
     tm.begin(kQuantize);
@@ -537,6 +547,29 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     HIP_TRY(launch_combine(b.dm, b.slot, T, Kg, H, out, st), "combine launch");
     tm.end(kCombine);
     if (keep) *keep = b;
+    return 0;
+}
+
+// The scratch of strata_moe_prefill_noalloc: one array per GPU the library
+// runs on, loaded with the code object and held until the process ends.  Its
+// device address comes from hipGetSymbolAddress once per device (the array's
+// name in host code is not a device address).
+static __device__ __align__(256) unsigned char scratch[STRATA_MOE_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[64] = {};
+
+int noalloc_scratch(char** out) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(STRATA_MOE_EINVAL, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        if (!p || !aligned(p, 256)) return fail(STRATA_MOE_EHIP, "the scratch array has no usable device address");
+        g_scratch_ptr[dev] = (char*)p;
+    }
+    *out = g_scratch_ptr[dev];
     return 0;
 }
 
@@ -664,6 +697,21 @@ int strata_moe_prefill(const float* x, const float* router_w, const strata_moe_e
     TRY(check_no_overlap(x, out, T * experts->hidden * 4));
     TRY(check_device());
     return run_layer(x, router_w, experts, T, K, out, (hipStream_t)stream, nullptr);
+}
+
+int strata_moe_prefill_noalloc(const float* x, const float* router_w, const strata_moe_experts* experts, int64_t T,
+                               int32_t K, float* out, void* stream) {
+    g_err.clear();
+    TRY(check_layer(T, K, experts));
+    if (T == 0) return 0;
+    if (!x || !router_w || !out) return fail(STRATA_MOE_EINVAL, "null x / router_w / out");
+    if (!aligned(x, 16) || !aligned(out, 16)) return fail(STRATA_MOE_EINVAL, "x and out must be 16-byte aligned");
+    TRY(check_no_overlap(x, out, T * experts->hidden * 4));
+    TRY(check_device());
+    char* ws = nullptr;
+    TRY(noalloc_scratch(&ws));
+    return run_layer(x, router_w, experts, T, K, out, (hipStream_t)stream, nullptr, nullptr, ws,
+                     STRATA_MOE_NOALLOC_SCRATCH_BYTES);
 }
 
 int strata_moe_prefill_debug(const float* x, const float* router_w, const strata_moe_experts* experts, int64_t T,

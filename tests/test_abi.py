@@ -219,3 +219,12 @@ def test_ring_sizes_and_host_checks(qm):
     st = _experts_struct(qm)
     assert lib.strata_moe_prefill_streamed(ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.byref(st), None, 8, 10,
                                            ctypes.c_void_p(16), None) == qm.EINVAL
+
+
+def test_noalloc_entry_point_checks_on_the_host(qm):
+    lib = qm.library()
+    st = _experts_struct(qm)
+    # argument errors come back before the scratch array or any device is touched
+    assert lib.strata_moe_prefill_noalloc(ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.byref(st), 8, 0,
+                                          ctypes.c_void_p(16), None) == qm.EINVAL
+    assert lib.strata_moe_prefill_noalloc(None, None, ctypes.byref(st), 0, 10, None, None) == 0  # T = 0: no-op
