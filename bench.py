@@ -22,6 +22,8 @@ Prints one JSON line on stdout (progress goes to stderr):
                bytes per second against the 8 TB/s HBM peak
   streamed     the same layer with every expert streamed from pinned host
                memory through rings of 96, 384 and 512 device slots
+  small_t      32- and 256-token chunks: ms per step, gate/up's weight GB/s,
+               and the same chunks through the other small-T kernel choices
   mfma_measured  the matrix unit's rates measured on this device
   cpu_baseline the CPU oracle (double precision) timed on this host on a
                bounded sample of the same workload
@@ -71,6 +73,8 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--rings", default="96,384,512",
                     help="ring sizes (slots) of the streamed-experts measurement, comma separated ('' = skip)")
     ap.add_argument("--ring-steps", type=int, default=5, help="timed steps per ring size")
+    ap.add_argument("--small-t", default="window_32,short_256",
+                    help="small-T workloads timed on the same experts, comma separated ('' = skip)")
     ap.add_argument("--cpu-tokens", type=int, default=4096, help="tokens in the CPU-oracle sample (0 = skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB after flushing the Infinity Cache "
@@ -278,6 +282,34 @@ def main() -> int:
             log(f"{s2.name}: {ms2:.3f} ms/step, hit experts' weights at {second['weight_gbs']} GB/s "
                 f"({100 * second['frac_hbm']:.1f}% of 8 TB/s)")
 
+    small_t = None
+    names = [w for w in args.small_t.split(",") if w.strip()]
+    if names and not s.shared and not s.skewed:
+        small_t = {}
+        gu_bytes = 2 * s.I * s.H * (2 / 8 + 2 / 32)  # one expert's packed gate/up matrix
+        for name in names:
+            s3 = S.shape(name)
+            if (s3.E, s3.H, s3.I, s3.fmt) != (s.E, s.H, s.I, s.fmt):
+                continue
+            x3 = torch.from_numpy(S.activations(s3, args.seed)).to(dev)
+            ex3 = base_experts if args.router_per_call else base_experts.with_prepared_router(wr)
+            out3 = torch.empty_like(x3)
+            ids3 = qm.strata_moe_prefill_debug(x3, wr, ex3, s3.K, out3)["ids"]
+            hit3 = hit_experts(torch, ids3, s3.E)
+            entry = {"T": s3.T, "hit_experts": hit3}
+            for label, flags in (("gemv", 0), ("mfma_only", qm.FLAG_NO_GEMV), ("per_slot_q8", qm.FLAG_PER_SLOT_Q8)):
+                exf = ex3.with_flags(flags)
+                region_ms(qm, torch, s3, x3, wr, exf, out3, 20)  # warm
+                ms3, _ = region_ms(qm, torch, s3, x3, wr, exf, out3, 200)
+                per3, kms3 = time_steps(qm, torch, s3, x3, wr, exf, out3, 100, 0)
+                gbs = hit3 * gu_bytes / (kms3["gate_up"] * 1e-3) / 1e9
+                entry[label] = {"ms_per_step": round(ms3, 4), "median_ms": round(statistics.median(per3), 4),
+                                "gate_up_ms": round(kms3["gate_up"], 4), "down_ms": round(kms3["down"], 4),
+                                "gate_up_weight_gbs": round(gbs, 1), "gate_up_frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+                log(f"{name} [{label}]: {ms3:.3f} ms/step, gate/up {kms3['gate_up']:.4f} ms "
+                    f"({gbs:.0f} GB/s of hit experts' weights), down {kms3['down']:.4f} ms")
+            small_t[name] = entry
+
     streamed = None
     rings = [int(r) for r in args.rings.split(",") if r.strip()]
     if rings and not s.shared:
@@ -370,6 +402,7 @@ def main() -> int:
         "roofline": roofline,
         "stream_all_1k": second,
         "streamed": streamed,
+        "small_t": small_t,
         "mfma_measured": mfma,
         "cpu_baseline": cpu,
     }

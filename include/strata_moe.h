@@ -90,7 +90,10 @@ extern "C" {
  *            and this is the sigmoid-gated sum).  The shared expert takes the
  *            routed experts' path: int8 input, gate/up, SwiGLU, int8 H, down.
  *            It is pair slot K of every token, so with it K <= 15 and
- *            E <= 1023.  Code that zero-initialises the struct has none. */
+ *            E <= 1023.  Code that zero-initialises the struct has none.
+ *   flags:   0 (the default), or a sum of the STRATA_MOE_FLAG_ values below;
+ *            they pick among kernels that compute the same layer (A/B
+ *            measurements).  Added last; zero-initialised code keeps 0. */
 typedef struct strata_moe_experts {
     int32_t n_expert; /* E */
     int32_t hidden;   /* H */
@@ -103,7 +106,19 @@ typedef struct strata_moe_experts {
     const float* router_bias;
     const void* router_prepared;
     const float* shared_gate;
+    int32_t flags;
 } strata_moe_experts;
+
+/* Chunks of at most two routed rows of an expert (most of them at decode-window
+ * sizes) go to a GEMV kernel on int8 dot products; this flag sends them to the
+ * small-chunk MFMA kernel instead. */
+#define STRATA_MOE_FLAG_NO_GEMV 1
+/* The per-slot q8_1 arm (the pages' MMQ form, Strata compare page,
+ * moe_fused.hpp header comment): for the GEMV's chunks the layer input is
+ * rounded to int8 again per routed slot, with each block's code sum, and the
+ * weight offset comes from those sums instead of the code lookup.  The same
+ * codes as the per-token rounding; only the data flow differs. */
+#define STRATA_MOE_FLAG_PER_SLOT_Q8 2
 
 /* Optional intermediate outputs of strata_moe_prefill_debug (each may be
  * NULL; all device pointers, sized for T tokens).  The library's own buffers

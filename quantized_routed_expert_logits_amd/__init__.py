@@ -27,6 +27,8 @@ EDATA = -5
 Q2_SYM = 1  # w = d * (q - 1.5)
 Q2_0 = 2    # w = d * (q - 1), the pages' Q2_0 packs
 FORMATS = {"q2_sym": Q2_SYM, "q2_0": Q2_0}
+FLAG_NO_GEMV = 1      # chunks of <= 2 rows to the small-chunk MFMA kernel instead of the GEMV
+FLAG_PER_SLOT_Q8 = 2  # the GEMV's input rounded per routed slot in the q8_1 form (A/B arm)
 
 
 class StrataMoeError(RuntimeError):
@@ -47,7 +49,7 @@ _i64, _i32 = ctypes.c_int64, ctypes.c_int32
 class ExpertsStruct(ctypes.Structure):
     _fields_ = [("n_expert", _i32), ("hidden", _i32), ("ffn", _i32), ("format", _i32),
                 ("gate_up", _P), ("gate_up_stride", _i64), ("down", _P), ("down_stride", _i64),
-                ("router_bias", _P), ("router_prepared", _P), ("shared_gate", _P)]
+                ("router_bias", _P), ("router_prepared", _P), ("shared_gate", _P), ("flags", _i32)]
 
 
 class DebugStruct(ctypes.Structure):
@@ -231,6 +233,7 @@ class Experts:
         self.router_bias = router_bias
         self.router_prepared = None
         self.shared_gate = None
+        self.flags = 0
         self._restruct()
 
     def _restruct(self):
@@ -238,7 +241,17 @@ class Experts:
                                     self.gate_up_stride, self.down.data_ptr(), self.down_stride,
                                     None if self.router_bias is None else self.router_bias.data_ptr(),
                                     None if self.router_prepared is None else self.router_prepared.data_ptr(),
-                                    None if self.shared_gate is None else self.shared_gate.data_ptr())
+                                    None if self.shared_gate is None else self.shared_gate.data_ptr(),
+                                    getattr(self, "flags", 0))
+
+    def with_flags(self, flags: int) -> "Experts":
+        """The same blobs with other kernel-choice flags (FLAG_NO_GEMV, FLAG_PER_SLOT_Q8)."""
+        import copy
+
+        other = copy.copy(self)
+        other.flags = int(flags)
+        other._restruct()
+        return other
 
     def with_router_bias(self, router_bias: torch.Tensor | None) -> "Experts":
         """The same blobs with another router bias (or none)."""
@@ -355,6 +368,7 @@ class HostExperts(Experts):
         self.router_bias = router_bias
         self.router_prepared = None
         self.shared_gate = None
+        self.flags = 0
         self._restruct()
 
     def pack(self, e0: int, codes_gu, scales_gu, codes_d, scales_d, stream=None):

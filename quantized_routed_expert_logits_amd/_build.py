@@ -23,7 +23,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libstrata_moe.so")
-SOURCES = ["strata_moe.hip", "k_quant.hip", "k_route.hip", "k_group.hip", "k_experts.hip", "k_pack.hip"]
+SOURCES = ["strata_moe.hip", "k_quant.hip", "k_route.hip", "k_group.hip", "k_experts.hip", "k_gemv.hip",
+           "k_pack.hip"]
 PROBE_LIB = os.path.join(HERE, "libstrata_probe.so")
 PROBE_SOURCES = ["probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -33,6 +33,7 @@ inline int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 inline int64_t max_tiles(int64_t n, int32_t E) { return n / kChunkRows + E; }
 
 constexpr int kSmallRows = 48;  // chunks of at most this many rows go to the small-chunk GEMM kernel
+constexpr int kGemvRows = 2;    // ... and of at most this many to the GEMV kernel (unless it is switched off)
 
 // The GEMMs' work lists, written on the GPU by the grouping (or from given
 // offsets): tiles[0, cap) the chunks of more than kSmallRows rows, tiles[cap,
@@ -66,6 +67,7 @@ struct ExpertRange {
     int32_t E = 0, e0 = 0, e1 = 0;
     int64_t ring0 = 0;
     int32_t nring = 0;
+    int32_t small_min_rows = 0;  // the small-chunk MFMA kernel skips chunks below this (the GEMV's)
 };
 inline int64_t chunk_list_cap(int64_t n, int32_t E) { return max_tiles(n, E); }
 
@@ -232,6 +234,34 @@ hipError_t launch_down(const uint8_t* blobs, int64_t stride, const ChunkLists& c
                        const int32_t* src, const float* prow, const _Float16* hb, const float* hst,
                        int64_t tiled_rows, const float* hs, const _Float16* huop, const float* hum, int32_t H,
                        int32_t I, float* dm, hipStream_t st, const ExpertRange& rng = ExpertRange());
+// The small-T GEMV over the small-chunk list's chunks of at most kGemvRows
+// rows (gate_up: activations act [act_rows][H] int8 by token through src, or
+// with asum by grouped row in the per-slot q8_1 form; writes hq / hs.  down:
+// act = H codes [n][I] by grouped row; writes the weighted rows y).
+struct GemvLaunch {
+    bool gate_up;
+    const uint8_t* blobs;
+    int64_t stride;
+    const int32_t* src;
+    const int8_t* act;
+    int64_t act_rows;
+    const float* ascale;
+    const int32_t* asum;
+    int32_t sym;
+    const float* prow;
+    int32_t H, I;
+    int8_t* hq;
+    float* hs;
+    float* y;
+};
+hipError_t launch_gemv(const GemvLaunch& l, const ChunkLists& cl, int64_t n, int32_t E, const ExpertRange& rng,
+                       hipStream_t st);
+// The per-slot q8_1 form of the layer input (the pages' MMQ path quantizes
+// each routed slot's row): row r of q8 / s / sum is x[src[r]] rounded as
+// launch_quantize rounds it (the same codes), with the block code sums.
+hipError_t launch_quantize_slots(const float* x, const int32_t* src, int64_t n, int32_t cols, int8_t* q8, float* s,
+                                 int32_t* sum, hipStream_t st);
+
 hipError_t launch_combine(const float* dm, const int32_t* slot, int64_t T, int32_t K, int32_t H, float* y,
                           hipStream_t st);
 

@@ -154,6 +154,7 @@ struct GemmArgs {
     int32_t e0, e1;
     int64_t ring0;         // nring > 0: expert e's blob is in slot (ring0 + e) % nring
     int32_t nring;
+    int32_t min_rows;      // small-chunk kernel: chunks with fewer rows are the GEMV kernel's
 };
 
 // Expert e's packed matrix: resident at blobs + e * stride, or in its slot of
@@ -869,6 +870,7 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_small_kernel(GemmArgs g) {
     const int chunk = lo + (local / ngroups) * 8 + (id & 7);
     if (chunk >= hi) return;
     const Tile tl = g.chunks[chunk];
+    if (tl.nrows < g.min_rows) return;  // uniform: the GEMV kernel takes this chunk
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int slab = kWaves * (local % ngroups) + wave;
     if (slab >= g.nslab) return;  // waves are independent: no workgroup barrier follows
@@ -951,7 +953,9 @@ void launch_gemms(GemmArgs g, GemmArgs gs_args, const ChunkLists& cl, int64_t n,
         a->e1 = rng.e1;
         a->ring0 = rng.ring0;
         a->nring = rng.nring;
+        a->min_rows = 0;
     }
+    gs_args.min_rows = rng.small_min_rows;
     g.first = rng.first;                                                   // big list: row 0 of the table
     gs_args.first = rng.first ? rng.first + ((int64_t)rng.E + 1) : nullptr;  // small list: row 1
     g.chunks = cl.tiles;
@@ -982,7 +986,7 @@ hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const ChunkLists
                           int32_t H, int32_t I, int8_t* hq, float* hs, hipStream_t st, const ExpertRange& rng) {
     const int64_t tiled_scale_bytes = tiled_rows / 16 * tiled_scale_stride(H / kBlock);
     const GemmArgs g{blobs, stride, nullptr, nullptr, 2 * I / kSlabRows, H, src, nullptr, xt, tiled_rows, xst,
-                     tiled_scale_bytes, xuop, xum, I, H, hq, hs, nullptr, nullptr, 0, 0, 0, 0};
+                     tiled_scale_bytes, xuop, xum, I, H, hq, hs, nullptr, nullptr, 0, 0, 0, 0, 0};
     GemmArgs gs = g;
     gs.act = xa;
     gs.act_rows = T;
@@ -998,7 +1002,7 @@ hipError_t launch_down(const uint8_t* blobs, int64_t stride, const ChunkLists& c
                        int32_t I, float* dm, hipStream_t st, const ExpertRange& rng) {
     const int64_t tiled_scale_bytes = tiled_rows / 16 * tiled_scale_stride(I / kBlock);
     const GemmArgs g{blobs, stride, nullptr, nullptr, H / kSlabRows, I, src, prow, hb, tiled_rows, hst,
-                     tiled_scale_bytes, huop, hum, I, H, nullptr, nullptr, dm, nullptr, 0, 0, 0, 0};
+                     tiled_scale_bytes, huop, hum, I, H, nullptr, nullptr, dm, nullptr, 0, 0, 0, 0, 0};
     GemmArgs gs = g;  // the small-chunk kernel reads the grouped rows' scales as rows
     gs.ascale = hs;
     gs.scale_bytes = n * (I / kBlock) * 4;

@@ -68,6 +68,47 @@ __global__ void __launch_bounds__(256) quantize_kernel(const float4* __restrict_
     if ((g & 7) == 0) s_out[g >> 3] = s;
 }
 
+// The per-slot q8_1 form: row r takes token src[r]'s input and rounds it as
+// quantize_kernel does (8 lanes per 32-value block, one float4 each, the same
+// arithmetic), so the codes and scales equal that token's; it also writes
+// each block's code sum.  One thread per float4 of the n x cols output.
+__global__ void __launch_bounds__(256) quantize_slots_kernel(const float* __restrict__ x,
+                                                             const int32_t* __restrict__ src, int64_t n,
+                                                             int32_t cols, int8_t* __restrict__ q8,
+                                                             float* __restrict__ s_out, int32_t* __restrict__ sum_out) {
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t n4 = n * (cols / 4);
+    const bool valid = g < n4;
+    const int64_t row = valid ? g / (cols / 4) : 0;
+    const int64_t c4 = valid ? g - row * (cols / 4) : 0;
+    const float4 v = valid ? reinterpret_cast<const float4*>(x + (int64_t)src[row] * cols)[c4]
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    a = fmaxf(a, __shfl_xor(a, 1));
+    a = fmaxf(a, __shfl_xor(a, 2));
+    a = fmaxf(a, __shfl_xor(a, 4));
+    const float s = a / 127.0f;
+    float q[4] = {0.f, 0.f, 0.f, 0.f};
+    if (s != 0.0f) {
+        q[0] = round_half_away(v.x / s);
+        q[1] = round_half_away(v.y / s);
+        q[2] = round_half_away(v.z / s);
+        q[3] = round_half_away(v.w / s);
+    }
+    int sum = (int)q[0] + (int)q[1] + (int)q[2] + (int)q[3];
+    sum += __shfl_xor(sum, 1);
+    sum += __shfl_xor(sum, 2);
+    sum += __shfl_xor(sum, 4);
+    if (!valid) return;
+    const uint32_t packed = ((uint32_t)(uint8_t)(int8_t)(int)q[0]) | ((uint32_t)(uint8_t)(int8_t)(int)q[1] << 8) |
+                            ((uint32_t)(uint8_t)(int8_t)(int)q[2] << 16) | ((uint32_t)(uint8_t)(int8_t)(int)q[3] << 24);
+    reinterpret_cast<uint32_t*>(q8)[g] = packed;
+    if ((g & 7) == 0) {
+        s_out[g >> 3] = s;
+        sum_out[g >> 3] = sum;
+    }
+}
+
 // fp16 hi/lo split of an fp32 value.  The asm barrier keeps v an fp32-rounded
 // value: otherwise the compiler fuses a producing multiply into the fp16
 // conversion (one rounding), and hi can differ by one ulp from the hi that lo
@@ -525,6 +566,15 @@ hipError_t launch_quantize_prescale(const float* x, int64_t rows, int32_t cols, 
     if (rows > 0)
         hipLaunchKernelGGL(quantize_prescale_kernel, dim3(grid_for(rows, 4)), dim3(256), 0, st, x, rows, cols, uoff,
                            q8, s, codes16, mult, xn, uop, umult, z);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_slots(const float* x, const int32_t* src, int64_t n, int32_t cols, int8_t* q8, float* s,
+                                 int32_t* sum, hipStream_t st) {
+    const int64_t n4 = n * (cols / 4);
+    if (n4 > 0)
+        hipLaunchKernelGGL(quantize_slots_kernel, dim3(grid_for(n4, 256)), dim3(256), 0, st, x, src, n, cols, q8, s,
+                           sum);
     return hipGetLastError();
 }
 

@@ -172,18 +172,21 @@ struct Buffers {
     _Float16* huop;
     float* hum;
     float* dm;
+    int8_t* sq;    // per-slot q8_1 arm: the layer input per grouped row, its scales and block code sums
+    float* ss;
+    int32_t* ssum;
     int64_t tiles_cap;
 };
 
 struct Offsets {
     size_t logits, wt, wb, wm, wnorm, pmax, amb, sel, ids, p, gids, gp, xq, xs, xa, xt, xst, xe, xn, xuop, xum, hist, base, offsets, tiles, ntiles, first, err, src, slot, prow, hq, hs,
-        trows, hb, hst, huop, hum, dm, total;
+        trows, hb, hst, huop, hum, dm, sq, ss, ssum, total;
     int64_t tiles_cap;
 };
 
 // K, E: the routing's; with a shared expert the grouping and the expert GEMMs
 // run over K + 1 pairs per token and E + 1 experts.
-Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I, bool shared) {
+Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I, bool shared, bool per_slot) {
     const int64_t nr = T * K;
     const int32_t Er = E;
     if (shared) ++K, ++E;
@@ -231,6 +234,9 @@ Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I, bool shared)
     o.huop = L.take<_Float16>(n * offset_operand_halves(I));
     o.hum = L.take<float>(n);
     o.dm = L.take<float>(n * H);
+    o.sq = per_slot ? L.take<int8_t>(n * H) : o.dm;
+    o.ss = per_slot ? L.take<float>(n * (H / kBlock)) : o.dm;
+    o.ssum = per_slot ? L.take<int32_t>(n * (H / kBlock)) : o.dm;
     o.total = L.off;
     return o;
 }
@@ -276,6 +282,9 @@ Buffers carve(char* ws, const Offsets& o) {
     b.huop = (_Float16*)(ws + o.huop);
     b.hum = (float*)(ws + o.hum);
     b.dm = (float*)(ws + o.dm);
+    b.sq = (int8_t*)(ws + o.sq);
+    b.ss = (float*)(ws + o.ss);
+    b.ssum = (int32_t*)(ws + o.ssum);
     b.tiles_cap = o.tiles_cap;
     return b;
 }
@@ -349,6 +358,8 @@ int check_experts(const strata_moe_experts* ex) {
         return fail(STRATA_MOE_EINVAL, "router_prepared must be 256-byte aligned");
     if (ex->shared_gate && !aligned(ex->shared_gate, 16))
         return fail(STRATA_MOE_EINVAL, "shared_gate must be 16-byte aligned");
+    if (ex->flags & ~(STRATA_MOE_FLAG_NO_GEMV | STRATA_MOE_FLAG_PER_SLOT_Q8))
+        return fail(STRATA_MOE_EINVAL, "unknown flags 0x%x", ex->flags);
     if (ex->shared_gate && ex->n_expert + 1 > kMaxExperts)
         return fail(STRATA_MOE_EINVAL, "n_expert %d leaves no room for the shared expert (at most %d)", ex->n_expert,
                     kMaxExperts - 1);
@@ -402,6 +413,43 @@ int check_no_overlap(const void* a, const void* b, int64_t bytes) {
     return 0;
 }
 
+bool use_gemv(const strata_moe_experts* ex) { return !(ex->flags & STRATA_MOE_FLAG_NO_GEMV); }
+bool per_slot_q8(const strata_moe_experts* ex) { return use_gemv(ex) && (ex->flags & STRATA_MOE_FLAG_PER_SLOT_Q8); }
+
+// The GEMV launches of the experts in rng (gate/up, or down), beside the MFMA
+// kernels of the same range: the small-chunk list's chunks of at most
+// kGemvRows rows.
+int launch_gemv_step(const strata_moe_experts* ex, bool gate_up, const uint8_t* blobs, int64_t stride,
+                     const Buffers& b, const ChunkLists& cl, int64_t T, int64_t n, int32_t Eg, const ExpertRange& rng,
+                     hipStream_t st) {
+    if (!use_gemv(ex)) return 0;
+    GemvLaunch l{};
+    l.gate_up = gate_up;
+    l.blobs = blobs;
+    l.stride = stride;
+    l.sym = ex->format == STRATA_MOE_Q2_SYM ? 1 : 0;
+    l.H = ex->hidden;
+    l.I = ex->ffn;
+    if (gate_up) {
+        const bool ps = per_slot_q8(ex);
+        l.src = b.src;
+        l.act = ps ? b.sq : b.xq;
+        l.act_rows = ps ? n : T;
+        l.ascale = ps ? b.ss : b.xs;
+        l.asum = ps ? b.ssum : nullptr;
+        l.hq = b.hq;
+        l.hs = b.hs;
+    } else {
+        l.act = b.hq;
+        l.act_rows = n;
+        l.ascale = b.hs;
+        l.prow = b.prow;
+        l.y = b.dm;
+    }
+    HIP_TRY(launch_gemv(l, cl, n, Eg, rng, st), "GEMV launch");
+    return 0;
+}
+
 // The expert phase with every expert streamed through the ring: batches of
 // at most a third of the ring in expert id order; each batch waits for its
 // last DMA, runs gate/up, the tiled H and down on its experts' rows, and
@@ -439,15 +487,19 @@ int run_streamed_experts(const strata_moe_experts* ex, strata_moe_ring* ring, co
         rng.e1 = e1;
         rng.ring0 = G0 % R;
         rng.nring = R;
+        rng.small_min_rows = use_gemv(ex) ? kGemvRows + 1 : 0;
         HIP_TRY(launch_gate_up((const uint8_t*)ring->slots, ring->slot_bytes, cl, n, Eg, b.src, b.xt, b.xst,
                                tiled_rows_cap(n, Eg), b.xa, b.xs, T, xuop, b.xum, H, I, b.hq, b.hs, st, rng),
                 "gate/up launch");
+        TRY(launch_gemv_step(ex, true, (const uint8_t*)ring->slots, ring->slot_bytes, b, cl, T, n, Eg, rng, st));
         HIP_TRY(launch_tile_h(b.hq, b.hs, cl, tiled_rows_cap(n, Eg) / 16, I, code_offset(ex), b.hb, b.hst, huop, b.hum,
                               st, rng),
                 "tile launch");
         HIP_TRY(launch_down((const uint8_t*)ring->slots + ring->gate_up_bytes, ring->slot_bytes, cl, n, Eg, b.src,
                             b.prow, b.hb, b.hst, tiled_rows_cap(n, Eg), b.hs, huop, b.hum, H, I, b.dm, st, rng),
                 "down launch");
+        TRY(launch_gemv_step(ex, false, (const uint8_t*)ring->slots + ring->gate_up_bytes, ring->slot_bytes, b, cl, T,
+                             n, Eg, rng, st));
         for (int64_t k = G0 + e0; k < G0 + e1; ++k) {
             const int s = (int)(k % R);
             HIP_TRY(hipEventRecord(ring->used[s], st), "hipEventRecord");
@@ -470,7 +522,7 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     const int32_t E = ex->n_expert, H = ex->hidden, I = ex->ffn;
     const int32_t Kg = K + shared, Eg = E + shared;  // the grouped pairs per token, the experts they go to
     const int64_t n = T * Kg;
-    const Offsets o = plan(T, K, E, H, I, shared);
+    const Offsets o = plan(T, K, E, H, I, shared, per_slot_q8(ex));
     char* ws = fixed_ws;
     if (fixed_ws) {
         if (o.total > fixed_bytes)
@@ -518,6 +570,8 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     // the big chunks' input codes and scales, gathered into the tiled layout
     HIP_TRY(launch_gather_tiles(b.xq, b.xs, b.src, cl, tiled_rows_cap(n, Eg) / 16, H, b.xt, b.xst, st),
             "gather launch");
+    // the per-slot q8_1 arm: every routed slot's input row rounded again, with block code sums
+    if (per_slot_q8(ex)) HIP_TRY(launch_quantize_slots(x, b.src, n, H, b.sq, b.ss, b.ssum, st), "quantize launch");
     tm.end(kGroup);
     if (ring) {
         tm.begin(kStreamed);
@@ -529,10 +583,13 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
         if (keep) *keep = b;
         return 0;
     }
+    ExpertRange all;  // every expert, resident
+    all.small_min_rows = use_gemv(ex) ? kGemvRows + 1 : 0;
     tm.begin(kGateUp);
     HIP_TRY(launch_gate_up((const uint8_t*)ex->gate_up, ex->gate_up_stride, cl, n, Eg, b.src, b.xt, b.xst,
-                           tiled_rows_cap(n, Eg), b.xa, b.xs, T, xuop, b.xum, H, I, b.hq, b.hs, st),
+                           tiled_rows_cap(n, Eg), b.xa, b.xs, T, xuop, b.xum, H, I, b.hq, b.hs, st, all),
             "gate/up launch");
+    TRY(launch_gemv_step(ex, true, (const uint8_t*)ex->gate_up, ex->gate_up_stride, b, cl, T, n, Eg, all, st));
     tm.end(kGateUp);
     tm.begin(kTileH);
     HIP_TRY(launch_tile_h(b.hq, b.hs, cl, tiled_rows_cap(n, Eg) / 16, I, code_offset(ex), b.hb, b.hst, huop, b.hum, st),
@@ -540,8 +597,9 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     tm.end(kTileH);
     tm.begin(kDown);
     HIP_TRY(launch_down((const uint8_t*)ex->down, ex->down_stride, cl, n, Eg, b.src, b.prow, b.hb, b.hst,
-                        tiled_rows_cap(n, Eg), b.hs, huop, b.hum, H, I, b.dm, st),
+                        tiled_rows_cap(n, Eg), b.hs, huop, b.hum, H, I, b.dm, st, all),
             "down launch");
+    TRY(launch_gemv_step(ex, false, (const uint8_t*)ex->down, ex->down_stride, b, cl, T, n, Eg, all, st));
     tm.end(kDown);
     tm.begin(kCombine);
     HIP_TRY(launch_combine(b.dm, b.slot, T, Kg, H, out, st), "combine launch");
@@ -625,7 +683,9 @@ int strata_moe_workspace_bytes(int64_t T, int32_t K, const strata_moe_experts* e
     g_err.clear();
     if (!bytes) return fail(STRATA_MOE_EINVAL, "bytes is NULL");
     TRY(check_layer(T, K, experts));
-    *bytes = plan(T, K, experts->n_expert, experts->hidden, experts->ffn, experts->shared_gate != nullptr).total;
+    *bytes = plan(T, K, experts->n_expert, experts->hidden, experts->ffn, experts->shared_gate != nullptr,
+                  per_slot_q8(experts))
+                 .total;
     return 0;
 }
 
@@ -943,9 +1003,29 @@ int strata_moe_gate_up(const int8_t* qx, const float* sx, const int32_t* offsets
     HIP_TRY(launch_prescale(qx, sx, T, H, code_offset(experts), xa, nullptr, xuop, xum, st), "prescale launch");
     HIP_TRY(launch_chunks_from_offsets(offsets, E, n, cl, st), "chunk list launch");  // and the tile table
     HIP_TRY(launch_gather_tiles(qx, sx, src, cl, tiled_rows_cap(n, E) / 16, H, xt, xst, st), "gather launch");
+    // the layer's kernel choice: chunks of at most kGemvRows rows to the GEMV
+    // (by token: the per-slot arm needs the fp32 input, which this entry has not)
+    ExpertRange all;
+    all.small_min_rows = use_gemv(experts) ? kGemvRows + 1 : 0;
     HIP_TRY(launch_gate_up((const uint8_t*)experts->gate_up, experts->gate_up_stride, cl, n, E, src, xt, xst,
-                           tiled_rows_cap(n, E), xa, sx, T, xuop, xum, H, I, qh, sh, st),
+                           tiled_rows_cap(n, E), xa, sx, T, xuop, xum, H, I, qh, sh, st, all),
             "gate/up launch");
+    if (use_gemv(experts)) {
+        GemvLaunch l{};
+        l.gate_up = true;
+        l.blobs = (const uint8_t*)experts->gate_up;
+        l.stride = experts->gate_up_stride;
+        l.src = src;
+        l.act = qx;
+        l.act_rows = T;
+        l.ascale = sx;
+        l.sym = experts->format == STRATA_MOE_Q2_SYM ? 1 : 0;
+        l.H = H;
+        l.I = I;
+        l.hq = qh;
+        l.hs = sh;
+        HIP_TRY(launch_gemv(l, cl, n, E, all, st), "GEMV launch");
+    }
     return 0;
 }
 
@@ -982,9 +1062,26 @@ int strata_moe_down(const int8_t* qh, const float* sh, const int32_t* offsets, c
     HIP_TRY(launch_tile_h(qh, sh, cl, tiled_rows_cap(n, E) / 16, I, code_offset(experts), hb, hst, huop, hum, st),
             "tile launch");
     HIP_TRY(launch_row_weights(slot, p, n, prow, st), "weights launch");
+    ExpertRange all;  // the layer's kernel choice, as strata_moe_gate_up
+    all.small_min_rows = use_gemv(experts) ? kGemvRows + 1 : 0;
     HIP_TRY(launch_down((const uint8_t*)experts->down, experts->down_stride, cl, n, E, src, prow, hb, hst,
-                        tiled_rows_cap(n, E), sh, huop, hum, H, I, dm, st),
+                        tiled_rows_cap(n, E), sh, huop, hum, H, I, dm, st, all),
             "down launch");
+    if (use_gemv(experts)) {
+        GemvLaunch l{};
+        l.gate_up = false;
+        l.blobs = (const uint8_t*)experts->down;
+        l.stride = experts->down_stride;
+        l.act = qh;
+        l.act_rows = n;
+        l.ascale = sh;
+        l.sym = experts->format == STRATA_MOE_Q2_SYM ? 1 : 0;
+        l.prow = prow;
+        l.H = H;
+        l.I = I;
+        l.y = dm;
+        HIP_TRY(launch_gemv(l, cl, n, E, all, st), "GEMV launch");
+    }
     HIP_TRY(launch_combine(dm, slot, T, K, H, out, st), "combine launch");
     return 0;
 }

@@ -99,9 +99,11 @@ def down_error_bound(s: S.LayerShape, ref: dict, seed: int = 0) -> np.ndarray:
     times the block's H scale with one fp32 FMA; the offset term of the
     symmetric map adds sum_b d u_b with u split into two fp16 halves (22
     bits); the routing-weight product and the K-term combine round in fp32 as
-    well.  Every rounding is relative to at most the sum of absolute terms,
-    and there are fewer than I / 32 + K + 8 of them on any output's path, so
-        |dy[t, j]| <= (I / 32 + K + 8) 2^-23 * sum_k p[t,k] sum_i |W_e[j,i]| |h[t,k,i]|.
+    well.  The GEMV kernel (chunks of one or two rows) takes the int32 block
+    sum times the block's H scale and then times d: two roundings per block.
+    Every rounding is relative to at most the sum of absolute terms, and
+    there are fewer than 2 I / 32 + K + 8 of them on any output's path, so
+        |dy[t, j]| <= (2 I / 32 + K + 8) 2^-23 * sum_k p[t,k] sum_i |W_e[j,i]| |h[t,k,i]|.
     The absolute weights come from the codes and fp16 scales directly."""
     n = s.T * s.K
     h_abs = np.abs(ref["qh"].astype(np.float64) * np.repeat(ref["sh"].astype(np.float64), 32, axis=1))
@@ -120,4 +122,4 @@ def down_error_bound(s: S.LayerShape, ref: dict, seed: int = 0) -> np.ndarray:
         contrib = h_abs[o0:o1] @ w_abs.T                      # [rows][H]
         pairs = inv[o0:o1]
         np.add.at(bound, src[o0:o1], contrib * p[pairs][:, None])
-    return (s.I / 32 + s.K + 8) * 2.0 ** -23 * bound
+    return (2 * s.I / 32 + s.K + 8) * 2.0 ** -23 * bound

@@ -110,8 +110,12 @@ def test_shared_expert_sizes_and_limits_on_the_host(qm):
     st = _experts_struct(qm)
     st.shared_gate = (1 << 12) + 4  # not 16-byte aligned
     assert lib.strata_moe_workspace_bytes(8, 10, ctypes.byref(st), ctypes.byref(b)) == qm.EINVAL
-    # the C struct's last field: ctypes offset after the router_prepared pointer
+    # the C struct's last fields: ctypes offsets after the router_prepared pointer
     assert qm.ExpertsStruct.shared_gate.offset == qm.ExpertsStruct.router_prepared.offset + ctypes.sizeof(ctypes.c_void_p)
+    assert qm.ExpertsStruct.flags.offset == qm.ExpertsStruct.shared_gate.offset + ctypes.sizeof(ctypes.c_void_p)
+    st = _experts_struct(qm)
+    st.flags = 4  # no such flag
+    assert lib.strata_moe_workspace_bytes(8, 10, ctypes.byref(st), ctypes.byref(b)) == qm.EINVAL
 
 
 def test_prefill_rejects_short_strides_and_null(qm):

@@ -216,7 +216,10 @@ STAGE_SHAPES = [S.shape("tiny"), S.custom(T=300, H=256, E=12, K=3, I=128), S.cus
                 # of the offset pass, the 8-deep record ring; about 24 rows per expert (the
                 # small-chunk kernel) and about 107 (the 4-wave kernel, 7 tiles)
                 S.custom(T=48, H=2560, E=4, K=2, I=1024), S.custom(T=160, H=2560, E=3, K=2, I=1024),
-                S.custom(T=96, H=2560, E=4, K=2, I=640, fmt="q2_0")]
+                S.custom(T=96, H=2560, E=4, K=2, I=640, fmt="q2_0"),
+                # one or two rows per expert: the GEMV kernel (decode-window sizes)
+                S.custom(T=20, H=256, E=64, K=4, I=128), S.custom(T=24, H=512, E=48, K=3, I=640, fmt="q2_0"),
+                S.custom(T=16, H=2560, E=32, K=2, I=1024)]
 
 
 @pytest.mark.parametrize("s", STAGE_SHAPES, ids=lambda s: s.name)
@@ -330,6 +333,37 @@ def test_layer_zero_tokens(qm):
     ex = gpu_experts(s)
     x = torch.empty((0, s.H), device="cuda")
     qm.strata_moe_prefill(x, _t(S.router_weight(s)), ex, s.K, torch.empty_like(x))
+
+
+# ------------------------------------------------------- small-T kernels
+SMALL_T = [S.shape("window_32"), S.custom(T=20, H=256, E=64, K=4, I=128),
+           S.custom(T=24, H=512, E=48, K=3, I=640, fmt="q2_0")]
+
+
+@pytest.mark.parametrize("s", SMALL_T, ids=lambda s: s.name)
+def test_small_t_kernel_choices(qm, s):
+    """The layer at decode-window sizes through its three kernel choices for
+    chunks of one or two rows: the int8 GEMV (default), the small-chunk MFMA
+    kernel (FLAG_NO_GEMV) and the GEMV on per-slot q8_1 inputs
+    (FLAG_PER_SLOT_Q8); each against the oracle."""
+    x, wr, ref = _stage_ref(s)
+    ex = gpu_experts(s)
+    sizes = np.diff(ref["offsets"])
+    assert np.count_nonzero((sizes > 0) & (sizes <= 2)) > 0  # the GEMV has chunks to take
+    outs = {}
+    for flags in (0, qm.FLAG_NO_GEMV, qm.FLAG_PER_SLOT_Q8):
+        out = torch.empty((s.T, s.H), dtype=torch.float32, device="cuda")
+        d = qm.strata_moe_prefill_debug(_t(x), _t(wr), ex.with_flags(flags), s.K, out)
+        g = {k: v.cpu().numpy() for k, v in d.items()}
+        for k in ("ids", "offsets", "src", "slot", "qx", "sx"):
+            assert np.array_equal(g[k], ref[k]), (flags, k)
+        rate = check_h_codes(g["qh"], g["sh"], ref["h"], ref["qh"], ref["sh"])
+        err = rel_err(g["out"], ref["y"])
+        print(f"{s.name} flags {flags}: max|dy|/max|y| = {err:.2e}, H-code mismatch rate {rate:.2e}")
+        assert rate < H_RATE and err <= Y_TOL
+        outs[flags] = g["out"]
+    # the three are not compared with each other bit for bit: their fp32 rounding orders differ, so an
+    # H code at a rounding near-tie may go either way (each is checked against the oracle above)
 
 
 # ------------------------------------------------- full-size layers, sampled

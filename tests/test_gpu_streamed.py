@@ -38,7 +38,8 @@ CASES = [(S.shape("tiny"), 3), (S.shape("tiny"), 7), (S.shape("tiny"), 64),
          (S.custom(T=300, H=256, E=12, K=3, I=128), 4),
          (S.custom(T=129, H=256, E=8, K=4, I=64, skewed=True), 1),
          (S.custom(T=160, H=512, E=6, K=2, I=640, fmt="q2_0", shared=True), 5),
-         (S.custom(T=200, H=256, E=10, K=3, I=128, shared=True), 2)]
+         (S.custom(T=200, H=256, E=10, K=3, I=128, shared=True), 2),
+         (S.custom(T=20, H=256, E=64, K=4, I=128), 5)]  # one or two rows per expert: the GEMV
 
 
 @pytest.mark.parametrize("s,R", CASES, ids=lambda v: v.name if hasattr(v, "name") else f"R{v}")
