@@ -23,8 +23,11 @@ Prints one JSON line on stdout (progress goes to stderr):
   streamed     the same layer with every expert streamed from pinned host
                memory through rings of 96, 384 and 512 device slots
   small_t      32- and 256-token chunks: ms per step, gate/up's weight GB/s,
-               and the same chunks through the other small-T kernel choices
+               for the layer's own kernel choice ("default") and each forced
+               one (MFMA only, the GEMV, the GEMV on per-slot q8_1 inputs)
   mfma_measured  the matrix unit's rates measured on this device
+  hbm_measured the read bandwidth a plain streaming kernel gets on this
+               device (the achievable ceiling beside the published 8 TB/s)
   cpu_baseline the CPU oracle (double precision) timed on this host on a
                bounded sample of the same workload
 
@@ -297,7 +300,9 @@ def main() -> int:
             ids3 = qm.strata_moe_prefill_debug(x3, wr, ex3, s3.K, out3)["ids"]
             hit3 = hit_experts(torch, ids3, s3.E)
             entry = {"T": s3.T, "hit_experts": hit3}
-            for label, flags in (("gemv", 0), ("mfma_only", qm.FLAG_NO_GEMV), ("per_slot_q8", qm.FLAG_PER_SLOT_Q8)):
+            arms = (("default", 0), ("mfma_only", qm.FLAG_NO_GEMV), ("gemv", qm.FLAG_GEMV_ALWAYS),
+                    ("gemv_per_slot_q8", qm.FLAG_GEMV_ALWAYS | qm.FLAG_PER_SLOT_Q8))
+            for label, flags in arms:
                 exf = ex3.with_flags(flags)
                 region_ms(qm, torch, s3, x3, wr, exf, out3, 20)  # warm
                 ms3, _ = region_ms(qm, torch, s3, x3, wr, exf, out3, 200)
@@ -346,7 +351,7 @@ def main() -> int:
                 f"({streamed['host_to_device_gbs'][str(R)]} GB/s of expert blobs over the host link)")
         del host
 
-    mfma = None
+    mfma = hbm = None
     if not args.no_probe:
         from quantized_routed_expert_logits_amd import probe
 
@@ -362,6 +367,10 @@ def main() -> int:
         mfma["scaled_blocks_unit"] = "T output-blocks/s (32-wide block products, each scaled into fp32)"
         log("MFMA rates (TOP/s): " + ", ".join(f"{k} {mfma[k]}" for k in probe.KINDS)
             + f"; scaled blocks fp16 {mfma['scaled_blocks_f16']} vs int8 {mfma['scaled_blocks_i8']} T/s")
+        reads = {str(g): round(probe.strata_probe_hbm_read(2 << 30, g)[0], 1) for g in (1024, 4096, 16384)}
+        hbm = {"read_gbs": max(reads.values()), "by_workgroups": reads, "bytes": 2 << 30,
+               "kernel": "16-byte loads, 4 in flight per thread, grid-stride, 256 threads per workgroup"}
+        log(f"HBM streaming read: {hbm['read_gbs']} GB/s (by workgroups {reads})")
 
     cpu = None
     if args.cpu_tokens > 0:
@@ -404,6 +413,7 @@ def main() -> int:
         "streamed": streamed,
         "small_t": small_t,
         "mfma_measured": mfma,
+        "hbm_measured": hbm,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

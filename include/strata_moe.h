@@ -109,16 +109,22 @@ typedef struct strata_moe_experts {
     int32_t flags;
 } strata_moe_experts;
 
-/* Chunks of at most two routed rows of an expert (most of them at decode-window
- * sizes) go to a GEMV kernel on int8 dot products; this flag sends them to the
- * small-chunk MFMA kernel instead. */
+/* Kernel choice for short chunks.  Where the call gives the experts at most
+ * two routed rows each on average (n = T * K pairs over E experts, n <= 2 E:
+ * decode-window sizes), chunks of at most 8 rows go to a GEMV kernel on int8
+ * dot products (two rows per pass over the weights) and the rest to the
+ * small-chunk MFMA kernel; otherwise every chunk takes an MFMA kernel.
+ * STRATA_MOE_FLAG_NO_GEMV keeps every chunk on the MFMA kernels;
+ * STRATA_MOE_FLAG_GEMV_ALWAYS gives the GEMV its chunks at any average. */
 #define STRATA_MOE_FLAG_NO_GEMV 1
 /* The per-slot q8_1 arm (the pages' MMQ form, Strata compare page,
  * moe_fused.hpp header comment): for the GEMV's chunks the layer input is
  * rounded to int8 again per routed slot, with each block's code sum, and the
- * weight offset comes from those sums instead of the code lookup.  The same
- * codes as the per-token rounding; only the data flow differs. */
+ * weight offset comes from those sums.  The same codes as the per-token
+ * rounding; only the data flow differs.  No effect where the GEMV does not
+ * run. */
 #define STRATA_MOE_FLAG_PER_SLOT_Q8 2
+#define STRATA_MOE_FLAG_GEMV_ALWAYS 4
 
 /* Optional intermediate outputs of strata_moe_prefill_debug (each may be
  * NULL; all device pointers, sized for T tokens).  The library's own buffers

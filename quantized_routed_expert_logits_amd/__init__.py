@@ -27,8 +27,9 @@ EDATA = -5
 Q2_SYM = 1  # w = d * (q - 1.5)
 Q2_0 = 2    # w = d * (q - 1), the pages' Q2_0 packs
 FORMATS = {"q2_sym": Q2_SYM, "q2_0": Q2_0}
-FLAG_NO_GEMV = 1      # chunks of <= 2 rows to the small-chunk MFMA kernel instead of the GEMV
-FLAG_PER_SLOT_Q8 = 2  # the GEMV's input rounded per routed slot in the q8_1 form (A/B arm)
+FLAG_NO_GEMV = 1        # every chunk to the MFMA kernels (no GEMV, also at decode-window sizes)
+FLAG_PER_SLOT_Q8 = 2    # the GEMV's input rounded per routed slot in the q8_1 form (A/B arm)
+FLAG_GEMV_ALWAYS = 4    # the GEMV takes chunks of <= 8 rows at any average rows per expert
 
 
 class StrataMoeError(RuntimeError):
@@ -245,7 +246,7 @@ class Experts:
                                     getattr(self, "flags", 0))
 
     def with_flags(self, flags: int) -> "Experts":
-        """The same blobs with other kernel-choice flags (FLAG_NO_GEMV, FLAG_PER_SLOT_Q8)."""
+        """The same blobs with other kernel-choice flags (FLAG_NO_GEMV, FLAG_PER_SLOT_Q8, FLAG_GEMV_ALWAYS)."""
         import copy
 
         other = copy.copy(self)

@@ -33,7 +33,8 @@ inline int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 inline int64_t max_tiles(int64_t n, int32_t E) { return n / kChunkRows + E; }
 
 constexpr int kSmallRows = 48;  // chunks of at most this many rows go to the small-chunk GEMM kernel
-constexpr int kGemvRows = 2;    // ... and of at most this many to the GEMV kernel (unless it is switched off)
+constexpr int kGemvRows = 2;     // rows per pass of the GEMV kernel
+constexpr int kGemvMaxRows = 8;  // the GEMV kernel takes chunks of at most this many rows, where it runs
 
 // The GEMMs' work lists, written on the GPU by the grouping (or from given
 // offsets): tiles[0, cap) the chunks of more than kSmallRows rows, tiles[cap,
@@ -68,6 +69,10 @@ struct ExpertRange {
     int64_t ring0 = 0;
     int32_t nring = 0;
     int32_t small_min_rows = 0;  // the small-chunk MFMA kernel skips chunks below this (the GEMV's)
+    // No expert has more rows than this in the call (the layer: T, since a
+    // token picks an expert at most once).  A kernel whose chunks cannot
+    // exist under it is not launched.
+    int64_t max_rows = INT64_MAX;
 };
 inline int64_t chunk_list_cap(int64_t n, int32_t E) { return max_tiles(n, E); }
 
@@ -234,8 +239,8 @@ hipError_t launch_down(const uint8_t* blobs, int64_t stride, const ChunkLists& c
                        const int32_t* src, const float* prow, const _Float16* hb, const float* hst,
                        int64_t tiled_rows, const float* hs, const _Float16* huop, const float* hum, int32_t H,
                        int32_t I, float* dm, hipStream_t st, const ExpertRange& rng = ExpertRange());
-// The small-T GEMV over the small-chunk list's chunks of at most kGemvRows
-// rows (gate_up: activations act [act_rows][H] int8 by token through src, or
+// The small-T GEMV over the small-chunk list's chunks of at most max_rows
+// (<= kGemvMaxRows) rows, kGemvRows per pass (gate_up: activations act [act_rows][H] int8 by token through src, or
 // with asum by grouped row in the per-slot q8_1 form; writes hq / hs.  down:
 // act = H codes [n][I] by grouped row; writes the weighted rows y).
 struct GemvLaunch {
@@ -253,6 +258,7 @@ struct GemvLaunch {
     int8_t* hq;
     float* hs;
     float* y;
+    int32_t max_rows;
 };
 hipError_t launch_gemv(const GemvLaunch& l, const ChunkLists& cl, int64_t n, int32_t E, const ExpertRange& rng,
                        hipStream_t st);

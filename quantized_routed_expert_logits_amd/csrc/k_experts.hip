@@ -947,7 +947,9 @@ void launch_gemms(GemmArgs g, GemmArgs gs_args, const ChunkLists& cl, int64_t n,
     const int64_t by_experts = n / kChunkRows + (ne < by_rows ? ne : by_rows);
     int64_t cap_big = cl.cap < by_rows ? cl.cap : by_rows;
     cap_big = cap_big < by_experts ? cap_big : by_experts;
-    const int64_t cap_small = cl.cap < ne ? cl.cap : ne;
+    if (rng.max_rows <= kSmallRows) cap_big = 0;  // every chunk is a small one
+    int64_t cap_small = cl.cap < ne ? cl.cap : ne;
+    if (rng.max_rows < rng.small_min_rows) cap_small = 0;  // every chunk is the GEMV's
     for (GemmArgs* a : {&g, &gs_args}) {
         a->e0 = rng.e0;
         a->e1 = rng.e1;

@@ -1,6 +1,6 @@
-// Grouped expert GEMV for chunks of at most kGemvRows routed rows: the
-// decode-window end of the prompt path, where most hit experts get one or two
-// rows.  There the MFMA kernels' fp16 unpack of the 2-bit codes dominates
+// Grouped expert GEMV for chunks of a few routed rows (at most max_rows, two
+// per pass over the weights): the decode-window end of the prompt path,
+// where most hit experts get one or two rows.  There the MFMA kernels' fp16 unpack of the 2-bit codes dominates
 // (25 vector instructions per 16 codes) while the matrix unit idles; this
 // kernel works on int8 codes with v_dot4_i32_i8 instead.
 //
@@ -11,20 +11,36 @@
 // into s32 (mma.sync m16n8k32); dot4 is the same product four at a time.
 //
 // Arithmetic.  A weight block is 32 codes q with an fp16 d; w = d (q - z),
-// z = 1.5 (symmetric map) or 1 (Q2_0).  The codes become int8 c = 2q - 3
-// (symmetric) or q - 1 (Q2_0) by a byte lookup (v_perm), so a block's sum
-// over an int8 activation block a is an exact int32 P = sum c a; the output
-// adds fp32(P) * s * d (times 1/2 for the symmetric map, once at the end).
-// The per-slot q8_1 arm (the pages' MMQ form, an A/B alternative) reads
-// activations quantized per routed slot with their block code sums A, keeps
-// the raw codes q and subtracts z * A instead: P = sum q a - z A (2 sum q a -
-// 3 A for the symmetric map).
+// z = 1.5 (symmetric map) or 1 (Q2_0).  Against an int8 activation block a
+// the block's sum is an exact int32: P = sum (q - 1) a - 0 for Q2_0, and for
+// the symmetric map 2 sum (q - 1.5) a = sum (2q) a - 3 sum a.  The kernel
+// takes the raw codes (doubled for the symmetric map) straight out of the
+// record with shifts and masks, and starts the int32 dot-product chain at the
+// offset term -z' sum a (z' = 1 or 3); the output adds fp32(P) * s * d, and
+// the symmetric map's factor 1/2 is applied once at the end.  The per-token
+// form computes each lane's part of sum a with two more dot4 against ones;
+// the per-slot q8_1 arm (the pages' MMQ form, an A/B alternative) reads
+// activations quantized per routed slot with their block code sums instead,
+// and only the first lane of a row adds the offset.
 //
-// Work split.  A workgroup takes one chunk and 4 consecutive 128-row slabs,
-// one per wave, as the small-chunk MFMA kernel does (same packed records:
-// lane l holds the 8 codes k = 8 (l / 16) .. + 7 of rows l % 16 + 16 f,
-// f = 0..7, in its 16 record bytes).  Each lane accumulates its k range; the
-// four lanes of a row add their sums at the end.
+// Work split.  A workgroup (4 waves) takes one chunk and 4 / S consecutive
+// 128-row slabs; the S waves of a slab split the reduction into S equal runs
+// of blocks (S = 4, 2 or 1, the largest that leaves runs of at least 16
+// blocks in whole ring turns).  The packed records are those of the MFMA
+// kernels: lane l holds the 8 codes k = 8 (l / 16) .. + 7 of rows l % 16 +
+// 16 f, f = 0..7, in its 16 record bytes.  Each lane accumulates its k range;
+// the four lanes of a row add their sums, then the slab's first wave adds the
+// other waves' sums from LDS in wave order (a fixed order: the result does
+// not depend on timing) and stores.  Short waves in numbers well above the
+// chip's resident capacity let the dispatcher balance the SIMDs; one wave
+// per slab over the whole reduction left some SIMDs with a wave more than
+// others and every wave a long serial chain of loads.
+// Blocks stream through a register ring kDepth deep: a block's codes, weight
+// scales, activation codes and activation scales (and code sums) are all
+// loaded kDepth blocks before their use, so no load is waited on in the
+// block it is used.  kDepth is 4 where it divides the run (always for
+// gate/up: the hidden size is a multiple of 128), else 2 (the FFN size is a
+// multiple of 64).
 #include "internal.h"
 
 namespace strata_moe {
@@ -33,8 +49,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3 for raw dword loads on gfx9 (gfx950)
-constexpr uint32_t kLookupSym = 0x0301FFFDu;  // bytes -3, -1, 1, 3: 2q - 3 for q = 0..3
-constexpr uint32_t kLookupQ20 = 0x020100FFu;  // bytes -1, 0, 1, 2: q - 1
+constexpr int kOnes = 0x01010101;         // four int8 ones: dot4 against them sums four codes
 
 struct GemvArgs {
     const uint8_t* blobs;  // packed matrices: expert e at blobs + e * stride, or in its ring slot
@@ -46,12 +61,13 @@ struct GemvArgs {
     const int32_t* first;    // optional expert range [e0, e1) through the grouping's first table
     int32_t e0, e1;
     int32_t nslab, Kd;
+    int32_t nsplit;       // S: waves per slab, each on nblk / S consecutive blocks
+    int32_t max_rows;     // the chunks of at most this many rows are this kernel's
     const int32_t* src;   // gate/up without the per-slot arm: token of each grouped row
     const int8_t* act;    // int8 activation rows [act_rows][Kd]
     int64_t act_rows;
     const float* ascale;  // their block scales [act_rows][Kd / 32]
     const int32_t* asum;  // per-slot arm: their block code sums [act_rows][Kd / 32], else null
-    int32_t sym;          // 1: w = d (q - 1.5), 0: w = d (q - 1)
     const float* prow;    // down: routing weight of each grouped row
     int32_t I, H;
     int8_t* hq;  // gate/up: H codes [n][I]
@@ -69,16 +85,20 @@ __device__ __forceinline__ float round_half_away(float t) {
     return copysignf(fminf(r, 127.0f), t);
 }
 
-// One record dword -> the int8 codes of its two rows: lo[0] / hi[0] = row A
-// (fragment 2p) k 0..3 / 4..7, lo[1] / hi[1] = row B.  Bits 2j, 2j+1 of each
-// byte hold code k = 2j (bytes 0, 1: rows A, B) or k = 2j + 1 (bytes 2, 3).
-template <bool kLookup>
-__device__ __forceinline__ void row_codes(uint32_t w, uint32_t lut, uint32_t (&lo)[2], uint32_t (&hi)[2]) {
+// One record dword -> the codes of its two rows as int8 (q, or 2q for the
+// symmetric map): lo[0] / hi[0] = row A (fragment 2p) k 0..3 / 4..7, lo[1] /
+// hi[1] = row B.  Bits 2j, 2j+1 of each byte hold code k = 2j (bytes 0, 1:
+// rows A, B) or k = 2j + 1 (bytes 2, 3).
+template <bool kSym>
+__device__ __forceinline__ void row_codes(uint32_t w, uint32_t (&lo)[2], uint32_t (&hi)[2]) {
     uint32_t x[4];
+    if constexpr (kSym) {
+        x[0] = (w << 1) & 0x06060606u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        x[j] = (w >> (2 * j)) & 0x03030303u;
-        if constexpr (kLookup) x[j] = __builtin_amdgcn_perm(lut, lut, x[j]);  // byte q -> its int8 code
+        for (int j = 1; j < 4; ++j) x[j] = (w >> (2 * j - 1)) & 0x06060606u;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = (w >> (2 * j)) & 0x03030303u;
     }
     lo[0] = __builtin_amdgcn_perm(x[1], x[0], 0x06040200u);  // A: k0 k1 k2 k3
     hi[0] = __builtin_amdgcn_perm(x[3], x[2], 0x06040200u);  // A: k4 k5 k6 k7
@@ -86,88 +106,120 @@ __device__ __forceinline__ void row_codes(uint32_t w, uint32_t lut, uint32_t (&l
     hi[1] = __builtin_amdgcn_perm(x[3], x[2], 0x07050301u);
 }
 
-// One wave: chunk tl (R rows) against slab `slab`.
-template <bool kGateUp, bool kQ81, int R>
-__device__ __forceinline__ void gemv_wave(const GemvArgs& g, const Tile& tl, int slab, int lane) {
+// The loads of one block of the ring.
+template <int R>
+struct RingSlot {
+    uint32_t c[4];     // the lane's 16 code bytes
+    uint32_t sw[4];    // its row's 8 fp16 weight scales
+    uint32_t a[R][2];  // per activation row its 8 codes of the lane's k range
+    float s[R];        // per activation row the block scale
+    int32_t A[R];      // per-slot arm: per activation row the block code sum
+};
+
+// Lane sums of the slab's other waves: [wave][row r16][fragment][row i].
+constexpr int kRedFloats = 16 * 8 * kGemvRows;
+
+// One wave: chunk tl (R rows) against slab `slab`, blocks [b0, b0 + nb) of
+// the reduction.  `part` is the wave's place among the slab's waves (0: the
+// one that stores); red: the workgroup's LDS sums; live: the slab exists (a
+// wave without one still meets the barrier).
+template <bool kGateUp, bool kQ81, bool kSym, int R, int kDepth>
+__device__ __forceinline__ void gemv_wave(const GemvArgs& g, const Tile& tl, int slab, int part, int lane,
+                                          bool live, float (*red)[kRedFloats]) {
     const int r16 = lane & 15, kg = lane >> 4;
     const int nblk = g.Kd / kBlock;
-    int64_t arow[R];
+    const int nb = nblk / g.nsplit, b0 = part * nb;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int arow[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
         const int row = tl.row0 + i;
-        arow[i] = (kGateUp && !kQ81) ? (int64_t)g.src[row] : (int64_t)row;
+        arow[i] = (kGateUp && !kQ81) ? g.src[row] : row;
     }
-    const uint8_t* rec = gemv_blob(g, tl.e) + (int64_t)slab * nblk * kRecordBytes;
-    const __amdgpu_buffer_rsrc_t rrec = __builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, nblk * kRecordBytes,
+    const uint8_t* rec = gemv_blob(g, tl.e) + ((int64_t)(live ? slab : 0) * nblk + b0) * kRecordBytes;
+    const __amdgpu_buffer_rsrc_t rrec = __builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, nb * kRecordBytes,
                                                                           kBufferWord3);
     const __amdgpu_buffer_rsrc_t ract = __builtin_amdgcn_make_buffer_rsrc(
         (void*)g.act, (short)0, (int)(g.act_rows * g.Kd), kBufferWord3);
-    const uint32_t lut = g.sym ? kLookupSym : kLookupQ20;
+    const __amdgpu_buffer_rsrc_t rscl = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)g.ascale, (short)0, (int)(g.act_rows * nblk * 4), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rsum = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)g.asum, (short)0, kQ81 ? (int)(g.act_rows * nblk * 4) : 0, kBufferWord3);
+    constexpr int zp = kSym ? 3 : 1;  // the offset's multiple of the code sum
     float acc[8][R];
 #pragma unroll
     for (int f = 0; f < 8; ++f)
 #pragma unroll
         for (int i = 0; i < R; ++i) acc[f][i] = 0.f;
 
-    // loads of block b: the lane's 16 code bytes and its row's 16 scale
-    // bytes, and per activation row its 8 codes of the lane's k range
-    auto load = [&](int b, uint32_t (&c)[4], uint32_t (&sw)[4], uint32_t (&a)[R][2]) {
-        b = b < nblk ? b : nblk - 1;
+    // Block b of the run (a block beyond the run re-reads its last one, never
+    // used).  The activation scale and sum addresses are the same on every
+    // lane.
+    auto load = [&](int b, RingSlot<R>& r) {
+        b = b < nb ? b : nb - 1;
+        const int ab = b0 + b;  // the block in the activation row
         const auto cv = __builtin_amdgcn_raw_buffer_load_b128(rrec, lane * 16, b * kRecordBytes, 0);
         const auto dv = __builtin_amdgcn_raw_buffer_load_b128(rrec, kRecordCodeBytes + r16 * 16, b * kRecordBytes, 0);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) c[p] = cv[p], sw[p] = dv[p];
+        for (int p = 0; p < 4; ++p) r.c[p] = cv[p], r.sw[p] = dv[p];
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-            const auto av = __builtin_amdgcn_raw_buffer_load_b64(ract, (int)(arow[i] * g.Kd) + 8 * kg, b * kBlock, 0);
-            a[i][0] = av[0];
-            a[i][1] = av[1];
+            const auto av = __builtin_amdgcn_raw_buffer_load_b64(ract, arow[i] * g.Kd + 8 * kg, ab * kBlock, 0);
+            r.a[i][0] = av[0];
+            r.a[i][1] = av[1];
+            r.s[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rscl, 0, (arow[i] * nblk + ab) * 4, 0));
+            if constexpr (kQ81)
+                r.A[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rsum, 0, (arow[i] * nblk + ab) * 4, 0);
         }
     };
-    uint32_t c[2][4], sw[2][4], a[2][R][2];
-    load(0, c[0], sw[0], a[0]);
-    for (int b = 0; b < nblk; b += 2) {
+    RingSlot<R> ring[kDepth];
+    // issued slot by slot: the loop waits for a slot's loads by their count
+    // (vmcnt), which only works if no later slot's loads went out before them
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int blk = b + u;
-            if (blk >= nblk) break;  // uniform
-            load(blk + 1, c[u ^ 1], sw[u ^ 1], a[u ^ 1]);
-            float s[R];
-            int32_t zs[R];  // per-slot arm: the offset term z * A (2z for the symmetric map), on lanes kg == 0
+    for (int j = 0; j < kDepth; ++j) {
+        load(j, ring[j]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int b = 0; live && b < nb; b += kDepth) {
+#pragma unroll
+        for (int j = 0; j < kDepth; ++j) {
+            const int blk = b + j;
+            RingSlot<R>& r = ring[j];
+            int32_t z[R];  // the chain's start: minus the offset term of this lane's part
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                s[i] = g.ascale[arow[i] * nblk + blk];
-                zs[i] = 0;
                 if constexpr (kQ81) {
-                    const int32_t A = g.asum[arow[i] * nblk + blk];
-                    zs[i] = kg == 0 ? (g.sym ? 3 * A : A) : 0;
+                    z[i] = kg == 0 ? -zp * r.A[i] : 0;
+                } else {
+                    int32_t sa = __builtin_amdgcn_sdot4((int)r.a[i][0], kOnes, 0, false);
+                    sa = __builtin_amdgcn_sdot4((int)r.a[i][1], kOnes, sa, false);
+                    z[i] = __mul24(sa, -zp);  // |sa| <= 8 * 127: a full-rate 24-bit multiply
                 }
             }
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 uint32_t lo[2], hi[2];
-                row_codes<!kQ81>(c[u][p], lut, lo, hi);
-                const float d0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(sw[u][p] & 0xffffu));
-                const float d1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(sw[u][p] >> 16));
+                row_codes<kSym>(r.c[p], lo, hi);
+                const float d0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(r.sw[p] & 0xffffu));
+                const float d1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(r.sw[p] >> 16));
 #pragma unroll
                 for (int i = 0; i < R; ++i) {
-                    int32_t pa = __builtin_amdgcn_sdot4((int)lo[0], (int)a[u][i][0], 0, false);
-                    pa = __builtin_amdgcn_sdot4((int)hi[0], (int)a[u][i][1], pa, false);
-                    int32_t pb = __builtin_amdgcn_sdot4((int)lo[1], (int)a[u][i][0], 0, false);
-                    pb = __builtin_amdgcn_sdot4((int)hi[1], (int)a[u][i][1], pb, false);
-                    if constexpr (kQ81) {
-                        if (g.sym) pa = 2 * pa, pb = 2 * pb;
-                        pa -= zs[i];
-                        pb -= zs[i];
-                    }
-                    acc[2 * p][i] = fmaf((float)pa * s[i], d0, acc[2 * p][i]);
-                    acc[2 * p + 1][i] = fmaf((float)pb * s[i], d1, acc[2 * p + 1][i]);
+                    int32_t pa = __builtin_amdgcn_sdot4((int)lo[0], (int)r.a[i][0], z[i], false);
+                    pa = __builtin_amdgcn_sdot4((int)hi[0], (int)r.a[i][1], pa, false);
+                    int32_t pb = __builtin_amdgcn_sdot4((int)lo[1], (int)r.a[i][0], z[i], false);
+                    pb = __builtin_amdgcn_sdot4((int)hi[1], (int)r.a[i][1], pb, false);
+                    acc[2 * p][i] = fmaf((float)pa * r.s[i], d0, acc[2 * p][i]);
+                    acc[2 * p + 1][i] = fmaf((float)pb * r.s[i], d1, acc[2 * p + 1][i]);
                 }
             }
+            // the slot's registers are free again: its next block's loads
+            // go there (kept after the products, so the ring holds kDepth
+            // blocks, not kDepth + 1)
+            __builtin_amdgcn_sched_barrier(0);
+            load(blk + kDepth, r);
         }
     }
     // the four lanes of a row (k ranges kg = 0..3) add their sums
-    const float half = g.sym ? 0.5f : 1.0f;  // the symmetric map's codes are 2 (q - 1.5)
 #pragma unroll
     for (int f = 0; f < 8; ++f)
 #pragma unroll
@@ -175,9 +227,29 @@ __device__ __forceinline__ void gemv_wave(const GemvArgs& g, const Tile& tl, int
             float v = acc[f][i];
             v += __shfl_xor(v, 16);
             v += __shfl_xor(v, 32);
-            acc[f][i] = v * half;
+            acc[f][i] = v;
         }
-
+    if (g.nsplit > 1) {  // uniform over the workgroup
+        if (part != 0 && kg == 0)
+#pragma unroll
+            for (int f = 0; f < 8; ++f)
+#pragma unroll
+                for (int i = 0; i < R; ++i) red[wave][(r16 * 8 + f) * kGemvRows + i] = acc[f][i];
+        __syncthreads();
+        if (part == 0)
+            for (int q = 1; q < g.nsplit; ++q)
+#pragma unroll
+                for (int f = 0; f < 8; ++f)
+#pragma unroll
+                    for (int i = 0; i < R; ++i) acc[f][i] += red[wave + q][(r16 * 8 + f) * kGemvRows + i];
+        __syncthreads();  // red is free for the chunk's next pass
+    }
+    if (!live || part != 0) return;
+    constexpr float half = kSym ? 0.5f : 1.0f;  // the symmetric map's codes are 2 (q - 1.5)
+#pragma unroll
+    for (int f = 0; f < 8; ++f)
+#pragma unroll
+        for (int i = 0; i < R; ++i) acc[f][i] *= half;
     if constexpr (kGateUp) {
         // fragments f < 4: gate rows j = 64 slab + 16 f + r16; f + 4: the up rows of the same j.
         // H block hb (32 values) holds fragments 2 hb, 2 hb + 1 of the 16 lanes r16.
@@ -220,28 +292,53 @@ __device__ __forceinline__ void gemv_wave(const GemvArgs& g, const Tile& tl, int
     }
 }
 
-// One workgroup per (chunk, group of 4 slabs) of the small-chunk list, all
-// groups of a chunk on one XCD; chunks of more than kGemvRows rows are the
-// small-chunk MFMA kernel's and are skipped here.
-template <bool kGateUp, bool kQ81>
-__global__ void __launch_bounds__(64 * kWaves) gemv_kernel(GemvArgs g) {
-    const int ngroups = (g.nslab + kWaves - 1) / kWaves;
+// One workgroup per (chunk, group of 4 / S slabs) of the small-chunk list,
+// all groups of a chunk on one XCD.  A chunk of r rows takes ceil(r / 2)
+// passes (two rows, the last one or two); chunks of more than max_rows rows
+// are the small-chunk MFMA kernel's and are skipped here.
+template <bool kGateUp, bool kQ81, bool kSym>
+__global__ void __launch_bounds__(64 * kWaves, 4) gemv_kernel(GemvArgs g) {
+    __shared__ float red[kWaves][kRedFloats];
+    const int per = kWaves / g.nsplit;  // slabs per workgroup
+    const int ngroups = (g.nslab + per - 1) / per;
     const int id = blockIdx.x;
     const int local = id >> 3;
     const int lo = g.first ? g.first[g.e0] : 0;
     const int hi = g.first ? g.first[g.e1] : *g.nchunks;
     const int chunk = lo + (local / ngroups) * 8 + (id & 7);
-    if (chunk >= hi) return;
+    if (chunk >= hi) return;  // uniform over the workgroup, before any barrier
     const Tile tl = g.chunks[chunk];
-    if (tl.nrows > kGemvRows || tl.nrows < 1) return;  // uniform over the workgroup
+    if (tl.nrows > g.max_rows || tl.nrows < 1) return;  // uniform
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int slab = kWaves * (local % ngroups) + wave;
-    if (slab >= g.nslab) return;  // waves are independent: no barrier follows
+    const int slab = per * (local % ngroups) + wave / g.nsplit;
+    const int part = wave % g.nsplit;
+    const bool live = slab < g.nslab;
     const int lane = threadIdx.x & 63;
-    if (tl.nrows == 1)
-        gemv_wave<kGateUp, kQ81, 1>(g, tl, slab, lane);
-    else
-        gemv_wave<kGateUp, kQ81, 2>(g, tl, slab, lane);
+    const bool deep = (g.Kd / kBlock / g.nsplit) % 4 == 0;
+    for (int r0 = 0; r0 < tl.nrows; r0 += kGemvRows) {  // every wave runs every pass (barriers inside)
+        Tile t = tl;
+        t.row0 = tl.row0 + r0;
+        t.nrows = tl.nrows - r0 < kGemvRows ? tl.nrows - r0 : kGemvRows;
+        if (t.nrows == 1) {
+            if (deep)
+                gemv_wave<kGateUp, kQ81, kSym, 1, 4>(g, t, slab, part, lane, live, red);
+            else
+                gemv_wave<kGateUp, kQ81, kSym, 1, 2>(g, t, slab, part, lane, live, red);
+        } else {
+            if (deep)
+                gemv_wave<kGateUp, kQ81, kSym, 2, 4>(g, t, slab, part, lane, live, red);
+            else
+                gemv_wave<kGateUp, kQ81, kSym, 2, 2>(g, t, slab, part, lane, live, red);
+        }
+    }
+}
+
+// S for a reduction of nblk blocks (nblk even): runs of at least 16 blocks
+// in whole turns of the ring.
+int gemv_split(int nblk) {
+    for (int S = 4; S > 1; S /= 2)
+        if (nblk / S >= 16 && nblk % (2 * S) == 0) return S;
+    return 1;
 }
 
 }  // namespace
@@ -250,7 +347,7 @@ hipError_t launch_gemv(const GemvLaunch& l, const ChunkLists& cl, int64_t n, int
                        hipStream_t st) {
     const int32_t ne = rng.first ? rng.e1 - rng.e0 : E;
     const int64_t cap = cl.cap < ne ? cl.cap : ne;  // at most one small chunk per expert
-    if (cap <= 0 || n <= 0) return hipGetLastError();
+    if (cap <= 0 || n <= 0 || l.max_rows < 1) return hipGetLastError();
     GemvArgs g{};
     g.blobs = l.blobs;
     g.stride = l.stride;
@@ -263,28 +360,30 @@ hipError_t launch_gemv(const GemvLaunch& l, const ChunkLists& cl, int64_t n, int
     g.e1 = rng.e1;
     g.nslab = l.gate_up ? 2 * l.I / kSlabRows : l.H / kSlabRows;
     g.Kd = l.gate_up ? l.H : l.I;
+    g.nsplit = gemv_split(g.Kd / kBlock);
+    g.max_rows = l.max_rows;
     g.src = l.src;
     g.act = l.act;
     g.act_rows = l.act_rows;
     g.ascale = l.ascale;
     g.asum = l.asum;
-    g.sym = l.sym;
     g.prow = l.prow;
     g.I = l.I;
     g.H = l.H;
     g.hq = l.hq;
     g.hs = l.hs;
     g.y = l.y;
-    const int ngroups = (g.nslab + kWaves - 1) / kWaves;
+    const int per = kWaves / g.nsplit;
+    const int ngroups = (g.nslab + per - 1) / per;
     const dim3 grid((unsigned)(8 * ((cap + 7) / 8) * ngroups));
-    if (l.gate_up) {
-        if (l.asum)
-            hipLaunchKernelGGL((gemv_kernel<true, true>), grid, dim3(64 * kWaves), 0, st, g);
-        else
-            hipLaunchKernelGGL((gemv_kernel<true, false>), grid, dim3(64 * kWaves), 0, st, g);
-    } else {
-        hipLaunchKernelGGL((gemv_kernel<false, false>), grid, dim3(64 * kWaves), 0, st, g);
-    }
+    void (*kernel)(GemvArgs);
+    if (l.gate_up && l.asum)
+        kernel = l.sym ? gemv_kernel<true, true, true> : gemv_kernel<true, true, false>;
+    else if (l.gate_up)
+        kernel = l.sym ? gemv_kernel<true, false, true> : gemv_kernel<true, false, false>;
+    else
+        kernel = l.sym ? gemv_kernel<false, false, true> : gemv_kernel<false, false, false>;
+    hipLaunchKernelGGL(kernel, grid, dim3(64 * kWaves), 0, st, g);
     return hipGetLastError();
 }
 

@@ -12,6 +12,9 @@
 //     applied per output (convert, multiply, FMA).  Output-blocks per second.
 //   strata_probe_mfma_f16: one v_mfma_f32_16x16x32_f16 on given operands
 //     (row-major A [16][32], B [32][16], C [16][16]), to check how it rounds.
+//   strata_probe_hbm_read: the read bandwidth a plain streaming kernel gets
+//     from HBM (16-byte loads, four in flight per thread, a grid-stride
+//     loop), the measured ceiling beside the published 8 TB/s.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -173,6 +176,22 @@ __global__ void mfma_f16_kernel(const float* __restrict__ A, const float* __rest
     for (int v = 0; v < 4; ++v) D[(4 * g + v) * 16 + r] = c[v];
 }
 
+// Streaming read of n16 16-byte words: four independent loads per thread and
+// turn, their XOR kept; a store only on a value the fill never makes, so
+// the kernel writes nothing and the loads cannot be dropped.
+__global__ void __launch_bounds__(256) hbm_read_kernel(const int4_t* __restrict__ src, int64_t n16,
+                                                       int4_t* __restrict__ out) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int4_t acc = {0, 0, 0, 0};
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const int4_t a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        acc ^= a ^ b ^ c ^ d;
+    }
+    for (; i < n16; i += stride) acc ^= src[i];
+    if (acc[0] == 0x5eed1e55 && acc[1] == 0x5eed1e55) out[blockIdx.x] = acc;
+}
+
 int run_timed(void (*launch)(hipStream_t), double* ms) {
     hipEvent_t e0, e1;
     if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return -4;
@@ -192,6 +211,13 @@ int run_timed(void (*launch)(hipStream_t), double* ms) {
 
 float* g_out = nullptr;
 int32_t g_iters = 0, g_groups = 0;
+const int4_t* g_src = nullptr;
+int64_t g_n16 = 0;
+
+void launch_read(hipStream_t st) {
+    hipLaunchKernelGGL(hbm_read_kernel, dim3(g_groups), dim3(256), 0, st, g_src, g_n16,
+                       reinterpret_cast<int4_t*>(g_out));
+}
 
 template <int kKind>
 void launch_rate(hipStream_t st) {
@@ -259,6 +285,32 @@ int strata_probe_mfma_f16(const float* A, const float* B, const float* C, float*
         if (hipMemcpy(D, d + 1280, 256 * 4, hipMemcpyDeviceToHost) != hipSuccess) rc = -4;
     }
     (void)hipFree(d);
+    return rc;
+}
+
+// Reads `bytes` (a multiple of 16, at least 1 MiB) of device memory filled
+// with ones, `groups` workgroups of 256 threads; the first pass is untimed.
+// With bytes well above the 256 MB Infinity Cache the timed pass streams
+// from HBM.  Writes GB/s (1e9 bytes) and the kernel time.  Returns 0, -1
+// (arguments), -4 (a HIP call failed).
+int strata_probe_hbm_read(int64_t bytes, int32_t groups, double* gbs, double* ms) {
+    if (bytes < (1 << 20) || bytes % 16 || groups < 1 || !gbs || !ms) return -1;
+    void* buf = nullptr;
+    if (hipMalloc(&buf, (size_t)bytes) != hipSuccess) return -4;
+    if (hipMalloc(&g_out, sizeof(int4_t) * groups) != hipSuccess) {
+        (void)hipFree(buf);
+        return -4;
+    }
+    int rc = hipMemset(buf, 1, (size_t)bytes) == hipSuccess ? 0 : -4;
+    g_src = static_cast<const int4_t*>(buf);
+    g_n16 = bytes / 16;
+    g_groups = groups;
+    if (rc == 0) rc = run_timed(launch_read, ms);
+    (void)hipFree(buf);
+    (void)hipFree(g_out);
+    g_out = nullptr;
+    g_src = nullptr;
+    *gbs = rc == 0 && *ms > 0 ? (double)bytes / (*ms * 1e-3) / 1e9 : 0.0;
     return rc;
 }
 

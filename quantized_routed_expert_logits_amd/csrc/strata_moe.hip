@@ -358,7 +358,7 @@ int check_experts(const strata_moe_experts* ex) {
         return fail(STRATA_MOE_EINVAL, "router_prepared must be 256-byte aligned");
     if (ex->shared_gate && !aligned(ex->shared_gate, 16))
         return fail(STRATA_MOE_EINVAL, "shared_gate must be 16-byte aligned");
-    if (ex->flags & ~(STRATA_MOE_FLAG_NO_GEMV | STRATA_MOE_FLAG_PER_SLOT_Q8))
+    if (ex->flags & ~(STRATA_MOE_FLAG_NO_GEMV | STRATA_MOE_FLAG_PER_SLOT_Q8 | STRATA_MOE_FLAG_GEMV_ALWAYS))
         return fail(STRATA_MOE_EINVAL, "unknown flags 0x%x", ex->flags);
     if (ex->shared_gate && ex->n_expert + 1 > kMaxExperts)
         return fail(STRATA_MOE_EINVAL, "n_expert %d leaves no room for the shared expert (at most %d)", ex->n_expert,
@@ -413,17 +413,36 @@ int check_no_overlap(const void* a, const void* b, int64_t bytes) {
     return 0;
 }
 
-bool use_gemv(const strata_moe_experts* ex) { return !(ex->flags & STRATA_MOE_FLAG_NO_GEMV); }
-bool per_slot_q8(const strata_moe_experts* ex) { return use_gemv(ex) && (ex->flags & STRATA_MOE_FLAG_PER_SLOT_Q8); }
+// The GEMV takes the small-chunk list's chunks of at most this many rows (0:
+// none).  It runs where the experts get at most two rows each on average
+// (n <= 2 E): there nearly every chunk is that short, and the MFMA kernel
+// left with the few longer ones costs one slab's pass in time however few
+// they are.  At larger averages the MFMA kernels take everything: there the
+// GEMV's passes (two rows each) cost more than the MFMA's one.
+int32_t gemv_rows(const strata_moe_experts* ex, int64_t n, int32_t Eg) {
+    if (ex->flags & STRATA_MOE_FLAG_NO_GEMV) return 0;
+    if ((ex->flags & STRATA_MOE_FLAG_GEMV_ALWAYS) || n <= 2 * (int64_t)Eg) return kGemvMaxRows;
+    return 0;
+}
+bool per_slot_q8(const strata_moe_experts* ex, int64_t n, int32_t Eg) {
+    return gemv_rows(ex, n, Eg) > 0 && (ex->flags & STRATA_MOE_FLAG_PER_SLOT_Q8);
+}
+// The small-chunk MFMA kernel's lower row bound beside the GEMV.
+int32_t small_min_rows(const strata_moe_experts* ex, int64_t n, int32_t Eg) {
+    const int32_t g = gemv_rows(ex, n, Eg);
+    return g > 0 ? g + 1 : 0;
+}
 
 // The GEMV launches of the experts in rng (gate/up, or down), beside the MFMA
 // kernels of the same range: the small-chunk list's chunks of at most
-// kGemvRows rows.
+// gemv_rows() rows.
 int launch_gemv_step(const strata_moe_experts* ex, bool gate_up, const uint8_t* blobs, int64_t stride,
                      const Buffers& b, const ChunkLists& cl, int64_t T, int64_t n, int32_t Eg, const ExpertRange& rng,
                      hipStream_t st) {
-    if (!use_gemv(ex)) return 0;
+    const int32_t rows = gemv_rows(ex, n, Eg);
+    if (rows == 0) return 0;
     GemvLaunch l{};
+    l.max_rows = rows;
     l.gate_up = gate_up;
     l.blobs = blobs;
     l.stride = stride;
@@ -431,7 +450,7 @@ int launch_gemv_step(const strata_moe_experts* ex, bool gate_up, const uint8_t* 
     l.H = ex->hidden;
     l.I = ex->ffn;
     if (gate_up) {
-        const bool ps = per_slot_q8(ex);
+        const bool ps = per_slot_q8(ex, n, Eg);
         l.src = b.src;
         l.act = ps ? b.sq : b.xq;
         l.act_rows = ps ? n : T;
@@ -487,7 +506,8 @@ int run_streamed_experts(const strata_moe_experts* ex, strata_moe_ring* ring, co
         rng.e1 = e1;
         rng.ring0 = G0 % R;
         rng.nring = R;
-        rng.small_min_rows = use_gemv(ex) ? kGemvRows + 1 : 0;
+        rng.small_min_rows = small_min_rows(ex, n, Eg);
+        rng.max_rows = T;
         HIP_TRY(launch_gate_up((const uint8_t*)ring->slots, ring->slot_bytes, cl, n, Eg, b.src, b.xt, b.xst,
                                tiled_rows_cap(n, Eg), b.xa, b.xs, T, xuop, b.xum, H, I, b.hq, b.hs, st, rng),
                 "gate/up launch");
@@ -522,7 +542,7 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     const int32_t E = ex->n_expert, H = ex->hidden, I = ex->ffn;
     const int32_t Kg = K + shared, Eg = E + shared;  // the grouped pairs per token, the experts they go to
     const int64_t n = T * Kg;
-    const Offsets o = plan(T, K, E, H, I, shared, per_slot_q8(ex));
+    const Offsets o = plan(T, K, E, H, I, shared, per_slot_q8(ex, n, Eg));
     char* ws = fixed_ws;
     if (fixed_ws) {
         if (o.total > fixed_bytes)
@@ -568,10 +588,12 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     HIP_TRY(launch_group(b.gids, b.gp, n, Kg, Eg, b.hist, b.base, b.offsets, cl, b.src, b.slot, b.prow, b.err, st),
             "group launch");
     // the big chunks' input codes and scales, gathered into the tiled layout
-    HIP_TRY(launch_gather_tiles(b.xq, b.xs, b.src, cl, tiled_rows_cap(n, Eg) / 16, H, b.xt, b.xst, st),
-            "gather launch");
+    // (none where no expert can have more than kSmallRows rows: T <= kSmallRows)
+    if (T > kSmallRows)
+        HIP_TRY(launch_gather_tiles(b.xq, b.xs, b.src, cl, tiled_rows_cap(n, Eg) / 16, H, b.xt, b.xst, st),
+                "gather launch");
     // the per-slot q8_1 arm: every routed slot's input row rounded again, with block code sums
-    if (per_slot_q8(ex)) HIP_TRY(launch_quantize_slots(x, b.src, n, H, b.sq, b.ss, b.ssum, st), "quantize launch");
+    if (per_slot_q8(ex, n, Eg)) HIP_TRY(launch_quantize_slots(x, b.src, n, H, b.sq, b.ss, b.ssum, st), "quantize launch");
     tm.end(kGroup);
     if (ring) {
         tm.begin(kStreamed);
@@ -584,7 +606,10 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
         return 0;
     }
     ExpertRange all;  // every expert, resident
-    all.small_min_rows = use_gemv(ex) ? kGemvRows + 1 : 0;
+    all.small_min_rows = small_min_rows(ex, n, Eg);
+    all.max_rows = T;
+    // the MFMA down kernels' tiled H: not needed where every chunk is the GEMV's
+    const bool mfma_down = all.small_min_rows == 0 || T >= all.small_min_rows;
     tm.begin(kGateUp);
     HIP_TRY(launch_gate_up((const uint8_t*)ex->gate_up, ex->gate_up_stride, cl, n, Eg, b.src, b.xt, b.xst,
                            tiled_rows_cap(n, Eg), b.xa, b.xs, T, xuop, b.xum, H, I, b.hq, b.hs, st, all),
@@ -592,8 +617,10 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     TRY(launch_gemv_step(ex, true, (const uint8_t*)ex->gate_up, ex->gate_up_stride, b, cl, T, n, Eg, all, st));
     tm.end(kGateUp);
     tm.begin(kTileH);
-    HIP_TRY(launch_tile_h(b.hq, b.hs, cl, tiled_rows_cap(n, Eg) / 16, I, code_offset(ex), b.hb, b.hst, huop, b.hum, st),
-            "tile launch");
+    if (mfma_down)
+        HIP_TRY(launch_tile_h(b.hq, b.hs, cl, tiled_rows_cap(n, Eg) / 16, I, code_offset(ex), b.hb, b.hst, huop,
+                              b.hum, st),
+                "tile launch");
     tm.end(kTileH);
     tm.begin(kDown);
     HIP_TRY(launch_down((const uint8_t*)ex->down, ex->down_stride, cl, n, Eg, b.src, b.prow, b.hb, b.hst,
@@ -683,8 +710,9 @@ int strata_moe_workspace_bytes(int64_t T, int32_t K, const strata_moe_experts* e
     g_err.clear();
     if (!bytes) return fail(STRATA_MOE_EINVAL, "bytes is NULL");
     TRY(check_layer(T, K, experts));
-    *bytes = plan(T, K, experts->n_expert, experts->hidden, experts->ffn, experts->shared_gate != nullptr,
-                  per_slot_q8(experts))
+    const int32_t sh = experts->shared_gate != nullptr;
+    *bytes = plan(T, K, experts->n_expert, experts->hidden, experts->ffn, sh,
+                  per_slot_q8(experts, T * (K + sh), experts->n_expert + sh))
                  .total;
     return 0;
 }
@@ -1003,15 +1031,16 @@ int strata_moe_gate_up(const int8_t* qx, const float* sx, const int32_t* offsets
     HIP_TRY(launch_prescale(qx, sx, T, H, code_offset(experts), xa, nullptr, xuop, xum, st), "prescale launch");
     HIP_TRY(launch_chunks_from_offsets(offsets, E, n, cl, st), "chunk list launch");  // and the tile table
     HIP_TRY(launch_gather_tiles(qx, sx, src, cl, tiled_rows_cap(n, E) / 16, H, xt, xst, st), "gather launch");
-    // the layer's kernel choice: chunks of at most kGemvRows rows to the GEMV
-    // (by token: the per-slot arm needs the fp32 input, which this entry has not)
+    // the layer's kernel choice for short chunks (the GEMV by token: the
+    // per-slot arm needs the fp32 input, which this entry has not)
     ExpertRange all;
-    all.small_min_rows = use_gemv(experts) ? kGemvRows + 1 : 0;
+    all.small_min_rows = small_min_rows(experts, n, E);
     HIP_TRY(launch_gate_up((const uint8_t*)experts->gate_up, experts->gate_up_stride, cl, n, E, src, xt, xst,
                            tiled_rows_cap(n, E), xa, sx, T, xuop, xum, H, I, qh, sh, st, all),
             "gate/up launch");
-    if (use_gemv(experts)) {
+    if (gemv_rows(experts, n, E) > 0) {
         GemvLaunch l{};
+        l.max_rows = gemv_rows(experts, n, E);
         l.gate_up = true;
         l.blobs = (const uint8_t*)experts->gate_up;
         l.stride = experts->gate_up_stride;
@@ -1063,12 +1092,13 @@ int strata_moe_down(const int8_t* qh, const float* sh, const int32_t* offsets, c
             "tile launch");
     HIP_TRY(launch_row_weights(slot, p, n, prow, st), "weights launch");
     ExpertRange all;  // the layer's kernel choice, as strata_moe_gate_up
-    all.small_min_rows = use_gemv(experts) ? kGemvRows + 1 : 0;
+    all.small_min_rows = small_min_rows(experts, n, E);
     HIP_TRY(launch_down((const uint8_t*)experts->down, experts->down_stride, cl, n, E, src, prow, hb, hst,
                         tiled_rows_cap(n, E), sh, huop, hum, H, I, dm, st, all),
             "down launch");
-    if (use_gemv(experts)) {
+    if (gemv_rows(experts, n, E) > 0) {
         GemvLaunch l{};
+        l.max_rows = gemv_rows(experts, n, E);
         l.gate_up = false;
         l.blobs = (const uint8_t*)experts->down;
         l.stride = experts->down_stride;

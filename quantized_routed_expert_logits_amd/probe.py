@@ -18,6 +18,7 @@ _f = ctypes.POINTER(ctypes.c_float)
 _lib.strata_probe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _d, _d]
 _lib.strata_probe_scaled_blocks.argtypes = [ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _d, _d]
 _lib.strata_probe_mfma_f16.argtypes = [_f, _f, _f, _f]
+_lib.strata_probe_hbm_read.argtypes = [ctypes.c_int64, ctypes.c_int32, _d, _d]
 
 # MFMA forms of strata_probe_mfma_rate, by index
 KINDS = ["f16_16x16x32", "f16_32x32x16", "i8_16x16x64", "i8_32x32x32", "i8_16x16x32", "i8_32x32x16"]
@@ -38,6 +39,15 @@ def strata_probe_scaled_blocks(int8: bool, groups: int = 4096, blocks: int = 512
     rc = _lib.strata_probe_scaled_blocks(int(int8), groups, blocks, ctypes.byref(r), ctypes.byref(ms))
     if rc != 0:
         raise RuntimeError(f"strata_probe_scaled_blocks failed ({rc})")
+    return r.value, ms.value
+
+
+def strata_probe_hbm_read(nbytes: int = 2 << 30, groups: int = 4096) -> tuple[float, float]:
+    """(GB/s, kernel ms) of a plain streaming read of nbytes from HBM."""
+    r, ms = ctypes.c_double(), ctypes.c_double()
+    rc = _lib.strata_probe_hbm_read(nbytes, groups, ctypes.byref(r), ctypes.byref(ms))
+    if rc != 0:
+        raise RuntimeError(f"strata_probe_hbm_read failed ({rc})")
     return r.value, ms.value
 
 

@@ -79,6 +79,9 @@ EXTRA_SHAPES = {
     "short_256": LayerShape("short_256", T=256, H=2560, E=512, K=10, I=1024),
     # a decode-sized window (320 pairs over 512 experts: mostly one row per hit expert)
     "window_32": LayerShape("window_32", T=32, H=2560, E=512, K=10, I=1024),
+    # 1.25 and 2.5 rows per expert on average: either side of the GEMV's threshold
+    "window_64": LayerShape("window_64", T=64, H=2560, E=512, K=10, I=1024),
+    "window_128": LayerShape("window_128", T=128, H=2560, E=512, K=10, I=1024),
     # the MoE half with its shared expert: the 8192-token chunk, and the pages'
     # geometry (there the shared expert has the routed experts' width, 640)
     "chunk_8k_shared": LayerShape("chunk_8k_shared", T=8192, H=2560, E=512, K=10, I=1024, shared=True),

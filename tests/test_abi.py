@@ -114,7 +114,7 @@ def test_shared_expert_sizes_and_limits_on_the_host(qm):
     assert qm.ExpertsStruct.shared_gate.offset == qm.ExpertsStruct.router_prepared.offset + ctypes.sizeof(ctypes.c_void_p)
     assert qm.ExpertsStruct.flags.offset == qm.ExpertsStruct.shared_gate.offset + ctypes.sizeof(ctypes.c_void_p)
     st = _experts_struct(qm)
-    st.flags = 4  # no such flag
+    st.flags = 8  # no such flag
     assert lib.strata_moe_workspace_bytes(8, 10, ctypes.byref(st), ctypes.byref(b)) == qm.EINVAL
 
 
@@ -232,3 +232,17 @@ def test_noalloc_entry_point_checks_on_the_host(qm):
     assert lib.strata_moe_prefill_noalloc(ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.byref(st), 8, 0,
                                           ctypes.c_void_p(16), None) == qm.EINVAL
     assert lib.strata_moe_prefill_noalloc(None, None, ctypes.byref(st), 0, 10, None, None) == 0  # T = 0: no-op
+
+
+def test_probe_library_exports_and_rejects_bad_arguments():
+    from quantized_routed_expert_logits_amd import probe
+    lib = ctypes.CDLL(probe.LIB_PATH)
+    for name in ("strata_probe_mfma_rate", "strata_probe_scaled_blocks", "strata_probe_mfma_f16",
+                 "strata_probe_hbm_read"):
+        assert hasattr(lib, name), name
+    d = ctypes.c_double()
+    # argument checks come before any HIP call
+    assert probe._lib.strata_probe_hbm_read(1000, 64, ctypes.byref(d), ctypes.byref(d)) == -1  # under 1 MiB
+    assert probe._lib.strata_probe_hbm_read((1 << 20) + 8, 64, ctypes.byref(d), ctypes.byref(d)) == -1  # not 16 | bytes
+    assert probe._lib.strata_probe_hbm_read(1 << 20, 0, ctypes.byref(d), ctypes.byref(d)) == -1
+    assert probe._lib.strata_probe_mfma_rate(99, 1, 1, ctypes.byref(d), ctypes.byref(d)) == -1

@@ -337,21 +337,29 @@ def test_layer_zero_tokens(qm):
 
 # ------------------------------------------------------- small-T kernels
 SMALL_T = [S.shape("window_32"), S.custom(T=20, H=256, E=64, K=4, I=128),
-           S.custom(T=24, H=512, E=48, K=3, I=640, fmt="q2_0")]
+           S.custom(T=24, H=512, E=48, K=3, I=640, fmt="q2_0"),
+           S.custom(T=64, H=256, E=32, K=3, I=192),  # 6 rows per expert: the GEMV only when forced
+           # T <= 8: every chunk is the GEMV's (the MFMA kernels and the tiled H are not launched)
+           S.custom(T=8, H=256, E=16, K=4, I=128), S.custom(T=6, H=512, E=12, K=3, I=192, fmt="q2_0")]
 
 
 @pytest.mark.parametrize("s", SMALL_T, ids=lambda s: s.name)
 def test_small_t_kernel_choices(qm, s):
-    """The layer at decode-window sizes through its three kernel choices for
-    chunks of one or two rows: the int8 GEMV (default), the small-chunk MFMA
-    kernel (FLAG_NO_GEMV) and the GEMV on per-slot q8_1 inputs
-    (FLAG_PER_SLOT_Q8); each against the oracle."""
+    """The layer at decode-window sizes through its kernel choices for short
+    chunks: the default (the int8 GEMV on chunks of <= 8 rows where the
+    experts average <= 2 rows, two rows per pass), the MFMA kernels only
+    (FLAG_NO_GEMV), the GEMV on per-slot q8_1 inputs (FLAG_PER_SLOT_Q8) and
+    the GEMV at any average (FLAG_GEMV_ALWAYS, alone and with the per-slot
+    arm); each against the oracle."""
     x, wr, ref = _stage_ref(s)
     ex = gpu_experts(s)
     sizes = np.diff(ref["offsets"])
-    assert np.count_nonzero((sizes > 0) & (sizes <= 2)) > 0  # the GEMV has chunks to take
+    assert np.count_nonzero((sizes > 0) & (sizes <= 2)) > 0  # single-pass chunks
+    assert np.count_nonzero((sizes > 2) & (sizes <= 8)) > 0  # several passes
+    print(f"{s.name}: rows per expert {s.T * s.K / s.E:.2f} on average, chunk sizes up to {sizes.max()}")
     outs = {}
-    for flags in (0, qm.FLAG_NO_GEMV, qm.FLAG_PER_SLOT_Q8):
+    for flags in (0, qm.FLAG_NO_GEMV, qm.FLAG_PER_SLOT_Q8, qm.FLAG_GEMV_ALWAYS,
+                  qm.FLAG_GEMV_ALWAYS | qm.FLAG_PER_SLOT_Q8):
         out = torch.empty((s.T, s.H), dtype=torch.float32, device="cuda")
         d = qm.strata_moe_prefill_debug(_t(x), _t(wr), ex.with_flags(flags), s.K, out)
         g = {k: v.cpu().numpy() for k, v in d.items()}
@@ -362,7 +370,7 @@ def test_small_t_kernel_choices(qm, s):
         print(f"{s.name} flags {flags}: max|dy|/max|y| = {err:.2e}, H-code mismatch rate {rate:.2e}")
         assert rate < H_RATE and err <= Y_TOL
         outs[flags] = g["out"]
-    # the three are not compared with each other bit for bit: their fp32 rounding orders differ, so an
+    # the arms are not compared with each other bit for bit: their fp32 rounding orders differ, so an
     # H code at a rounding near-tie may go either way (each is checked against the oracle above)
 
 
