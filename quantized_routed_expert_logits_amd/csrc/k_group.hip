@@ -11,7 +11,8 @@
 // page, Prefill::run, MoE half), which makes the tables unique and exactly
 // comparable.
 //
-// Three launches, none of which waits on the host:
+// Three launches, none of which waits on the host (one, group_small_kernel,
+// where the pairs fill at most kGroupSmallChunks chunks):
 //   hist    one workgroup per chunk of 2048 pairs: LDS histogram of its ids;
 //   scan    one workgroup: per expert the exclusive prefix over chunks, the
 //           counts' exclusive scan over experts (offsets), and the two lists
@@ -22,6 +23,10 @@
 //           over the id bits (multi-split); a first pass counts per wave and
 //           expert, a scan over the waves gives each wave's first rows, and a
 //           second pass assigns the rows in pair order.
+// group_small_kernel does the three in one workgroup for short prompts, which
+// otherwise pay three launches' latency for little work: the histogram in
+// LDS, the same scan, then the chunks' scatter one after the other with a
+// running first row per expert.
 #include "internal.h"
 
 namespace strata_moe {
@@ -180,6 +185,11 @@ __global__ void __launch_bounds__(1024) group_scan_kernel(const int32_t* __restr
 }
 
 constexpr int kScatterWaves = kGroupChunk / 256;  // 8 waves of 256 pairs per chunk
+// group_small_kernel up to this many chunks: one.  Its chunks' scatter runs
+// one after another on one CU; at 5 chunks (1024 tokens, K = 10) it measured
+// 55 us against 19 us for the three kernels, at one chunk 13 us against 21
+// plus two launch gaps.
+constexpr int kGroupSmallChunks = 1;
 
 // The lanes of this wave whose id equals this lane's (all lanes with a valid
 // id take part in the ballots); 0 for an invalid id.
@@ -193,6 +203,48 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int32_t e, bool ok, int nb
     return ok ? same : 0ull;
 }
 
+// The multi-split scatter of the pairs [i0, i0 + 256) by one wave, as
+// group_scatter_kernel's two passes: count[e] gets the wave's count per
+// expert (pass 1), then (pass 2, with count[e] set to the wave's first row per
+// expert) the rows in pair order.
+__device__ __forceinline__ void scatter_count(const int32_t* __restrict__ ids, int64_t n, int32_t E, int nbits,
+                                              int64_t i0, int lane, int32_t* count) {
+    for (int step = 0; step < 4; ++step) {
+        const int64_t i = i0 + step * 64 + lane;
+        const int32_t e = i < n ? ids[i] : -1;
+        const bool ok = e >= 0 && e < E;
+        const uint64_t same = same_expert_lanes(e, ok, nbits);
+        if (ok && (same >> lane) == 1ull) count[e] += __popcll(same);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+__device__ __forceinline__ void scatter_rows(const int32_t* __restrict__ ids, const float* __restrict__ p, int64_t n,
+                                             int32_t K, int32_t E, int nbits, int64_t i0, int lane, int32_t* next,
+                                             int32_t* __restrict__ src, int32_t* __restrict__ slot,
+                                             float* __restrict__ prow) {
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int step = 0; step < 4; ++step) {
+        const int64_t i = i0 + step * 64 + lane;
+        const int32_t e = i < n ? ids[i] : -1;
+        const bool ok = e >= 0 && e < E;
+        const uint64_t same = same_expert_lanes(e, ok, nbits);
+        const int rank = __popcll(same & below);
+        const int first = ok ? next[e] : 0;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        if (ok) {
+            const int row = first + rank;
+            slot[i] = row;
+            src[row] = (int32_t)(i / K);
+            if (prow) prow[row] = p[i];
+            if ((same >> lane) == 1ull) next[e] = first + __popcll(same);  // the highest lane of this expert
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 __global__ void __launch_bounds__(64 * kScatterWaves) group_scatter_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ p, int64_t n, int32_t K, int32_t E,
     const int32_t* __restrict__ base, const int32_t* __restrict__ offsets, int32_t* __restrict__ src,
@@ -204,17 +256,7 @@ __global__ void __launch_bounds__(64 * kScatterWaves) group_scatter_kernel(
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     const int64_t i0 = (int64_t)blockIdx.x * kGroupChunk + 256 * w;
-    const uint64_t below = (1ull << lane) - 1ull;
-    // pass 1: this wave's count per expert (the highest lane of each expert adds)
-    for (int step = 0; step < 4; ++step) {
-        const int64_t i = i0 + step * 64 + lane;
-        const int32_t e = i < n ? ids[i] : -1;
-        const bool ok = e >= 0 && e < E;
-        const uint64_t same = same_expert_lanes(e, ok, nbits);
-        if (ok && (same >> lane) == 1ull) next[w][e] += __popcll(same);
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-    }
+    scatter_count(ids, n, E, nbits, i0, lane, next[w]);
     __syncthreads();
     // each wave's first row per expert: the chunk's first row, then the waves before it
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
@@ -226,25 +268,69 @@ __global__ void __launch_bounds__(64 * kScatterWaves) group_scatter_kernel(
         }
     }
     __syncthreads();
-    // pass 2: rows in pair order
-    for (int step = 0; step < 4; ++step) {
-        const int64_t i = i0 + step * 64 + lane;
-        const int32_t e = i < n ? ids[i] : -1;
-        const bool ok = e >= 0 && e < E;
-        const uint64_t same = same_expert_lanes(e, ok, nbits);
-        const int rank = __popcll(same & below);
-        const int first = ok ? next[w][e] : 0;
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        if (ok) {
-            const int row = first + rank;
-            slot[i] = row;
-            src[row] = (int32_t)(i / K);
-            if (prow) prow[row] = p[i];
-            if ((same >> lane) == 1ull) next[w][e] = first + __popcll(same);  // the highest lane of this expert
+    scatter_rows(ids, p, n, K, E, nbits, i0, lane, next[w], src, slot, prow);
+}
+
+// All of the grouping in one workgroup of 1024 threads, for n pairs in at
+// most kGroupSmallChunks chunks of kGroupChunk: the same tables as the three
+// kernels (the same scan; the scatter's order is pair order either way).
+__global__ void __launch_bounds__(1024) group_small_kernel(const int32_t* __restrict__ ids,
+                                                           const float* __restrict__ p, int64_t n, int32_t K,
+                                                           int32_t E, int32_t* __restrict__ offsets, ChunkLists cl,
+                                                           int32_t* __restrict__ src, int32_t* __restrict__ slot,
+                                                           float* __restrict__ prow, int32_t* __restrict__ err) {
+    __shared__ int32_t cur[kMaxExperts];  // counts, then each expert's next free row
+    __shared__ int32_t next[kScatterWaves][kMaxExperts];
+    __shared__ int total_rows, total_tiled, total_big, total_small;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) cur[e] = 0;
+    __syncthreads();
+    bool bad = false;
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+        const int32_t e = ids[i];
+        if (e < 0 || e >= E)
+            bad = true;
+        else
+            atomicAdd(&cur[e], 1);
+    }
+    if (bad) atomicOr(err, 1);
+    __syncthreads();
+    const int e = threadIdx.x;
+    const int cnt = e < E ? cur[e] : 0;
+    const int off = block_exclusive_scan(cnt, &total_rows);
+    const int toff = block_exclusive_scan((cnt + 15) / 16 * 16, &total_tiled);
+    int per = 0;
+    const int nt = e < E ? chunk_split(cnt, &per) : 0;
+    const int ns = small_chunks(cnt, nt, per);
+    const int bpos = block_exclusive_scan(nt - ns, &total_big);
+    const int spos = block_exclusive_scan(ns, &total_small);
+    if (e < E) {
+        offsets[e] = off;
+        emit_chunks(cl, e, off, cnt, nt, per, bpos, spos, toff);
+        write_first(cl, E, e, bpos, spos, toff / 16);
+        cur[e] = off;
+    }
+    if (e == 0) offsets[E] = (int32_t)n;
+    finish_lists(cl, E, total_big, total_small, total_tiled);
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int64_t c0 = 0; c0 < n; c0 += kGroupChunk) {
+        for (int i = threadIdx.x; i < kScatterWaves * E; i += blockDim.x) next[i / E][i % E] = 0;
+        __syncthreads();  // also orders the cur[] writes above and the last chunk's rows
+        if (w < kScatterWaves) scatter_count(ids, n, E, nbits, c0 + 256 * w, lane, next[w]);
+        __syncthreads();
+        for (int ee = threadIdx.x; ee < E; ee += blockDim.x) {
+            int run = cur[ee];
+            for (int ww = 0; ww < kScatterWaves; ++ww) {
+                const int t = next[ww][ee];
+                next[ww][ee] = run;
+                run += t;
+            }
+            cur[ee] = run;
         }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
+        __syncthreads();
+        if (w < kScatterWaves) scatter_rows(ids, p, n, K, E, nbits, c0 + 256 * w, lane, next[w], src, slot, prow);
+        __syncthreads();
     }
 }
 
@@ -282,7 +368,10 @@ hipError_t launch_group(const int32_t* ids, const float* p, int64_t n, int32_t K
                         int32_t* base, int32_t* offsets, const ChunkLists& cl, int32_t* src, int32_t* slot,
                         float* prow, int32_t* err, hipStream_t st) {
     const int64_t nchunks = (n + kGroupChunk - 1) / kGroupChunk;
-    if (nchunks > 0) {
+    if (nchunks > 0 && nchunks <= kGroupSmallChunks) {
+        hipLaunchKernelGGL(group_small_kernel, dim3(1), dim3(1024), 0, st, ids, p, n, K, E, offsets, cl, src, slot,
+                           prow, err);
+    } else if (nchunks > 0) {
         hipLaunchKernelGGL(group_hist_kernel, dim3((unsigned)nchunks), dim3(256), 0, st, ids, n, E, hist, err);
         hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(1024), 0, st, hist, nchunks, n, E, base, offsets, cl);
         hipLaunchKernelGGL(group_scatter_kernel, dim3((unsigned)nchunks), dim3(64 * kScatterWaves), 0, st, ids, p,

@@ -182,8 +182,17 @@ __global__ void __launch_bounds__(256, 2) router_mfma_kernel(const float* __rest
                                                              int32_t E, int32_t Ep, float* __restrict__ out) {
     __shared__ half8_t a_lds[2][4][2][64];  // [buffer][token tile][hi, lo][lane]
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, kg = lane >> 4;
-    const int n0 = blockIdx.x * kRtN;
-    const int64_t m0 = (int64_t)blockIdx.y * kRtM;
+    // XCD-aware order: the dispatcher deals consecutive workgroups to the 8
+    // XCDs in turn, so within each run of 8 token tiles the gx expert tiles
+    // of one token tile take ids 8 apart and share an XCD: the tile's input
+    // rows come from HBM once and from that XCD's L2 after (a last partial
+    // run keeps the plain order)
+    const int gx = gridDim.x, gy = gridDim.y;
+    const int lin = blockIdx.y * gx + blockIdx.x, grp = lin / (8 * gx), rr = lin % (8 * gx);
+    const bool full = gy - 8 * grp >= 8;
+    const int bx = full ? rr / 8 : rr % gx, by = full ? 8 * grp + rr % 8 : 8 * grp + rr / gx;
+    const int n0 = bx * kRtN;
+    const int64_t m0 = (int64_t)by * kRtM;
     const int nk = H / 32, kper = nk / gridDim.z, kb0 = blockIdx.z * kper, kb1 = kb0 + kper;
 
     // staging role: token row sr of the tile, value group sk (8 values) of the k block
@@ -684,13 +693,19 @@ __device__ __forceinline__ void wave_dot2_fp64(const float* __restrict__ x, cons
     v2 = wave_sum(a2);
 }
 
-// One wave per listed token (grid-stride over the list), no workgroup
-// barrier.  Candidates: every expert within delta below the K-th value (this
-// includes all K selected).  Selected ranks outside every near-tie keep their
-// fp32 value: each is at least delta away from any value that is re-scored,
-// so the merged order is the exact one.  The others are re-scored one at a
-// time as wave-wide fp64 dot products; then the candidates are re-ranked.
-// Lane l keeps the candidates among experts l, l + 64, ... in registers.
+// Listed tokens are taken one per workgroup where the list is short (at most
+// kResolveWide tokens: short prompts wait for one token's latency), else one
+// per wave (a long list fills the chip either way, and four waves per token
+// would not all be resident).  Candidates: every expert within delta below
+// the K-th value (this includes all K selected).  Selected ranks outside
+// every near-tie keep their fp32 value: each is at least delta away from any
+// value that is re-scored, so the merged order is the exact one.  The others
+// are re-scored as wave-wide fp64 dot products, two at a time; with a
+// workgroup per token its 4 waves take every fourth pair of the list, the
+// values meet in LDS and wave 0 re-ranks the candidates.  Each value comes
+// from the same dot-product routine whichever wave computes it.  Lane l
+// keeps the candidates among experts l, l + 64, ... in registers.
+constexpr int kResolveWide = 512;
 template <int kSlots>
 __global__ void __launch_bounds__(256) topk_resolve_kernel(const float* __restrict__ logits, int nsplit,
                                                            int64_t T, const float* __restrict__ x,
@@ -701,9 +716,14 @@ __global__ void __launch_bounds__(256) topk_resolve_kernel(const float* __restri
                                                            const int32_t* __restrict__ amb,
                                                            const int32_t* __restrict__ sel,
                                                            int32_t* __restrict__ ids, float* __restrict__ p_out) {
+    __shared__ double rescored[kMaxExperts];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = amb[0];
-    for (int it = blockIdx.x * kWaves + wave; it < n; it += gridDim.x * kWaves) {  // uniform over the wave
+    const bool wide = n <= kResolveWide;  // uniform over the grid
+    const int per = wide ? 1 : kWaves;    // tokens per workgroup and turn
+    for (int it0 = blockIdx.x * per; it0 < n; it0 += gridDim.x * per) {  // uniform over the workgroup
+        const int it = wide ? it0 : it0 + wave;
+        if (it >= n) continue;  // a wave without a token this turn (one per wave only: no barrier there)
         const int64_t t = amb[1 + it];
         Selection<kSlots> S;  // the select pass's ranking of this token, and its logits
         load_logits(logits + t * E, nsplit, T * E, E, lane, S);
@@ -729,12 +749,12 @@ __global__ void __launch_bounds__(256) topk_resolve_kernel(const float* __restri
             todo |= (uint32_t)(c && !stable) << i;
         }
         const float* xr = x + t * H;
-        // the experts to re-score, two at a time (uniform over the wave): each
-        // round takes the next two set bits of the slots' candidate masks
+        // the experts to re-score in list order, two per pair; with a
+        // workgroup per token this wave takes pairs wave, wave + 4, ...
         uint64_t m[kSlots];
 #pragma unroll
         for (int i = 0; i < kSlots; ++i) m[i] = __ballot((todo >> i) & 1u);
-        for (;;) {
+        for (int pair = 0;; ++pair) {
             int e1 = -1, e2 = -1;
 #pragma unroll
             for (int i = 0; i < kSlots; ++i) {
@@ -748,6 +768,7 @@ __global__ void __launch_bounds__(256) topk_resolve_kernel(const float* __restri
                 }
             }
             if (e1 < 0) break;
+            if (wide && (pair & (kWaves - 1)) != wave) continue;
             double v1, v2 = 0.0;
             if (e2 >= 0)
                 wave_dot2_fp64(xr, wt + (int64_t)e1 * H, wt + (int64_t)e2 * H, H, lane, v1, v2);
@@ -757,31 +778,47 @@ __global__ void __launch_bounds__(256) topk_resolve_kernel(const float* __restri
                 v1 += (double)bias[e1];
                 if (e2 >= 0) v2 += (double)bias[e2];
             }
+            if (wide) {
+                if (lane == 0) {
+                    rescored[e1] = v1;
+                    if (e2 >= 0) rescored[e2] = v2;
+                }
+            } else {
 #pragma unroll
-            for (int i = 0; i < kSlots; ++i) {
-                const int e = lane + 64 * i;
-                cv[i] = e == e1 ? v1 : e == e2 ? v2 : cv[i];
+                for (int i = 0; i < kSlots; ++i) {
+                    const int e = lane + 64 * i;
+                    cv[i] = e == e1 ? v1 : e == e2 ? v2 : cv[i];
+                }
             }
         }
-        double lv[kMaxTopK];
-        int li[kMaxTopK];
-        uint32_t tk = 0;
-#pragma unroll
-        for (int k = 0; k < kMaxTopK; ++k) {
-            lv[k] = -DBL_MAX;
-            li[k] = INT_MAX;
-            if (k >= K) continue;
-            Best<double> b{-DBL_MAX, INT_MAX};
+        if (wide) {
+            __syncthreads();
 #pragma unroll
             for (int i = 0; i < kSlots; ++i)
-                if (((cand & ~tk) >> i) & 1u) take_better(b, cv[i], lane + 64 * i);
-            b = wave_best(b);
-            const int bi = b.i;
-            lv[k] = b.v;
-            li[k] = bi;
-            if (bi < E && (bi & 63) == lane) tk |= 1u << (bi >> 6);
+                if ((todo >> i) & 1u) cv[i] = rescored[lane + 64 * i];
         }
-        write_token(lv, li, K, lane, t, ids, p_out);
+        if (!wide || wave == 0) {
+            double lv[kMaxTopK];
+            int li[kMaxTopK];
+            uint32_t tk = 0;
+#pragma unroll
+            for (int k = 0; k < kMaxTopK; ++k) {
+                lv[k] = -DBL_MAX;
+                li[k] = INT_MAX;
+                if (k >= K) continue;
+                Best<double> b{-DBL_MAX, INT_MAX};
+#pragma unroll
+                for (int i = 0; i < kSlots; ++i)
+                    if (((cand & ~tk) >> i) & 1u) take_better(b, cv[i], lane + 64 * i);
+                b = wave_best(b);
+                const int bi = b.i;
+                lv[k] = b.v;
+                li[k] = bi;
+                if (bi < E && (bi & 63) == lane) tk |= 1u << (bi >> 6);
+            }
+            write_token(lv, li, K, lane, t, ids, p_out);
+        }
+        if (wide) __syncthreads();  // rescored is free for the next token
     }
 }
 
@@ -826,7 +863,7 @@ hipError_t launch_topk(const float* logits, const float* x, const float* xn, con
         else
             hipLaunchKernelGGL(topk_select_kernel<kPerLane>, sg, dim3(64 * kWaves), 0, st, logits, ns, T, H, E, K, xn,
                                wnorm, amb, sel, ids, p);
-        const unsigned grid = (unsigned)((T < 8192 ? T : 8192) + kWaves - 1) / kWaves;
+        const unsigned grid = (unsigned)(T < 2048 ? T : 2048);  // one workgroup per listed token at a time
         if (E <= 512)
             hipLaunchKernelGGL(topk_resolve_kernel<8>, dim3(grid), dim3(256), 0, st, logits, ns, T, x, wt, bias, H, E,
                                K, xn, wnorm, amb, sel, ids, p);

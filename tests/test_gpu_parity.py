@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import oracle
+import packed_layout
 import synthetic as S
 from layers import (canonical_expert, check_h_codes, down_error_bound, gate_bound, getter, gpu_experts, rel_err,
                     shared_args)
@@ -70,6 +71,23 @@ def test_pack_unpack_round_trip(qm, shape):
         assert np.array_equal(sg[e].cpu().numpy().view(np.uint16), c.scales_gu)
         assert np.array_equal(cd[e].cpu().numpy(), c.codes_d)
         assert np.array_equal(sd[e].cpu().numpy().view(np.uint16), c.scales_d)
+
+
+@pytest.mark.parametrize("shape", [S.shape("tiny"), S.custom(T=1, H=384, E=3, K=1, I=192),
+                                   S.custom(T=1, H=2560, E=2, K=1, I=1024)])
+def test_packed_layout_host_decode(qm, shape):
+    """The packed blobs, copied to the host and decoded there from the layout's
+    definition (tests/packed_layout.py), give back the canonical codes and
+    scales: the packer writes the documented layout."""
+    ex = gpu_experts(shape)
+    gu = ex.gate_up.cpu().numpy()
+    dn = ex.down.cpu().numpy()
+    for e in range(shape.E):
+        c = canonical_expert(shape, e)
+        got = packed_layout.decode_expert(gu[e * ex.gate_up_stride:(e + 1) * ex.gate_up_stride],
+                                          dn[e * ex.down_stride:(e + 1) * ex.down_stride], shape.H, shape.I)
+        for g, want in zip(got, (c.codes_gu, c.scales_gu, c.codes_d, c.scales_d)):
+            assert np.array_equal(g, want)
 
 
 # -------------------------------------------------------------------- route
@@ -178,8 +196,12 @@ def test_route_outlier_channels(qm):
 
 
 # -------------------------------------------------------------------- group
+# n = T K pairs: up to one chunk of 2048 takes the one-workgroup kernel (204 x 10 is the last such), more
+# the three-kernel path
 @pytest.mark.parametrize("T,E,K,skew", [(64, 16, 2, 0.0), (3000, 512, 10, 0.0), (4096, 512, 10, 3.0),
-                                        (32768, 512, 10, 0.0), (257, 1024, 16, 0.0), (9, 1, 1, 0.0)])
+                                        (32768, 512, 10, 0.0), (257, 1024, 16, 0.0), (9, 1, 1, 0.0),
+                                        (204, 512, 10, 0.0), (205, 512, 10, 0.0), (128, 1024, 16, 3.0),
+                                        (1024, 512, 10, 3.0)])
 def test_group_bit_exact(qm, T, E, K, skew):
     rng = np.random.default_rng(T + E)
     logits = rng.standard_normal((T, E)) - skew * np.log1p(np.arange(E))[None, :]
