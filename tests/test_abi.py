@@ -246,3 +246,14 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert probe._lib.strata_probe_hbm_read((1 << 20) + 8, 64, ctypes.byref(d), ctypes.byref(d)) == -1  # not 16 | bytes
     assert probe._lib.strata_probe_hbm_read(1 << 20, 0, ctypes.byref(d), ctypes.byref(d)) == -1
     assert probe._lib.strata_probe_mfma_rate(99, 1, 1, ctypes.byref(d), ctypes.byref(d)) == -1
+
+
+def test_one_call_is_limited_by_its_tiled_operands(qm):
+    """(T*K + 15*E) * max(H, I) * 2 bytes must stay below 2 GiB: about 41,000
+    tokens at H = 2560, K = 10, E = 512; longer prompts run as several calls."""
+    st = _experts_struct(qm)
+    b = ctypes.c_size_t()
+    lib = qm.library()
+    assert lib.strata_moe_workspace_bytes(40000, 10, ctypes.byref(st), ctypes.byref(b)) == 0
+    assert lib.strata_moe_workspace_bytes(42000, 10, ctypes.byref(st), ctypes.byref(b)) == qm.EINVAL
+    assert "too large" in qm.strata_moe_last_error()

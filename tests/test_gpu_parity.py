@@ -270,7 +270,10 @@ def test_down_stage(qm, s):
 
 
 # --------------------------------------------------------------- the layer
-LAYER_SHAPES = STAGE_SHAPES + [S.custom(T=129, H=256, E=8, K=4, I=64, skewed=True)]
+LAYER_SHAPES = STAGE_SHAPES + [S.custom(T=129, H=256, E=8, K=4, I=64, skewed=True),
+                               # the largest widths the library takes (H = I = 4096), and the most
+                               # experts and pairs per token (E = 1024, K = 16)
+                               S.custom(T=24, H=4096, E=4, K=2, I=4096), S.custom(T=64, H=256, E=1024, K=16, I=64)]
 
 
 @pytest.mark.parametrize("s", LAYER_SHAPES, ids=lambda s: s.name)
@@ -289,7 +292,9 @@ def test_layer_all_intermediates(qm, s):
 
 SHARED_SHAPES = [S.custom(T=200, H=256, E=10, K=3, I=128, shared=True),
                  S.custom(T=160, H=512, E=6, K=2, I=640, fmt="q2_0", shared=True),
-                 S.custom(T=129, H=256, E=8, K=4, I=64, skewed=True, shared=True)]
+                 S.custom(T=129, H=256, E=8, K=4, I=64, skewed=True, shared=True),
+                 # with the shared expert the grouping reaches E + 1 = 1024 experts and K + 1 = 16 slots
+                 S.custom(T=64, H=256, E=1023, K=15, I=64, shared=True)]
 
 
 @pytest.mark.parametrize("s", SHARED_SHAPES, ids=lambda s: s.name)
