@@ -146,6 +146,18 @@ def region_ms(qm, torch, s, x, wr, experts, out, steps: int):
     return ev0.elapsed_time(ev1) / steps, 1e3 * (time.perf_counter() - wall0) / steps
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or "" where it cannot be read."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def hit_experts(torch, ids, nexp: int) -> int:
     return int((torch.bincount(ids.reshape(-1).long(), minlength=nexp) > 0).sum())
 
@@ -385,7 +397,8 @@ def main() -> int:
         dt = time.perf_counter() - t0
         cpu = {"value": round(len(tok) / dt, 2), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
                "sample": f"{len(tok)} random tokens of the {s.name} layer, full layer per token "
-                         f"(router, top-K, quantize, {s.K + s.shared} expert FFNs, combine) in double; {dt:.2f} s"}
+                         f"(router, top-K, quantize, {s.K + s.shared} expert FFNs, combine) in double; {dt:.2f} s",
+               "cpu_model": cpu_model()}
 
     line = {
         "metric": METRIC,
