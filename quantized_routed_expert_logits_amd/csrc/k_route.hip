@@ -591,20 +591,34 @@ __device__ __forceinline__ void write_token(const V (&lv)[kMaxTopK], const int (
 // One wave per token: tokens without a near-tie are finished here; the others
 // are appended to `amb` (amb[0] = count, then token ids) for the resolve pass,
 // with their fp32 ranking in `sel` (kSelWords per token: the ranked expert
-// ids, the loose-rank mask, the K-th value), which that pass then reuses.
+// ids, the loose-rank mask, the K-th value), which that pass then reuses.  A
+// workgroup of kSelectWaves tokens counts its near-tie tokens in LDS and
+// takes their list places with one atomic on amb[0]: one atomic per token
+// measured 25 us of the pass's 47 at 8192 tokens (the counter serializes
+// them).
+// Short calls (up to kSelectShort tokens) keep 4-wave workgroups: there the
+// tokens spread over more CUs, and the list has few entries anyway.
 constexpr int kWaves = 4;
-template <int kSlots>
-__global__ void __launch_bounds__(256) topk_select_kernel(const float* __restrict__ logits, int nsplit, int64_t T,
-                                                          int32_t H, int32_t E, int32_t K,
-                                                          const float* __restrict__ xn,
-                                                          const float* __restrict__ wnorm, int32_t* __restrict__ amb,
-                                                          int32_t* __restrict__ sel, int32_t* __restrict__ ids,
-                                                          float* __restrict__ p_out) {
+constexpr int kSelectShort = 256;
+template <int kSlots, int kSelectWaves>
+__global__ void __launch_bounds__(64 * kSelectWaves) topk_select_kernel(const float* __restrict__ logits, int nsplit,
+                                                                        int64_t T, int32_t H, int32_t E, int32_t K,
+                                                                        const float* __restrict__ xn,
+                                                                        const float* __restrict__ wnorm,
+                                                                        int32_t* __restrict__ amb,
+                                                                        int32_t* __restrict__ sel,
+                                                                        int32_t* __restrict__ ids,
+                                                                        float* __restrict__ p_out) {
+    __shared__ int wg_count, wg_base;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * kWaves + wave;
-    if (t >= T) return;  // whole wave; this kernel has no block-level barrier
+    const int64_t t = (int64_t)blockIdx.x * kSelectWaves + wave;
+    if (threadIdx.x == 0) wg_count = 0;
+    __syncthreads();
+    const bool live = t < T;  // every wave meets the barriers below
     Selection<kSlots> S;
-    select_token(logits + t * E, nsplit, T * E, E, K, tie_coeff(H) * xn[t] * *wnorm, lane, S);
+    S.loose = 0;
+    if (live) select_token(logits + t * E, nsplit, T * E, E, K, tie_coeff(H) * xn[t] * *wnorm, lane, S);
+    int local = 0;
     if (S.loose) {
         int word = 0;
 #pragma unroll
@@ -613,17 +627,18 @@ __global__ void __launch_bounds__(256) topk_select_kernel(const float* __restric
         if (lane == kMaxTopK) word = (int)S.loose;
         if (lane == kMaxTopK + 1) word = __builtin_bit_cast(int, S.vK);
         if (lane < kSelWords) sel[t * kSelWords + lane] = word;
-        if (lane == 0) {
-            const int slot = atomicAdd(amb, 1);
-            amb[1 + slot] = (int32_t)t;
-        }
-        return;
-    }
-    float lv[kMaxTopK];
-    int li[kMaxTopK];
+        if (lane == 0) local = atomicAdd(&wg_count, 1);  // LDS
+    } else if (live) {
+        float lv[kMaxTopK];
+        int li[kMaxTopK];
 #pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k) lv[k] = S.selv[k], li[k] = S.seli[k];
-    write_token(lv, li, K, lane, t, ids, p_out);
+        for (int k = 0; k < kMaxTopK; ++k) lv[k] = S.selv[k], li[k] = S.seli[k];
+        write_token(lv, li, K, lane, t, ids, p_out);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0 && wg_count > 0) wg_base = atomicAdd(amb, wg_count);
+    __syncthreads();
+    if (S.loose && lane == 0) amb[1 + wg_base + local] = (int32_t)t;
 }
 
 // The fp64 dot product x[0..H) . w[0..H) over one wave (every lane ends with
@@ -837,7 +852,10 @@ hipError_t launch_router_prep(const float* wr, int32_t H, int32_t E, const Route
 hipError_t launch_router(const float* x, const float* xm, const float* wr, const float* bias, int64_t T, int32_t H,
                          int32_t E, const RouterScratch& rs, float* logits, hipStream_t st) {
     if (T <= 0) return hipGetLastError();
-    if (wr) launch_router_prep(wr, H, E, rs, st);
+    if (wr) {
+        const hipError_t e = launch_router_prep(wr, H, E, rs, st);
+        if (e != hipSuccess) return e;
+    }
     const int32_t Ep = (int32_t)router_padded_experts(E);
     if (!xm) {  // the input rows' multipliers and norms
         hipLaunchKernelGGL(row_scale_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, x, T, H, rs.xm, rs.xn);
@@ -856,13 +874,11 @@ hipError_t launch_topk(const float* logits, const float* x, const float* xn, con
     if (T > 0) {
         if (!amb_zeroed) hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, amb, 1, 0);
         const int ns = router_splits(T, H, E);
-        const dim3 sg((unsigned)((T + kWaves - 1) / kWaves));
-        if (E <= 512)
-            hipLaunchKernelGGL(topk_select_kernel<8>, sg, dim3(64 * kWaves), 0, st, logits, ns, T, H, E, K, xn, wnorm,
-                               amb, sel, ids, p);
-        else
-            hipLaunchKernelGGL(topk_select_kernel<kPerLane>, sg, dim3(64 * kWaves), 0, st, logits, ns, T, H, E, K, xn,
-                               wnorm, amb, sel, ids, p);
+        const int sw = T <= kSelectShort ? 4 : 16;  // waves (tokens) per workgroup
+        const dim3 sg((unsigned)((T + sw - 1) / sw));
+        auto* select = E <= 512 ? (sw == 4 ? topk_select_kernel<8, 4> : topk_select_kernel<8, 16>)
+                                : (sw == 4 ? topk_select_kernel<kPerLane, 4> : topk_select_kernel<kPerLane, 16>);
+        hipLaunchKernelGGL(select, sg, dim3(64 * sw), 0, st, logits, ns, T, H, E, K, xn, wnorm, amb, sel, ids, p);
         const unsigned grid = (unsigned)(T < 2048 ? T : 2048);  // one workgroup per listed token at a time
         if (E <= 512)
             hipLaunchKernelGGL(topk_resolve_kernel<8>, dim3(grid), dim3(256), 0, st, logits, ns, T, x, wt, bias, H, E,
