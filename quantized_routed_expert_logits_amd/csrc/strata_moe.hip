@@ -483,14 +483,30 @@ int run_streamed_experts(const strata_moe_experts* ex, strata_moe_ring* ring, co
     const int64_t G0 = ring->next, end = G0 + Eg;
     int64_t issued = G0, consumed = G0;
     const char* host = (const char*)ex->gate_up;
-    auto issue = [&](int64_t upto) -> int {  // enqueue the DMAs of entries [issued, upto)
-        for (; issued < upto; ++issued) {
-            const int s = (int)(issued % R);
-            if (ring->used_recorded[s]) HIP_TRY(hipStreamWaitEvent(ring->copy, ring->used[s], 0), "hipStreamWaitEvent");
-            HIP_TRY(hipMemcpyAsync(ring->slots + (int64_t)s * ring->slot_bytes, host + (issued - G0) * ring->slot_bytes,
-                                   ring->slot_bytes, hipMemcpyHostToDevice, ring->copy),
+    // Enqueue the DMAs of entries [issued, upto).  Consecutive entries of one
+    // batch go in one copy as far as the ring does not wrap (host blobs and
+    // slots are both one slot apart): slot-sized copies measured ~37 GB/s on
+    // the host link, copies of many slots ~56 GB/s.  A run waits for every
+    // slot's last use first; each slot gets its copied event after the run,
+    // and a run never spans two batches, so a batch's last event still covers
+    // the batch.
+    auto issue = [&](int64_t upto) -> int {
+        while (issued < upto) {
+            const int64_t batch_end = G0 + ((issued - G0) / per + 1) * per;
+            const int s0 = (int)(issued % R);
+            int64_t run_end = upto < batch_end ? upto : batch_end;
+            if (run_end > issued + (R - s0)) run_end = issued + (R - s0);  // no wrap inside a copy
+            for (int64_t k = issued; k < run_end; ++k) {
+                const int s = (int)(k % R);
+                if (ring->used_recorded[s])
+                    HIP_TRY(hipStreamWaitEvent(ring->copy, ring->used[s], 0), "hipStreamWaitEvent");
+            }
+            HIP_TRY(hipMemcpyAsync(ring->slots + (int64_t)s0 * ring->slot_bytes, host + (issued - G0) * ring->slot_bytes,
+                                   (size_t)(run_end - issued) * ring->slot_bytes, hipMemcpyHostToDevice, ring->copy),
                     "hipMemcpyAsync (expert DMA)");
-            HIP_TRY(hipEventRecord(ring->copied[s], ring->copy), "hipEventRecord");
+            for (int64_t k = issued; k < run_end; ++k)
+                HIP_TRY(hipEventRecord(ring->copied[k % R], ring->copy), "hipEventRecord");
+            issued = run_end;
         }
         return 0;
     };
