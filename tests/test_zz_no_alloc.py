@@ -30,6 +30,8 @@ def _inputs(s):
     (S.custom(T=160, H=512, E=6, K=2, I=640, fmt="q2_0", shared=True),
      S.custom(T=33, H=512, E=6, K=2, I=640, fmt="q2_0", shared=True)),
     (S.shape("stream_all_1k"), S.shape("short_256")),
+    # the second call takes the GEMV (0.6 rows per expert) after an MFMA-only call
+    (S.shape("short_256"), S.shape("window_32")),
 ], ids=lambda s: s.name)
 def test_noalloc_matches_prefill_on_two_calls(qm, big, small):
     ex = gpu_experts(big)
