@@ -486,8 +486,10 @@ int run_streamed_experts(const strata_moe_experts* ex, strata_moe_ring* ring, co
     // Enqueue the DMAs of entries [issued, upto).  Consecutive entries of one
     // batch go in one copy as far as the ring does not wrap (host blobs and
     // slots are both one slot apart): slot-sized copies measured ~37 GB/s on
-    // the host link, copies of many slots ~56 GB/s.  A run waits for every
-    // slot's last use first; each slot gets its copied event after the run,
+    // the host link, copies of many slots ~56 GB/s.  A run first waits for
+    // its slots' last use: the used events are recorded on the compute stream
+    // in entry order, so the run's last slot (the latest earlier entry among
+    // them) covers the others.  Each slot gets its copied event after the run,
     // and a run never spans two batches, so a batch's last event still covers
     // the batch.
     auto issue = [&](int64_t upto) -> int {
@@ -496,10 +498,12 @@ int run_streamed_experts(const strata_moe_experts* ex, strata_moe_ring* ring, co
             const int s0 = (int)(issued % R);
             int64_t run_end = upto < batch_end ? upto : batch_end;
             if (run_end > issued + (R - s0)) run_end = issued + (R - s0);  // no wrap inside a copy
-            for (int64_t k = issued; k < run_end; ++k) {
+            for (int64_t k = run_end - 1; k >= issued; --k) {  // the latest recorded use among the run's slots
                 const int s = (int)(k % R);
-                if (ring->used_recorded[s])
+                if (ring->used_recorded[s]) {
                     HIP_TRY(hipStreamWaitEvent(ring->copy, ring->used[s], 0), "hipStreamWaitEvent");
+                    break;
+                }
             }
             HIP_TRY(hipMemcpyAsync(ring->slots + (int64_t)s0 * ring->slot_bytes, host + (issued - G0) * ring->slot_bytes,
                                    (size_t)(run_end - issued) * ring->slot_bytes, hipMemcpyHostToDevice, ring->copy),
