@@ -22,7 +22,7 @@ Prints one JSON line on stdout (progress goes to stderr):
                bytes per second against the 8 TB/s HBM peak
   streamed     the same layer with every expert streamed from pinned host
                memory through rings of 96, 384 and 512 device slots
-  small_t      32- and 256-token chunks: ms per step, gate/up's weight GB/s,
+  small_t      32- to 256-token chunks: ms per step, gate/up's weight GB/s,
                for the layer's own kernel choice ("default") and each forced
                one (MFMA only, the GEMV, the GEMV on per-slot q8_1 inputs)
   mfma_measured  the matrix unit's rates measured on this device
@@ -76,7 +76,7 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--rings", default="96,384,512",
                     help="ring sizes (slots) of the streamed-experts measurement, comma separated ('' = skip)")
     ap.add_argument("--ring-steps", type=int, default=5, help="timed steps per ring size")
-    ap.add_argument("--small-t", default="window_32,short_256",
+    ap.add_argument("--small-t", default="window_32,window_64,window_128,short_256",
                     help="small-T workloads timed on the same experts, comma separated ('' = skip)")
     ap.add_argument("--cpu-tokens", type=int, default=4096, help="tokens in the CPU-oracle sample (0 = skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
