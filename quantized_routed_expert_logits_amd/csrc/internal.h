@@ -225,11 +225,30 @@ hipError_t launch_row_weights(const int32_t* slot, const float* p, int64_t n, fl
 // none); writes int8
 // H codes hq and scales hs.
 // n = routed rows, E = experts (bounds of the two chunk lists' lengths).
+// Optionally the MFMA kernels' epilogue also writes the down GEMM's operand
+// for their chunks, as launch_tile_h would from hq / hs: hb and hst (tiled
+// codes and scales, padding rows zero) and, if hu is non-null, each block's
+// u = -uoff * scale * (code sum) as floats [rows][offset_operand_halves / 2]
+// (hu aliases the offset operand uop, which launch_offset_rows then builds
+// in place).  With hb set, hq may be null: the MFMA kernels then write no
+// int8 H codes (the GEMV's chunks still get theirs from the GEMV launch).
+struct HTiled {
+    _Float16* hb = nullptr;
+    float* hst = nullptr;
+    float* hu = nullptr;
+    float uoff = 0.f;
+};
 hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const ChunkLists& cl, int64_t n, int32_t E,
                           const int32_t* src, const _Float16* xt, const float* xst, int64_t tiled_rows,
                           const _Float16* xa, const float* xs, int64_t T, const _Float16* xuop, const float* xum,
                           int32_t H, int32_t I, int8_t* hq, float* hs, hipStream_t st,
-                          const ExpertRange& rng = ExpertRange());
+                          const ExpertRange& rng = ExpertRange(), const HTiled& ht = HTiled());
+// The offset operand of rows [0, n) in place: hu holds each row's block
+// values u (floats, row stride offset_operand_halves(cols) / 2, as HTiled
+// writes them); each row becomes its hi/lo fp16 operand (the layout of
+// launch_prescale's uop) with its multiplier in umult, bit-identical to
+// launch_tile_h's.  Rows no kernel wrote get meaningless values.
+hipError_t launch_offset_rows(float* hu, int64_t n, int32_t cols, float* umult, hipStream_t st);
 // down: hb / hst = the tiled H codes and block scales (launch_tile_h) for
 // the 4-wave kernel (tiled_rows rows), hs = the grouped rows' block scales
 // [n][I/32] for the small-chunk kernel (which reads its codes from hb too),

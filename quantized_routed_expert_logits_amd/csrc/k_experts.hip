@@ -155,6 +155,12 @@ struct GemmArgs {
     int64_t ring0;         // nring > 0: expert e's blob is in slot (ring0 + e) % nring
     int32_t nring;
     int32_t min_rows;      // small-chunk kernel: chunks with fewer rows are the GEMV kernel's
+    // gate/up (optional): the down GEMM's operand written from the epilogue
+    // (HTiled); null: only hq / hs
+    _Float16* hbt = nullptr;
+    float* hbs = nullptr;
+    float* hu = nullptr;
+    float huoff = 0.f;
 };
 
 // Expert e's packed matrix: resident at blobs + e * stride, or in its slot of
@@ -378,16 +384,44 @@ __device__ __forceinline__ void gate_up_store(const GemmArgs& g, const Tile& tl,
         for (int ff = 0; ff < 2; ++ff)
 #pragma unroll
             for (int v = 0; v < 4; ++v) q[ff][v] = sh != 0.0f ? round_half_away(h[ff][v] / sh) : 0.0f;
-        if (r < tl.nrows) {
-            const int64_t row = tl.row0 + r;
-            int8_t* dst = g.hq + row * g.I + 64 * slab + 32 * hb + 4 * kg;
+        if (g.hbt) {  // uniform
+            // the down GEMM's operand: tile tl.tile0 + r / 16, block 2 slab + hb;
+            // this lane's values k = 16 ff + 4 kg + v sit in group 2 ff + kg / 2
+            // at positions 4 (kg & 1) + v; padding rows get zeros
+            const bool valid = r < tl.nrows;
+            const int bb = 2 * slab + hb, nq = (nbi + 3) / 4, rr = r & 15;
+            const int64_t t = tl.tile0 + (r >> 4);
+            int sum = 0;
 #pragma unroll
             for (int ff = 0; ff < 2; ++ff) {
-                const uint32_t packed = (uint32_t)(uint8_t)(int8_t)(int)q[ff][0] |
-                                        (uint32_t)(uint8_t)(int8_t)(int)q[ff][1] << 8 |
-                                        (uint32_t)(uint8_t)(int8_t)(int)q[ff][2] << 16 |
-                                        (uint32_t)(uint8_t)(int8_t)(int)q[ff][3] << 24;
-                *reinterpret_cast<uint32_t*>(dst + 16 * ff) = packed;
+                half4_t h4;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    h4[v] = valid ? (_Float16)q[ff][v] : (_Float16)0.0f;
+                    sum += valid ? (int)q[ff][v] : 0;
+                }
+                *reinterpret_cast<half4_t*>(g.hbt + ((t * nbi + bb) * 64 + 16 * (2 * ff + (kg >> 1)) + rr) * 8 +
+                                            4 * (kg & 1)) = h4;
+            }
+            sum += __shfl_xor(sum, 16);
+            sum += __shfl_xor(sum, 32);
+            if (kg == 0) {
+                g.hbs[((t * nq + (bb >> 2)) * 16 + rr) * 4 + (bb & 3)] = valid ? sh : 0.0f;
+                if (valid && g.hu) g.hu[(tl.row0 + r) * (int64_t)((nbi + 31) / 32 * 32) + bb] = -g.huoff * sh * (float)sum;
+            }
+        }
+        if (r < tl.nrows) {
+            const int64_t row = tl.row0 + r;
+            if (g.hq) {  // uniform; null when only the tiled operand is wanted
+                int8_t* dst = g.hq + row * g.I + 64 * slab + 32 * hb + 4 * kg;
+#pragma unroll
+                for (int ff = 0; ff < 2; ++ff) {
+                    const uint32_t packed = (uint32_t)(uint8_t)(int8_t)(int)q[ff][0] |
+                                            (uint32_t)(uint8_t)(int8_t)(int)q[ff][1] << 8 |
+                                            (uint32_t)(uint8_t)(int8_t)(int)q[ff][2] << 16 |
+                                            (uint32_t)(uint8_t)(int8_t)(int)q[ff][3] << 24;
+                    *reinterpret_cast<uint32_t*>(dst + 16 * ff) = packed;
+                }
             }
             if (kg == 0) g.hs[row * nbi + 2 * slab + hb] = sh;
         }
@@ -985,10 +1019,15 @@ void launch_gemms(GemmArgs g, GemmArgs gs_args, const ChunkLists& cl, int64_t n,
 hipError_t launch_gate_up(const uint8_t* blobs, int64_t stride, const ChunkLists& cl, int64_t n, int32_t E,
                           const int32_t* src, const _Float16* xt, const float* xst, int64_t tiled_rows,
                           const _Float16* xa, const float* xs, int64_t T, const _Float16* xuop, const float* xum,
-                          int32_t H, int32_t I, int8_t* hq, float* hs, hipStream_t st, const ExpertRange& rng) {
+                          int32_t H, int32_t I, int8_t* hq, float* hs, hipStream_t st, const ExpertRange& rng,
+                          const HTiled& ht) {
     const int64_t tiled_scale_bytes = tiled_rows / 16 * tiled_scale_stride(H / kBlock);
-    const GemmArgs g{blobs, stride, nullptr, nullptr, 2 * I / kSlabRows, H, src, nullptr, xt, tiled_rows, xst,
-                     tiled_scale_bytes, xuop, xum, I, H, hq, hs, nullptr, nullptr, 0, 0, 0, 0, 0};
+    GemmArgs g{blobs, stride, nullptr, nullptr, 2 * I / kSlabRows, H, src, nullptr, xt, tiled_rows, xst,
+               tiled_scale_bytes, xuop, xum, I, H, hq, hs, nullptr, nullptr, 0, 0, 0, 0, 0};
+    g.hbt = ht.hb;
+    g.hbs = ht.hst;
+    g.hu = ht.hu;
+    g.huoff = ht.uoff;
     GemmArgs gs = g;
     gs.act = xa;
     gs.act_rows = T;

@@ -337,6 +337,47 @@ __global__ void __launch_bounds__(256) tile_h_kernel(const int8_t* __restrict__ 
         }
 }
 
+// launch_offset_rows: two rows per wave, lane 32 h + j of row 2 w + h takes
+// blocks j, j + 32, ...: the row's largest |u| (a shuffle over the 32 lanes),
+// its multiplier, then each block's hi/lo written over the row's floats
+// (every lane's floats are in registers before the first store).
+__global__ void __launch_bounds__(256) offset_rows_kernel(float* __restrict__ hu, int64_t n, int32_t nb,
+                                                          float* __restrict__ umult) {
+    const int lane = threadIdx.x & 63, j = lane & 31;
+    const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2 + (lane >> 5);
+    const int nch = (nb + 31) / 32;
+    float* ur = hu + row * (int64_t)nch * 32;
+    float u[kMaxOffsetChunks];
+    float umax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kMaxOffsetChunks; ++c) {
+        const int b = 32 * c + j;
+        u[c] = row < n && c < nch && b < nb ? ur[b] : 0.0f;
+        umax = fmaxf(umax, fabsf(u[c]));
+    }
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) umax = fmaxf(umax, __shfl_xor(umax, off));
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (row >= n) return;
+    int eu = 0;
+    if (umax > 0.0f) frexpf(umax, &eu);
+    eu = eu < -100 ? -100 : eu;
+    const float dn = ldexpf(1.0f, -eu);
+    if (j == 0) umult[row] = ldexpf(1.0f, eu);
+    _Float16* dst = reinterpret_cast<_Float16*>(ur);
+#pragma unroll
+    for (int c = 0; c < kMaxOffsetChunks; ++c) {
+        const int b = 32 * c + j;
+        if (c < nch) {
+            _Float16 h, l;
+            split_hi_lo(u[c] * dn, h, l);  // exact: a power-of-two scaling; padding blocks: zero
+            dst[16 * (b >> 3) + (b & 7)] = h;
+            dst[16 * (b >> 3) + 8 + (b & 7)] = l;
+        }
+    }
+}
+
 // The 4-wave gate/up kernel's operand in the tiled layout: tile t of the
 // tile table (if its chunk is big) holds grouped rows trows[t], each the
 // token src[row]; its int8 codes become fp16 (exact) in [tile][block][group
@@ -557,6 +598,13 @@ hipError_t launch_tile_h(const int8_t* q, const float* s, const ChunkLists& cl, 
     if (tiles_cap > 0)
         hipLaunchKernelGGL(tile_h_kernel, dim3((unsigned)tiles_cap), dim3(256), tile_h_lds_bytes(cols), st, q, s,
                            cl.trows, cl.sched + 2, cols, uoff, out, sout, uop, umult, first_tile, rng.e0, rng.e1);
+    return hipGetLastError();
+}
+
+hipError_t launch_offset_rows(float* hu, int64_t n, int32_t cols, float* umult, hipStream_t st) {
+    if (n > 0)
+        hipLaunchKernelGGL(offset_rows_kernel, dim3((unsigned)((n + 7) / 8)), dim3(256), 0, st, hu, n, cols / kBlock,
+                           umult);
     return hipGetLastError();
 }
 

@@ -630,17 +630,21 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     all.max_rows = T;
     // the MFMA down kernels' tiled H: not needed where every chunk is the GEMV's
     const bool mfma_down = all.small_min_rows == 0 || T >= all.small_min_rows;
+    // the MFMA gate/up kernels' epilogue writes the down GEMM's tiled operand
+    // and the offset pass's block values of their chunks' rows
+    HTiled ht;
+    if (mfma_down) ht = HTiled{b.hb, b.hst, huop ? reinterpret_cast<float*>(huop) : nullptr, code_offset(ex)};
     tm.begin(kGateUp);
+    // (their int8 H codes only where the caller keeps the intermediates)
     HIP_TRY(launch_gate_up((const uint8_t*)ex->gate_up, ex->gate_up_stride, cl, n, Eg, b.src, b.xt, b.xst,
-                           tiled_rows_cap(n, Eg), b.xa, b.xs, T, xuop, b.xum, H, I, b.hq, b.hs, st, all),
+                           tiled_rows_cap(n, Eg), b.xa, b.xs, T, xuop, b.xum, H, I, mfma_down && !keep ? nullptr : b.hq,
+                           b.hs, st, all, ht),
             "gate/up launch");
     TRY(launch_gemv_step(ex, true, (const uint8_t*)ex->gate_up, ex->gate_up_stride, b, cl, T, n, Eg, all, st));
     tm.end(kGateUp);
     tm.begin(kTileH);
-    if (mfma_down)
-        HIP_TRY(launch_tile_h(b.hq, b.hs, cl, tiled_rows_cap(n, Eg) / 16, I, code_offset(ex), b.hb, b.hst, huop,
-                              b.hum, st),
-                "tile launch");
+    if (mfma_down && huop)
+        HIP_TRY(launch_offset_rows(reinterpret_cast<float*>(huop), n, I, b.hum, st), "offset operand launch");
     tm.end(kTileH);
     tm.begin(kDown);
     HIP_TRY(launch_down((const uint8_t*)ex->down, ex->down_stride, cl, n, Eg, b.src, b.prow, b.hb, b.hst,
