@@ -290,6 +290,23 @@ def test_layer_all_intermediates(qm, s):
     assert rel_err(g["out"], ref["y"]) <= Y_TOL
 
 
+@pytest.mark.parametrize("s", LAYER_SHAPES, ids=lambda s: s.name)
+def test_layer_down_operand_from_epilogue_matches_stage_path(qm, s):
+    # In the layer the gate/up epilogue writes the down GEMM's tiled fp16
+    # operand and block values of the offset pass itself; the single-step
+    # down entry builds both from the int8 H codes.  Same bits either way,
+    # and the plain entry (which writes no int8 H codes) matches the debug
+    # entry (which does).
+    x, wr = S.activations(s), S.router_weight(s)
+    ex = gpu_experts(s)
+    out = torch.empty((s.T, s.H), dtype=torch.float32, device="cuda")
+    d = qm.strata_moe_prefill_debug(_t(x), _t(wr), ex, s.K, out)
+    y = qm.strata_moe_down(d["qh"], d["sh"], d["offsets"], d["src"], d["slot"], d["p"], ex, torch.empty_like(out))
+    assert torch.equal(y, out)
+    y2 = qm.strata_moe_prefill(_t(x), _t(wr), ex, s.K, torch.empty_like(out))
+    assert torch.equal(y2, out)
+
+
 SHARED_SHAPES = [S.custom(T=200, H=256, E=10, K=3, I=128, shared=True),
                  S.custom(T=160, H=512, E=6, K=2, I=640, fmt="q2_0", shared=True),
                  S.custom(T=129, H=256, E=8, K=4, I=64, skewed=True, shared=True),
