@@ -337,45 +337,48 @@ __global__ void __launch_bounds__(256) tile_h_kernel(const int8_t* __restrict__ 
         }
 }
 
-// launch_offset_rows: two rows per wave, lane 32 h + j of row 2 w + h takes
-// blocks j, j + 32, ...: the row's largest |u| (a shuffle over the 32 lanes),
-// its multiplier, then each block's hi/lo written over the row's floats
-// (every lane's floats are in registers before the first store).
+// launch_offset_rows: L lanes per row (L = 4 nch rounded up to a power of
+// two), lane G of a row takes value group G (blocks 8G .. 8G + 7): its 8
+// floats in, the row's largest |u| (a shuffle over the L lanes), its
+// multiplier, then the group's hi and lo halves written over the same 32
+// bytes it read.
 __global__ void __launch_bounds__(256) offset_rows_kernel(float* __restrict__ hu, int64_t n, int32_t nb,
                                                           float* __restrict__ umult) {
-    const int lane = threadIdx.x & 63, j = lane & 31;
-    const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2 + (lane >> 5);
-    const int nch = (nb + 31) / 32;
-    float* ur = hu + row * (int64_t)nch * 32;
-    float u[kMaxOffsetChunks];
+    const int nch = (nb + 31) / 32, L = nch == 1 ? 4 : nch == 2 ? 8 : 16;
+    const int lane = threadIdx.x & 63, G = lane & (L - 1);
+    const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / L) + lane / L;
+    const bool mine = row < n && G < 4 * nch;
+    float* ug = hu + row * (int64_t)nch * 32 + 8 * G;
+    float u[8];
+    if (mine) {
+        const float4 u0 = reinterpret_cast<const float4*>(ug)[0], u1 = reinterpret_cast<const float4*>(ug)[1];
+        u[0] = u0.x; u[1] = u0.y; u[2] = u0.z; u[3] = u0.w;
+        u[4] = u1.x; u[5] = u1.y; u[6] = u1.z; u[7] = u1.w;
+    }
     float umax = 0.0f;
 #pragma unroll
-    for (int c = 0; c < kMaxOffsetChunks; ++c) {
-        const int b = 32 * c + j;
-        u[c] = row < n && c < nch && b < nb ? ur[b] : 0.0f;
-        umax = fmaxf(umax, fabsf(u[c]));
+    for (int i = 0; i < 8; ++i) {
+        if (!mine || 8 * G + i >= nb) u[i] = 0.0f;  // padding blocks: zero operand
+        umax = fmaxf(umax, fabsf(u[i]));
     }
-#pragma unroll
-    for (int off = 1; off < 32; off <<= 1) umax = fmaxf(umax, __shfl_xor(umax, off));
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    if (row >= n) return;
+    for (int off = 1; off < L; off <<= 1) umax = fmaxf(umax, __shfl_xor(umax, off));
+    if (!mine) return;
     int eu = 0;
     if (umax > 0.0f) frexpf(umax, &eu);
     eu = eu < -100 ? -100 : eu;
     const float dn = ldexpf(1.0f, -eu);
-    if (j == 0) umult[row] = ldexpf(1.0f, eu);
-    _Float16* dst = reinterpret_cast<_Float16*>(ur);
+    if (G == 0) umult[row] = ldexpf(1.0f, eu);
+    half8_t hi, lo;
 #pragma unroll
-    for (int c = 0; c < kMaxOffsetChunks; ++c) {
-        const int b = 32 * c + j;
-        if (c < nch) {
-            _Float16 h, l;
-            split_hi_lo(u[c] * dn, h, l);  // exact: a power-of-two scaling; padding blocks: zero
-            dst[16 * (b >> 3) + (b & 7)] = h;
-            dst[16 * (b >> 3) + 8 + (b & 7)] = l;
-        }
+    for (int i = 0; i < 8; ++i) {
+        _Float16 h, l;
+        split_hi_lo(u[i] * dn, h, l);  // exact: a power-of-two scaling
+        hi[i] = h;
+        lo[i] = l;
     }
+    half8_t* dst = reinterpret_cast<half8_t*>(ug);
+    dst[0] = hi;
+    dst[1] = lo;
 }
 
 // The 4-wave gate/up kernel's operand in the tiled layout: tile t of the
@@ -603,8 +606,11 @@ hipError_t launch_tile_h(const int8_t* q, const float* s, const ChunkLists& cl, 
 
 hipError_t launch_offset_rows(float* hu, int64_t n, int32_t cols, float* umult, hipStream_t st) {
     if (n > 0)
-        hipLaunchKernelGGL(offset_rows_kernel, dim3((unsigned)((n + 7) / 8)), dim3(256), 0, st, hu, n, cols / kBlock,
-                           umult);
+    {
+        const int nch = (cols / kBlock + 31) / 32, L = nch == 1 ? 4 : nch == 2 ? 8 : 16, rows = 4 * (64 / L);
+        hipLaunchKernelGGL(offset_rows_kernel, dim3((unsigned)((n + rows - 1) / rows)), dim3(256), 0, st, hu, n,
+                           cols / kBlock, umult);
+    }
     return hipGetLastError();
 }
 
