@@ -12,7 +12,6 @@ constexpr int kChunkRows = 192;   // grouped rows per GEMM work item (12 tiles o
 constexpr int kGroupChunk = 2048; // (token, k) pairs per grouping chunk
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
-constexpr int kSelWords = kMaxTopK + 2;  // a near-tie token's fp32 ranking, kept for the resolve pass
 constexpr int kSlabRows = 128;    // weight rows per GEMM work item (8 MFMA fragments of 16)
 constexpr int kRecordCodeBytes = 1024;                    // one slab's codes of one 32-wide block
 constexpr int kRecordBytes = kRecordCodeBytes + 256;      // ... plus its 128 fp16 scales
@@ -199,12 +198,11 @@ inline RouterPrepared router_prepared_layout(int32_t H, int32_t E) {
     return r;
 }
 // xn: the input rows' Euclidean norms, wnorm: the router columns' largest
-// (the near-tie window's error bound).  amb: scratch of T+1 ints (the list of tokens with a near-tie), amb[0] set to
-// 0 here unless the caller already did (amb_zeroed); sel: scratch of
-// T * kSelWords ints; wt from the router scratch.
+// (the near-tie window's error bound); wt from the router scratch (the fp64
+// re-score of near-tie tokens reads expert columns as rows of it).
 hipError_t launch_topk(const float* logits, const float* x, const float* xn, const float* wt, const float* wnorm,
-                       const float* bias, int64_t T, int32_t H, int32_t E, int32_t K, int32_t* amb, int32_t* sel,
-                       int32_t* ids, float* p, hipStream_t st, bool amb_zeroed = false);
+                       const float* bias, int64_t T, int32_t H, int32_t E, int32_t K, int32_t* ids, float* p,
+                       hipStream_t st);
 
 // The shared expert's pair slot: ids / p [T][K] copied to gids / gp [T][K+1]
 // with slot K = (E, sigmoid(x[t] . wg)).  x, wg 16-byte aligned; H % 128 == 0.

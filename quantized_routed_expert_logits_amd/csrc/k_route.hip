@@ -588,59 +588,6 @@ __device__ __forceinline__ void write_token(const V (&lv)[kMaxTopK], const int (
     }
 }
 
-// One wave per token: tokens without a near-tie are finished here; the others
-// are appended to `amb` (amb[0] = count, then token ids) for the resolve pass,
-// with their fp32 ranking in `sel` (kSelWords per token: the ranked expert
-// ids, the loose-rank mask, the K-th value), which that pass then reuses.  A
-// workgroup of kSelectWaves tokens counts its near-tie tokens in LDS and
-// takes their list places with one atomic on amb[0]: one atomic per token
-// measured 25 us of the pass's 47 at 8192 tokens (the counter serializes
-// them).
-// Short calls (up to kSelectShort tokens) keep 4-wave workgroups: there the
-// tokens spread over more CUs, and the list has few entries anyway.
-constexpr int kWaves = 4;
-constexpr int kSelectShort = 256;
-template <int kSlots, int kSelectWaves>
-__global__ void __launch_bounds__(64 * kSelectWaves) topk_select_kernel(const float* __restrict__ logits, int nsplit,
-                                                                        int64_t T, int32_t H, int32_t E, int32_t K,
-                                                                        const float* __restrict__ xn,
-                                                                        const float* __restrict__ wnorm,
-                                                                        int32_t* __restrict__ amb,
-                                                                        int32_t* __restrict__ sel,
-                                                                        int32_t* __restrict__ ids,
-                                                                        float* __restrict__ p_out) {
-    __shared__ int wg_count, wg_base;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * kSelectWaves + wave;
-    if (threadIdx.x == 0) wg_count = 0;
-    __syncthreads();
-    const bool live = t < T;  // every wave meets the barriers below
-    Selection<kSlots> S;
-    S.loose = 0;
-    if (live) select_token(logits + t * E, nsplit, T * E, E, K, tie_coeff(H) * xn[t] * *wnorm, lane, S);
-    int local = 0;
-    if (S.loose) {
-        int word = 0;
-#pragma unroll
-        for (int k = 0; k < kMaxTopK; ++k)
-            if (lane == k) word = S.seli[k];
-        if (lane == kMaxTopK) word = (int)S.loose;
-        if (lane == kMaxTopK + 1) word = __builtin_bit_cast(int, S.vK);
-        if (lane < kSelWords) sel[t * kSelWords + lane] = word;
-        if (lane == 0) local = atomicAdd(&wg_count, 1);  // LDS
-    } else if (live) {
-        float lv[kMaxTopK];
-        int li[kMaxTopK];
-#pragma unroll
-        for (int k = 0; k < kMaxTopK; ++k) lv[k] = S.selv[k], li[k] = S.seli[k];
-        write_token(lv, li, K, lane, t, ids, p_out);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0 && wg_count > 0) wg_base = atomicAdd(amb, wg_count);
-    __syncthreads();
-    if (S.loose && lane == 0) amb[1 + wg_base + local] = (int32_t)t;
-}
-
 // The fp64 dot product x[0..H) . w[0..H) over one wave (every lane ends with
 // the same sum).  Lane l takes 4 consecutive elements of every 256, up to
 // kDotBatch such groups of loads in flight at once; a tail of H % 256
@@ -708,133 +655,134 @@ __device__ __forceinline__ void wave_dot2_fp64(const float* __restrict__ x, cons
     v2 = wave_sum(a2);
 }
 
-// Listed tokens are taken one per workgroup where the list is short (at most
-// kResolveWide tokens: short prompts wait for one token's latency), else one
-// per wave (a long list fills the chip either way, and four waves per token
-// would not all be resident).  Candidates: every expert within delta below
-// the K-th value (this includes all K selected).  Selected ranks outside
-// every near-tie keep their fp32 value: each is at least delta away from any
-// value that is re-scored, so the merged order is the exact one.  The others
-// are re-scored as wave-wide fp64 dot products, two at a time; with a
-// workgroup per token its 4 waves take every fourth pair of the list, the
-// values meet in LDS and wave 0 re-ranks the candidates.  Each value comes
-// from the same dot-product routine whichever wave computes it.  Lane l
-// keeps the candidates among experts l, l + 64, ... in registers.
-constexpr int kResolveWide = 512;
-template <int kSlots>
-__global__ void __launch_bounds__(256) topk_resolve_kernel(const float* __restrict__ logits, int nsplit,
-                                                           int64_t T, const float* __restrict__ x,
-                                                           const float* __restrict__ wt,
-                                                           const float* __restrict__ bias, int32_t H, int32_t E,
-                                                           int32_t K, const float* __restrict__ xn,
-                                                           const float* __restrict__ wnorm,
-                                                           const int32_t* __restrict__ amb,
-                                                           const int32_t* __restrict__ sel,
-                                                           int32_t* __restrict__ ids, float* __restrict__ p_out) {
-    __shared__ double rescored[kMaxExperts];
+// One top-K pass per token, in fp32 first: the ranking of the token's
+// summed logits and the near-tie window.  A token whose ranks are all
+// further apart than the window is finished at once.  Otherwise every
+// expert within the window below the K-th value (this includes all K
+// selected) is a candidate; selected ranks outside every near-tie keep their
+// fp32 value (each is at least the window away from any value that is
+// re-scored, so the merged order is the exact one), and the others are
+// re-scored as wave-wide fp64 dot products of the input row and the
+// expert's weight column, two at a time.  Lane l keeps the candidates among
+// experts l, l + 64, ... in registers.
+// kWide (short calls, up to kSelectShort tokens): a workgroup of 4 waves per
+// token; every wave ranks the token (the same bits), the waves take every
+// fourth pair of the re-score list, the values meet in LDS and wave 0
+// re-ranks: a short prompt waits for one token's latency.  Otherwise a wave
+// per token, kSelectWaves tokens per workgroup, each wave re-scoring its own
+// token's list.  Each value comes from the same dot-product routine
+// whichever wave computes it.
+constexpr int kWaves = 4;
+constexpr int kSelectShort = 256;
+template <int kSlots, int kSelectWaves, bool kWide>
+__global__ void __launch_bounds__(64 * kSelectWaves) topk_kernel(const float* __restrict__ logits, int nsplit,
+                                                                int64_t T, const float* __restrict__ x,
+                                                                const float* __restrict__ wt,
+                                                                const float* __restrict__ bias, int32_t H, int32_t E,
+                                                                int32_t K, const float* __restrict__ xn,
+                                                                const float* __restrict__ wnorm,
+                                                                int32_t* __restrict__ ids, float* __restrict__ p_out) {
+    static_assert(!kWide || kSelectWaves == kWaves, "a workgroup of kWaves waves per token");
+    __shared__ double rescored[kWide ? kMaxExperts : 1];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int n = amb[0];
-    const bool wide = n <= kResolveWide;  // uniform over the grid
-    const int per = wide ? 1 : kWaves;    // tokens per workgroup and turn
-    for (int it0 = blockIdx.x * per; it0 < n; it0 += gridDim.x * per) {  // uniform over the workgroup
-        const int it = wide ? it0 : it0 + wave;
-        if (it >= n) continue;  // a wave without a token this turn (one per wave only: no barrier there)
-        const int64_t t = amb[1 + it];
-        Selection<kSlots> S;  // the select pass's ranking of this token, and its logits
-        load_logits(logits + t * E, nsplit, T * E, E, lane, S);
-        const int32_t* sm = sel + t * kSelWords;
-#pragma unroll
-        for (int k = 0; k < kMaxTopK; ++k) S.seli[k] = sm[k];
-        S.loose = (uint32_t)sm[kMaxTopK];
-        S.vK = __builtin_bit_cast(float, sm[kMaxTopK + 1]);
-        S.delta = tie_window(S.vK, tie_coeff(H) * xn[t] * *wnorm);  // as the select pass took it
-        const float thr = S.vK - S.delta;
-        double cv[kSlots];
-        uint32_t cand = 0, todo = 0;
-#pragma unroll
-        for (int i = 0; i < kSlots; ++i) {
-            const int e = lane + 64 * i;
-            const bool c = e < E && S.v[i] >= thr;
-            bool stable = false;
-#pragma unroll
-            for (int k = 0; k < kMaxTopK; ++k)
-                if (k < K && !((S.loose >> k) & 1u) && S.seli[k] == e) stable = true;
-            cv[i] = (double)S.v[i];
-            cand |= (uint32_t)c << i;
-            todo |= (uint32_t)(c && !stable) << i;
-        }
-        const float* xr = x + t * H;
-        // the experts to re-score in list order, two per pair; with a
-        // workgroup per token this wave takes pairs wave, wave + 4, ...
-        uint64_t m[kSlots];
-#pragma unroll
-        for (int i = 0; i < kSlots; ++i) m[i] = __ballot((todo >> i) & 1u);
-        for (int pair = 0;; ++pair) {
-            int e1 = -1, e2 = -1;
-#pragma unroll
-            for (int i = 0; i < kSlots; ++i) {
-                if (e1 < 0 && m[i]) {
-                    e1 = (__ffsll((unsigned long long)m[i]) - 1) + 64 * i;
-                    m[i] &= m[i] - 1ull;
-                }
-                if (e1 >= 0 && e2 < 0 && m[i]) {
-                    e2 = (__ffsll((unsigned long long)m[i]) - 1) + 64 * i;
-                    m[i] &= m[i] - 1ull;
-                }
-            }
-            if (e1 < 0) break;
-            if (wide && (pair & (kWaves - 1)) != wave) continue;
-            double v1, v2 = 0.0;
-            if (e2 >= 0)
-                wave_dot2_fp64(xr, wt + (int64_t)e1 * H, wt + (int64_t)e2 * H, H, lane, v1, v2);
-            else
-                v1 = wave_dot_fp64(xr, wt + (int64_t)e1 * H, H, lane);
-            if (bias) {
-                v1 += (double)bias[e1];
-                if (e2 >= 0) v2 += (double)bias[e2];
-            }
-            if (wide) {
-                if (lane == 0) {
-                    rescored[e1] = v1;
-                    if (e2 >= 0) rescored[e2] = v2;
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < kSlots; ++i) {
-                    const int e = lane + 64 * i;
-                    cv[i] = e == e1 ? v1 : e == e2 ? v2 : cv[i];
-                }
-            }
-        }
-        if (wide) {
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < kSlots; ++i)
-                if ((todo >> i) & 1u) cv[i] = rescored[lane + 64 * i];
-        }
-        if (!wide || wave == 0) {
-            double lv[kMaxTopK];
+    const int64_t t = kWide ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * kSelectWaves + wave;
+    if (t >= T) return;  // kWide: uniform over the workgroup; otherwise no barrier follows
+    Selection<kSlots> S;
+    select_token(logits + t * E, nsplit, T * E, E, K, tie_coeff(H) * xn[t] * *wnorm, lane, S);
+    if (!S.loose) {  // kWide: the same for every wave of the workgroup
+        if (!kWide || wave == 0) {
+            float lv[kMaxTopK];
             int li[kMaxTopK];
-            uint32_t tk = 0;
 #pragma unroll
-            for (int k = 0; k < kMaxTopK; ++k) {
-                lv[k] = -DBL_MAX;
-                li[k] = INT_MAX;
-                if (k >= K) continue;
-                Best<double> b{-DBL_MAX, INT_MAX};
-#pragma unroll
-                for (int i = 0; i < kSlots; ++i)
-                    if (((cand & ~tk) >> i) & 1u) take_better(b, cv[i], lane + 64 * i);
-                b = wave_best(b);
-                const int bi = b.i;
-                lv[k] = b.v;
-                li[k] = bi;
-                if (bi < E && (bi & 63) == lane) tk |= 1u << (bi >> 6);
-            }
+            for (int k = 0; k < kMaxTopK; ++k) lv[k] = S.selv[k], li[k] = S.seli[k];
             write_token(lv, li, K, lane, t, ids, p_out);
         }
-        if (wide) __syncthreads();  // rescored is free for the next token
+        return;
     }
+    const float thr = S.vK - S.delta;
+    double cv[kSlots];
+    uint32_t cand = 0, todo = 0;
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i) {
+        const int e = lane + 64 * i;
+        const bool c = e < E && S.v[i] >= thr;
+        bool stable = false;
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k)
+            if (k < K && !((S.loose >> k) & 1u) && S.seli[k] == e) stable = true;
+        cv[i] = (double)S.v[i];
+        cand |= (uint32_t)c << i;
+        todo |= (uint32_t)(c && !stable) << i;
+    }
+    const float* xr = x + t * H;
+    // the experts to re-score in list order, two per pair; with a workgroup
+    // per token this wave takes pairs wave, wave + 4, ...
+    uint64_t m[kSlots];
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i) m[i] = __ballot((todo >> i) & 1u);
+    for (int pair = 0;; ++pair) {
+        int e1 = -1, e2 = -1;
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i) {
+            if (e1 < 0 && m[i]) {
+                e1 = (__ffsll((unsigned long long)m[i]) - 1) + 64 * i;
+                m[i] &= m[i] - 1ull;
+            }
+            if (e1 >= 0 && e2 < 0 && m[i]) {
+                e2 = (__ffsll((unsigned long long)m[i]) - 1) + 64 * i;
+                m[i] &= m[i] - 1ull;
+            }
+        }
+        if (e1 < 0) break;
+        if (kWide && (pair & (kWaves - 1)) != wave) continue;
+        double v1, v2 = 0.0;
+        if (e2 >= 0)
+            wave_dot2_fp64(xr, wt + (int64_t)e1 * H, wt + (int64_t)e2 * H, H, lane, v1, v2);
+        else
+            v1 = wave_dot_fp64(xr, wt + (int64_t)e1 * H, H, lane);
+        if (bias) {
+            v1 += (double)bias[e1];
+            if (e2 >= 0) v2 += (double)bias[e2];
+        }
+        if (kWide) {
+            if (lane == 0) {
+                rescored[e1] = v1;
+                if (e2 >= 0) rescored[e2] = v2;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kSlots; ++i) {
+                const int e = lane + 64 * i;
+                cv[i] = e == e1 ? v1 : e == e2 ? v2 : cv[i];
+            }
+        }
+    }
+    if (kWide) {
+        __syncthreads();
+        if (wave != 0) return;
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i)
+            if ((todo >> i) & 1u) cv[i] = rescored[lane + 64 * i];
+    }
+    double lv[kMaxTopK];
+    int li[kMaxTopK];
+    uint32_t tk = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) {
+        lv[k] = -DBL_MAX;
+        li[k] = INT_MAX;
+        if (k >= K) continue;
+        Best<double> b{-DBL_MAX, INT_MAX};
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i)
+            if (((cand & ~tk) >> i) & 1u) take_better(b, cv[i], lane + 64 * i);
+        b = wave_best(b);
+        const int bi = b.i;
+        lv[k] = b.v;
+        li[k] = bi;
+        if (bi < E && (bi & 63) == lane) tk |= 1u << (bi >> 6);
+    }
+    write_token(lv, li, K, lane, t, ids, p_out);
 }
 
 }  // namespace
@@ -869,23 +817,20 @@ hipError_t launch_router(const float* x, const float* xm, const float* wr, const
 }
 
 hipError_t launch_topk(const float* logits, const float* x, const float* xn, const float* wt, const float* wnorm,
-                       const float* bias, int64_t T, int32_t H, int32_t E, int32_t K, int32_t* amb, int32_t* sel,
-                       int32_t* ids, float* p, hipStream_t st, bool amb_zeroed) {
+                       const float* bias, int64_t T, int32_t H, int32_t E, int32_t K, int32_t* ids, float* p,
+                       hipStream_t st) {
     if (T > 0) {
-        if (!amb_zeroed) hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, amb, 1, 0);
         const int ns = router_splits(T, H, E);
-        const int sw = T <= kSelectShort ? 4 : 16;  // waves (tokens) per workgroup
-        const dim3 sg((unsigned)((T + sw - 1) / sw));
-        auto* select = E <= 512 ? (sw == 4 ? topk_select_kernel<8, 4> : topk_select_kernel<8, 16>)
-                                : (sw == 4 ? topk_select_kernel<kPerLane, 4> : topk_select_kernel<kPerLane, 16>);
-        hipLaunchKernelGGL(select, sg, dim3(64 * sw), 0, st, logits, ns, T, H, E, K, xn, wnorm, amb, sel, ids, p);
-        const unsigned grid = (unsigned)(T < 2048 ? T : 2048);  // one workgroup per listed token at a time
-        if (E <= 512)
-            hipLaunchKernelGGL(topk_resolve_kernel<8>, dim3(grid), dim3(256), 0, st, logits, ns, T, x, wt, bias, H, E,
-                               K, xn, wnorm, amb, sel, ids, p);
-        else
-            hipLaunchKernelGGL(topk_resolve_kernel<kPerLane>, dim3(grid), dim3(256), 0, st, logits, ns, T, x, wt, bias,
-                               H, E, K, xn, wnorm, amb, sel, ids, p);
+        if (T <= kSelectShort) {  // a workgroup per token
+            auto* k = E <= 512 ? topk_kernel<8, kWaves, true> : topk_kernel<kPerLane, kWaves, true>;
+            hipLaunchKernelGGL(k, dim3((unsigned)T), dim3(64 * kWaves), 0, st, logits, ns, T, x, wt, bias, H, E, K,
+                               xn, wnorm, ids, p);
+        } else {  // a wave per token, 4 per workgroup (16 measured 72 vs 60 us at 8192 tokens)
+            constexpr int kw = 4;
+            auto* k = E <= 512 ? topk_kernel<8, kw, false> : topk_kernel<kPerLane, kw, false>;
+            hipLaunchKernelGGL(k, dim3((unsigned)((T + kw - 1) / kw)), dim3(64 * kw), 0, st, logits, ns, T, x, wt,
+                               bias, H, E, K, xn, wnorm, ids, p);
+        }
     }
     return hipGetLastError();
 }

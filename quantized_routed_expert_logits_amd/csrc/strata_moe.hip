@@ -139,8 +139,6 @@ struct Buffers {
     float* wm;
     float* wnorm;
     float* pmax;
-    int32_t* amb;
-    int32_t* sel;
     int32_t* ids;   // the routing: [T][K]
     float* p;
     int32_t* gids;  // the grouped pairs: [T][K+1] with a shared expert, else ids / p
@@ -179,7 +177,7 @@ struct Buffers {
 };
 
 struct Offsets {
-    size_t logits, wt, wb, wm, wnorm, pmax, amb, sel, ids, p, gids, gp, xq, xs, xa, xt, xst, xe, xn, xuop, xum, hist, base, offsets, tiles, ntiles, first, err, src, slot, prow, hq, hs,
+    size_t logits, wt, wb, wm, wnorm, pmax, ids, p, gids, gp, xq, xs, xa, xt, xst, xe, xn, xuop, xum, hist, base, offsets, tiles, ntiles, first, err, src, slot, prow, hq, hs,
         trows, hb, hst, huop, hum, dm, sq, ss, ssum, total;
     int64_t tiles_cap;
 };
@@ -201,8 +199,6 @@ Offsets plan(int64_t T, int32_t K, int32_t E, int32_t H, int32_t I, bool shared,
     o.wm = L.take<float>(router_padded_experts(Er));
     o.wnorm = L.take<float>(1);
     o.pmax = L.take<float>((int64_t)((H + 31) / 32) * Er);
-    o.amb = L.take<int32_t>(T + 1);
-    o.sel = L.take<int32_t>(T * kSelWords);
     o.ids = L.take<int32_t>(nr);
     o.p = L.take<float>(nr);
     o.gids = shared ? L.take<int32_t>(n) : o.ids;
@@ -249,8 +245,6 @@ Buffers carve(char* ws, const Offsets& o) {
     b.wm = (float*)(ws + o.wm);
     b.wnorm = (float*)(ws + o.wnorm);
     b.pmax = (float*)(ws + o.pmax);
-    b.amb = (int32_t*)(ws + o.amb);
-    b.sel = (int32_t*)(ws + o.sel);
     b.ids = (int32_t*)(ws + o.ids);
     b.p = (float*)(ws + o.p);
     b.gids = (int32_t*)(ws + o.gids);
@@ -576,11 +570,11 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
     CallTimer tm(st);
     tm.begin(kQuantize);
     // one pass over x: int8 codes and scales, their fp16 copy, row multipliers and
-    // offset operand; it also clears the top-K near-tie count and the id error flag
+    // offset operand; it also clears the id error flag
     _Float16* xuop = has_offset(ex) ? b.xuop : nullptr;
     _Float16* huop = has_offset(ex) ? b.huop : nullptr;
     HIP_TRY(launch_quantize_prescale(x, T, H, code_offset(ex), b.xq, b.xs, b.xa, b.xe, b.xn, xuop, b.xum, st,
-                                     ZeroWords{{b.amb, b.err}}),
+                                     ZeroWords{{b.err, nullptr}}),
             "quantize launch");
     tm.end(kQuantize);
     tm.begin(kRouter);
@@ -597,8 +591,7 @@ int run_layer(const float* x, const float* wr, const strata_moe_experts* ex, int
             "router launch");
     tm.end(kRouter);
     tm.begin(kTopK);
-    HIP_TRY(launch_topk(b.logits, x, b.xn, rs.wt, rs.wnorm, ex->router_bias, T, H, E, K, b.amb, b.sel, b.ids, b.p, st,
-                        true),
+    HIP_TRY(launch_topk(b.logits, x, b.xn, rs.wt, rs.wnorm, ex->router_bias, T, H, E, K, b.ids, b.p, st),
             "top-K launch");
     if (shared)
         HIP_TRY(launch_shared_slot(x, ex->shared_gate, b.ids, b.p, T, H, K, E, b.gids, b.gp, st), "shared gate launch");
@@ -965,7 +958,6 @@ int strata_moe_route(const float* x, const float* router_w, const float* bias, i
     hipStream_t st = (hipStream_t)stream;
     Layout L;
     const size_t lo = L.take<float>(router_logit_floats(T, H, E)), o_wt = L.take<float>((int64_t)E * H);
-    const size_t o_amb = L.take<int32_t>(T + 1), o_sel = L.take<int32_t>(T * kSelWords);
     const size_t o_wb = L.take<_Float16>(router_padded_experts(E) * H * 2);
     const size_t o_wm = L.take<float>(router_padded_experts(E)), o_xm = L.take<float>(T);
     const size_t o_wn = L.take<float>(1), o_xn = L.take<float>(T);
@@ -977,9 +969,7 @@ int strata_moe_route(const float* x, const float* router_w, const float* bias, i
     const RouterScratch rs{wt, (_Float16*)(ws + o_wb), (float*)(ws + o_wm), (float*)(ws + o_wn), (float*)(ws + o_xm),
                            (float*)(ws + o_xn), (float*)(ws + o_pm)};
     HIP_TRY(launch_router(x, nullptr, router_w, bias, T, H, E, rs, logits, st), "router launch");
-    HIP_TRY(launch_topk(logits, x, rs.xn, wt, rs.wnorm, bias, T, H, E, K, (int32_t*)(ws + o_amb), (int32_t*)(ws + o_sel),
-                        ids, p, st),
-            "top-K launch");
+    HIP_TRY(launch_topk(logits, x, rs.xn, wt, rs.wnorm, bias, T, H, E, K, ids, p, st), "top-K launch");
     return 0;
 }
 
