@@ -154,7 +154,7 @@ struct RouterScratch {
 // The router GEMM splits the reduction over H into router_splits() ranges
 // when a chunk is short (too few workgroups otherwise); logits then holds
 // that many partial [T][E] arrays, which the top-K adds in order.
-constexpr int kMaxRouterSplits = 4;
+constexpr int kMaxRouterSplits = 8;
 inline int router_splits(int64_t T, int32_t H, int32_t E) {
     const int64_t nk = H / 32, wgs = ((T + 63) / 64) * ((E + 127) / 128);
     int s = 1;
