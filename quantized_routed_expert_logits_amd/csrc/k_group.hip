@@ -67,31 +67,36 @@ __device__ int chunk_split(int cnt, int* per) {
     return (cnt + p - 1) / p;
 }
 
-// Exclusive scan of one value per thread over a workgroup of 1024 threads.
-__device__ int block_exclusive_scan(int v, int* total) {
-    __shared__ int wsum[16];
+// Exclusive scans of four values per thread over a workgroup of 1024
+// threads, side by side (one pass of barriers for the four): returns the
+// four exclusive prefixes, and the four totals in *total.
+__device__ int4 block_exclusive_scan4(int4 v, int4* total) {
+    __shared__ int4 wsum4[16];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int incl = v;
+    int4 incl = v;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
+        const int4 o = make_int4(__shfl_up(incl.x, off), __shfl_up(incl.y, off), __shfl_up(incl.z, off),
+                                 __shfl_up(incl.w, off));
+        if (lane >= off) incl.x += o.x, incl.y += o.y, incl.z += o.z, incl.w += o.w;
     }
-    if (lane == 63) wsum[wave] = incl;
+    if (lane == 63) wsum4[wave] = incl;
     __syncthreads();
     if (wave == 0) {
-        int w = lane < 16 ? wsum[lane] : 0;
-        int wi = w;
+        const int4 w = lane < 16 ? wsum4[lane] : make_int4(0, 0, 0, 0);
+        int4 wi = w;
 #pragma unroll
         for (int off = 1; off < 16; off <<= 1) {
-            const int o = __shfl_up(wi, off);
-            if (lane >= off) wi += o;
+            const int4 o = make_int4(__shfl_up(wi.x, off), __shfl_up(wi.y, off), __shfl_up(wi.z, off),
+                                     __shfl_up(wi.w, off));
+            if (lane >= off) wi.x += o.x, wi.y += o.y, wi.z += o.z, wi.w += o.w;
         }
-        if (lane < 16) wsum[lane] = wi - w;  // exclusive over waves
+        if (lane < 16) wsum4[lane] = make_int4(wi.x - w.x, wi.y - w.y, wi.z - w.z, wi.w - w.w);  // exclusive over waves
         if (lane == 15) *total = wi;
     }
     __syncthreads();
-    const int r = wsum[wave] + incl - v;
+    const int4 b = wsum4[wave];
+    const int4 r = make_int4(b.x + incl.x - v.x, b.y + incl.y - v.y, b.z + incl.z - v.z, b.w + incl.w - v.w);
     __syncthreads();
     return r;
 }
@@ -146,7 +151,6 @@ __device__ void finish_lists(const ChunkLists& cl, int32_t E, int nbig, int nsma
 __global__ void __launch_bounds__(1024) group_scan_kernel(const int32_t* __restrict__ hist, int64_t nchunks, int64_t n,
                                                           int32_t E, int32_t* __restrict__ base,
                                                           int32_t* __restrict__ offsets, ChunkLists cl) {
-    __shared__ int total_rows, total_tiled, total_big, total_small;
     const int e = threadIdx.x;
     int cnt = 0;
     if (e < E) {
@@ -168,13 +172,14 @@ __global__ void __launch_bounds__(1024) group_scan_kernel(const int32_t* __restr
             cnt += h;
         }
     }
-    const int off = block_exclusive_scan(e < E ? cnt : 0, &total_rows);
-    const int toff = block_exclusive_scan(e < E ? (cnt + 15) / 16 * 16 : 0, &total_tiled);
     int per = 0;
     const int nt = e < E ? chunk_split(cnt, &per) : 0;
     const int ns = small_chunks(cnt, nt, per);
-    const int bpos = block_exclusive_scan(nt - ns, &total_big);
-    const int spos = block_exclusive_scan(ns, &total_small);
+    __shared__ int4 tot4;
+    const int4 pre = block_exclusive_scan4(make_int4(e < E ? cnt : 0, e < E ? (cnt + 15) / 16 * 16 : 0, nt - ns, ns),
+                                           &tot4);
+    const int off = pre.x, toff = pre.y, bpos = pre.z, spos = pre.w;
+    const int total_big = tot4.z, total_small = tot4.w, total_tiled = tot4.y;
     if (e < E) {
         offsets[e] = off;
         emit_chunks(cl, e, off, cnt, nt, per, bpos, spos, toff);
@@ -281,7 +286,6 @@ __global__ void __launch_bounds__(1024) group_small_kernel(const int32_t* __rest
                                                            float* __restrict__ prow, int32_t* __restrict__ err) {
     __shared__ int32_t cur[kMaxExperts];  // counts, then each expert's next free row
     __shared__ int32_t next[kScatterWaves][kMaxExperts];
-    __shared__ int total_rows, total_tiled, total_big, total_small;
     for (int e = threadIdx.x; e < E; e += blockDim.x) cur[e] = 0;
     __syncthreads();
     bool bad = false;
@@ -296,13 +300,13 @@ __global__ void __launch_bounds__(1024) group_small_kernel(const int32_t* __rest
     __syncthreads();
     const int e = threadIdx.x;
     const int cnt = e < E ? cur[e] : 0;
-    const int off = block_exclusive_scan(cnt, &total_rows);
-    const int toff = block_exclusive_scan((cnt + 15) / 16 * 16, &total_tiled);
     int per = 0;
     const int nt = e < E ? chunk_split(cnt, &per) : 0;
     const int ns = small_chunks(cnt, nt, per);
-    const int bpos = block_exclusive_scan(nt - ns, &total_big);
-    const int spos = block_exclusive_scan(ns, &total_small);
+    __shared__ int4 tot4;
+    const int4 pre = block_exclusive_scan4(make_int4(cnt, (cnt + 15) / 16 * 16, nt - ns, ns), &tot4);
+    const int off = pre.x, toff = pre.y, bpos = pre.z, spos = pre.w;
+    const int total_big = tot4.z, total_small = tot4.w, total_tiled = tot4.y;
     if (e < E) {
         offsets[e] = off;
         emit_chunks(cl, e, off, cnt, nt, per, bpos, spos, toff);
@@ -339,16 +343,16 @@ __global__ void __launch_bounds__(1024) group_small_kernel(const int32_t* __rest
 // index past their buffers, whatever the offsets hold.
 __global__ void __launch_bounds__(1024) chunks_from_offsets_kernel(const int32_t* __restrict__ offsets, int32_t E,
                                                                    int64_t n, ChunkLists cl) {
-    __shared__ int total_tiled, total_big, total_small;
     const int e = threadIdx.x;
     int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
     if (e < E && (offsets[e] < 0 || cnt < 0 || offsets[e + 1] > n)) cnt = 0;
-    const int toff = block_exclusive_scan((cnt + 15) / 16 * 16, &total_tiled);
     int per = 0;
     const int nt = chunk_split(cnt, &per);
     const int ns = small_chunks(cnt, nt, per);
-    const int bpos = block_exclusive_scan(nt - ns, &total_big);
-    const int spos = block_exclusive_scan(ns, &total_small);
+    __shared__ int4 tot4;
+    const int4 pre = block_exclusive_scan4(make_int4(0, (cnt + 15) / 16 * 16, nt - ns, ns), &tot4);
+    const int toff = pre.y, bpos = pre.z, spos = pre.w;
+    const int total_big = tot4.z, total_small = tot4.w, total_tiled = tot4.y;
     if (e < E) {
         emit_chunks(cl, e, offsets[e], cnt, nt, per, bpos, spos, toff);
         write_first(cl, E, e, bpos, spos, toff / 16);
