@@ -1,7 +1,8 @@
 // Grouped expert GEMMs: gate/up with SwiGLU and the int8 rounding of H fused
-// in the epilogue; down with the routing weight applied in its epilogue,
-// writing each routed row's output to its grouped row; and the combine that
-// adds a token's K rows.
+// in the epilogue (which can also write H straight into down's tiled fp16
+// operand, with the block values of down's offset pass); down with the
+// routing weight applied in its epilogue, writing each routed row's output to
+// its grouped row; and the combine that adds a token's K rows.
 //
 // Strata compare v0.1.35...v0.1.37 page, include/strata/prefill/moe_fused.hpp,
 // experts: per expert, gate/up on the int8 activations of its grouped rows
