@@ -35,12 +35,12 @@
 // chip's resident capacity let the dispatcher balance the SIMDs; one wave
 // per slab over the whole reduction left some SIMDs with a wave more than
 // others and every wave a long serial chain of loads.
-// Blocks stream through a register ring kDepth deep: a block's codes, weight
-// scales, activation codes and activation scales (and code sums) are all
-// loaded kDepth blocks before their use, so no load is waited on in the
-// block it is used.  kDepth is 4 where it divides the run (always for
-// gate/up: the hidden size is a multiple of 128), else 2 (the FFN size is a
-// multiple of 64).
+// Blocks stream through a register ring kDepth = 2 deep: a block's codes,
+// weight scales, activation codes and activation scales (and code sums) are
+// all loaded two blocks before their use, so no load is waited on in the
+// block it is used (every run has even length).  A 4-deep ring measured the
+// same for gate/up and 4 us slower for down at 32 tokens; the 2-deep one
+// fits in 74 VGPRs, 6 waves per SIMD.
 #include "internal.h"
 
 namespace strata_moe {
@@ -297,7 +297,7 @@ __device__ __forceinline__ void gemv_wave(const GemvArgs& g, const Tile& tl, int
 // passes (two rows, the last one or two); chunks of more than max_rows rows
 // are the small-chunk MFMA kernel's and are skipped here.
 template <bool kGateUp, bool kQ81, bool kSym>
-__global__ void __launch_bounds__(64 * kWaves, 4) gemv_kernel(GemvArgs g) {
+__global__ void __launch_bounds__(64 * kWaves, 6) gemv_kernel(GemvArgs g) {
     __shared__ float red[kWaves][kRedFloats];
     const int per = kWaves / g.nsplit;  // slabs per workgroup
     const int ngroups = (g.nslab + per - 1) / per;
@@ -314,22 +314,14 @@ __global__ void __launch_bounds__(64 * kWaves, 4) gemv_kernel(GemvArgs g) {
     const int part = wave % g.nsplit;
     const bool live = slab < g.nslab;
     const int lane = threadIdx.x & 63;
-    const bool deep = (g.Kd / kBlock / g.nsplit) % 4 == 0;
     for (int r0 = 0; r0 < tl.nrows; r0 += kGemvRows) {  // every wave runs every pass (barriers inside)
         Tile t = tl;
         t.row0 = tl.row0 + r0;
         t.nrows = tl.nrows - r0 < kGemvRows ? tl.nrows - r0 : kGemvRows;
-        if (t.nrows == 1) {
-            if (deep)
-                gemv_wave<kGateUp, kQ81, kSym, 1, 4>(g, t, slab, part, lane, live, red);
-            else
-                gemv_wave<kGateUp, kQ81, kSym, 1, 2>(g, t, slab, part, lane, live, red);
-        } else {
-            if (deep)
-                gemv_wave<kGateUp, kQ81, kSym, 2, 4>(g, t, slab, part, lane, live, red);
-            else
-                gemv_wave<kGateUp, kQ81, kSym, 2, 2>(g, t, slab, part, lane, live, red);
-        }
+        if (t.nrows == 1)
+            gemv_wave<kGateUp, kQ81, kSym, 1, 2>(g, t, slab, part, lane, live, red);
+        else
+            gemv_wave<kGateUp, kQ81, kSym, 2, 2>(g, t, slab, part, lane, live, red);
     }
 }
 
