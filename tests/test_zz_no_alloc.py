@@ -64,3 +64,33 @@ def test_noalloc_rejects_a_call_larger_than_its_scratch(qm):
     assert ei.value.code == qm.EINVAL and "scratch" in str(ei.value)
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)  # nothing ran
+
+
+@pytest.mark.parametrize("s", [S.custom(T=300, H=256, E=12, K=3, I=128), S.shape("window_32")], ids=lambda s: s.name)
+def test_noalloc_call_captured_in_a_graph(qm, s):
+    # The entry point makes no allocation, memset or synchronisation, so a
+    # caller can capture it in a HIP graph.  Each replay, with the program's
+    # own eager work and synchronisations between replays, gives the bits of
+    # the eager call.
+    ex = gpu_experts(s)
+    x, wr = _inputs(s)
+    ref = qm.strata_moe_prefill(x, wr, ex, s.K, torch.empty_like(x))
+    torch.cuda.synchronize()
+    out = torch.empty_like(x)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):  # one eager call first on the capture stream
+        qm.strata_moe_prefill_noalloc(x, wr, ex, s.K, out, stream=stream)
+    stream.synchronize()
+    assert torch.equal(out, ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        qm.strata_moe_prefill_noalloc(x, wr, ex, s.K, out, stream=stream)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        y = qm.strata_moe_prefill(x, wr, ex, s.K, torch.empty_like(x))  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref)
