@@ -100,9 +100,11 @@ def _route_case(qm, x, wr, bias, K):
     assert np.abs(p.astype(np.float64).sum(1) - 1).max() <= 1e-6
 
 
-def test_route_many_experts(qm):
+# the top-K takes a workgroup per token up to 1024 tokens, a wave per token above
+@pytest.mark.parametrize("T", [200, 1500])
+def test_route_many_experts(qm, T):
     """More than 512 experts: the selection keeps 16 logits per lane."""
-    s = S.custom(T=200, H=256, E=1000, K=12, I=32)
+    s = S.custom(T=T, H=256, E=1000, K=12, I=32)
     x, wr = S.activations(s, 6), S.router_weight(s, 6)
     wr[:, 777] = wr[:, 5]           # an exact tie across the two halves of the expert range
     _route_case(qm, x, wr, None, s.K)
@@ -117,10 +119,11 @@ def test_route_exact_ties_and_zero_router(qm):
     _route_case(qm, x, np.zeros_like(wr), None, s.K)   # all equal: 0..K-1, p = 1/K
 
 
-def test_route_near_ties_are_settled_exactly(qm):
+@pytest.mark.parametrize("T", [512, 1536])
+def test_route_near_ties_are_settled_exactly(qm, T):
     """Columns that differ by one fp32 ulp in a single entry: logits a few
     1e-7 apart, below fp32 accumulation noise."""
-    s = S.custom(T=512, H=1024, E=64, K=10, I=32)
+    s = S.custom(T=T, H=1024, E=64, K=10, I=32)
     x, wr = S.activations(s, 4), S.router_weight(s, 4)
     for a, b in [(3, 17), (40, 41), (9, 60)]:
         wr[:, b] = wr[:, a]
