@@ -310,6 +310,32 @@ def test_layer_down_operand_from_epilogue_matches_stage_path(qm, s):
     assert torch.equal(y2, out)
 
 
+def test_layer_every_token_on_the_same_experts(qm):
+    # A router bias sends every token to the same K experts: each of them
+    # gets all T rows (six chunks of the 4-wave kernels apiece), the other
+    # experts none.
+    s = S.custom(T=1000, H=256, E=24, K=4, I=128)
+    x, wr = S.activations(s), S.router_weight(s)
+    bias = np.zeros(s.E, np.float32)
+    hot = [3, 7, 11, 20]
+    bias[hot] = 100.0
+    ref = oracle.layer(x, wr, bias, getter(s), s.E, s.K, want_h=True, fmt=s.fmt)
+    ex = gpu_experts(s).with_router_bias(_t(bias))
+    out = torch.empty((s.T, s.H), dtype=torch.float32, device="cuda")
+    d = qm.strata_moe_prefill_debug(_t(x), _t(wr), ex, s.K, out)
+    g = {k: v.cpu().numpy() for k, v in d.items()}
+    assert np.array_equal(np.sort(g["ids"], axis=1), np.tile(hot, (s.T, 1)))
+    counts = np.diff(g["offsets"])
+    assert np.array_equal(np.nonzero(counts)[0], hot) and np.all(counts[hot] == s.T)
+    for k in ("ids", "offsets", "src", "slot", "qx", "sx"):
+        assert np.array_equal(g[k], ref[k]), k
+    assert np.abs(g["p"] - ref["p"]).max() <= P_TOL
+    assert check_h_codes(g["qh"], g["sh"], ref["h"], ref["qh"], ref["sh"]) < H_RATE
+    assert rel_err(g["out"], ref["y"]) <= Y_TOL
+    y = qm.strata_moe_prefill(_t(x), _t(wr), ex, s.K, torch.empty_like(out))
+    assert torch.equal(y, out)
+
+
 SHARED_SHAPES = [S.custom(T=200, H=256, E=10, K=3, I=128, shared=True),
                  S.custom(T=160, H=512, E=6, K=2, I=640, fmt="q2_0", shared=True),
                  S.custom(T=129, H=256, E=8, K=4, I=64, skewed=True, shared=True),
