@@ -110,6 +110,16 @@ def test_route_many_experts(qm, T):
     _route_case(qm, x, wr, None, s.K)
 
 
+@pytest.mark.parametrize("T", [100, 1100])
+def test_route_every_expert_selected(qm, T):
+    """K = E: every expert is selected, in rank order, and there is no rank
+    K + 1 for the near-tie window to look at."""
+    s = S.custom(T=T, H=256, E=12, K=12, I=32)
+    x, wr = S.activations(s, 7), S.router_weight(s, 7)
+    wr[:, 9] = wr[:, 2]  # an exact tie: lower index first
+    _route_case(qm, x, wr, None, s.K)
+
+
 def test_route_exact_ties_and_zero_router(qm):
     s = S.custom(T=300, H=512, E=40, K=7, I=32)
     x, wr = S.activations(s, 3), S.router_weight(s, 3)
@@ -276,7 +286,9 @@ def test_down_stage(qm, s):
 LAYER_SHAPES = STAGE_SHAPES + [S.custom(T=129, H=256, E=8, K=4, I=64, skewed=True),
                                # the largest widths the library takes (H = I = 4096), and the most
                                # experts and pairs per token (E = 1024, K = 16)
-                               S.custom(T=24, H=4096, E=4, K=2, I=4096), S.custom(T=64, H=256, E=1024, K=16, I=64)]
+                               S.custom(T=24, H=4096, E=4, K=2, I=4096), S.custom(T=64, H=256, E=1024, K=16, I=64),
+                               # every token on every expert (K = E: no rank K + 1 to compare against)
+                               S.custom(T=100, H=256, E=6, K=6, I=64)]
 
 
 @pytest.mark.parametrize("s", LAYER_SHAPES, ids=lambda s: s.name)
