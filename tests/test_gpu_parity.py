@@ -288,7 +288,9 @@ LAYER_SHAPES = STAGE_SHAPES + [S.custom(T=129, H=256, E=8, K=4, I=64, skewed=Tru
                                # experts and pairs per token (E = 1024, K = 16)
                                S.custom(T=24, H=4096, E=4, K=2, I=4096), S.custom(T=64, H=256, E=1024, K=16, I=64),
                                # every token on every expert (K = E: no rank K + 1 to compare against)
-                               S.custom(T=100, H=256, E=6, K=6, I=64)]
+                               S.custom(T=100, H=256, E=6, K=6, I=64),
+                               # a single token (one row for each of K experts)
+                               S.custom(T=1, H=256, E=16, K=4, I=128)]
 
 
 @pytest.mark.parametrize("s", LAYER_SHAPES, ids=lambda s: s.name)
