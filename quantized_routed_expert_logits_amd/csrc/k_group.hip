@@ -40,9 +40,19 @@ __global__ void __launch_bounds__(256) group_hist_kernel(const int32_t* __restri
     __syncthreads();
     const int64_t i0 = (int64_t)blockIdx.x * kGroupChunk;
     const int64_t i1 = i0 + kGroupChunk < n ? i0 + kGroupChunk : n;
+    // the thread's kGroupChunk / 256 ids, all loads in flight at once
+    constexpr int kPer = kGroupChunk / 256;
+    int32_t ev[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int64_t i = i0 + threadIdx.x + 256 * j;
+        ev[j] = i < i1 ? ids[i] : 0;
+    }
     bool bad = false;
-    for (int64_t i = i0 + threadIdx.x; i < i1; i += blockDim.x) {
-        const int32_t e = ids[i];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        if (i0 + threadIdx.x + 256 * j >= i1) continue;
+        const int32_t e = ev[j];
         if (e < 0 || e >= E)
             bad = true;
         else
@@ -211,12 +221,28 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int32_t e, bool ok, int nb
 // The multi-split scatter of the pairs [i0, i0 + 256) by one wave, as
 // group_scatter_kernel's two passes: count[e] gets the wave's count per
 // expert (pass 1), then (pass 2, with count[e] set to the wave's first row per
-// expert) the rows in pair order.
-__device__ __forceinline__ void scatter_count(const int32_t* __restrict__ ids, int64_t n, int32_t E, int nbits,
-                                              int64_t i0, int lane, int32_t* count) {
+// expert) the rows in pair order.  The wave's ids and weights are loaded once,
+// all in flight together (pair i0 + 64 step + lane in entry step of the
+// lane), and both passes work from the registers.
+struct WavePairs {
+    int32_t e[4];  // expert id, -1 past n
+    float p[4];    // routing weight (when the rows' weights are wanted)
+};
+__device__ __forceinline__ WavePairs load_pairs(const int32_t* __restrict__ ids, const float* __restrict__ p,
+                                                int64_t n, int64_t i0, int lane) {
+    WavePairs v;
+#pragma unroll
     for (int step = 0; step < 4; ++step) {
         const int64_t i = i0 + step * 64 + lane;
-        const int32_t e = i < n ? ids[i] : -1;
+        v.e[step] = i < n ? ids[i] : -1;
+        v.p[step] = p && i < n ? p[i] : 0.0f;
+    }
+    return v;
+}
+__device__ __forceinline__ void scatter_count(const WavePairs& v, int32_t E, int nbits, int lane, int32_t* count) {
+#pragma unroll
+    for (int step = 0; step < 4; ++step) {
+        const int32_t e = v.e[step];
         const bool ok = e >= 0 && e < E;
         const uint64_t same = same_expert_lanes(e, ok, nbits);
         if (ok && (same >> lane) == 1ull) count[e] += __popcll(same);
@@ -224,14 +250,14 @@ __device__ __forceinline__ void scatter_count(const int32_t* __restrict__ ids, i
         __builtin_amdgcn_wave_barrier();
     }
 }
-__device__ __forceinline__ void scatter_rows(const int32_t* __restrict__ ids, const float* __restrict__ p, int64_t n,
-                                             int32_t K, int32_t E, int nbits, int64_t i0, int lane, int32_t* next,
-                                             int32_t* __restrict__ src, int32_t* __restrict__ slot,
-                                             float* __restrict__ prow) {
+__device__ __forceinline__ void scatter_rows(const WavePairs& v, int32_t K, int32_t E, int nbits, int64_t i0,
+                                             int lane, int32_t* next, int32_t* __restrict__ src,
+                                             int32_t* __restrict__ slot, float* __restrict__ prow) {
     const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
     for (int step = 0; step < 4; ++step) {
         const int64_t i = i0 + step * 64 + lane;
-        const int32_t e = i < n ? ids[i] : -1;
+        const int32_t e = v.e[step];
         const bool ok = e >= 0 && e < E;
         const uint64_t same = same_expert_lanes(e, ok, nbits);
         const int rank = __popcll(same & below);
@@ -242,7 +268,7 @@ __device__ __forceinline__ void scatter_rows(const int32_t* __restrict__ ids, co
             const int row = first + rank;
             slot[i] = row;
             src[row] = (int32_t)(i / K);
-            if (prow) prow[row] = p[i];
+            if (prow) prow[row] = v.p[step];
             if ((same >> lane) == 1ull) next[e] = first + __popcll(same);  // the highest lane of this expert
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -261,7 +287,8 @@ __global__ void __launch_bounds__(64 * kScatterWaves) group_scatter_kernel(
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     const int64_t i0 = (int64_t)blockIdx.x * kGroupChunk + 256 * w;
-    scatter_count(ids, n, E, nbits, i0, lane, next[w]);
+    const WavePairs v = load_pairs(ids, prow ? p : nullptr, n, i0, lane);
+    scatter_count(v, E, nbits, lane, next[w]);
     __syncthreads();
     // each wave's first row per expert: the chunk's first row, then the waves before it
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
@@ -273,7 +300,7 @@ __global__ void __launch_bounds__(64 * kScatterWaves) group_scatter_kernel(
         }
     }
     __syncthreads();
-    scatter_rows(ids, p, n, K, E, nbits, i0, lane, next[w], src, slot, prow);
+    scatter_rows(v, K, E, nbits, i0, lane, next[w], src, slot, prow);
 }
 
 // All of the grouping in one workgroup of 1024 threads, for n pairs in at
@@ -321,7 +348,11 @@ __global__ void __launch_bounds__(1024) group_small_kernel(const int32_t* __rest
     for (int64_t c0 = 0; c0 < n; c0 += kGroupChunk) {
         for (int i = threadIdx.x; i < kScatterWaves * E; i += blockDim.x) next[i / E][i % E] = 0;
         __syncthreads();  // also orders the cur[] writes above and the last chunk's rows
-        if (w < kScatterWaves) scatter_count(ids, n, E, nbits, c0 + 256 * w, lane, next[w]);
+        WavePairs v{};
+        if (w < kScatterWaves) {
+            v = load_pairs(ids, prow ? p : nullptr, n, c0 + 256 * w, lane);
+            scatter_count(v, E, nbits, lane, next[w]);
+        }
         __syncthreads();
         for (int ee = threadIdx.x; ee < E; ee += blockDim.x) {
             int run = cur[ee];
@@ -333,7 +364,7 @@ __global__ void __launch_bounds__(1024) group_small_kernel(const int32_t* __rest
             cur[ee] = run;
         }
         __syncthreads();
-        if (w < kScatterWaves) scatter_rows(ids, p, n, K, E, nbits, c0 + 256 * w, lane, next[w], src, slot, prow);
+        if (w < kScatterWaves) scatter_rows(v, K, E, nbits, c0 + 256 * w, lane, next[w], src, slot, prow);
         __syncthreads();
     }
 }

@@ -14,20 +14,24 @@
 // below the K-th value) are recomputed as fp64 dot products and everything
 // within delta of the K-th value is re-ranked.  With delta above twice the
 // logits' error, the result equals the ranking of the exact logits.
-// delta = max(kTieRel * max(1, |l_K|), 2 * err_t), with err_t the token's
+// delta = 2 err_t (1% on top for the fp32 norms), with err_t the token's
 // error bound.  Each term of the dot product is carried as three fp16
 // products (hi*hi + hi*lo + lo*hi of the two operands' halves: within
 // 2^-20 |x w| of x w), each exact in fp32.  v_mfma_f32_16x16x32_f16 sums its
 // 32 products in fp32-class arithmetic (at most 31 additions) and then adds
-// that sum to the accumulator, so a product passes through at most 31 + 3H/32
-// additions (3 H / 32 MFMAs in the accumulator chain), plus a few for the
-// split reduction and the bias; each addition is taken within 2^-23 of its
-// exact result (truncation as well as rounding), relative to at most
-// sum_h |x_h w_h| <= ||x||_2 ||w_e||_2 (Cauchy-Schwarz).  So
-//     err_t = ((3 H / 32 + 40) 2^-23 + 2^-20) ||x_t||_2 max_e ||w_e||_2.
+// that sum to the accumulator.  The reduction over H is split into ns equal
+// ranges, each its own accumulator chain of 3 (H / 32) / ns MFMAs; the
+// epilogue adds the bias to range 0 and the top-K adds the ns partial values
+// in order (ns roundings, each relative to at most sum_h |x_h w_h| + |b_e|).
+// So a product passes through at most 31 + 3 H / (32 ns) + ns additions; each
+// addition is taken within 2^-23 of its exact result (truncation as well as
+// rounding), and sum_h |x_h w_h| <= ||x||_2 ||w_e||_2 (Cauchy-Schwarz).
+// With 9 additions to spare:
+//     err_t = ((3 H / (32 ns) + ns + 40) 2^-23 + 2^-20) ||x_t||_2 max_e ||w_e||_2
+//             + (ns + 1) 2^-23 max_e |b_e|.
 // At the synthetic workloads' scale the largest deviation from fp64 logits is
-// about 3e-5 and err_t about 5e-3; inputs with outlier channels raise err_t
-// with ||x_t||.
+// about 3e-5 and err_t 1.4e-3 (ns = 8) to 5e-3 (ns = 1); inputs with outlier
+// channels raise err_t with ||x_t||.
 #include "internal.h"
 
 #include <cfloat>
@@ -37,12 +41,12 @@ namespace strata_moe {
 
 namespace {
 
-constexpr float kTieRel = 1.0f / 1024.0f;
-
-// 2 err_t / (||x_t|| max_e ||w_e||), with 1% on top for the fp32 norms.
-__device__ __forceinline__ float tie_coeff(int32_t H) {
-    return 2.02f * ((3.0f * (float)(H / 32) + 40.0f) * 0x1p-23f + 0x1p-20f);
+// The near-tie window delta = 2 err_t, with 1% on top for the fp32 norms:
+// tie_coeff(H, ns) ||x_t|| max_e ||w_e|| + tie_bias_coeff(ns) max_e |b_e|.
+__device__ __forceinline__ float tie_coeff(int32_t H, int ns) {
+    return 2.02f * ((3.0f * (float)(H / 32 / ns) + (float)ns + 40.0f) * 0x1p-23f + 0x1p-20f);
 }
+__device__ __forceinline__ float tie_bias_coeff(int ns) { return 2.02f * (float)(ns + 1) * 0x1p-23f; }
 
 // ---------------------------------------------------------------- logits
 // logits[T][E] = x[T][H] . wr[H][E] (+ bias) on the MFMA unit.  Each fp32
@@ -174,7 +178,7 @@ struct RouterStage {
     half8_t b[2][2];        // [expert tile][hi, lo]
 };
 
-__global__ void __launch_bounds__(256, 2) router_mfma_kernel(const float* __restrict__ x,
+__global__ void __launch_bounds__(256, 4) router_mfma_kernel(const float* __restrict__ x,
                                                              const float* __restrict__ xm,
                                                              const _Float16* __restrict__ wb,
                                                              const float* __restrict__ wm,
@@ -486,14 +490,9 @@ __device__ __forceinline__ void load_logits(const float* __restrict__ l, int nsp
     }
 }
 
-// The near-tie window of a token: kTieRel of its K-th value, or twice its
-// logits' error bound, whichever is wider.  bnd = tie_coeff(H) * ||x_t|| *
-// max_e ||w_e||.
-__device__ __forceinline__ float tie_window(float vK, float bnd) { return fmaxf(kTieRel * fmaxf(1.0f, fabsf(vK)), bnd); }
-
 template <int kSlots>
 __device__ __forceinline__ void select_token(const float* __restrict__ l, int nsplit, int64_t sstride, int32_t E,
-                                             int32_t K, float bnd, int lane, Selection<kSlots>& S) {
+                                             int32_t K, float delta, int lane, Selection<kSlots>& S) {
     load_logits(l, nsplit, sstride, E, lane, S);
     S.rounds = K < E ? K + 1 : K;
 #pragma unroll
@@ -544,7 +543,7 @@ __device__ __forceinline__ void select_token(const float* __restrict__ l, int ns
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k)
         if (k == K - 1) S.vK = S.selv[k];
-    S.delta = tie_window(S.vK, bnd);
+    S.delta = delta;
     S.loose = 0;
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k) {
@@ -688,7 +687,16 @@ __global__ void __launch_bounds__(64 * kSelectWaves) topk_kernel(const float* __
     const int64_t t = kWide ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * kSelectWaves + wave;
     if (t >= T) return;  // kWide: uniform over the workgroup; otherwise no barrier follows
     Selection<kSlots> S;
-    select_token(logits + t * E, nsplit, T * E, E, K, tie_coeff(H) * xn[t] * *wnorm, lane, S);
+    // the largest |b_e| (the bias's share of the error bound)
+    float bm = 0.0f;
+    if (bias) {
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i)
+            if (lane + 64 * i < E) bm = fmaxf(bm, fabsf(bias[lane + 64 * i]));
+        for (int o = 1; o < 64; o <<= 1) bm = fmaxf(bm, __shfl_xor(bm, o));
+    }
+    const float delta = tie_coeff(H, nsplit) * xn[t] * *wnorm + tie_bias_coeff(nsplit) * bm;
+    select_token(logits + t * E, nsplit, T * E, E, K, delta, lane, S);
     if (!S.loose) {  // kWide: the same for every wave of the workgroup
         if (!kWide || wave == 0) {
             float lv[kMaxTopK];
