@@ -169,18 +169,21 @@ def test_route_all_tokens(qm, name):
     assert np.abs(p.astype(np.float64).sum(1) - 1).max() <= 1e-6
 
 
-def router_error_bound(x, wr):
+def router_error_bound(x, wr, bias=None):
     """Per-token bound of the GPU logits' error, as the routing kernels model
     it: three fp16 products per term (hi and lo halves, 2^-20 of |x||w|
     together), each passing through at most 31 additions inside an MFMA and
     3 H / 32 accumulator additions, plus a few for the split reduction and the
     bias, each within 2^-23 of its result; sum_h |x_h w_he| <=
-    ||x||_2 ||w_e||_2."""
+    ||x||_2 ||w_e||_2.  The bias passes through at most 9 roundings (8 split
+    ranges and its own addition).  This is the bound of one split range, the
+    widest; the kernels' window counts the actual ranges."""
     H = x.shape[1]
     c = (3 * H / 32 + 40) * 2.0 ** -23 + 2.0 ** -20
     xn = np.linalg.norm(x.astype(np.float64), axis=1)
     wn = np.linalg.norm(wr.astype(np.float64), axis=0).max()
-    return c * xn * wn
+    bm = 0.0 if bias is None else float(np.abs(bias.astype(np.float64)).max())
+    return c * xn * wn + 9 * 2.0 ** -23 * bm
 
 
 def test_route_outlier_channels(qm):
@@ -205,6 +208,37 @@ def test_route_outlier_channels(qm):
           f"{boundary_gaps(logits, s.K).min():.3e}, mismatched tokens {int((ids != ids_r).any(1).sum())}")
     assert np.array_equal(ids, ids_r)
     tol = 2.0 * router_error_bound(x, wr)[:, None] + 1e-6
+    assert np.all(np.abs(p - p_r) <= tol)
+
+
+@pytest.mark.parametrize("T", [300, 1500])
+def test_route_large_bias(qm, T):
+    """A bias of 1e5 on every expert: there the fp32 logits are 7.8e-3 apart,
+    and each of the router's split ranges rounds the running sum near 1e5, so
+    two experts whose exact logits are less than about two such steps apart
+    can come out one step apart in the wrong order.  Columns 20..40 form a
+    ladder (w_e = w_20 + (e - 20) c u) whose logits are a fraction of a step
+    apart for a typical token, and carry 10 more bias, so the top K come from
+    the ladder.  The dot products' own error is about 2e-4 here: only the
+    bias's share of the error bound puts such pairs inside the near-tie window
+    (a host model of the split sums misranks 5 of 300 and 14 of 1500 tokens
+    outside a window without it).  ids bit-exact; p within the softmax's
+    response to the bound."""
+    s = S.custom(T=T, H=256, E=64, K=4, I=32)
+    x, wr = S.activations(s, 8), S.router_weight(s, 8)
+    u = np.random.default_rng(9).standard_normal(s.H)
+    for e in range(21, 41):
+        wr[:, e] = (wr[:, 20].astype(np.float64) + (e - 20) * 4e-4 * u).astype(np.float32)
+    bias = np.full(s.E, 1e5, np.float32)
+    bias[20:41] = np.float32(1e5 + 10)
+    ids, p = qm.strata_moe_route(_t(x), _t(wr), _t(bias), s.K)
+    logits = oracle.router_logits(x, wr, bias)
+    ids_r, p_r = oracle.topk_softmax(logits, s.K)
+    ids, p = ids.cpu().numpy(), p.cpu().numpy()
+    print(f"large bias: min boundary gap {boundary_gaps(logits, s.K).min():.3e}, "
+          f"mismatched tokens {int((ids != ids_r).any(1).sum())}")
+    assert np.array_equal(ids, ids_r)
+    tol = 2.0 * router_error_bound(x, wr, bias)[:, None] + 1e-6
     assert np.all(np.abs(p - p_r) <= tol)
 
 
