@@ -10,6 +10,12 @@
 //     formulations: fp16 MFMA with the weight scale inside the operand and
 //     one FMA per output (the layer's form), and int8 MFMA with both scales
 //     applied per output (convert, multiply, FMA).  Output-blocks per second.
+//   strata_probe_scaled_tiles: the same fp16 form at the shape of the 4-wave
+//     gate/up kernel (6 output tiles of 32 x 32 per wave and block: 24
+//     v_mfma_f32_16x16x32_f16 and 96 FMAs), or with v_mfma_f32_32x32x16_f16
+//     (two chained per tile and block, 16 FMAs per lane), operands in
+//     registers: the ceiling of the exact block-scaled products before any
+//     load, unpack or barrier.
 //   strata_probe_mfma_f16: one v_mfma_f32_16x16x32_f16 on given operands
 //     (row-major A [16][32], B [32][16], C [16][16]), to check how it rounds.
 //   strata_probe_hbm_read: the read bandwidth a plain streaming kernel gets
@@ -158,6 +164,54 @@ __global__ void __launch_bounds__(64 * kWavesPerGroup) scaled_blocks_kernel(int3
     if (lane == 0) out[blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6)] = r;
 }
 
+// Per block, kTiles output tiles of 32 x 32 (the rows of tile t come from
+// its own A operands): kForm 0 forms each with four v_mfma_f32_16x16x32_f16
+// (zero accumulator), kForm 1 with two chained v_mfma_f32_32x32x16_f16; then
+// one FMA per output with the block's activation scale.  Every tile's A
+// operands differ as vectors (no two products are the same expression, so
+// the compiler keeps every MFMA).
+template <int kForm, int kTiles>
+__global__ void __launch_bounds__(64 * kWavesPerGroup, 2) scaled_tiles_kernel(int32_t blocks, int32_t seed,
+                                                                             float* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int s = seed + lane;
+    float acc[kTiles][16] = {};
+    float ssc = 1.0f + (float)(s & 15) * 0x1p-12f;
+    half8_t a[kTiles][4], b[2];
+    for (int t = 0; t < kTiles; ++t)
+        for (int f = 0; f < 4; ++f)
+            for (int i = 0; i < 8; ++i) a[t][f][i] = (_Float16)(float)(((s * (2 * t + 1) + 5 * f + 3 * i) & 7) - 3);
+    for (int j = 0; j < 2; ++j)
+        for (int i = 0; i < 8; ++i) b[j][i] = (_Float16)(float)(s - i + j);
+    const half8_t one = {1, 1, 1, 1, 1, 1, 1, 1};
+    for (int blk = 0; blk < blocks; ++blk) {
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+            if constexpr (kForm == 0) {
+#pragma unroll
+                for (int f = 0; f < 4; ++f) {
+                    const float4_t p =
+                        __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t][f], b[0], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[t][4 * f + v] = fmaf(p[v], ssc, acc[t][4 * f + v]);
+                }
+            } else {
+                float16_t p = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[t][0], b[0], (float16_t){}, 0, 0, 0);
+                p = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[t][1], b[1], p, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[t][v] = fmaf(p[v], ssc, acc[t][v]);
+            }
+        }
+        b[0] += one;  // the next block's operands
+        b[1] += one;
+        ssc += 0x1p-20f;
+    }
+    float r = 0.f;
+    for (int t = 0; t < kTiles; ++t)
+        for (int i = 0; i < 16; ++i) r += acc[t][i];
+    if (lane == 0) out[blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6)] = r;
+}
+
 // One 16x16x32 fp16 MFMA on row-major operands, one wave.  The lane layout
 // of the instruction: A lane l holds row l % 16, k = 8 (l / 16) .. + 7; B
 // lane l holds column l % 16, the same k; C/D lane l holds rows
@@ -227,6 +281,11 @@ template <bool kI8>
 void launch_scaled(hipStream_t st) {
     hipLaunchKernelGGL(scaled_blocks_kernel<kI8>, dim3(g_groups), dim3(64 * kWavesPerGroup), 0, st, g_iters, 0, g_out);
 }
+template <int kForm, int kTiles>
+void launch_tiles(hipStream_t st) {
+    hipLaunchKernelGGL((scaled_tiles_kernel<kForm, kTiles>), dim3(g_groups), dim3(64 * kWavesPerGroup), 0, st,
+                       g_iters, 0, g_out);
+}
 
 }  // namespace
 
@@ -265,6 +324,28 @@ int strata_probe_scaled_blocks(int i8, int32_t groups, int32_t blocks, double* o
     (void)hipFree(g_out);
     g_out = nullptr;
     const double n = (double)groups * kWavesPerGroup * blocks * 1024.0;
+    *out_blocks_per_s = rc == 0 && *ms > 0 ? n / (*ms * 1e-3) : 0.0;
+    return rc;
+}
+
+// form 0: v_mfma_f32_16x16x32_f16, 1: v_mfma_f32_32x32x16_f16; tiles 1 or 6
+// output tiles of 32 x 32 per wave and block.  Writes 32 x 32 x tiles x
+// blocks output-blocks per wave over the kernel time, per second.  Returns
+// 0, -1 (arguments), -4 (a HIP call failed).
+int strata_probe_scaled_tiles(int form, int tiles, int32_t groups, int32_t blocks, double* out_blocks_per_s,
+                              double* ms) {
+    if ((form != 0 && form != 1) || (tiles != 1 && tiles != 6) || groups < 1 || blocks < 1 || !out_blocks_per_s ||
+        !ms)
+        return -1;
+    if (hipMalloc(&g_out, sizeof(float) * groups * kWavesPerGroup) != hipSuccess) return -4;
+    g_iters = blocks;
+    g_groups = groups;
+    void (*fn)(hipStream_t) = form == 0 ? (tiles == 1 ? launch_tiles<0, 1> : launch_tiles<0, 6>)
+                                        : (tiles == 1 ? launch_tiles<1, 1> : launch_tiles<1, 6>);
+    const int rc = run_timed(fn, ms);
+    (void)hipFree(g_out);
+    g_out = nullptr;
+    const double n = (double)groups * kWavesPerGroup * blocks * 1024.0 * tiles;
     *out_blocks_per_s = rc == 0 && *ms > 0 ? n / (*ms * 1e-3) : 0.0;
     return rc;
 }

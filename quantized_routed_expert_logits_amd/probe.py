@@ -17,6 +17,7 @@ _d = ctypes.POINTER(ctypes.c_double)
 _f = ctypes.POINTER(ctypes.c_float)
 _lib.strata_probe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _d, _d]
 _lib.strata_probe_scaled_blocks.argtypes = [ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _d, _d]
+_lib.strata_probe_scaled_tiles.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _d, _d]
 _lib.strata_probe_mfma_f16.argtypes = [_f, _f, _f, _f]
 _lib.strata_probe_hbm_read.argtypes = [ctypes.c_int64, ctypes.c_int32, _d, _d]
 
@@ -39,6 +40,17 @@ def strata_probe_scaled_blocks(int8: bool, groups: int = 4096, blocks: int = 512
     rc = _lib.strata_probe_scaled_blocks(int(int8), groups, blocks, ctypes.byref(r), ctypes.byref(ms))
     if rc != 0:
         raise RuntimeError(f"strata_probe_scaled_blocks failed ({rc})")
+    return r.value, ms.value
+
+
+def strata_probe_scaled_tiles(form: str, tiles: int, groups: int = 2048, blocks: int = 512) -> tuple[float, float]:
+    """(scaled output-blocks per second, kernel ms) of the fp16 form at `tiles` (1 or 6) output tiles of
+    32 x 32 per wave and block; form "16x16x32" (the layer's MFMA) or "32x32x16"."""
+    r, ms = ctypes.c_double(), ctypes.c_double()
+    rc = _lib.strata_probe_scaled_tiles(["16x16x32", "32x32x16"].index(form), tiles, groups, blocks,
+                                        ctypes.byref(r), ctypes.byref(ms))
+    if rc != 0:
+        raise RuntimeError(f"strata_probe_scaled_tiles failed ({rc})")
     return r.value, ms.value
 
 

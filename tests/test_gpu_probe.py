@@ -4,7 +4,10 @@ before it adds the accumulator (so the accumulator sees one addition per
 instruction), and that sum is within 31 fp32 additions' error (2^-23 each,
 truncation included) of the exact one.  Crafted operands make a wrong premise
 visible: an accumulator added first would lose the small products, and a sum
-outside the bound would show on the cancelling cases."""
+outside the bound would show on the cancelling cases.
+
+The probe's rates must also stay below the published dense peaks: a rate
+above its peak means the compiler dropped work from the measured kernel."""
 import numpy as np
 import pytest
 
@@ -68,3 +71,24 @@ def test_mfma_f16_sum_within_the_error_model(probe):
         assert ok, (prods[:3], d)
     ok, d = _within_model(probe, [(1.0, 0.5)] * 32, 2.0 ** 24)
     assert ok
+
+
+# published dense peaks of the MI355X matrix unit (no sparsity), ops/s
+PEAK_F16 = 2.5e15
+PEAK_I8 = 5.0e15
+
+
+def test_probe_rates_below_published_peaks(probe):
+    for kind in probe.KINDS:
+        rate, _ = probe.strata_probe_mfma_rate(kind)
+        peak = PEAK_F16 if kind.startswith("f16") else PEAK_I8
+        assert 0 < rate <= 1.05 * peak, (kind, rate)
+    # a scaled output-block is 32 multiply-adds (64 ops) on the fp16 or int8 unit
+    for i8 in (False, True):
+        rate, _ = probe.strata_probe_scaled_blocks(i8)
+        assert 0 < rate * 64 <= 1.05 * (PEAK_I8 if i8 else PEAK_F16), (i8, rate)
+    for form in ("16x16x32", "32x32x16"):
+        for tiles in (1, 6):
+            rate, _ = probe.strata_probe_scaled_tiles(form, tiles)
+            print(f"scaled tiles {form} x {tiles}: {rate / 1e12:.1f} T output-blocks/s")
+            assert 0 < rate * 64 <= 1.05 * PEAK_F16, (form, tiles, rate)
