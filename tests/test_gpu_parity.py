@@ -1,8 +1,9 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle.
 
 Bars: routing ids, grouping tables and the layer input's int8 codes and
-scales bit-exact; routing weights within 2e-5 absolute (fp32 logits: about
-4e-6 of logit error, far below); SwiGLU-output codes equal except at rounding
+scales bit-exact; routing weights within 2e-5 absolute (a softmax of the
+fp32-class logits: measured 1.6e-7 at the tiny layer to 5.0e-6 at 32768
+tokens, growing with the router's accumulation chain); SwiGLU-output codes equal except at rounding
 ties of the oracle's exact quotient (then off by one), at a rate below 1e-3;
 the down stage fed the oracle's H codes within max|err| / max|ref| <= 1e-5
 (and a per-output fp32 rounding bound); the layer output within
@@ -20,7 +21,7 @@ from layers import (canonical_expert, check_h_codes, down_error_bound, gate_boun
 
 pytestmark = pytest.mark.gpu
 
-P_TOL = 2e-5
+P_TOL = 2e-5     # routing weights: the fp32-class logits' softmax (1e-6 holds only up to 2048 tokens)
 Y_TOL = 2e-3
 DOWN_TOL = 1e-5   # the down stage alone, on the oracle's H codes
 H_RATE = 1e-3     # largest share of SwiGLU-output codes that may sit one step off at a rounding tie
@@ -163,7 +164,8 @@ def test_route_all_tokens(qm, name):
     gap = boundary_gaps(logits, s.K)
     ids, p = ids.cpu().numpy(), p.cpu().numpy()
     print(f"{name}: {s.T} tokens, min boundary gap {gap.min():.3e}, tokens below 1e-6: {(gap < 1e-6).sum()}, "
-          f"mismatched tokens: {int((ids != ids_r).any(1).sum())}")
+          f"mismatched tokens: {int((ids != ids_r).any(1).sum())}, max |dp| {np.abs(p - p_r).max():.2e}, "
+          f"tokens with |dp| > 1e-6: {int((np.abs(p - p_r) > 1e-6).any(1).sum())}")
     assert np.array_equal(ids, ids_r)
     assert np.abs(p - p_r).max() <= P_TOL
     assert np.abs(p.astype(np.float64).sum(1) - 1).max() <= 1e-6
