@@ -215,7 +215,7 @@ int strata_moe_prefill(const float* x, const float* router_w, const strata_moe_e
  * library (one per GPU, held until the process ends), so the call allocates
  * and frees nothing.  A call whose workspace (strata_moe_workspace_bytes)
  * exceeds it fails with EINVAL and enqueues nothing: at H = 2560, I = 1024,
- * E = 512, K = 10 that is above 2,160 tokens.  Every call on one GPU
+ * E = 512, K = 10 that is above 2,246 tokens.  Every call on one GPU
  * shares that GPU's array: calls that overlap on one GPU (other streams,
  * other host threads) race and must not be made.  Nothing in the array needs
  * to start at zero; the flags a call relies on are cleared by its own first

@@ -152,16 +152,13 @@ struct RouterScratch {
     float* pmax;
 };
 // The router GEMM splits the reduction over H into router_splits() ranges
-// until the launch has 1024 workgroups (4 per CU) or 8 ranges; logits then
-// holds that many partial [T][E] arrays, which the top-K adds in order.  Each
-// range is its own accumulator chain, so more ranges also narrow the top-K's
-// near-tie window (2 ranges at 8192 tokens: 26% of the tokens re-scored
-// instead of 39%).
+// until the launch has 512 workgroups (2 per CU) or 8 ranges; logits then
+// holds that many partial [T][E] arrays, which the top-K adds in order.
 constexpr int kMaxRouterSplits = 8;
 inline int router_splits(int64_t T, int32_t H, int32_t E) {
     const int64_t nk = H / 32, wgs = ((T + 63) / 64) * ((E + 127) / 128);
     int s = 1;
-    while (s < kMaxRouterSplits && wgs * s < 1024 && nk % (4 * s) == 0) s *= 2;
+    while (s < kMaxRouterSplits && wgs * s < 512 && nk % (4 * s) == 0) s *= 2;
     return s;
 }
 inline int64_t router_logit_floats(int64_t T, int32_t H, int32_t E) { return router_splits(T, H, E) * T * E; }

@@ -20,18 +20,20 @@
 // 2^-20 |x w| of x w), each exact in fp32.  v_mfma_f32_16x16x32_f16 sums its
 // 32 products in fp32-class arithmetic (at most 31 additions) and then adds
 // that sum to the accumulator.  The reduction over H is split into ns equal
-// ranges, each its own accumulator chain of 3 (H / 32) / ns MFMAs; the
-// epilogue adds the bias to range 0 and the top-K adds the ns partial values
-// in order (ns roundings, each relative to at most sum_h |x_h w_h| + |b_e|).
-// So a product passes through at most 31 + 3 H / (32 ns) + ns additions; each
-// addition is taken within 2^-23 of its exact result (truncation as well as
-// rounding), and sum_h |x_h w_h| <= ||x||_2 ||w_e||_2 (Cauchy-Schwarz).
-// With 9 additions to spare:
-//     err_t = ((3 H / (32 ns) + ns + 40) 2^-23 + 2^-20) ||x_t||_2 max_e ||w_e||_2
+// ranges; within a range the fp32 accumulator chains end after kRouterChain
+// k blocks (3 MFMAs each) and are added into fp64 sums, which the epilogue
+// rounds to fp32 once (with the bias, in range 0); the top-K adds the ns
+// range values in order.  So a product passes through at most
+// 31 + 3 min(H / (32 ns), kRouterChain) fp32 additions, the fp64 ones (each
+// within 2^-52, counted as one more) and ns roundings of a value at most
+// sum_h |x_h w_h| + |b_e|; each fp32 addition is taken within 2^-23 of its
+// exact result (truncation as well as rounding), and sum_h |x_h w_h| <=
+// ||x||_2 ||w_e||_2 (Cauchy-Schwarz).  With 8 additions to spare:
+//     err_t = ((3 min(H / (32 ns), 8) + ns + 40) 2^-23 + 2^-20) ||x_t||_2 max_e ||w_e||_2
 //             + (ns + 1) 2^-23 max_e |b_e|.
-// At the synthetic workloads' scale the largest deviation from fp64 logits is
-// about 3e-5 and err_t 1.4e-3 (ns = 8) to 5e-3 (ns = 1); inputs with outlier
-// channels raise err_t with ||x_t||.
+// At the synthetic workloads' scale err_t is about 1.2e-3, and the largest
+// deviation from fp64 logits a few 1e-6; inputs with outlier channels raise
+// err_t with ||x_t||.
 #include "internal.h"
 
 #include <cfloat>
@@ -41,10 +43,15 @@ namespace strata_moe {
 
 namespace {
 
+// The router's fp32 accumulator chains end after this many k blocks (3 MFMAs
+// each) and go into fp64 sums.
+constexpr int kRouterChain = 8;
+
 // The near-tie window delta = 2 err_t, with 1% on top for the fp32 norms:
 // tie_coeff(H, ns) ||x_t|| max_e ||w_e|| + tie_bias_coeff(ns) max_e |b_e|.
 __device__ __forceinline__ float tie_coeff(int32_t H, int ns) {
-    return 2.02f * ((3.0f * (float)(H / 32 / ns) + (float)ns + 40.0f) * 0x1p-23f + 0x1p-20f);
+    const int chain = H / 32 / ns < kRouterChain ? H / 32 / ns : kRouterChain;  // blocks per chain
+    return 2.02f * ((3.0f * (float)chain + (float)ns + 40.0f) * 0x1p-23f + 0x1p-20f);
 }
 __device__ __forceinline__ float tie_bias_coeff(int ns) { return 2.02f * (float)(ns + 1) * 0x1p-23f; }
 
@@ -168,9 +175,10 @@ __global__ void __launch_bounds__(256) router_prep_kernel(const float* __restric
 // block to hi/lo fp16 into LDS (each thread 8 values), one barrier, then each
 // wave reads the 4 x 2 A fragments and runs 4 x 2 x 3 MFMAs.  Input values
 // and B fragments (1 KB loads in fragment order) are loaded two k blocks
-// ahead.  Workgroup z of gridDim.z takes the z-th of gridDim.z equal ranges
-// of k blocks (each of even length) and writes its partial logits to slice z
-// (the bias goes into slice 0).
+// ahead.  The fp32 accumulators are added into fp64 sums every kRouterChain
+// k blocks (see the error bound above).  Workgroup z of gridDim.z takes the
+// z-th of gridDim.z equal ranges of k blocks (each of even length) and writes
+// its partial logits to slice z (the bias goes into slice 0).
 constexpr int kRtM = 64, kRtN = 128;
 
 struct RouterStage {
@@ -178,7 +186,7 @@ struct RouterStage {
     half8_t b[2][2];        // [expert tile][hi, lo]
 };
 
-__global__ void __launch_bounds__(256, 4) router_mfma_kernel(const float* __restrict__ x,
+__global__ void __launch_bounds__(256, 2) router_mfma_kernel(const float* __restrict__ x,
                                                              const float* __restrict__ xm,
                                                              const _Float16* __restrict__ wb,
                                                              const float* __restrict__ wm,
@@ -239,11 +247,27 @@ __global__ void __launch_bounds__(256, 4) router_mfma_kernel(const float* __rest
         a_lds[kb & 1][stile][0][slane] = hi;
         a_lds[kb & 1][stile][1][slane] = lo;
     };
+    // fp32 accumulator chains of at most kRouterChain blocks, each added into
+    // an fp64 sum when it ends.  The k loop runs in kRouterChain-block steps
+    // of four block pairs; after pair i the accumulators of token tile i end
+    // their chains (so each pair adds two of the eight while the others'
+    // MFMAs run).  A shorter rest of the range starts fresh chains.
+    static_assert(kRouterChain == 8, "four block pairs per step, one token tile's chains ending after each");
     float4_t acc[4][2];
+    double dacc[4][2][4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int et = 0; et < 2; ++et) acc[mt][et] = (float4_t){0.f, 0.f, 0.f, 0.f};
+        for (int et = 0; et < 2; ++et) {
+            acc[mt][et] = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int v = 0; v < 4; ++v) dacc[mt][et][v] = 0.0;
+        }
+    auto end_chain = [&](int mt, int et) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) dacc[mt][et][v] += (double)acc[mt][et][v];
+        acc[mt][et] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    };
     auto products = [&](int kb, const RouterStage& S) {
         half8_t a[4][2];
 #pragma unroll
@@ -262,9 +286,7 @@ __global__ void __launch_bounds__(256, 4) router_mfma_kernel(const float* __rest
     };
 
     RouterStage s0, s1;
-    load(kb0, s0);
-    load(kb0 + 1, s1);
-    for (int kb = kb0; kb < kb1; kb += 2) {
+    auto pair = [&](int kb) {  // blocks kb and kb + 1
         stage(kb, s0);
         __syncthreads();
         products(kb, s0);
@@ -273,7 +295,32 @@ __global__ void __launch_bounds__(256, 4) router_mfma_kernel(const float* __rest
         __syncthreads();
         products(kb + 1, s1);
         load(kb + 3, s1);
+    };
+    auto end_all = [&]() {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int et = 0; et < 2; ++et) end_chain(mt, et);
+    };
+    load(kb0, s0);
+    load(kb0 + 1, s1);
+    int kb = kb0;
+    for (; kb + kRouterChain <= kb1; kb += kRouterChain) {
+#pragma unroll
+        for (int i = 0; i < kRouterChain / 2; ++i) {
+            pair(kb + 2 * i);
+            end_chain(i, 0);
+            end_chain(i, 1);
+            // one pair at a time: letting later pairs' loads move up took 244 VGPRs
+            // against 186 (2 workgroups per CU either way; 365 vs 340 us at 32768 tokens)
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
+    if (kb < kb1) {  // uniform: the rest of the range, fewer than kRouterChain blocks
+        end_all();
+        for (; kb < kb1; kb += 2) pair(kb);
+    }
+    end_all();  // the last chains
 
     float* part = out + (int64_t)blockIdx.z * T * E;
 #pragma unroll
@@ -286,7 +333,8 @@ __global__ void __launch_bounds__(256, 4) router_mfma_kernel(const float* __rest
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int64_t t = m0 + 16 * mt + 4 * kg + v;
-                if (t < T) part[t * E + e] = acc[mt][et][v] * xm[t] * we + be;
+                // the multipliers are powers of two: one rounding, to fp32
+                if (t < T) part[t * E + e] = (float)(dacc[mt][et][v] * (double)xm[t] * (double)we + (double)be);
             }
     }
 }

@@ -1,9 +1,9 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle.
 
 Bars: routing ids, grouping tables and the layer input's int8 codes and
-scales bit-exact; routing weights within 2e-5 absolute (a softmax of the
-fp32-class logits: measured 1.6e-7 at the tiny layer to 5.0e-6 at 32768
-tokens, growing with the router's accumulation chain); SwiGLU-output codes equal except at rounding
+scales bit-exact; routing weights within 1e-6 absolute (a softmax of the
+fp32-class logits, whose accumulator chains are at most 8 blocks long:
+measured 1.6e-7 to 8.4e-7); SwiGLU-output codes equal except at rounding
 ties of the oracle's exact quotient (then off by one), at a rate below 1e-3;
 the down stage fed the oracle's H codes within max|err| / max|ref| <= 1e-5
 (and a per-output fp32 rounding bound); the layer output within
@@ -21,7 +21,7 @@ from layers import (canonical_expert, check_h_codes, down_error_bound, gate_boun
 
 pytestmark = pytest.mark.gpu
 
-P_TOL = 2e-5     # routing weights: the fp32-class logits' softmax (1e-6 holds only up to 2048 tokens)
+P_TOL = 1e-6     # routing weights: a softmax of the fp32-class logits
 Y_TOL = 2e-3
 DOWN_TOL = 1e-5   # the down stage alone, on the oracle's H codes
 H_RATE = 1e-3     # largest share of SwiGLU-output codes that may sit one step off at a rounding tie
@@ -178,8 +178,9 @@ def router_error_bound(x, wr, bias=None):
     3 H / 32 accumulator additions, plus a few for the split reduction and the
     bias, each within 2^-23 of its result; sum_h |x_h w_he| <=
     ||x||_2 ||w_e||_2.  The bias passes through at most 9 roundings (8 split
-    ranges and its own addition).  This is the bound of one split range, the
-    widest; the kernels' window counts the actual ranges."""
+    ranges and its own addition).  This counts one accumulator chain over all
+    of H, wider than the kernels' own bound (their chains end every 8 k blocks
+    into fp64 sums)."""
     H = x.shape[1]
     c = (3 * H / 32 + 40) * 2.0 ** -23 + 2.0 ** -20
     xn = np.linalg.norm(x.astype(np.float64), axis=1)
@@ -379,7 +380,9 @@ def test_layer_every_token_on_the_same_experts(qm):
     assert np.array_equal(np.nonzero(counts)[0], hot) and np.all(counts[hot] == s.T)
     for k in ("ids", "offsets", "src", "slot", "qx", "sx"):
         assert np.array_equal(g[k], ref[k]), k
-    assert np.abs(g["p"] - ref["p"]).max() <= P_TOL
+    # logits near 100 are 7.6e-6 apart in fp32: p within the softmax's response to the logits' bound
+    tol = 2.0 * router_error_bound(x, wr, bias)[:, None] + 1e-6
+    assert np.all(np.abs(g["p"] - ref["p"]) <= tol)
     assert check_h_codes(g["qh"], g["sh"], ref["h"], ref["qh"], ref["sh"]) < H_RATE
     assert rel_err(g["out"], ref["y"]) <= Y_TOL
     y = qm.strata_moe_prefill(_t(x), _t(wr), ex, s.K, torch.empty_like(out))
