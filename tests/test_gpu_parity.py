@@ -518,7 +518,19 @@ def _check_grouping_props(g, T, K, E):
 @pytest.mark.parametrize("name", ["stream_all_1k", "chunk_8k", "skewed_4k", "long_32k", "pages_q2_0_2k",
                                   "chunk_8k_shared", "pages_shared_2k", "short_256", "window_32"])
 def test_full_layer_sampled(qm, name):
-    s = S.shape(name)
+    _full_layer_sampled(qm, S.shape(name), name)
+
+
+def test_full_layer_longest_call(qm):
+    """The longest call the library takes at these widths: its tiled operands
+    ((T K + 15 E) x 2560 fp16 values) stay under 2 GiB up to 41,175 tokens.
+    At 40,960 they hold 2.14e9 bytes, so every buffer size and byte offset of
+    the GEMMs' buffer resources sits just under 2^31."""
+    s = S.custom(T=40960, H=2560, E=512, K=10, I=1024)
+    _full_layer_sampled(qm, s, "longest call")
+
+
+def _full_layer_sampled(qm, s, name):
     ex = gpu_experts(s)
     x, wr, bias = S.activations(s), S.router_weight(s), S.router_bias(s)
     xt, wt = _t(x), _t(wr)
