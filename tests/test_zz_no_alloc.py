@@ -66,6 +66,29 @@ def test_noalloc_rejects_a_call_larger_than_its_scratch(qm):
     assert torch.all(out == 7.0)  # nothing ran
 
 
+def test_noalloc_at_its_largest_call(qm):
+    """The longest call whose workspace fits the array (about 2,250 tokens at
+    H = 2560, I = 1024, E = 512, K = 10) against strata_moe_prefill, bit for
+    bit; one token more is rejected."""
+    base = S.shape("stream_all_1k")
+    ex = gpu_experts(base)
+    lo, hi = 1, 1 << 16  # the largest T whose workspace fits, by bisection on the sizing call
+    while lo < hi:
+        mid = (lo + hi + 1) // 2
+        lo, hi = (mid, hi) if qm.strata_moe_workspace_bytes(mid, base.K, ex) <= qm.NOALLOC_SCRATCH_BYTES else (lo, mid - 1)
+    s = S.custom(T=lo, H=base.H, E=base.E, K=base.K, I=base.I)
+    x, wr = _inputs(s)
+    y = qm.strata_moe_prefill(x, wr, ex, s.K, torch.empty_like(x))
+    out = torch.full_like(x, float("nan"))
+    qm.strata_moe_prefill_noalloc(x, wr, ex, s.K, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, y), s.T
+    x1 = torch.zeros((lo + 1, s.H), device="cuda")
+    with pytest.raises(qm.StrataMoeError) as ei:
+        qm.strata_moe_prefill_noalloc(x1, wr, ex, s.K, torch.empty_like(x1))
+    assert ei.value.code == qm.EINVAL
+
+
 @pytest.mark.parametrize("s", [S.custom(T=300, H=256, E=12, K=3, I=128), S.shape("window_32")], ids=lambda s: s.name)
 def test_noalloc_call_captured_in_a_graph(qm, s):
     # The entry point makes no allocation, memset or synchronisation, so a
