@@ -720,7 +720,7 @@ __device__ __forceinline__ void wave_dot2_fp64(const float* __restrict__ x, cons
 // token's list.  Each value comes from the same dot-product routine
 // whichever wave computes it.
 constexpr int kWaves = 4;
-constexpr int kSelectShort = 1024;  // wide up to here: 30 vs 38 us at 1024 tokens, 102 vs 67 at 8192
+constexpr int kSelectShort = 1024;  // wide up to here: 29 vs 33 us at 1024 tokens, 102 vs 67 at 8192
 template <int kSlots, int kSelectWaves, bool kWide>
 __global__ void __launch_bounds__(64 * kSelectWaves) topk_kernel(const float* __restrict__ logits, int nsplit,
                                                                 int64_t T, const float* __restrict__ x,
