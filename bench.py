@@ -381,10 +381,15 @@ def main() -> int:
         # the 32x32x16 MFMA: the ceiling of the exact block-scaled products, operands in registers
         for form in ("16x16x32", "32x32x16"):
             mfma[f"scaled_tiles6_f16_{form}"] = round(probe.strata_probe_scaled_tiles(form, 6)[0] / 1e12, 3)
+        # that shape with activation loads (0), plus the unpack and the LDS exchange, a barrier per block
+        # (1) or per two blocks (2)
+        for step in (0, 1, 2):
+            mfma[f"block_step{step}"] = round(probe.strata_probe_block_step(step)[0] / 1e12, 3)
         log("MFMA rates (TOP/s): " + ", ".join(f"{k} {mfma[k]}" for k in probe.KINDS)
             + f"; scaled blocks fp16 {mfma['scaled_blocks_f16']} vs int8 {mfma['scaled_blocks_i8']} T/s"
             + f"; at the kernel's 6 tiles: 16x16x32 {mfma['scaled_tiles6_f16_16x16x32']}, "
-            + f"32x32x16 {mfma['scaled_tiles6_f16_32x32x16']} T/s")
+            + f"32x32x16 {mfma['scaled_tiles6_f16_32x32x16']} T/s; block step "
+            + ", ".join(str(mfma[f"block_step{i}"]) for i in range(3)) + " T/s")
         reads = {str(g): round(probe.strata_probe_hbm_read(2 << 30, g)[0], 1) for g in (1024, 4096, 16384)}
         hbm = {"read_gbs": max(reads.values()), "by_workgroups": reads, "bytes": 2 << 30,
                "kernel": "16-byte loads, 4 in flight per thread, grid-stride, 256 threads per workgroup"}

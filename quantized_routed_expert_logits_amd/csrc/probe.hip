@@ -16,6 +16,12 @@
 //     (two chained per tile and block, 16 FMAs per lane), operands in
 //     registers: the ceiling of the exact block-scaled products before any
 //     load, unpack or barrier.
+//   strata_probe_block_step: that shape built up toward the kernel's block
+//     step: (0) the products and FMAs with the three activation fragments of
+//     each block loaded from a small buffer; (1) plus a stand-in for the
+//     weight unpack (one dword per lane, 25 VALU into two fragments) whose
+//     fragments the four waves exchange through LDS with one barrier per
+//     block; (2) the same with one barrier per two blocks.
 //   strata_probe_mfma_f16: one v_mfma_f32_16x16x32_f16 on given operands
 //     (row-major A [16][32], B [32][16], C [16][16]), to check how it rounds.
 //   strata_probe_hbm_read: the read bandwidth a plain streaming kernel gets
@@ -212,6 +218,91 @@ __global__ void __launch_bounds__(64 * kWavesPerGroup, 2) scaled_tiles_kernel(in
     if (lane == 0) out[blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6)] = r;
 }
 
+// The block step of the 4-wave gate/up kernel, built up (see the file
+// header).  kStep 0: 8 weight fragments in registers; 1 and 2: each wave
+// makes two of them from a loaded dword and the waves exchange them through
+// LDS (buffers kb & 1, or kb & 3 with one barrier per block pair).  Every
+// wave: 3 token tiles x 8 fragments of MFMAs and one FMA per output, the next
+// block's 3 activation fragments loaded from act (256 fragments of 1 KiB).
+template <int kStep>
+__global__ void __launch_bounds__(64 * kWavesPerGroup, 2) block_step_kernel(int32_t blocks, int32_t seed,
+                                                                           const half8_t* __restrict__ act,
+                                                                           const uint32_t* __restrict__ rec,
+                                                                           float* __restrict__ out) {
+    typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+    __shared__ half8_t a_lds[kStep == 2 ? 4 : 2][8][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, s = seed + lane;
+    float4_t acc[8][3] = {};
+    float ssc = 1.0f + (float)(s & 15) * 0x1p-12f;
+    half8_t a[8], bf[2][3];
+    for (int f = 0; f < 8; ++f)
+        for (int i = 0; i < 8; ++i) a[f][i] = (_Float16)(float)(((s * (2 * f + 1) + 3 * i) & 7) - 3);
+    for (int t = 0; t < 3; ++t)
+        for (int i = 0; i < 8; ++i) bf[0][t][i] = bf[1][t][i] = (_Float16)(float)(s - i + t);
+    const int base = (blockIdx.x * kWavesPerGroup + wave) % 16;
+    // two fp16 fragments from one dword: 8 AND-ORs (a shift for the high codes), 8 packed subtracts and
+    // 8 packed multiplies, as the kernel's unpack
+    auto unpack = [&](int b, half8_t& r0, half8_t& r1) {
+        const uint32_t xw = rec[((base + b) & 255) * 256 + threadIdx.x], hi = xw >> 10;
+        const half2_t c = {(_Float16)1025.0f, (_Float16)1025.0f}, d = {(_Float16)0.01f, (_Float16)0.02f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t o0 = ((q < 5 ? xw : hi) & (0x00030003u << (2 * (q % 5)))) | (0x64006400u - (q << 26));
+            const uint32_t o1 =
+                (((q + 4) < 5 ? xw : hi) & (0x00030003u << (2 * ((q + 4) % 5)))) | (0x64006400u - ((q + 4) << 26));
+            const half2_t v0 = (__builtin_bit_cast(half2_t, o0) - c) * d, v1 = (__builtin_bit_cast(half2_t, o1) - c) * d;
+            r0[2 * q] = v0[0], r0[2 * q + 1] = v0[1];
+            r1[2 * q] = v1[0], r1[2 * q + 1] = v1[1];
+        }
+    };
+    auto products = [&](int b, int h) {
+#pragma unroll
+        for (int t = 0; t < 3; ++t) bf[h ^ 1][t] = act[((base + 3 * b + t) & 255) * 64 + lane];
+#pragma unroll
+        for (int f = 0; f < 8; ++f)
+#pragma unroll
+            for (int t = 0; t < 3; ++t) {
+                const float4_t p =
+                    __builtin_amdgcn_mfma_f32_16x16x32_f16(a[f], bf[h][t], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[f][t][v] = fmaf(p[v], ssc, acc[f][t][v]);
+            }
+        ssc += 0x1p-20f;
+    };
+    for (int blk = 0; blk < blocks; blk += 2) {
+        if constexpr (kStep == 2) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                half8_t r0, r1;
+                unpack(blk + h, r0, r1);
+                a_lds[(blk + h) & 3][2 * wave][lane] = r0;
+                a_lds[(blk + h) & 3][2 * wave + 1][lane] = r1;
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int b = blk + h;
+            if constexpr (kStep == 1) {
+                half8_t r0, r1;
+                unpack(b, r0, r1);
+                a_lds[b & 1][2 * wave][lane] = r0;
+                a_lds[b & 1][2 * wave + 1][lane] = r1;
+                __syncthreads();
+            }
+            if constexpr (kStep > 0) {
+#pragma unroll
+                for (int f = 0; f < 8; ++f) a[f] = a_lds[b & (kStep == 2 ? 3 : 1)][f][lane];
+            }
+            products(b, h);
+        }
+    }
+    float r = 0.f;
+    for (int f = 0; f < 8; ++f)
+        for (int t = 0; t < 3; ++t) r += acc[f][t][0] + acc[f][t][3];
+    if (lane == 0) out[blockIdx.x * kWavesPerGroup + wave] = r;
+}
+
 // One 16x16x32 fp16 MFMA on row-major operands, one wave.  The lane layout
 // of the instruction: A lane l holds row l % 16, k = 8 (l / 16) .. + 7; B
 // lane l holds column l % 16, the same k; C/D lane l holds rows
@@ -281,6 +372,13 @@ template <bool kI8>
 void launch_scaled(hipStream_t st) {
     hipLaunchKernelGGL(scaled_blocks_kernel<kI8>, dim3(g_groups), dim3(64 * kWavesPerGroup), 0, st, g_iters, 0, g_out);
 }
+const half8_t* g_act = nullptr;
+const uint32_t* g_rec = nullptr;
+template <int kStep>
+void launch_step(hipStream_t st) {
+    hipLaunchKernelGGL(block_step_kernel<kStep>, dim3(g_groups), dim3(64 * kWavesPerGroup), 0, st, g_iters, 0, g_act,
+                       g_rec, g_out);
+}
 template <int kForm, int kTiles>
 void launch_tiles(hipStream_t st) {
     hipLaunchKernelGGL((scaled_tiles_kernel<kForm, kTiles>), dim3(g_groups), dim3(64 * kWavesPerGroup), 0, st,
@@ -346,6 +444,41 @@ int strata_probe_scaled_tiles(int form, int tiles, int32_t groups, int32_t block
     (void)hipFree(g_out);
     g_out = nullptr;
     const double n = (double)groups * kWavesPerGroup * blocks * 1024.0 * tiles;
+    *out_blocks_per_s = rc == 0 && *ms > 0 ? n / (*ms * 1e-3) : 0.0;
+    return rc;
+}
+
+// step 0, 1 or 2 (see block_step_kernel); blocks even.  Writes 6 x 32 x 32
+// output-blocks per wave and block over the kernel time, per second.
+// Returns 0, -1 (arguments), -4 (a HIP call failed).
+int strata_probe_block_step(int step, int32_t groups, int32_t blocks, double* out_blocks_per_s, double* ms) {
+    if (step < 0 || step > 2 || groups < 1 || blocks < 2 || blocks % 2 || !out_blocks_per_s || !ms) return -1;
+    void* act = nullptr;
+    void* rec = nullptr;
+    if (hipMalloc(&act, sizeof(half8_t) * 64 * 256) != hipSuccess) return -4;
+    if (hipMalloc(&rec, sizeof(uint32_t) * 256 * 256) != hipSuccess) {
+        (void)hipFree(act);
+        return -4;
+    }
+    int rc = hipMemset(act, 0, sizeof(half8_t) * 64 * 256) == hipSuccess &&
+                     hipMemset(rec, 0x5a, sizeof(uint32_t) * 256 * 256) == hipSuccess &&
+                     hipMalloc(&g_out, sizeof(float) * groups * kWavesPerGroup) == hipSuccess
+                 ? 0
+                 : -4;
+    if (rc == 0) {
+        g_act = static_cast<const half8_t*>(act);
+        g_rec = static_cast<const uint32_t*>(rec);
+        g_iters = blocks;
+        g_groups = groups;
+        rc = run_timed(step == 0 ? launch_step<0> : step == 1 ? launch_step<1> : launch_step<2>, ms);
+        (void)hipFree(g_out);
+        g_out = nullptr;
+    }
+    (void)hipFree(act);
+    (void)hipFree(rec);
+    g_act = nullptr;
+    g_rec = nullptr;
+    const double n = (double)groups * kWavesPerGroup * blocks * 1024.0 * 6;
     *out_blocks_per_s = rc == 0 && *ms > 0 ? n / (*ms * 1e-3) : 0.0;
     return rc;
 }

@@ -18,6 +18,7 @@ _f = ctypes.POINTER(ctypes.c_float)
 _lib.strata_probe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _d, _d]
 _lib.strata_probe_scaled_blocks.argtypes = [ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _d, _d]
 _lib.strata_probe_scaled_tiles.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _d, _d]
+_lib.strata_probe_block_step.argtypes = [ctypes.c_int, ctypes.c_int32, ctypes.c_int32, _d, _d]
 _lib.strata_probe_mfma_f16.argtypes = [_f, _f, _f, _f]
 _lib.strata_probe_hbm_read.argtypes = [ctypes.c_int64, ctypes.c_int32, _d, _d]
 
@@ -51,6 +52,17 @@ def strata_probe_scaled_tiles(form: str, tiles: int, groups: int = 2048, blocks:
                                         ctypes.byref(r), ctypes.byref(ms))
     if rc != 0:
         raise RuntimeError(f"strata_probe_scaled_tiles failed ({rc})")
+    return r.value, ms.value
+
+
+def strata_probe_block_step(step: int, groups: int = 2048, blocks: int = 512) -> tuple[float, float]:
+    """(scaled output-blocks per second, kernel ms) of the gate/up block step built up: 0 the products and
+    FMAs with activation loads, 1 plus the unpack stand-in and the LDS exchange with a barrier per block,
+    2 the same with a barrier per two blocks."""
+    r, ms = ctypes.c_double(), ctypes.c_double()
+    rc = _lib.strata_probe_block_step(step, groups, blocks, ctypes.byref(r), ctypes.byref(ms))
+    if rc != 0:
+        raise RuntimeError(f"strata_probe_block_step failed ({rc})")
     return r.value, ms.value
 
 

@@ -238,7 +238,7 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     from quantized_routed_expert_logits_amd import probe
     lib = ctypes.CDLL(probe.LIB_PATH)
     for name in ("strata_probe_mfma_rate", "strata_probe_scaled_blocks", "strata_probe_scaled_tiles",
-                 "strata_probe_mfma_f16", "strata_probe_hbm_read"):
+                 "strata_probe_block_step", "strata_probe_mfma_f16", "strata_probe_hbm_read"):
         assert hasattr(lib, name), name
     d = ctypes.c_double()
     # argument checks come before any HIP call
@@ -248,6 +248,8 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert probe._lib.strata_probe_mfma_rate(99, 1, 1, ctypes.byref(d), ctypes.byref(d)) == -1
     assert probe._lib.strata_probe_scaled_tiles(2, 6, 1, 1, ctypes.byref(d), ctypes.byref(d)) == -1  # form
     assert probe._lib.strata_probe_scaled_tiles(0, 4, 1, 1, ctypes.byref(d), ctypes.byref(d)) == -1  # tiles
+    assert probe._lib.strata_probe_block_step(3, 1, 2, ctypes.byref(d), ctypes.byref(d)) == -1  # step
+    assert probe._lib.strata_probe_block_step(0, 1, 3, ctypes.byref(d), ctypes.byref(d)) == -1  # odd blocks
 
 
 def test_one_call_is_limited_by_its_tiled_operands(qm):

@@ -92,3 +92,7 @@ def test_probe_rates_below_published_peaks(probe):
             rate, _ = probe.strata_probe_scaled_tiles(form, tiles)
             print(f"scaled tiles {form} x {tiles}: {rate / 1e12:.1f} T output-blocks/s")
             assert 0 < rate * 64 <= 1.05 * PEAK_F16, (form, tiles, rate)
+    for step in (0, 1, 2):
+        rate, _ = probe.strata_probe_block_step(step)
+        print(f"block step {step}: {rate / 1e12:.1f} T output-blocks/s")
+        assert 0 < rate * 64 <= 1.05 * PEAK_F16, (step, rate)
