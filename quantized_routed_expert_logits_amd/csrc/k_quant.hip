@@ -391,7 +391,7 @@ __global__ void __launch_bounds__(256) offset_rows_kernel(float* __restrict__ hu
 // padded by 8 bytes), then lane 16 g + r of a wave writes row r, group g of
 // a block, so each block's fragment is one contiguous 1 KiB store; wave w
 // takes blocks w, w + 4, ...  Rows past a tile's nrows are zeros.
-constexpr int kGatherCols = 640;                               // columns per slice (20 blocks, 5 scale groups)
+constexpr int kGatherCols = 1280;  // columns per slice (40 blocks, 10 scale groups; 640 measured 4 us slower at T = 8192)
 constexpr int kGatherPer = (16 * (kGatherCols / 16) + 255) / 256;  // 16-byte pieces per thread
 inline size_t gather_tiles_lds_bytes(int32_t cols) {
     const int sc = cols < kGatherCols ? cols : kGatherCols;
