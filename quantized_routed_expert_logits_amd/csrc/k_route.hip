@@ -624,9 +624,15 @@ __device__ __forceinline__ void write_token(const V (&lv)[kMaxTopK], const int (
                                             int64_t t, int32_t* __restrict__ ids, float* __restrict__ p_out) {
     V mine = lv[0];
     int mi = li[0];
+    // a chain of selects; the empty asm keeps the compiler from turning it
+    // into a table in scratch memory indexed by the lane
 #pragma unroll
-    for (int k = 1; k < kMaxTopK; ++k)
-        if (lane == k) mine = lv[k], mi = li[k];
+    for (int k = 1; k < kMaxTopK; ++k) {
+        const bool me = lane == k;
+        mine = me ? lv[k] : mine;
+        mi = me ? li[k] : mi;
+        asm volatile("" : "+v"(mine), "+v"(mi));
+    }
     const float ev = lane < K ? expf((float)(mine - lv[0])) : 0.0f;
     const float z = wave_sum_f(ev);
     if (lane < K) {
