@@ -727,8 +727,11 @@ __device__ __forceinline__ void wave_dot2_fp64(const float* __restrict__ x, cons
 // whichever wave computes it.
 constexpr int kWaves = 4;
 constexpr int kSelectShort = 1024;  // wide up to here: 29 vs 33 us at 1024 tokens, 102 vs 67 at 8192
+// The narrow form held to 5 waves per SIMD (96 VGPRs; the compiler spills a
+// few of the re-score's registers): 42 vs 43 us at 8192 tokens, 102 vs 111 at
+// 32768 (6 waves: 47 and 107).
 template <int kSlots, int kSelectWaves, bool kWide>
-__global__ void __launch_bounds__(64 * kSelectWaves) topk_kernel(const float* __restrict__ logits, int nsplit,
+__global__ void __launch_bounds__(64 * kSelectWaves, kWide ? 1 : 5) topk_kernel(const float* __restrict__ logits, int nsplit,
                                                                 int64_t T, const float* __restrict__ x,
                                                                 const float* __restrict__ wt,
                                                                 const float* __restrict__ bias, int32_t H, int32_t E,
