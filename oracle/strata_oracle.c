@@ -3,7 +3,7 @@
  *
  * TEST INFRASTRUCTURE ONLY.  This is a plain, slow, double-precision reference
  * used by the tests, the smoke check and the benchmark's CPU-baseline leg to
- * judge the HIP library.  The product path never links, loads or calls it, and
+ * check the HIP library.  The product path never links, loads or calls it, and
  * it shares no code, header, table or helper with that library.
  *
  * What it computes, and where the pages say so:
